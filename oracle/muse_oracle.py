@@ -1,0 +1,540 @@
+"""Plain, slow, float64 CPU oracle for Multipole Semantic Attention (MuSe).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this
+module: only the test suite, the smoke check and the CPU-baseline leg of the
+benchmark do.  It shares no code with the HIP library.
+
+Sources (cited by page and section; the pages are scraped text about
+arXiv 2509.10406, "Multipole Semantic Attention: A Fast Approximation of
+Softmax Attention for Pretraining", Mitchell and Kersting):
+
+* [GIST-BSC]  gist.science page, Technical Summary, Core Mechanisms,
+  "Bidirectional Semantic Clustering": queries and keys are clustered
+  separately, each in its own space.
+* [GIST-DEC]  same page, Core Mechanisms, "Decomposition": q = centroid +
+  residual, k = centroid + residual; of the four terms of the exponent
+  (centroid+residual).(centroid+residual) the residual-residual term is the
+  only one dropped.
+* [GIST-H2S]  same page, Core Mechanisms, "Hierarchical Two-Stage
+  Attention" and "Exponential Tilting": query-cluster centroids attend to
+  key clusters and give query-cluster-specific summaries (stage 1); each
+  query refines with its residual (stage 2).
+* [GIST-RAA]  same page, Core Mechanisms, "Retrieval-Augmented
+  Approximation": the top-k1 key clusters by tilted summary score are
+  attended exactly; the rest go through the summaries.
+* [NEWX-ABS]  newx.sg page, "Abstract" (first version): monopole
+  (centroid) approximation plus dipole correction; O(NCD) acausal and
+  O(NCD log N) causal; causal attention by a hierarchical block
+  decomposition with exact local blocks and approximated long-range blocks.
+
+Readings of points the pages leave open (each one listed in the design
+document):
+
+* clustering is Lloyd k-means with squared Euclidean distance on the raw
+  vectors, a fixed number of iterations, seeded initial points, ties to the
+  lowest cluster index, empty clusters keep their previous centroid;
+* the softmax scale s multiplies q.k (default 1/sqrt(D)); clustering uses
+  the unscaled vectors;
+* the dipole of a key cluster c is M_c = sum_j v_j (k_j - mu_c)^T and it is
+  evaluated at the query-cluster centroid nu_I (first-order tilt), so the
+  tilted summary is T_Ic = S_c + s M_c nu_I with S_c = sum_j v_j; the
+  normaliser of the far field is the exact count n_c (the count dipole is
+  identically zero);
+* the score used for retrieval is sigma_Ic = s nu_I.mu_c + ln n_c (log of the
+  monopole tilted mass), ties to the lower cluster index;
+* the causal scheme is the dyadic hierarchy of ``causal_plan``.
+
+Parity pins for every function here live in tests/test_oracle_*.py
+(brute-force exact limits, closed forms, a direct first-order Taylor check
+with its epsilon^2 error law, invariants, scipy's k-means and central finite
+differences for the backward).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# Problem configuration
+# ----------------------------------------------------------------------------
+@dataclass
+class MuseConfig:
+    """Hyperparameters: the pages say MuSe needs only these (NEWX-ABS)."""
+
+    cq: int = 16          # query clusters per problem (clamped to the set size)
+    ck: int = 16          # key clusters per problem (clamped to the set size)
+    iters: int = 10       # Lloyd iterations
+    topk: int = 0         # k1 retrieved key clusters per query cluster
+    block: int = 0        # causal local block size B
+    causal: bool = False
+    dipole: bool = True   # False: monopole only (T_Ic = S_c)
+    scale: float = 0.0    # <= 0 means 1/sqrt(D)
+
+    def s(self, D: int) -> float:
+        return self.scale if self.scale > 0 else 1.0 / math.sqrt(D)
+
+
+# ----------------------------------------------------------------------------
+# O1: Lloyd k-means, done literally (GIST-BSC; reading: Lloyd, fixed T)
+# ----------------------------------------------------------------------------
+def sq_dist(X: np.ndarray, mu: np.ndarray, rows: int = 1024) -> np.ndarray:
+    """||x_j - mu_c||^2 for every (j, c), summed term by term (no expansion)."""
+    X = np.asarray(X, np.float64)
+    mu = np.asarray(mu, np.float64)
+    out = np.empty((X.shape[0], mu.shape[0]), np.float64)
+    for r0 in range(0, X.shape[0], rows):
+        diff = X[r0:r0 + rows, None, :] - mu[None, :, :]
+        out[r0:r0 + rows] = np.einsum("ncd,ncd->nc", diff, diff)
+    return out
+
+
+def assign_step(X: np.ndarray, mu: np.ndarray) -> np.ndarray:
+    """Nearest centroid; np.argmin returns the first (lowest) index on ties."""
+    return np.argmin(sq_dist(X, mu), axis=1)
+
+
+def update_step(X: np.ndarray, labels: np.ndarray, mu_prev: np.ndarray) -> np.ndarray:
+    """Mean of each cluster's members; an empty cluster keeps its centroid."""
+    X = np.asarray(X, np.float64)
+    mu = np.array(mu_prev, np.float64, copy=True)
+    for c in range(mu.shape[0]):
+        members = X[labels == c]
+        if len(members):
+            mu[c] = members.sum(axis=0) / len(members)
+    return mu
+
+
+def kmeans(X, C: int, iters: int, init_idx, history: bool = False):
+    """Lloyd's algorithm from the points X[init_idx] as starting centroids.
+
+    Returns (labels of the last assignment, centroids after the last
+    update[, list of (labels_t, mu_t) for t = 1..iters]).
+    """
+    X = np.asarray(X, np.float64)
+    init_idx = np.asarray(init_idx, np.int64)[:C]
+    assert len(set(init_idx.tolist())) == C, "initial indices must be distinct"
+    mu = X[init_idx].copy()
+    labels = np.zeros(X.shape[0], np.int64)
+    hist = []
+    for _ in range(iters):
+        labels = assign_step(X, mu)
+        mu = update_step(X, labels, mu)
+        if history:
+            hist.append((labels.copy(), mu.copy()))
+    if history:
+        return labels, mu, hist
+    return labels, mu
+
+
+def default_init(n: int, C: int) -> np.ndarray:
+    """Evenly spaced starting points floor(c n / C): the library's default."""
+    return np.array([(c * n) // C for c in range(C)], np.int64)
+
+
+# ----------------------------------------------------------------------------
+# O2-O4: cluster statistics, scores, retrieval, tilted summaries
+# ----------------------------------------------------------------------------
+def key_stats(K, V, labels, C):
+    """Monopole (n_c, mu_c, S_c) and dipole M_c = sum_j v_j (k_j - mu_c)^T
+    of every key cluster (NEWX-ABS: centroid approximation + dipole)."""
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    D, Dv = K.shape[1], V.shape[1]
+    n = np.zeros(C, np.int64)
+    mu = np.zeros((C, D))
+    S = np.zeros((C, Dv))
+    M = np.zeros((C, Dv, D))
+    for c in range(C):
+        idx = np.nonzero(labels == c)[0]
+        n[c] = len(idx)
+        if n[c] == 0:
+            continue
+        mu[c] = K[idx].sum(axis=0) / n[c]
+        S[c] = V[idx].sum(axis=0)
+        M[c] = V[idx].T @ (K[idx] - mu[c])      # sum of outer products
+    return n, mu, S, M
+
+
+def query_stats(Q, labels, C):
+    """Size m_I and centroid nu_I of every query cluster (GIST-DEC)."""
+    Q = np.asarray(Q, np.float64)
+    m = np.zeros(C, np.int64)
+    nu = np.zeros((C, Q.shape[1]))
+    for c in range(C):
+        idx = np.nonzero(labels == c)[0]
+        m[c] = len(idx)
+        if m[c]:
+            nu[c] = Q[idx].sum(axis=0) / m[c]
+    return m, nu
+
+
+def cluster_scores(nu, mu, n, s):
+    """sigma_Ic = s nu_I.mu_c + ln n_c; -inf for empty key clusters.
+
+    exp(sigma_Ic) is the monopole estimate of sum_{j in c} exp(s nu_I.k_j),
+    the tilted mass of cluster c seen from query centroid nu_I (GIST-RAA).
+    """
+    with np.errstate(divide="ignore"):
+        logn = np.where(n > 0, np.log(np.maximum(n, 1).astype(np.float64)), -np.inf)
+    return s * (np.asarray(nu) @ np.asarray(mu).T) + logn[None, :]
+
+
+def select_topk(sig_row, k1):
+    """The k1 largest scores among non-empty clusters, ties to the lower
+    index; returns a sorted array of cluster ids (GIST-RAA, cluster
+    selection).  k1 is clamped to the number of non-empty clusters."""
+    valid = [c for c in range(len(sig_row)) if np.isfinite(sig_row[c])]
+    order = sorted(valid, key=lambda c: (-sig_row[c], c))
+    return np.array(sorted(order[:max(0, k1)]), np.int64)
+
+
+def tilted_summaries(S, M, nu, s, dipole=True):
+    """T_Ic = S_c + s M_c nu_I: the value sum of cluster c seen from query
+    cluster I, to first order in the tilt exp(s nu_I.(k_j - mu_c))
+    (GIST-H2S exponential tilting; NEWX-ABS dipole correction)."""
+    T = np.broadcast_to(S[None, :, :], (nu.shape[0],) + S.shape).copy()
+    if dipole:
+        T += s * np.einsum("cde,Ie->Icd", M, nu)
+    return T
+
+
+# ----------------------------------------------------------------------------
+# O5: one acausal problem (two stages: far field + exact retrieval)
+# ----------------------------------------------------------------------------
+@dataclass
+class ProblemResult:
+    o: np.ndarray              # [n_q, Dv] normalised partial output
+    lse: np.ndarray            # [n_q]
+    aq: np.ndarray             # query labels
+    ak: np.ndarray             # key labels
+    R: list                    # retrieved key clusters per query cluster
+    n: np.ndarray = None
+    mu: np.ndarray = None
+    S: np.ndarray = None
+    M: np.ndarray = None
+    m: np.ndarray = None
+    nu: np.ndarray = None
+    T: np.ndarray = None
+    sigma: np.ndarray = None
+    mu_q: np.ndarray = None    # query k-means centroids (== nu where non-empty)
+    extra: dict = field(default_factory=dict)
+
+
+def solve_problem(Q, K, V, s, Cq, Ck, k1, iters, init_q=None, init_k=None,
+                  aq=None, ak=None, R=None, dipole=True):
+    """One acausal MuSe problem: queries Q [n_q, D] against keys K, V.
+
+    aq/ak/R, when given, replace the clustering and the retrieval (the
+    shared-state comparison with the GPU); otherwise they are computed.
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    nq, nk = Q.shape[0], K.shape[0]
+    Cq, Ck = min(Cq, nq), min(Ck, nk)
+    mu_q = None
+    if ak is None:
+        ik = default_init(nk, Ck) if init_k is None else np.asarray(init_k)[:Ck]
+        ak, _ = kmeans(K, Ck, iters, ik)
+    if aq is None:
+        iq = default_init(nq, Cq) if init_q is None else np.asarray(init_q)[:Cq]
+        aq, mu_q = kmeans(Q, Cq, iters, iq)
+    ak = np.asarray(ak, np.int64)
+    aq = np.asarray(aq, np.int64)
+    n, mu, S, M = key_stats(K, V, ak, Ck)
+    m, nu = query_stats(Q, aq, Cq)
+    sig = cluster_scores(nu, mu, n, s)
+    if R is None:
+        R = [select_topk(sig[I], k1) if m[I] > 0 else np.zeros(0, np.int64)
+             for I in range(Cq)]
+    T = tilted_summaries(S, M, nu, s, dipole)
+
+    Dv = V.shape[1]
+    o = np.zeros((nq, Dv))
+    lse = np.zeros(nq)
+    for I in range(Cq):
+        rows = np.nonzero(aq == I)[0]
+        if len(rows) == 0:
+            continue
+        retrieved = [int(c) for c in R[I]]
+        ek = np.nonzero(np.isin(ak, retrieved))[0]
+        far = np.array([c for c in range(Ck) if n[c] > 0 and c not in retrieved], np.int64)
+        # Items of query i: exact keys (weight 1, value v_j) and far clusters
+        # (logit s q_i.mu_c, weight n_c, total value T_Ic).  Per GIST-DEC the
+        # centroid term, q_i.mu_c and nu_I.(k_j - mu_c) are kept; the residual
+        # cross term (q_i - nu_I).(k_j - mu_c) is dropped.
+        ell = s * (Q[rows] @ K[ek].T)                      # [r, |ek|]
+        lam = s * (Q[rows] @ mu[far].T)                    # [r, |far|]
+        logw = np.concatenate([ell, lam + np.log(n[far].astype(np.float64))[None, :]], axis=1)
+        if logw.shape[1] == 0:
+            continue
+        mx = logw.max(axis=1, keepdims=True)
+        we = np.exp(ell - mx)
+        wf = np.exp(lam - mx)
+        den = we.sum(axis=1) + wf @ n[far].astype(np.float64)
+        num = we @ V[ek] + wf @ T[I, far]
+        o[rows] = num / den[:, None]
+        lse[rows] = mx[:, 0] + np.log(den)
+    return ProblemResult(o=o, lse=lse, aq=aq, ak=ak, R=R, n=n, mu=mu, S=S, M=M,
+                         m=m, nu=nu, T=T, sigma=sig, mu_q=mu_q)
+
+
+# ----------------------------------------------------------------------------
+# O6/O7: whole calls.  Layout [B, H, N, D]; query head h uses KV head
+# floor(h * Hkv / Hq).
+# ----------------------------------------------------------------------------
+def causal_plan(N: int, Bblk: int):
+    """Dyadic block hierarchy (NEWX-ABS: exact local blocks plus long-range
+    blocks on log N levels).  Level l has span m = Bblk 2^l; segment t keys
+    are rows [2mt, 2mt + m), its queries rows [2mt + m, min(2mt + 2m, N)).
+    Returns a list of dicts (level, t, k0, kn, q0, qn) in level-major order.
+    """
+    nb = -(-N // Bblk)
+    L = 0 if nb <= 1 else int(math.ceil(math.log2(nb)))
+    plan = []
+    for lev in range(L):
+        m = Bblk << lev
+        t = 0
+        while t * 2 * m + m < N:
+            k0 = t * 2 * m
+            q0 = k0 + m
+            plan.append(dict(level=lev, t=t, k0=k0, kn=m, q0=q0, qn=min(m, N - q0)))
+            t += 1
+    return plan
+
+
+def acausal_plan(N: int):
+    return [dict(level=0, t=0, k0=0, kn=N, q0=0, qn=N)]
+
+
+def merge_partials(parts):
+    """Log-sum-exp merge of normalised partials [(o, lse), ...]."""
+    lses = np.stack([p[1] for p in parts])
+    top = np.max(lses, axis=0)
+    top = np.where(np.isfinite(top), top, 0.0)
+    w = np.exp(lses - top)
+    tot = w.sum(axis=0)
+    o = sum(w[k][:, None] * parts[k][0] for k in range(len(parts))) / tot[:, None]
+    return o, top + np.log(tot)
+
+
+def local_causal(Q, K, V, s, Bblk):
+    """Exact attention of row i over keys [Bblk floor(i/Bblk), i]."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    N = Q.shape[0]
+    o = np.zeros((N, V.shape[1]))
+    lse = np.zeros(N)
+    for b0 in range(0, N, Bblk):
+        b1 = min(b0 + Bblk, N)
+        logits = s * (Q[b0:b1] @ K[b0:b1].T)
+        mask = np.tril(np.ones((b1 - b0, b1 - b0), bool))
+        logits = np.where(mask, logits, -np.inf)
+        mx = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - mx)
+        den = p.sum(axis=1, keepdims=True)
+        o[b0:b1] = (p @ V[b0:b1]) / den
+        lse[b0:b1] = mx[:, 0] + np.log(den[:, 0])
+    return o, lse
+
+
+def forward_head(Qh, Kh, Vh, cfg: MuseConfig, inits=None, shared=None):
+    """MuSe for one query head against its KV head: [N, D] each.
+
+    inits:  optional dict problem_index -> (init_q, init_k)
+    shared: optional dict problem_index -> (aq, ak, R) from another run
+    Returns (o, lse, list of ProblemResult).
+    """
+    N, D = Qh.shape
+    s = cfg.s(D)
+    plan = causal_plan(N, cfg.block) if cfg.causal else acausal_plan(N)
+    parts_o = np.zeros((len(plan), N, Vh.shape[1]))
+    parts_l = np.full((len(plan), N), -np.inf)
+    results = []
+    for p, pr in enumerate(plan):
+        q0, qn, k0, kn = pr["q0"], pr["qn"], pr["k0"], pr["kn"]
+        iq, ik = (inits or {}).get(p, (None, None))
+        aq, ak, R = (shared or {}).get(p, (None, None, None))
+        r = solve_problem(Qh[q0:q0 + qn], Kh[k0:k0 + kn], Vh[k0:k0 + kn], s,
+                          cfg.cq, cfg.ck, cfg.topk, cfg.iters, iq, ik, aq, ak, R,
+                          cfg.dipole)
+        parts_o[p, q0:q0 + qn] = r.o
+        parts_l[p, q0:q0 + qn] = r.lse
+        results.append(r)
+    if not cfg.causal:
+        return parts_o[0], parts_l[0], results
+    lo, ll = local_causal(Qh, Kh, Vh, s, cfg.block)
+    o, lse = merge_partials([(lo, ll)] + [(parts_o[p], parts_l[p]) for p in range(len(plan))])
+    return o, lse, results
+
+
+def forward(Q, K, V, cfg: MuseConfig, inits=None, shared=None, heads=None):
+    """Q [B, Hq, N, D], K/V [B, Hkv, N, D].  Returns O, lse and per-(b, h)
+    problem results.  inits/shared are dicts keyed by (b, h) holding the
+    per-problem dicts of ``forward_head``.  heads restricts the (b, h)
+    pairs computed (others stay zero)."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    B, Hq, N, _ = Q.shape
+    Hkv = K.shape[1]
+    O = np.zeros((B, Hq, N, V.shape[3]))
+    L = np.zeros((B, Hq, N))
+    res = {}
+    for b in range(B):
+        for h in range(Hq):
+            if heads is not None and (b, h) not in heads:
+                continue
+            g = (h * Hkv) // Hq
+            o, l, r = forward_head(Q[b, h], K[b, g], V[b, g], cfg,
+                                   (inits or {}).get((b, h)), (shared or {}).get((b, h)))
+            O[b, h], L[b, h], res[(b, h)] = o, l, r
+    return O, L, res
+
+
+def exact_attention(Q, K, V, s, causal=False):
+    """Brute-force softmax attention (the quantity MuSe approximates)."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    logits = s * (Q @ np.swapaxes(K, -1, -2))
+    if causal:
+        N = Q.shape[-2]
+        logits = np.where(np.tril(np.ones((N, K.shape[-2]), bool)), logits, -np.inf)
+    mx = logits.max(axis=-1, keepdims=True)
+    p = np.exp(logits - mx)
+    den = p.sum(axis=-1, keepdims=True)
+    return (p @ V) / den, (mx + np.log(den))[..., 0]
+
+
+# ----------------------------------------------------------------------------
+# O9: backward with the assignments, retrieval sets and counts held fixed
+# ----------------------------------------------------------------------------
+def backward_problem(Q, K, V, s, aq, ak, R, Cq, Ck, lse, Delta, dO, dipole=True):
+    """Gradient contributions of one acausal problem.
+
+    Every quantity of ``solve_problem`` is differentiated except the labels,
+    the retrieval sets and the counts, which are constants.  lse and Delta
+    are the final (merged) per-query values, so the same function serves
+    the causal parts.  Returns (dQ, dK, dV) for the problem's rows.
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    nq, nk = Q.shape[0], K.shape[0]
+    D, Dv = K.shape[1], V.shape[1]
+    n, mu, S, M = key_stats(K, V, ak, Ck)
+    m, nu = query_stats(Q, aq, Cq)
+    T = tilted_summaries(S, M, nu, s, dipole)
+    dQ = np.zeros((nq, D))
+    dK = np.zeros((nk, D))
+    dV = np.zeros((nk, Dv))
+    dT = np.zeros((Cq, Ck, Dv))
+    dmu = np.zeros((Ck, D))
+    for I in range(Cq):
+        rows = np.nonzero(aq == I)[0]
+        if len(rows) == 0:
+            continue
+        retrieved = [int(c) for c in R[I]]
+        ek = np.nonzero(np.isin(ak, retrieved))[0]
+        far = np.array([c for c in range(Ck) if n[c] > 0 and c not in retrieved], np.int64)
+        Qr, dOr = Q[rows], dO[rows]
+        # exact items: p_ij = exp(l_ij - lse_i), dl_ij = p_ij (dO_i.v_j - Delta_i)
+        p = np.exp(s * (Qr @ K[ek].T) - lse[rows, None])
+        dl = p * (dOr @ V[ek].T - Delta[rows, None])
+        dQ[rows] += s * (dl @ K[ek])
+        dK[ek] += s * (dl.T @ Qr)
+        dV[ek] += p.T @ dOr
+        # far items: rho_ic = exp(lam_ic - lse_i),
+        # dlam_ic = rho_ic (dO_i.T_Ic - n_c Delta_i), dT_Ic = sum_i rho_ic dO_i
+        rho = np.exp(s * (Qr @ mu[far].T) - lse[rows, None])
+        dlam = rho * (dOr @ T[I, far].T - Delta[rows, None] * n[far][None, :])
+        dT[I, far] += rho.T @ dOr
+        dQ[rows] += s * (dlam @ mu[far])
+        dmu[far] += s * (dlam.T @ Qr)
+    # through T_Ic = S_c + s M_c nu_I
+    dS = dT.sum(axis=0)
+    dM = np.zeros((Ck, Dv, D))
+    dnu = np.zeros((Cq, D))
+    if dipole:
+        dM = s * np.einsum("Icd,Ie->cde", dT, nu)
+        dnu = s * np.einsum("cde,Icd->Ie", M, dT)
+    # through nu_I = mean of its queries
+    for I in range(Cq):
+        rows = np.nonzero(aq == I)[0]
+        if len(rows):
+            dQ[rows] += dnu[I] / len(rows)
+    # through S_c, M_c = sum v (k - mu)^T and mu_c = mean of its keys
+    for c in range(Ck):
+        idx = np.nonzero(ak == c)[0]
+        if len(idx) == 0:
+            continue
+        dV[idx] += dS[c][None, :] + (K[idx] - mu[c]) @ dM[c].T
+        dK[idx] += (V[idx] - S[c] / n[c]) @ dM[c] + dmu[c][None, :] / n[c]
+    return dQ, dK, dV
+
+
+def local_backward(Q, K, V, s, Bblk, lse, Delta, dO):
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    N = Q.shape[0]
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b0 in range(0, N, Bblk):
+        b1 = min(b0 + Bblk, N)
+        logits = s * (Q[b0:b1] @ K[b0:b1].T)
+        mask = np.tril(np.ones((b1 - b0, b1 - b0), bool))
+        p = np.where(mask, np.exp(logits - lse[b0:b1, None]), 0.0)
+        dp = dO[b0:b1] @ V[b0:b1].T
+        dl = p * (dp - Delta[b0:b1, None])
+        dQ[b0:b1] += s * dl @ K[b0:b1]
+        dK[b0:b1] += s * dl.T @ Q[b0:b1]
+        dV[b0:b1] += p.T @ dO[b0:b1]
+    return dQ, dK, dV
+
+
+def backward(Q, K, V, dO, cfg: MuseConfig, O, lse, results, heads=None):
+    """dQ, dK, dV of ``forward`` with labels, retrieval sets and counts
+    fixed to those in ``results`` (as returned by forward).  dK and dV sum
+    over the query heads that share a KV head."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    dO = np.asarray(dO, np.float64)
+    B, Hq, N, D = Q.shape
+    Hkv = K.shape[1]
+    s = cfg.s(D)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b in range(B):
+        for h in range(Hq):
+            if heads is not None and (b, h) not in heads:
+                continue
+            g = (h * Hkv) // Hq
+            Delta = np.einsum("nd,nd->n", dO[b, h], np.asarray(O[b, h], np.float64))
+            plan = causal_plan(N, cfg.block) if cfg.causal else acausal_plan(N)
+            for p, pr in enumerate(plan):
+                r = results[(b, h)][p]
+                q0, qn, k0, kn = pr["q0"], pr["qn"], pr["k0"], pr["kn"]
+                Cq, Ck = min(cfg.cq, qn), min(cfg.ck, kn)
+                a, bb, c = backward_problem(Q[b, h, q0:q0 + qn], K[b, g, k0:k0 + kn],
+                                            V[b, g, k0:k0 + kn], s, r.aq, r.ak, r.R, Cq, Ck,
+                                            lse[b, h, q0:q0 + qn], Delta[q0:q0 + qn],
+                                            dO[b, h, q0:q0 + qn], cfg.dipole)
+                dQ[b, h, q0:q0 + qn] += a
+                dK[b, g, k0:k0 + kn] += bb
+                dV[b, g, k0:k0 + kn] += c
+            if cfg.causal:
+                a, bb, c = local_backward(Q[b, h], K[b, g], V[b, g], s, cfg.block,
+                                          lse[b, h], Delta, dO[b, h])
+                dQ[b, h] += a
+                dK[b, g] += bb
+                dV[b, g] += c
+    return dQ, dK, dV

@@ -1,0 +1,79 @@
+"""Pins for the oracle's Lloyd k-means (clustering of queries and of keys,
+each in its own space: gist.science Technical Summary, Core Mechanisms,
+Bidirectional Semantic Clustering).  The reading "Lloyd, fixed iterations,
+ties to the lowest index, empty clusters keep their centroid" is pinned to
+scipy's independent kmeans2, which implements exactly that loop."""
+import warnings
+
+import numpy as np
+import pytest
+
+from oracle import muse_oracle as mo
+
+
+def _scipy_kmeans(X, init, iters):
+    from scipy.cluster.vq import kmeans2
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        cb, lab = kmeans2(X, X[init].copy(), iter=iters, minit="matrix", missing="warn")
+    return lab, cb
+
+
+@pytest.mark.parametrize("trial", range(40))
+def test_kmeans_matches_scipy(trial):
+    rng = np.random.default_rng(1000 + trial)
+    n = int(rng.integers(20, 300))
+    D = int(rng.integers(1, 9))
+    C = int(rng.integers(1, min(n, 24) + 1))
+    iters = int(rng.integers(1, 12))
+    if trial % 4 == 0:
+        # few distinct values: exact distance ties and empty clusters
+        X = rng.integers(-2, 3, size=(n, D)).astype(np.float64)
+        X[: n // 2] = X[0]
+    else:
+        X = rng.standard_normal((n, D))
+    init = rng.choice(n, C, replace=False)
+    if trial % 4 == 0:
+        # distinct starting indices may still hold equal points: scipy and
+        # the oracle both start from the same coordinates
+        pass
+    lab, mu = mo.kmeans(X, C, iters, init)
+    slab, smu = _scipy_kmeans(X, init, iters)
+    assert np.array_equal(lab, slab)
+    np.testing.assert_allclose(mu, smu, rtol=0, atol=1e-12)
+
+
+def test_kmeans_fixed_point_invariants():
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((500, 6))
+    init = rng.choice(500, 12, replace=False)
+    lab, mu, hist = mo.kmeans(X, 12, 8, init, history=True)
+    prev = X[init]
+    for labels_t, mu_t in hist:
+        d = ((X[:, None, :] - prev[None]) ** 2).sum(-1)
+        assert np.array_equal(labels_t, np.argmin(d, axis=1))
+        for c in range(12):
+            mem = X[labels_t == c]
+            want = mem.mean(0) if len(mem) else prev[c]
+            np.testing.assert_allclose(mu_t[c], want, atol=1e-13)
+        prev = mu_t
+    assert np.array_equal(lab, hist[-1][0])
+
+
+def test_kmeans_recovers_separated_mixture():
+    rng = np.random.default_rng(3)
+    C, D, n = 8, 16, 800
+    centres = rng.standard_normal((C, D)) * 10
+    truth = rng.integers(0, C, n)
+    X = centres[truth] + 0.1 * rng.standard_normal((n, D))
+    init = np.array([np.nonzero(truth == c)[0][0] for c in range(C)])
+    lab, mu = mo.kmeans(X, C, 5, init)
+    assert np.array_equal(lab, truth)
+    for c in range(C):
+        np.testing.assert_allclose(mu[c], X[truth == c].mean(0), atol=1e-12)
+
+
+def test_default_init_is_distinct_and_in_range():
+    for n, C in [(1, 1), (5, 5), (1000, 16), (1024, 128), (17, 16)]:
+        ii = mo.default_init(n, C)
+        assert len(set(ii.tolist())) == C and ii.min() >= 0 and ii.max() < n
