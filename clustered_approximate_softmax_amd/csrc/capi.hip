@@ -1,0 +1,395 @@
+// Host engine behind the C ABI of include/muse.h: argument checks, the
+// problem plan of a call, the state/workspace layout and the launch order
+// on the caller's stream.  Nothing here allocates device memory or
+// synchronises (except muse_timing_collect, which waits for its events).
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/muse.h"
+#include "common.h"
+#include "launch.h"
+
+namespace muse {
+
+hipError_t launch_perm_only(const Plan& pl, const CSet& s0, hipStream_t st);
+
+// Problems whose point count is at most this run all Lloyd iterations in one
+// workgroup; larger ones are split into chunks with one launch per iteration.
+static const int KM_LOCAL_MAX = 2048;
+
+int g_ktime_on = 0;
+namespace {
+struct KtRec {
+  hipEvent_t a, b;
+  const char* name;
+};
+std::vector<hipEvent_t> g_pool;
+std::vector<KtRec> g_pending;
+hipEvent_t g_pre = nullptr;
+struct KtTot {
+  std::string name;
+  double ms;
+  int64_t n;
+};
+std::vector<KtTot> g_tot;
+std::string g_hip_err;
+
+hipEvent_t ev_get() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+void ktime_pre(hipStream_t st) {
+  g_pre = ev_get();
+  if (g_pre) (void)hipEventRecord(g_pre, st);
+}
+void ktime_post(const char* name, hipStream_t st) {
+  hipEvent_t e = ev_get();
+  if (!e || !g_pre) return;
+  (void)hipEventRecord(e, st);
+  g_pending.push_back({g_pre, e, name});
+  g_pre = nullptr;
+}
+
+void set_smem_once(const void* fn, size_t bytes) {
+  static std::unordered_set<const void*> done;
+  if (done.count(fn)) return;
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  done.insert(fn);
+}
+
+// ---------------------------------------------------------------------------
+static int build_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, const muse_cfg* cfg,
+                      Plan& pl) {
+  memset(&pl, 0, sizeof(pl));
+  if (!cfg) return MUSE_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || (D != 64 && D != 128)) return MUSE_EINVAL;
+  if (Hq % Hkv != 0) return MUSE_EINVAL;
+  if (cfg->cq < 1 || cfg->cq > MUSE_MAX_CLUSTERS || cfg->ck != cfg->cq) return MUSE_EINVAL;
+  if (cfg->iters < 1 || cfg->topk < 0) return MUSE_EINVAL;
+  if (cfg->causal != 0 && cfg->causal != 1) return MUSE_EINVAL;
+  if (cfg->causal && cfg->block < 1) return MUSE_EINVAL;
+  if (B * Hq * N * D >= (int64_t)1 << 40 || N >= ((int64_t)1 << 30)) return MUSE_EUNSUPPORTED;
+  pl.B = (int)B; pl.Hq = (int)Hq; pl.Hkv = (int)Hkv; pl.N = (int)N; pl.D = (int)D;
+  pl.C = cfg->cq;
+  pl.iters = cfg->iters;
+  pl.topk = cfg->topk;
+  pl.k1w = std::max(1, std::min(cfg->topk, cfg->cq));
+  pl.dipole = cfg->dipole ? 1 : 0;
+  pl.causal = cfg->causal;
+  pl.blk = cfg->causal ? cfg->block : 0;
+  pl.scale = cfg->scale > 0.f ? cfg->scale : (float)(1.0 / sqrt((double)D));
+  if (!pl.causal) {
+    pl.nlev = 1;
+    pl.lev_m[0] = (int)N;
+    pl.lev_nseg[0] = 1;
+    pl.lev_pfirst[0] = 0;
+    pl.lev_pfirst[1] = 1;
+    pl.P = 1;
+    return MUSE_OK;
+  }
+  const int64_t nb = (N + pl.blk - 1) / pl.blk;
+  int L = 0;
+  while (((int64_t)1 << L) < nb) ++L;
+  if (L > MUSE_MAXLEV) return MUSE_EUNSUPPORTED;
+  pl.nlev = L;
+  int P = 0;
+  for (int l = 0; l < L; ++l) {
+    const int64_t m = (int64_t)pl.blk << l;
+    const int64_t nseg = N > m ? (N - m + 2 * m - 1) / (2 * m) : 0;
+    pl.lev_m[l] = (int)m;
+    pl.lev_nseg[l] = (int)nseg;
+    pl.lev_pfirst[l] = P;
+    P += (int)nseg;
+  }
+  pl.lev_pfirst[L] = P;
+  pl.P = P;
+  return MUSE_OK;
+}
+
+static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  muse_layout L;
+  int plocal;
+  KmLarge lg;
+};
+
+static void build_kmlarge(const Plan& pl, int heads_total, int sub, int& plocal, KmLarge& lg) {
+  memset(&lg, 0, sizeof(lg));
+  plocal = 0;
+  int first_large = pl.nlev;
+  for (int l = 0; l < pl.nlev; ++l) {
+    if (pl.lev_m[l] > KM_LOCAL_MAX) { first_large = l; break; }
+    plocal += pl.lev_nseg[l];
+  }
+  int64_t pts = 0;
+  for (int l = first_large; l < pl.nlev; ++l) pts += (int64_t)heads_total * pl.lev_nseg[l] * pl.lev_m[l];
+  int ch = 2048;
+  while (ch > sub && pts / ch < 1024) ch /= 2;
+  lg.ch = ch;
+  int nl = 0, cf = 0, pf = 0;
+  for (int l = first_large; l < pl.nlev; ++l) {
+    if (pl.lev_nseg[l] == 0) continue;
+    lg.lev[nl] = l;
+    lg.nch[nl] = (pl.lev_m[l] + ch - 1) / ch;
+    lg.cfirst[nl] = cf;
+    lg.pfirst[nl] = pf;
+    cf += heads_total * pl.lev_nseg[l] * lg.nch[nl];
+    pf += heads_total * pl.lev_nseg[l];
+    ++nl;
+  }
+  lg.nl = nl;
+  lg.cfirst[nl] = cf;
+  lg.pfirst[nl] = pf;
+}
+
+static void build_layout(const Plan& pl, int dtype, Layout& out) {
+  muse_layout& L = out.L;
+  memset(&L, 0, sizeof(L));
+  const size_t BHq = (size_t)pl.B * pl.Hq, BHk = (size_t)pl.B * pl.Hkv;
+  const size_t N = pl.N, D = pl.D, C = pl.C, P = pl.P, nl = pl.nlev;
+  L.P = pl.P;
+  L.L = pl.nlev;
+  L.C = pl.C;
+  L.k1w = pl.k1w;
+  L.Cp32 = (pl.C + 31) / 32 * 32;
+  size_t o = 0;
+  L.q_labels = o; o = al(o + nl * BHq * N * 4);
+  L.k_labels = o; o = al(o + nl * BHk * N * 4);
+  L.q_perm = o; o = al(o + nl * BHq * N * 4);
+  L.k_perm = o; o = al(o + nl * BHk * N * 4);
+  L.q_offs = o; o = al(o + BHq * P * (C + 1) * 4);
+  L.k_offs = o; o = al(o + BHk * P * (C + 1) * 4);
+  L.q_cent = o; o = al(o + BHq * P * C * D * 4);
+  L.k_cent = o; o = al(o + BHk * P * C * D * 4);
+  L.mu = o; o = al(o + BHk * P * C * D * 4);
+  L.S = o; o = al(o + BHk * P * C * D * 4);
+  L.M = o; o = al(o + BHk * P * D * C * D * 4);
+  L.R = o; o = al(o + BHq * P * C * pl.k1w * 4);
+  L.state_bytes = std::max<size_t>(o, 256);
+  build_kmlarge(pl, (int)(BHq + BHk), kmeans_sub(dtype, pl.D), out.plocal, out.lg);
+  size_t w = 0;
+  L.ws_T = w; w = al(w + BHq * P * C * D * L.Cp32 * 4);
+  L.ws_oacc = w; w = al(w + (pl.causal ? BHq * N * D * 4 : 0));
+  L.ws_lacc = w; w = al(w + (pl.causal ? BHq * N * 4 : 0));
+  L.ws_part = w; w = al(w + (size_t)out.lg.cfirst[out.lg.nl] * C * D * 4);
+  L.ws_pcnt = w; w = al(w + (size_t)out.lg.cfirst[out.lg.nl] * C * 4);
+  L.ws_bytes = std::max<size_t>(w, 256);
+}
+
+static int hip_fail(hipError_t e) {
+  g_hip_err = hipGetErrorString(e);
+  return MUSE_EHIP;
+}
+
+}  // namespace muse
+
+using namespace muse;
+
+extern "C" {
+
+const char* muse_strerror(int code) {
+  switch (code) {
+    case MUSE_OK: return "success";
+    case MUSE_EINVAL: return "invalid argument (shape, dtype, pointer or parameter)";
+    case MUSE_EWORKSPACE: return "workspace or state buffer too small";
+    case MUSE_EUNSUPPORTED: return "unsupported request";
+    case MUSE_EHIP: return "HIP launch or runtime error";
+    default: return "unknown error";
+  }
+}
+
+const char* muse_last_hip_error(void) { return g_hip_err.c_str(); }
+
+int muse_plan(int64_t N, const muse_cfg* cfg, int32_t* out, int64_t cap, int64_t* count) {
+  if (!count) return MUSE_EINVAL;
+  Plan pl;
+  int rc = build_plan(1, 1, 1, N, 64, cfg, pl);
+  if (rc) return rc;
+  *count = pl.P;
+  for (int p = 0; p < pl.P && p < cap; ++p) {
+    if (!out) return MUSE_EINVAL;
+    Geom g = prob_geom(pl, p);
+    int32_t* r = out + 6 * (size_t)p;
+    r[0] = g.lev;
+    r[1] = p - pl.lev_pfirst[g.lev];
+    r[2] = g.k0; r[3] = g.kn; r[4] = g.q0; r[5] = g.qn;
+  }
+  return MUSE_OK;
+}
+
+int muse_layout_query(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, muse_dtype dtype,
+                      const muse_cfg* cfg, muse_layout* out) {
+  if (!out || (dtype != MUSE_F32 && dtype != MUSE_BF16)) return MUSE_EINVAL;
+  Plan pl;
+  int rc = build_plan(B, Hq, Hkv, N, D, cfg, pl);
+  if (rc) return rc;
+  Layout lay;
+  build_layout(pl, (int)dtype, lay);
+  *out = lay.L;
+  return MUSE_OK;
+}
+
+int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, int64_t B, int64_t Hq,
+                 int64_t Hkv, int64_t N, int64_t D, const muse_cfg* cfg, const int32_t* init_q,
+                 const int32_t* init_k, void* O, float* lse, void* state, size_t state_bytes,
+                 void* ws, size_t ws_bytes, void* stream) {
+  if (!Q || !K || !V || !O || !lse || !state || !ws) return MUSE_EINVAL;
+  if (dtype != MUSE_F32 && dtype != MUSE_BF16) return MUSE_EINVAL;
+  Plan pl;
+  int rc = build_plan(B, Hq, Hkv, N, D, cfg, pl);
+  if (rc) return rc;
+  Layout lay;
+  build_layout(pl, (int)dtype, lay);
+  const muse_layout& L = lay.L;
+  if (state_bytes < L.state_bytes || ws_bytes < L.ws_bytes) return MUSE_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* sb = (char*)state;
+  char* wb = (char*)ws;
+  CSet qs{Q, pl.B * pl.Hq, 1, init_q, (int32_t*)(sb + L.q_labels), (int32_t*)(sb + L.q_perm),
+          (int32_t*)(sb + L.q_offs), (float*)(sb + L.q_cent)};
+  CSet ks{K, pl.B * pl.Hkv, 0, init_k, (int32_t*)(sb + L.k_labels), (int32_t*)(sb + L.k_perm),
+          (int32_t*)(sb + L.k_offs), (float*)(sb + L.k_cent)};
+  AttnBufs ab;
+  memset(&ab, 0, sizeof(ab));
+  ab.Q = Q; ab.K = K; ab.V = V;
+  ab.qs = qs; ab.ks = ks;
+  ab.kst = KStats{(float*)(sb + L.mu), (float*)(sb + L.S), (float*)(sb + L.M)};
+  ab.R = (int32_t*)(sb + L.R);
+  ab.T = (float*)(wb + L.ws_T);
+  ab.Cp32 = (int32_t)L.Cp32;
+  ab.oacc = (float*)(wb + L.ws_oacc);
+  ab.lacc = (float*)(wb + L.ws_lacc);
+  ab.O = O;
+  ab.lse = lse;
+  hipError_t e = hipGetLastError();  // clear stale errors from earlier calls
+  (void)e;
+  if (pl.P > 0) {
+    if ((e = launch_kmeans(pl, (int)dtype, qs, ks, lay.plocal, lay.lg, (float*)(wb + L.ws_part),
+                           (int32_t*)(wb + L.ws_pcnt), st)) != hipSuccess)
+      return hip_fail(e);
+    if ((e = launch_summarize(pl, (int)dtype, ks, V, ab.kst, st)) != hipSuccess) return hip_fail(e);
+    if ((e = launch_score_topk(pl, ab, st)) != hipSuccess) return hip_fail(e);
+    if ((e = launch_tilt(pl, (int)dtype, ab, st)) != hipSuccess) return hip_fail(e);
+  }
+  if ((e = launch_attn(pl, (int)dtype, ab, st)) != hipSuccess) return hip_fail(e);
+  return MUSE_OK;
+}
+
+size_t muse_cluster_ws_size(int64_t G, int64_t n, int64_t D, muse_dtype dtype, int32_t C) {
+  muse_cfg cfg{C, C, 1, 0, 0, 0, 1, 0, 0.f};
+  Plan pl;
+  if (build_plan(1, G, G, n, D, &cfg, pl)) return 0;
+  int plocal;
+  KmLarge lg;
+  build_kmlarge(pl, (int)G, kmeans_sub((int)dtype, (int)D), plocal, lg);
+  return al((size_t)lg.cfirst[lg.nl] * C * D * 4) + al((size_t)lg.cfirst[lg.nl] * C * 4) + 256;
+}
+
+int musecluster(const void* X, muse_dtype dtype, int64_t G, int64_t n, int64_t D, int32_t C,
+                int32_t iters, const int32_t* init_idx, int32_t* assign, float* centroids,
+                int32_t* perm, int32_t* offs, void* ws, size_t ws_bytes, void* stream) {
+  if (!X || !assign || !centroids || !perm || !offs) return MUSE_EINVAL;
+  if (dtype != MUSE_F32 && dtype != MUSE_BF16) return MUSE_EINVAL;
+  muse_cfg cfg{C, C, iters, 0, 0, 0, 1, 0, 0.f};
+  Plan pl;
+  int rc = build_plan(1, G, G, n, D, &cfg, pl);
+  if (rc) return rc;
+  int plocal;
+  KmLarge lg;
+  build_kmlarge(pl, (int)G, kmeans_sub((int)dtype, (int)D), plocal, lg);
+  const size_t need = muse_cluster_ws_size(G, n, D, dtype, C);
+  if (lg.nl > 0 && (!ws || ws_bytes < need)) return MUSE_EWORKSPACE;
+  CSet s0{X, (int)G, 1, init_idx, assign, perm, offs, centroids};
+  CSet s1{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
+  float* part = (float*)ws;
+  int32_t* pcnt = ws ? (int32_t*)((char*)ws + al((size_t)lg.cfirst[lg.nl] * C * D * 4)) : nullptr;
+  (void)hipGetLastError();
+  hipError_t e = launch_kmeans(pl, (int)dtype, s0, s1, plocal, lg, part, pcnt, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MUSE_OK;
+}
+
+int musesummarize(const void* K, const void* V, muse_dtype dtype, int64_t G, int64_t n, int64_t D,
+                  int32_t C, const int32_t* assign, int32_t* perm, int32_t* offs, float* mu,
+                  float* S, float* M, void* stream) {
+  if (!K || !V || !assign || !perm || !offs || !mu || !S || !M) return MUSE_EINVAL;
+  if (dtype != MUSE_F32 && dtype != MUSE_BF16) return MUSE_EINVAL;
+  muse_cfg cfg{C, C, 1, 0, 0, 0, 1, 0, 0.f};
+  Plan pl;
+  int rc = build_plan(1, G, G, n, D, &cfg, pl);
+  if (rc) return rc;
+  CSet ks{K, (int)G, 0, nullptr, const_cast<int32_t*>(assign), perm, offs, nullptr};
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipError_t e = launch_perm_only(pl, ks, st);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_summarize(pl, (int)dtype, ks, V, KStats{mu, S, M}, st);
+  if (e != hipSuccess) return hip_fail(e);
+  return MUSE_OK;
+}
+
+size_t muse_bwd_ws_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, muse_dtype dtype,
+                        const muse_cfg* cfg) {
+  (void)B; (void)Hq; (void)Hkv; (void)N; (void)D; (void)dtype; (void)cfg;
+  return 256;
+}
+
+int museattn_bwd(const void* Q, const void* K, const void* V, const void* O, const float* lse,
+                 const void* dO, muse_dtype dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                 int64_t D, const muse_cfg* cfg, const void* state, size_t state_bytes, void* dQ,
+                 void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
+  (void)Q; (void)K; (void)V; (void)O; (void)lse; (void)dO; (void)dtype; (void)B; (void)Hq;
+  (void)Hkv; (void)N; (void)D; (void)cfg; (void)state; (void)state_bytes; (void)dQ; (void)dK;
+  (void)dV; (void)ws; (void)ws_bytes; (void)stream;
+  return MUSE_EUNSUPPORTED;
+}
+
+int muse_timing_enable(int on) {
+  g_ktime_on = on ? 1 : 0;
+  return MUSE_OK;
+}
+
+int muse_timing_collect(void) {
+  for (auto& r : g_pending) {
+    (void)hipEventSynchronize(r.b);
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, r.a, r.b);
+    auto it = std::find_if(g_tot.begin(), g_tot.end(), [&](const KtTot& t) { return t.name == r.name; });
+    if (it == g_tot.end()) g_tot.push_back({r.name, (double)ms, 1});
+    else { it->ms += ms; it->n += 1; }
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_pending.clear();
+  return MUSE_OK;
+}
+
+int muse_timing_reset(void) {
+  muse_timing_collect();
+  g_tot.clear();
+  return MUSE_OK;
+}
+
+int muse_timing_get(int i, const char** name, double* total_ms, int64_t* launches) {
+  if (i < 0 || i >= (int)g_tot.size()) return MUSE_EINVAL;
+  if (name) *name = g_tot[i].name.c_str();
+  if (total_ms) *total_ms = g_tot[i].ms;
+  if (launches) *launches = g_tot[i].n;
+  return MUSE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal launch interface between the host engine and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <type_traits>
+
+#include "common.h"
+
+namespace muse {
+
+// Large k-means problems: the levels whose span exceeds the in-workgroup
+// limit, each split into chunks of `ch` points (one workgroup per chunk).
+struct KmLarge {
+  int32_t nl;                       // number of large levels
+  int32_t ch;                       // points per chunk
+  int32_t lev[MUSE_MAXLEV];         // plan level of each entry
+  int32_t nch[MUSE_MAXLEV];         // chunks per problem
+  int32_t cfirst[MUSE_MAXLEV + 1];  // first chunk of each entry (both sets)
+  int32_t pfirst[MUSE_MAXLEV + 1];  // first problem of each entry (both sets)
+};
+
+// Per-kernel timing with HIP events on the launch stream (off by default).
+extern int g_ktime_on;
+void ktime_pre(hipStream_t st);
+void ktime_post(const char* name, hipStream_t st);
+void set_smem_once(const void* fn, size_t bytes);
+
+hipError_t launch_kmeans(const Plan& pl, int dtype, const CSet& s0, const CSet& s1, int plocal,
+                         const KmLarge& lg, float* part, int32_t* pcnt, hipStream_t st);
+size_t kmeans_smem_bytes(int dtype, int D, int C);
+int kmeans_sub(int dtype, int D);
+
+// Key-cluster statistics n, mu, S, M of every key problem of `ks`.
+struct KStats {
+  float* mu;    // [heads][P][C][D]
+  float* S;     // [heads][P][C][D]
+  float* M;     // [heads][P][D][C][D]  (value dim, cluster, key dim)
+};
+hipError_t launch_summarize(const Plan& pl, int dtype, const CSet& ks, const void* V, KStats st_,
+                            hipStream_t st);
+
+// Scores + top-k retrieval, and tilted summaries.
+struct AttnBufs {
+  const void* Q; const void* K; const void* V;
+  CSet qs, ks;            // query / key clustering (labels, perm, offs, cent)
+  KStats kst;
+  int32_t* R;             // [B*Hq][P][C][k1w]
+  float* T;               // [B*Hq][P][C][D][Cp32] tilted summaries (I, d, c)
+  int32_t Cp32;           // C rounded up to 32
+  float* oacc;            // causal running output [B*Hq][N][D] (fp32)
+  float* lacc;            // causal running lse [B*Hq][N]
+  void* O; float* lse;    // outputs
+};
+hipError_t launch_score_topk(const Plan& pl, const AttnBufs& b, hipStream_t st);
+hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
+hipError_t launch_attn(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
+
+}  // namespace muse
+
+#define MUSE_KT_PRE(st) \
+  do { if (muse::g_ktime_on) muse::ktime_pre(st); } while (0)
+#define MUSE_KT_POST(name, st) \
+  do { if (muse::g_ktime_on) muse::ktime_post(name, st); } while (0)

@@ -1,0 +1,221 @@
+/*
+ * muse.h - C ABI of the MuSe (Multipole Semantic Attention) library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * MuSe approximates softmax attention (arXiv 2509.10406, "Multipole Semantic
+ * Attention: A Fast Approximation of Softmax Attention for Pretraining").
+ * Passages are cited by page and section:
+ *   [GIST]  gist.science page, Technical Summary, Core Mechanisms
+ *   [NEWX]  newx.sg page, Abstract
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are row-major.  Attention inputs use the layout [B, H, N, D]:
+ *   Q has Hq heads, K and V have Hkv heads, Hq % Hkv == 0, and query head h
+ *   reads KV head floor(h * Hkv / Hq) (grouped-query attention).  The value
+ *   dimension equals D.  D must be 64 or 128.
+ * - dtype: MUSE_BF16 (bfloat16 storage, fp32 accumulation) or MUSE_F32.
+ *   Outputs O, dQ, dK, dV use the input dtype; lse and all statistics are fp32.
+ * - Every pointer argument that names a tensor is a DEVICE pointer on the
+ *   current HIP device, except where a function says "host".  The caller
+ *   allocates and owns all memory (inputs, outputs, state, workspace); the
+ *   library never allocates, frees or synchronises.  Work is queued on
+ *   `stream` (a hipStream_t; NULL is the default stream) and is asynchronous.
+ * - Return value: MUSE_OK (0) or a negative error code.  All argument
+ *   checks happen on the host before the first launch, so an error return
+ *   means nothing was queued, except MUSE_EHIP (a launch failed; the HIP
+ *   error string is available from muse_last_hip_error()).
+ * - Clamping (documented, not errors): a problem with n < C points uses
+ *   C_eff = n clusters; k1 is clamped to the number of non-empty key
+ *   clusters of each problem.
+ */
+#ifndef MUSE_H
+#define MUSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MUSE_F32 = 0, MUSE_BF16 = 1 } muse_dtype;
+
+enum {
+  MUSE_OK = 0,
+  MUSE_EINVAL = -1,       /* bad shape, dtype, null pointer or parameter */
+  MUSE_EWORKSPACE = -2,   /* workspace or state buffer too small */
+  MUSE_EUNSUPPORTED = -3, /* valid request this build does not handle */
+  MUSE_EHIP = -4          /* a HIP launch or runtime call failed */
+};
+
+#define MUSE_MAX_CLUSTERS 256
+
+/*
+ * Hyperparameters.  The pages state that MuSe needs only hyperparameters
+ * and no architectural change [NEWX]: the cluster counts, the number of
+ * retrieved clusters k1 ([GIST] Retrieval-Augmented Approximation), the
+ * causal flag and the local block size of the causal hierarchy [NEWX].
+ *   cq, ck   clusters per query / key problem, 1..256.  This build uses one
+ *            count for both sides and requires cq == ck.
+ *   iters    Lloyd iterations, >= 1.
+ *   topk     k1, clusters per query cluster attended exactly, >= 0.
+ *   block    causal local block size (>= 1); ignored when causal == 0.
+ *   causal   0: acausal; 1: causal hierarchy (exact local blocks of size
+ *            `block`, approximated off-diagonal blocks on ceil(log2(
+ *            ceil(N/block))) dyadic levels).
+ *   dipole   1: monopole + dipole summaries; 0: monopole only.
+ *   scale    softmax scale s applied to q.k; <= 0 means 1/sqrt(D).
+ */
+typedef struct {
+  int32_t cq, ck, iters, topk, block, causal, dipole, reserved;
+  float scale;
+} muse_cfg;
+
+/*
+ * Byte offsets of the arrays held in the `state` buffer that museattn_fwd
+ * fills and museattn_bwd reads (the fixed assignments of the backward).
+ * P = problems per head (1 when acausal), L = levels (1 when acausal),
+ * C = cq, k1w = max(1, min(topk, C)).
+ *   q_labels  int32 [L][B*Hq][N]      query cluster of each row per level
+ *   k_labels  int32 [L][B*Hkv][N]
+ *   q_perm    int32 [L][B*Hq][N]      per problem, sorted position -> row
+ *   k_perm    int32 [L][B*Hkv][N]     (positions relative to the problem's
+ *                                      first row, row ids absolute)
+ *   q_offs    int32 [B*Hq][P][C+1]    cluster segment starts in q_perm
+ *   k_offs    int32 [B*Hkv][P][C+1]
+ *   q_cent    fp32  [B*Hq][P][C][D]   query-cluster centroids nu
+ *   k_cent    fp32  [B*Hkv][P][C][D]  key k-means centroids
+ *   mu        fp32  [B*Hkv][P][C][D]  key-cluster centroids mu
+ *   S         fp32  [B*Hkv][P][C][D]  value sums
+ *   M         fp32  [B*Hkv][P][D][C][D] dipoles, index (value dim, c, key dim)
+ *   R         int32 [B*Hq][P][C][k1w] retrieved clusters, ascending, -1 pad
+ * Problem p of a head: level l and segment t in level-major order (see
+ * muse_plan).  Counts are k_offs[c+1] - k_offs[c].
+ */
+typedef struct {
+  int64_t P, L, C, k1w, Cp32;
+  size_t q_labels, k_labels, q_perm, k_perm, q_offs, k_offs, q_cent, k_cent, mu, S, M, R;
+  size_t state_bytes;
+  /* workspace arrays (scratch; valid after museattn_fwd until the next call) */
+  size_t ws_T;      /* fp32 [B*Hq][P][C][D][Cp32] tilted summaries (I, d, c) */
+  size_t ws_oacc;   /* fp32 [B*Hq][N][D] causal running output */
+  size_t ws_lacc;   /* fp32 [B*Hq][N] causal running lse */
+  size_t ws_part;   /* k-means chunk partial sums */
+  size_t ws_pcnt;
+  size_t ws_bytes;
+} muse_layout;
+
+/*
+ * Problem list of a call (host-only; no GPU needed).  Writes up to `cap`
+ * rows of 6 int32 (level, t, k0, kn, q0, qn) to `out` (host memory) and the
+ * number of problems per head to *count.  Acausal: one problem with keys
+ * and queries = all N rows.  Causal: level l has span m = block * 2^l;
+ * segment t has keys rows [2mt, 2mt + m) and queries rows
+ * [2mt + m, min(2mt + 2m, N)), for every t with 2mt + m < N ([NEWX]
+ * hierarchical block decomposition).
+ */
+int muse_plan(int64_t N, const muse_cfg* cfg, int32_t* out, int64_t cap, int64_t* count);
+
+/*
+ * Sizes and array offsets for a call with these shapes (host-only).
+ * Returns MUSE_EINVAL for unsupported shapes or parameters.
+ */
+int muse_layout_query(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, muse_dtype dtype,
+                      const muse_cfg* cfg, muse_layout* out);
+
+/*
+ * musecluster - Lloyd k-means of G independent point sets ([GIST]
+ * Bidirectional Semantic Clustering: queries and keys are clustered
+ * separately, each set in its own space).
+ *   X          [G, n, D] points (dtype)
+ *   C          clusters per set, 1..256 (clamped to n)
+ *   iters      Lloyd iterations >= 1
+ *   init_idx   int32 [G, C] starting point indices in [0, n), distinct per
+ *              set (out-of-range values are clamped), or NULL for
+ *              floor(c n / C_eff)
+ *   assign     int32 [G, n] out: cluster of each point after the last
+ *              assignment step (ties: lowest index)
+ *   centroids  fp32 [G, C, D] out: mean of each cluster's members after the
+ *              last update (empty clusters keep their previous centroid;
+ *              rows >= C_eff are zero)
+ *   perm       int32 [G, n] out: points in cluster-contiguous, stable order
+ *   offs       int32 [G, C+1] out: segment starts in perm
+ *   ws         workspace of at least muse_cluster_ws_size() bytes
+ */
+size_t muse_cluster_ws_size(int64_t G, int64_t n, int64_t D, muse_dtype dtype, int32_t C);
+int musecluster(const void* X, muse_dtype dtype, int64_t G, int64_t n, int64_t D, int32_t C,
+                int32_t iters, const int32_t* init_idx, int32_t* assign, float* centroids,
+                int32_t* perm, int32_t* offs, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * musesummarize - monopole and dipole statistics of given key clusters
+ * ([NEWX]: centroid approximation plus dipole correction).
+ *   K, V      [G, n, D] keys and values (dtype)
+ *   assign    int32 [G, n] cluster of each key, in [0, min(C, n))
+ *   perm      int32 [G, n] out: stable cluster-contiguous order
+ *   offs      int32 [G, C+1] out: segment starts; n_c = offs[c+1] - offs[c]
+ *   mu        fp32 [G, C, D] out: mu_c = mean of the keys of c (0 if empty)
+ *   S         fp32 [G, C, D] out: S_c = sum of the values of c
+ *   M         fp32 [G, D, C, D] out: M[g][d][c][e] = sum_j v_jd (k_je - mu_ce)
+ */
+int musesummarize(const void* K, const void* V, muse_dtype dtype, int64_t G, int64_t n, int64_t D,
+                  int32_t C, const int32_t* assign, int32_t* perm, int32_t* offs, float* mu,
+                  float* S, float* M, void* stream);
+
+/*
+ * museattn_fwd - MuSe attention forward ([GIST] Decomposition, Hierarchical
+ * Two-Stage Attention, Exponential Tilting, Retrieval-Augmented
+ * Approximation; [NEWX] monopole + dipole, causal hierarchy).
+ *   Q [B,Hq,N,D], K, V [B,Hkv,N,D]  inputs (dtype)
+ *   init_q     int32 [B*Hq][P][C] starting indices of the query k-means of
+ *              every problem (relative to the problem's first query row) or
+ *              NULL for floor(c n / C_eff)
+ *   init_k     int32 [B*Hkv][P][C] same for keys, or NULL
+ *   O          [B,Hq,N,D] out (dtype)
+ *   lse        fp32 [B,Hq,N] out: log of each row's softmax normaliser
+ *   state      out: assignments and statistics (muse_layout), state_bytes
+ *   ws         scratch, ws_bytes >= muse_layout.ws_bytes
+ */
+int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, int64_t B, int64_t Hq,
+                 int64_t Hkv, int64_t N, int64_t D, const muse_cfg* cfg, const int32_t* init_q,
+                 const int32_t* init_k, void* O, float* lse, void* state, size_t state_bytes,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * museattn_bwd - gradients of museattn_fwd with the cluster assignments,
+ * retrieval sets and counts held fixed (those saved in `state` by the
+ * forward on the same Q, K, V); differentiates through the centroids, value
+ * sums, dipoles and tilted summaries.
+ *   O, lse     forward outputs; dO [B,Hq,N,D] upstream gradient (dtype)
+ *   dQ [B,Hq,N,D], dK, dV [B,Hkv,N,D] out (dtype); dK and dV sum over the
+ *              query heads sharing a KV head.
+ *   ws         scratch, ws_bytes >= muse_bwd_ws_size()
+ */
+size_t muse_bwd_ws_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, muse_dtype dtype,
+                        const muse_cfg* cfg);
+int museattn_bwd(const void* Q, const void* K, const void* V, const void* O, const float* lse,
+                 const void* dO, muse_dtype dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                 int64_t D, const muse_cfg* cfg, const void* state, size_t state_bytes, void* dQ,
+                 void* dK, void* dV, void* ws, size_t ws_bytes, void* stream);
+
+/* Error text for a return code; HIP error text of the last MUSE_EHIP. */
+const char* muse_strerror(int code);
+const char* muse_last_hip_error(void);
+
+/*
+ * Per-kernel timing with HIP events recorded on the launch stream around
+ * every kernel the library queues.  muse_timing_enable(1) starts recording,
+ * muse_timing_collect() waits for the recorded events and adds their
+ * durations to per-kernel totals, muse_timing_get() reads total ms and
+ * launch count of entry `i` (returns MUSE_EINVAL past the last entry).
+ */
+int muse_timing_enable(int on);
+int muse_timing_collect(void);
+int muse_timing_reset(void);
+int muse_timing_get(int i, const char** name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MUSE_H */

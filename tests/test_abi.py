@@ -1,0 +1,99 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and
+exports every function include/muse.h declares, the problem plan equals the
+oracle's causal hierarchy, and argument validation returns error codes
+before anything is queued."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from clustered_approximate_softmax_amd import muse as M
+from oracle import muse_oracle as mo
+
+
+def test_library_exports_every_declared_function():
+    L = M.lib()
+    names = M.header_functions()
+    assert {"musecluster", "musesummarize", "museattn_fwd", "museattn_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror():
+    L = M.lib()
+    for code in (0, -1, -2, -3, -4, 7):
+        assert len(L.muse_strerror(code)) > 3
+
+
+@pytest.mark.parametrize("N,B", [(64, 8), (65, 8), (100, 16), (1024, 64), (16384, 512), (65536, 1024),
+                                 (30, 64), (1000, 16)])
+def test_plan_matches_oracle_hierarchy(N, B):
+    got = M.plan(N, M.make_cfg(8, causal=True, block=B))
+    want = mo.causal_plan(N, B)
+    assert len(got) == len(want)
+    for g, w in zip(got, want):
+        assert tuple(g) == (w["level"], w["t"], w["k0"], w["kn"], w["q0"], w["qn"])
+
+
+def test_acausal_plan_is_one_problem():
+    got = M.plan(777, M.make_cfg(8))
+    assert got.tolist() == [[0, 0, 0, 777, 0, 777]]
+
+
+def test_layout_sizes():
+    cfg = M.make_cfg(64, 10, 4)
+    lay = M.layout(1, 8, 8, 8192, 64, M.MUSE_BF16, cfg)
+    assert lay["P"] == 1 and lay["L"] == 1 and lay["k1w"] == 4 and lay["Cp32"] == 64
+    assert lay["M"] + 8 * 64 * 64 * 64 * 4 <= lay["R"]
+    assert lay["state_bytes"] >= lay["R"] + 8 * 64 * 4 * 4
+    assert lay["ws_bytes"] >= 8 * 64 * 64 * 64 * 4
+    c4 = M.layout(1, 32, 8, 65536, 64, M.MUSE_BF16, M.make_cfg(128, 10, 8, True, 1024))
+    assert c4["P"] == 63 and c4["L"] == 6
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _fwd(cfg, B=1, Hq=2, Hkv=2, N=256, D=64, dtype=M.MUSE_BF16, ws=1 << 40, st=1 << 40, ptr=FAKE):
+    return M.lib().museattn_fwd(ptr, ptr, ptr, dtype, B, Hq, Hkv, N, D, ctypes.byref(cfg), None, None, ptr,
+                                ptr, ptr, st, ptr, ws, None)
+
+
+@pytest.mark.parametrize("kw,cfgkw", [
+    (dict(D=32), {}), (dict(D=96), {}), (dict(Hq=3, Hkv=2), {}), (dict(N=0), {}), (dict(B=0), {}),
+    (dict(dtype=7), {}), ({}, dict(C=0)), ({}, dict(C=257)), ({}, dict(iters=0)),
+    ({}, dict(topk=-1)), ({}, dict(causal=True, block=0)),
+])
+def test_fwd_rejects_bad_arguments(kw, cfgkw):
+    c = dict(C=16, iters=3, topk=1, causal=False, block=0)
+    c.update(cfgkw)
+    assert _fwd(M.make_cfg(**c), **kw) == -1
+
+
+def test_fwd_rejects_unequal_cluster_counts_and_nulls():
+    cfg = M.make_cfg(16, 3, 1)
+    cfg.ck = 8
+    assert _fwd(cfg) == -1
+    assert _fwd(M.make_cfg(16, 3, 1), ptr=None) == -1
+
+
+def test_fwd_rejects_small_buffers():
+    cfg = M.make_cfg(16, 3, 1)
+    assert _fwd(cfg, ws=16) == -2
+    assert _fwd(cfg, st=16) == -2
+
+
+def test_cluster_and_summarize_reject_bad_arguments():
+    L = M.lib()
+    assert L.musecluster(FAKE, 1, 2, 100, 48, 8, 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.musecluster(FAKE, 1, 2, 100, 64, 300, 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.musecluster(None, 1, 2, 100, 64, 8, 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    # a large problem needs workspace for its chunk partials
+    assert L.muse_cluster_ws_size(2, 100000, 64, 1, 64) > 0
+    assert L.musecluster(FAKE, 1, 2, 100000, 64, 64, 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None) == -2
+    assert L.musesummarize(FAKE, FAKE, 1, 2, 100, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+
+
+def test_backward_reports_unsupported_until_built():
+    # fixed-assignment backward entry point exists in the ABI
+    assert hasattr(M.lib(), "museattn_bwd")

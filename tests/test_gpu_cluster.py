@@ -1,0 +1,104 @@
+"""GPU parity of the clustering and summary entry points (musecluster,
+musesummarize) against the oracle.
+
+k-means is checked in lockstep: the GPU run with t iterations is compared
+with one oracle Lloyd step taken from the GPU's centroids after t-1
+iterations, so a flip at a distance tie cannot cascade.  Labels must equal
+the fp64 nearest centroid except at relative distance ties (1e-5);
+centroids must equal the fp64 mean of the GPU's members; the permutation
+and segment offsets are integers and must be bit-exact."""
+import numpy as np
+import pytest
+
+from clustered_approximate_softmax_amd import muse as M
+from oracle import muse_oracle as mo
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _points(G, n, D, dtype, comps, seed):
+    r = np.random.default_rng(seed)
+    centres = r.standard_normal((G, comps, D)) / np.sqrt(8)
+    lab = r.integers(0, comps, (G, n))
+    X = np.take_along_axis(centres, lab[..., None], 1) + 0.3 * r.standard_normal((G, n, D))
+    return gu.synth.to_dtype(X, dtype)
+
+
+CASES = [
+    # G, n, D, C, dtype, iters  (n <= 2048: in-workgroup path; larger: chunked path)
+    (2, 1024, 64, 16, "f32", 4),
+    (2, 1000, 64, 40, "bf16", 4),
+    (3, 777, 128, 64, "bf16", 3),
+    (2, 5000, 64, 64, "bf16", 3),
+    (1, 9000, 128, 128, "bf16", 2),
+    (2, 3000, 64, 32, "f32", 2),
+    (2, 10, 64, 16, "bf16", 3),     # fewer points than clusters: C_eff = n
+    (1, 600, 64, 256, "bf16", 2),   # maximum cluster count
+]
+
+
+@pytest.mark.parametrize("G,n,D,C,dtype,iters", CASES)
+def test_kmeans_lockstep(G, n, D, C, dtype, iters):
+    import torch
+    X = _points(G, n, D, dtype, comps=max(4, C // 2), seed=G * n + C)
+    Xd = gu.to_dev(X, dtype)
+    rng = np.random.default_rng(5)
+    Ce = min(C, n)
+    init = np.full((G, C), -1, np.int32)
+    for g in range(G):
+        init[g, :Ce] = rng.choice(n, Ce, replace=False)
+    initd = torch.from_numpy(init).cuda()
+    prev = np.stack([X[g][init[g, :Ce]].astype(np.float64) for g in range(G)])
+    for t in range(1, iters + 1):
+        a, cent, perm, offs = M.musecluster(Xd, C, t, initd)
+        torch.cuda.synchronize()
+        a, cent, perm, offs = (x.cpu().numpy() for x in (a, cent, perm, offs))
+        for g in range(G):
+            assert a[g].min() >= 0 and a[g].max() < Ce
+            gu.check_labels(X[g], prev[g], a[g])
+            want = mo.update_step(X[g], a[g], prev[g])
+            scale = np.abs(X[g]).max()
+            np.testing.assert_allclose(cent[g, :Ce], want, rtol=0, atol=2e-6 * scale)
+            assert np.all(cent[g, Ce:] == 0)
+            order = np.argsort(a[g], kind="stable")
+            assert np.array_equal(perm[g], order)
+            cnt = np.bincount(a[g], minlength=C)
+            assert np.array_equal(offs[g], np.concatenate([[0], np.cumsum(cnt)]))
+        prev = cent[:, :Ce].astype(np.float64)
+
+
+def test_kmeans_default_init_and_determinism():
+    import torch
+    X = _points(2, 4096, 64, "bf16", 32, 9)
+    Xd = gu.to_dev(X, "bf16")
+    r1 = [x.cpu() for x in M.musecluster(Xd, 32, 5)]
+    r2 = [x.cpu() for x in M.musecluster(Xd, 32, 5)]
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
+    # default init = floor(c n / C): one oracle run from the same start agrees
+    lab, mu = mo.kmeans(X[0], 32, 1, mo.default_init(4096, 32))
+    a1 = M.musecluster(Xd, 32, 1)[0].cpu().numpy()
+    gu.check_labels(X[0], X[0][mo.default_init(4096, 32)], a1[0])
+
+
+@pytest.mark.parametrize("G,n,D,C,dtype", [(2, 700, 64, 16, "f32"), (2, 3000, 64, 64, "bf16"),
+                                           (1, 500, 128, 100, "bf16"), (1, 64, 64, 32, "f32")])
+def test_summarize_matches_oracle(G, n, D, C, dtype):
+    import torch
+    r = np.random.default_rng(n)
+    K = gu.synth.to_dtype(r.standard_normal((G, n, D)), dtype)
+    V = gu.synth.to_dtype(r.standard_normal((G, n, D)), dtype)
+    a = r.integers(0, min(C, n) // 2 + 1, (G, n)).astype(np.int32) * 2   # every other cluster empty
+    a = np.minimum(a, min(C, n) - 1)
+    perm, offs, mu, S, Mm = M.musesummarize(gu.to_dev(K, dtype), gu.to_dev(V, dtype),
+                                             torch.from_numpy(a).cuda(), C)
+    torch.cuda.synchronize()
+    perm, offs, mu, S, Mm = (x.cpu().numpy() for x in (perm, offs, mu, S, Mm))
+    for g in range(G):
+        n_, mu_, S_, M_ = mo.key_stats(K[g], V[g], a[g], C)
+        assert np.array_equal(perm[g], np.argsort(a[g], kind="stable"))
+        assert np.array_equal(offs[g], np.concatenate([[0], np.cumsum(n_)]))
+        np.testing.assert_allclose(mu[g], mu_, atol=2e-6)
+        np.testing.assert_allclose(S[g], S_, atol=2e-5 * max(1, np.sqrt(n / C)))
+        np.testing.assert_allclose(np.transpose(Mm[g], (1, 0, 2)), M_, atol=5e-5 * max(1, np.sqrt(n / C)))
