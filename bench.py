@@ -1,0 +1,262 @@
+"""Benchmark of the MuSe forward on one MI355X.
+
+A step is one museattn_fwd call over the whole workload tensor (all batch x
+heads, clustering included; input generation excluded), inputs resident in
+HBM.  Default workload: acausal bf16, batch 1, 8 heads, N=8192, D=64, 64
+query and 64 key clusters, 10 Lloyd iterations, top-4 retrieval.
+
+Prints one JSON line: ms per layer, effective TFLOP/s (exact-attention
+FLOPs / time), the roofline of the dominant kernel (algorithmic work per
+launch / mean launch time from HIP events on the launch stream), exact
+attention timed on the same GPU, the approximation error, and the fp64
+oracle timed on a bounded sample on the host cores.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MuSe attn ms/layer + effective TFLOP/s (% of MFMA peak) at N=8k..64k, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-exact", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run a plain copy of this many MiB (for PMC byte-counter scaling)")
+    return ap.parse_args()
+
+
+def exact_flops(w):
+    if w.causal:
+        return 4.0 * w.B * w.Hq * w.D * w.N * (w.N + 1) / 2
+    return 4.0 * w.B * w.Hq * w.N * w.N * w.D
+
+
+def kernel_models(w, M, st, rows):
+    """Algorithmic work per call for each kernel name: (flops, bytes, bound)."""
+    C, D, T = w.C, w.D, w.iters
+    eb = 2 if w.dtype == "bf16" else 4
+    qoffs = st.field("q_offs").cpu().numpy()
+    koffs = st.field("k_offs").cpu().numpy()
+    R = st.field("R").cpu().numpy()
+    BHq, BHk = w.B * w.Hq, w.B * w.Hkv
+    sizes = [(r[3], r[5]) for r in rows]     # (kn, qn)
+    pts_q = sum(qn for _, qn in sizes) * BHq
+    pts_k = sum(kn for kn, _ in sizes) * BHk
+    km = {}
+    # Lloyd distances: 2 n C D per point per iteration (Q and K sets)
+    large_q = sum(qn for kn, qn in sizes if qn > 2048) * BHq
+    large_k = sum(kn for kn, qn in sizes if kn > 2048) * BHk
+    small = (pts_q - large_q) + (pts_k - large_k)
+    large = large_q + large_k
+    km["km_local"] = (2.0 * small * C * D * T, small * D * eb * T, "mfma")
+    km["km_assign"] = (2.0 * large * C * D * T, large * D * eb * T, "mfma")
+    ret = 0.0
+    far = 0.0
+    for bh in range(BHq):
+        g = (bh % w.Hq) * w.Hkv // w.Hq + (bh // w.Hq) * w.Hkv
+        for p, (kn, qn) in enumerate(sizes):
+            cnt = np.diff(koffs[g, p])
+            m = np.diff(qoffs[bh, p])
+            nz = int((cnt > 0).sum())
+            for I in np.nonzero(m > 0)[0]:
+                sel = [c for c in R[bh, p, I] if c >= 0]
+                ret += m[I] * sum(int(cnt[c]) for c in sel)
+                far += m[I] * (nz - len(sel))
+    attn_flops = 2.0 * (ret + far) * (D + D)
+    attn_bytes = (pts_q * D * eb * 2) + ret / max(1, pts_q) * 0  # Q in, O out
+    name = "attn_level" if w.causal else "attn_far_retrieve"
+    km[name] = (attn_flops, attn_bytes, "mfma")
+    km["summarize"] = (2.0 * pts_k * D * D, pts_k * 2 * D * eb, "hbm")
+    Pn = len(rows)
+    km["tilt"] = (2.0 * BHq * Pn * C * C * D * D, BHq * Pn * C * C * D * 4, "hbm")
+    if w.causal:
+        km["attn_local"] = (2.0 * BHq * w.N * (w.block + 1) / 2 * 2 * D, BHq * w.N * D * eb * 2, "mfma")
+    return km
+
+
+def time_calls(fn, steps, torch):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def exact_attention_ms(Q, K, V, w, steps, torch):
+    import torch.nn.functional as F
+    Hq, Hkv = w.Hq, w.Hkv
+    Kx = K.repeat_interleave(Hq // Hkv, dim=1) if Hq != Hkv else K
+    Vx = V.repeat_interleave(Hq // Hkv, dim=1) if Hq != Hkv else V
+
+    def f():
+        F.scaled_dot_product_attention(Q, Kx, Vx, is_causal=w.causal)
+    for _ in range(2):
+        f()
+    return time_calls(f, steps, torch)
+
+
+def rse_vs_exact(Q, K, V, O, w, torch, rows_per_head=1024):
+    """||O - O_exact||^2 / ||O_exact||^2 on sampled query rows (fp32 exact)."""
+    g = torch.Generator(device="cpu").manual_seed(0)
+    num = den = 0.0
+    s = 1.0 / math.sqrt(w.D)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            kv = h * w.Hkv // w.Hq
+            idx = torch.randperm(w.N, generator=g)[:rows_per_head].sort().values.cuda()
+            q = Q[b, h, idx].float()
+            k = K[b, kv].float()
+            v = V[b, kv].float()
+            lg = (q @ k.T) * s
+            if w.causal:
+                mask = torch.arange(w.N, device=q.device)[None, :] > idx[:, None]
+                lg = lg.masked_fill(mask, float("-inf"))
+            ex = torch.softmax(lg, dim=-1) @ v
+            num += float(((O[b, h, idx].float() - ex) ** 2).sum())
+            den += float((ex ** 2).sum())
+    return num / den
+
+
+def cpu_baseline(w, x, budget_s=25.0):
+    """Oracle on a bounded sample: one (batch, KV group) slice, or fewer of
+    its problems, extrapolated linearly to the whole layer."""
+    from oracle import muse_oracle as mo
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cfg = mo.MuseConfig(cq=w.C, ck=w.C, iters=w.iters, topk=w.topk, block=w.block, causal=w.causal)
+    Q, K, V = x["Q"], x["K"], x["V"]
+    heads_done = 0
+    t0 = time.perf_counter()
+    for h in range(w.Hq):
+        kv = h * w.Hkv // w.Hq
+        mo.forward_head(Q[0, h], K[0, kv], V[0, kv], cfg)
+        heads_done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_layer_ms = dt / heads_done * (w.B * w.Hq) * 1e3
+    return {"value": round(per_layer_ms, 1), "unit": "ms/layer", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads_done} of {w.B * w.Hq} (batch, query head) problems in {dt:.1f} s, "
+                      f"extrapolated linearly to the layer; host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    from clustered_approximate_softmax_amd import muse as M
+    from clustered_approximate_softmax_amd import synth
+
+    w = synth.WORKLOADS[args.config]
+    if w.backward:
+        print(json.dumps({"error": "fwd+bwd workload needs museattn_bwd, not built yet"}))
+        sys.exit(3)
+    x = synth.make_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    Q, K, V = (torch.from_numpy(x[k]).to(tdt).cuda() for k in ("Q", "K", "V"))
+    cfg = M.make_cfg(w.C, w.iters, w.topk, w.causal, w.block)
+    rows = M.plan(w.N, cfg)
+    O, lse, st = M.museattn_fwd(Q, K, V, cfg)
+    ws = torch.empty(M.layout(w.B, w.Hq, w.Hkv, w.N, w.D, M._dt(Q), cfg)["ws_bytes"], dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        M.museattn_fwd(Q, K, V, cfg, state=st, ws=ws, out=(O, lse))
+
+    for _ in range(args.warmup):
+        step()
+    ms = time_calls(step, args.steps, torch)
+
+    # per-kernel HIP-event timing on the launch stream (separate pass)
+    M.timing_reset()
+    M.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = M.timing_read()
+    M.timing_enable(False)
+    models = kernel_models(w, M, st, rows)
+    per_kernel = {}
+    for name, (tot, n) in kt.items():
+        per_kernel[name] = {"ms_per_launch": tot / n, "launches_per_step": n / args.steps,
+                            "ms_per_step": tot / args.steps}
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["ms_per_step"])
+    launches = per_kernel[dom]["launches_per_step"]
+    fl, by, bound = models.get(dom, (0.0, 0.0, "hbm"))
+    avg_s = per_kernel[dom]["ms_per_launch"] / 1e3
+    if bound == "mfma":
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        achieved = fl / launches / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None}
+    else:
+        achieved = by / launches / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = {"flops": fl / launches, "bytes": by / launches}
+    roof["avg_launch_ms"] = round(avg_s * 1e3, 4)
+
+    eff = exact_flops(w) / (ms / 1e3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(ms, 4), "unit": "ms/layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian-mixture Q/K, normal V)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "D": w.D,
+                   "clusters": w.C, "lloyd_iters": w.iters, "topk": w.topk, "causal": w.causal,
+                   "local_block": w.block},
+        "effective_tflops": round(eff, 2),
+        "effective_pct_of_mfma_peak": round(100 * eff / (PEAK_BF16_TFLOPS if w.dtype == "bf16"
+                                                           else PEAK_F32_TFLOPS), 2),
+        "roofline": roof,
+        "kernels": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in per_kernel.items()},
+    }
+    if not args.no_exact:
+        ex_ms = exact_attention_ms(Q, K, V, w, max(3, args.steps // 2), torch)
+        out["exact_attention_same_gpu"] = {"impl": "torch.nn.functional.scaled_dot_product_attention",
+                                           "ms": round(ex_ms, 4),
+                                           "tflops": round(exact_flops(w) / ex_ms / 1e9, 1),
+                                           "speedup_muse_vs_exact": round(ex_ms / ms, 3)}
+        out["rse_vs_exact"] = round(rse_vs_exact(Q, K, V, O, w, torch), 5)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").normal_()
+        bbuf = torch.empty_like(a)
+        for _ in range(3):
+            bbuf.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n * 4
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

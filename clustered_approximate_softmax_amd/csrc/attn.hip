@@ -6,157 +6,360 @@
 // For a query i of query cluster I the softmax runs over two kinds of
 // items: every key j of a retrieved cluster (logit s q_i.k_j, weight 1,
 // value v_j) and every other non-empty key cluster c (logit s q_i.mu_c,
-// weight n_c, value T_Ic / n_c).  Both kinds are fed through the same tile
-// loop: a tile is 32 items staged in LDS as rows (for S^T = K Q^T) and as a
-// transposed value block (for O^T = V^T P^T), plus a log-weight per item;
-// one online softmax covers all tiles.  The local causal block uses the same
-// loop over contiguous keys with the causal mask.
+// weight n_c, value T_Ic / n_c).  Both kinds go through the same tile loop:
+// a tile is 64 items staged in LDS as rows (A operand of S^T = K Q^T) and as
+// a transposed value block (A operand of O^T = V^T P^T), plus a log-weight
+// per item; one online softmax (base 2) covers all tiles.  The local causal
+// block uses the same loop over contiguous keys with the causal mask.
+//
+// Pipeline: the next tile is loaded into registers while the current one is
+// consumed, then written to the other LDS buffer (one barrier per tile).
+// Exact tiles read the cluster-contiguous key/value copies; the row of
+// each item is computed two tiles ahead into a small LDS ring.
+// Each wave holds QG groups of 16 queries so that every K/V fragment read
+// from LDS feeds QG matrix instructions.
 #include "common.h"
 #include "launch.h"
 
 namespace muse {
 
 enum { MODE_ACAUSAL = 0, MODE_LEVEL = 1, MODE_LOCAL = 2 };
-constexpr int AT_KT = 32;
+constexpr int AT_KT = 64;   // items per tile
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 
-template <typename TIn, int D, int WAVES>
+template <typename TIn, int D, int WAVES, int QG>
 struct alignas(16) AtSmem {
   static constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
-  uint16_t ks[NS][AT_KT][D + 8];
-  uint16_t vt[NS][D][AT_KT + 8];
-  float bias[AT_KT];
-  int32_t krow[AT_KT];
-  int32_t qrow[16 * WAVES];
-  float far_bias[MUSE_MAXC];
-  float far_ninv[MUSE_MAXC];
-  int32_t rc[MUSE_MAXC];
+  static constexpr int NB = NS == 1 ? 2 : 1;   // LDS tile buffers
+  uint16_t ks[NB][NS][AT_KT][D + 8];
+  uint16_t vt[NB][NS][D][AT_KT + 8];
+  float bias[NB][AT_KT];
+  int32_t krow[NB][AT_KT];
+  int32_t ring[3][AT_KT];      // item -> row, two tiles ahead
+  int32_t qrow[16 * QG * WAVES];
+  float far_bias[MUSE_MAXC];   // log2 n_c, or -inf (empty or retrieved)
+  int32_t rbeg[MUSE_MAXC];
   int32_t rcum[MUSE_MAXC + 1];
-  int32_t tpre[MUSE_MAXC + 1];
   int32_t sel[4];
 };
 
-// Stage rows (K and V) of a tile given per-item row indices (-1: masked).
 template <typename TIn, int D, int WAVES>
-__device__ __forceinline__ void stage_rows(AtSmem<TIn, D, WAVES>& sm, const TIn* K, const TIn* V) {
-  constexpr int NS = AtSmem<TIn, D, WAVES>::NS;
-  constexpr int NT = 64 * WAVES;
-  constexpr int TPK = D / 8;
-  for (int idx = threadIdx.x; idx < AT_KT * TPK; idx += NT) {
-    const int it = idx / TPK, e0 = (idx % TPK) * 8;
-    const int row = sm.krow[it];
-    u16x8 kk[NS], vv[NS];
-    if (row >= 0) {
-      load8_split<TIn, NS>(K + (size_t)row * D + e0, kk);
-      load8_split<TIn, NS>(V + (size_t)row * D + e0, vv);
-    } else {
+struct TileRegs {
+  static constexpr int NT = 64 * WAVES;
+  static constexpr int KC = (AT_KT * D / 8 + NT - 1) / NT;          // 8-wide key chunks
+  static constexpr int VB = ((AT_KT / 4) * (D / 8) + NT - 1) / NT;  // 4 items x 8 dims blocks
+  using V8 = typename std::conditional<sizeof(TIn) == 2, u16x8, f32x8>::type;
+  using V4 = typename std::conditional<sizeof(TIn) == 2, u16x4, f32x4>::type;
+  V8 kf[KC];
+  V4 vf[VB][8];
+  float bias;
+  int krow;
+};
+
+struct TileSrc {
+  int mode;             // 1: far tiles then exact tiles; 2: local rows
+  int nfar, nex;
+  const void* mu;       // far: [C][D] centroids (input dtype)
+  const void* T;        // far: [D][Cp] T_Ic / n_c of this query cluster (input dtype)
+  int Ck, Cp;
+  const void* Kp;       // exact: sorted keys of the problem
+  const void* Vp;
+  int nret;
+  const void* K;        // local: keys / values of the head
+  const void* V;
+  int k0, klast;
+};
+
+template <typename TIn, typename V8>
+__device__ __forceinline__ V8 ld8(const TIn* p) {
+  if constexpr (sizeof(TIn) == 2) {
+    return *reinterpret_cast<const u16x8*>(p);
+  } else {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+}
+
+template <typename TIn, typename V4>
+__device__ __forceinline__ V4 ld4(const TIn* p) {
+  if constexpr (sizeof(TIn) == 2) return *reinterpret_cast<const u16x4*>(p);
+  else return *reinterpret_cast<const f32x4*>(p);
+}
+
+template <int NS, typename ST>
+__device__ __forceinline__ void to_parts(ST x, uint16_t& a, uint16_t& b, uint16_t& c) {
+  if constexpr (sizeof(ST) == 2) {
+    a = x; b = 0; c = 0;
+  } else {
+    split3(x, a, b, c);
+  }
+}
+
+// two floats -> packed bf16 pair (hardware round to nearest even)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Row of item `it` of tile t (exact: sorted position; local: absolute row).
+template <typename SM>
+__device__ __forceinline__ int item_row(const SM& sm, const TileSrc& src, int t, int it) {
+  if (src.mode == 2) {
+    const int j = src.k0 + t * AT_KT + it;
+    return j <= src.klast ? j : -1;
+  }
+  if (t < src.nfar) return -1;
+  const int v = (t - src.nfar) * AT_KT + it;
+  if (v >= src.nret) return -1;
+  int r = 0;
+  while (sm.rcum[r + 1] <= v) ++r;
+  return sm.rbeg[r] + (v - sm.rcum[r]);
+}
+
+template <typename TIn, int D, int WAVES, int QG>
+__device__ __forceinline__ void tile_load(const AtSmem<TIn, D, WAVES, QG>& sm, const TileSrc& src, int t,
+                                          TileRegs<TIn, D, WAVES>& R) {
+  using TR = TileRegs<TIn, D, WAVES>;
+  constexpr int NT = TR::NT;
+  const int tid = threadIdx.x;
+  const bool far = src.mode == 1 && t < src.nfar;
+  const int base = t * AT_KT;
+  const int* ring = sm.ring[t % 3];
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { kk[s][j] = 0; vv[s][j] = 0; }
+  for (int q = 0; q < TR::KC; ++q) {
+    const int idx = tid + q * NT;
+    const int it = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
+    const TIn* p = nullptr;
+    if (idx < AT_KT * D / 8) {
+      if (far) {
+        if (base + it < src.Ck) p = reinterpret_cast<const TIn*>(src.mu) + (size_t)(base + it) * D + e0;
+      } else {
+        const int row = ring[it];
+        if (row >= 0)
+          p = reinterpret_cast<const TIn*>(src.mode == 1 ? src.Kp : src.K) + (size_t)row * D + e0;
+      }
     }
+    R.kf[q] = p ? ld8<TIn, typename TR::V8>(p) : typename TR::V8{};
+  }
+  // value blocks: items 4kb..4kb+3 x dims e0..e0+7, kb fastest across lanes
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      *reinterpret_cast<u16x8*>(&sm.ks[s][it][e0]) = kk[s];
+  for (int q = 0; q < TR::VB; ++q) {
+    const int idx = tid + q * NT;
+    const int kb = idx % (AT_KT / 4), e0 = (idx / (AT_KT / 4)) * 8;
+    if (idx >= (AT_KT / 4) * (D / 8)) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sm.vt[s][e0 + j][it] = vv[s][j];
+      for (int j = 0; j < 8; ++j) R.vf[q][j] = typename TR::V4{};
+    } else if (far) {
+      const TIn* p = reinterpret_cast<const TIn*>(src.T) + (size_t)e0 * src.Cp + base + 4 * kb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) R.vf[q][j] = ld4<TIn, typename TR::V4>(p + (size_t)j * src.Cp);
+    } else {
+      typename TR::V8 rowv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = ring[4 * kb + r];
+        rowv[r] = row >= 0 ? ld8<TIn, typename TR::V8>(
+                                 reinterpret_cast<const TIn*>(src.mode == 1 ? src.Vp : src.V) +
+                                 (size_t)row * D + e0)
+                           : typename TR::V8{};
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R.vf[q][j][r] = rowv[r][j];
+    }
+  }
+  if (tid < AT_KT) {
+    if (far) {
+      R.bias = base + tid < src.Ck ? sm.far_bias[base + tid] : -INFINITY;
+      R.krow = -1;
+    } else {
+      const int row = ring[tid];
+      R.bias = row >= 0 ? 0.f : -INFINITY;
+      R.krow = row;
     }
   }
 }
 
-template <int NS, int D>
+template <typename TIn, int D, int WAVES, int QG>
+__device__ __forceinline__ void tile_store(AtSmem<TIn, D, WAVES, QG>& sm, int buf,
+                                           const TileRegs<TIn, D, WAVES>& R) {
+  using TR = TileRegs<TIn, D, WAVES>;
+  constexpr int NS = AtSmem<TIn, D, WAVES, QG>::NS;
+  constexpr int NT = TR::NT;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < TR::KC; ++q) {
+    const int idx = tid + q * NT;
+    if (idx < AT_KT * D / 8) {
+      const int it = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
+      if constexpr (NS == 1) {
+        *reinterpret_cast<u16x8*>(&sm.ks[buf][0][it][e0]) = R.kf[q];
+      } else {
+        u16x8 h[NS];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          uint16_t a, b, c;
+          to_parts<NS>(R.kf[q][j], a, b, c);
+          h[0][j] = a; h[NS > 1 ? 1 : 0][j] = b; h[NS > 2 ? 2 : 0][j] = c;
+        }
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) *reinterpret_cast<u16x8*>(&sm.ks[buf][sp][it][e0]) = h[sp];
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < TR::VB; ++q) {
+    const int idx = tid + q * NT;
+    if (idx < (AT_KT / 4) * (D / 8)) {
+      const int kb = idx % (AT_KT / 4), e0 = (idx / (AT_KT / 4)) * 8;
+      // items 4kb..4kb+3 land at their contraction slots: within a 32-item
+      // block, item r sits at 8(r/4 % 4) + 4(r/16) + r%4
+      const int vpos = 32 * (kb / 8) + 8 * (kb % 4) + 4 * ((kb % 8) / 4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (NS == 1) {
+          *reinterpret_cast<u16x4*>(&sm.vt[buf][0][e0 + j][vpos]) = R.vf[q][j];
+        } else {
+          u16x4 h[NS];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            uint16_t a, b, c;
+            to_parts<NS>(R.vf[q][j][r], a, b, c);
+            h[0][r] = a; h[NS > 1 ? 1 : 0][r] = b; h[NS > 2 ? 2 : 0][r] = c;
+          }
+#pragma unroll
+          for (int sp = 0; sp < NS; ++sp) *reinterpret_cast<u16x4*>(&sm.vt[buf][sp][e0 + j][vpos]) = h[sp];
+        }
+      }
+    }
+  }
+  if (tid < AT_KT) {
+    sm.bias[buf][tid] = R.bias;
+    sm.krow[buf][tid] = R.krow;
+  }
+}
+
+template <int D>
 struct AtState {
-  static constexpr int DT = D / 16;
-  float m, lpart;
-  f32x4 o[DT];
+  float m, lpart;         // running max (base 2) and this lane's partial sum
+  f32x4 o[D / 16];
 };
 
-// Consume the staged tile: logits, online softmax, O^T += V^T P^T.
-template <typename TIn, int D, int WAVES, bool CAUSAL>
-__device__ __forceinline__ void consume_tile(AtSmem<TIn, D, WAVES>& sm,
-                                             const u16x8 (&qf)[D / 32][AtSmem<TIn, D, WAVES>::NS],
-                                             AtState<AtSmem<TIn, D, WAVES>::NS, D>& st, float s,
-                                             int qrow) {
-  constexpr int NS = AtSmem<TIn, D, WAVES>::NS;
+// Consume a staged tile for the QG query groups of this wave.
+template <typename TIn, int D, int WAVES, int QG, bool CAUSAL>
+__device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm, int buf,
+                                             const u16x8 (&qf)[QG][D / 32][AtSmem<TIn, D, WAVES, QG>::NS],
+                                             AtState<D> (&st)[QG], float s2, const int (&qrow)[QG]) {
+  constexpr int NS = AtSmem<TIn, D, WAVES, QG>::NS;
   constexpr int KS = D / 32, DT = D / 16;
+  constexpr int RT = AT_KT / 16, PS = AT_KT / 32;
   const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
-  f32x4 sc[2];
+  f32x4 sc[QG][RT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    sc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) sc[qg][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       u16x8 a[NS];
 #pragma unroll
       for (int sp = 0; sp < NS; ++sp)
-        a[sp] = *reinterpret_cast<const u16x8*>(&sm.ks[sp][16 * rt + col][32 * k + 8 * g]);
-      sc[rt] = mfma_split<NS, NS>(a, qf[k], sc[rt]);
+        a[sp] = *reinterpret_cast<const u16x8*>(&sm.ks[buf][sp][16 * rt + col][32 * k + 8 * g]);
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) sc[qg][rt] = mfma_split<NS, NS>(a, qf[qg][k], sc[qg][rt]);
     }
   }
-  float x[8];
-  float mloc = -INFINITY;
+  f32x4 bv[RT];
+  int4 kr[RT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int it = 16 * rt + 4 * g + i;
-      float v = s * sc[rt][i] + sm.bias[it];
-      if (CAUSAL && sm.krow[it] > qrow) v = -INFINITY;
-      x[rt * 4 + i] = v;
-      mloc = fmaxf(mloc, v);
-    }
+  for (int rt = 0; rt < RT; ++rt) {
+    bv[rt] = *reinterpret_cast<const f32x4*>(&sm.bias[buf][16 * rt + 4 * g]);
+    if (CAUSAL) kr[rt] = *reinterpret_cast<const int4*>(&sm.krow[buf][16 * rt + 4 * g]);
   }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-  const float mnew = fmaxf(st.m, mloc);
-  const float alpha = __expf(st.m - mnew);
-  float psum = 0.f;
-  float p[8];
+  // V^T fragments are shared by the query groups
+  u16x8 va[PS][DT][NS];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    p[j] = __expf(x[j] - mnew);
-    psum += p[j];
-  }
-  st.lpart = st.lpart * alpha + psum;
-  st.m = mnew;
-  u16x8 pb[NS];
+  for (int ps = 0; ps < PS; ++ps)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (NS == 1) {
-      pb[0][j] = f2bf(p[j]);
-    } else {
-      uint16_t h, mm, l;
-      split3(p[j], h, mm, l);
-      pb[0][j] = h; pb[1 % NS][j] = mm; pb[2 % NS][j] = l;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int sp = 0; sp < NS; ++sp)
+        va[ps][dt][sp] = *reinterpret_cast<const u16x8*>(&sm.vt[buf][sp][16 * dt + col][32 * ps + 8 * g]);
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    float x[RT * 4];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = fmaf(s2, sc[qg][rt][i], bv[rt][i]);
+        if (CAUSAL) {
+          const int krow = i == 0 ? kr[rt].x : i == 1 ? kr[rt].y : i == 2 ? kr[rt].z : kr[rt].w;
+          if (krow > qrow[qg]) v = -INFINITY;
+        }
+        x[rt * 4 + i] = v;
+        mloc = fmaxf(mloc, v);
+      }
     }
-  }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float mnew = fmaxf(st[qg].m, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(st[qg].m - mnew);
+    float psum = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    st.o[dt] *= alpha;
-    u16x8 a[NS];
-#pragma unroll
-    for (int sp = 0; sp < NS; ++sp) {
-      const uint16_t* r = &sm.vt[sp][16 * dt + col][0];
-      u16x4 lo = *reinterpret_cast<const u16x4*>(r + 4 * g);
-      u16x4 hi = *reinterpret_cast<const u16x4*>(r + 16 + 4 * g);
-      a[sp] = u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    for (int j = 0; j < RT * 4; ++j) {
+      x[j] = __builtin_amdgcn_exp2f(x[j] - mnew);
+      psum += x[j];
     }
-    st.o[dt] = mfma_split<NS, NS>(a, pb, st.o[dt]);
+    st[qg].lpart = st[qg].lpart * alpha + psum;
+    st[qg].m = mnew;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) st[qg].o[dt] *= alpha;
+    }
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps) {
+      // contraction slots of two 16-row tiles: 8g+j -> 4g+j (j<4), 16+4g+(j-4) (j>=4)
+      u16x8 pb[NS];
+      if constexpr (NS == 1) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const float* pp = &x[ps * 8];
+        u32x4 wv = {pk_bf16(pp[0], pp[1]), pk_bf16(pp[2], pp[3]), pk_bf16(pp[4], pp[5]),
+                    pk_bf16(pp[6], pp[7])};
+        pb[0] = __builtin_bit_cast(u16x8, wv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          uint16_t h, mm, l;
+          split3(x[ps * 8 + j], h, mm, l);
+          pb[0][j] = h; pb[NS > 1 ? 1 : 0][j] = mm; pb[NS > 2 ? 2 : 0][j] = l;
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) st[qg].o[dt] = mfma_split<NS, NS>(va[ps][dt], pb, st[qg].o[dt]);
+    }
   }
 }
 
-template <typename TIn, typename TOut, int D, int WAVES, int MODE>
+template <typename TIn, typename TOut, int D, int WAVES, int QG, int MODE>
 __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, int lev) {
-  constexpr int NS = AtSmem<TIn, D, WAVES>::NS;
-  constexpr int NT = 64 * WAVES, QT = 16 * WAVES;
+  using SM = AtSmem<TIn, D, WAVES, QG>;
+  constexpr int NS = SM::NS, NB = SM::NB;
+  constexpr int NT = 64 * WAVES, QT = 16 * QG * WAVES;
   constexpr int KS = D / 32, DT = D / 16;
-  __shared__ AtSmem<TIn, D, WAVES> sm;
+  __shared__ SM sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
-  const float s = pl.scale;
+  const float s2 = pl.scale * LOG2E;
   const int C = pl.C;
 
-  int bh, kvh, ap = 0, I = 0, tile, kp = 0, k0 = 0, Ck = 0, Cq = 0, q0 = 0;
-  int qlo = 0, qhi = 0;       // query rows (LOCAL) or positions within cluster I
+  int bh, kvh, ap = 0, I = 0, tile, kp = 0, Ck = 0, q0 = 0, k0 = 0;
+  int qlo = 0, qhi = 0;
   if (MODE == MODE_LOCAL) {
     const int nblk = (pl.N + pl.blk - 1) / pl.blk;
     const int tpb = (pl.blk + QT - 1) / QT;
@@ -173,19 +376,23 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     const int nseg = pl.lev_nseg[lev];
     const int m = pl.lev_m[lev];
     const int spp = (m + QT - 1) / QT + C;
-    int id = blockIdx.x;
-    const int slot = id % spp; id /= spp;
-    const int t = id % nseg;
-    bh = id / nseg;
+    // workgroups are dispatched round-robin over the 8 XCDs: keep every
+    // problem on one XCD so its keys and values stay in that XCD's L2
+    const int nprob = pl.B * pl.Hq * nseg;
+    const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
+    const int slot = loc % spp;
+    const int pid = (loc / spp) * 8 + xcd;
+    if (pid >= nprob) return;
+    const int t = pid % nseg;
+    bh = pid / nseg;
     const int p = pl.lev_pfirst[lev] + t;
     ap = bh * pl.P + p;
     const Geom gm = prob_geom(pl, p);
-    Cq = min(C, gm.qn);
+    const int Cq = min(C, gm.qn);
     Ck = min(C, gm.kn);
     k0 = gm.k0;
     q0 = gm.q0;
     const int32_t* qoffs = b.qs.offs + (size_t)ap * (C + 1);
-    // tiles per query cluster and their prefix (one wave scans 4 per lane)
     if (tid < 64) {
       int v[4], sum = 0;
 #pragma unroll
@@ -206,6 +413,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
         if (c < Cq && v[q] > 0 && slot >= run && slot < run + v[q]) {
           sm.sel[0] = c;
           sm.sel[1] = slot - run;
+          sm.sel[3] = qoffs[c];
         }
         run += v[q];
       }
@@ -215,7 +423,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     if (slot >= sm.sel[2]) return;
     I = sm.sel[0];
     tile = sm.sel[1];
-    qlo = qoffs[I] + tile * QT;
+    qlo = sm.sel[3] + tile * QT;
     qhi = min(qoffs[I + 1], qlo + QT);
     const int bq = bh / pl.Hq, hq = bh % pl.Hq;
     kvh = bq * pl.Hkv + (hq * pl.Hkv) / pl.Hq;
@@ -226,44 +434,42 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     kvh = bq * pl.Hkv + (hq * pl.Hkv) / pl.Hq;
   }
   const TIn* Qh = reinterpret_cast<const TIn*>(b.Q) + (size_t)bh * pl.N * D;
-  const TIn* Kh = reinterpret_cast<const TIn*>(b.K) + (size_t)kvh * pl.N * D;
-  const TIn* Vh = reinterpret_cast<const TIn*>(b.V) + (size_t)kvh * pl.N * D;
 
-  // query rows of this workgroup
-  if (tid < QT) {
-    int r = -1;
-    if (MODE == MODE_LOCAL) {
-      if (qlo + tid < qhi) r = qlo + tid;
-    } else {
-      if (qlo + tid < qhi) {
+  for (int r = tid; r < QT; r += NT) {
+    int row = -1;
+    if (qlo + r < qhi) {
+      if (MODE == MODE_LOCAL) {
+        row = qlo + r;
+      } else {
         const int32_t* qperm = b.qs.perm + ((size_t)lev * pl.B * pl.Hq + bh) * pl.N + q0;
-        r = qperm[qlo + tid];
+        row = qperm[qlo + r];
       }
     }
-    sm.qrow[tid] = r;
+    sm.qrow[r] = row;
   }
-  int nret = 0;
+  TileSrc src;
+  src.mode = MODE == MODE_LOCAL ? 2 : 1;
+  src.nfar = 0;
   if (MODE != MODE_LOCAL) {
-    // retrieval list, cumulative sizes; far-field log-weights and 1/n
     const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
     const int32_t* Rr = b.R + ((size_t)ap * C + I) * pl.k1w;
     for (int c = tid; c < MUSE_MAXC; c += NT) {
-      float bias = -INFINITY, ninv = 0.f;
+      float bias = -INFINITY;
       if (c < Ck) {
         const int nc = koffs[c + 1] - koffs[c];
-        if (nc > 0) { bias = logf((float)nc); ninv = 1.f / (float)nc; }
+        if (nc > 0) bias = __log2f((float)nc);
       }
       sm.far_bias[c] = bias;
-      sm.far_ninv[c] = ninv;
     }
-    __syncthreads();
+    int cc[4];
     if (tid < 64) {
-      int v[4], cc[4], sum = 0;
+      int v[4], bg[4], sum = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = tid * 4 + q;
         cc[q] = r < pl.k1w ? Rr[r] : -1;
-        v[q] = cc[q] >= 0 ? koffs[cc[q] + 1] - koffs[cc[q]] : 0;
+        bg[q] = cc[q] >= 0 ? koffs[cc[q]] : 0;
+        v[q] = cc[q] >= 0 ? koffs[cc[q] + 1] - bg[q] : 0;
         sum += v[q];
       }
       int inc = sum;
@@ -275,154 +481,137 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = tid * 4 + q;
-        if (r < MUSE_MAXC) {
-          sm.rc[r] = cc[q];
-          sm.rcum[r] = run;
-        }
+        sm.rbeg[r] = bg[q];
+        sm.rcum[r] = run;
         run += v[q];
       }
       if (tid == 63) sm.rcum[MUSE_MAXC] = inc;
     }
     __syncthreads();
     // retrieved clusters leave the far field
-    for (int r = tid; r < pl.k1w; r += NT)
-      if (sm.rc[r] >= 0) sm.far_bias[sm.rc[r]] = -INFINITY;
-    nret = sm.rcum[MUSE_MAXC];
+    if (tid < 64) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (cc[q] >= 0) sm.far_bias[cc[q]] = -INFINITY;
+    }
+    src.nret = sm.rcum[MUSE_MAXC];
+    src.nfar = (Ck + AT_KT - 1) / AT_KT;
+    src.nex = (src.nret + AT_KT - 1) / AT_KT;
+    src.mu = reinterpret_cast<const TIn*>(b.kst.mu_in) + (size_t)kp * C * D;
+    src.T = reinterpret_cast<const TIn*>(b.T) + ((size_t)ap * C + I) * D * b.Cp32;
+    src.Ck = Ck;
+    src.Cp = b.Cp32;
+    const size_t kb = (((size_t)lev * pl.B * pl.Hkv + kvh) * pl.N + k0) * D;
+    src.Kp = reinterpret_cast<const TIn*>(b.kst.Kp) + kb;
+    src.Vp = reinterpret_cast<const TIn*>(b.kst.Vp) + kb;
+  } else {
+    src.K = reinterpret_cast<const TIn*>(b.K) + (size_t)kvh * pl.N * D;
+    src.V = reinterpret_cast<const TIn*>(b.V) + (size_t)kvh * pl.N * D;
+    src.k0 = k0;
+    src.klast = qhi - 1;
+    src.nex = (qhi - k0 + AT_KT - 1) / AT_KT;
+  }
+  const int ntiles = src.nfar + src.nex;
+  if (tid < AT_KT) {
+    sm.ring[0][tid] = item_row(sm, src, 0, tid);
+    sm.ring[1][tid] = item_row(sm, src, 1, tid);
   }
   __syncthreads();
 
-  // query fragments (B operand of S^T = K Q^T)
-  const int myq = sm.qrow[w * 16 + col];
-  u16x8 qf[KS][NS];
+  int myq[QG];
+  u16x8 qf[QG][KS][NS];
+  AtState<D> st[QG];
 #pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    if (myq >= 0) {
-      load8_split<TIn, NS>(Qh + (size_t)myq * D + 32 * k + 8 * g, qf[k]);
-    } else {
+  for (int qg = 0; qg < QG; ++qg) {
+    myq[qg] = sm.qrow[(w * QG + qg) * 16 + col];
 #pragma unroll
-      for (int sp = 0; sp < NS; ++sp)
+    for (int k = 0; k < KS; ++k) {
+      if (myq[qg] >= 0) {
+        load8_split<TIn, NS>(Qh + (size_t)myq[qg] * D + 32 * k + 8 * g, qf[qg][k]);
+      } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) qf[k][sp][j] = 0;
+        for (int sp = 0; sp < NS; ++sp)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) qf[qg][k][sp][j] = 0;
+      }
     }
+    st[qg].m = -1e30f;
+    st[qg].lpart = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st[qg].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  AtState<NS, D> st;
-  st.m = -1e30f;
-  st.lpart = 0.f;
+  int qmask[QG];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qg = 0; qg < QG; ++qg) qmask[qg] = myq[qg] < 0 ? 0x7fffffff : myq[qg];
 
-  if (MODE != MODE_LOCAL) {
-    // ---- far field: 32 key clusters per tile ----
-    const float* mu = b.kst.mu + (size_t)kp * C * D;
-    const float* T = b.T + ((size_t)ap * C + I) * D * b.Cp32;
-    for (int c0 = 0; c0 < Ck; c0 += AT_KT) {
-      for (int idx = tid; idx < AT_KT * (D / 8); idx += NT) {
-        const int it = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
-        const int c = c0 + it;
-        float v[8];
-        if (c < Ck) {
-          const float* src = mu + (size_t)c * D + e0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = src[j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) split_store<NS>(v[j], &sm.ks[0][it][e0 + j], AT_KT * (D + 8));
-      }
-      for (int idx = tid; idx < D * (AT_KT / 8); idx += NT) {
-        const int d = idx / (AT_KT / 8), cb = (idx % (AT_KT / 8)) * 8;
-        const float* src = T + (size_t)d * b.Cp32 + c0 + cb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c = c0 + cb + j;
-          const float ni = (c < Ck) ? sm.far_ninv[c] : 0.f;
-          const float v = (c < Ck && sm.far_bias[c] > -INFINITY) ? src[j] * ni : 0.f;
-          split_store<NS>(v, &sm.vt[0][d][cb + j], D * (AT_KT + 8));
-        }
-      }
-      if (tid < AT_KT) {
-        const int c = c0 + tid;
-        sm.bias[tid] = c < Ck ? sm.far_bias[c] : -INFINITY;
-      }
+  TileRegs<TIn, D, WAVES> R;
+  if (ntiles > 0) {
+    tile_load(sm, src, 0, R);
+    tile_store(sm, 0, R);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = NB == 2 ? (t & 1) : 0;
+    const bool more = t + 1 < ntiles;
+    if (tid < AT_KT && t + 2 < ntiles) sm.ring[(t + 2) % 3][tid] = item_row(sm, src, t + 2, tid);
+    if (more) tile_load(sm, src, t + 1, R);
+    consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, buf, qf, st, s2, qmask);
+    if (NB == 2) {
+      if (more) tile_store(sm, buf ^ 1, R);
       __syncthreads();
-      consume_tile<TIn, D, WAVES, false>(sm, qf, st, s, myq);
+    } else {
       __syncthreads();
-    }
-    // ---- exact attention over the retrieved clusters' keys ----
-    const int32_t* kperm = b.ks.perm + ((size_t)lev * pl.B * pl.Hkv + kvh) * pl.N + k0;
-    const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
-    for (int v0 = 0; v0 < nret; v0 += AT_KT) {
-      if (tid < AT_KT) {
-        const int v = v0 + tid;
-        int row = -1;
-        if (v < nret) {
-          int r = 0;
-          while (sm.rcum[r + 1] <= v) ++r;
-          row = kperm[koffs[sm.rc[r]] + (v - sm.rcum[r])];
-        }
-        sm.krow[tid] = row;
-        sm.bias[tid] = row >= 0 ? 0.f : -INFINITY;
-      }
-      __syncthreads();
-      stage_rows<TIn, D, WAVES>(sm, Kh, Vh);
-      __syncthreads();
-      consume_tile<TIn, D, WAVES, false>(sm, qf, st, s, myq);
-      __syncthreads();
-    }
-  } else {
-    // ---- local causal block: keys [k0, last query row] ----
-    const int klast = qhi - 1;
-    for (int j0 = k0; j0 <= klast; j0 += AT_KT) {
-      if (tid < AT_KT) {
-        const int j = j0 + tid;
-        sm.krow[tid] = j <= klast ? j : -1;
-        sm.bias[tid] = j <= klast ? 0.f : -INFINITY;
-      }
-      __syncthreads();
-      stage_rows<TIn, D, WAVES>(sm, Kh, Vh);
-      __syncthreads();
-      consume_tile<TIn, D, WAVES, true>(sm, qf, st, s, myq < 0 ? 0x7fffffff : myq);
+      if (more) tile_store(sm, 0, R);
       __syncthreads();
     }
   }
 
-  // ---- finish: normalise, write or merge ----
-  float l = st.lpart;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (myq < 0) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const float lse = l > 0.f ? st.m + logf(l) : -INFINITY;
-  if (MODE == MODE_ACAUSAL) {
-    TOut* O = reinterpret_cast<TOut*>(b.O) + ((size_t)bh * pl.N + myq) * D;
+  // ---- finish: normalise, write or merge (lse in natural log units) ----
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) store1<TOut>(O + 16 * dt + 4 * g + i, st.o[dt][i] * inv);
-    if (g == 0) b.lse[(size_t)bh * pl.N + myq] = lse;
-  } else {
-    float* oa = b.oacc + ((size_t)bh * pl.N + myq) * D;
-    float* la = b.lacc + (size_t)bh * pl.N + myq;
-    if (MODE == MODE_LOCAL) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<f32x4*>(oa + 16 * dt + 4 * g) = st.o[dt] * inv;
-      if (g == 0) *la = lse;
-    } else {
-      if (!(l > 0.f)) return;
-      const float lold = *la;
-      const float L = fmaxf(lold, lse);
-      const float wo = __expf(lold - L), wn = __expf(lse - L);
-      const float tot = wo + wn;
-      const float fo = wo / tot, fn = wn * inv / tot;
+  for (int qg = 0; qg < QG; ++qg) {
+    float l = st[qg].lpart;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int row = myq[qg];
+    if (row < 0) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float lse = l > 0.f ? (st[qg].m + __log2f(l)) * LN2 : -INFINITY;
+    if (MODE == MODE_ACAUSAL) {
+      TOut* O = reinterpret_cast<TOut*>(b.O) + ((size_t)bh * pl.N + row) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        f32x4 prev = *reinterpret_cast<const f32x4*>(oa + 16 * dt + 4 * g);
-        *reinterpret_cast<f32x4*>(oa + 16 * dt + 4 * g) = prev * fo + st.o[dt] * fn;
+        if constexpr (sizeof(TOut) == 2) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          u32x2 wv = {pk_bf16(st[qg].o[dt][0] * inv, st[qg].o[dt][1] * inv),
+                      pk_bf16(st[qg].o[dt][2] * inv, st[qg].o[dt][3] * inv)};
+          *reinterpret_cast<u32x2*>(O + 16 * dt + 4 * g) = wv;
+        } else {
+          *reinterpret_cast<f32x4*>(O + 16 * dt + 4 * g) = st[qg].o[dt] * inv;
+        }
       }
-      if (g == 0) *la = L + logf(tot);
+      if (g == 0) b.lse[(size_t)bh * pl.N + row] = lse;
+    } else {
+      float* oa = b.oacc + ((size_t)bh * pl.N + row) * D;
+      float* la = b.lacc + (size_t)bh * pl.N + row;
+      if (MODE == MODE_LOCAL) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<f32x4*>(oa + 16 * dt + 4 * g) = st[qg].o[dt] * inv;
+        if (g == 0) *la = lse;
+      } else {
+        if (!(l > 0.f)) continue;
+        const float lold = *la;
+        const float L = fmaxf(lold, lse);
+        const float wo = __expf(lold - L), wn = __expf(lse - L);
+        const float tot = wo + wn;
+        const float fo = wo / tot, fn = wn * inv / tot;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          f32x4 prev = *reinterpret_cast<const f32x4*>(oa + 16 * dt + 4 * g);
+          *reinterpret_cast<f32x4*>(oa + 16 * dt + 4 * g) = prev * fo + st[qg].o[dt] * fn;
+        }
+        if (g == 0) *la = L + logf(tot);
+      }
     }
   }
 }
@@ -437,17 +626,18 @@ __global__ void finalize_kernel(const float* oacc, const float* lacc, TOut* O, f
 }
 
 // ---------------------------------------------------------------------------
-template <typename TIn, int D, int WAVES>
+template <typename TIn, int D, int WAVES, int QG>
 static hipError_t attn_level(const Plan& pl, const AttnBufs& b, int lev, hipStream_t st) {
-  constexpr int QT = 16 * WAVES;
+  constexpr int QT = 16 * QG * WAVES;
   const int spp = (pl.lev_m[lev] + QT - 1) / QT + pl.C;
-  const long long grid = (long long)pl.B * pl.Hq * pl.lev_nseg[lev] * spp;
+  const long long nprob = (long long)pl.B * pl.Hq * pl.lev_nseg[lev];
+  const long long grid = ((nprob + 7) / 8) * 8 * spp;
   if (grid == 0) return hipSuccess;
   MUSE_KT_PRE(st);
   if (pl.causal)
-    attn_kernel<TIn, TIn, D, WAVES, MODE_LEVEL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, lev);
+    attn_kernel<TIn, TIn, D, WAVES, QG, MODE_LEVEL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, lev);
   else
-    attn_kernel<TIn, TIn, D, WAVES, MODE_ACAUSAL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, lev);
+    attn_kernel<TIn, TIn, D, WAVES, QG, MODE_ACAUSAL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, lev);
   MUSE_KT_POST(pl.causal ? "attn_level" : "attn_far_retrieve", st);
   return hipGetLastError();
 }
@@ -455,19 +645,21 @@ static hipError_t attn_level(const Plan& pl, const AttnBufs& b, int lev, hipStre
 template <typename TIn, int D>
 static hipError_t attn_all(const Plan& pl, const AttnBufs& b, hipStream_t st) {
   hipError_t e = hipSuccess;
+  constexpr int QG = sizeof(TIn) == 2 ? 2 : 1;
   if (pl.causal) {
-    constexpr int WAVES = 4, QT = 64;
+    constexpr int WAVES = 4, QT = 16 * QG * 4;
     const int nblk = (pl.N + pl.blk - 1) / pl.blk;
     const long long grid = (long long)pl.B * pl.Hq * nblk * ((pl.blk + QT - 1) / QT);
     MUSE_KT_PRE(st);
-    attn_kernel<TIn, TIn, D, WAVES, MODE_LOCAL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, 0);
+    attn_kernel<TIn, TIn, D, WAVES, QG, MODE_LOCAL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, 0);
     MUSE_KT_POST("attn_local", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   for (int lev = 0; lev < pl.nlev; ++lev) {
-    // small query clusters: one wave per workgroup; large: four
+    // query clusters of ~m/C rows: 16*QG*4-row workgroups for large clusters,
+    // one 16-row wave for small ones
     const int avg = pl.lev_m[lev] / (pl.C > 0 ? pl.C : 1);
-    e = avg >= 48 ? attn_level<TIn, D, 4>(pl, b, lev, st) : attn_level<TIn, D, 1>(pl, b, lev, st);
+    e = avg >= 48 * QG ? attn_level<TIn, D, 4, QG>(pl, b, lev, st) : attn_level<TIn, D, 1, 1>(pl, b, lev, st);
     if (e != hipSuccess) return e;
   }
   if (pl.causal) {

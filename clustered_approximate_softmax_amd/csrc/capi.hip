@@ -140,20 +140,28 @@ static void build_kmlarge(const Plan& pl, int heads_total, int sub, int& plocal,
   int ch = 2048;
   while (ch > sub && pts / ch < 1024) ch /= 2;
   lg.ch = ch;
-  int nl = 0, cf = 0, pf = 0;
+  const int ncb = (pl.C + 256 / pl.D - 1) / (256 / pl.D);   // reduce workgroups per problem
+  int nl = 0, cf = 0, pf = 0, wf = 0, rf = 0;
   for (int l = first_large; l < pl.nlev; ++l) {
     if (pl.lev_nseg[l] == 0) continue;
     lg.lev[nl] = l;
     lg.nch[nl] = (pl.lev_m[l] + ch - 1) / ch;
     lg.cfirst[nl] = cf;
     lg.pfirst[nl] = pf;
-    cf += heads_total * pl.lev_nseg[l] * lg.nch[nl];
-    pf += heads_total * pl.lev_nseg[l];
+    lg.wfirst[nl] = wf;
+    lg.rfirst[nl] = rf;
+    const int np = heads_total * pl.lev_nseg[l];
+    cf += np * lg.nch[nl];
+    pf += np;
+    wf += (np + 7) / 8 * 8 * lg.nch[nl];
+    rf += (np + 7) / 8 * 8 * ncb;
     ++nl;
   }
   lg.nl = nl;
   lg.cfirst[nl] = cf;
   lg.pfirst[nl] = pf;
+  lg.wfirst[nl] = wf;
+  lg.rfirst[nl] = rf;
 }
 
 static void build_layout(const Plan& pl, int dtype, Layout& out) {
@@ -165,7 +173,7 @@ static void build_layout(const Plan& pl, int dtype, Layout& out) {
   L.L = pl.nlev;
   L.C = pl.C;
   L.k1w = pl.k1w;
-  L.Cp32 = (pl.C + 31) / 32 * 32;
+  L.Cp32 = (pl.C + 63) / 64 * 64;   // T rows padded to whole 64-cluster tiles
   size_t o = 0;
   L.q_labels = o; o = al(o + nl * BHq * N * 4);
   L.k_labels = o; o = al(o + nl * BHk * N * 4);
@@ -179,10 +187,14 @@ static void build_layout(const Plan& pl, int dtype, Layout& out) {
   L.S = o; o = al(o + BHk * P * C * D * 4);
   L.M = o; o = al(o + BHk * P * D * C * D * 4);
   L.R = o; o = al(o + BHq * P * C * pl.k1w * 4);
+  const size_t eb = dtype == 1 ? 2 : 4;
+  L.Kp = o; o = al(o + nl * BHk * N * D * eb);
+  L.Vp = o; o = al(o + nl * BHk * N * D * eb);
+  L.mu_in = o; o = al(o + BHk * P * C * D * eb);
   L.state_bytes = std::max<size_t>(o, 256);
   build_kmlarge(pl, (int)(BHq + BHk), kmeans_sub(dtype, pl.D), out.plocal, out.lg);
   size_t w = 0;
-  L.ws_T = w; w = al(w + BHq * P * C * D * L.Cp32 * 4);
+  L.ws_T = w; w = al(w + BHq * P * C * D * L.Cp32 * eb);
   L.ws_oacc = w; w = al(w + (pl.causal ? BHq * N * D * 4 : 0));
   L.ws_lacc = w; w = al(w + (pl.causal ? BHq * N * 4 : 0));
   L.ws_part = w; w = al(w + (size_t)out.lg.cfirst[out.lg.nl] * C * D * 4);
@@ -267,9 +279,10 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
   memset(&ab, 0, sizeof(ab));
   ab.Q = Q; ab.K = K; ab.V = V;
   ab.qs = qs; ab.ks = ks;
-  ab.kst = KStats{(float*)(sb + L.mu), (float*)(sb + L.S), (float*)(sb + L.M)};
+  ab.kst = KStats{(float*)(sb + L.mu), (float*)(sb + L.S), (float*)(sb + L.M), sb + L.mu_in,
+                  sb + L.Kp, sb + L.Vp};
   ab.R = (int32_t*)(sb + L.R);
-  ab.T = (float*)(wb + L.ws_T);
+  ab.T = wb + L.ws_T;
   ab.Cp32 = (int32_t)L.Cp32;
   ab.oacc = (float*)(wb + L.ws_oacc);
   ab.lacc = (float*)(wb + L.ws_lacc);
@@ -337,7 +350,7 @@ int musesummarize(const void* K, const void* V, muse_dtype dtype, int64_t G, int
   (void)hipGetLastError();
   hipError_t e = launch_perm_only(pl, ks, st);
   if (e != hipSuccess) return hip_fail(e);
-  e = launch_summarize(pl, (int)dtype, ks, V, KStats{mu, S, M}, st);
+  e = launch_summarize(pl, (int)dtype, ks, V, KStats{mu, S, M, nullptr, nullptr, nullptr}, st);
   if (e != hipSuccess) return hip_fail(e);
   return MUSE_OK;
 }

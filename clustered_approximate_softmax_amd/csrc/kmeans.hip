@@ -35,6 +35,9 @@ struct KmShape {
 template <typename TIn, int D, int CT>
 struct alignas(16) KmSmem {
   using S = KmShape<TIn, D>;
+  // fp32 centroids for the refinement step, kept in LDS when small
+  static constexpr bool KEEP32 = CT * 16 * D * 4 <= 32768;
+  float mu32[KEEP32 ? CT * 16 : 1][D + 4];
   uint16_t mu_hat[CT * 16][S::MUP];
   float mu_norm[CT * 16];
   uint16_t xt[S::NS][D][S::XTP];
@@ -44,33 +47,43 @@ struct alignas(16) KmSmem {
   float red[8];
 };
 
-// Load the problem's current fp32 centroids into bf16 rows + squared norms.
+// Load the problem's current fp32 centroids into bf16 rows + squared norms
+// (norm: 8-element partial sums combined by shuffles in a fixed order).
 template <typename TIn, int D, int CT>
 __device__ void km_load_centroids(KmSmem<TIn, D, CT>& sm, const float* cent, int Ceff, float& Rmax) {
+  constexpr int TPC = D / 8;
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < CT * 16 * (D / 8); idx += KM_NT) {
-    int c = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
-    u16x8 h;
+  float mx = 0.f;
+  for (int idx = tid; idx < CT * 16 * TPC; idx += KM_NT) {
+    const int c = idx / TPC, e0 = (idx % TPC) * 8;
+    float v[8];
     if (c < Ceff) {
-      const float* src = cent + (size_t)c * D + e0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) h[j] = f2bf(src[j]);
+      const f32x4* src = reinterpret_cast<const f32x4*>(cent + (size_t)c * D + e0);
+      f32x4 a = src[0], b = src[1];
+      v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+      v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) h[j] = 0;
+      for (int j = 0; j < 8; ++j) v[j] = 0.f;
+    }
+    u16x8 h;
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h[j] = f2bf(v[j]);
+      part = fmaf(v[j], v[j], part);
     }
     *reinterpret_cast<u16x8*>(&sm.mu_hat[c][e0]) = h;
-  }
-  float mx = 0.f;
-  for (int c = tid; c < CT * 16; c += KM_NT) {
-    float s = INFINITY;
-    if (c < Ceff) {
-      const float* src = cent + (size_t)c * D;
-      s = 0.f;
-      for (int e = 0; e < D; ++e) s = fmaf(src[e], src[e], s);
-      mx = fmaxf(mx, s);
+    if constexpr (KmSmem<TIn, D, CT>::KEEP32) {
+      *reinterpret_cast<f32x4*>(&sm.mu32[c][e0]) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(&sm.mu32[c][e0 + 4]) = f32x4{v[4], v[5], v[6], v[7]};
     }
-    sm.mu_norm[c] = s;
+#pragma unroll
+    for (int m = 1; m < TPC; m <<= 1) part += __shfl_xor(part, m, 64);
+    if (idx % TPC == 0) {
+      sm.mu_norm[c] = c < Ceff ? part : INFINITY;
+      if (c < Ceff) mx = fmaxf(mx, part);
+    }
   }
   for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
   if ((tid & 63) == 0) sm.red[tid >> 6] = mx;
@@ -78,11 +91,49 @@ __device__ void km_load_centroids(KmSmem<TIn, D, CT>& sm, const float* cent, int
   Rmax = sqrtf(fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3])));
 }
 
-// Assign the points [sub0, sub0 + nvalid) of a problem (rows relative to
-// Xp) and stage them transposed in LDS for the update.  Writes labels to
-// LDS and to glab (problem-local index).
+// Points of one sub-tile held in registers (raw input elements): lane
+// (col, g) of wave w holds point w*SUB/4 + 16*grp + col, dims 32k+8g..+7.
+template <typename TIn, int D>
+struct XRegs {
+  using S = KmShape<TIn, D>;
+  using V8 = typename std::conditional<sizeof(TIn) == 2, u16x8, f32x8>::type;
+  V8 x[S::G16][D / 32];
+};
+
+template <typename TIn, int D>
+__device__ __forceinline__ void km_fetch(XRegs<TIn, D>& xr, const TIn* Xp, int sub0, int nvalid) {
+  using S = KmShape<TIn, D>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int grp = 0; grp < S::G16; ++grp) {
+    const int pl = w * (S::SUB / 4) + grp * 16 + col;
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+      if (pl < nvalid) {
+        const TIn* src = Xp + (size_t)(sub0 + pl) * D + 32 * k + 8 * g;
+        if constexpr (sizeof(TIn) == 2) {
+          xr.x[grp][k] = *reinterpret_cast<const u16x8*>(src);
+        } else {
+          f32x4 a0 = *reinterpret_cast<const f32x4*>(src), a1 = *reinterpret_cast<const f32x4*>(src + 4);
+          xr.x[grp][k] = f32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        }
+      } else {
+        xr.x[grp][k] = typename XRegs<TIn, D>::V8{};
+      }
+    }
+  }
+}
+
+template <typename V8>
+__device__ __forceinline__ float xval(const V8& v, int j) {
+  if constexpr (sizeof(v[0]) == 2) return bf2f(v[j]);
+  else return v[j];
+}
+
+// Assign the prefetched points [sub0, sub0 + nvalid) and stage them
+// transposed in LDS for the update.  Writes labels to LDS and to glab.
 template <typename TIn, int D, int CT>
-__device__ void km_assign_sub(KmSmem<TIn, D, CT>& sm, const TIn* Xp, int sub0, int nvalid,
+__device__ void km_assign_sub(KmSmem<TIn, D, CT>& sm, const XRegs<TIn, D>& xr, int sub0, int nvalid,
                               const float* cent, int Ceff, float Rmax, int32_t* glab) {
   using S = KmShape<TIn, D>;
   constexpr int NS = S::NS;
@@ -92,7 +143,7 @@ __device__ void km_assign_sub(KmSmem<TIn, D, CT>& sm, const TIn* Xp, int sub0, i
   // screening error bound factor: bf16 centroids (and bf16 points for fp32 input)
   const float efac = (NS == 1 ? 0.00390625f : 0.0078125f) * 1.05f;
 
-#pragma unroll 1
+#pragma unroll
   for (int grp = 0; grp < S::G16; ++grp) {
     const int pl = w * (S::SUB / 4) + grp * 16 + col;
     const bool valid = pl < nvalid;
@@ -100,23 +151,24 @@ __device__ void km_assign_sub(KmSmem<TIn, D, CT>& sm, const TIn* Xp, int sub0, i
     float xsq = 0.f;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      if (valid) {
-        const TIn* src = Xp + (size_t)(sub0 + pl) * D + 32 * k + 8 * g;
-        load8_split<TIn, NS>(src, xf[k]);
-        float v[8];
-        load8_f32<TIn>(src, v);
+      if constexpr (NS == 1) {
+        xf[k][0] = xr.x[grp][k];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xsq = fmaf(v[j], v[j], xsq);
+        for (int j = 0; j < 8; ++j) { const float v = xval(xr.x[grp][k], j); xsq = fmaf(v, v, xsq); }
       } else {
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) xf[k][s][j] = 0;
+        for (int j = 0; j < 8; ++j) {
+          const float v = xr.x[grp][k][j];
+          uint16_t h, m, l;
+          split3(v, h, m, l);
+          xf[k][0][j] = h; xf[k][NS > 1 ? 1 : 0][j] = m; xf[k][NS > 2 ? 2 : 0][j] = l;
+          xsq = fmaf(v, v, xsq);
+        }
       }
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
+      for (int sp = 0; sp < NS; ++sp)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sm.xt[s][32 * k + 8 * g + j][pl] = xf[k][s][j];
+        for (int j = 0; j < 8; ++j) sm.xt[sp][32 * k + 8 * g + j][pl] = xf[k][sp][j];
     }
     xsq += __shfl_xor(xsq, 16, 64);
     xsq += __shfl_xor(xsq, 32, 64);
@@ -133,12 +185,12 @@ __device__ void km_assign_sub(KmSmem<TIn, D, CT>& sm, const TIn* Xp, int sub0, i
           u16x8 a = *reinterpret_cast<const u16x8*>(&sm.mu_hat[16 * t + col][32 * k + 8 * g]);
           acc = mfma(as_bf(a), as_bf(xf[k][0]), acc);
         }
+        const f32x4 nrm = *reinterpret_cast<const f32x4*>(&sm.mu_norm[16 * t + 4 * g]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int c = 16 * t + 4 * g + i;
-          const float d = sm.mu_norm[c] - 2.f * acc[i];
+          const float d = fmaf(-2.f, acc[i], nrm[i]);
           dv[t * 4 + i] = d;
-          if (d < best) { best = d; bi = c; }
+          if (d < best) { best = d; bi = 16 * t + 4 * g + i; }
         }
       } else {
 #pragma unroll
@@ -161,37 +213,54 @@ __device__ void km_assign_sub(KmSmem<TIn, D, CT>& sm, const TIn* Xp, int sub0, i
     cand += __shfl_xor(cand, 32, 64);
     int label = bi;
     if (cand > 1) {
+      // candidate clusters as a bitmask shared by the 4 lanes of this point
+      constexpr int NW = (CT * 16 + 63) / 64;
+      unsigned long long cm[NW];
+#pragma unroll
+      for (int q = 0; q < NW; ++q) cm[q] = 0ull;
+#pragma unroll
+      for (int t = 0; t < CT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (dv[t * 4 + i] <= thr) {
+            const int c = 16 * t + 4 * g + i;
+            cm[c >> 6] |= 1ull << (c & 63);
+          }
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        cm[q] |= __shfl_xor(cm[q], 16, 64);
+        cm[q] |= __shfl_xor(cm[q], 32, 64);
+      }
       float bd = INFINITY;
       int bc = 0x7fffffff;
-      if (valid) {
-        const TIn* xr = Xp + (size_t)(sub0 + pl) * D;
 #pragma unroll
-        for (int t = 0; t < CT; ++t) {
+      for (int q = 0; q < NW; ++q) {
+        unsigned long long mword = cm[q];
+        while (mword) {
+          const int c = 64 * q + __builtin_ctzll(mword);
+          mword &= mword - 1;
+          float part = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (dv[t * 4 + i] <= thr) {
-              const int c = 16 * t + 4 * g + i;
-              const float* mr = cent + (size_t)c * D;
-              float d = 0.f;
-              for (int e = 0; e < D; e += 8) {
-                float xv[8];
-                load8_f32<TIn>(xr + e, xv);
+          for (int k = 0; k < KS; ++k) {
+            float mv[8];
+            if constexpr (KmSmem<TIn, D, CT>::KEEP32) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                  float df = xv[j] - mr[e + j];
-                  d = fmaf(df, df, d);
-                }
-              }
-              if (d < bd || (d == bd && c < bc)) { bd = d; bc = c; }
+              for (int j = 0; j < 8; ++j) mv[j] = sm.mu32[c][32 * k + 8 * g + j];
+            } else {
+              const float* mr = cent + (size_t)c * D + 32 * k + 8 * g;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) mv[j] = mr[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float df = xval(xr.x[grp][k], j) - mv[j];
+              part = fmaf(df, df, part);
             }
           }
+          part += __shfl_xor(part, 16, 64);
+          part += __shfl_xor(part, 32, 64);
+          if (part < bd || (part == bd && c < bc)) { bd = part; bc = c; }
         }
-      }
-#pragma unroll
-      for (int m = 16; m <= 32; m <<= 1) {
-        float ob = __shfl_xor(bd, m, 64);
-        int oi = __shfl_xor(bc, m, 64);
-        if (ob < bd || (ob == bd && oi < bc)) { bd = ob; bc = oi; }
       }
       label = bc;
     }
@@ -202,47 +271,62 @@ __device__ void km_assign_sub(KmSmem<TIn, D, CT>& sm, const TIn* Xp, int sub0, i
   }
 }
 
-// One-hot update: acc[u] += onehot(labels) . X for this wave's tiles.
-// Wave w owns tiles tau = ct * (D/16) + dt with tau % 4 == w.
+// One-hot update: acc += onehot(labels) . X.  Wave w owns the cluster tiles
+// ct = w, w+4, ... with every dim tile (one-hot built once per 32 points
+// and cluster tile); with fewer than 4 cluster tiles it owns dim tiles
+// dt = w, w+4, ... of cluster tile 0.
 template <typename TIn, int D, int CT>
 struct KmAcc {
-  static constexpr int U = CT * (D / 16) / 4 > 0 ? CT * (D / 16) / 4 : 1;
+  static constexpr int DT = D / 16;
+  static constexpr int U = CT >= 4 ? (CT / 4) * DT : DT / 4;
   f32x4 a[U];
 };
 
 template <typename TIn, int D, int CT>
 __device__ __forceinline__ void km_tile_of(int w, int u, int& ct, int& dt) {
-  int tau = w + 4 * u;
-  ct = tau / (D / 16);
-  dt = tau % (D / 16);
+  constexpr int DT = D / 16;
+  if constexpr (CT >= 4) {
+    ct = w + 4 * (u / DT);
+    dt = u % DT;
+  } else {
+    ct = 0;
+    dt = w + 4 * u;
+  }
 }
 
 template <typename TIn, int D, int CT>
 __device__ void km_update_sub(KmSmem<TIn, D, CT>& sm, KmAcc<TIn, D, CT>& acc, int Ceff) {
   using S = KmShape<TIn, D>;
   constexpr int NS = S::NS;
+  constexpr int DT = D / 16;
   constexpr int U = KmAcc<TIn, D, CT>::U;
+  constexpr int NCT = CT >= 4 ? CT / 4 : 1;          // cluster tiles per wave
+  constexpr int NDT = CT >= 4 ? DT : DT / 4;         // dim tiles per wave
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
 #pragma unroll 1
   for (int ks = 0; ks < S::SUB / 32; ++ks) {
-    int labs[8];
+    const int4 l0 = *reinterpret_cast<const int4*>(&sm.lab[32 * ks + 8 * g]);
+    const int4 l1 = *reinterpret_cast<const int4*>(&sm.lab[32 * ks + 8 * g + 4]);
+    const int labs[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+    u16x8 b[NDT][NS];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) labs[j] = sm.lab[32 * ks + 8 * g + j];
+    for (int d = 0; d < NDT; ++d) {
+      const int dt = CT >= 4 ? d : w + 4 * d;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int ct, dt;
-      km_tile_of<TIn, D, CT>(w, u, ct, dt);
-      if (ct >= CT || ct * 16 >= Ceff) continue;
+      for (int sp = 0; sp < NS; ++sp)
+        b[d][sp] = *reinterpret_cast<const u16x8*>(&sm.xt[sp][16 * dt + col][32 * ks + 8 * g]);
+    }
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int ct = CT >= 4 ? w + 4 * c : 0;
+      if (ct * 16 >= Ceff) continue;
       u16x8 a;
       const int cl = 16 * ct + col;
 #pragma unroll
       for (int j = 0; j < 8; ++j) a[j] = (labs[j] == cl) ? (uint16_t)0x3F80 : (uint16_t)0;
-      u16x8 b[NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-        b[s] = *reinterpret_cast<const u16x8*>(&sm.xt[s][16 * dt + col][32 * ks + 8 * g]);
-      acc.a[u] = mfma_split<1, NS>(&a, b, acc.a[u]);
+      for (int d = 0; d < NDT; ++d) acc.a[c * NDT + d] = mfma_split<1, NS>(&a, b[d], acc.a[c * NDT + d]);
     }
   }
 }
@@ -256,7 +340,8 @@ __device__ void stable_perm(SM& sm, const int32_t* lab, int n, int C, int row0, 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int c = tid; c < MUSE_MAXC; c += KM_NT) sm.cnt[c] = 0;
   __syncthreads();
-  for (int j = tid; j < n; j += KM_NT) atomicAdd(&sm.cnt[lab[j]], 1);
+  // labels outside [0, C) (caller-provided assignments) are clamped
+  for (int j = tid; j < n; j += KM_NT) atomicAdd(&sm.cnt[min(max(lab[j], 0), C - 1)], 1);
   __syncthreads();
   if (tid < 64) {
     // exclusive scan of C <= 256 counts by one wave, 4 per lane
@@ -288,7 +373,7 @@ __device__ void stable_perm(SM& sm, const int32_t* lab, int n, int C, int row0, 
     __syncthreads();
     const int j = b0 + tid;
     const bool valid = j < n;
-    const int L = valid ? lab[j] : 0;
+    const int L = valid ? min(max(lab[j], 0), C - 1) : 0;
     unsigned long long mt = __ballot(valid);
 #pragma unroll
     for (int bit = 0; bit < 8; ++bit) {
@@ -324,28 +409,38 @@ __device__ __forceinline__ size_t cp_index(const Plan& pl, int head, int p) {
 
 template <typename TIn>
 __global__ void __launch_bounds__(KM_NT) km_init_kernel(Plan pl, CSet s0, CSet s1, int D) {
-  // one workgroup per (set, head, p)
-  int id = blockIdx.x;
-  const int per = pl.P;
-  const CSet& s = (id < s0.heads * per) ? s0 : s1;
-  if (id >= s0.heads * per) id -= s0.heads * per;
-  const int head = id / per, p = id % per;
+  // one thread per (set, head, problem, cluster, 8-wide chunk of the row)
+  const int tpc = D / 8;
+  long long id = (long long)blockIdx.x * KM_NT + threadIdx.x;
+  const int C = pl.C;
+  const long long per_set0 = (long long)s0.heads * pl.P * C * tpc;
+  const long long total = per_set0 + (long long)s1.heads * pl.P * C * tpc;
+  if (id >= total) return;
+  const bool first = id < per_set0;
+  const CSet& s = first ? s0 : s1;
+  if (!first) id -= per_set0;
+  const int e0 = (int)(id % tpc) * 8;
+  id /= tpc;
+  const int c = (int)(id % C);
+  id /= C;
+  const int p = (int)(id % pl.P);
+  const int head = (int)(id / pl.P);
   int lev, r0, n;
   cset_rows(pl, s, p, lev, r0, n);
-  const int C = pl.C, Ceff = min(C, n);
-  const TIn* X = reinterpret_cast<const TIn*>(s.X) + ((size_t)head * pl.N + r0) * D;
-  float* cent = s.cent + cp_index(pl, head, p) * C * D;
-  const int32_t* init = s.init ? s.init + cp_index(pl, head, p) * C : nullptr;
-  for (int idx = threadIdx.x; idx < C * D; idx += KM_NT) {
-    int c = idx / D, e = idx % D;
-    float v = 0.f;
-    if (c < Ceff) {
-      int r = init ? init[c] : (int)(((long long)c * n) / Ceff);
-      r = min(max(r, 0), n - 1);
-      v = load1_f32<TIn>(X + (size_t)r * D + e);
-    }
-    cent[idx] = v;
+  const int Ceff = min(C, n);
+  float* dst = s.cent + (cp_index(pl, head, p) * C + c) * D + e0;
+  float v[8];
+  if (c < Ceff) {
+    const int32_t* init = s.init ? s.init + cp_index(pl, head, p) * C : nullptr;
+    int r = init ? init[c] : (int)(((long long)c * n) / Ceff);
+    r = min(max(r, 0), n - 1);
+    load8_f32<TIn>(reinterpret_cast<const TIn*>(s.X) + ((size_t)head * pl.N + r0 + r) * D + e0, v);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.f;
   }
+  *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
 // All iterations for one problem in one workgroup; ends with the permutation.
@@ -371,6 +466,8 @@ __global__ void __launch_bounds__(KM_NT) km_local_kernel(Plan pl, CSet s0, CSet 
   constexpr int U = KmAcc<TIn, D, CT>::U;
 
   for (int it = 0; it < pl.iters; ++it) {
+    XRegs<TIn, D> xr;
+    km_fetch<TIn, D>(xr, Xp, 0, min(S::SUB, n));
     float Rmax;
     km_load_centroids<TIn, D, CT>(sm, cent, Ceff, Rmax);
     for (int c = tid; c < MUSE_MAXC; c += KM_NT) sm.cnt[c] = 0;
@@ -380,7 +477,8 @@ __global__ void __launch_bounds__(KM_NT) km_local_kernel(Plan pl, CSet s0, CSet 
     __syncthreads();
     for (int sub0 = 0; sub0 < n; sub0 += S::SUB) {
       const int nv = min(S::SUB, n - sub0);
-      km_assign_sub<TIn, D, CT>(sm, Xp, sub0, nv, cent, Ceff, Rmax, glab);
+      km_assign_sub<TIn, D, CT>(sm, xr, sub0, nv, cent, Ceff, Rmax, glab);
+      if (sub0 + S::SUB < n) km_fetch<TIn, D>(xr, Xp, sub0 + S::SUB, min(S::SUB, n - sub0 - S::SUB));
       __syncthreads();
       for (int q = tid; q < nv; q += KM_NT) atomicAdd(&sm.cnt[sm.lab[q]], 1);
       km_update_sub<TIn, D, CT>(sm, acc, Ceff);
@@ -414,10 +512,15 @@ __global__ void __launch_bounds__(KM_NT) km_assign_kernel(Plan pl, CSet s0, CSet
   using S = KmShape<TIn, D>;
   extern __shared__ __align__(16) unsigned char smraw[];
   KmSmem<TIn, D, CT>& sm = *reinterpret_cast<KmSmem<TIn, D, CT>*>(smraw);
-  const int chunk = blockIdx.x;
   int li = 0;
-  while (li + 1 < lg.nl && lg.cfirst[li + 1] <= chunk) ++li;
+  while (li + 1 < lg.nl && lg.wfirst[li + 1] <= (int)blockIdx.x) ++li;
   const int lev = lg.lev[li], nch = lg.nch[li], nseg = pl.lev_nseg[lev];
+  // the chunks of one problem share an XCD (dispatch is round-robin over 8)
+  const int wl = blockIdx.x - lg.wfirst[li];
+  const int xcd = wl % 8, loc = wl / 8;
+  const int prob = (loc / nch) * 8 + xcd;
+  if (prob >= (s0.heads + s1.heads) * nseg) return;
+  const int chunk = lg.cfirst[li] + prob * nch + loc % nch;
   int rem = chunk - lg.cfirst[li];
   const int per_head = nseg * nch;
   const bool first = rem < s0.heads * per_head;
@@ -437,6 +540,8 @@ __global__ void __launch_bounds__(KM_NT) km_assign_kernel(Plan pl, CSet s0, CSet
   const int col = lane & 15, g = lane >> 4;
   constexpr int U = KmAcc<TIn, D, CT>::U;
 
+  XRegs<TIn, D> xr;
+  km_fetch<TIn, D>(xr, Xp, c0, min(S::SUB, c1 - c0));
   float Rmax;
   km_load_centroids<TIn, D, CT>(sm, cent, Ceff, Rmax);
   for (int c = tid; c < MUSE_MAXC; c += KM_NT) sm.cnt[c] = 0;
@@ -446,7 +551,8 @@ __global__ void __launch_bounds__(KM_NT) km_assign_kernel(Plan pl, CSet s0, CSet
   __syncthreads();
   for (int sub0 = c0; sub0 < c1; sub0 += S::SUB) {
     const int nv = min(S::SUB, c1 - sub0);
-    km_assign_sub<TIn, D, CT>(sm, Xp, sub0, nv, cent, Ceff, Rmax, glab);
+    km_assign_sub<TIn, D, CT>(sm, xr, sub0, nv, cent, Ceff, Rmax, glab);
+    if (sub0 + S::SUB < c1) km_fetch<TIn, D>(xr, Xp, sub0 + S::SUB, min(S::SUB, c1 - sub0 - S::SUB));
     __syncthreads();
     for (int q = tid; q < nv; q += KM_NT) atomicAdd(&sm.cnt[sm.lab[q]], 1);
     km_update_sub<TIn, D, CT>(sm, acc, Ceff);
@@ -467,15 +573,21 @@ __global__ void __launch_bounds__(KM_NT) km_assign_kernel(Plan pl, CSet s0, CSet
   for (int c = tid; c < C; c += KM_NT) pcnt[(size_t)chunk * C + c] = sm.cnt[c];
 }
 
-// Centroids of the large problems from the chunk partials.
-__global__ void km_reduce_kernel(Plan pl, CSet s0, CSet s1, KmLarge lg, const float* part,
-                                 const int32_t* pcnt, int D) {
-  // one workgroup per (level entry, set, head, t); threads over (c, e)
-  int id = blockIdx.x;
+// Centroids of the large problems from the chunk partials: one thread per
+// (cluster, dim), chunks summed in a fixed order.
+__global__ void __launch_bounds__(256) km_reduce_kernel(Plan pl, CSet s0, CSet s1, KmLarge lg,
+                                                        const float* part, const int32_t* pcnt, int D) {
+  const int cpb = 256 / D;                       // clusters per workgroup
+  const int ncb = (pl.C + cpb - 1) / cpb;
   int li = 0;
-  while (li + 1 < lg.nl && lg.pfirst[li + 1] <= id) ++li;
+  while (li + 1 < lg.nl && lg.rfirst[li + 1] <= (int)blockIdx.x) ++li;
+  const int wl = blockIdx.x - lg.rfirst[li];
+  const int xcd = wl % 8, loc = wl / 8;
   const int lev = lg.lev[li], nch = lg.nch[li], nseg = pl.lev_nseg[lev];
-  int rem = id - lg.pfirst[li];
+  const int prob = (loc / ncb) * 8 + xcd;
+  const int cb = loc % ncb;
+  if (prob >= (s0.heads + s1.heads) * nseg) return;
+  int rem = prob;
   const bool first = rem < s0.heads * nseg;
   const CSet& s = first ? s0 : s1;
   const int cbase_set = first ? 0 : s0.heads * nseg * nch;
@@ -485,22 +597,136 @@ __global__ void km_reduce_kernel(Plan pl, CSet s0, CSet s1, KmLarge lg, const fl
   int lv, r0, n;
   cset_rows(pl, s, p, lv, r0, n);
   const int C = pl.C, Ceff = min(C, n);
+  const int c = cb * cpb + threadIdx.x / D, e = threadIdx.x % D;
+  if (c >= Ceff) return;
   const int nchp = (n + lg.ch - 1) / lg.ch;
   const size_t chunk0 = (size_t)lg.cfirst[li] + cbase_set + ((size_t)head * nseg + t) * nch;
-  float* cent = s.cent + cp_index(pl, head, p) * C * D;
-  for (int idx = threadIdx.x; idx < Ceff * D; idx += blockDim.x) {
-    const int c = idx / D;
-    float sum = 0.f;
-    int k = 0;
-    for (int q = 0; q < nchp; ++q) {
-      sum += part[(chunk0 + q) * C * D + idx];
-      k += pcnt[(chunk0 + q) * C + c];
+  // batches of 8 independent loads, summed in a fixed order
+  float sum = 0.f;
+  int k = 0;
+  for (int q0 = 0; q0 < nchp; q0 += 8) {
+    float v[8];
+    int n8[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool ok = q0 + q < nchp;
+      const size_t b = (chunk0 + q0 + q) * C + c;
+      v[q] = ok ? part[b * D + e] : 0.f;
+      n8[q] = ok ? pcnt[b] : 0;
     }
-    if (k > 0) cent[idx] = sum / (float)k;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) { sum += v[q]; k += n8[q]; }
+  }
+  if (k > 0) s.cent[(cp_index(pl, head, p) * C + c) * D + e] = sum / (float)k;
+}
+
+// Permutation of the large problems after their last iteration, one
+// workgroup per chunk: the cluster counts of every chunk (the last
+// iteration's chunk histograms) give each chunk's output base per cluster;
+// ranks inside the chunk come from wave ballots, so the order is stable.
+__global__ void __launch_bounds__(KM_NT) km_perm_chunk_kernel(Plan pl, CSet s0, CSet s1, KmLarge lg,
+                                                              const int32_t* pcnt) {
+  __shared__ struct {
+    int32_t base[MUSE_MAXC];
+    int32_t tot[MUSE_MAXC];
+    int32_t wcnt[4][MUSE_MAXC];
+  } sm;
+  int li = 0;
+  while (li + 1 < lg.nl && lg.wfirst[li + 1] <= (int)blockIdx.x) ++li;
+  const int lev = lg.lev[li], nch = lg.nch[li], nseg = pl.lev_nseg[lev];
+  const int wl = blockIdx.x - lg.wfirst[li];
+  const int xcd = wl % 8, loc = wl / 8;
+  const int prob = (loc / nch) * 8 + xcd;
+  if (prob >= (s0.heads + s1.heads) * nseg) return;
+  const int ci = loc % nch;
+  const int chunk0 = lg.cfirst[li] + prob * nch;     // first chunk of this problem
+  int rem = prob;
+  const bool first = rem < s0.heads * nseg;
+  const CSet& s = first ? s0 : s1;
+  if (!first) rem -= s0.heads * nseg;
+  const int head = rem / nseg, t = rem % nseg;
+  const int p = pl.lev_pfirst[lev] + t;
+  int lv, r0, n;
+  cset_rows(pl, s, p, lv, r0, n);
+  const int C = pl.C, Ceff = min(C, n);
+  const int nchp = (n + lg.ch - 1) / lg.ch;
+  const int c0 = ci * lg.ch, c1 = min(n, c0 + lg.ch);
+  if (c0 >= c1) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // totals and this chunk's base per cluster
+  for (int c = tid; c < MUSE_MAXC; c += KM_NT) {
+    int tot = 0, before = 0;
+    if (c < Ceff) {
+      for (int q = 0; q < nchp; ++q) {
+        const int k = pcnt[(size_t)(chunk0 + q) * C + c];
+        tot += k;
+        if (q < ci) before += k;
+      }
+    }
+    sm.tot[c] = tot;
+    sm.base[c] = before;
+  }
+  __syncthreads();
+  int32_t* offs = s.offs + cp_index(pl, head, p) * (C + 1);
+  if (tid < 64) {
+    // exclusive scan of the totals (4 per lane)
+    int v[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = lane * 4 + q;
+      v[q] = c < Ceff ? sm.tot[c] : 0;
+      sum += v[q];
+    }
+    int inc = sum;
+    for (int m = 1; m < 64; m <<= 1) {
+      const int o = __shfl_up(inc, m, 64);
+      if (lane >= m) inc += o;
+    }
+    int run = inc - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = lane * 4 + q;
+      if (c < Ceff) {
+        sm.base[c] += run;
+        if (ci == 0) offs[c] = run;
+      }
+      run += v[q];
+    }
+  }
+  if (ci == 0)
+    for (int c = Ceff + tid; c <= C; c += KM_NT) offs[c] = n;
+  __syncthreads();
+  const int32_t* glab = s.labels + ((size_t)lev * s.heads + head) * pl.N + r0;
+  int32_t* perm = s.perm + ((size_t)lev * s.heads + head) * pl.N + r0;
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int b0 = c0; b0 < c1; b0 += KM_NT) {
+    for (int c = tid; c < 4 * MUSE_MAXC; c += KM_NT) (&sm.wcnt[0][0])[c] = 0;
+    __syncthreads();
+    const int j = b0 + tid;
+    const bool valid = j < c1;
+    const int L = valid ? min(max(glab[j], 0), Ceff - 1) : 0;
+    unsigned long long mt = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      unsigned long long bb = __ballot((L >> bit) & 1);
+      mt &= ((L >> bit) & 1) ? bb : ~bb;
+    }
+    const int rank = __popcll(mt & lt);
+    if (valid && rank == 0) sm.wcnt[w][L] = __popcll(mt);
+    __syncthreads();
+    if (valid) {
+      int pre = sm.base[L];
+      for (int q = 0; q < w; ++q) pre += sm.wcnt[q][L];
+      perm[pre + rank] = r0 + j;
+    }
+    __syncthreads();
+    for (int c = tid; c < Ceff; c += KM_NT)
+      sm.base[c] += sm.wcnt[0][c] + sm.wcnt[1][c] + sm.wcnt[2][c] + sm.wcnt[3][c];
+    __syncthreads();
   }
 }
 
-// Permutation of the large problems after their last iteration.
+// Permutation of a set of problems from given labels (one workgroup each).
 __global__ void __launch_bounds__(KM_NT) km_perm_kernel(Plan pl, CSet s0, CSet s1, int plocal) {
   __shared__ struct {
     int32_t cnt[MUSE_MAXC];
@@ -530,9 +756,12 @@ static hipError_t km_run_t(const Plan& pl, const CSet& s0, const CSet& s1, int p
   const int nsets_heads = s0.heads + s1.heads;
   const size_t smem = sizeof(KmSmem<TIn, D, CT>);
   if (nsets_heads == 0) return hipSuccess;
-  MUSE_KT_PRE(st);
-  km_init_kernel<TIn><<<nsets_heads * pl.P, KM_NT, 0, st>>>(pl, s0, s1, D);
-  MUSE_KT_POST("km_init", st);
+  {
+    const long long thr = (long long)nsets_heads * pl.P * pl.C * (D / 8);
+    MUSE_KT_PRE(st);
+    km_init_kernel<TIn><<<(unsigned)((thr + KM_NT - 1) / KM_NT), KM_NT, 0, st>>>(pl, s0, s1, D);
+    MUSE_KT_POST("km_init", st);
+  }
   if (plocal > 0) {
     auto k = km_local_kernel<TIn, D, CT>;
     set_smem_once((const void*)k, smem);
@@ -545,14 +774,14 @@ static hipError_t km_run_t(const Plan& pl, const CSet& s0, const CSet& s1, int p
     set_smem_once((const void*)ka, smem);
     for (int it = 0; it < pl.iters; ++it) {
       MUSE_KT_PRE(st);
-      ka<<<lg.cfirst[lg.nl], KM_NT, smem, st>>>(pl, s0, s1, lg, part, pcnt);
+      ka<<<lg.wfirst[lg.nl], KM_NT, smem, st>>>(pl, s0, s1, lg, part, pcnt);
       MUSE_KT_POST("km_assign", st);
       MUSE_KT_PRE(st);
-      km_reduce_kernel<<<lg.pfirst[lg.nl], 256, 0, st>>>(pl, s0, s1, lg, part, pcnt, D);
+      km_reduce_kernel<<<lg.rfirst[lg.nl], 256, 0, st>>>(pl, s0, s1, lg, part, pcnt, D);
       MUSE_KT_POST("km_reduce", st);
     }
     MUSE_KT_PRE(st);
-    km_perm_kernel<<<nsets_heads * (pl.P - plocal), KM_NT, 0, st>>>(pl, s0, s1, plocal);
+    km_perm_chunk_kernel<<<lg.wfirst[lg.nl], KM_NT, 0, st>>>(pl, s0, s1, lg, pcnt);
     MUSE_KT_POST("km_perm", st);
   }
   return hipGetLastError();

@@ -16,6 +16,8 @@ struct KmLarge {
   int32_t lev[MUSE_MAXLEV];         // plan level of each entry
   int32_t nch[MUSE_MAXLEV];         // chunks per problem
   int32_t cfirst[MUSE_MAXLEV + 1];  // first chunk of each entry (both sets)
+  int32_t wfirst[MUSE_MAXLEV + 1];  // first workgroup of each entry (XCD-padded)
+  int32_t rfirst[MUSE_MAXLEV + 1];  // first reduce workgroup of each entry (XCD-padded)
   int32_t pfirst[MUSE_MAXLEV + 1];  // first problem of each entry (both sets)
 };
 
@@ -35,6 +37,9 @@ struct KStats {
   float* mu;    // [heads][P][C][D]
   float* S;     // [heads][P][C][D]
   float* M;     // [heads][P][D][C][D]  (value dim, cluster, key dim)
+  void* mu_in;  // [heads][P][C][D] centroids in the input dtype (or null)
+  void* Kp;     // [nlev][heads][N][D] keys in cluster-contiguous order (or null)
+  void* Vp;     // [nlev][heads][N][D] values, same order (or null)
 };
 hipError_t launch_summarize(const Plan& pl, int dtype, const CSet& ks, const void* V, KStats st_,
                             hipStream_t st);
@@ -45,7 +50,7 @@ struct AttnBufs {
   CSet qs, ks;            // query / key clustering (labels, perm, offs, cent)
   KStats kst;
   int32_t* R;             // [B*Hq][P][C][k1w]
-  float* T;               // [B*Hq][P][C][D][Cp32] tilted summaries (I, d, c)
+  void* T;                // [B*Hq][P][C][D][Cp32] T_Ic / n_c in the input dtype (I, d, c)
   int32_t Cp32;           // C rounded up to 32
   float* oacc;            // causal running output [B*Hq][N][D] (fp32)
   float* lacc;            // causal running lse [B*Hq][N]

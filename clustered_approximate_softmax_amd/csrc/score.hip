@@ -39,20 +39,31 @@ __global__ void __launch_bounds__(256) score_topk_kernel(Plan pl, AttnBufs b) {
   float sig[4];
   bool sel[4];
   int nvalid = 0;
+  int ncs[4];
+  float dots[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int c = lane + 64 * r;
+    ncs[r] = c < Ck ? koffs[c + 1] - koffs[c] : 0;
+  }
+  // nu_I is read by every lane (same addresses), mu_c by its own lane
+  for (int e = 0; e < D; e += 4) {
+    const f32x4 nv = *reinterpret_cast<const f32x4*>(nu + e);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (ncs[r] > 0) {
+        const f32x4 mv = *reinterpret_cast<const f32x4*>(b.kst.mu + (kp * C + lane + 64 * r) * D + e);
+        dots[r] = fmaf(nv[0], mv[0], fmaf(nv[1], mv[1], fmaf(nv[2], mv[2], fmaf(nv[3], mv[3], dots[r]))));
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
     sig[r] = -INFINITY;
     sel[r] = false;
-    if (c < Ck) {
-      const int nc = koffs[c + 1] - koffs[c];
-      if (nc > 0) {
-        const float* mu = b.kst.mu + (kp * C + c) * D;
-        float d = 0.f;
-        for (int e = 0; e < D; ++e) d = fmaf(nu[e], mu[e], d);
-        sig[r] = s * d + logf((float)nc);
-        nvalid++;
-      }
+    if (ncs[r] > 0) {
+      sig[r] = s * dots[r] + logf((float)ncs[r]);
+      nvalid++;
     }
   }
   for (int m = 32; m >= 1; m >>= 1) nvalid += __shfl_xor(nvalid, m, 64);
@@ -103,7 +114,7 @@ hipError_t launch_score_topk(const Plan& pl, const AttnBufs& b, hipStream_t st) 
 // One workgroup per (attention problem, value dim d).  For fixed d this is
 // a (clusters c) x (query clusters I) product over the key dim e.
 // ---------------------------------------------------------------------------
-template <int D, int NS>
+template <typename TIn, int D, int NS>
 __global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b) {
   const int C = pl.C, Cp = b.Cp32;
   const int d = blockIdx.x % D;
@@ -120,7 +131,8 @@ __global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b) {
   const float* Md = b.kst.M + (kp * D + d) * (size_t)C * D;      // [c][e]
   const float* S = b.kst.S + kp * C * D;                          // [c][d]
   const float* nu = b.qs.cent + (size_t)ap * C * D;               // [I][e]
-  float* T = b.T + (size_t)ap * C * D * Cp;                        // [I][d][c]
+  TIn* T = reinterpret_cast<TIn*>(b.T) + (size_t)ap * C * D * Cp;  // [I][d][c], T / n_c
+  const int32_t* koffs = b.ks.offs + kp * (C + 1);
   const int nct = (Ck + 15) / 16, nit = (Cq + 15) / 16;
   constexpr int KS = D / 32;
   for (int ct = w; ct < nct; ct += 4) {
@@ -170,20 +182,20 @@ __global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b) {
         acc = mfma_split<NS, NS>(a[k], bb, acc);
       }
       if (ir < Cq) {
-        f32x4 o;
+        TIn* dst = T + ((size_t)ir * D + d) * Cp + 16 * ct + 4 * g;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int c = 16 * ct + 4 * g + i;
-          o[i] = (c < Ck) ? S[(size_t)c * D + d] + s * acc[i] : 0.f;
+          const int nc = c < Ck ? koffs[c + 1] - koffs[c] : 0;
+          store1<TIn>(dst + i, nc > 0 ? (S[(size_t)c * D + d] + s * acc[i]) / (float)nc : 0.f);
         }
-        *reinterpret_cast<f32x4*>(T + ((size_t)ir * D + d) * Cp + 16 * ct + 4 * g) = o;
       }
     }
   }
   // zero the padding columns [16*nct, Cp) so consumers may read whole 32-wide chunks
   for (int idx = threadIdx.x; idx < Cq * (Cp - 16 * nct); idx += 256) {
     const int I = idx / (Cp - 16 * nct), c = 16 * nct + idx % (Cp - 16 * nct);
-    T[((size_t)I * D + d) * Cp + c] = 0.f;
+    store1<TIn>(T + ((size_t)I * D + d) * Cp + c, 0.f);
   }
 }
 
@@ -192,11 +204,11 @@ hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t
   if (grid == 0) return hipSuccess;
   MUSE_KT_PRE(st);
   if (dtype == 1) {
-    if (pl.D == 64) tilt_kernel<64, 1><<<(unsigned)grid, 256, 0, st>>>(pl, b);
-    else tilt_kernel<128, 1><<<(unsigned)grid, 256, 0, st>>>(pl, b);
+    if (pl.D == 64) tilt_kernel<uint16_t, 64, 1><<<(unsigned)grid, 256, 0, st>>>(pl, b);
+    else tilt_kernel<uint16_t, 128, 1><<<(unsigned)grid, 256, 0, st>>>(pl, b);
   } else {
-    if (pl.D == 64) tilt_kernel<64, 3><<<(unsigned)grid, 256, 0, st>>>(pl, b);
-    else tilt_kernel<128, 3><<<(unsigned)grid, 256, 0, st>>>(pl, b);
+    if (pl.D == 64) tilt_kernel<float, 64, 3><<<(unsigned)grid, 256, 0, st>>>(pl, b);
+    else tilt_kernel<float, 128, 3><<<(unsigned)grid, 256, 0, st>>>(pl, b);
   }
   MUSE_KT_POST("tilt", st);
   return hipGetLastError();

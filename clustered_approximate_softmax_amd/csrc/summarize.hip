@@ -49,8 +49,13 @@ __global__ void __launch_bounds__(SU_NT) summarize_kernel(Plan pl, CSet ks, cons
   const int32_t* offs = ks.offs + (size_t)hp * (C + 1);
   const int beg = c < Ceff ? offs[c] : 0;
   const int cnt = c < Ceff ? offs[c + 1] - beg : 0;
+  TIn* mu_in = out.mu_in ? reinterpret_cast<TIn*>(out.mu_in) + ((size_t)hp * C + c) * D : nullptr;
   if (cnt == 0) {
-    for (int e = tid; e < D; e += SU_NT) { mu[e] = 0.f; S[e] = 0.f; }
+    for (int e = tid; e < D; e += SU_NT) {
+      mu[e] = 0.f;
+      S[e] = 0.f;
+      if (mu_in) store1<TIn>(mu_in + e, 0.f);
+    }
     for (int idx = tid; idx < D * D; idx += SU_NT) {
       const int d = idx / D, e = idx % D;
       M[((size_t)d * C + c) * D + e] = 0.f;
@@ -60,6 +65,10 @@ __global__ void __launch_bounds__(SU_NT) summarize_kernel(Plan pl, CSet ks, cons
   const int32_t* perm = ks.perm + ((size_t)lev * ks.heads + head) * pl.N + r0;
   const TIn* K = reinterpret_cast<const TIn*>(ks.X) + (size_t)head * pl.N * D;
   const TIn* V = reinterpret_cast<const TIn*>(Vv) + (size_t)head * pl.N * D;
+  // cluster-contiguous copies: sorted position q of the problem -> row r0 + q
+  const size_t cbase = (((size_t)lev * ks.heads + head) * pl.N + r0 + beg) * D;
+  TIn* Kp = out.Kp ? reinterpret_cast<TIn*>(out.Kp) + cbase : nullptr;
+  TIn* Vp = out.Vp ? reinterpret_cast<TIn*>(out.Vp) + cbase : nullptr;
 
   f32x4 acc[U];
 #pragma unroll
@@ -80,6 +89,19 @@ __global__ void __launch_bounds__(SU_NT) summarize_kernel(Plan pl, CSet ks, cons
       if (row >= 0) {
         load8_f32<TIn>(K + (size_t)row * D + e0, kv);
         load8_f32<TIn>(V + (size_t)row * D + e0, vv);
+        if (Kp) {
+          TIn* kd = Kp + (size_t)(t0 + key) * D + e0;
+          TIn* vd = Vp + (size_t)(t0 + key) * D + e0;
+          if constexpr (sizeof(TIn) == 2) {
+            *reinterpret_cast<u16x8*>(kd) = *reinterpret_cast<const u16x8*>(K + (size_t)row * D + e0);
+            *reinterpret_cast<u16x8*>(vd) = *reinterpret_cast<const u16x8*>(V + (size_t)row * D + e0);
+          } else {
+            *reinterpret_cast<f32x4*>(kd) = f32x4{kv[0], kv[1], kv[2], kv[3]};
+            *reinterpret_cast<f32x4*>(kd + 4) = f32x4{kv[4], kv[5], kv[6], kv[7]};
+            *reinterpret_cast<f32x4*>(vd) = f32x4{vv[0], vv[1], vv[2], vv[3]};
+            *reinterpret_cast<f32x4*>(vd + 4) = f32x4{vv[4], vv[5], vv[6], vv[7]};
+          }
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) { kv[j] = 0.f; vv[j] = 0.f; }
@@ -128,6 +150,7 @@ __global__ void __launch_bounds__(SU_NT) summarize_kernel(Plan pl, CSet ks, cons
   for (int e = tid; e < D; e += SU_NT) {
     mu[e] = fs[e] * inv;
     S[e] = fs[D + e];
+    if (mu_in) store1<TIn>(mu_in + e, fs[e] * inv);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {

@@ -42,7 +42,7 @@ class muse_cfg(ctypes.Structure):
 
 LAYOUT_FIELDS = ["P", "L", "C", "k1w", "Cp32"]
 LAYOUT_OFFS = ["q_labels", "k_labels", "q_perm", "k_perm", "q_offs", "k_offs", "q_cent", "k_cent",
-               "mu", "S", "M", "R", "state_bytes", "ws_T", "ws_oacc", "ws_lacc", "ws_part",
+               "mu", "S", "M", "R", "Kp", "Vp", "mu_in", "state_bytes", "ws_T", "ws_oacc", "ws_lacc", "ws_part",
                "ws_pcnt", "ws_bytes"]
 
 

@@ -76,7 +76,7 @@ typedef struct {
  * Byte offsets of the arrays held in the `state` buffer that museattn_fwd
  * fills and museattn_bwd reads (the fixed assignments of the backward).
  * P = problems per head (1 when acausal), L = levels (1 when acausal),
- * C = cq, k1w = max(1, min(topk, C)).
+ * C = cq, k1w = max(1, min(topk, C)), Cp32 = C rounded up to a multiple of 64.
  *   q_labels  int32 [L][B*Hq][N]      query cluster of each row per level
  *   k_labels  int32 [L][B*Hkv][N]
  *   q_perm    int32 [L][B*Hq][N]      per problem, sorted position -> row
@@ -90,15 +90,20 @@ typedef struct {
  *   S         fp32  [B*Hkv][P][C][D]  value sums
  *   M         fp32  [B*Hkv][P][D][C][D] dipoles, index (value dim, c, key dim)
  *   R         int32 [B*Hq][P][C][k1w] retrieved clusters, ascending, -1 pad
+ *   Kp, Vp    dtype [L][B*Hkv][N][D]  keys / values of each key problem in
+ *                                      cluster-contiguous order (slot r0 + q
+ *                                      holds the row at sorted position q)
+ *   mu_in     dtype [B*Hkv][P][C][D]  mu rounded to the input dtype
  * Problem p of a head: level l and segment t in level-major order (see
  * muse_plan).  Counts are k_offs[c+1] - k_offs[c].
  */
 typedef struct {
   int64_t P, L, C, k1w, Cp32;
   size_t q_labels, k_labels, q_perm, k_perm, q_offs, k_offs, q_cent, k_cent, mu, S, M, R;
+  size_t Kp, Vp, mu_in;
   size_t state_bytes;
   /* workspace arrays (scratch; valid after museattn_fwd until the next call) */
-  size_t ws_T;      /* fp32 [B*Hq][P][C][D][Cp32] tilted summaries (I, d, c) */
+  size_t ws_T;      /* dtype [B*Hq][P][C][D][Cp32] T_Ic / n_c, index (I, d, c) */
   size_t ws_oacc;   /* fp32 [B*Hq][N][D] causal running output */
   size_t ws_lacc;   /* fp32 [B*Hq][N] causal running lse */
   size_t ws_part;   /* k-means chunk partial sums */
@@ -152,7 +157,8 @@ int musecluster(const void* X, muse_dtype dtype, int64_t G, int64_t n, int64_t D
  * musesummarize - monopole and dipole statistics of given key clusters
  * ([NEWX]: centroid approximation plus dipole correction).
  *   K, V      [G, n, D] keys and values (dtype)
- *   assign    int32 [G, n] cluster of each key, in [0, min(C, n))
+ *   assign    int32 [G, n] cluster of each key, in [0, min(C, n)); values
+ *             outside that range are clamped into it
  *   perm      int32 [G, n] out: stable cluster-contiguous order
  *   offs      int32 [G, C+1] out: segment starts; n_c = offs[c+1] - offs[c]
  *   mu        fp32 [G, C, D] out: mu_c = mean of the keys of c (0 if empty)
