@@ -56,7 +56,7 @@ def kernel_models(w, M, st, rows):
     koffs = st.field("k_offs").cpu().numpy()
     R = st.field("R").cpu().numpy()
     BHq, BHk = w.B * w.Hq, w.B * w.Hkv
-    sizes = [(r[3], r[5]) for r in rows]     # (kn, qn)
+    sizes = [(int(r[3]), int(r[5])) for r in rows]     # (kn, qn)
     pts_q = sum(qn for _, qn in sizes) * BHq
     pts_k = sum(kn for kn, _ in sizes) * BHk
     km = {}
@@ -67,18 +67,16 @@ def kernel_models(w, M, st, rows):
     large = large_q + large_k
     km["km_local"] = (2.0 * small * C * D * T, small * D * eb * T, "mfma")
     km["km_assign"] = (2.0 * large * C * D * T, large * D * eb * T, "mfma")
-    ret = 0.0
-    far = 0.0
-    for bh in range(BHq):
-        g = (bh % w.Hq) * w.Hkv // w.Hq + (bh // w.Hq) * w.Hkv
-        for p, (kn, qn) in enumerate(sizes):
-            cnt = np.diff(koffs[g, p])
-            m = np.diff(qoffs[bh, p])
-            nz = int((cnt > 0).sum())
-            for I in np.nonzero(m > 0)[0]:
-                sel = [c for c in R[bh, p, I] if c >= 0]
-                ret += m[I] * sum(int(cnt[c]) for c in sel)
-                far += m[I] * (nz - len(sel))
+    # retrieved keys and far clusters summed over every query of every problem
+    m = np.diff(qoffs, axis=-1).astype(np.float64)                       # [BHq, P, C]
+    kvmap = np.array([(bh // w.Hq) * w.Hkv + (bh % w.Hq) * w.Hkv // w.Hq for bh in range(BHq)])
+    cnt = np.diff(koffs, axis=-1)[kvmap].astype(np.float64)              # [BHq, P, C]
+    Rc = np.clip(R, 0, None)
+    rsz = np.take_along_axis(cnt[:, :, None, :].repeat(R.shape[2], 2), Rc, axis=3) * (R >= 0)
+    ret = float((m * rsz.sum(-1)).sum())
+    nz = (cnt > 0).sum(-1)                                               # [BHq, P]
+    nsel = (R >= 0).sum(-1)                                              # [BHq, P, C]
+    far = float((m * (nz[:, :, None] - nsel)).sum())
     attn_flops = 2.0 * (ret + far) * (D + D)
     attn_bytes = (pts_q * D * eb * 2) + ret / max(1, pts_q) * 0  # Q in, O out
     name = "attn_level" if w.causal else "attn_far_retrieve"

@@ -224,11 +224,14 @@ class ProblemResult:
 
 
 def solve_problem(Q, K, V, s, Cq, Ck, k1, iters, init_q=None, init_k=None,
-                  aq=None, ak=None, R=None, dipole=True):
+                  aq=None, ak=None, R=None, dipole=True, qrows=None):
     """One acausal MuSe problem: queries Q [n_q, D] against keys K, V.
 
     aq/ak/R, when given, replace the clustering and the retrieval (the
     shared-state comparison with the GPU); otherwise they are computed.
+    qrows, when given, limits the per-query outputs to those rows (every
+    cluster statistic is still taken over the whole problem); the other
+    rows of o and lse stay zero.
     """
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
@@ -250,13 +253,22 @@ def solve_problem(Q, K, V, s, Cq, Ck, k1, iters, init_q=None, init_k=None,
     if R is None:
         R = [select_topk(sig[I], k1) if m[I] > 0 else np.zeros(0, np.int64)
              for I in range(Cq)]
-    T = tilted_summaries(S, M, nu, s, dipole)
+    want = None if qrows is None else np.zeros(nq, bool)
+    if want is not None:
+        want[np.asarray(qrows, np.int64)] = True
+    need = None if want is None else sorted(set(aq[want].tolist()))
+    if need is None:
+        T = tilted_summaries(S, M, nu, s, dipole)
+    else:
+        T = np.zeros((Cq, Ck, S.shape[1]))
+        if need:
+            T[need] = tilted_summaries(S, M, nu[need], s, dipole)
 
     Dv = V.shape[1]
     o = np.zeros((nq, Dv))
     lse = np.zeros(nq)
     for I in range(Cq):
-        rows = np.nonzero(aq == I)[0]
+        rows = np.nonzero((aq == I) if want is None else ((aq == I) & want))[0]
         if len(rows) == 0:
             continue
         retrieved = [int(c) for c in R[I]]
@@ -315,20 +327,31 @@ def merge_partials(parts):
     lses = np.stack([p[1] for p in parts])
     top = np.max(lses, axis=0)
     top = np.where(np.isfinite(top), top, 0.0)
-    w = np.exp(lses - top)
-    tot = w.sum(axis=0)
-    o = sum(w[k][:, None] * parts[k][0] for k in range(len(parts))) / tot[:, None]
-    return o, top + np.log(tot)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        w = np.exp(lses - top)
+        tot = w.sum(axis=0)
+        o = sum(w[k][:, None] * parts[k][0] for k in range(len(parts))) / tot[:, None]
+        return o, top + np.log(tot)
 
 
-def local_causal(Q, K, V, s, Bblk):
-    """Exact attention of row i over keys [Bblk floor(i/Bblk), i]."""
+def local_causal(Q, K, V, s, Bblk, qrows=None):
+    """Exact attention of row i over keys [Bblk floor(i/Bblk), i] (only the
+    rows in qrows when given)."""
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
     N = Q.shape[0]
     o = np.zeros((N, V.shape[1]))
     lse = np.zeros(N)
+    if qrows is not None:
+        for i in np.asarray(qrows, np.int64):
+            b0 = (i // Bblk) * Bblk
+            lg = s * (K[b0:i + 1] @ Q[i])
+            mx = lg.max()
+            p = np.exp(lg - mx)
+            o[i] = (p @ V[b0:i + 1]) / p.sum()
+            lse[i] = mx + math.log(p.sum())
+        return o, lse
     for b0 in range(0, N, Bblk):
         b1 = min(b0 + Bblk, N)
         logits = s * (Q[b0:b1] @ K[b0:b1].T)
@@ -342,11 +365,13 @@ def local_causal(Q, K, V, s, Bblk):
     return o, lse
 
 
-def forward_head(Qh, Kh, Vh, cfg: MuseConfig, inits=None, shared=None):
+def forward_head(Qh, Kh, Vh, cfg: MuseConfig, inits=None, shared=None, qrows=None):
     """MuSe for one query head against its KV head: [N, D] each.
 
     inits:  optional dict problem_index -> (init_q, init_k)
     shared: optional dict problem_index -> (aq, ak, R) from another run
+    qrows:  optional absolute query rows; only their outputs are computed
+            and problems holding none of them are skipped (None results)
     Returns (o, lse, list of ProblemResult).
     """
     N, D = Qh.shape
@@ -355,19 +380,26 @@ def forward_head(Qh, Kh, Vh, cfg: MuseConfig, inits=None, shared=None):
     parts_o = np.zeros((len(plan), N, Vh.shape[1]))
     parts_l = np.full((len(plan), N), -np.inf)
     results = []
+    qset = None if qrows is None else np.asarray(sorted(set(int(i) for i in qrows)), np.int64)
     for p, pr in enumerate(plan):
         q0, qn, k0, kn = pr["q0"], pr["qn"], pr["k0"], pr["kn"]
         iq, ik = (inits or {}).get(p, (None, None))
         aq, ak, R = (shared or {}).get(p, (None, None, None))
+        sub = None
+        if qset is not None:
+            sub = qset[(qset >= q0) & (qset < q0 + qn)] - q0
+            if len(sub) == 0:
+                results.append(None)
+                continue
         r = solve_problem(Qh[q0:q0 + qn], Kh[k0:k0 + kn], Vh[k0:k0 + kn], s,
                           cfg.cq, cfg.ck, cfg.topk, cfg.iters, iq, ik, aq, ak, R,
-                          cfg.dipole)
+                          cfg.dipole, qrows=sub)
         parts_o[p, q0:q0 + qn] = r.o
         parts_l[p, q0:q0 + qn] = r.lse
         results.append(r)
     if not cfg.causal:
         return parts_o[0], parts_l[0], results
-    lo, ll = local_causal(Qh, Kh, Vh, s, cfg.block)
+    lo, ll = local_causal(Qh, Kh, Vh, s, cfg.block, qrows=qset)
     o, lse = merge_partials([(lo, ll)] + [(parts_o[p], parts_l[p]) for p in range(len(plan))])
     return o, lse, results
 

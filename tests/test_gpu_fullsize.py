@@ -1,0 +1,91 @@
+"""GPU parity at the workloads' full sizes (acausal 8k; causal 16k and 64k,
+D = 64 and 128), in the launch configuration bench.py times.
+
+The GPU runs the whole workload; the oracle then recomputes, from the GPU's
+assignments and retrieval sets, the outputs of sampled (batch, head) pairs
+and query rows (every cluster statistic of the problems involved is taken
+over the whole problem).  Retrieval sets must be valid top-k1 sets of the
+oracle's scores, centroids must be the mean of the GPU's members, and the
+permutation and segment offsets must be bit-exact."""
+import numpy as np
+import pytest
+
+from clustered_approximate_softmax_amd import muse as M
+from clustered_approximate_softmax_amd import synth
+from oracle import muse_oracle as mo
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_full(name, heads, nrows):
+    import torch
+    w = synth.WORKLOADS[name]
+    x = synth.make_inputs(w, with_do=False)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    Q, K, V = (torch.from_numpy(x[k]).to(tdt).cuda() for k in "QKV")
+    cfg = M.make_cfg(w.C, w.iters, w.topk, w.causal, w.block)
+    O, lse, st = M.museattn_fwd(Q, K, V, cfg)
+    torch.cuda.synchronize()
+    rows_plan = M.plan(w.N, cfg)
+    ocfg = mo.MuseConfig(cq=w.C, ck=w.C, iters=w.iters, topk=w.topk, block=w.block, causal=w.causal)
+    ql, kl, R = (st.field(f).cpu().numpy() for f in ("q_labels", "k_labels", "R"))
+    koffs, qoffs, kperm = (st.field(f).cpu().numpy() for f in ("k_offs", "q_offs", "k_perm"))
+    kcent, mu = st.field("k_cent").cpu().numpy(), st.field("mu").cpu().numpy()
+    rng = np.random.default_rng(7)
+    report = []
+    for (b, h) in heads:
+        g = (h * w.Hkv) // w.Hq
+        bh, bg = b * w.Hq + h, b * w.Hkv + g
+        qrows = np.sort(rng.choice(w.N, nrows, replace=False))
+        shared = {}
+        for p, (lev, t, k0, kn, q0, qn) in enumerate(rows_plan):
+            Cq = min(w.C, qn)
+            Rp = [np.array(sorted(c for c in R[bh, p, I] if c >= 0), np.int64) for I in range(Cq)]
+            shared[p] = (ql[lev, bh, q0:q0 + qn].astype(np.int64), kl[lev, bg, k0:k0 + kn].astype(np.int64), Rp)
+        Qh, Kh, Vh = x["Q"][b, h], x["K"][b, g], x["V"][b, g]
+        o_ref, l_ref, res = mo.forward_head(Qh, Kh, Vh, ocfg, shared=shared, qrows=qrows)
+        Og = O[b, h].float().cpu().numpy()
+        err = gu.max_rel(Og[qrows], o_ref[qrows])
+        assert err <= gu.TOL[w.dtype], (name, b, h, err)
+        np.testing.assert_allclose(lse[b, h].cpu().numpy()[qrows], l_ref[qrows], atol=50 * gu.TOL[w.dtype])
+        # retrieval validity, integer outputs and centroids of the problems touched
+        for p, r in enumerate(res):
+            if r is None:
+                continue
+            lev, t, k0, kn, q0, qn = rows_plan[p]
+            gu.check_retrieval({(b, h): [r]}, {(b, h): [shared[p]]}, w.topk)
+            ak = shared[p][1]
+            Ck = min(w.C, kn)
+            assert np.array_equal(kperm[lev, bg, k0:k0 + kn], k0 + np.argsort(ak, kind="stable"))
+            cnt = np.bincount(ak, minlength=w.C)[: w.C]
+            assert np.array_equal(koffs[bg, p], np.concatenate([[0], np.cumsum(cnt)]))
+            Kp = Kh[k0:k0 + kn].astype(np.float64)
+            for c in np.nonzero(cnt[:Ck])[0][:8]:
+                want = Kp[ak == c].mean(0)
+                np.testing.assert_allclose(mu[bg, p, c], want, atol=3e-6 * max(1.0, np.abs(Kp).max()))
+                np.testing.assert_allclose(kcent[bg, p, c], want, atol=3e-6 * max(1.0, np.abs(Kp).max()))
+        o_ex, _ = mo.exact_attention(Qh[qrows], Kh, Vh, ocfg.s(w.D)) if not w.causal else (None, None)
+        if w.causal:
+            o_ex = np.stack([mo.exact_attention(Qh[i:i + 1], Kh[:i + 1], Vh[:i + 1], ocfg.s(w.D))[0][0]
+                             for i in qrows])
+        rse = float(np.sum((Og[qrows] - o_ex) ** 2) / np.sum(o_ex ** 2))
+        report.append((b, h, err, rse))
+    print(name, "max rel err vs oracle / RSE vs exact per sampled head:", report)
+    return report
+
+
+def test_full_c2_acausal_8k():
+    _run_full("c2", [(0, 0), (0, 7)], 2048)
+
+
+def test_full_c3_causal_16k_batch4():
+    _run_full("c3", [(0, 0), (3, 7)], 256)
+
+
+def test_full_c4_causal_64k_gqa_d64():
+    _run_full("c4", [(0, 0), (0, 31)], 96)
+
+
+def test_full_c5_causal_64k_gqa_d128_forward():
+    _run_full("c5", [(0, 5)], 64)

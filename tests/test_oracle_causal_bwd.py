@@ -140,3 +140,14 @@ def test_backward_causal_all_retrieved_equals_causal_softmax_gradient():
     np.testing.assert_allclose(dQ[0], q.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dK[0, 0], k.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dV[0, 0], v.grad.numpy(), atol=1e-12)
+
+
+def test_row_restricted_forward_equals_full_forward():
+    Q, K, V, _ = _rand(9, Hq=1, Hkv=1, N=90, D=4)
+    cfg = mo.MuseConfig(cq=3, ck=4, iters=3, topk=1, block=8, causal=True)
+    o, l, _ = mo.forward_head(Q[0, 0], K[0, 0], V[0, 0], cfg)
+    rows = [0, 7, 8, 33, 64, 89]
+    o2, l2, res = mo.forward_head(Q[0, 0], K[0, 0], V[0, 0], cfg, qrows=rows)
+    np.testing.assert_allclose(o2[rows], o[rows], atol=1e-13)
+    np.testing.assert_allclose(l2[rows], l[rows], atol=1e-13)
+    assert any(r is None for r in res)
