@@ -1,0 +1,1199 @@
+// Backward of the MuSe forward with the cluster assignments, retrieval sets
+// and counts held fixed (the differentiable path of the two-stage attention:
+// gist.science page, Technical Summary, Core Mechanisms; newx.sg page,
+// Abstract: monopole + dipole summaries, causal hierarchy).
+//
+// A far-field item (cluster c seen from query cluster I) behaves exactly
+// like a key with row mu_c, value T_Ic / n_c and log-weight ln n_c, so the
+// softmax-backward formulas give, per query i and item x with
+// p = exp(logit - lse_i) and dl = p (dO_i . value_x - Delta_i):
+//   dq_i += s sum_x dl k_x;  "dk_x" = s sum_i dl q_i;  "dv_x" = sum_i p dO_i.
+// For a far item, "dk" is the gradient of mu_c through its logits and
+// "dv" / n_c is dT_Ic.  The summaries are then differentiated through
+// T_Ic = S_c + s M_c nu_I, S_c = sum v_j, M_c = sum v_j (k_j - mu_c)^T,
+// mu_c = mean k_j and nu_I = mean q_i.
+//
+// Kernels, per causal level in order (every output row is owned by one
+// workgroup per launch, so there are no atomics and the result does not
+// depend on scheduling):
+//   bwd_q       query-centric: dq_i over far, retrieved and local items
+//   bwd_kv      item-centric: dk, dv of retrieved keys (gathered over every
+//               query cluster of the query-head group that retrieved them),
+//               of local causal blocks, and dT / mu-gradient partials of the
+//               far items of each query cluster
+//   reduce_k    dS_c = sum_I dT_Ic, dmu_c (far logits) per key cluster
+//   gemm dM     dM_c = s sum_I dT_Ic nu_I^T         (split-bf16 MFMA)
+//   gemm dnu    dnu_I = s sum_c M_c^T dT_Ic          (split-bf16 MFMA)
+//   spread_q    dq_i += dnu_I / m_I
+//   bcast_k     dk_j += dM_c^T (v_j - S_c/n_c) + dmu_c / n_c,
+//               dv_j += dS_c + dM_c (k_j - mu_c)
+#include "common.h"
+#include "launch.h"
+
+namespace muse {
+
+constexpr float B_LOG2E = 1.4426950408889634f;
+constexpr int QB = 32;   // queries per tile in the item-centric kernel
+
+template <typename TIn>
+struct BwdTraits {
+  static constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;   // bf16 parts per operand
+  static constexpr int BT = sizeof(TIn) == 2 ? 64 : 32; // items per query-centric tile
+};
+
+__device__ __forceinline__ uint32_t b_pk_bf16(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 floats (contraction slots in order) -> NS bf16 parts
+template <int NS>
+__device__ __forceinline__ void pack8(const float* x, u16x8* out) {
+  if constexpr (NS == 1) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 w = {b_pk_bf16(x[0], x[1]), b_pk_bf16(x[2], x[3]), b_pk_bf16(x[4], x[5]), b_pk_bf16(x[6], x[7])};
+    out[0] = __builtin_bit_cast(u16x8, w);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint16_t h, m, l;
+      split3(x[j], h, m, l);
+      out[0][j] = h;
+      out[1][j] = m;
+      if (NS > 2) out[2][j] = l;
+    }
+  }
+}
+
+template <int NS>
+__device__ __forceinline__ void zero8(u16x8* out) {
+#pragma unroll
+  for (int sp = 0; sp < NS; ++sp)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[sp][j] = 0;
+}
+
+// position of item r (0..31 of a 32-item block) in contraction-slot order
+__device__ __forceinline__ int slot_of(int r) {
+  return r < 16 ? 8 * (r / 4) + (r % 4) : 8 * ((r - 16) / 4) + 4 + (r % 4);
+}
+
+// wave-0 scan over per-cluster tile counts: the (cluster, tile) of `slot`.
+// sel[0] = cluster, sel[1] = tile within it, sel[2] = total tiles.
+__device__ __forceinline__ void find_slot(const int32_t* offs, int Cn, int tile, int slot, int* sel) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    int v[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = tid * 4 + q;
+      v[q] = c < Cn ? (offs[c + 1] - offs[c] + tile - 1) / tile : 0;
+      sum += v[q];
+    }
+    int inc = sum;
+    for (int mm = 1; mm < 64; mm <<= 1) {
+      const int o = __shfl_up(inc, mm, 64);
+      if (tid >= mm) inc += o;
+    }
+    int run = inc - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = tid * 4 + q;
+      if (c < Cn && v[q] > 0 && slot >= run && slot < run + v[q]) {
+        sel[0] = c;
+        sel[1] = slot - run;
+      }
+      run += v[q];
+    }
+    if (tid == 63) sel[2] = inc;
+  }
+}
+
+struct BwdArgs {
+  Plan pl;
+  AttnBufs a;
+  const void* dO;
+  const float* lse;
+  float* delta;   // [B*Hq][N]
+  float* dq;      // [B*Hq][N][D]   fp32 accumulators
+  float* dk;      // [B*Hkv][N][D]
+  float* dv;
+  // per-level buffers; lp = bh * nseg + t, kl = kvh * nseg + t
+  float* dT;      // [lp][C][D][C]   (I, d, c): sum_i p dO_i / n_c over far items
+  float* G;       // [lp][C][C][D]   (I, c, e): s sum_i dl q_i over far items
+  float* dnu;     // [lp][C][D]
+  float* dS;      // [kl][C][D]
+  float* dmu;     // [kl][C][D]
+  float* dM;      // [kl][D][C][D]   (d, c, e)
+};
+
+// ===========================================================================
+// Delta_i = dO_i . O_i ; zero fill ; fp32 -> output dtype
+// ===========================================================================
+template <typename TIn>
+__global__ void bwd_delta_kernel(const TIn* O, const TIn* dO, float* delta, long long rows, int D) {
+  const long long r = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  float s = 0.f;
+  for (int e = 0; e < D; e += 8) {
+    float a[8], b[8];
+    load8_f32<TIn>(O + r * D + e, a);
+    load8_f32<TIn>(dO + r * D + e, b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s = fmaf(a[j], b[j], s);
+  }
+  delta[r] = s;
+}
+
+__global__ void bwd_zero_kernel(float* p, long long n) {
+  const long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i + 3 < n) *reinterpret_cast<f32x4*>(p + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+  else for (long long k = i; k < n; ++k) p[k] = 0.f;
+}
+
+template <typename TOut>
+__global__ void bwd_out_kernel(const float* src, TOut* dst, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) store1<TOut>(dst + i, src[i]);
+}
+
+// ===========================================================================
+// Query-centric kernel: 64 queries (4 waves x 16) against tiles of BT items.
+// S^T = K Q^T and dP^T = V dO^T (items as rows), dS^T = P^T (dP^T - Delta),
+// dQ^T += K^T dS^T.
+// ===========================================================================
+enum { BQ_PROBLEM = 0, BQ_LOCAL = 1 };
+
+template <typename TIn, int D>
+struct alignas(16) BqSmem {
+  static constexpr int NS = BwdTraits<TIn>::NS, BT = BwdTraits<TIn>::BT;
+  uint16_t ks[NS][BT][D + 8];    // K rows
+  uint16_t vs[NS][BT][D + 8];    // V rows
+  uint16_t kt[NS][D][BT + 8];    // K^T in contraction-slot order
+  float bias[BT];
+  int32_t irow[BT];              // item -> source row, -1 if none
+  int32_t qrow[64];
+  float far_bias[MUSE_MAXC];
+  int32_t rbeg[MUSE_MAXC];
+  int32_t rcum[MUSE_MAXC + 1];
+  int32_t sel[4];
+};
+
+// Stage BT items: rows of K and V, and K^T.  Far items: rows of mu_c and
+// columns of T / n_c (stored (d, c)).
+template <typename TIn, int D>
+__device__ __forceinline__ void bq_stage(BqSmem<TIn, D>& sm, bool far, const TIn* Kb, const TIn* Vb,
+                                         const TIn* mu, const TIn* T, int Cp, int c0, int Ck) {
+  using SM = BqSmem<TIn, D>;
+  constexpr int NS = SM::NS, BT = SM::BT;
+  for (int idx = threadIdx.x; idx < (BT / 4) * (D / 8); idx += 256) {
+    const int kb = idx % (BT / 4), e0 = (idx / (BT / 4)) * 8;
+    float kv[4][8], vv[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int it = 4 * kb + r;
+      const TIn* kp = nullptr;
+      const TIn* vp = nullptr;
+      if (far) {
+        if (c0 + it < Ck) kp = mu + (size_t)(c0 + it) * D + e0;
+      } else {
+        const int row = sm.irow[it];
+        if (row >= 0) { kp = Kb + (size_t)row * D + e0; vp = Vb + (size_t)row * D + e0; }
+      }
+      if (kp) {
+        load8_f32<TIn>(kp, kv[r]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kv[r][j] = 0.f;
+      }
+      if (!far) {
+        if (vp) {
+          load8_f32<TIn>(vp, vv[r]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vv[r][j] = 0.f;
+        }
+      }
+    }
+    if (far) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const TIn* tp = T + (size_t)(e0 + j) * Cp + c0 + 4 * kb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vv[r][j] = load1_f32<TIn>(tp + r);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int it = 4 * kb + r;
+      const int pos = 32 * (it / 32) + slot_of(it % 32);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        split_store<NS>(kv[r][j], &sm.ks[0][it][e0 + j], BT * (D + 8));
+        split_store<NS>(vv[r][j], &sm.vs[0][it][e0 + j], BT * (D + 8));
+        split_store<NS>(kv[r][j], &sm.kt[0][e0 + j][pos], D * (BT + 8));
+      }
+    }
+  }
+}
+
+template <typename TIn, int D, int MODE>
+__global__ void __launch_bounds__(256) bwd_q_kernel(BwdArgs A, int lev) {
+  using SM = BqSmem<TIn, D>;
+  constexpr int NS = SM::NS, BT = SM::BT, KS = D / 32, DT = D / 16, RT = BT / 16, PS = BT / 32;
+  extern __shared__ __align__(16) unsigned char bq_raw[];
+  SM& sm = *reinterpret_cast<SM*>(bq_raw);
+  const Plan& pl = A.pl;
+  const AttnBufs& b = A.a;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
+  const float s = pl.scale, s2 = pl.scale * B_LOG2E;
+  const int C = pl.C;
+  int bh, ap = 0, I = 0, Ck = 0, q0 = 0, k0 = 0, qlo, qhi;
+  if (MODE == BQ_LOCAL) {
+    const int nblk = (pl.N + pl.blk - 1) / pl.blk, tpb = (pl.blk + 63) / 64;
+    int id = blockIdx.x;
+    const int tile = id % tpb; id /= tpb;
+    const int blk = id % nblk;
+    bh = id / nblk;
+    k0 = blk * pl.blk;
+    qlo = k0 + tile * 64;
+    qhi = min(min(k0 + pl.blk, pl.N), qlo + 64);
+    if (qlo >= qhi) return;
+  } else {
+    const int nseg = pl.lev_nseg[lev], m = pl.lev_m[lev];
+    const int spp = (m + 63) / 64 + C;
+    int id = blockIdx.x;
+    const int slot = id % spp; id /= spp;
+    const int t = id % nseg;
+    bh = id / nseg;
+    const int p = pl.lev_pfirst[lev] + t;
+    ap = bh * pl.P + p;
+    const Geom gm = prob_geom(pl, p);
+    const int Cq = min(C, gm.qn);
+    Ck = min(C, gm.kn);
+    k0 = gm.k0;
+    q0 = gm.q0;
+    const int32_t* qoffs = b.qs.offs + (size_t)ap * (C + 1);
+    find_slot(qoffs, Cq, 64, slot, sm.sel);
+    __syncthreads();
+    if (slot >= sm.sel[2]) return;
+    I = sm.sel[0];
+    qlo = qoffs[I] + sm.sel[1] * 64;
+    qhi = min(qoffs[I + 1], qlo + 64);
+  }
+  const int kvh = (bh / pl.Hq) * pl.Hkv + ((bh % pl.Hq) * pl.Hkv) / pl.Hq;
+  const int kp = kvh * pl.P + (ap % pl.P);
+  if (tid < 64) {
+    int r = -1;
+    if (qlo + tid < qhi) {
+      if (MODE == BQ_LOCAL) r = qlo + tid;
+      else r = b.qs.perm[((size_t)lev * pl.B * pl.Hq + bh) * pl.N + q0 + qlo + tid];
+    }
+    sm.qrow[tid] = r;
+  }
+  int nfar = 0, nret = 0;
+  if (MODE != BQ_LOCAL) {
+    const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
+    const int32_t* Rr = b.R + ((size_t)ap * C + I) * pl.k1w;
+    for (int c = tid; c < MUSE_MAXC; c += 256) {
+      float bias = -INFINITY;
+      if (c < Ck) {
+        const int nc = koffs[c + 1] - koffs[c];
+        if (nc > 0) bias = __log2f((float)nc);
+      }
+      sm.far_bias[c] = bias;
+    }
+    int cc[4];
+    if (tid < 64) {
+      int v[4], bg[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = tid * 4 + q;
+        cc[q] = r < pl.k1w ? Rr[r] : -1;
+        bg[q] = cc[q] >= 0 ? koffs[cc[q]] : 0;
+        v[q] = cc[q] >= 0 ? koffs[cc[q] + 1] - bg[q] : 0;
+        sum += v[q];
+      }
+      int inc = sum;
+      for (int mm = 1; mm < 64; mm <<= 1) {
+        const int o = __shfl_up(inc, mm, 64);
+        if (tid >= mm) inc += o;
+      }
+      int run = inc - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = tid * 4 + q;
+        sm.rbeg[r] = bg[q];
+        sm.rcum[r] = run;
+        run += v[q];
+      }
+      if (tid == 63) sm.rcum[MUSE_MAXC] = inc;
+    }
+    __syncthreads();
+    // retrieved clusters leave the far field
+    if (tid < 64) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (cc[q] >= 0) sm.far_bias[cc[q]] = -INFINITY;
+    }
+    nret = sm.rcum[MUSE_MAXC];
+    nfar = (Ck + BT - 1) / BT;
+  } else {
+    nret = qhi - k0;
+  }
+  __syncthreads();
+  const TIn* Qh = reinterpret_cast<const TIn*>(b.Q) + (size_t)bh * pl.N * D;
+  const TIn* dOh = reinterpret_cast<const TIn*>(A.dO) + (size_t)bh * pl.N * D;
+  const int myq = sm.qrow[w * 16 + col];
+  u16x8 qf[KS][NS], df[KS][NS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    if (myq >= 0) {
+      load8_split<TIn, NS>(Qh + (size_t)myq * D + 32 * k + 8 * g, qf[k]);
+      load8_split<TIn, NS>(dOh + (size_t)myq * D + 32 * k + 8 * g, df[k]);
+    } else {
+      zero8<NS>(qf[k]);
+      zero8<NS>(df[k]);
+    }
+  }
+  const float lse2 = myq >= 0 ? A.lse[(size_t)bh * pl.N + myq] * B_LOG2E : 0.f;
+  const float dlt = myq >= 0 ? A.delta[(size_t)bh * pl.N + myq] : 0.f;
+  f32x4 dqt[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dqt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const TIn* Kb;
+  const TIn* Vb;
+  const TIn* mu = nullptr;
+  const TIn* T = nullptr;
+  if (MODE == BQ_LOCAL) {
+    Kb = reinterpret_cast<const TIn*>(b.K) + (size_t)kvh * pl.N * D;
+    Vb = reinterpret_cast<const TIn*>(b.V) + (size_t)kvh * pl.N * D;
+  } else {
+    const size_t kb = (((size_t)lev * pl.B * pl.Hkv + kvh) * pl.N + k0) * D;
+    Kb = reinterpret_cast<const TIn*>(b.kst.Kp) + kb;
+    Vb = reinterpret_cast<const TIn*>(b.kst.Vp) + kb;
+    mu = reinterpret_cast<const TIn*>(b.kst.mu_in) + (size_t)kp * C * D;
+    T = reinterpret_cast<const TIn*>(b.T) + ((size_t)ap * C + I) * D * b.Cp32;
+  }
+  const int nex = (nret + BT - 1) / BT;
+  for (int t = 0; t < nfar + nex; ++t) {
+    const bool far = t < nfar;
+    const int base = (far ? t : t - nfar) * BT;
+    if (tid < BT) {
+      const int it = base + tid;
+      int row = -1;
+      float bias = -INFINITY;
+      if (far) {
+        bias = it < Ck ? sm.far_bias[it] : -INFINITY;
+      } else if (MODE == BQ_LOCAL) {
+        if (it < nret) { row = k0 + it; bias = 0.f; }
+      } else if (it < nret) {
+        int r = 0;
+        while (sm.rcum[r + 1] <= it) ++r;
+        row = sm.rbeg[r] + (it - sm.rcum[r]);
+        bias = 0.f;
+      }
+      sm.irow[tid] = row;
+      sm.bias[tid] = bias;
+    }
+    __syncthreads();
+    bq_stage<TIn, D>(sm, far, Kb, Vb, mu, T, b.Cp32, base, Ck);
+    __syncthreads();
+    float ds[RT * 4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        u16x8 ak[NS], av[NS];
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) {
+          ak[sp] = *reinterpret_cast<const u16x8*>(&sm.ks[sp][16 * rt + col][32 * k + 8 * g]);
+          av[sp] = *reinterpret_cast<const u16x8*>(&sm.vs[sp][16 * rt + col][32 * k + 8 * g]);
+        }
+        sc = mfma_split<NS, NS>(ak, qf[k], sc);
+        dp = mfma_split<NS, NS>(av, df[k], dp);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int it = 16 * rt + 4 * g + i;
+        float x = fmaf(s2, sc[i], sm.bias[it]);
+        // local block: key row k0 + base + it is visible to query myq when <= myq
+        if (MODE == BQ_LOCAL && k0 + base + it > myq) x = -INFINITY;
+        const float p = myq >= 0 ? __builtin_amdgcn_exp2f(x - lse2) : 0.f;
+        ds[rt * 4 + i] = p * (dp[i] - dlt);
+      }
+    }
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps) {
+      u16x8 db[NS];
+      pack8<NS>(&ds[ps * 8], db);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        u16x8 a[NS];
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp)
+          a[sp] = *reinterpret_cast<const u16x8*>(&sm.kt[sp][16 * dt + col][32 * ps + 8 * g]);
+        dqt[dt] = mfma_split<NS, NS>(a, db, dqt[dt]);
+      }
+    }
+    __syncthreads();
+  }
+  if (myq < 0) return;
+  float* dq = A.dq + ((size_t)bh * pl.N + myq) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const f32x4 prev = *reinterpret_cast<const f32x4*>(dq + 16 * dt + 4 * g);
+    *reinterpret_cast<f32x4*>(dq + 16 * dt + 4 * g) = prev + dqt[dt] * s;
+  }
+}
+
+// ===========================================================================
+// Item-centric kernel: a workgroup owns 64 items (4 waves x 16) and streams
+// the queries that see them in tiles of QB.  S = Q K^T, dP = dO V^T (queries
+// as rows), dS = P (dP - Delta), dV^T += dO^T P, dK^T += Q^T dS.
+// ===========================================================================
+enum { BK_EXACT = 0, BK_FAR = 1, BK_LOCAL = 2 };
+
+template <typename TIn, int D>
+struct alignas(16) BkSmem {
+  static constexpr int NS = BwdTraits<TIn>::NS;
+  uint16_t qs[NS][QB][D + 8];     // Q rows
+  uint16_t os[NS][QB][D + 8];     // dO rows
+  uint16_t qt[NS][D][QB + 8];     // Q^T, slot order
+  uint16_t ot[NS][D][QB + 8];     // dO^T, slot order
+  float lse2[QB];
+  float dlt[QB];
+  int32_t qrow[QB];
+  int32_t list[256];              // (query head, query cluster) pairs retrieving the cluster
+  int32_t wc[4];
+  int32_t sel[4];
+};
+
+template <typename TIn, int D>
+__device__ __forceinline__ void bk_stage_queries(BkSmem<TIn, D>& sm, const TIn* Qh, const TIn* dOh,
+                                                 const float* lse, const float* delta) {
+  constexpr int NS = BkSmem<TIn, D>::NS;
+  for (int idx = threadIdx.x; idx < QB * (D / 8); idx += 256) {
+    const int q = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
+    const int row = sm.qrow[q];
+    float qv[8], ov[8];
+    if (row >= 0) {
+      load8_f32<TIn>(Qh + (size_t)row * D + e0, qv);
+      load8_f32<TIn>(dOh + (size_t)row * D + e0, ov);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { qv[j] = 0.f; ov[j] = 0.f; }
+    }
+    const int pos = slot_of(q);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      split_store<NS>(qv[j], &sm.qs[0][q][e0 + j], QB * (D + 8));
+      split_store<NS>(ov[j], &sm.os[0][q][e0 + j], QB * (D + 8));
+      split_store<NS>(qv[j], &sm.qt[0][e0 + j][pos], D * (QB + 8));
+      split_store<NS>(ov[j], &sm.ot[0][e0 + j][pos], D * (QB + 8));
+    }
+  }
+  if (threadIdx.x < QB) {
+    const int row = sm.qrow[threadIdx.x];
+    sm.lse2[threadIdx.x] = row >= 0 ? lse[row] * B_LOG2E : 0.f;
+    sm.dlt[threadIdx.x] = row >= 0 ? delta[row] : 0.f;
+  }
+}
+
+// One query tile against this wave's 16 items (the lane's column).
+template <typename TIn, int D, bool CAUSAL>
+__device__ __forceinline__ void bk_consume(const BkSmem<TIn, D>& sm,
+                                           const u16x8 (&kf)[D / 32][BwdTraits<TIn>::NS],
+                                           const u16x8 (&vf)[D / 32][BwdTraits<TIn>::NS], float ibias,
+                                           int irow, float s2, f32x4 (&dvt)[D / 16], f32x4 (&dkt)[D / 16]) {
+  constexpr int NS = BwdTraits<TIn>::NS, KS = D / 32, DT = D / 16;
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+  float p[8], dsv[8];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      u16x8 aq[NS], ad[NS];
+#pragma unroll
+      for (int sp = 0; sp < NS; ++sp) {
+        aq[sp] = *reinterpret_cast<const u16x8*>(&sm.qs[sp][16 * rt + col][32 * k + 8 * g]);
+        ad[sp] = *reinterpret_cast<const u16x8*>(&sm.os[sp][16 * rt + col][32 * k + 8 * g]);
+      }
+      sc = mfma_split<NS, NS>(aq, kf[k], sc);
+      dp = mfma_split<NS, NS>(ad, vf[k], dp);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 16 * rt + 4 * g + i;
+      const int qr = sm.qrow[q];
+      float x = fmaf(s2, sc[i], ibias);
+      if (qr < 0 || (CAUSAL && irow > qr)) x = -INFINITY;
+      const float pv = __builtin_amdgcn_exp2f(x - sm.lse2[q]);
+      p[rt * 4 + i] = pv;
+      dsv[rt * 4 + i] = pv * (dp[i] - sm.dlt[q]);
+    }
+  }
+  u16x8 pb[NS], db[NS];
+  pack8<NS>(p, pb);
+  pack8<NS>(dsv, db);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    u16x8 a[NS], c[NS];
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) {
+      a[sp] = *reinterpret_cast<const u16x8*>(&sm.ot[sp][16 * dt + col][8 * g]);
+      c[sp] = *reinterpret_cast<const u16x8*>(&sm.qt[sp][16 * dt + col][8 * g]);
+    }
+    dvt[dt] = mfma_split<NS, NS>(a, pb, dvt[dt]);
+    dkt[dt] = mfma_split<NS, NS>(c, db, dkt[dt]);
+  }
+}
+
+// Queries rows[qa .. qb) of head bh (rows == nullptr: rows qa .. qb themselves).
+template <typename TIn, int D, bool CAUSAL>
+__device__ __forceinline__ void bk_query_range(BkSmem<TIn, D>& sm, const BwdArgs& A, int bh, const int32_t* rows,
+                                               int qa, int qb, const u16x8 (&kf)[D / 32][BwdTraits<TIn>::NS],
+                                               const u16x8 (&vf)[D / 32][BwdTraits<TIn>::NS], float ibias,
+                                               int irow, float s2, f32x4 (&dvt)[D / 16], f32x4 (&dkt)[D / 16]) {
+  const Plan& pl = A.pl;
+  const TIn* Qh = reinterpret_cast<const TIn*>(A.a.Q) + (size_t)bh * pl.N * D;
+  const TIn* dOh = reinterpret_cast<const TIn*>(A.dO) + (size_t)bh * pl.N * D;
+  for (int q0 = qa; q0 < qb; q0 += QB) {
+    if (threadIdx.x < QB) {
+      const int q = q0 + threadIdx.x;
+      sm.qrow[threadIdx.x] = q < qb ? (rows ? rows[q] : q) : -1;
+    }
+    __syncthreads();
+    bk_stage_queries<TIn, D>(sm, Qh, dOh, A.lse + (size_t)bh * pl.N, A.delta + (size_t)bh * pl.N);
+    __syncthreads();
+    bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
+    __syncthreads();
+  }
+}
+
+template <typename TIn, int D, int KIND>
+__global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs A, int lev) {
+  using SM = BkSmem<TIn, D>;
+  constexpr int NS = SM::NS, KS = D / 32, DT = D / 16;
+  extern __shared__ __align__(16) unsigned char bk_raw[];
+  SM& sm = *reinterpret_cast<SM*>(bk_raw);
+  const Plan& pl = A.pl;
+  const AttnBufs& b = A.a;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
+  const float s = pl.scale, s2 = pl.scale * B_LOG2E;
+  const int C = pl.C, Gq = pl.Hq / pl.Hkv;
+  int bq = 0, kvh = 0, p = 0, t = 0, nseg = 1, kp = 0, Ck = 0, c = 0, ibeg = 0, iend = 0, ap = 0, I = 0;
+  int bh = 0, blk1 = 0;
+  Geom gm{};
+  if (KIND == BK_LOCAL) {
+    const int nblk = (pl.N + pl.blk - 1) / pl.blk, tpb = (pl.blk + 63) / 64;
+    int id = blockIdx.x;
+    const int tile = id % tpb; id /= tpb;
+    const int blk = id % nblk;
+    kvh = id / nblk;
+    bq = kvh / pl.Hkv;
+    const int blk0 = blk * pl.blk;
+    blk1 = min(blk0 + pl.blk, pl.N);
+    ibeg = blk0 + tile * 64;
+    iend = min(blk1, ibeg + 64);
+    if (ibeg >= iend) return;
+  } else if (KIND == BK_EXACT) {
+    nseg = pl.lev_nseg[lev];
+    const int m = pl.lev_m[lev];
+    const int spp = (m + 63) / 64 + C;
+    int id = blockIdx.x;
+    const int slot = id % spp; id /= spp;
+    t = id % nseg;
+    kvh = id / nseg;
+    bq = kvh / pl.Hkv;
+    p = pl.lev_pfirst[lev] + t;
+    kp = kvh * pl.P + p;
+    gm = prob_geom(pl, p);
+    Ck = min(C, gm.kn);
+    const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
+    find_slot(koffs, Ck, 64, slot, sm.sel);
+    __syncthreads();
+    if (slot >= sm.sel[2]) return;
+    c = sm.sel[0];
+    ibeg = koffs[c] + sm.sel[1] * 64;
+    iend = min(koffs[c + 1], ibeg + 64);
+  } else {  // BK_FAR: items are the key clusters ct*64 .. ct*64+63 seen from query cluster I
+    nseg = pl.lev_nseg[lev];
+    const int nct = (C + 63) / 64;
+    int id = blockIdx.x;
+    const int ct = id % nct; id /= nct;
+    I = id % C; id /= C;
+    t = id % nseg;
+    bh = id / nseg;
+    bq = bh / pl.Hq;
+    kvh = bq * pl.Hkv + ((bh % pl.Hq) * pl.Hkv) / pl.Hq;
+    p = pl.lev_pfirst[lev] + t;
+    ap = bh * pl.P + p;
+    kp = kvh * pl.P + p;
+    gm = prob_geom(pl, p);
+    Ck = min(C, gm.kn);
+    if (I >= min(C, gm.qn)) return;
+    ibeg = ct * 64;
+    iend = min(C, ibeg + 64);
+  }
+
+  // ---- this lane's item (wave w owns items 16w .. 16w+15) ----
+  const int item = ibeg + 16 * w + col;
+  const bool ivalid = item < iend;
+  u16x8 kf[KS][NS], vf[KS][NS];
+  float ibias = -INFINITY;
+  int irow = -1;
+  {
+    const TIn* kp_ = nullptr;
+    const TIn* vp_ = nullptr;
+    if (KIND == BK_LOCAL) {
+      if (ivalid) {
+        kp_ = reinterpret_cast<const TIn*>(b.K) + ((size_t)kvh * pl.N + item) * D;
+        vp_ = reinterpret_cast<const TIn*>(b.V) + ((size_t)kvh * pl.N + item) * D;
+        irow = item;
+        ibias = 0.f;
+      }
+    } else if (KIND == BK_EXACT) {
+      if (ivalid) {
+        const size_t kb = (((size_t)lev * pl.B * pl.Hkv + kvh) * pl.N + gm.k0 + item) * D;
+        kp_ = reinterpret_cast<const TIn*>(b.kst.Kp) + kb;
+        vp_ = reinterpret_cast<const TIn*>(b.kst.Vp) + kb;
+        irow = b.ks.perm[((size_t)lev * pl.B * pl.Hkv + kvh) * pl.N + gm.k0 + item];
+        ibias = 0.f;
+      }
+    } else if (ivalid && item < Ck) {
+      const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
+      const int nc = koffs[item + 1] - koffs[item];
+      bool ret = false;
+      const int32_t* Rr = b.R + ((size_t)ap * C + I) * pl.k1w;
+      for (int r = 0; r < pl.k1w; ++r) ret |= (Rr[r] == item);
+      if (nc > 0 && !ret) ibias = __log2f((float)nc);
+      kp_ = reinterpret_cast<const TIn*>(b.kst.mu_in) + ((size_t)kp * C + item) * D;
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      if (kp_) load8_split<TIn, NS>(kp_ + 32 * k + 8 * g, kf[k]);
+      else zero8<NS>(kf[k]);
+      if (KIND == BK_FAR) {
+        // value of a far item: column `item` of T_I / n_c, stored (d, c)
+        const TIn* T = reinterpret_cast<const TIn*>(b.T) + ((size_t)ap * C + I) * D * b.Cp32;
+        float v8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          v8[j] = kp_ ? load1_f32<TIn>(T + (size_t)(32 * k + 8 * g + j) * b.Cp32 + item) : 0.f;
+        if constexpr (NS == 1) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vf[k][0][j] = f2bf(v8[j]);
+        } else {
+          pack8<NS>(v8, vf[k]);
+        }
+      } else {
+        if (vp_) load8_split<TIn, NS>(vp_ + 32 * k + 8 * g, vf[k]);
+        else zero8<NS>(vf[k]);
+      }
+    }
+  }
+  f32x4 dvt[DT], dkt[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dvt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dkt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- the queries that see these items ----
+  if (KIND == BK_EXACT) {
+    // (query head of the group, query cluster) pairs whose retrieval set holds c,
+    // scanned in a fixed order, at most 256 per round
+    const int Cq = min(C, gm.qn);
+    const int total = Gq * Cq;
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < total; base += 256) {
+      const int e = base + tid;
+      bool hit = false;
+      if (e < total) {
+        const int hl = e / Cq, Iq = e % Cq;
+        const int bhx = bq * pl.Hq + (kvh % pl.Hkv) * Gq + hl;
+        const int32_t* Rr = b.R + (((size_t)bhx * pl.P + p) * C + Iq) * pl.k1w;
+        for (int r = 0; r < pl.k1w; ++r) hit |= (Rr[r] == c);
+      }
+      const unsigned long long bal = __ballot(hit);
+      if (lane == 0) sm.wc[w] = __popcll(bal);
+      __syncthreads();
+      int off = 0;
+      for (int q = 0; q < w; ++q) off += sm.wc[q];
+      if (hit) sm.list[off + __popcll(bal & lt)] = e;
+      const int cnt = sm.wc[0] + sm.wc[1] + sm.wc[2] + sm.wc[3];
+      __syncthreads();
+      for (int li = 0; li < cnt; ++li) {
+        const int ent = sm.list[li];
+        const int hl = ent / Cq, Iq = ent % Cq;
+        const int bhx = bq * pl.Hq + (kvh % pl.Hkv) * Gq + hl;
+        const int32_t* qoffs = b.qs.offs + ((size_t)bhx * pl.P + p) * (C + 1);
+        const int32_t* qperm = b.qs.perm + ((size_t)lev * pl.B * pl.Hq + bhx) * pl.N + gm.q0;
+        bk_query_range<TIn, D, false>(sm, A, bhx, qperm, qoffs[Iq], qoffs[Iq + 1], kf, vf, ibias, irow, s2,
+                                      dvt, dkt);
+      }
+      __syncthreads();
+    }
+  } else if (KIND == BK_FAR) {
+    const int32_t* qoffs = b.qs.offs + (size_t)ap * (C + 1);
+    const int32_t* qperm = b.qs.perm + ((size_t)lev * pl.B * pl.Hq + bh) * pl.N + gm.q0;
+    bk_query_range<TIn, D, false>(sm, A, bh, qperm, qoffs[I], qoffs[I + 1], kf, vf, ibias, -1, s2, dvt, dkt);
+  } else {
+    // local causal block: the queries from the tile's first row to the block end, every head of the group
+    for (int hl = 0; hl < Gq; ++hl) {
+      const int bhx = bq * pl.Hq + (kvh % pl.Hkv) * Gq + hl;
+      bk_query_range<TIn, D, true>(sm, A, bhx, nullptr, ibeg, blk1, kf, vf, ibias, irow, s2, dvt, dkt);
+    }
+  }
+  if (!ivalid) return;
+  // ---- outputs: lane holds dims d = 16dt + 4g + i of its item ----
+  if (KIND == BK_FAR) {
+    float inv = 0.f;
+    if (item < Ck) {
+      const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
+      const int nc = koffs[item + 1] - koffs[item];
+      inv = nc > 0 ? 1.f / (float)nc : 0.f;
+    }
+    const size_t lp = (size_t)bh * nseg + t;
+    float* dT = A.dT + (lp * C + I) * (size_t)D * C;          // (d, c)
+    float* G = A.G + ((lp * C + I) * C + item) * (size_t)D;    // (c, e)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dT[(size_t)(16 * dt + 4 * g + i) * C + item] = dvt[dt][i] * inv;
+      *reinterpret_cast<f32x4*>(G + 16 * dt + 4 * g) = dkt[dt] * s;
+    }
+  } else {
+    float* dk = A.dk + ((size_t)kvh * pl.N + irow) * D;
+    float* dv = A.dv + ((size_t)kvh * pl.N + irow) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4 pk = *reinterpret_cast<const f32x4*>(dk + 16 * dt + 4 * g);
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(dv + 16 * dt + 4 * g);
+      *reinterpret_cast<f32x4*>(dk + 16 * dt + 4 * g) = pk + dkt[dt] * s;
+      *reinterpret_cast<f32x4*>(dv + 16 * dt + 4 * g) = pv + dvt[dt];
+    }
+  }
+}
+
+// ===========================================================================
+// Batched fp32 contraction on split-bf16 MFMA: C[m][n] = sum_k A[m][k] B[k][n]
+// per batch, 64 x 64 output tile per workgroup, k in steps of 32.  The
+// problem type supplies the batch view, the element loads and the store;
+// B is read along n, A along k (A_KC) or along m.
+// ===========================================================================
+template <int NS>
+__device__ __forceinline__ void split_parts(float x, uint16_t* dst, int stride) {
+  if constexpr (NS == 1) {
+    dst[0] = f2bf(x);
+  } else {
+    uint16_t h, m, l;
+    split3(x, h, m, l);
+    dst[0] = h;
+    dst[stride] = m;
+    if (NS > 2) dst[2 * stride] = l;
+  }
+}
+
+template <class P, int NS>
+__global__ void __launch_bounds__(256) bwd_gemm_kernel(P prob) {
+  __shared__ __align__(16) uint16_t As[NS][64][40];
+  __shared__ __align__(16) uint16_t Bs[NS][64][40];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
+  int id = blockIdx.x;
+  const int tn = id % prob.ntiles; id /= prob.ntiles;
+  const int tm = id % prob.mtiles; id /= prob.mtiles;
+  typename P::View v;
+  prob.view(id, v);
+  const int m0 = tm * 64, n0 = tn * 64;
+  if (m0 >= v.M || n0 >= v.N) return;
+  f32x4 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < v.K; k0 += 32) {
+    {
+      float x[8];
+      if constexpr (P::A_KC) {
+        const int m = tid / 4, kk = (tid % 4) * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          x[j] = (m0 + m < v.M && k0 + kk + j < v.K) ? prob.a(v, m0 + m, k0 + kk + j) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) split_parts<NS>(x[j], &As[0][m][kk + j], 64 * 40);
+      } else {
+        const int kk = tid / 8, mm = (tid % 8) * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          x[j] = (m0 + mm + j < v.M && k0 + kk < v.K) ? prob.a(v, m0 + mm + j, k0 + kk) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) split_parts<NS>(x[j], &As[0][mm + j][kk], 64 * 40);
+      }
+    }
+    {
+      float x[8];
+      const int kk = tid / 8, nn = (tid % 8) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        x[j] = (n0 + nn + j < v.N && k0 + kk < v.K) ? prob.b(v, k0 + kk, n0 + nn + j) : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) split_parts<NS>(x[j], &Bs[0][nn + j][kk], 64 * 40);
+    }
+    __syncthreads();
+    u16x8 a[NS];
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) a[sp] = *reinterpret_cast<const u16x8*>(&As[sp][16 * w + col][8 * g]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u16x8 bb[NS];
+#pragma unroll
+      for (int sp = 0; sp < NS; ++sp) bb[sp] = *reinterpret_cast<const u16x8*>(&Bs[sp][16 * q + col][8 * g]);
+      acc[q] = mfma_split<NS, NS>(a, bb, acc[q]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 16 * w + 4 * g + i, n = n0 + 16 * q + col;
+      if (m < v.M && n < v.N) prob.c(v, m, n, acc[q][i]);
+    }
+}
+
+// dnu_I[e] = s sum_{d,c} dT_I[d][c] M[d][c][e]; batch = lp = bh * nseg + t
+struct GemmDnu {
+  static constexpr bool A_KC = true;
+  Plan pl;
+  int lev, mtiles, ntiles;
+  const float* dT;
+  const float* Mst;
+  float* dnu;
+  struct View { int M, N, K; const float* A; const float* B; float* C; };
+  __device__ void view(int batch, View& v) const {
+    const int nseg = pl.lev_nseg[lev];
+    const int t = batch % nseg, bh = batch / nseg;
+    const int p = pl.lev_pfirst[lev] + t;
+    const Geom gm = prob_geom(pl, p);
+    const int kvh = (bh / pl.Hq) * pl.Hkv + ((bh % pl.Hq) * pl.Hkv) / pl.Hq;
+    const size_t kp = (size_t)kvh * pl.P + p;
+    v.M = min(pl.C, gm.qn);
+    v.N = pl.D;
+    v.K = pl.D * pl.C;
+    v.A = dT + (size_t)batch * pl.C * pl.D * pl.C;
+    v.B = Mst + kp * pl.D * pl.C * pl.D;
+    v.C = dnu + (size_t)batch * pl.C * pl.D;
+  }
+  __device__ float a(const View& v, int m, int k) const { return v.A[(size_t)m * v.K + k]; }
+  __device__ float b(const View& v, int k, int n) const { return v.B[(size_t)k * pl.D + n]; }
+  __device__ void c(const View& v, int m, int n, float x) const { v.C[(size_t)m * pl.D + n] = pl.scale * x; }
+};
+
+// dM[d][c][e] = s sum_{h,I} dT_{h,I}[d][c] nu_{h,I}[e]; batch = kl = kvh * nseg + t
+struct GemmDm {
+  static constexpr bool A_KC = false;
+  Plan pl;
+  int lev, mtiles, ntiles;
+  const float* dT;
+  const float* nu;   // query centroids [B*Hq][P][C][D]
+  float* dM;
+  struct View { int M, N, K, Cq, t, p, bh0; float* C; };
+  __device__ void view(int batch, View& v) const {
+    const int nseg = pl.lev_nseg[lev];
+    const int t = batch % nseg, kvh = batch / nseg;
+    const int p = pl.lev_pfirst[lev] + t;
+    const Geom gm = prob_geom(pl, p);
+    const int Gq = pl.Hq / pl.Hkv;
+    v.Cq = min(pl.C, gm.qn);
+    v.M = pl.D * pl.C;
+    v.N = pl.D;
+    v.K = Gq * pl.C;
+    v.t = t;
+    v.p = p;
+    v.bh0 = (kvh / pl.Hkv) * pl.Hq + (kvh % pl.Hkv) * Gq;
+    v.C = dM + (size_t)batch * pl.D * pl.C * pl.D;
+  }
+  __device__ float a(const View& v, int m, int k) const {
+    const int h = k / pl.C, I = k % pl.C;
+    if (I >= v.Cq) return 0.f;
+    const size_t lp = (size_t)(v.bh0 + h) * pl.lev_nseg[lev] + v.t;
+    return dT[(lp * pl.C + I) * (size_t)pl.D * pl.C + m];
+  }
+  __device__ float b(const View& v, int k, int n) const {
+    const int h = k / pl.C, I = k % pl.C;
+    if (I >= v.Cq) return 0.f;
+    const size_t ap = (size_t)(v.bh0 + h) * pl.P + v.p;
+    return nu[(ap * pl.C + I) * pl.D + n];
+  }
+  __device__ void c(const View& v, int m, int n, float x) const { v.C[(size_t)m * pl.D + n] = pl.scale * x; }
+};
+
+// ===========================================================================
+// dS_c[d] = sum_{h,I} dT_{h,I}[d][c] ; dmu_c[e] = sum_{h,I} G_{h,I}[c][e]
+// one thread per (kl, index in C*D)
+// ===========================================================================
+__global__ void __launch_bounds__(256) bwd_reduce_k_kernel(BwdArgs A, int lev) {
+  const Plan& pl = A.pl;
+  const int C = pl.C, D = pl.D, Gq = pl.Hq / pl.Hkv;
+  const int nseg = pl.lev_nseg[lev];
+  const int per = (C * D + 255) / 256;
+  const int kl = blockIdx.x / per;
+  const int idx = (blockIdx.x % per) * 256 + threadIdx.x;
+  if (idx >= C * D) return;
+  const int t = kl % nseg, kvh = kl / nseg;
+  const int p = pl.lev_pfirst[lev] + t;
+  const Geom gm = prob_geom(pl, p);
+  const int Cq = min(C, gm.qn);
+  const int bh0 = (kvh / pl.Hkv) * pl.Hq + (kvh % pl.Hkv) * Gq;
+  float sS = 0.f, sMu = 0.f;
+  for (int h = 0; h < Gq; ++h) {
+    const size_t lp = (size_t)(bh0 + h) * nseg + t;
+    for (int I = 0; I < Cq; ++I) {
+      sS += A.dT[(lp * C + I) * (size_t)D * C + idx];
+      sMu += A.G[(lp * C + I) * (size_t)C * D + idx];
+    }
+  }
+  const int d = idx / C, c = idx % C;   // the dT index is (d, c)
+  A.dS[((size_t)kl * C + c) * D + d] = sS;
+  A.dmu[(size_t)kl * C * D + idx] = sMu;
+}
+
+// dq_i += dnu_I / m_I for every query of the level; one thread per (row, 4 dims)
+__global__ void __launch_bounds__(256) bwd_spread_q_kernel(BwdArgs A, int lev) {
+  const Plan& pl = A.pl;
+  const AttnBufs& b = A.a;
+  const int D = pl.D, C = pl.C;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int per = D / 4;
+  const long long rowid = gid / per;
+  if (rowid >= (long long)pl.B * pl.Hq * pl.N) return;
+  const int e0 = (int)(gid % per) * 4;
+  const int bh = (int)(rowid / pl.N), r = (int)(rowid % pl.N);
+  const int nseg = pl.lev_nseg[lev], m = pl.lev_m[lev];
+  int t = 0;
+  if (pl.causal) {
+    t = r / (2 * m);
+    if (t >= nseg || r < 2 * m * t + m) return;
+  }
+  const int p = pl.lev_pfirst[lev] + t;
+  const size_t ap = (size_t)bh * pl.P + p;
+  const Geom gm = prob_geom(pl, p);
+  const int Cq = min(C, gm.qn);
+  const int I = min(max(b.qs.labels[((size_t)lev * pl.B * pl.Hq + bh) * pl.N + r], 0), Cq - 1);
+  const int32_t* qoffs = b.qs.offs + ap * (C + 1);
+  const int mI = qoffs[I + 1] - qoffs[I];
+  if (mI <= 0) return;
+  const float inv = 1.f / (float)mI;
+  const size_t lp = (size_t)bh * nseg + t;
+  const f32x4 g4 = *reinterpret_cast<const f32x4*>(A.dnu + (lp * C + I) * D + e0);
+  float* dq = A.dq + ((size_t)bh * pl.N + r) * D + e0;
+  *reinterpret_cast<f32x4*>(dq) = *reinterpret_cast<const f32x4*>(dq) + g4 * inv;
+}
+
+// dk_j += dM_c^T (v_j - S_c/n_c) + dmu_c / n_c ; dv_j += dS_c + dM_c (k_j - mu_c)
+// one workgroup per (kl, cluster, 64 keys)
+template <typename TIn, int D>
+struct alignas(16) BcSmem {
+  float dM[D][D + 1];     // (value dim d, key dim e)
+  float vc[64][D + 4];    // v_j - S_c / n_c
+  float kc[64][D + 4];    // k_j - mu_c
+  float aux[2][D];        // dS_c, dmu_c / n_c
+  int32_t rows[64];
+  int32_t sel[4];
+};
+
+template <typename TIn, int D>
+__global__ void __launch_bounds__(256) bwd_bcast_k_kernel(BwdArgs A, int lev) {
+  using SM = BcSmem<TIn, D>;
+  extern __shared__ __align__(16) unsigned char bc_raw[];
+  SM& sm = *reinterpret_cast<SM*>(bc_raw);
+  const Plan& pl = A.pl;
+  const AttnBufs& b = A.a;
+  const int C = pl.C;
+  const int nseg = pl.lev_nseg[lev], m = pl.lev_m[lev];
+  const int spp = (m + 63) / 64 + C;
+  int id = blockIdx.x;
+  const int slot = id % spp; id /= spp;
+  const int t = id % nseg;
+  const int kvh = id / nseg;
+  const int p = pl.lev_pfirst[lev] + t;
+  const size_t kp = (size_t)kvh * pl.P + p;
+  const size_t kl = (size_t)kvh * nseg + t;
+  const Geom gm = prob_geom(pl, p);
+  const int Ck = min(C, gm.kn);
+  const int32_t* koffs = b.ks.offs + kp * (C + 1);
+  const int tid = threadIdx.x;
+  find_slot(koffs, Ck, 64, slot, sm.sel);
+  __syncthreads();
+  if (slot >= sm.sel[2]) return;
+  const int c = sm.sel[0];
+  const int beg = koffs[c] + sm.sel[1] * 64, cnt = min(koffs[c + 1], beg + 64) - beg;
+  const float inv = 1.f / (float)(koffs[c + 1] - koffs[c]);
+  const bool dip = pl.dipole != 0;
+  if (dip)
+    for (int idx = tid; idx < D * D; idx += 256) {
+      const int d = idx / D, e = idx % D;
+      sm.dM[d][e] = A.dM[((kl * D + d) * C + c) * D + e];
+    }
+  for (int e = tid; e < D; e += 256) {
+    sm.aux[0][e] = A.dS[(kl * C + c) * D + e];
+    sm.aux[1][e] = A.dmu[(kl * C + c) * D + e] * inv;
+  }
+  const size_t rb = ((size_t)lev * pl.B * pl.Hkv + kvh) * pl.N + gm.k0 + beg;
+  const TIn* Kp = reinterpret_cast<const TIn*>(b.kst.Kp) + rb * D;
+  const TIn* Vp = reinterpret_cast<const TIn*>(b.kst.Vp) + rb * D;
+  const float* Sc = b.kst.S + (kp * C + c) * D;
+  const float* muc = b.kst.mu + (kp * C + c) * D;
+  for (int idx = tid; idx < 64 * (D / 8); idx += 256) {
+    const int j = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
+    float kv[8], vv[8];
+    if (j < cnt) {
+      load8_f32<TIn>(Kp + (size_t)j * D + e0, kv);
+      load8_f32<TIn>(Vp + (size_t)j * D + e0, vv);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) { kv[q] = 0.f; vv[q] = 0.f; }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      sm.kc[j][e0 + q] = kv[q] - muc[e0 + q];
+      sm.vc[j][e0 + q] = vv[q] - Sc[e0 + q] * inv;
+    }
+  }
+  if (tid < 64) sm.rows[tid] = tid < cnt ? b.ks.perm[rb + tid] : -1;
+  __syncthreads();
+  // thread -> output dim e, keys j = grp, grp + NG, ...
+  constexpr int NG = 256 / D, NJ = 64 / NG;
+  const int e = tid % D, grp = tid / D;
+  float gk[NJ], gv[NJ];
+#pragma unroll
+  for (int q = 0; q < NJ; ++q) { gk[q] = sm.aux[1][e]; gv[q] = sm.aux[0][e]; }
+  if (dip) {
+    for (int d = 0; d < D; d += 4) {
+      float mc[4], mr[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { mc[u] = sm.dM[d + u][e]; mr[u] = sm.dM[e][d + u]; }
+#pragma unroll
+      for (int q = 0; q < NJ; ++q) {
+        const int j = grp + NG * q;
+        const f32x4 vj = *reinterpret_cast<const f32x4*>(&sm.vc[j][d]);
+        const f32x4 kj = *reinterpret_cast<const f32x4*>(&sm.kc[j][d]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          gk[q] = fmaf(mc[u], vj[u], gk[q]);
+          gv[q] = fmaf(mr[u], kj[u], gv[q]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NJ; ++q) {
+    const int j = grp + NG * q;
+    if (j >= cnt) continue;
+    const size_t o = ((size_t)kvh * pl.N + sm.rows[j]) * D + e;
+    A.dk[o] += gk[q];
+    A.dv[o] += gv[q];
+  }
+}
+
+// ===========================================================================
+template <typename TIn, int D>
+static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hipStream_t st) {
+  const Plan& pl = A.pl;
+  constexpr int NSG = sizeof(TIn) == 2 ? 2 : 3;   // parts for the cluster-level contractions
+  hipError_t e;
+  const long long nq = (long long)pl.B * pl.Hq * pl.N, nk = (long long)pl.B * pl.Hkv * pl.N;
+  const size_t bq_smem = sizeof(BqSmem<TIn, D>), bk_smem = sizeof(BkSmem<TIn, D>);
+  const size_t bc_smem = sizeof(BcSmem<TIn, D>);
+  set_smem_once((const void*)bwd_q_kernel<TIn, D, BQ_LOCAL>, bq_smem);
+  set_smem_once((const void*)bwd_q_kernel<TIn, D, BQ_PROBLEM>, bq_smem);
+  set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_LOCAL>, bk_smem);
+  set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_EXACT>, bk_smem);
+  set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_FAR>, bk_smem);
+  set_smem_once((const void*)bwd_bcast_k_kernel<TIn, D>, bc_smem);
+  MUSE_KT_PRE(st);
+  bwd_zero_kernel<<<(unsigned)((nq * D / 4 + 255) / 256), 256, 0, st>>>(A.dq, nq * D);
+  bwd_zero_kernel<<<(unsigned)((nk * D / 4 + 255) / 256), 256, 0, st>>>(A.dk, nk * D);
+  bwd_zero_kernel<<<(unsigned)((nk * D / 4 + 255) / 256), 256, 0, st>>>(A.dv, nk * D);
+  bwd_delta_kernel<TIn><<<(unsigned)((nq + 255) / 256), 256, 0, st>>>(
+      reinterpret_cast<const TIn*>(A.a.O), reinterpret_cast<const TIn*>(A.dO), A.delta, nq, D);
+  MUSE_KT_POST("bwd_prep", st);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (pl.causal) {
+    const long long nblk = (pl.N + pl.blk - 1) / pl.blk, tpb = (pl.blk + 63) / 64;
+    MUSE_KT_PRE(st);
+    bwd_q_kernel<TIn, D, BQ_LOCAL><<<(unsigned)(pl.B * pl.Hq * nblk * tpb), 256, bq_smem, st>>>(A, 0);
+    MUSE_KT_POST("bwd_q_local", st);
+    MUSE_KT_PRE(st);
+    bwd_kv_kernel<TIn, D, BK_LOCAL><<<(unsigned)(pl.B * pl.Hkv * nblk * tpb), 256, bk_smem, st>>>(A, 0);
+    MUSE_KT_POST("bwd_kv_local", st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int C = pl.C;
+  for (int lev = 0; lev < pl.nlev; ++lev) {
+    const long long nseg = pl.lev_nseg[lev];
+    if (nseg == 0) continue;
+    const long long m = pl.lev_m[lev];
+    const long long spp = (m + 63) / 64 + C;
+    MUSE_KT_PRE(st);
+    bwd_q_kernel<TIn, D, BQ_PROBLEM><<<(unsigned)(pl.B * pl.Hq * nseg * spp), 256, bq_smem, st>>>(A, lev);
+    MUSE_KT_POST("bwd_q", st);
+    MUSE_KT_PRE(st);
+    bwd_kv_kernel<TIn, D, BK_EXACT><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 256, bk_smem, st>>>(A, lev);
+    MUSE_KT_POST("bwd_kv", st);
+    MUSE_KT_PRE(st);
+    bwd_kv_kernel<TIn, D, BK_FAR>
+        <<<(unsigned)(pl.B * pl.Hq * nseg * C * ((C + 63) / 64)), 256, bk_smem, st>>>(A, lev);
+    MUSE_KT_POST("bwd_far", st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    MUSE_KT_PRE(st);
+    bwd_reduce_k_kernel<<<(unsigned)(pl.B * pl.Hkv * nseg * ((C * D + 255) / 256)), 256, 0, st>>>(A, lev);
+    if (pl.dipole) {
+      GemmDm gdm{pl, lev, (D * C + 63) / 64, (D + 63) / 64, A.dT, A.a.qs.cent, A.dM};
+      bwd_gemm_kernel<GemmDm, NSG>
+          <<<(unsigned)(pl.B * pl.Hkv * nseg * gdm.mtiles * gdm.ntiles), 256, 0, st>>>(gdm);
+      GemmDnu gdn{pl, lev, (C + 63) / 64, (D + 63) / 64, A.dT, A.a.kst.M, A.dnu};
+      bwd_gemm_kernel<GemmDnu, NSG>
+          <<<(unsigned)(pl.B * pl.Hq * nseg * gdn.mtiles * gdn.ntiles), 256, 0, st>>>(gdn);
+      bwd_spread_q_kernel<<<(unsigned)((nq * (D / 4) + 255) / 256), 256, 0, st>>>(A, lev);
+    }
+    bwd_bcast_k_kernel<TIn, D><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 256, bc_smem, st>>>(A, lev);
+    MUSE_KT_POST("bwd_cluster", st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  MUSE_KT_PRE(st);
+  bwd_out_kernel<TIn><<<(unsigned)((nq * D + 255) / 256), 256, 0, st>>>(A.dq, reinterpret_cast<TIn*>(dQo), nq * D);
+  bwd_out_kernel<TIn><<<(unsigned)((nk * D + 255) / 256), 256, 0, st>>>(A.dk, reinterpret_cast<TIn*>(dKo), nk * D);
+  bwd_out_kernel<TIn><<<(unsigned)((nk * D + 255) / 256), 256, 0, st>>>(A.dv, reinterpret_cast<TIn*>(dVo), nk * D);
+  MUSE_KT_POST("bwd_out", st);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
+  BwdArgs A;
+  A.pl = L.pl;
+  A.a = L.a;
+  A.dO = L.dO;
+  A.lse = L.lse;
+  A.delta = L.delta;
+  A.dq = L.dq;
+  A.dk = L.dk;
+  A.dv = L.dv;
+  A.dT = L.dT;
+  A.G = L.G;
+  A.dnu = L.dnu;
+  A.dS = L.dS;
+  A.dmu = L.dmu;
+  A.dM = L.dM;
+  if (L.dtype == 1)
+    return L.pl.D == 64 ? bwd_all<uint16_t, 64>(A, L.dQ, L.dK, L.dV, st)
+                        : bwd_all<uint16_t, 128>(A, L.dQ, L.dK, L.dV, st);
+  return L.pl.D == 64 ? bwd_all<float, 64>(A, L.dQ, L.dK, L.dV, st)
+                      : bwd_all<float, 128>(A, L.dQ, L.dK, L.dV, st);
+}
+
+}  // namespace muse

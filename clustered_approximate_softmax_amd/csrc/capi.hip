@@ -202,6 +202,34 @@ static void build_layout(const Plan& pl, int dtype, Layout& out) {
   L.ws_bytes = std::max<size_t>(w, 256);
 }
 
+// Backward scratch: recomputed T, Delta, fp32 gradient accumulators and the
+// per-level cluster gradients (sized for the level with the most segments).
+struct BwdLayout {
+  size_t T, delta, dq, dk, dv, dT, G, dnu, dS, dmu, dM, bytes;
+};
+
+static void build_bwd_layout(const Plan& pl, int dtype, BwdLayout& o) {
+  const size_t BHq = (size_t)pl.B * pl.Hq, BHk = (size_t)pl.B * pl.Hkv;
+  const size_t N = pl.N, D = pl.D, C = pl.C, P = pl.P;
+  const size_t Cp = (pl.C + 63) / 64 * 64;
+  const size_t eb = dtype == 1 ? 2 : 4;
+  size_t ms = 0;
+  for (int l = 0; l < pl.nlev; ++l) ms = std::max<size_t>(ms, (size_t)pl.lev_nseg[l]);
+  size_t w = 0;
+  o.T = w; w = al(w + BHq * P * C * D * Cp * eb);
+  o.delta = w; w = al(w + BHq * N * 4);
+  o.dq = w; w = al(w + BHq * N * D * 4);
+  o.dk = w; w = al(w + BHk * N * D * 4);
+  o.dv = w; w = al(w + BHk * N * D * 4);
+  o.dT = w; w = al(w + BHq * ms * C * D * C * 4);
+  o.G = w; w = al(w + BHq * ms * C * C * D * 4);
+  o.dnu = w; w = al(w + BHq * ms * C * D * 4);
+  o.dS = w; w = al(w + BHk * ms * C * D * 4);
+  o.dmu = w; w = al(w + BHk * ms * C * D * 4);
+  o.dM = w; w = al(w + BHk * ms * D * C * D * 4);
+  o.bytes = std::max<size_t>(w, 256);
+}
+
 static int hip_fail(hipError_t e) {
   g_hip_err = hipGetErrorString(e);
   return MUSE_EHIP;
@@ -357,18 +385,68 @@ int musesummarize(const void* K, const void* V, muse_dtype dtype, int64_t G, int
 
 size_t muse_bwd_ws_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, muse_dtype dtype,
                         const muse_cfg* cfg) {
-  (void)B; (void)Hq; (void)Hkv; (void)N; (void)D; (void)dtype; (void)cfg;
-  return 256;
+  if (dtype != MUSE_F32 && dtype != MUSE_BF16) return 0;
+  Plan pl;
+  if (build_plan(B, Hq, Hkv, N, D, cfg, pl)) return 0;
+  BwdLayout bl;
+  build_bwd_layout(pl, (int)dtype, bl);
+  return bl.bytes;
 }
 
 int museattn_bwd(const void* Q, const void* K, const void* V, const void* O, const float* lse,
                  const void* dO, muse_dtype dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                  int64_t D, const muse_cfg* cfg, const void* state, size_t state_bytes, void* dQ,
                  void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
-  (void)Q; (void)K; (void)V; (void)O; (void)lse; (void)dO; (void)dtype; (void)B; (void)Hq;
-  (void)Hkv; (void)N; (void)D; (void)cfg; (void)state; (void)state_bytes; (void)dQ; (void)dK;
-  (void)dV; (void)ws; (void)ws_bytes; (void)stream;
-  return MUSE_EUNSUPPORTED;
+  if (!Q || !K || !V || !O || !lse || !dO || !state || !dQ || !dK || !dV || !ws) return MUSE_EINVAL;
+  if (dtype != MUSE_F32 && dtype != MUSE_BF16) return MUSE_EINVAL;
+  Plan pl;
+  int rc = build_plan(B, Hq, Hkv, N, D, cfg, pl);
+  if (rc) return rc;
+  Layout lay;
+  build_layout(pl, (int)dtype, lay);
+  const muse_layout& L = lay.L;
+  BwdLayout bl;
+  build_bwd_layout(pl, (int)dtype, bl);
+  if (state_bytes < L.state_bytes || ws_bytes < bl.bytes) return MUSE_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* sb = (char*)const_cast<void*>(state);
+  char* wb = (char*)ws;
+  AttnBufs ab;
+  memset(&ab, 0, sizeof(ab));
+  ab.Q = Q; ab.K = K; ab.V = V;
+  ab.qs = CSet{Q, pl.B * pl.Hq, 1, nullptr, (int32_t*)(sb + L.q_labels), (int32_t*)(sb + L.q_perm),
+               (int32_t*)(sb + L.q_offs), (float*)(sb + L.q_cent)};
+  ab.ks = CSet{K, pl.B * pl.Hkv, 0, nullptr, (int32_t*)(sb + L.k_labels), (int32_t*)(sb + L.k_perm),
+               (int32_t*)(sb + L.k_offs), (float*)(sb + L.k_cent)};
+  ab.kst = KStats{(float*)(sb + L.mu), (float*)(sb + L.S), (float*)(sb + L.M), sb + L.mu_in,
+                  sb + L.Kp, sb + L.Vp};
+  ab.R = (int32_t*)(sb + L.R);
+  ab.T = wb + bl.T;
+  ab.Cp32 = (int32_t)L.Cp32;
+  ab.O = const_cast<void*>(O);
+  ab.lse = const_cast<float*>(lse);
+  hipError_t e = hipGetLastError();  // clear stale errors from earlier calls
+  (void)e;
+  if (pl.P > 0 && (e = launch_tilt(pl, (int)dtype, ab, st)) != hipSuccess) return hip_fail(e);
+  BwdLaunch bw;
+  bw.pl = pl;
+  bw.dtype = (int)dtype;
+  bw.a = ab;
+  bw.dO = dO;
+  bw.lse = lse;
+  bw.delta = (float*)(wb + bl.delta);
+  bw.dq = (float*)(wb + bl.dq);
+  bw.dk = (float*)(wb + bl.dk);
+  bw.dv = (float*)(wb + bl.dv);
+  bw.dT = (float*)(wb + bl.dT);
+  bw.G = (float*)(wb + bl.G);
+  bw.dnu = (float*)(wb + bl.dnu);
+  bw.dS = (float*)(wb + bl.dS);
+  bw.dmu = (float*)(wb + bl.dmu);
+  bw.dM = (float*)(wb + bl.dM);
+  bw.dQ = dQ; bw.dK = dK; bw.dV = dV;
+  if ((e = launch_bwd(bw, st)) != hipSuccess) return hip_fail(e);
+  return MUSE_OK;
 }
 
 int muse_timing_enable(int on) {

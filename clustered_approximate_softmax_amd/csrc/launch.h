@@ -60,6 +60,25 @@ hipError_t launch_score_topk(const Plan& pl, const AttnBufs& b, hipStream_t st);
 hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
 hipError_t launch_attn(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
 
+// Backward with the forward's clustering state held fixed.
+struct BwdLaunch {
+  Plan pl;
+  int dtype;
+  AttnBufs a;             // forward state; a.T holds the recomputed T / n_c, a.O the forward output
+  const void* dO;
+  const float* lse;
+  float* delta;           // [B*Hq][N]
+  float* dq; float* dk; float* dv;   // fp32 accumulators, [heads][N][D]
+  float* dT;              // per-level scratch, see bwd.hip
+  float* G;
+  float* dnu;
+  float* dS;
+  float* dmu;
+  float* dM;
+  void* dQ; void* dK; void* dV;      // outputs in the input dtype
+};
+hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st);
+
 }  // namespace muse
 
 #define MUSE_KT_PRE(st) \

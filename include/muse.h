@@ -191,12 +191,26 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
 /*
  * museattn_bwd - gradients of museattn_fwd with the cluster assignments,
  * retrieval sets and counts held fixed (those saved in `state` by the
- * forward on the same Q, K, V); differentiates through the centroids, value
- * sums, dipoles and tilted summaries.
- *   O, lse     forward outputs; dO [B,Hq,N,D] upstream gradient (dtype)
- *   dQ [B,Hq,N,D], dK, dV [B,Hkv,N,D] out (dtype); dK and dV sum over the
- *              query heads sharing a KV head.
- *   ws         scratch, ws_bytes >= muse_bwd_ws_size()
+ * forward on the same Q, K, V and cfg); differentiates through the
+ * centroids, value sums, dipoles and tilted summaries (the far-field item
+ * of cluster c for query cluster I is a pseudo-key mu_c with value
+ * T_Ic / n_c and log-weight ln n_c; gist.science page, Technical Summary,
+ * Core Mechanisms; newx.sg page, Abstract).
+ *   Q, K, V    the forward's inputs (device, dtype, [B,H,N,D] row-major)
+ *   O, lse     the forward's outputs (device)
+ *   dO         [B,Hq,N,D] upstream gradient (device, dtype)
+ *   state      the forward's state buffer (device, read-only here)
+ *   dQ         [B,Hq,N,D] out (device, dtype)
+ *   dK, dV     [B,Hkv,N,D] out (device, dtype); sums over the query heads
+ *              sharing a KV head
+ *   ws         device scratch of ws_bytes >= muse_bwd_ws_size() bytes,
+ *              owned by the caller; its contents are undefined afterwards
+ *   stream     HIP stream (null = default); the call only queues work.
+ * Accumulation is fp32 in a fixed order (no atomics): repeated calls give
+ * bit-identical results.  Returns MUSE_EINVAL for null pointers or shapes /
+ * parameters museattn_fwd rejects, MUSE_EWORKSPACE when state_bytes or
+ * ws_bytes is too small, MUSE_EHIP when a launch fails.
+ * muse_bwd_ws_size returns 0 for invalid arguments.
  */
 size_t muse_bwd_ws_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, muse_dtype dtype,
                         const muse_cfg* cfg);

@@ -97,3 +97,17 @@ def test_cluster_and_summarize_reject_bad_arguments():
 def test_backward_reports_unsupported_until_built():
     # fixed-assignment backward entry point exists in the ABI
     assert hasattr(M.lib(), "museattn_bwd")
+
+
+def test_bwd_ws_size_and_null_checks():
+    L = M.lib()
+    cfg = M.make_cfg(16, 2, 2, True, 64)
+    n = L.muse_bwd_ws_size(1, 4, 2, 1000, 64, 1, ctypes.byref(cfg))
+    # at least the fp32 gradient accumulators and Delta
+    assert n >= (4 * 1000 * 64 + 2 * 2 * 1000 * 64 + 4 * 1000) * 4
+    bad = M.make_cfg(16, 2, 2, True, 64)
+    assert L.muse_bwd_ws_size(1, 3, 2, 1000, 64, 1, ctypes.byref(bad)) == 0      # Hq % Hkv != 0
+    assert L.muse_bwd_ws_size(1, 4, 2, 1000, 96, 1, ctypes.byref(bad)) == 0      # D unsupported
+    rc = L.museattn_bwd(None, None, None, None, None, None, 1, 1, 4, 2, 1000, 64, ctypes.byref(cfg),
+                        None, 0, None, None, None, None, 0, None)
+    assert rc == -1
