@@ -1,8 +1,9 @@
-"""Benchmark of the MuSe forward on one MI355X.
+"""Benchmark of the MuSe hot path on one MI355X.
 
 A step is one museattn_fwd call over the whole workload tensor (all batch x
 heads, clustering included; input generation excluded), inputs resident in
-HBM.  Default workload: acausal bf16, batch 1, 8 heads, N=8192, D=64, 64
+HBM; for the training workload (--config c5) a step is museattn_fwd followed
+by museattn_bwd.  Default workload: acausal bf16, batch 1, 8 heads, N=8192, D=64, 64
 query and 64 key clusters, 10 Lloyd iterations, top-4 retrieval.
 
 Prints one JSON line: ms per layer, effective TFLOP/s (exact-attention
@@ -43,9 +44,10 @@ def parse():
 
 
 def exact_flops(w):
-    if w.causal:
-        return 4.0 * w.B * w.Hq * w.D * w.N * (w.N + 1) / 2
-    return 4.0 * w.B * w.Hq * w.N * w.N * w.D
+    """Exact softmax-attention FLOPs of the step (forward: QK^T and PV;
+    backward adds five products of the same size: x 3.5 for fwd + bwd)."""
+    f = 4.0 * w.B * w.Hq * w.D * (w.N * (w.N + 1) / 2 if w.causal else w.N * w.N)
+    return 3.5 * f if w.backward else f
 
 
 def kernel_models(w, M, st, rows):
@@ -86,6 +88,19 @@ def kernel_models(w, M, st, rows):
     km["tilt"] = (2.0 * BHq * Pn * C * C * D * D, BHq * Pn * C * C * D * 4, "hbm")
     if w.causal:
         km["attn_local"] = (2.0 * BHq * w.N * (w.block + 1) / 2 * 2 * D, BHq * w.N * D * eb * 2, "mfma")
+    if w.backward:
+        # per (query, item) pair: S and dP, then dQ (query-centric) or dK and dV (item-centric)
+        loc = BHq * w.N * (w.block + 1) / 2 if w.causal else 0.0
+        km["bwd_q"] = (6.0 * D * (ret + far), pts_q * D * eb * 3, "mfma")
+        km["bwd_kv"] = (8.0 * D * ret, pts_k * D * eb * 4, "mfma")
+        km["bwd_far"] = (8.0 * D * far, BHq * Pn * C * C * D * 4 * 2, "mfma")
+        km["bwd_q_local"] = (6.0 * D * loc, BHq * w.N * D * eb * 3, "mfma")
+        km["bwd_kv_local"] = (8.0 * D * loc, BHq * w.N * D * eb * 2, "mfma")
+        # dM and dnu contractions (C x C x D x D per problem each) and the key broadcast
+        km["bwd_cluster"] = (2.0 * 2.0 * BHq * Pn * C * C * D * D + 4.0 * pts_k * D * D,
+                             BHq * Pn * C * C * D * 4 * 3, "mfma")
+        f, b_, bd = km["tilt"]
+        km["tilt"] = (2 * f, 2 * b_, bd)          # recomputed once in the backward
     return km
 
 
@@ -99,13 +114,25 @@ def time_calls(fn, steps, torch):
 
 
 def exact_attention_ms(Q, K, V, w, steps, torch):
+    """torch SDPA on the same tensors (KV heads repeated for GQA); for the
+    training workload forward + backward, restricted to the fused flash /
+    memory-efficient kernels (no math fallback)."""
     import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
     Hq, Hkv = w.Hq, w.Hkv
-    Kx = K.repeat_interleave(Hq // Hkv, dim=1) if Hq != Hkv else K
-    Vx = V.repeat_interleave(Hq // Hkv, dim=1) if Hq != Hkv else V
+    Kx = (K.repeat_interleave(Hq // Hkv, dim=1) if Hq != Hkv else K).contiguous()
+    Vx = (V.repeat_interleave(Hq // Hkv, dim=1) if Hq != Hkv else V).contiguous()
+    if w.backward:
+        q, k, v = (t.detach().clone().requires_grad_(True) for t in (Q, Kx, Vx))
+        go = torch.randn_like(q)
 
-    def f():
-        F.scaled_dot_product_attention(Q, Kx, Vx, is_causal=w.causal)
+        def f():
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+                o = F.scaled_dot_product_attention(q, k, v, is_causal=w.causal)
+                o.backward(go)
+    else:
+        def f():
+            F.scaled_dot_product_attention(Q, Kx, Vx, is_causal=w.causal)
     for _ in range(2):
         f()
     return time_calls(f, steps, torch)
@@ -172,9 +199,6 @@ def main():
     from clustered_approximate_softmax_amd import synth
 
     w = synth.WORKLOADS[args.config]
-    if w.backward:
-        print(json.dumps({"error": "fwd+bwd workload needs museattn_bwd, not built yet"}))
-        sys.exit(3)
     x = synth.make_inputs(w)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     Q, K, V = (torch.from_numpy(x[k]).to(tdt).cuda() for k in ("Q", "K", "V"))
@@ -183,9 +207,16 @@ def main():
     O, lse, st = M.museattn_fwd(Q, K, V, cfg)
     ws = torch.empty(M.layout(w.B, w.Hq, w.Hkv, w.N, w.D, M._dt(Q), cfg)["ws_bytes"], dtype=torch.uint8,
                      device="cuda")
+    if w.backward:
+        dO = torch.from_numpy(x["dO"]).to(tdt).cuda()
+        bws = torch.empty(M.bwd_ws_size(w.B, w.Hq, w.Hkv, w.N, w.D, M._dt(Q), cfg), dtype=torch.uint8,
+                          device="cuda")
+        grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
 
     def step():
         M.museattn_fwd(Q, K, V, cfg, state=st, ws=ws, out=(O, lse))
+        if w.backward:
+            M.museattn_bwd(Q, K, V, O, lse, dO, cfg, st, ws=bws, out=grads)
 
     for _ in range(args.warmup):
         step()

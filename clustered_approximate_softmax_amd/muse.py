@@ -252,16 +252,29 @@ def museattn_fwd(Q, K, V, cfg: muse_cfg, init_q=None, init_k=None, state=None, w
     return O, lse, state
 
 
-def museattn_bwd(Q, K, V, O, lse, dO, cfg: muse_cfg, state: State, ws=None):
+def bwd_ws_size(B, Hq, Hkv, N, D, dtype, cfg: muse_cfg) -> int:
+    n = lib().muse_bwd_ws_size(B, Hq, Hkv, N, D, dtype, ctypes.byref(cfg))
+    if n == 0:
+        raise MuseError("muse_bwd_ws_size", -1, "invalid shape or parameters")
+    return n
+
+
+def museattn_bwd(Q, K, V, O, lse, dO, cfg: muse_cfg, state: State, ws=None, out=None):
+    """Gradients (dQ, dK, dV) of museattn_fwd with the clustering in `state`
+    held fixed.  ws (uint8, >= bwd_ws_size bytes) and out=(dQ, dK, dV) may be
+    passed in to reuse buffers."""
     torch = _torch()
     _dev_check(Q, K, V, O, lse, dO)
     B, Hq, N, D = Q.shape
     Hkv = K.shape[1]
     dt = _dt(Q)
-    wsb = lib().muse_bwd_ws_size(B, Hq, Hkv, N, D, dt, ctypes.byref(cfg))
+    wsb = bwd_ws_size(B, Hq, Hkv, N, D, dt, cfg)
     if ws is None or ws.numel() < wsb:
-        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=Q.device)
-    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=Q.device)
+    if out is None:
+        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    else:
+        dQ, dK, dV = out
     rc = lib().museattn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse), _ptr(dO), dt, B, Hq, Hkv, N, D,
                             ctypes.byref(cfg), _ptr(state.buf), state.buf.numel(), _ptr(dQ), _ptr(dK),
                             _ptr(dV), _ptr(ws), ws.numel(), _stream())

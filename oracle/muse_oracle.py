@@ -570,3 +570,74 @@ def backward(Q, K, V, dO, cfg: MuseConfig, O, lse, results, heads=None):
                 dK[b, g] += bb
                 dV[b, g] += c
     return dQ, dK, dV
+
+
+def rows_read_by_query_backward(N, cfg: MuseConfig, shared, rows):
+    """The query rows whose O and lse ``backward_query_rows`` reads for the
+    given rows: the rows themselves plus every member of their query
+    cluster in each problem holding them (nu_I couples a cluster's queries)."""
+    plan = causal_plan(N, cfg.block) if cfg.causal else acausal_plan(N)
+    need = set(int(i) for i in rows)
+    for p, pr in enumerate(plan):
+        q0, qn = pr["q0"], pr["qn"]
+        aq = np.asarray(shared[p][0])
+        for i in rows:
+            if q0 <= i < q0 + qn:
+                need.update(int(q0 + j) for j in np.nonzero(aq == aq[i - q0])[0])
+    return np.array(sorted(need), np.int64)
+
+
+def backward_query_rows(Qh, Kh, Vh, dOh, cfg: MuseConfig, O, lse, shared, rows):
+    """dQ of one query head at ``rows`` only, from the same formulas as
+    ``backward_problem`` and ``local_backward`` (assignments, retrieval
+    sets and counts fixed as in ``shared``: problem -> (aq, ak, R)).  O and
+    lse are read only at ``rows_read_by_query_backward``."""
+    Qh = np.asarray(Qh, np.float64)
+    Kh = np.asarray(Kh, np.float64)
+    Vh = np.asarray(Vh, np.float64)
+    dOh = np.asarray(dOh, np.float64)
+    O = np.asarray(O, np.float64)
+    N, D = Qh.shape
+    s = cfg.s(D)
+    rows = np.asarray(rows, np.int64)
+    out = np.zeros((len(rows), D))
+    plan = causal_plan(N, cfg.block) if cfg.causal else acausal_plan(N)
+    for p, pr in enumerate(plan):
+        q0, qn, k0, kn = pr["q0"], pr["qn"], pr["k0"], pr["kn"]
+        here = [(k, int(i) - q0) for k, i in enumerate(rows) if q0 <= i < q0 + qn]
+        if not here:
+            continue
+        aq, ak, R = shared[p]
+        aq, ak = np.asarray(aq), np.asarray(ak)
+        Cq, Ck = min(cfg.cq, qn), min(cfg.ck, kn)
+        K, V, Q = Kh[k0:k0 + kn], Vh[k0:k0 + kn], Qh[q0:q0 + qn]
+        n, mu, S, M = key_stats(K, V, ak, Ck)
+        m, nu = query_stats(Q, aq, Cq)
+        T = tilted_summaries(S, M, nu, s, cfg.dipole)
+        for I in sorted(set(int(aq[j]) for _, j in here)):
+            members = np.nonzero(aq == I)[0]
+            retrieved = [int(c) for c in R[I]]
+            ek = np.nonzero(np.isin(ak, retrieved))[0]
+            far = np.array([c for c in range(Ck) if n[c] > 0 and c not in retrieved], np.int64)
+            g = q0 + members
+            L = lse[g]
+            Delta = np.sum(dOh[g] * O[g], axis=1)
+            # dT_I over the far clusters (all members), then dnu_I
+            rho = np.exp(s * (Q[members] @ mu[far].T) - L[:, None])
+            dT = rho.T @ dOh[g]
+            dnu = s * np.einsum("cde,cd->e", M[far], dT) if cfg.dipole else np.zeros(D)
+            for k, j in here:
+                if aq[j] != I:
+                    continue
+                jj = int(np.nonzero(members == j)[0][0])
+                pe = np.exp(s * (K[ek] @ Q[j]) - L[jj])
+                dl = pe * (V[ek] @ dOh[q0 + j] - Delta[jj])
+                dlam = rho[jj] * (T[I, far] @ dOh[q0 + j] - Delta[jj] * n[far])
+                out[k] += s * (dl @ K[ek]) + s * (dlam @ mu[far]) + dnu / len(members)
+    if cfg.causal:
+        for k, i in enumerate(rows):
+            b0 = (int(i) // cfg.block) * cfg.block
+            pe = np.exp(s * (Kh[b0:i + 1] @ Qh[i]) - lse[i])
+            dl = pe * (Vh[b0:i + 1] @ dOh[i] - np.dot(dOh[i], O[i]))
+            out[k] += s * (dl @ Kh[b0:i + 1])
+    return out

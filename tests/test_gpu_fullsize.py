@@ -89,3 +89,64 @@ def test_full_c4_causal_64k_gqa_d64():
 
 def test_full_c5_causal_64k_gqa_d128_forward():
     _run_full("c5", [(0, 5)], 64)
+
+
+def test_full_c5_causal_64k_gqa_d128_backward():
+    """Fwd + bwd at 64k, D=128, GQA 32/8.  dQ at sampled rows (rows whose
+    causal levels differ) against the oracle's row-restricted backward; dK
+    and dV over whole KV heads through identities of the fixed-assignment
+    map that hold at any size: sum_j dV_j = sum_i dO_i, <dV, V> = sum_i
+    dO_i . O_i, sum_j dK_j = 0 and <dQ, Q> = <dK, K> per KV group."""
+    import time
+
+    import torch
+    w = synth.WORKLOADS["c5"]
+    x = synth.make_inputs(w, with_do=True)
+    Q, K, V, dO = (torch.from_numpy(x[k]).to(torch.bfloat16).cuda() for k in ("Q", "K", "V", "dO"))
+    cfg = M.make_cfg(w.C, w.iters, w.topk, w.causal, w.block)
+    O, lse, st = M.museattn_fwd(Q, K, V, cfg)
+    dQ, dK, dV = M.museattn_bwd(Q, K, V, O, lse, dO, cfg, st)
+    torch.cuda.synchronize()
+    for t in (dQ, dK, dV):
+        assert bool(torch.isfinite(t.float()).all())
+    Gq = w.Hq // w.Hkv
+    f64 = torch.float64
+    for g in range(w.Hkv):
+        hs = list(range(g * Gq, (g + 1) * Gq))
+        dv, vv, dk, kk = dV[0, g].to(f64), V[0, g].to(f64), dK[0, g].to(f64), K[0, g].to(f64)
+        do = dO[0, hs].to(f64)
+        # row sums of probabilities are one
+        lhs, rhs = dv.sum(0), do.sum((0, 1))
+        assert float((lhs - rhs).abs().max()) <= 2e-3 * float(dv.abs().sum(0).max()), g
+        # linearity in V
+        a, b = float((dv * vv).sum()), float((do * O[0, hs].to(f64)).sum())
+        assert abs(a - b) <= 2e-3 * float((dv * vv).abs().sum()), (g, a, b)
+        # common key shift
+        assert float(dk.sum(0).abs().max()) <= 2e-3 * float(dk.abs().sum(0).max()), g
+        # O(lam Q, K / lam) = O(Q, K)
+        a, b = float((dQ[0, hs].to(f64) * Q[0, hs].to(f64)).sum()), float((dk * kk).sum())
+        assert abs(a - b) <= 2e-3 * float((dk * kk).abs().sum()), (g, a, b)
+    # sampled dQ rows of one head against the oracle
+    b, h = 0, 5
+    g = (h * w.Hkv) // w.Hq
+    rows_plan = M.plan(w.N, cfg)
+    ql, kl, R = (st.field(f).cpu().numpy() for f in ("q_labels", "k_labels", "R"))
+    shared = {}
+    for p, (lev, t, k0, kn, q0, qn) in enumerate(rows_plan):
+        Cq = min(w.C, qn)
+        Rp = [np.array(sorted(c for c in R[h, p, I] if c >= 0), np.int64) for I in range(Cq)]
+        shared[p] = (ql[lev, h, q0:q0 + qn].astype(np.int64), kl[lev, g, k0:k0 + kn].astype(np.int64), Rp)
+    ocfg = mo.MuseConfig(cq=w.C, ck=w.C, iters=w.iters, topk=w.topk, block=w.block, causal=w.causal)
+    # block indices 63, 42, 21, 1 take part in levels {0..5}, {1,3,5}, {0,2,4}, {0}
+    rows = np.array([63 * 1024 + 1000, 42 * 1024 + 5, 21 * 1024 + 511, 1 * 1024 + 1023])
+    rows = np.concatenate([rows, np.random.default_rng(11).choice(w.N, 8, replace=False)])
+    need = mo.rows_read_by_query_backward(w.N, ocfg, shared, rows)
+    t0 = time.perf_counter()
+    Qh, Kh, Vh, dOh = x["Q"][b, h], x["K"][b, g], x["V"][b, g], x["dO"][b, h]
+    o_ref, l_ref, _ = mo.forward_head(Qh, Kh, Vh, ocfg, shared=shared, qrows=need)
+    dq_ref = mo.backward_query_rows(Qh, Kh, Vh, dOh, ocfg, o_ref, l_ref, shared, rows)
+    got = dQ[b, h].float().cpu().numpy()[rows]
+    err = gu.max_rel(got, dq_ref)
+    print(f"c5 dQ rows {rows.tolist()} ({len(need)} rows read, oracle {time.perf_counter() - t0:.1f} s): "
+          f"max rel err {err:.3e}")
+    assert err <= 2e-2, err

@@ -151,3 +151,42 @@ def test_row_restricted_forward_equals_full_forward():
     np.testing.assert_allclose(o2[rows], o[rows], atol=1e-13)
     np.testing.assert_allclose(l2[rows], l[rows], atol=1e-13)
     assert any(r is None for r in res)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_restricted_query_backward_equals_full_backward(causal):
+    Q, K, V, dO = _rand(10, Hq=1, Hkv=1, N=75, D=4)
+    cfg = mo.MuseConfig(cq=4, ck=3, iters=3, topk=1, block=8, causal=causal, scale=0.8)
+    O, L, res = mo.forward(Q, K, V, cfg)
+    dQ, _, _ = mo.backward(Q, K, V, dO, cfg, O, L, res)
+    shared = {p: (r.aq, r.ak, r.R) for p, r in enumerate(res[(0, 0)])}
+    rows = [0, 9, 16, 40, 74]
+    need = mo.rows_read_by_query_backward(75, cfg, shared, rows)
+    assert set(rows) <= set(need.tolist())
+    # O and lse outside the rows read are poisoned: the result must not change
+    Op = np.full_like(O[0, 0], np.nan)
+    Lp = np.full_like(L[0, 0], np.nan)
+    Op[need], Lp[need] = O[0, 0][need], L[0, 0][need]
+    got = mo.backward_query_rows(Q[0, 0], K[0, 0], V[0, 0], dO[0, 0], cfg, Op, Lp, shared, rows)
+    np.testing.assert_allclose(got, dQ[0, 0][rows], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_global_identities(causal):
+    """Identities of the fixed-assignment MuSe map used as full-size checks:
+    probabilities of every row sum to one (sum_j dV_j = sum_i dO_i); a common
+    shift of every key leaves each row's logits shifted by a constant
+    (sum_j dK_j = 0); O is linear in V (<dV, V> = sum_i dO_i . O_i); and
+    O(lam Q, K / lam) = O(Q, K) (<dQ, Q> = <dK, K>), per KV-head group."""
+    Q, K, V, dO = _rand(12, B=1, Hq=4, Hkv=2, N=50, D=4)
+    cfg = mo.MuseConfig(cq=3, ck=4, iters=2, topk=1, block=8, causal=causal, scale=0.7)
+    O, L, res = mo.forward(Q, K, V, cfg)
+    dQ, dK, dV = mo.backward(Q, K, V, dO, cfg, O, L, res)
+    for g in range(2):
+        hs = [h for h in range(4) if (h * 2) // 4 == g]
+        np.testing.assert_allclose(dV[0, g].sum(0), sum(dO[0, h].sum(0) for h in hs), atol=1e-10)
+        np.testing.assert_allclose(dK[0, g].sum(0), 0.0, atol=1e-10)
+        np.testing.assert_allclose(np.sum(dV[0, g] * V[0, g]), sum(np.sum(dO[0, h] * O[0, h]) for h in hs),
+                                   rtol=1e-10)
+        np.testing.assert_allclose(sum(np.sum(dQ[0, h] * Q[0, h]) for h in hs), np.sum(dK[0, g] * K[0, g]),
+                                   rtol=1e-10, atol=1e-10)
