@@ -68,7 +68,9 @@ def kernel_models(w, M, st, rows):
     small = (pts_q - large_q) + (pts_k - large_k)
     large = large_q + large_k
     km["km_local"] = (2.0 * small * C * D * T, small * D * eb * T, "mfma")
-    km["km_assign"] = (2.0 * large * C * D * T, large * D * eb * T, "mfma")
+    # assignment reads every point once per iteration: intensity C flop/B, below the bf16
+    # ridge, so it is priced against HBM
+    km["km_assign"] = (2.0 * large * C * D * T, large * D * eb * T, "hbm")
     # retrieved keys and far clusters summed over every query of every problem
     m = np.diff(qoffs, axis=-1).astype(np.float64)                       # [BHq, P, C]
     kvmap = np.array([(bh // w.Hq) * w.Hkv + (bh % w.Hq) * w.Hkv // w.Hq for bh in range(BHq)])
@@ -102,6 +104,26 @@ def kernel_models(w, M, st, rows):
         f, b_, bd = km["tilt"]
         km["tilt"] = (2 * f, 2 * b_, bd)          # recomputed once in the backward
     return km
+
+
+def measured_traffic(w, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of this workload (scaled by the copy calibration), or
+    None when there is none or the kernel's source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{'c' + str(w.number)}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("kernels", {}).get(kernel)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in (rec["source"], "common.h"):
+        with open(os.path.join(ROOT, "clustered_approximate_softmax_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != rec["source_sha"]:
+        return None
+    return int(rec["bytes_per_dispatch"])
 
 
 def time_calls(fn, steps, torch):
@@ -248,6 +270,7 @@ def main():
         achieved = by / launches / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof["traffic"] = measured_traffic(w, dom)
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = {"flops": fl / launches, "bytes": by / launches}
     roof["avg_launch_ms"] = round(avg_s * 1e3, 4)
