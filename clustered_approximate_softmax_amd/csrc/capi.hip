@@ -127,9 +127,10 @@ struct Layout {
   KmLarge lg;
 };
 
-static void build_kmlarge(const Plan& pl, int heads_total, int sub, int& plocal, KmLarge& lg) {
+static void build_kmlarge(const Plan& pl, int heads_total, int dtype, int& plocal, KmLarge& lg) {
   memset(&lg, 0, sizeof(lg));
   plocal = 0;
+  const int sub = kmeans_sub(dtype, pl.D);
   int first_large = pl.nlev;
   for (int l = 0; l < pl.nlev; ++l) {
     if (pl.lev_m[l] > KM_LOCAL_MAX) { first_large = l; break; }
@@ -164,6 +165,12 @@ static void build_kmlarge(const Plan& pl, int heads_total, int sub, int& plocal,
   lg.rfirst[nl] = rf;
 }
 
+// k-means scratch: chunk partial sums and counts.
+static void km_ws_bytes(const KmLarge& lg, int C, int D, size_t& part, size_t& pcnt) {
+  part = al((size_t)lg.cfirst[lg.nl] * C * D * 4);
+  pcnt = al((size_t)lg.cfirst[lg.nl] * C * 4);
+}
+
 static void build_layout(const Plan& pl, int dtype, Layout& out) {
   muse_layout& L = out.L;
   memset(&L, 0, sizeof(L));
@@ -192,13 +199,15 @@ static void build_layout(const Plan& pl, int dtype, Layout& out) {
   L.Vp = o; o = al(o + nl * BHk * N * D * eb);
   L.mu_in = o; o = al(o + BHk * P * C * D * eb);
   L.state_bytes = std::max<size_t>(o, 256);
-  build_kmlarge(pl, (int)(BHq + BHk), kmeans_sub(dtype, pl.D), out.plocal, out.lg);
+  build_kmlarge(pl, (int)(BHq + BHk), dtype, out.plocal, out.lg);
   size_t w = 0;
   L.ws_T = w; w = al(w + BHq * P * C * D * L.Cp32 * eb);
   L.ws_oacc = w; w = al(w + (pl.causal ? BHq * N * D * 4 : 0));
   L.ws_lacc = w; w = al(w + (pl.causal ? BHq * N * 4 : 0));
-  L.ws_part = w; w = al(w + (size_t)out.lg.cfirst[out.lg.nl] * C * D * 4);
-  L.ws_pcnt = w; w = al(w + (size_t)out.lg.cfirst[out.lg.nl] * C * 4);
+  size_t kp_bytes, kc_bytes;
+  km_ws_bytes(out.lg, pl.C, pl.D, kp_bytes, kc_bytes);
+  L.ws_part = w; w = al(w + kp_bytes);
+  L.ws_pcnt = w; w = al(w + kc_bytes);
   L.ws_bytes = std::max<size_t>(w, 256);
 }
 
@@ -336,8 +345,10 @@ size_t muse_cluster_ws_size(int64_t G, int64_t n, int64_t D, muse_dtype dtype, i
   if (build_plan(1, G, G, n, D, &cfg, pl)) return 0;
   int plocal;
   KmLarge lg;
-  build_kmlarge(pl, (int)G, kmeans_sub((int)dtype, (int)D), plocal, lg);
-  return al((size_t)lg.cfirst[lg.nl] * C * D * 4) + al((size_t)lg.cfirst[lg.nl] * C * 4) + 256;
+  build_kmlarge(pl, (int)G, (int)dtype, plocal, lg);
+  size_t a, b;
+  km_ws_bytes(lg, C, (int)D, a, b);
+  return a + b + 256;
 }
 
 int musecluster(const void* X, muse_dtype dtype, int64_t G, int64_t n, int64_t D, int32_t C,
@@ -351,13 +362,15 @@ int musecluster(const void* X, muse_dtype dtype, int64_t G, int64_t n, int64_t D
   if (rc) return rc;
   int plocal;
   KmLarge lg;
-  build_kmlarge(pl, (int)G, kmeans_sub((int)dtype, (int)D), plocal, lg);
+  build_kmlarge(pl, (int)G, (int)dtype, plocal, lg);
   const size_t need = muse_cluster_ws_size(G, n, D, dtype, C);
   if (lg.nl > 0 && (!ws || ws_bytes < need)) return MUSE_EWORKSPACE;
   CSet s0{X, (int)G, 1, init_idx, assign, perm, offs, centroids};
   CSet s1{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
+  size_t kp_bytes, kc_bytes;
+  km_ws_bytes(lg, C, (int)D, kp_bytes, kc_bytes);
   float* part = (float*)ws;
-  int32_t* pcnt = ws ? (int32_t*)((char*)ws + al((size_t)lg.cfirst[lg.nl] * C * D * 4)) : nullptr;
+  int32_t* pcnt = ws ? (int32_t*)((char*)ws + kp_bytes) : nullptr;
   (void)hipGetLastError();
   hipError_t e = launch_kmeans(pl, (int)dtype, s0, s1, plocal, lg, part, pcnt, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e);

@@ -26,6 +26,10 @@ constexpr int KM_NT = 256;  // threads per workgroup (4 waves)
 template <typename TIn, int D>
 struct KmShape {
   static constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
+  // bf16 inputs: centroid operand in two bf16 parts (hi, lo of -2 mu); the
+  // padding slots D..D+7 of the hi rows carry the squared norm for one extra
+  // k-step.  fp32 inputs: bf16 mu
+  static constexpr int NP = NS == 1 ? 2 : 1;
   static constexpr int MUP = D + 8;  // padded centroid row (bf16 elements)
   static constexpr int SUB = (NS == 3 && D == 128) ? 64 : 256;
   static constexpr int XTP = SUB + 8;  // padded transposed row
@@ -36,9 +40,9 @@ template <typename TIn, int D, int CT>
 struct alignas(16) KmSmem {
   using S = KmShape<TIn, D>;
   // fp32 centroids for the refinement step, kept in LDS when small
-  static constexpr bool KEEP32 = CT * 16 * D * 4 <= 32768;
+  static constexpr bool KEEP32 = CT * 16 * D * 4 <= (S::NS == 1 ? 16384 : 32768);
   float mu32[KEEP32 ? CT * 16 : 1][D + 4];
-  uint16_t mu_hat[CT * 16][S::MUP];
+  uint16_t mu_hat[S::NP][CT * 16][S::MUP];
   float mu_norm[CT * 16];
   uint16_t xt[S::NS][D][S::XTP];
   int32_t lab[S::SUB];
@@ -47,10 +51,13 @@ struct alignas(16) KmSmem {
   float red[8];
 };
 
-// Load the problem's current fp32 centroids into bf16 rows + squared norms
-// (norm: 8-element partial sums combined by shuffles in a fixed order).
-template <typename TIn, int D, int CT>
-__device__ void km_load_centroids(KmSmem<TIn, D, CT>& sm, const float* cent, int Ceff, float& Rmax) {
+// Screening operands from fp32 centroid rows (global or LDS): bf16 rows
+// (two parts of -2 mu for bf16 inputs, with the squared norm in an extra
+// k-step), fp32 squared norms and the largest norm.  Norms are 8-element
+// partial sums combined by shuffles in a fixed order.
+template <typename TIn, int D, int CT, typename SM>
+__device__ void km_centroids(SM& sm, const float* src, int stride, bool write32, int Ceff, float& Rmax) {
+  using S = KmShape<TIn, D>;
   constexpr int TPC = D / 8;
   const int tid = threadIdx.x;
   float mx = 0.f;
@@ -58,37 +65,63 @@ __device__ void km_load_centroids(KmSmem<TIn, D, CT>& sm, const float* cent, int
     const int c = idx / TPC, e0 = (idx % TPC) * 8;
     float v[8];
     if (c < Ceff) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(cent + (size_t)c * D + e0);
-      f32x4 a = src[0], b = src[1];
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src + (size_t)c * stride + e0);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + (size_t)c * stride + e0 + 4);
       v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
       v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = 0.f;
     }
-    u16x8 h;
+    u16x8 h, l;
     float part = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      h[j] = f2bf(v[j]);
       part = fmaf(v[j], v[j], part);
+      if constexpr (S::NS == 1) {
+        const float m2 = -2.f * v[j];
+        h[j] = f2bf(m2);
+        l[j] = f2bf(m2 - bf2f(h[j]));
+      } else {
+        h[j] = f2bf(v[j]);
+      }
     }
-    *reinterpret_cast<u16x8*>(&sm.mu_hat[c][e0]) = h;
-    if constexpr (KmSmem<TIn, D, CT>::KEEP32) {
-      *reinterpret_cast<f32x4*>(&sm.mu32[c][e0]) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(&sm.mu32[c][e0 + 4]) = f32x4{v[4], v[5], v[6], v[7]};
+    *reinterpret_cast<u16x8*>(&sm.mu_hat[0][c][e0]) = h;
+    if constexpr (S::NS == 1) *reinterpret_cast<u16x8*>(&sm.mu_hat[S::NP - 1][c][e0]) = l;
+    if constexpr (SM::KEEP32) {
+      if (write32) {
+        *reinterpret_cast<f32x4*>(&sm.mu32[c][e0]) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(&sm.mu32[c][e0 + 4]) = f32x4{v[4], v[5], v[6], v[7]};
+      }
     }
 #pragma unroll
     for (int m = 1; m < TPC; m <<= 1) part += __shfl_xor(part, m, 64);
     if (idx % TPC == 0) {
       sm.mu_norm[c] = c < Ceff ? part : INFINITY;
       if (c < Ceff) mx = fmaxf(mx, part);
+      if constexpr (S::NS == 1) {
+        // extra k-step: slots (1, |mu|^2 hi, |mu|^2 lo, 1) pair with the point's
+        // (|x|^2 hi, 1, 1, |x|^2 lo) in lane group 0 (the other groups' point
+        // slots are zero); absent clusters get a huge finite norm
+        const float nn = c < Ceff ? part : 1e30f;
+        u16x8 e = {0, 0, 0, 0, 0, 0, 0, 0};
+        e[0] = 0x3F80;
+        e[1] = f2bf(nn);
+        e[2] = c < Ceff ? f2bf(nn - bf2f(e[1])) : (uint16_t)0;
+        e[3] = 0x3F80;
+        *reinterpret_cast<u16x8*>(&sm.mu_hat[0][c][D]) = e;
+      }
     }
   }
   for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
   if ((tid & 63) == 0) sm.red[tid >> 6] = mx;
   __syncthreads();
   Rmax = sqrtf(fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3])));
+}
+
+template <typename TIn, int D, int CT>
+__device__ void km_load_centroids(KmSmem<TIn, D, CT>& sm, const float* cent, int Ceff, float& Rmax) {
+  km_centroids<TIn, D, CT>(sm, cent, D, true, Ceff, Rmax);
 }
 
 // Points of one sub-tile held in registers (raw input elements): lane
@@ -124,24 +157,193 @@ __device__ __forceinline__ void km_fetch(XRegs<TIn, D>& xr, const TIn* Xp, int s
   }
 }
 
+// median of three signed integers (one VALU instruction)
+__device__ __forceinline__ int med3i(int a, int b, int c) {
+  int r;
+  asm("v_med3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 template <typename V8>
 __device__ __forceinline__ float xval(const V8& v, int j) {
   if constexpr (sizeof(v[0]) == 2) return bf2f(v[j]);
   else return v[j];
 }
 
+// bf16 inputs.  Two-part screening: the point is exact in bf16 and
+// -2 mu = hi + lo to 2^-16, so acc = |x|^2 + |mu|^2 - 2 x.mu (norms through
+// the extra k-step) is the squared distance to about 2^-15 |x| |mu|.  Keys
+// hold the distance bits with the low bits replaced by the cluster index
+// (16t + i here, 4g added after the loop); the smallest two keys per point
+// are tracked with min / med3 on signed integers (a distance rounded below
+// zero orders first).  Points whose two best keys lie within the screening
+// error of each other are decided by fp32 distances to the candidate
+// clusters, lowest index on ties.
+template <typename TIn, int D, int CT, typename SM>
+__device__ void km_assign_bf16(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nvalid, const float* cent,
+                               int Ceff, float Rmax, int32_t* glab) {
+  using S = KmShape<TIn, D>;
+  constexpr int KS = D / 32;
+  constexpr int IB = CT <= 8 ? 7 : 8;
+  constexpr int KMASK = ~((1 << IB) - 1);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int grp = 0; grp < S::G16; ++grp) {
+    const int pl = w * (S::SUB / 4) + grp * 16 + col;
+    const bool valid = pl < nvalid;
+    float xsq = 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = xval(xr.x[grp][k], j);
+        xsq = fmaf(v, v, xsq);
+        sm.xt[0][32 * k + 8 * g + j][pl] = xr.x[grp][k][j];
+      }
+    }
+    xsq += __shfl_xor(xsq, 16, 64);
+    xsq += __shfl_xor(xsq, 32, 64);
+    u16x8 bn = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (g == 0) {
+      const uint16_t xh = f2bf(xsq);
+      bn[0] = xh;
+      bn[1] = 0x3F80;
+      bn[2] = 0x3F80;
+      bn[3] = f2bf(xsq - bf2f(xh));
+    }
+    int m1 = 0x7fffffff, m2 = 0x7fffffff;
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+      if (t * 16 < Ceff) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          const u16x8 alo = *reinterpret_cast<const u16x8*>(&sm.mu_hat[1][16 * t + col][32 * k + 8 * g]);
+          acc = mfma(as_bf(alo), as_bf(xr.x[grp][k]), acc);
+        }
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          const u16x8 ahi = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][16 * t + col][32 * k + 8 * g]);
+          acc = mfma(as_bf(ahi), as_bf(xr.x[grp][k]), acc);
+        }
+        const u16x8 an = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][16 * t + col][D]);
+        acc = mfma(as_bf(an), as_bf(bn), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = (__float_as_int(acc[i]) & KMASK) | (16 * t + i);
+          const int n2 = med3i(m1, m2, key);
+          m1 = min(m1, key);
+          m2 = n2;
+        }
+      }
+    }
+    m1 |= 4 * g;
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+      const int b1 = __shfl_xor(m1, m, 64), b2 = __shfl_xor(m2, m, 64);
+      m2 = min(max(m1, b1), min(m2, b2));
+      m1 = min(m1, b1);
+    }
+    int label = m1 & ((1 << IB) - 1);
+    const float f1 = __int_as_float(m1 & KMASK), f2 = __int_as_float(m2 & KMASK);
+    const float xn = sqrtf(xsq);
+    // screening error (split residual, accumulation, norm split) plus key truncation
+    const float margin = 2.44140625e-4f * xn * Rmax + 1.220703125e-4f * (xsq + Rmax * Rmax) +
+                         (IB == 7 ? 3.0517578125e-05f : 6.103515625e-05f) * (fabsf(f1) + fabsf(f2));
+    const bool need = valid && Ceff > 1 && (f2 - f1 <= margin);
+    if (__any(need)) {
+      // candidates within the margin; the screening MFMAs are recomputed by the
+      // whole wave (an MFMA reads its operands from every lane, active or not)
+      const float thr = f1 + margin;
+      constexpr int NW = (CT * 16 + 63) / 64;
+      unsigned long long cm[NW];
+#pragma unroll
+      for (int q = 0; q < NW; ++q) cm[q] = 0ull;
+      for (int t = 0; t < CT; ++t) {
+        if (t * 16 >= Ceff) break;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          const u16x8 alo = *reinterpret_cast<const u16x8*>(&sm.mu_hat[1][16 * t + col][32 * k + 8 * g]);
+          acc = mfma(as_bf(alo), as_bf(xr.x[grp][k]), acc);
+        }
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          const u16x8 ahi = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][16 * t + col][32 * k + 8 * g]);
+          acc = mfma(as_bf(ahi), as_bf(xr.x[grp][k]), acc);
+        }
+        const u16x8 an = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][16 * t + col][D]);
+        acc = mfma(as_bf(an), as_bf(bn), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 16 * t + 4 * g + i;
+          if (need && c < Ceff && acc[i] <= thr) cm[c >> 6] |= 1ull << (c & 63);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        cm[q] |= __shfl_xor(cm[q], 16, 64);
+        cm[q] |= __shfl_xor(cm[q], 32, 64);
+      }
+      // exact fp32 distances of the candidates (lanes of points that need no
+      // refinement have an empty mask)
+      float bd = INFINITY;
+      int bc = 0x7fffffff;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        unsigned long long mword = cm[q];
+        while (mword) {
+          const int c = 64 * q + __builtin_ctzll(mword);
+          mword &= mword - 1;
+          float part = 0.f;
+#pragma unroll
+          for (int k = 0; k < KS; ++k) {
+            float mv[8];
+            if constexpr (SM::KEEP32) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) mv[j] = sm.mu32[c][32 * k + 8 * g + j];
+            } else {
+              const float* mr = cent + (size_t)c * D + 32 * k + 8 * g;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) mv[j] = mr[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float df = xval(xr.x[grp][k], j) - mv[j];
+              part = fmaf(df, df, part);
+            }
+          }
+          part += __shfl_xor(part, 16, 64);
+          part += __shfl_xor(part, 32, 64);
+          if (part < bd || (part == bd && c < bc)) { bd = part; bc = c; }
+        }
+      }
+      if (need) label = bc;
+    }
+    if (g == 0) {
+      sm.lab[pl] = valid ? label : -1;
+      if (valid) glab[sub0 + pl] = label;
+    }
+  }
+}
+
 // Assign the prefetched points [sub0, sub0 + nvalid) and stage them
 // transposed in LDS for the update.  Writes labels to LDS and to glab.
-template <typename TIn, int D, int CT>
-__device__ void km_assign_sub(KmSmem<TIn, D, CT>& sm, const XRegs<TIn, D>& xr, int sub0, int nvalid,
+template <typename TIn, int D, int CT, typename SM>
+__device__ void km_assign_sub(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nvalid,
                               const float* cent, int Ceff, float Rmax, int32_t* glab) {
   using S = KmShape<TIn, D>;
   constexpr int NS = S::NS;
   constexpr int KS = D / 32;
+  if constexpr (NS == 1) {
+    km_assign_bf16<TIn, D, CT>(sm, xr, sub0, nvalid, cent, Ceff, Rmax, glab);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
-  // screening error bound factor: bf16 centroids (and bf16 points for fp32 input)
-  const float efac = (NS == 1 ? 0.00390625f : 0.0078125f) * 1.05f;
+  // screening error bound factor: bf16 centroids and bf16 points (fp32 input)
+  const float efac = 0.0078125f * 1.05f;
 
 #pragma unroll
   for (int grp = 0; grp < S::G16; ++grp) {
@@ -182,7 +384,7 @@ __device__ void km_assign_sub(KmSmem<TIn, D, CT>& sm, const XRegs<TIn, D>& xr, i
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-          u16x8 a = *reinterpret_cast<const u16x8*>(&sm.mu_hat[16 * t + col][32 * k + 8 * g]);
+          u16x8 a = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][16 * t + col][32 * k + 8 * g]);
           acc = mfma(as_bf(a), as_bf(xf[k][0]), acc);
         }
         const f32x4 nrm = *reinterpret_cast<const f32x4*>(&sm.mu_norm[16 * t + 4 * g]);
@@ -243,7 +445,7 @@ __device__ void km_assign_sub(KmSmem<TIn, D, CT>& sm, const XRegs<TIn, D>& xr, i
 #pragma unroll
           for (int k = 0; k < KS; ++k) {
             float mv[8];
-            if constexpr (KmSmem<TIn, D, CT>::KEEP32) {
+            if constexpr (SM::KEEP32) {
 #pragma unroll
               for (int j = 0; j < 8; ++j) mv[j] = sm.mu32[c][32 * k + 8 * g + j];
             } else {
@@ -294,8 +496,8 @@ __device__ __forceinline__ void km_tile_of(int w, int u, int& ct, int& dt) {
   }
 }
 
-template <typename TIn, int D, int CT>
-__device__ void km_update_sub(KmSmem<TIn, D, CT>& sm, KmAcc<TIn, D, CT>& acc, int Ceff) {
+template <typename TIn, int D, int CT, typename SM>
+__device__ void km_update_sub(SM& sm, KmAcc<TIn, D, CT>& acc, int Ceff) {
   using S = KmShape<TIn, D>;
   constexpr int NS = S::NS;
   constexpr int DT = D / 16;
