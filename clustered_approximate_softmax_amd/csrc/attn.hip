@@ -36,7 +36,7 @@ struct alignas(16) AtSmem {
   uint16_t vt[NB][NS][D][AT_KT + 8];
   float bias[NB][AT_KT];
   int32_t krow[NB][AT_KT];
-  int32_t ring[3][AT_KT];      // item -> row, two tiles ahead
+  int32_t ring[4][AT_KT];      // item -> row, up to three tiles ahead
   int32_t qrow[16 * QG * WAVES];
   float far_bias[MUSE_MAXC];   // log2 n_c, or -inf (empty or retrieved)
   int32_t rbeg[MUSE_MAXC];
@@ -127,7 +127,7 @@ __device__ __forceinline__ void tile_load(const AtSmem<TIn, D, WAVES, QG>& sm, c
   const int tid = threadIdx.x;
   const bool far = src.mode == 1 && t < src.nfar;
   const int base = t * AT_KT;
-  const int* ring = sm.ring[t % 3];
+  const int* ring = sm.ring[t & 3];
 #pragma unroll
   for (int q = 0; q < TR::KC; ++q) {
     const int idx = tid + q * NT;
@@ -280,15 +280,6 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
     bv[rt] = *reinterpret_cast<const f32x4*>(&sm.bias[buf][16 * rt + 4 * g]);
     if (CAUSAL) kr[rt] = *reinterpret_cast<const int4*>(&sm.krow[buf][16 * rt + 4 * g]);
   }
-  // V^T fragments are shared by the query groups
-  u16x8 va[PS][DT][NS];
-#pragma unroll
-  for (int ps = 0; ps < PS; ++ps)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int sp = 0; sp < NS; ++sp)
-        va[ps][dt][sp] = *reinterpret_cast<const u16x8*>(&sm.vt[buf][sp][16 * dt + col][32 * ps + 8 * g]);
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     float x[RT * 4];
@@ -340,14 +331,22 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
           pb[0][j] = h; pb[NS > 1 ? 1 : 0][j] = mm; pb[NS > 2 ? 2 : 0][j] = l;
         }
       }
+      // V^T fragments of this 32-item block (read per query group: fewer live registers)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) st[qg].o[dt] = mfma_split<NS, NS>(va[ps][dt], pb, st[qg].o[dt]);
+      for (int dt = 0; dt < DT; ++dt) {
+        u16x8 va[NS];
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp)
+          va[sp] = *reinterpret_cast<const u16x8*>(&sm.vt[buf][sp][16 * dt + col][32 * ps + 8 * g]);
+        st[qg].o[dt] = mfma_split<NS, NS>(va, pb, st[qg].o[dt]);
+      }
     }
   }
 }
 
 template <typename TIn, typename TOut, int D, int WAVES, int QG, int MODE>
-__global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, int lev) {
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D == 64 && WAVES == 4 ? 2 : 1)))
+attn_kernel(Plan pl, AttnBufs b, int lev) {
   using SM = AtSmem<TIn, D, WAVES, QG>;
   constexpr int NS = SM::NS, NB = SM::NB;
   constexpr int NT = 64 * WAVES, QT = 16 * QG * WAVES;
@@ -515,6 +514,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   if (tid < AT_KT) {
     sm.ring[0][tid] = item_row(sm, src, 0, tid);
     sm.ring[1][tid] = item_row(sm, src, 1, tid);
+    sm.ring[2][tid] = item_row(sm, src, 2, tid);
   }
   __syncthreads();
 
@@ -544,22 +544,37 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) qmask[qg] = myq[qg] < 0 ? 0x7fffffff : myq[qg];
 
-  TileRegs<TIn, D, WAVES> R;
-  if (ntiles > 0) {
-    tile_load(sm, src, 0, R);
-    tile_store(sm, 0, R);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = NB == 2 ? (t & 1) : 0;
-    const bool more = t + 1 < ntiles;
-    if (tid < AT_KT && t + 2 < ntiles) sm.ring[(t + 2) % 3][tid] = item_row(sm, src, t + 2, tid);
-    if (more) tile_load(sm, src, t + 1, R);
-    consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, buf, qf, st, s2, qmask);
-    if (NB == 2) {
-      if (more) tile_store(sm, buf ^ 1, R);
+  if constexpr (NB == 2) {
+    // two tiles in flight in registers: the loads of tile t+2 are issued
+    // before tile t is consumed and written to LDS after tile t+1 is
+    TileRegs<TIn, D, WAVES> R0, R1;
+    if (ntiles > 0) tile_load(sm, src, 0, R0);
+    if (ntiles > 1) tile_load(sm, src, 1, R1);
+    if (ntiles > 0) tile_store(sm, 0, R0);
+    __syncthreads();
+    auto step = [&](int t, TileRegs<TIn, D, WAVES>& Rload, const TileRegs<TIn, D, WAVES>& Rstore) {
+      if (tid < AT_KT && t + 3 < ntiles) sm.ring[(t + 3) & 3][tid] = item_row(sm, src, t + 3, tid);
+      if (t + 2 < ntiles) tile_load(sm, src, t + 2, Rload);
+      consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, t & 1, qf, st, s2, qmask);
+      if (t + 1 < ntiles) tile_store(sm, (t + 1) & 1, Rstore);
       __syncthreads();
-    } else {
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, R0, R1);
+      if (t + 1 < ntiles) step(t + 1, R1, R0);
+    }
+  } else {
+    TileRegs<TIn, D, WAVES> R;
+    if (ntiles > 0) {
+      tile_load(sm, src, 0, R);
+      tile_store(sm, 0, R);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const bool more = t + 1 < ntiles;
+      if (tid < AT_KT && t + 2 < ntiles) sm.ring[(t + 2) & 3][tid] = item_row(sm, src, t + 2, tid);
+      if (more) tile_load(sm, src, t + 1, R);
+      consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, 0, qf, st, s2, qmask);
       __syncthreads();
       if (more) tile_store(sm, 0, R);
       __syncthreads();
@@ -656,10 +671,12 @@ static hipError_t attn_all(const Plan& pl, const AttnBufs& b, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   for (int lev = 0; lev < pl.nlev; ++lev) {
-    // query clusters of ~m/C rows: 16*QG*4-row workgroups for large clusters,
-    // one 16-row wave for small ones
+    // query clusters of ~m/C rows: the query tile (rows per workgroup) follows
+    // the mean cluster size so that ragged clusters waste few tile rows
     const int avg = pl.lev_m[lev] / (pl.C > 0 ? pl.C : 1);
-    e = avg >= 48 * QG ? attn_level<TIn, D, 4, QG>(pl, b, lev, st) : attn_level<TIn, D, 1, 1>(pl, b, lev, st);
+    if (QG == 2 && avg >= 160) e = attn_level<TIn, D, 4, QG>(pl, b, lev, st);
+    else if (avg >= 48) e = attn_level<TIn, D, 4, 1>(pl, b, lev, st);
+    else e = attn_level<TIn, D, 1, 1>(pl, b, lev, st);
     if (e != hipSuccess) return e;
   }
   if (pl.causal) {
