@@ -98,9 +98,12 @@ def kernel_models(w, M, st, rows):
         km["bwd_far"] = (8.0 * D * far, BHq * Pn * C * C * D * 4 * 2, "mfma")
         km["bwd_q_local"] = (6.0 * D * loc, BHq * w.N * D * eb * 3, "mfma")
         km["bwd_kv_local"] = (8.0 * D * loc, BHq * w.N * D * eb * 2, "mfma")
-        # dM and dnu contractions (C x C x D x D per problem each) and the key broadcast
-        km["bwd_cluster"] = (2.0 * 2.0 * BHq * Pn * C * C * D * D + 4.0 * pts_k * D * D,
-                             BHq * Pn * C * C * D * 4 * 3, "mfma")
+        # dM and dnu contractions (C x C x D x D per problem each), reductions and broadcasts
+        km["bwd_dM"] = (2.0 * BHq * Pn * C * C * D * D, BHq * Pn * C * C * D * 4, "mfma")
+        km["bwd_dnu"] = (2.0 * BHq * Pn * C * C * D * D, BHq * Pn * C * C * D * 4, "mfma")
+        km["bwd_reduce_k"] = (0.0, BHq * Pn * C * C * D * 4 * 2, "hbm")
+        km["bwd_spread_q"] = (0.0, pts_q * D * 4 * 2, "hbm")
+        km["bwd_bcast_k"] = (4.0 * pts_k * D * D, pts_k * D * (eb * 2 + 4 * 4), "mfma")
         f, b_, bd = km["tilt"]
         km["tilt"] = (2 * f, 2 * b_, bd)          # recomputed once in the backward
     return km

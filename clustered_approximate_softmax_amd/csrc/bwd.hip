@@ -182,12 +182,53 @@ struct alignas(16) BqSmem {
 
 // Stage BT items: rows of K and V, and K^T.  Far items: rows of mu_c and
 // columns of T / n_c (stored (d, c)).
-template <typename TIn, int D>
+template <typename TIn, int D, int NT>
 __device__ __forceinline__ void bq_stage(BqSmem<TIn, D>& sm, bool far, const TIn* Kb, const TIn* Vb,
                                          const TIn* mu, const TIn* T, int Cp, int c0, int Ck) {
   using SM = BqSmem<TIn, D>;
   constexpr int NS = SM::NS, BT = SM::BT;
-  for (int idx = threadIdx.x; idx < (BT / 4) * (D / 8); idx += 256) {
+  if constexpr (NS == 1) {
+    // bf16: raw 16-byte row chunks; K^T as 4-item runs in slot order
+    for (int idx = threadIdx.x; idx < (BT / 4) * (D / 8); idx += NT) {
+      const int kb = idx % (BT / 4), e0 = (idx / (BT / 4)) * 8;
+      u16x8 kr[4], vr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int it = 4 * kb + r;
+        kr[r] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        vr[r] = kr[r];
+        if (far) {
+          if (c0 + it < Ck) kr[r] = *reinterpret_cast<const u16x8*>(mu + (size_t)(c0 + it) * D + e0);
+        } else {
+          const int row = sm.irow[it];
+          if (row >= 0) {
+            kr[r] = *reinterpret_cast<const u16x8*>(Kb + (size_t)row * D + e0);
+            vr[r] = *reinterpret_cast<const u16x8*>(Vb + (size_t)row * D + e0);
+          }
+        }
+      }
+      if (far) {
+        // T / n_c is stored (d, c): four consecutive clusters per dim
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u16x4 t4 = *reinterpret_cast<const u16x4*>(T + (size_t)(e0 + j) * Cp + c0 + 4 * kb);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vr[r][j] = t4[r];
+        }
+      }
+      const int pos = 32 * ((4 * kb) / 32) + slot_of((4 * kb) % 32);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<u16x8*>(&sm.ks[0][4 * kb + r][e0]) = kr[r];
+        *reinterpret_cast<u16x8*>(&sm.vs[0][4 * kb + r][e0]) = vr[r];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<u16x4*>(&sm.kt[0][e0 + j][pos]) = u16x4{kr[0][j], kr[1][j], kr[2][j], kr[3][j]};
+    }
+    return;
+  }
+  for (int idx = threadIdx.x; idx < (BT / 4) * (D / 8); idx += NT) {
     const int kb = idx % (BT / 4), e0 = (idx / (BT / 4)) * 8;
     float kv[4][8], vv[4][8];
 #pragma unroll
@@ -238,10 +279,12 @@ __device__ __forceinline__ void bq_stage(BqSmem<TIn, D>& sm, bool far, const TIn
   }
 }
 
-template <typename TIn, int D, int MODE>
-__global__ void __launch_bounds__(256) bwd_q_kernel(BwdArgs A, int lev) {
+// WAVES waves of 16 queries each (one wave for small query clusters)
+template <typename TIn, int D, int MODE, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) bwd_q_kernel(BwdArgs A, int lev) {
   using SM = BqSmem<TIn, D>;
   constexpr int NS = SM::NS, BT = SM::BT, KS = D / 32, DT = D / 16, RT = BT / 16, PS = BT / 32;
+  constexpr int NT = 64 * WAVES, QT = 16 * WAVES;
   extern __shared__ __align__(16) unsigned char bq_raw[];
   SM& sm = *reinterpret_cast<SM*>(bq_raw);
   const Plan& pl = A.pl;
@@ -251,18 +294,18 @@ __global__ void __launch_bounds__(256) bwd_q_kernel(BwdArgs A, int lev) {
   const int C = pl.C;
   int bh, ap = 0, I = 0, Ck = 0, q0 = 0, k0 = 0, qlo, qhi;
   if (MODE == BQ_LOCAL) {
-    const int nblk = (pl.N + pl.blk - 1) / pl.blk, tpb = (pl.blk + 63) / 64;
+    const int nblk = (pl.N + pl.blk - 1) / pl.blk, tpb = (pl.blk + QT - 1) / QT;
     int id = blockIdx.x;
     const int tile = id % tpb; id /= tpb;
     const int blk = id % nblk;
     bh = id / nblk;
     k0 = blk * pl.blk;
-    qlo = k0 + tile * 64;
-    qhi = min(min(k0 + pl.blk, pl.N), qlo + 64);
+    qlo = k0 + tile * QT;
+    qhi = min(min(k0 + pl.blk, pl.N), qlo + QT);
     if (qlo >= qhi) return;
   } else {
     const int nseg = pl.lev_nseg[lev], m = pl.lev_m[lev];
-    const int spp = (m + 63) / 64 + C;
+    const int spp = (m + QT - 1) / QT + C;
     int id = blockIdx.x;
     const int slot = id % spp; id /= spp;
     const int t = id % nseg;
@@ -275,12 +318,12 @@ __global__ void __launch_bounds__(256) bwd_q_kernel(BwdArgs A, int lev) {
     k0 = gm.k0;
     q0 = gm.q0;
     const int32_t* qoffs = b.qs.offs + (size_t)ap * (C + 1);
-    find_slot(qoffs, Cq, 64, slot, sm.sel);
+    find_slot(qoffs, Cq, QT, slot, sm.sel);
     __syncthreads();
     if (slot >= sm.sel[2]) return;
     I = sm.sel[0];
-    qlo = qoffs[I] + sm.sel[1] * 64;
-    qhi = min(qoffs[I + 1], qlo + 64);
+    qlo = qoffs[I] + sm.sel[1] * QT;
+    qhi = min(qoffs[I + 1], qlo + QT);
   }
   const int kvh = (bh / pl.Hq) * pl.Hkv + ((bh % pl.Hq) * pl.Hkv) / pl.Hq;
   const int kp = kvh * pl.P + (ap % pl.P);
@@ -296,7 +339,7 @@ __global__ void __launch_bounds__(256) bwd_q_kernel(BwdArgs A, int lev) {
   if (MODE != BQ_LOCAL) {
     const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
     const int32_t* Rr = b.R + ((size_t)ap * C + I) * pl.k1w;
-    for (int c = tid; c < MUSE_MAXC; c += 256) {
+    for (int c = tid; c < MUSE_MAXC; c += NT) {
       float bias = -INFINITY;
       if (c < Ck) {
         const int nc = koffs[c + 1] - koffs[c];
@@ -399,7 +442,7 @@ __global__ void __launch_bounds__(256) bwd_q_kernel(BwdArgs A, int lev) {
       sm.bias[tid] = bias;
     }
     __syncthreads();
-    bq_stage<TIn, D>(sm, far, Kb, Vb, mu, T, b.Cp32, base, Ck);
+    bq_stage<TIn, D, NT>(sm, far, Kb, Vb, mu, T, b.Cp32, base, Ck);
     __syncthreads();
     float ds[RT * 4];
 #pragma unroll
@@ -472,11 +515,46 @@ struct alignas(16) BkSmem {
   int32_t sel[4];
 };
 
-template <typename TIn, int D>
+template <typename TIn, int D, int NT>
 __device__ __forceinline__ void bk_stage_queries(BkSmem<TIn, D>& sm, const TIn* Qh, const TIn* dOh,
                                                  const float* lse, const float* delta) {
   constexpr int NS = BkSmem<TIn, D>::NS;
-  for (int idx = threadIdx.x; idx < QB * (D / 8); idx += 256) {
+  if constexpr (NS == 1) {
+    // bf16: 4 queries x 8 dims per thread; rows as 16-byte chunks, the
+    // transposes as 4-query runs in slot order
+    for (int idx = threadIdx.x; idx < (QB / 4) * (D / 8); idx += NT) {
+      const int qb = idx % (QB / 4), e0 = (idx / (QB / 4)) * 8;
+      u16x8 qr[4], orr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = sm.qrow[4 * qb + r];
+        qr[r] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        orr[r] = qr[r];
+        if (row >= 0) {
+          qr[r] = *reinterpret_cast<const u16x8*>(Qh + (size_t)row * D + e0);
+          orr[r] = *reinterpret_cast<const u16x8*>(dOh + (size_t)row * D + e0);
+        }
+      }
+      const int pos = slot_of(4 * qb);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<u16x8*>(&sm.qs[0][4 * qb + r][e0]) = qr[r];
+        *reinterpret_cast<u16x8*>(&sm.os[0][4 * qb + r][e0]) = orr[r];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        *reinterpret_cast<u16x4*>(&sm.qt[0][e0 + j][pos]) = u16x4{qr[0][j], qr[1][j], qr[2][j], qr[3][j]};
+        *reinterpret_cast<u16x4*>(&sm.ot[0][e0 + j][pos]) = u16x4{orr[0][j], orr[1][j], orr[2][j], orr[3][j]};
+      }
+    }
+    if (threadIdx.x < QB) {
+      const int row = sm.qrow[threadIdx.x];
+      sm.lse2[threadIdx.x] = row >= 0 ? lse[row] * B_LOG2E : 0.f;
+      sm.dlt[threadIdx.x] = row >= 0 ? delta[row] : 0.f;
+    }
+    return;
+  }
+  for (int idx = threadIdx.x; idx < QB * (D / 8); idx += NT) {
     const int q = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
     const int row = sm.qrow[q];
     float qv[8], ov[8];
@@ -554,7 +632,7 @@ __device__ __forceinline__ void bk_consume(const BkSmem<TIn, D>& sm,
 }
 
 // Queries rows[qa .. qb) of head bh (rows == nullptr: rows qa .. qb themselves).
-template <typename TIn, int D, bool CAUSAL>
+template <typename TIn, int D, bool CAUSAL, int NT>
 __device__ __forceinline__ void bk_query_range(BkSmem<TIn, D>& sm, const BwdArgs& A, int bh, const int32_t* rows,
                                                int qa, int qb, const u16x8 (&kf)[D / 32][BwdTraits<TIn>::NS],
                                                const u16x8 (&vf)[D / 32][BwdTraits<TIn>::NS], float ibias,
@@ -568,17 +646,19 @@ __device__ __forceinline__ void bk_query_range(BkSmem<TIn, D>& sm, const BwdArgs
       sm.qrow[threadIdx.x] = q < qb ? (rows ? rows[q] : q) : -1;
     }
     __syncthreads();
-    bk_stage_queries<TIn, D>(sm, Qh, dOh, A.lse + (size_t)bh * pl.N, A.delta + (size_t)bh * pl.N);
+    bk_stage_queries<TIn, D, NT>(sm, Qh, dOh, A.lse + (size_t)bh * pl.N, A.delta + (size_t)bh * pl.N);
     __syncthreads();
     bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
     __syncthreads();
   }
 }
 
-template <typename TIn, int D, int KIND>
-__global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs A, int lev) {
+// WAVES waves of 16 items each (one wave for small key clusters)
+template <typename TIn, int D, int KIND, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) {
   using SM = BkSmem<TIn, D>;
   constexpr int NS = SM::NS, KS = D / 32, DT = D / 16;
+  constexpr int NT = 64 * WAVES, IT = 16 * WAVES;
   extern __shared__ __align__(16) unsigned char bk_raw[];
   SM& sm = *reinterpret_cast<SM*>(bk_raw);
   const Plan& pl = A.pl;
@@ -590,7 +670,7 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs A, int lev) {
   int bh = 0, blk1 = 0;
   Geom gm{};
   if (KIND == BK_LOCAL) {
-    const int nblk = (pl.N + pl.blk - 1) / pl.blk, tpb = (pl.blk + 63) / 64;
+    const int nblk = (pl.N + pl.blk - 1) / pl.blk, tpb = (pl.blk + IT - 1) / IT;
     int id = blockIdx.x;
     const int tile = id % tpb; id /= tpb;
     const int blk = id % nblk;
@@ -598,13 +678,13 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs A, int lev) {
     bq = kvh / pl.Hkv;
     const int blk0 = blk * pl.blk;
     blk1 = min(blk0 + pl.blk, pl.N);
-    ibeg = blk0 + tile * 64;
-    iend = min(blk1, ibeg + 64);
+    ibeg = blk0 + tile * IT;
+    iend = min(blk1, ibeg + IT);
     if (ibeg >= iend) return;
   } else if (KIND == BK_EXACT) {
     nseg = pl.lev_nseg[lev];
     const int m = pl.lev_m[lev];
-    const int spp = (m + 63) / 64 + C;
+    const int spp = (m + IT - 1) / IT + C;
     int id = blockIdx.x;
     const int slot = id % spp; id /= spp;
     t = id % nseg;
@@ -615,12 +695,12 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs A, int lev) {
     gm = prob_geom(pl, p);
     Ck = min(C, gm.kn);
     const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
-    find_slot(koffs, Ck, 64, slot, sm.sel);
+    find_slot(koffs, Ck, IT, slot, sm.sel);
     __syncthreads();
     if (slot >= sm.sel[2]) return;
     c = sm.sel[0];
-    ibeg = koffs[c] + sm.sel[1] * 64;
-    iend = min(koffs[c + 1], ibeg + 64);
+    ibeg = koffs[c] + sm.sel[1] * IT;
+    iend = min(koffs[c + 1], ibeg + IT);
   } else {  // BK_FAR: items are the key clusters ct*64 .. ct*64+63 seen from query cluster I
     nseg = pl.lev_nseg[lev];
     const int nct = (C + 63) / 64;
@@ -637,8 +717,8 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs A, int lev) {
     gm = prob_geom(pl, p);
     Ck = min(C, gm.kn);
     if (I >= min(C, gm.qn)) return;
-    ibeg = ct * 64;
-    iend = min(C, ibeg + 64);
+    ibeg = ct * IT;
+    iend = min(C, ibeg + IT);
   }
 
   // ---- this lane's item (wave w owns items 16w .. 16w+15) ----
@@ -711,7 +791,7 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs A, int lev) {
     const int Cq = min(C, gm.qn);
     const int total = Gq * Cq;
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < total; base += 256) {
+    for (int base = 0; base < total; base += NT) {
       const int e = base + tid;
       bool hit = false;
       if (e < total) {
@@ -726,7 +806,9 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs A, int lev) {
       int off = 0;
       for (int q = 0; q < w; ++q) off += sm.wc[q];
       if (hit) sm.list[off + __popcll(bal & lt)] = e;
-      const int cnt = sm.wc[0] + sm.wc[1] + sm.wc[2] + sm.wc[3];
+      int cnt = 0;
+#pragma unroll
+      for (int q = 0; q < WAVES; ++q) cnt += sm.wc[q];
       __syncthreads();
       for (int li = 0; li < cnt; ++li) {
         const int ent = sm.list[li];
@@ -734,20 +816,21 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs A, int lev) {
         const int bhx = bq * pl.Hq + (kvh % pl.Hkv) * Gq + hl;
         const int32_t* qoffs = b.qs.offs + ((size_t)bhx * pl.P + p) * (C + 1);
         const int32_t* qperm = b.qs.perm + ((size_t)lev * pl.B * pl.Hq + bhx) * pl.N + gm.q0;
-        bk_query_range<TIn, D, false>(sm, A, bhx, qperm, qoffs[Iq], qoffs[Iq + 1], kf, vf, ibias, irow, s2,
-                                      dvt, dkt);
+        bk_query_range<TIn, D, false, NT>(sm, A, bhx, qperm, qoffs[Iq], qoffs[Iq + 1], kf, vf, ibias, irow,
+                                          s2, dvt, dkt);
       }
       __syncthreads();
     }
   } else if (KIND == BK_FAR) {
     const int32_t* qoffs = b.qs.offs + (size_t)ap * (C + 1);
     const int32_t* qperm = b.qs.perm + ((size_t)lev * pl.B * pl.Hq + bh) * pl.N + gm.q0;
-    bk_query_range<TIn, D, false>(sm, A, bh, qperm, qoffs[I], qoffs[I + 1], kf, vf, ibias, -1, s2, dvt, dkt);
+    bk_query_range<TIn, D, false, NT>(sm, A, bh, qperm, qoffs[I], qoffs[I + 1], kf, vf, ibias, -1, s2, dvt,
+                                      dkt);
   } else {
     // local causal block: the queries from the tile's first row to the block end, every head of the group
     for (int hl = 0; hl < Gq; ++hl) {
       const int bhx = bq * pl.Hq + (kvh % pl.Hkv) * Gq + hl;
-      bk_query_range<TIn, D, true>(sm, A, bhx, nullptr, ibeg, blk1, kf, vf, ibias, irow, s2, dvt, dkt);
+      bk_query_range<TIn, D, true, NT>(sm, A, bhx, nullptr, ibeg, blk1, kf, vf, ibias, irow, s2, dvt, dkt);
     }
   }
   if (!ivalid) return;
@@ -1109,11 +1192,11 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
   const long long nq = (long long)pl.B * pl.Hq * pl.N, nk = (long long)pl.B * pl.Hkv * pl.N;
   const size_t bq_smem = sizeof(BqSmem<TIn, D>), bk_smem = sizeof(BkSmem<TIn, D>);
   const size_t bc_smem = sizeof(BcSmem<TIn, D>);
-  set_smem_once((const void*)bwd_q_kernel<TIn, D, BQ_LOCAL>, bq_smem);
-  set_smem_once((const void*)bwd_q_kernel<TIn, D, BQ_PROBLEM>, bq_smem);
-  set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_LOCAL>, bk_smem);
-  set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_EXACT>, bk_smem);
-  set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_FAR>, bk_smem);
+  set_smem_once((const void*)bwd_q_kernel<TIn, D, BQ_LOCAL, 4>, bq_smem);
+  set_smem_once((const void*)bwd_q_kernel<TIn, D, BQ_PROBLEM, 4>, bq_smem);
+  set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_LOCAL, 4>, bk_smem);
+  set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_EXACT, 4>, bk_smem);
+  set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_FAR, 4>, bk_smem);
   set_smem_once((const void*)bwd_bcast_k_kernel<TIn, D>, bc_smem);
   MUSE_KT_PRE(st);
   bwd_zero_kernel<<<(unsigned)((nq * D / 4 + 255) / 256), 256, 0, st>>>(A.dq, nq * D);
@@ -1126,10 +1209,10 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
   if (pl.causal) {
     const long long nblk = (pl.N + pl.blk - 1) / pl.blk, tpb = (pl.blk + 63) / 64;
     MUSE_KT_PRE(st);
-    bwd_q_kernel<TIn, D, BQ_LOCAL><<<(unsigned)(pl.B * pl.Hq * nblk * tpb), 256, bq_smem, st>>>(A, 0);
+    bwd_q_kernel<TIn, D, BQ_LOCAL, 4><<<(unsigned)(pl.B * pl.Hq * nblk * tpb), 256, bq_smem, st>>>(A, 0);
     MUSE_KT_POST("bwd_q_local", st);
     MUSE_KT_PRE(st);
-    bwd_kv_kernel<TIn, D, BK_LOCAL><<<(unsigned)(pl.B * pl.Hkv * nblk * tpb), 256, bk_smem, st>>>(A, 0);
+    bwd_kv_kernel<TIn, D, BK_LOCAL, 4><<<(unsigned)(pl.B * pl.Hkv * nblk * tpb), 256, bk_smem, st>>>(A, 0);
     MUSE_KT_POST("bwd_kv_local", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -1139,30 +1222,42 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
     if (nseg == 0) continue;
     const long long m = pl.lev_m[lev];
     const long long spp = (m + 63) / 64 + C;
+    static const char* const qn[8] = {"bwd_q_L0", "bwd_q_L1", "bwd_q_L2", "bwd_q_L3", "bwd_q_L4", "bwd_q_L5",
+                                      "bwd_q_L6", "bwd_q_L7+"};
+    static const char* const kn[8] = {"bwd_kv_L0", "bwd_kv_L1", "bwd_kv_L2", "bwd_kv_L3", "bwd_kv_L4",
+                                      "bwd_kv_L5", "bwd_kv_L6", "bwd_kv_L7+"};
     MUSE_KT_PRE(st);
-    bwd_q_kernel<TIn, D, BQ_PROBLEM><<<(unsigned)(pl.B * pl.Hq * nseg * spp), 256, bq_smem, st>>>(A, lev);
-    MUSE_KT_POST("bwd_q", st);
+    bwd_q_kernel<TIn, D, BQ_PROBLEM, 4><<<(unsigned)(pl.B * pl.Hq * nseg * spp), 256, bq_smem, st>>>(A, lev);
+    MUSE_KT_POST(qn[lev < 7 ? lev : 7], st);
     MUSE_KT_PRE(st);
-    bwd_kv_kernel<TIn, D, BK_EXACT><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 256, bk_smem, st>>>(A, lev);
-    MUSE_KT_POST("bwd_kv", st);
+    bwd_kv_kernel<TIn, D, BK_EXACT, 4><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 256, bk_smem, st>>>(A, lev);
+    MUSE_KT_POST(kn[lev < 7 ? lev : 7], st);
     MUSE_KT_PRE(st);
-    bwd_kv_kernel<TIn, D, BK_FAR>
+    bwd_kv_kernel<TIn, D, BK_FAR, 4>
         <<<(unsigned)(pl.B * pl.Hq * nseg * C * ((C + 63) / 64)), 256, bk_smem, st>>>(A, lev);
     MUSE_KT_POST("bwd_far", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     MUSE_KT_PRE(st);
     bwd_reduce_k_kernel<<<(unsigned)(pl.B * pl.Hkv * nseg * ((C * D + 255) / 256)), 256, 0, st>>>(A, lev);
+    MUSE_KT_POST("bwd_reduce_k", st);
     if (pl.dipole) {
       GemmDm gdm{pl, lev, (D * C + 63) / 64, (D + 63) / 64, A.dT, A.a.qs.cent, A.dM};
+      MUSE_KT_PRE(st);
       bwd_gemm_kernel<GemmDm, NSG>
           <<<(unsigned)(pl.B * pl.Hkv * nseg * gdm.mtiles * gdm.ntiles), 256, 0, st>>>(gdm);
+      MUSE_KT_POST("bwd_dM", st);
       GemmDnu gdn{pl, lev, (C + 63) / 64, (D + 63) / 64, A.dT, A.a.kst.M, A.dnu};
+      MUSE_KT_PRE(st);
       bwd_gemm_kernel<GemmDnu, NSG>
           <<<(unsigned)(pl.B * pl.Hq * nseg * gdn.mtiles * gdn.ntiles), 256, 0, st>>>(gdn);
+      MUSE_KT_POST("bwd_dnu", st);
+      MUSE_KT_PRE(st);
       bwd_spread_q_kernel<<<(unsigned)((nq * (D / 4) + 255) / 256), 256, 0, st>>>(A, lev);
+      MUSE_KT_POST("bwd_spread_q", st);
     }
+    MUSE_KT_PRE(st);
     bwd_bcast_k_kernel<TIn, D><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 256, bc_smem, st>>>(A, lev);
-    MUSE_KT_POST("bwd_cluster", st);
+    MUSE_KT_POST("bwd_bcast_k", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   MUSE_KT_PRE(st);
