@@ -138,8 +138,10 @@ static void build_kmlarge(const Plan& pl, int heads_total, int dtype, int& ploca
   }
   int64_t pts = 0;
   for (int l = first_large; l < pl.nlev; ++l) pts += (int64_t)heads_total * pl.lev_nseg[l] * pl.lev_m[l];
+  // points per chunk: at least two sub-tiles (fewer partial sums to reduce),
+  // smaller while that leaves fewer than 1024 chunks
   int ch = 2048;
-  while (ch > sub && pts / ch < 1024) ch /= 2;
+  while (ch > 2 * sub && pts / ch < 1024) ch /= 2;
   lg.ch = ch;
   const int ncb = (pl.C + 256 / pl.D - 1) / (256 / pl.D);   // reduce workgroups per problem
   int nl = 0, cf = 0, pf = 0, wf = 0, rf = 0;

@@ -31,7 +31,7 @@ struct KmShape {
   // k-step.  fp32 inputs: bf16 mu
   static constexpr int NP = NS == 1 ? 2 : 1;
   static constexpr int MUP = D + 8;  // padded centroid row (bf16 elements)
-  static constexpr int SUB = (NS == 3 && D == 128) ? 64 : 256;
+  static constexpr int SUB = NS == 1 ? 128 : (D == 128 ? 64 : 256);
   static constexpr int XTP = SUB + 8;  // padded transposed row
   static constexpr int G16 = SUB / 64; // 16-point groups per wave per sub-tile
 };
@@ -40,7 +40,7 @@ template <typename TIn, int D, int CT>
 struct alignas(16) KmSmem {
   using S = KmShape<TIn, D>;
   // fp32 centroids for the refinement step, kept in LDS when small
-  static constexpr bool KEEP32 = CT * 16 * D * 4 <= (S::NS == 1 ? 16384 : 32768);
+  static constexpr bool KEEP32 = S::NS == 3 && CT * 16 * D * 4 <= 32768;
   float mu32[KEEP32 ? CT * 16 : 1][D + 4];
   uint16_t mu_hat[S::NP][CT * 16][S::MUP];
   float mu_norm[CT * 16];
@@ -1033,6 +1033,6 @@ size_t kmeans_smem_bytes(int dtype, int D, int C) {
                  : pick(float{}, std::integral_constant<int, 128>{});
 }
 
-int kmeans_sub(int dtype, int D) { return (dtype == 0 && D == 128) ? 64 : 256; }
+int kmeans_sub(int dtype, int D) { return dtype == 1 ? 128 : (D == 128 ? 64 : 256); }
 
 }  // namespace muse
