@@ -7,17 +7,33 @@
 // items: every key j of a retrieved cluster (logit s q_i.k_j, weight 1,
 // value v_j) and every other non-empty key cluster c (logit s q_i.mu_c,
 // weight n_c, value T_Ic / n_c).  Both kinds go through the same tile loop:
-// a tile is 64 items staged in LDS as rows (A operand of S^T = K Q^T) and as
-// a transposed value block (A operand of O^T = V^T P^T), plus a log-weight
-// per item; one online softmax (base 2) covers all tiles.  The local causal
-// block uses the same loop over contiguous keys with the causal mask.
+// a tile is 64 items, staged in LDS as key rows (A operand of S^T = K Q^T)
+// and as value columns (A operand of O^T = V^T P^T); one online softmax
+// (base 2) covers all tiles.  The local causal block uses the same loop over
+// contiguous keys with the causal mask.
 //
-// Pipeline: the next tile is loaded into registers while the current one is
-// consumed, then written to the other LDS buffer (one barrier per tile).
-// Exact tiles read the cluster-contiguous key/value copies; the row of
-// each item is computed two tiles ahead into a small LDS ring.
-// Each wave holds QG groups of 16 queries so that every K/V fragment read
-// from LDS feeds QG matrix instructions.
+// Tiles.  A far tile is 64 consecutive key clusters (centroid rows, and the
+// columns of T_I, which is stored dim-major).  An exact tile is 64
+// consecutive rows of the cluster-contiguous key copy, starting at a multiple
+// of 8: a retrieved cluster [lo, hi) is covered by tiles from lo rounded down
+// to 8 in steps of 64, and rows outside [lo, hi) are masked.  Values come
+// from a dim-major copy of the same rows (built by vt_kernel), so both halves
+// of a tile are 64 x 16-byte row segments: they are copied global -> LDS by
+// the direct-to-LDS loads, with no register staging and no transposition.
+//
+// Pipeline: ST LDS stages, tile t+ST-1 is in flight while tile t is
+// consumed; one barrier per tile.  The waits on the copies are explicit
+// (s_waitcnt vmcnt with the number of copies issued after the tile), so the
+// loop holds no other global loads.  LDS rows are 16-byte-chunk swizzled so
+// that the fragment reads are free of bank conflicts.
+//
+// Contraction order: the S^T MFMA of row tile rt reads, for its A row c, the
+// key item 32(rt/2) + 8(c/4) + 4(rt%2) + c%4, so that the scores a lane holds
+// for two consecutive row tiles are 8 consecutive items: they pack directly
+// into the P^T operand of the value MFMA, whose V^T operand is then a plain
+// 16-byte read of one value column.
+// Each wave holds QG groups of 16 queries so that every fragment read from
+// LDS feeds QG matrix instructions.
 #include "common.h"
 #include "launch.h"
 
@@ -28,72 +44,150 @@ constexpr int AT_KT = 64;   // items per tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-template <typename TIn, int D, int WAVES, int QG>
-struct alignas(16) AtSmem {
-  static constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
-  static constexpr int NB = NS == 1 ? 2 : 1;   // LDS tile buffers
-  uint16_t ks[NB][NS][AT_KT][D + 8];
-  uint16_t vt[NB][NS][D][AT_KT + 8];
-  float bias[NB][AT_KT];
-  int32_t krow[NB][AT_KT];
-  int32_t ring[4][AT_KT];      // item -> row, up to three tiles ahead
-  int32_t qrow[16 * QG * WAVES];
-  float far_bias[MUSE_MAXC];   // log2 n_c, or -inf (empty or retrieved)
-  int32_t rbeg[MUSE_MAXC];
-  int32_t rcum[MUSE_MAXC + 1];
-  int32_t sel[4];
+// One 16-byte direct-to-LDS copy per lane: lane l's 16 bytes at `src` land
+// at LDS byte lds + 16 l (lds wave-uniform).  Written as assembly so that the
+// compiler does not track it: it would otherwise wait for every copy in
+// flight before any read of the stage array, and the loop's explicit waits
+// cover these copies.  The instruction writes no register.
+__device__ __forceinline__ void lds_copy16(const void* src, const void* lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(a), "v"(src) : "memory", "m0");
+}
+
+// s_waitcnt immediate for vmcnt(v) and lgkmcnt(l), expcnt left alone.
+__host__ __device__ constexpr int at_wait(int v, int l) {
+  return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (l << 8);
+}
+
+template <typename TIn, int D>
+struct AtGeo {
+  static constexpr int E = 16 / (int)sizeof(TIn);            // elements per 16-byte chunk
+  static constexpr int CHK = D / E;                           // chunks per key row
+  static constexpr int CHV = AT_KT / E;                       // chunks per value column row
+  static constexpr int KB = AT_KT * D * (int)sizeof(TIn);     // key block bytes
+  static constexpr int SB = 2 * KB;                           // stage bytes
+  static constexpr int ST = SB <= 16384 ? 3 : 2;              // stages
 };
 
-template <typename TIn, int D, int WAVES>
-struct TileRegs {
-  static constexpr int NT = 64 * WAVES;
-  static constexpr int KC = (AT_KT * D / 8 + NT - 1) / NT;          // 8-wide key chunks
-  static constexpr int VB = ((AT_KT / 4) * (D / 8) + NT - 1) / NT;  // 4 items x 8 dims blocks
-  using V8 = typename std::conditional<sizeof(TIn) == 2, u16x8, f32x8>::type;
-  using V4 = typename std::conditional<sizeof(TIn) == 2, u16x4, f32x4>::type;
-  V8 kf[KC];
-  V4 vf[VB][8];
-  float bias;
-  int krow;
+// chunk swizzles (chunk position = logical chunk ^ key)
+__device__ __forceinline__ int keyk(int r) { return (r & 3) | ((r >> 1) & 4); }
+__device__ __forceinline__ int keyv(int d) { return d & 7; }
+
+// Everything in LDS but the tile stages, which are a __shared__ array of
+// their own: the compiler then sees that reads of these tables cannot alias
+// the copies in flight and does not wait for them.
+template <typename TIn, int D, int WAVES, int QG>
+struct alignas(16) AtSmem {
+  float far_bias[MUSE_MAXC];   // log2 n_c, or -inf (empty or retrieved)
+  int32_t seg_lo[MUSE_MAXC];   // retrieved clusters (non-empty), absolute rows
+  int32_t seg_hi[MUSE_MAXC];
+  int32_t qrow[16 * QG * WAVES];
+  int32_t sel[8];
 };
 
 struct TileSrc {
-  int mode;             // 1: far tiles then exact tiles; 2: local rows
-  int nfar, nex;
-  const void* mu;       // far: [C][D] centroids (input dtype)
-  const void* T;        // far: [D][Cp] T_Ic / n_c of this query cluster (input dtype)
+  const void* Kx;     // key rows, absolute row index (sorted copy or input K)
+  const void* Vt;     // value columns [D][nv] of the same rows
+  int nv;             // Vt row length (multiple of 8)
+  int kmax;           // last key row that may be read
+  const void* mu;     // far: centroid rows [C][D]
+  const void* T;      // far: T_I / n_c, [D][Cp]
   int Ck, Cp;
-  const void* Kp;       // exact: sorted keys of the problem
-  const void* Vp;
-  int nret;
-  const void* K;        // local: keys / values of the head
-  const void* V;
-  int k0, klast;
+  int nfar, nseg;
 };
 
-template <typename TIn, typename V8>
-__device__ __forceinline__ V8 ld8(const TIn* p) {
-  if constexpr (sizeof(TIn) == 2) {
-    return *reinterpret_cast<const u16x8*>(p);
-  } else {
-    f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+// Walks the tile list in order: nfar far tiles, then for each retrieved
+// cluster the tiles covering it.  All fields are wave-uniform.
+struct Cursor {
+  int t, j, row0, lo, hi;
+};
+
+template <typename SM>
+__device__ __forceinline__ Cursor cur_seg(const SM& sm, const TileSrc& src, int t, int j) {
+  const bool ok = j < src.nseg;
+  const int lo = __builtin_amdgcn_readfirstlane(sm.seg_lo[ok ? j : 0]);
+  const int hi = __builtin_amdgcn_readfirstlane(sm.seg_hi[ok ? j : 0]);
+  Cursor c;
+  c.t = t;
+  c.j = j;
+  c.lo = ok ? lo : 0;
+  c.hi = ok ? hi : 0;
+  c.row0 = c.lo & ~7;
+  return c;
+}
+
+template <typename SM>
+__device__ __forceinline__ Cursor cur_first(const SM& sm, const TileSrc& src) {
+  Cursor c = cur_seg(sm, src, 0, 0);
+  if (src.nfar > 0) c.row0 = 0;
+  return c;
+}
+
+template <typename SM>
+__device__ __forceinline__ Cursor cur_next(const SM& sm, const TileSrc& src, Cursor c) {
+  const int t = c.t + 1;
+  if (t < src.nfar) {
+    c.t = t;
+    c.row0 = AT_KT * t;
+    return c;
+  }
+  if (t == src.nfar) return cur_seg(sm, src, t, 0);
+  if (c.row0 + AT_KT >= c.hi && c.j < src.nseg) return cur_seg(sm, src, t, c.j + 1);
+  c.t = t;
+  c.row0 += AT_KT;
+  return c;
+}
+
+// Copy tile (cursor c) into stage s: every thread issues the same number of
+// 16-byte direct-to-LDS loads; rows past the end read clamped, valid rows.
+template <typename TIn, int D, int WAVES>
+__device__ __forceinline__ void issue_tile(unsigned char* stg, const TileSrc& src, const Cursor& c) {
+  using G = AtGeo<TIn, D>;
+  constexpr int NT = 64 * WAVES;
+  static_assert(AT_KT * G::CHK % NT == 0 && D * G::CHV % NT == 0, "copies must cover the workgroup");
+  const int tid = threadIdx.x, w = tid >> 6;
+  const bool far = c.t < src.nfar;
+  unsigned char* kst = stg;
+  unsigned char* vst = stg + G::KB;
+  const TIn* kb = reinterpret_cast<const TIn*>(far ? src.mu : src.Kx);
+  const int kcap = far ? src.Ck - 1 : src.kmax;
+#pragma unroll
+  for (int m = 0; m < AT_KT * G::CHK / NT; ++m) {
+    const int ci = m * NT + tid;
+    const int r = ci / G::CHK, pos = ci % G::CHK;
+    const int row = min(c.row0 + r, kcap);
+    const TIn* p = kb + (size_t)row * D + (pos ^ keyk(r)) * G::E;
+    lds_copy16(p, kst + (m * NT + 64 * w) * 16);
+  }
+  const TIn* vb = reinterpret_cast<const TIn*>(far ? src.T : src.Vt);
+  const int vstride = far ? src.Cp : src.nv;
+  const int vcap = far ? src.Cp - G::E : src.nv - G::E;
+#pragma unroll
+  for (int m = 0; m < D * G::CHV / NT; ++m) {
+    const int ci = m * NT + tid;
+    const int d = ci / G::CHV, pos = ci % G::CHV;
+    const int col = min(c.row0 + (pos ^ keyv(d)) * G::E, vcap);
+    const TIn* p = vb + (size_t)d * vstride + col;
+    lds_copy16(p, vst + (m * NT + 64 * w) * 16);
   }
 }
 
-template <typename TIn, typename V4>
-__device__ __forceinline__ V4 ld4(const TIn* p) {
-  if constexpr (sizeof(TIn) == 2) return *reinterpret_cast<const u16x4*>(p);
-  else return *reinterpret_cast<const f32x4*>(p);
-}
-
-template <int NS, typename ST>
-__device__ __forceinline__ void to_parts(ST x, uint16_t& a, uint16_t& b, uint16_t& c) {
-  if constexpr (sizeof(ST) == 2) {
-    a = x; b = 0; c = 0;
+// 8 consecutive elements (logical 8-element group lg of a row) as NS bf16 parts.
+template <typename TIn, int NS>
+__device__ __forceinline__ void lds_frag(const unsigned char* row, int lg, int key, u16x8* out) {
+  if constexpr (sizeof(TIn) == 2) {
+    out[0] = *reinterpret_cast<const u16x8*>(row + ((lg ^ key) << 4));
   } else {
-    split3(x, a, b, c);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + (((2 * lg) ^ key) << 4));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(row + (((2 * lg + 1) ^ key) << 4));
+    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint16_t h, m, l;
+      split3(v[j], h, m, l);
+      out[0][j] = h;
+      if (NS > 1) { out[NS > 1 ? 1 : 0][j] = m; out[NS > 2 ? 2 : 0][j] = l; }
+    }
   }
 }
 
@@ -104,195 +198,72 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Row of item `it` of tile t (exact: sorted position; local: absolute row).
-template <typename SM>
-__device__ __forceinline__ int item_row(const SM& sm, const TileSrc& src, int t, int it) {
-  if (src.mode == 2) {
-    const int j = src.k0 + t * AT_KT + it;
-    return j <= src.klast ? j : -1;
-  }
-  if (t < src.nfar) return -1;
-  const int v = (t - src.nfar) * AT_KT + it;
-  if (v >= src.nret) return -1;
-  int r = 0;
-  while (sm.rcum[r + 1] <= v) ++r;
-  return sm.rbeg[r] + (v - sm.rcum[r]);
-}
-
-template <typename TIn, int D, int WAVES, int QG>
-__device__ __forceinline__ void tile_load(const AtSmem<TIn, D, WAVES, QG>& sm, const TileSrc& src, int t,
-                                          TileRegs<TIn, D, WAVES>& R) {
-  using TR = TileRegs<TIn, D, WAVES>;
-  constexpr int NT = TR::NT;
-  const int tid = threadIdx.x;
-  const bool far = src.mode == 1 && t < src.nfar;
-  const int base = t * AT_KT;
-  const int* ring = sm.ring[t & 3];
-#pragma unroll
-  for (int q = 0; q < TR::KC; ++q) {
-    const int idx = tid + q * NT;
-    const int it = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
-    const TIn* p = nullptr;
-    if (idx < AT_KT * D / 8) {
-      if (far) {
-        if (base + it < src.Ck) p = reinterpret_cast<const TIn*>(src.mu) + (size_t)(base + it) * D + e0;
-      } else {
-        const int row = ring[it];
-        if (row >= 0)
-          p = reinterpret_cast<const TIn*>(src.mode == 1 ? src.Kp : src.K) + (size_t)row * D + e0;
-      }
-    }
-    R.kf[q] = p ? ld8<TIn, typename TR::V8>(p) : typename TR::V8{};
-  }
-  // value blocks: items 4kb..4kb+3 x dims e0..e0+7, kb fastest across lanes
-#pragma unroll
-  for (int q = 0; q < TR::VB; ++q) {
-    const int idx = tid + q * NT;
-    const int kb = idx % (AT_KT / 4), e0 = (idx / (AT_KT / 4)) * 8;
-    if (idx >= (AT_KT / 4) * (D / 8)) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) R.vf[q][j] = typename TR::V4{};
-    } else if (far) {
-      const TIn* p = reinterpret_cast<const TIn*>(src.T) + (size_t)e0 * src.Cp + base + 4 * kb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) R.vf[q][j] = ld4<TIn, typename TR::V4>(p + (size_t)j * src.Cp);
-    } else {
-      typename TR::V8 rowv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = ring[4 * kb + r];
-        rowv[r] = row >= 0 ? ld8<TIn, typename TR::V8>(
-                                 reinterpret_cast<const TIn*>(src.mode == 1 ? src.Vp : src.V) +
-                                 (size_t)row * D + e0)
-                           : typename TR::V8{};
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) R.vf[q][j][r] = rowv[r][j];
-    }
-  }
-  if (tid < AT_KT) {
-    if (far) {
-      R.bias = base + tid < src.Ck ? sm.far_bias[base + tid] : -INFINITY;
-      R.krow = -1;
-    } else {
-      const int row = ring[tid];
-      R.bias = row >= 0 ? 0.f : -INFINITY;
-      R.krow = row;
-    }
-  }
-}
-
-template <typename TIn, int D, int WAVES, int QG>
-__device__ __forceinline__ void tile_store(AtSmem<TIn, D, WAVES, QG>& sm, int buf,
-                                           const TileRegs<TIn, D, WAVES>& R) {
-  using TR = TileRegs<TIn, D, WAVES>;
-  constexpr int NS = AtSmem<TIn, D, WAVES, QG>::NS;
-  constexpr int NT = TR::NT;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int q = 0; q < TR::KC; ++q) {
-    const int idx = tid + q * NT;
-    if (idx < AT_KT * D / 8) {
-      const int it = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
-      if constexpr (NS == 1) {
-        *reinterpret_cast<u16x8*>(&sm.ks[buf][0][it][e0]) = R.kf[q];
-      } else {
-        u16x8 h[NS];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          uint16_t a, b, c;
-          to_parts<NS>(R.kf[q][j], a, b, c);
-          h[0][j] = a; h[NS > 1 ? 1 : 0][j] = b; h[NS > 2 ? 2 : 0][j] = c;
-        }
-#pragma unroll
-        for (int sp = 0; sp < NS; ++sp) *reinterpret_cast<u16x8*>(&sm.ks[buf][sp][it][e0]) = h[sp];
-      }
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < TR::VB; ++q) {
-    const int idx = tid + q * NT;
-    if (idx < (AT_KT / 4) * (D / 8)) {
-      const int kb = idx % (AT_KT / 4), e0 = (idx / (AT_KT / 4)) * 8;
-      // items 4kb..4kb+3 land at their contraction slots: within a 32-item
-      // block, item r sits at 8(r/4 % 4) + 4(r/16) + r%4
-      const int vpos = 32 * (kb / 8) + 8 * (kb % 4) + 4 * ((kb % 8) / 4);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if constexpr (NS == 1) {
-          *reinterpret_cast<u16x4*>(&sm.vt[buf][0][e0 + j][vpos]) = R.vf[q][j];
-        } else {
-          u16x4 h[NS];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            uint16_t a, b, c;
-            to_parts<NS>(R.vf[q][j][r], a, b, c);
-            h[0][r] = a; h[NS > 1 ? 1 : 0][r] = b; h[NS > 2 ? 2 : 0][r] = c;
-          }
-#pragma unroll
-          for (int sp = 0; sp < NS; ++sp) *reinterpret_cast<u16x4*>(&sm.vt[buf][sp][e0 + j][vpos]) = h[sp];
-        }
-      }
-    }
-  }
-  if (tid < AT_KT) {
-    sm.bias[buf][tid] = R.bias;
-    sm.krow[buf][tid] = R.krow;
-  }
-}
-
 template <int D>
 struct AtState {
   float m, lpart;         // running max (base 2) and this lane's partial sum
   f32x4 o[D / 16];
 };
 
-// Consume a staged tile for the QG query groups of this wave.
+// Consume the tile (cursor c) staged in stage s for the QG query groups of
+// this wave.  Score slot (rt, 4g + i) of a lane is item
+// 32(rt/2) + 8g + 4(rt%2) + i of the tile.
 template <typename TIn, int D, int WAVES, int QG, bool CAUSAL>
-__device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm, int buf,
-                                             const u16x8 (&qf)[QG][D / 32][AtSmem<TIn, D, WAVES, QG>::NS],
+__device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm, const unsigned char* stg,
+                                             const Cursor& c,
+                                             bool far,
+                                             const u16x8 (&qf)[QG][D / 32][sizeof(TIn) == 2 ? 1 : 3],
                                              AtState<D> (&st)[QG], float s2, const int (&qrow)[QG]) {
-  constexpr int NS = AtSmem<TIn, D, WAVES, QG>::NS;
+  using G = AtGeo<TIn, D>;
+  constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
   constexpr int KS = D / 32, DT = D / 16;
   constexpr int RT = AT_KT / 16, PS = AT_KT / 32;
+  constexpr int KROW = D * (int)sizeof(TIn), VROW = AT_KT * (int)sizeof(TIn);
   const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+  const unsigned char* kst = stg;
+  const unsigned char* vst = stg + G::KB;
   f32x4 sc[QG][RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
+    const int r = 32 * (rt >> 1) + 8 * (col >> 2) + 4 * (rt & 1) + (col & 3);
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) sc[qg][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       u16x8 a[NS];
-#pragma unroll
-      for (int sp = 0; sp < NS; ++sp)
-        a[sp] = *reinterpret_cast<const u16x8*>(&sm.ks[buf][sp][16 * rt + col][32 * k + 8 * g]);
+      lds_frag<TIn, NS>(kst + r * KROW, 4 * k + g, keyk(r), a);
 #pragma unroll
       for (int qg = 0; qg < QG; ++qg) sc[qg][rt] = mfma_split<NS, NS>(a, qf[qg][k], sc[qg][rt]);
     }
   }
+  // log-weights of the lane's items (far), or which rows lie in [lo, hi)
+  // (exact: a masked row's logit is replaced, not offset, since rows outside
+  // the key segments of a level hold unspecified values)
   f32x4 bv[RT];
-  int4 kr[RT];
+  uint32_t ok = 0;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    bv[rt] = *reinterpret_cast<const f32x4*>(&sm.bias[buf][16 * rt + 4 * g]);
-    if (CAUSAL) kr[rt] = *reinterpret_cast<const int4*>(&sm.krow[buf][16 * rt + 4 * g]);
+    const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
+    if (far) {
+      bv[rt] = *reinterpret_cast<const f32x4*>(&sm.far_bias[c.row0 + it0]);
+    } else {
+      bv[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((unsigned)(c.row0 + it0 + i - c.lo) < (unsigned)(c.hi - c.lo)) ok |= 1u << (rt * 4 + i);
+    }
   }
+  if (far) ok = 0xffffu;
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     float x[RT * 4];
     float mloc = -INFINITY;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
+      const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v = fmaf(s2, sc[qg][rt][i], bv[rt][i]);
-        if (CAUSAL) {
-          const int krow = i == 0 ? kr[rt].x : i == 1 ? kr[rt].y : i == 2 ? kr[rt].z : kr[rt].w;
-          if (krow > qrow[qg]) v = -INFINITY;
-        }
+        float v = (ok >> (rt * 4 + i)) & 1u ? fmaf(s2, sc[qg][rt][i], bv[rt][i]) : -INFINITY;
+        if (CAUSAL && c.row0 + it0 + i > qrow[qg]) v = -INFINITY;
         x[rt * 4 + i] = v;
         mloc = fmaxf(mloc, v);
       }
@@ -301,13 +272,13 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
     const float mnew = fmaxf(st[qg].m, mloc);
     const float alpha = __builtin_amdgcn_exp2f(st[qg].m - mnew);
-    float psum = 0.f;
+    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < RT * 4; ++j) {
       x[j] = __builtin_amdgcn_exp2f(x[j] - mnew);
-      psum += x[j];
+      ps4[j & 3] += x[j];
     }
-    st[qg].lpart = st[qg].lpart * alpha + psum;
+    st[qg].lpart = st[qg].lpart * alpha + ((ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
     st[qg].m = mnew;
     if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -315,7 +286,7 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
     }
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) {
-      // contraction slots of two 16-row tiles: 8g+j -> 4g+j (j<4), 16+4g+(j-4) (j>=4)
+      // P^T slots 8g + j: items 32ps + 8g + j
       u16x8 pb[NS];
       if constexpr (NS == 1) {
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -331,13 +302,11 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
           pb[0][j] = h; pb[NS > 1 ? 1 : 0][j] = mm; pb[NS > 2 ? 2 : 0][j] = l;
         }
       }
-      // V^T fragments of this 32-item block (read per query group: fewer live registers)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + col;
         u16x8 va[NS];
-#pragma unroll
-        for (int sp = 0; sp < NS; ++sp)
-          va[sp] = *reinterpret_cast<const u16x8*>(&sm.vt[buf][sp][16 * dt + col][32 * ps + 8 * g]);
+        lds_frag<TIn, NS>(vst + d * VROW, 4 * ps + g, keyv(d), va);
         st[qg].o[dt] = mfma_split<NS, NS>(va, pb, st[qg].o[dt]);
       }
     }
@@ -345,13 +314,17 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
 }
 
 template <typename TIn, typename TOut, int D, int WAVES, int QG, int MODE>
-__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D == 64 && WAVES == 4 ? 2 : 1)))
-attn_kernel(Plan pl, AttnBufs b, int lev) {
+__global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, int lev) {
   using SM = AtSmem<TIn, D, WAVES, QG>;
-  constexpr int NS = SM::NS, NB = SM::NB;
+  using G = AtGeo<TIn, D>;
+  constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
   constexpr int NT = 64 * WAVES, QT = 16 * QG * WAVES;
   constexpr int KS = D / 32, DT = D / 16;
+  constexpr int ST = G::ST, PD = ST - 1;
+  constexpr int LPT = (AT_KT * G::CHK + D * G::CHV) / NT;   // copies per thread per tile
+  static_assert(PD * LPT <= 63, "copies in flight exceed the counter");
   __shared__ SM sm;
+  __shared__ __attribute__((aligned(16))) unsigned char stg[ST][G::SB];   // tile stages [key rows | value columns]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
   const float s2 = pl.scale * LOG2E;
@@ -446,8 +419,14 @@ attn_kernel(Plan pl, AttnBufs b, int lev) {
     }
     sm.qrow[r] = row;
   }
+  const size_t esz = sizeof(TIn);
   TileSrc src;
-  src.mode = MODE == MODE_LOCAL ? 2 : 1;
+  src.nv = b.Nv;
+  src.kmax = pl.N - 1;
+  src.Ck = 1;
+  src.Cp = b.Cp32;
+  src.mu = b.kst.mu_in;
+  src.T = b.T;
   src.nfar = 0;
   if (MODE != MODE_LOCAL) {
     const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
@@ -462,13 +441,15 @@ attn_kernel(Plan pl, AttnBufs b, int lev) {
     }
     int cc[4];
     if (tid < 64) {
-      int v[4], bg[4], sum = 0;
+      // compact the non-empty retrieved clusters into segments of absolute rows
+      int lo[4], hi[4], v[4], sum = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = tid * 4 + q;
         cc[q] = r < pl.k1w ? Rr[r] : -1;
-        bg[q] = cc[q] >= 0 ? koffs[cc[q]] : 0;
-        v[q] = cc[q] >= 0 ? koffs[cc[q] + 1] - bg[q] : 0;
+        lo[q] = cc[q] >= 0 ? koffs[cc[q]] : 0;
+        hi[q] = cc[q] >= 0 ? koffs[cc[q] + 1] : 0;
+        v[q] = hi[q] > lo[q] ? 1 : 0;
         sum += v[q];
       }
       int inc = sum;
@@ -477,14 +458,20 @@ attn_kernel(Plan pl, AttnBufs b, int lev) {
         if (tid >= mm) inc += o;
       }
       int run = inc - sum;
+      int ntl = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = tid * 4 + q;
-        sm.rbeg[r] = bg[q];
-        sm.rcum[r] = run;
-        run += v[q];
+        if (v[q]) {
+          const int alo = k0 + lo[q], ahi = k0 + hi[q];
+          sm.seg_lo[run] = alo;
+          sm.seg_hi[run] = ahi;
+          ntl += (ahi - (alo & ~7) + AT_KT - 1) / AT_KT;
+          ++run;
+        }
       }
-      if (tid == 63) sm.rcum[MUSE_MAXC] = inc;
+      // total exact tiles
+      for (int mm = 32; mm >= 1; mm >>= 1) ntl += __shfl_xor(ntl, mm, 64);
+      if (tid == 63) { sm.sel[4] = inc; sm.sel[5] = ntl; }   // inclusive total, and the all-reduced count
     }
     __syncthreads();
     // retrieved clusters leave the far field
@@ -493,47 +480,51 @@ attn_kernel(Plan pl, AttnBufs b, int lev) {
       for (int q = 0; q < 4; ++q)
         if (cc[q] >= 0) sm.far_bias[cc[q]] = -INFINITY;
     }
-    src.nret = sm.rcum[MUSE_MAXC];
+    src.nseg = __builtin_amdgcn_readfirstlane(sm.sel[4]);
     src.nfar = (Ck + AT_KT - 1) / AT_KT;
-    src.nex = (src.nret + AT_KT - 1) / AT_KT;
-    src.mu = reinterpret_cast<const TIn*>(b.kst.mu_in) + (size_t)kp * C * D;
-    src.T = reinterpret_cast<const TIn*>(b.T) + ((size_t)ap * C + I) * D * b.Cp32;
-    src.Ck = Ck;
-    src.Cp = b.Cp32;
-    const size_t kb = (((size_t)lev * pl.B * pl.Hkv + kvh) * pl.N + k0) * D;
-    src.Kp = reinterpret_cast<const TIn*>(b.kst.Kp) + kb;
-    src.Vp = reinterpret_cast<const TIn*>(b.kst.Vp) + kb;
+    src.Ck = max(Ck, 1);
+    src.mu = reinterpret_cast<const unsigned char*>(b.kst.mu_in) + (size_t)kp * C * D * esz;
+    src.T = reinterpret_cast<const unsigned char*>(b.T) + ((size_t)ap * C + I) * D * b.Cp32 * esz;
+    const size_t slice = (size_t)lev * pl.B * pl.Hkv + kvh;
+    src.Kx = reinterpret_cast<const unsigned char*>(b.kst.Kp) + slice * pl.N * D * esz;
+    src.Vt = reinterpret_cast<const unsigned char*>(b.Vt) + slice * D * (size_t)b.Nv * esz;
   } else {
-    src.K = reinterpret_cast<const TIn*>(b.K) + (size_t)kvh * pl.N * D;
-    src.V = reinterpret_cast<const TIn*>(b.V) + (size_t)kvh * pl.N * D;
-    src.k0 = k0;
-    src.klast = qhi - 1;
-    src.nex = (qhi - k0 + AT_KT - 1) / AT_KT;
-  }
-  const int ntiles = src.nfar + src.nex;
-  if (tid < AT_KT) {
-    sm.ring[0][tid] = item_row(sm, src, 0, tid);
-    sm.ring[1][tid] = item_row(sm, src, 1, tid);
-    sm.ring[2][tid] = item_row(sm, src, 2, tid);
+    // the block's keys up to its last query row
+    if (tid == 0) {
+      sm.seg_lo[0] = k0;
+      sm.seg_hi[0] = qhi;
+    }
+    src.nseg = 1;
+    src.Kx = reinterpret_cast<const TIn*>(b.K) + (size_t)kvh * pl.N * D;
+    const size_t slice = (size_t)pl.nlev * pl.B * pl.Hkv + kvh;   // input-order copy follows the levels
+    src.Vt = reinterpret_cast<const unsigned char*>(b.Vt) + slice * D * (size_t)b.Nv * esz;
   }
   __syncthreads();
+  const int ntiles = MODE == MODE_LOCAL ? (qhi - (k0 & ~7) + AT_KT - 1) / AT_KT
+                                        : src.nfar + __builtin_amdgcn_readfirstlane(sm.sel[5]);
 
+  // ---- tile loop ----
+  Cursor lc = cur_first(sm, src), cc = lc;
+#pragma unroll
+  for (int p = 0; p < PD; ++p) {
+    issue_tile<TIn, D, WAVES>(stg[p], src, lc);
+    lc = cur_next(sm, src, lc);
+  }
+  // query fragments (loaded after the first copies are on their way)
   int myq[QG];
   u16x8 qf[QG][KS][NS];
   AtState<D> st[QG];
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     myq[qg] = sm.qrow[(w * QG + qg) * 16 + col];
+    // lanes without a query row load row 0; their outputs are not written
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      if (myq[qg] >= 0) {
-        load8_split<TIn, NS>(Qh + (size_t)myq[qg] * D + 32 * k + 8 * g, qf[qg][k]);
-      } else {
+      load8_split<TIn, NS>(Qh + (size_t)max(myq[qg], 0) * D + 32 * k + 8 * g, qf[qg][k]);
+      // keep the fragments in registers (a read-only load could otherwise be
+      // re-issued inside the tile loop)
 #pragma unroll
-        for (int sp = 0; sp < NS; ++sp)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) qf[qg][k][sp][j] = 0;
-      }
+      for (int sp = 0; sp < NS; ++sp) asm volatile("" : "+v"(qf[qg][k][sp]));
     }
     st[qg].m = -1e30f;
     st[qg].lpart = 0.f;
@@ -542,44 +533,25 @@ attn_kernel(Plan pl, AttnBufs b, int lev) {
   }
   int qmask[QG];
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg) qmask[qg] = myq[qg] < 0 ? 0x7fffffff : myq[qg];
+  for (int qg = 0; qg < QG; ++qg) qmask[qg] = myq[qg] < 0 ? -1 : myq[qg];
 
-  if constexpr (NB == 2) {
-    // two tiles in flight in registers: the loads of tile t+2 are issued
-    // before tile t is consumed and written to LDS after tile t+1 is
-    TileRegs<TIn, D, WAVES> R0, R1;
-    if (ntiles > 0) tile_load(sm, src, 0, R0);
-    if (ntiles > 1) tile_load(sm, src, 1, R1);
-    if (ntiles > 0) tile_store(sm, 0, R0);
-    __syncthreads();
-    auto step = [&](int t, TileRegs<TIn, D, WAVES>& Rload, const TileRegs<TIn, D, WAVES>& Rstore) {
-      if (tid < AT_KT && t + 3 < ntiles) sm.ring[(t + 3) & 3][tid] = item_row(sm, src, t + 3, tid);
-      if (t + 2 < ntiles) tile_load(sm, src, t + 2, Rload);
-      consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, t & 1, qf, st, s2, qmask);
-      if (t + 1 < ntiles) tile_store(sm, (t + 1) & 1, Rstore);
-      __syncthreads();
-    };
-    for (int t = 0; t < ntiles; t += 2) {
-      step(t, R0, R1);
-      if (t + 1 < ntiles) step(t + 1, R1, R0);
-    }
-  } else {
-    TileRegs<TIn, D, WAVES> R;
-    if (ntiles > 0) {
-      tile_load(sm, src, 0, R);
-      tile_store(sm, 0, R);
-    }
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      const bool more = t + 1 < ntiles;
-      if (tid < AT_KT && t + 2 < ntiles) sm.ring[(t + 2) & 3][tid] = item_row(sm, src, t + 2, tid);
-      if (more) tile_load(sm, src, t + 1, R);
-      consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, 0, qf, st, s2, qmask);
-      __syncthreads();
-      if (more) tile_store(sm, 0, R);
-      __syncthreads();
-    }
+  int sl = PD % ST, sc_ = 0;   // stage of the next copy, stage being consumed
+  for (int t = 0; t < ntiles; ++t) {
+    // this thread's copies of tile t have landed (PD-1 later tiles may be in
+    // flight); after the barrier every thread's have, and tile t-1 is consumed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(at_wait((PD - 1) * LPT, 0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue_tile<TIn, D, WAVES>(stg[sl], src, lc);
+    lc = cur_next(sm, src, lc);
+    consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, stg[sc_], cc, cc.t < src.nfar, qf, st, s2, qmask);
+    cc = cur_next(sm, src, cc);
+    sl = sl + 1 == ST ? 0 : sl + 1;
+    sc_ = sc_ + 1 == ST ? 0 : sc_ + 1;
   }
+  // no copy into LDS may still be in flight when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(at_wait(0, 0));
 
   // ---- finish: normalise, write or merge (lse in natural log units) ----
 #pragma unroll
@@ -631,6 +603,45 @@ attn_kernel(Plan pl, AttnBufs b, int lev) {
   }
 }
 
+// Dim-major copies of the values: slice s < nsorted is the cluster-contiguous
+// copy of level/head s, the next B*Hkv slices are the input V.  Vt[s][d][j]
+// = V_s[j][d] for the rows j that hold values, zero for the others and for
+// N <= j < Nv.
+template <typename TIn, int D>
+__global__ void __launch_bounds__(256) vt_kernel(Plan pl, const void* Vp, const void* V, void* Vt, int Nv,
+                                                 int nsorted) {
+  const int N = pl.N;
+  constexpr int E = 16 / (int)sizeof(TIn), CH = D / E;
+  using V16 = typename std::conditional<sizeof(TIn) == 2, u16x8, f32x4>::type;
+  __shared__ TIn tile[AT_KT][D + 2];
+  const int nb = (Nv + AT_KT - 1) / AT_KT;
+  const int s = blockIdx.x / nb, blk = blockIdx.x % nb;
+  const TIn* src = s < nsorted ? reinterpret_cast<const TIn*>(Vp) + (size_t)s * N * D
+                               : reinterpret_cast<const TIn*>(V) + (size_t)(s - nsorted) * N * D;
+  TIn* dst = reinterpret_cast<TIn*>(Vt) + (size_t)s * D * Nv;
+  const int j0 = blk * AT_KT;
+  // causal levels: only the key segments [2tm, 2tm + m) of a level's sorted
+  // copy are written; every other column becomes zero
+  const int m = s < nsorted && pl.causal ? pl.lev_m[s / (pl.B * pl.Hkv)] : 0;
+  for (int idx = threadIdx.x; idx < AT_KT * CH; idx += 256) {
+    const int r = idx / CH, e0 = (idx % CH) * E;
+    const int j = j0 + r;
+    V16 v{};
+    if (j < N && (m == 0 || (j / m) % 2 == 0)) v = *reinterpret_cast<const V16*>(src + (size_t)j * D + e0);
+#pragma unroll
+    for (int e = 0; e < E; ++e) tile[r][e0 + e] = v[e];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < D * (AT_KT / E); idx += 256) {
+    const int d = idx / (AT_KT / E), jj = (idx % (AT_KT / E)) * E;
+    if (j0 + jj >= Nv) continue;
+    V16 v;
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = tile[jj + e][d];
+    *reinterpret_cast<V16*>(dst + (size_t)d * Nv + j0 + jj) = v;
+  }
+}
+
 template <typename TOut>
 __global__ void finalize_kernel(const float* oacc, const float* lacc, TOut* O, float* lse,
                                 long long rows, int D) {
@@ -641,6 +652,18 @@ __global__ void finalize_kernel(const float* oacc, const float* lacc, TOut* O, f
 }
 
 // ---------------------------------------------------------------------------
+template <typename TIn, int D>
+static hipError_t launch_vt(const Plan& pl, const AttnBufs& b, hipStream_t st) {
+  const int nsorted = pl.nlev * pl.B * pl.Hkv;
+  const int nslice = nsorted + (pl.causal ? pl.B * pl.Hkv : 0);
+  const long long grid = (long long)nslice * ((b.Nv + AT_KT - 1) / AT_KT);
+  if (grid == 0) return hipSuccess;
+  MUSE_KT_PRE(st);
+  vt_kernel<TIn, D><<<(unsigned)grid, 256, 0, st>>>(pl, b.kst.Vp, b.V, b.Vt, b.Nv, nsorted);
+  MUSE_KT_POST("value_transpose", st);
+  return hipGetLastError();
+}
+
 template <typename TIn, int D, int WAVES, int QG>
 static hipError_t attn_level(const Plan& pl, const AttnBufs& b, int lev, hipStream_t st) {
   constexpr int QT = 16 * QG * WAVES;
@@ -659,7 +682,8 @@ static hipError_t attn_level(const Plan& pl, const AttnBufs& b, int lev, hipStre
 
 template <typename TIn, int D>
 static hipError_t attn_all(const Plan& pl, const AttnBufs& b, hipStream_t st) {
-  hipError_t e = hipSuccess;
+  hipError_t e = launch_vt<TIn, D>(pl, b, st);
+  if (e != hipSuccess) return e;
   constexpr int QG = sizeof(TIn) == 2 ? 2 : 1;
   if (pl.causal) {
     constexpr int WAVES = 4, QT = 16 * QG * 4;
@@ -676,7 +700,8 @@ static hipError_t attn_all(const Plan& pl, const AttnBufs& b, hipStream_t st) {
     const int avg = pl.lev_m[lev] / (pl.C > 0 ? pl.C : 1);
     if (QG == 2 && avg >= 160) e = attn_level<TIn, D, 4, QG>(pl, b, lev, st);
     else if (avg >= 48) e = attn_level<TIn, D, 4, 1>(pl, b, lev, st);
-    else e = attn_level<TIn, D, 1, 1>(pl, b, lev, st);
+    else if constexpr (sizeof(TIn) == 2 || D == 64) e = attn_level<TIn, D, 1, 1>(pl, b, lev, st);
+    else e = attn_level<TIn, D, 4, 1>(pl, b, lev, st);   // one wave could not keep a tile's copies counted
     if (e != hipSuccess) return e;
   }
   if (pl.causal) {

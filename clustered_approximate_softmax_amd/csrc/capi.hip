@@ -183,6 +183,7 @@ static void build_layout(const Plan& pl, int dtype, Layout& out) {
   L.C = pl.C;
   L.k1w = pl.k1w;
   L.Cp32 = (pl.C + 63) / 64 * 64;   // T rows padded to whole 64-cluster tiles
+  L.Nv = (pl.N + 7) / 8 * 8;         // value-column rows padded to whole 16-byte chunks
   size_t o = 0;
   L.q_labels = o; o = al(o + nl * BHq * N * 4);
   L.k_labels = o; o = al(o + nl * BHk * N * 4);
@@ -206,6 +207,7 @@ static void build_layout(const Plan& pl, int dtype, Layout& out) {
   L.ws_T = w; w = al(w + BHq * P * C * D * L.Cp32 * eb);
   L.ws_oacc = w; w = al(w + (pl.causal ? BHq * N * D * 4 : 0));
   L.ws_lacc = w; w = al(w + (pl.causal ? BHq * N * 4 : 0));
+  L.ws_Vt = w; w = al(w + (nl + (pl.causal ? 1 : 0)) * BHk * D * (size_t)L.Nv * eb);
   size_t kp_bytes, kc_bytes;
   km_ws_bytes(out.lg, pl.C, pl.D, kp_bytes, kc_bytes);
   L.ws_part = w; w = al(w + kp_bytes);
@@ -325,6 +327,8 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
   ab.Cp32 = (int32_t)L.Cp32;
   ab.oacc = (float*)(wb + L.ws_oacc);
   ab.lacc = (float*)(wb + L.ws_lacc);
+  ab.Vt = wb + L.ws_Vt;
+  ab.Nv = (int32_t)L.Nv;
   ab.O = O;
   ab.lse = lse;
   hipError_t e = hipGetLastError();  // clear stale errors from earlier calls

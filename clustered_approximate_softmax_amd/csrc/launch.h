@@ -52,6 +52,8 @@ struct AttnBufs {
   int32_t* R;             // [B*Hq][P][C][k1w]
   void* T;                // [B*Hq][P][C][D][Cp32] T_Ic / n_c in the input dtype (I, d, c)
   int32_t Cp32;           // C rounded up to 32
+  void* Vt;               // value columns: [nlev*B*Hkv sorted copies (+ B*Hkv input V)][D][Nv]
+  int32_t Nv;             // N rounded up to 8
   float* oacc;            // causal running output [B*Hq][N][D] (fp32)
   float* lacc;            // causal running lse [B*Hq][N]
   void* O; float* lse;    // outputs

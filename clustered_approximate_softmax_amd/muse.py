@@ -40,9 +40,9 @@ class muse_cfg(ctypes.Structure):
                 ("dipole", ctypes.c_int32), ("reserved", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
-LAYOUT_FIELDS = ["P", "L", "C", "k1w", "Cp32"]
+LAYOUT_FIELDS = ["P", "L", "C", "k1w", "Cp32", "Nv"]
 LAYOUT_OFFS = ["q_labels", "k_labels", "q_perm", "k_perm", "q_offs", "k_offs", "q_cent", "k_cent",
-               "mu", "S", "M", "R", "Kp", "Vp", "mu_in", "state_bytes", "ws_T", "ws_oacc", "ws_lacc", "ws_part",
+               "mu", "S", "M", "R", "Kp", "Vp", "mu_in", "state_bytes", "ws_T", "ws_oacc", "ws_lacc", "ws_Vt", "ws_part",
                "ws_pcnt", "ws_bytes"]
 
 

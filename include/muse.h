@@ -76,7 +76,8 @@ typedef struct {
  * Byte offsets of the arrays held in the `state` buffer that museattn_fwd
  * fills and museattn_bwd reads (the fixed assignments of the backward).
  * P = problems per head (1 when acausal), L = levels (1 when acausal),
- * C = cq, k1w = max(1, min(topk, C)), Cp32 = C rounded up to a multiple of 64.
+ * C = cq, k1w = max(1, min(topk, C)), Cp32 = C rounded up to a multiple of 64,
+ * Nv = N rounded up to a multiple of 8.
  *   q_labels  int32 [L][B*Hq][N]      query cluster of each row per level
  *   k_labels  int32 [L][B*Hkv][N]
  *   q_perm    int32 [L][B*Hq][N]      per problem, sorted position -> row
@@ -98,7 +99,7 @@ typedef struct {
  * muse_plan).  Counts are k_offs[c+1] - k_offs[c].
  */
 typedef struct {
-  int64_t P, L, C, k1w, Cp32;
+  int64_t P, L, C, k1w, Cp32, Nv;
   size_t q_labels, k_labels, q_perm, k_perm, q_offs, k_offs, q_cent, k_cent, mu, S, M, R;
   size_t Kp, Vp, mu_in;
   size_t state_bytes;
@@ -106,6 +107,8 @@ typedef struct {
   size_t ws_T;      /* dtype [B*Hq][P][C][D][Cp32] T_Ic / n_c, index (I, d, c) */
   size_t ws_oacc;   /* fp32 [B*Hq][N][D] causal running output */
   size_t ws_lacc;   /* fp32 [B*Hq][N] causal running lse */
+  size_t ws_Vt;     /* dtype [L*B*Hkv (+ B*Hkv when causal)][D][Nv] value columns of the sorted
+                       copies (then of the input V), Nv = N rounded up to 8 */
   size_t ws_part;   /* k-means chunk partial sums */
   size_t ws_pcnt;
   size_t ws_bytes;

@@ -47,6 +47,11 @@ def test_layout_sizes():
     assert lay["M"] + 8 * 64 * 64 * 64 * 4 <= lay["R"]
     assert lay["state_bytes"] >= lay["R"] + 8 * 64 * 4 * 4
     assert lay["ws_bytes"] >= 8 * 64 * 64 * 64 * 4
+    # value columns: one sorted copy per head, rows padded to 8 (acausal: no input-order copy)
+    assert lay["Nv"] == 8192 and lay["ws_Vt"] + 8 * 64 * 8192 * 2 <= lay["ws_bytes"]
+    odd = M.layout(1, 1, 1, 1001, 64, M.MUSE_BF16, M.make_cfg(16, 3, 2, True, 100))
+    assert odd["Nv"] == 1008
+    assert odd["ws_Vt"] + (odd["L"] + 1) * 64 * 1008 * 2 <= odd["ws_bytes"]
     c4 = M.layout(1, 32, 8, 65536, 64, M.MUSE_BF16, M.make_cfg(128, 10, 8, True, 1024))
     assert c4["P"] == 63 and c4["L"] == 6
 
