@@ -22,13 +22,18 @@ FLAGS = [
 ]
 
 
+# per-source extra flags: the attention kernels keep MFMA accumulators in
+# VGPRs (no copies between accumulation and arithmetic registers)
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(f for f in os.listdir(SRC) if f.endswith(".hip"))
 
 
 def _compile(name):
     obj = os.path.join(OUT, name[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(SRC, name), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(name, []), "-c", os.path.join(SRC, name), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

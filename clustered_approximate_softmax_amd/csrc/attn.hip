@@ -212,7 +212,8 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
                                              const Cursor& c,
                                              bool far,
                                              const u16x8 (&qf)[QG][D / 32][sizeof(TIn) == 2 ? 1 : 3],
-                                             AtState<D> (&st)[QG], float s2, const int (&qrow)[QG]) {
+                                             AtState<D> (&st)[QG], float s2, const int (&qrow)[QG],
+                                             int qmin) {
   using G = AtGeo<TIn, D>;
   constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
   constexpr int KS = D / 32, DT = D / 16;
@@ -235,55 +236,83 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
       for (int qg = 0; qg < QG; ++qg) sc[qg][rt] = mfma_split<NS, NS>(a, qf[qg][k], sc[qg][rt]);
     }
   }
-  // log-weights of the lane's items (far), or which rows lie in [lo, hi)
-  // (exact: a masked row's logit is replaced, not offset, since rows outside
+  // A plain tile lies inside [lo, hi) and (causal) below every query row of
+  // the workgroup: no mask, unit weights.
+  const bool plain = !far && c.row0 >= c.lo && c.row0 + AT_KT <= c.hi && (!CAUSAL || c.row0 + AT_KT - 1 <= qmin);
+  // otherwise: log-weights of the lane's items (far), or which rows lie in
+  // [lo, hi) (a masked row's logit is replaced, not offset, since rows outside
   // the key segments of a level hold unspecified values)
   f32x4 bv[RT];
-  uint32_t ok = 0;
+  uint32_t ok = 0xffffu;
+  if (!plain) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
-    if (far) {
-      bv[rt] = *reinterpret_cast<const f32x4*>(&sm.far_bias[c.row0 + it0]);
-    } else {
-      bv[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RT; ++rt) {
+      const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
+      if (far) {
+        bv[rt] = *reinterpret_cast<const f32x4*>(&sm.far_bias[c.row0 + it0]);
+      } else {
+        bv[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if ((unsigned)(c.row0 + it0 + i - c.lo) < (unsigned)(c.hi - c.lo)) ok |= 1u << (rt * 4 + i);
+        for (int i = 0; i < 4; ++i)
+          if ((unsigned)(c.row0 + it0 + i - c.lo) >= (unsigned)(c.hi - c.lo)) ok &= ~(1u << (rt * 4 + i));
+      }
     }
   }
-  if (far) ok = 0xffffu;
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     float x[RT * 4];
     float mloc = -INFINITY;
+    if (plain) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = (ok >> (rt * 4 + i)) & 1u ? fmaf(s2, sc[qg][rt][i], bv[rt][i]) : -INFINITY;
-        if (CAUSAL && c.row0 + it0 + i > qrow[qg]) v = -INFINITY;
-        x[rt * 4 + i] = v;
-        mloc = fmaxf(mloc, v);
+        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sc[qg][rt][i]);
+      mloc *= s2;
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = (ok >> (rt * 4 + i)) & 1u ? fmaf(s2, sc[qg][rt][i], bv[rt][i]) : -INFINITY;
+          if (CAUSAL && c.row0 + it0 + i > qrow[qg]) v = -INFINITY;
+          x[rt * 4 + i] = v;
+          mloc = fmaxf(mloc, v);
+        }
       }
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float mnew = fmaxf(st[qg].m, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(st[qg].m - mnew);
-    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < RT * 4; ++j) {
-      x[j] = __builtin_amdgcn_exp2f(x[j] - mnew);
-      ps4[j & 3] += x[j];
-    }
-    st[qg].lpart = st[qg].lpart * alpha + ((ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
-    st[qg].m = mnew;
-    if (__any(alpha != 1.f)) {
+    // lazy rescale: the running max of a row moves only when the tile's max
+    // exceeds it by more than 8 (weights stay below 2^8, exact in the end
+    // since output and normaliser share the same max)
+    const float mcand = fmaxf(st[qg].m, mloc);
+    const bool grow = mcand > st[qg].m + 8.f;
+    if (__any(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(st[qg].m - mcand) : 1.f;
+      st[qg].lpart *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) st[qg].o[dt] *= alpha;
+      st[qg].m = grow ? mcand : st[qg].m;
     }
+    const float mref = st[qg].m;
+    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+    if (plain) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[rt * 4 + i] = __builtin_amdgcn_exp2f(fmaf(sc[qg][rt][i], s2, -mref));
+          ps4[i] += x[rt * 4 + i];
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RT * 4; ++j) {
+        x[j] = __builtin_amdgcn_exp2f(x[j] - mref);
+        ps4[j & 3] += x[j];
+      }
+    }
+    st[qg].lpart += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) {
       // P^T slots 8g + j: items 32ps + 8g + j
@@ -545,7 +574,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     asm volatile("" ::: "memory");
     issue_tile<TIn, D, WAVES>(stg[sl], src, lc);
     lc = cur_next(sm, src, lc);
-    consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, stg[sc_], cc, cc.t < src.nfar, qf, st, s2, qmask);
+    consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, stg[sc_], cc, cc.t < src.nfar, qf, st, s2, qmask,
+                                                       qlo);
     cc = cur_next(sm, src, cc);
     sl = sl + 1 == ST ? 0 : sl + 1;
     sc_ = sc_ + 1 == ST ? 0 : sc_ + 1;
