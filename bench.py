@@ -14,6 +14,7 @@ oracle timed on a bounded sample on the host cores.
 """
 import argparse
 import json
+import re
 import math
 import os
 import sys
@@ -256,8 +257,17 @@ def main():
     kt = M.timing_read()
     M.timing_enable(False)
     models = kernel_models(w, M, st, rows)
-    per_kernel = {}
+    # per-level launches (name_L<l>) are summed under their kernel's name
+    agg, levels = {}, {}
     for name, (tot, n) in kt.items():
+        base = re.sub(r"_L\d+$", "", name)
+        a = agg.setdefault(base, [0.0, 0])
+        a[0] += tot
+        a[1] += n
+        if base != name:
+            levels[name] = {"ms_per_launch": tot / n, "launches_per_step": n / args.steps}
+    per_kernel = {}
+    for name, (tot, n) in agg.items():
         per_kernel[name] = {"ms_per_launch": tot / n, "launches_per_step": n / args.steps,
                             "ms_per_step": tot / args.steps}
     dom = max(per_kernel, key=lambda k: per_kernel[k]["ms_per_step"])
@@ -292,6 +302,7 @@ def main():
                                                            else PEAK_F32_TFLOPS), 2),
         "roofline": roof,
         "kernels": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in per_kernel.items()},
+        "levels": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in levels.items()},
     }
     if not args.no_exact:
         ex_ms = exact_attention_ms(Q, K, V, w, max(3, args.steps // 2), torch)

@@ -706,7 +706,9 @@ static hipError_t attn_level(const Plan& pl, const AttnBufs& b, int lev, hipStre
     attn_kernel<TIn, TIn, D, WAVES, QG, MODE_LEVEL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, lev);
   else
     attn_kernel<TIn, TIn, D, WAVES, QG, MODE_ACAUSAL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, lev);
-  MUSE_KT_POST(pl.causal ? "attn_level" : "attn_far_retrieve", st);
+  static const char* const lname[8] = {"attn_level_L0", "attn_level_L1", "attn_level_L2", "attn_level_L3",
+                                       "attn_level_L4", "attn_level_L5", "attn_level_L6", "attn_level_L7"};
+  MUSE_KT_POST(pl.causal ? (lev < 8 ? lname[lev] : "attn_level") : "attn_far_retrieve", st);
   return hipGetLastError();
 }
 

@@ -179,9 +179,44 @@ __device__ __forceinline__ float xval(const V8& v, int j) {
 // zero orders first).  Points whose two best keys lie within the screening
 // error of each other are decided by fp32 distances to the candidate
 // clusters, lowest index on ties.
+// Screening sums of 16 points (lane (col, g): point col) against the TB
+// cluster tiles t0 .. t0+TB-1: every centroid fragment of the batch is read
+// from LDS first, then the MFMAs run interleaved over TB independent
+// accumulators (per accumulator: lo parts, hi parts, norm step, as before).
+template <int D, int TB, typename SM, typename V8>
+__device__ __forceinline__ void km_screen_batch(const SM& sm, const V8 (&x)[D / 32], const u16x8& bn, int t0,
+                                                f32x4 (&acc)[TB]) {
+  constexpr int KS = D / 32;
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+  u16x8 flo[TB][KS], fhi[TB][KS], fnm[TB];
+#pragma unroll
+  for (int u = 0; u < TB; ++u) {
+    const int row = 16 * (t0 + u) + col;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      flo[u][k] = *reinterpret_cast<const u16x8*>(&sm.mu_hat[1][row][32 * k + 8 * g]);
+      fhi[u][k] = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][row][32 * k + 8 * g]);
+    }
+    fnm[u] = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][row][D]);
+  }
+#pragma unroll
+  for (int u = 0; u < TB; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int u = 0; u < TB; ++u) acc[u] = mfma(as_bf(flo[u][k]), as_bf(x[k]), acc[u]);
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int u = 0; u < TB; ++u) acc[u] = mfma(as_bf(fhi[u][k]), as_bf(x[k]), acc[u]);
+#pragma unroll
+  for (int u = 0; u < TB; ++u) acc[u] = mfma(as_bf(fnm[u]), as_bf(bn), acc[u]);
+}
+
 template <typename TIn, int D, int CT, typename SM>
 __device__ void km_assign_bf16(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nvalid, const float* cent,
                                int Ceff, float Rmax, int32_t* glab) {
+  constexpr int TB = CT < 4 ? CT : 4;   // cluster tiles per screening batch
   using S = KmShape<TIn, D>;
   constexpr int KS = D / 32;
   constexpr int IB = CT <= 8 ? 7 : 8;
@@ -213,30 +248,28 @@ __device__ void km_assign_bf16(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nv
       bn[3] = f2bf(xsq - bf2f(xh));
     }
     int m1 = 0x7fffffff, m2 = 0x7fffffff;
+    // batches of up to TB cluster tiles; a batch with 1 or 2 live tiles runs
+    // at that width (rows of absent clusters carry a huge norm and never win)
+    auto keys = [&](auto tbc, int t0) {
+      constexpr int TBX = decltype(tbc)::value;
+      f32x4 acc[TBX];
+      km_screen_batch<D, TBX>(sm, xr.x[grp], bn, t0, acc);
 #pragma unroll
-    for (int t = 0; t < CT; ++t) {
-      if (t * 16 < Ceff) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const u16x8 alo = *reinterpret_cast<const u16x8*>(&sm.mu_hat[1][16 * t + col][32 * k + 8 * g]);
-          acc = mfma(as_bf(alo), as_bf(xr.x[grp][k]), acc);
-        }
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const u16x8 ahi = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][16 * t + col][32 * k + 8 * g]);
-          acc = mfma(as_bf(ahi), as_bf(xr.x[grp][k]), acc);
-        }
-        const u16x8 an = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][16 * t + col][D]);
-        acc = mfma(as_bf(an), as_bf(bn), acc);
+      for (int u = 0; u < TBX; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = (__float_as_int(acc[i]) & KMASK) | (16 * t + i);
+          const int key = (__float_as_int(acc[u][i]) & KMASK) | (16 * (t0 + u) + i);
           const int n2 = med3i(m1, m2, key);
           m1 = min(m1, key);
           m2 = n2;
         }
-      }
+    };
+#pragma unroll
+    for (int t0 = 0; t0 < CT; t0 += TB) {
+      const int live = min(TB, (Ceff - 16 * t0 + 15) / 16);
+      if (live > 2) keys(std::integral_constant<int, TB>{}, t0);
+      else if (live == 2) keys(std::integral_constant<int, TB < 2 ? TB : 2>{}, t0);
+      else if (live == 1) keys(std::integral_constant<int, 1>{}, t0);
     }
     m1 |= 4 * g;
 #pragma unroll
@@ -260,26 +293,24 @@ __device__ void km_assign_bf16(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nv
       unsigned long long cm[NW];
 #pragma unroll
       for (int q = 0; q < NW; ++q) cm[q] = 0ull;
-      for (int t = 0; t < CT; ++t) {
-        if (t * 16 >= Ceff) break;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      auto cands = [&](auto tbc, int t0) {
+        constexpr int TBX = decltype(tbc)::value;
+        f32x4 acc[TBX];
+        km_screen_batch<D, TBX>(sm, xr.x[grp], bn, t0, acc);
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const u16x8 alo = *reinterpret_cast<const u16x8*>(&sm.mu_hat[1][16 * t + col][32 * k + 8 * g]);
-          acc = mfma(as_bf(alo), as_bf(xr.x[grp][k]), acc);
-        }
+        for (int u = 0; u < TBX; ++u)
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const u16x8 ahi = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][16 * t + col][32 * k + 8 * g]);
-          acc = mfma(as_bf(ahi), as_bf(xr.x[grp][k]), acc);
-        }
-        const u16x8 an = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][16 * t + col][D]);
-        acc = mfma(as_bf(an), as_bf(bn), acc);
+          for (int i = 0; i < 4; ++i) {
+            const int c = 16 * (t0 + u) + 4 * g + i;
+            if (need && c < Ceff && acc[u][i] <= thr) cm[c >> 6] |= 1ull << (c & 63);
+          }
+      };
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = 16 * t + 4 * g + i;
-          if (need && c < Ceff && acc[i] <= thr) cm[c >> 6] |= 1ull << (c & 63);
-        }
+      for (int t0 = 0; t0 < CT; t0 += TB) {
+        const int live = min(TB, (Ceff - 16 * t0 + 15) / 16);
+        if (live > 2) cands(std::integral_constant<int, TB>{}, t0);
+        else if (live == 2) cands(std::integral_constant<int, TB < 2 ? TB : 2>{}, t0);
+        else if (live == 1) cands(std::integral_constant<int, 1>{}, t0);
       }
 #pragma unroll
       for (int q = 0; q < NW; ++q) {
@@ -475,12 +506,12 @@ __device__ void km_assign_sub(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nva
 
 // One-hot update: acc += onehot(labels) . X.  Wave w owns the cluster tiles
 // ct = w, w+4, ... with every dim tile (one-hot built once per 32 points
-// and cluster tile); with fewer than 4 cluster tiles it owns dim tiles
-// dt = w, w+4, ... of cluster tile 0.
+// and cluster tile); with 2 cluster tiles it owns tile w & 1, dim tiles
+// w/2, w/2 + 2, ...; with one, dim tiles dt = w, w+4, ... of tile 0.
 template <typename TIn, int D, int CT>
 struct KmAcc {
   static constexpr int DT = D / 16;
-  static constexpr int U = CT >= 4 ? (CT / 4) * DT : DT / 4;
+  static constexpr int U = CT >= 4 ? (CT / 4) * DT : CT == 2 ? DT / 2 : DT / 4;
   f32x4 a[U];
 };
 
@@ -490,6 +521,9 @@ __device__ __forceinline__ void km_tile_of(int w, int u, int& ct, int& dt) {
   if constexpr (CT >= 4) {
     ct = w + 4 * (u / DT);
     dt = u % DT;
+  } else if constexpr (CT == 2) {
+    ct = w & 1;
+    dt = (w >> 1) + 2 * u;
   } else {
     ct = 0;
     dt = w + 4 * u;
@@ -502,11 +536,11 @@ __device__ void km_update_sub(SM& sm, KmAcc<TIn, D, CT>& acc, int Ceff) {
   constexpr int NS = S::NS;
   constexpr int DT = D / 16;
   constexpr int U = KmAcc<TIn, D, CT>::U;
-  constexpr int NCT = CT >= 4 ? CT / 4 : 1;          // cluster tiles per wave
-  constexpr int NDT = CT >= 4 ? DT : DT / 4;         // dim tiles per wave
+  constexpr int NCT = CT >= 4 ? CT / 4 : 1;                          // cluster tiles per wave
+  constexpr int NDT = CT >= 4 ? DT : CT == 2 ? DT / 2 : DT / 4;      // dim tiles per wave
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
-#pragma unroll 1
+#pragma unroll 2
   for (int ks = 0; ks < S::SUB / 32; ++ks) {
     const int4 l0 = *reinterpret_cast<const int4*>(&sm.lab[32 * ks + 8 * g]);
     const int4 l1 = *reinterpret_cast<const int4*>(&sm.lab[32 * ks + 8 * g + 4]);
@@ -514,14 +548,14 @@ __device__ void km_update_sub(SM& sm, KmAcc<TIn, D, CT>& acc, int Ceff) {
     u16x8 b[NDT][NS];
 #pragma unroll
     for (int d = 0; d < NDT; ++d) {
-      const int dt = CT >= 4 ? d : w + 4 * d;
+      const int dt = CT >= 4 ? d : CT == 2 ? (w >> 1) + 2 * d : w + 4 * d;
 #pragma unroll
       for (int sp = 0; sp < NS; ++sp)
         b[d][sp] = *reinterpret_cast<const u16x8*>(&sm.xt[sp][16 * dt + col][32 * ks + 8 * g]);
     }
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
-      const int ct = CT >= 4 ? w + 4 * c : 0;
+      const int ct = CT >= 4 ? w + 4 * c : CT == 2 ? (w & 1) : 0;
       if (ct * 16 >= Ceff) continue;
       u16x8 a;
       const int cl = 16 * ct + col;
@@ -993,6 +1027,7 @@ template <typename TIn, int D>
 static hipError_t km_run_d(const Plan& pl, const CSet& s0, const CSet& s1, int plocal,
                            const KmLarge& lg, float* part, int32_t* pcnt, hipStream_t st) {
   if (pl.C <= 16) return km_run_t<TIn, D, 1>(pl, s0, s1, plocal, lg, part, pcnt, st);
+  if (pl.C <= 32) return km_run_t<TIn, D, 2>(pl, s0, s1, plocal, lg, part, pcnt, st);
   if (pl.C <= 64) return km_run_t<TIn, D, 4>(pl, s0, s1, plocal, lg, part, pcnt, st);
   if (pl.C <= 128) return km_run_t<TIn, D, 8>(pl, s0, s1, plocal, lg, part, pcnt, st);
   return km_run_t<TIn, D, 16>(pl, s0, s1, plocal, lg, part, pcnt, st);
@@ -1022,6 +1057,7 @@ size_t kmeans_smem_bytes(int dtype, int D, int C) {
     using T = decltype(tin);
     constexpr int DD = decltype(dd)::value;
     if (C <= 16) return sizeof(KmSmem<T, DD, 1>);
+    if (C <= 32) return sizeof(KmSmem<T, DD, 2>);
     if (C <= 64) return sizeof(KmSmem<T, DD, 4>);
     if (C <= 128) return sizeof(KmSmem<T, DD, 8>);
     return sizeof(KmSmem<T, DD, 16>);
