@@ -639,13 +639,13 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
 // N <= j < Nv.
 template <typename TIn, int D>
 __global__ void __launch_bounds__(256) vt_kernel(Plan pl, const void* Vp, const void* V, void* Vt, int Nv,
-                                                 int nsorted) {
+                                                 int nsorted, int sfirst) {
   const int N = pl.N;
   constexpr int E = 16 / (int)sizeof(TIn), CH = D / E;
   using V16 = typename std::conditional<sizeof(TIn) == 2, u16x8, f32x4>::type;
   __shared__ TIn tile[AT_KT][D + 2];
   const int nb = (Nv + AT_KT - 1) / AT_KT;
-  const int s = blockIdx.x / nb, blk = blockIdx.x % nb;
+  const int s = sfirst + (int)(blockIdx.x / nb), blk = blockIdx.x % nb;
   const TIn* src = s < nsorted ? reinterpret_cast<const TIn*>(Vp) + (size_t)s * N * D
                                : reinterpret_cast<const TIn*>(V) + (size_t)(s - nsorted) * N * D;
   TIn* dst = reinterpret_cast<TIn*>(Vt) + (size_t)s * D * Nv;
@@ -685,11 +685,14 @@ __global__ void finalize_kernel(const float* oacc, const float* lacc, TOut* O, f
 template <typename TIn, int D>
 static hipError_t launch_vt(const Plan& pl, const AttnBufs& b, hipStream_t st) {
   const int nsorted = pl.nlev * pl.B * pl.Hkv;
-  const int nslice = nsorted + (pl.causal ? pl.B * pl.Hkv : 0);
+  // without retrieval no tile reads the sorted copies: only the input-order
+  // slices (causal local blocks) are needed
+  const int sfirst = pl.topk > 0 ? 0 : nsorted;
+  const int nslice = nsorted + (pl.causal ? pl.B * pl.Hkv : 0) - sfirst;
   const long long grid = (long long)nslice * ((b.Nv + AT_KT - 1) / AT_KT);
   if (grid == 0) return hipSuccess;
   MUSE_KT_PRE(st);
-  vt_kernel<TIn, D><<<(unsigned)grid, 256, 0, st>>>(pl, b.kst.Vp, b.V, b.Vt, b.Nv, nsorted);
+  vt_kernel<TIn, D><<<(unsigned)grid, 256, 0, st>>>(pl, b.kst.Vp, b.V, b.Vt, b.Nv, nsorted, sfirst);
   MUSE_KT_POST("value_transpose", st);
   return hipGetLastError();
 }
