@@ -536,8 +536,10 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   Cursor lc = cur_first(sm, src), cc = lc;
 #pragma unroll
   for (int p = 0; p < PD; ++p) {
-    issue_tile<TIn, D, WAVES>(stg[p], src, lc);
-    lc = cur_next(sm, src, lc);
+    if (p < ntiles) {
+      issue_tile<TIn, D, WAVES>(stg[p], src, lc);
+      lc = cur_next(sm, src, lc);
+    }
   }
   // query fragments (loaded after the first copies are on their way)
   int myq[QG];
@@ -566,14 +568,18 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
 
   int sl = PD % ST, sc_ = 0;   // stage of the next copy, stage being consumed
   for (int t = 0; t < ntiles; ++t) {
-    // this thread's copies of tile t have landed (PD-1 later tiles may be in
-    // flight); after the barrier every thread's have, and tile t-1 is consumed
+    // this thread's copies of tile t have landed (the PD-1 later tiles, when
+    // they exist, may be in flight); after the barrier every thread's have,
+    // and tile t-1 is consumed.  Only real tiles are copied.
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(at_wait((PD - 1) * LPT, 0));
+    if (t + PD - 1 < ntiles) __builtin_amdgcn_s_waitcnt(at_wait((PD - 1) * LPT, 0));
+    else __builtin_amdgcn_s_waitcnt(at_wait(0, 0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue_tile<TIn, D, WAVES>(stg[sl], src, lc);
-    lc = cur_next(sm, src, lc);
+    if (t + PD < ntiles) {
+      issue_tile<TIn, D, WAVES>(stg[sl], src, lc);
+      lc = cur_next(sm, src, lc);
+    }
     consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, stg[sc_], cc, cc.t < src.nfar, qf, st, s2, qmask,
                                                        qlo);
     cc = cur_next(sm, src, cc);
