@@ -111,12 +111,14 @@ hipError_t launch_score_topk(const Plan& pl, const AttnBufs& b, hipStream_t st) 
 
 // ---------------------------------------------------------------------------
 // T[ap][I][d][c] = (S[kp][c][d] + s sum_e M[kp][d][c][e] nu[ap][I][e]) / n_c
-// One workgroup per (key problem, block of tb value dims d), serving every
-// query head of the key head's group: for fixed d this is a (clusters c) x
-// (query clusters I) product over the key dim e, with A = rows of M (read
-// once from memory) and B = nu^T (staged in LDS per query head).  A lane's
-// result is four consecutive clusters of one query cluster, stored as one
-// short contiguous run.  Columns c in [C, Cp) are written as zeros.
+// One workgroup per (key problem, query head of its group, block of tb value
+// dims d): for fixed d this is a (clusters c) x (query clusters I) product
+// over the key dim e, with A = rows of M (registers) and B = nu^T (staged in
+// LDS).  Small workgroups keep many in flight per CU, which hides the load
+// latency of each; the workgroups of one key problem run on one XCD, so the
+// query heads of its group re-read M from that XCD's L2.  A lane's result is
+// four consecutive clusters of one query cluster, stored as one contiguous
+// run.  Columns c in [C, Cp) are written as zeros.
 // ---------------------------------------------------------------------------
 constexpr int TILT_IC = 128;   // query clusters staged at a time
 
@@ -126,15 +128,19 @@ struct alignas(16) TiltSmem {
 };
 
 template <typename TIn, int D, int NS>
-__global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b, int tb) {
+__global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b, int tb, long long kps) {
   using SM = TiltSmem<TIn, D, NS>;
   extern __shared__ __align__(16) unsigned char tilt_raw[];
   SM& sm = *reinterpret_cast<SM*>(tilt_raw);
   constexpr int KS = D / 32;
   const int NDB = D / tb;
   const int C = pl.C, Cp = b.Cp32, Gq = pl.Hq / pl.Hkv;
-  const int db = blockIdx.x % NDB;
-  const size_t kp = blockIdx.x / NDB;
+  const int per = Gq * NDB;                       // workgroups per key problem
+  const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
+  const long long kp = (long long)(loc / per) * 8 + xcd;
+  if (kp >= kps) return;
+  const int u = loc % per;
+  const int db = u % NDB, hl = u / NDB;
   const int kvh = (int)(kp / pl.P), p = (int)(kp % pl.P);
   const int bq = kvh / pl.Hkv, kh = kvh % pl.Hkv;
   const Geom gm = prob_geom(pl, p);
@@ -146,89 +152,87 @@ __global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b, int tb) 
   const float* Sk = b.kst.S + kp * (size_t)C * D;         // [c][d]
   const int32_t* koffs = b.ks.offs + kp * (C + 1);
   const int nct = Cp / 16;
-  for (int hl = 0; hl < Gq; ++hl) {
-    const size_t ap = (size_t)(bq * pl.Hq + kh * Gq + hl) * pl.P + p;
-    const float* nu = b.qs.cent + ap * (size_t)C * D;        // [I][e]
-    TIn* T = reinterpret_cast<TIn*>(b.T) + ap * (size_t)C * D * Cp;   // [I][d][c]
-    for (int i0 = 0; i0 < Cq; i0 += TILT_IC) {
-      const int nit = (min(TILT_IC, Cq - i0) + 15) / 16;
-      __syncthreads();
-      for (int idx = tid; idx < nit * 16 * (D / 8); idx += 256) {
-        const int r = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
-        const int I = i0 + r;
-        float v[8];
-        if (I < Cq) {
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(nu + (size_t)I * D + e0);
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(nu + (size_t)I * D + e0 + 4);
-          v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
-          v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
-        } else {
+  const size_t ap = (size_t)(bq * pl.Hq + kh * Gq + hl) * pl.P + p;
+  const float* nu = b.qs.cent + ap * (size_t)C * D;        // [I][e]
+  TIn* T = reinterpret_cast<TIn*>(b.T) + ap * (size_t)C * D * Cp;   // [I][d][c]
+  for (int i0 = 0; i0 < Cq; i0 += TILT_IC) {
+    const int nit = (min(TILT_IC, Cq - i0) + 15) / 16;
+    __syncthreads();
+    for (int idx = tid; idx < nit * 16 * (D / 8); idx += 256) {
+      const int r = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
+      const int I = i0 + r;
+      float v[8];
+      if (I < Cq) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(nu + (size_t)I * D + e0);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(nu + (size_t)I * D + e0 + 4);
+        v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
+        v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
+      } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) split_store<NS>(v[j], &sm.nu[0][r][e0 + j], TILT_IC * (D + 8));
+        for (int j = 0; j < 8; ++j) v[j] = 0.f;
       }
-      __syncthreads();
-      for (int dd = 0; dd < tb; ++dd) {
-        const int d = db * tb + dd;
-        for (int ct = w; ct < nct; ct += 4) {
-          const int cr = 16 * ct + col;          // A row: cluster
-          u16x8 a[KS][NS];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) split_store<NS>(v[j], &sm.nu[0][r][e0 + j], TILT_IC * (D + 8));
+    }
+    __syncthreads();
+    for (int dd = 0; dd < tb; ++dd) {
+      const int d = db * tb + dd;
+      for (int ct = w; ct < nct; ct += 4) {
+        const int cr = 16 * ct + col;          // A row: cluster
+        u16x8 a[KS][NS];
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          float v[8];
+          if (cr < Ck) {
+            const float* src = Mk + ((size_t)d * C + cr) * D + 32 * k + 8 * g;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+            v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
+            v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            uint16_t h, m, l;
+            split3(v[j], h, m, l);
+            a[k][0][j] = NS == 1 ? f2bf(v[j]) : h;
+            if (NS > 1) { a[k][NS > 1 ? 1 : 0][j] = m; a[k][NS > 2 ? 2 : 0][j] = l; }
+          }
+        }
+        // the lane's four clusters: value sum and 1 / n_c
+        float sv[4], inv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 16 * ct + 4 * g + i;
+          const int nc = c < Ck ? koffs[c + 1] - koffs[c] : 0;
+          inv[i] = nc > 0 ? 1.f / (float)nc : 0.f;
+          sv[i] = nc > 0 ? Sk[(size_t)c * D + d] : 0.f;
+        }
+        for (int it = 0; it < nit; ++it) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int k = 0; k < KS; ++k) {
-            float v[8];
-            if (cr < Ck) {
-              const float* src = Mk + ((size_t)d * C + cr) * D + 32 * k + 8 * g;
-              const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-              const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-              v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
-              v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
+            u16x8 bb[NS];
+#pragma unroll
+            for (int sp = 0; sp < NS; ++sp)
+              bb[sp] = *reinterpret_cast<const u16x8*>(&sm.nu[sp][16 * it + col][32 * k + 8 * g]);
+            acc = mfma_split<NS, NS>(a[k], bb, acc);
+          }
+          const int I = i0 + 16 * it + col;
+          if (I < Cq) {
+            TIn* dst = T + ((size_t)I * D + d) * Cp + 16 * ct + 4 * g;
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (sv[i] + s * acc[i]) * inv[i];
+            if constexpr (sizeof(TIn) == 2) {
+              typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+              u32x2 wv = {(uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16),
+                          (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16)};
+              *reinterpret_cast<u32x2*>(dst) = wv;
             } else {
-#pragma unroll
-              for (int j = 0; j < 8; ++j) v[j] = 0.f;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              uint16_t h, m, l;
-              split3(v[j], h, m, l);
-              a[k][0][j] = NS == 1 ? f2bf(v[j]) : h;
-              if (NS > 1) { a[k][NS > 1 ? 1 : 0][j] = m; a[k][NS > 2 ? 2 : 0][j] = l; }
-            }
-          }
-          // the lane's four clusters: value sum and 1 / n_c
-          float sv[4], inv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = 16 * ct + 4 * g + i;
-            const int nc = c < Ck ? koffs[c + 1] - koffs[c] : 0;
-            inv[i] = nc > 0 ? 1.f / (float)nc : 0.f;
-            sv[i] = nc > 0 ? Sk[(size_t)c * D + d] : 0.f;
-          }
-          for (int it = 0; it < nit; ++it) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < KS; ++k) {
-              u16x8 bb[NS];
-#pragma unroll
-              for (int sp = 0; sp < NS; ++sp)
-                bb[sp] = *reinterpret_cast<const u16x8*>(&sm.nu[sp][16 * it + col][32 * k + 8 * g]);
-              acc = mfma_split<NS, NS>(a[k], bb, acc);
-            }
-            const int I = i0 + 16 * it + col;
-            if (I < Cq) {
-              TIn* dst = T + ((size_t)I * D + d) * Cp + 16 * ct + 4 * g;
-              float o[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) o[i] = (sv[i] + s * acc[i]) * inv[i];
-              if constexpr (sizeof(TIn) == 2) {
-                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                u32x2 wv = {(uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16),
-                            (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16)};
-                *reinterpret_cast<u32x2*>(dst) = wv;
-              } else {
-                *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
-              }
+              *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
             }
           }
         }
@@ -237,30 +241,29 @@ __global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b, int tb) 
   }
 }
 
+template <typename TIn, int D, int NS>
+static void tilt_go(const Plan& pl, const AttnBufs& b, long long kps, int tb, hipStream_t st) {
+  using SM = TiltSmem<TIn, D, NS>;
+  const int per = (pl.Hq / pl.Hkv) * (pl.D / tb);
+  const unsigned grid = (unsigned)(((kps + 7) / 8) * 8 * per);
+  set_smem_once((const void*)tilt_kernel<TIn, D, NS>, sizeof(SM));
+  tilt_kernel<TIn, D, NS><<<grid, 256, sizeof(SM), st>>>(pl, b, tb, kps);
+}
+
 hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st) {
   const long long kps = (long long)pl.B * pl.Hkv * pl.P;
   if (kps == 0) return hipSuccess;
-  // dims per workgroup: up to 8, fewer when that leaves the chip under-filled
-  int tb = 8;
-  while (tb > 1 && kps * (pl.D / tb) < 512) tb /= 2;
-  const unsigned grid = (unsigned)(kps * (pl.D / tb));
+  // dims per workgroup: up to 4, fewer when that leaves the chip under-filled
+  const long long heads = kps * (pl.Hq / pl.Hkv);
+  int tb = 4;
+  while (tb > 1 && heads * (pl.D / tb) < 2048) tb /= 2;
   MUSE_KT_PRE(st);
   if (dtype == 1) {
-    if (pl.D == 64) {
-      set_smem_once((const void*)tilt_kernel<uint16_t, 64, 1>, sizeof(TiltSmem<uint16_t, 64, 1>));
-      tilt_kernel<uint16_t, 64, 1><<<grid, 256, sizeof(TiltSmem<uint16_t, 64, 1>), st>>>(pl, b, tb);
-    } else {
-      set_smem_once((const void*)tilt_kernel<uint16_t, 128, 1>, sizeof(TiltSmem<uint16_t, 128, 1>));
-      tilt_kernel<uint16_t, 128, 1><<<grid, 256, sizeof(TiltSmem<uint16_t, 128, 1>), st>>>(pl, b, tb);
-    }
+    if (pl.D == 64) tilt_go<uint16_t, 64, 1>(pl, b, kps, tb, st);
+    else tilt_go<uint16_t, 128, 1>(pl, b, kps, tb, st);
   } else {
-    if (pl.D == 64) {
-      set_smem_once((const void*)tilt_kernel<float, 64, 3>, sizeof(TiltSmem<float, 64, 3>));
-      tilt_kernel<float, 64, 3><<<grid, 256, sizeof(TiltSmem<float, 64, 3>), st>>>(pl, b, tb);
-    } else {
-      set_smem_once((const void*)tilt_kernel<float, 128, 3>, sizeof(TiltSmem<float, 128, 3>));
-      tilt_kernel<float, 128, 3><<<grid, 256, sizeof(TiltSmem<float, 128, 3>), st>>>(pl, b, tb);
-    }
+    if (pl.D == 64) tilt_go<float, 64, 3>(pl, b, kps, tb, st);
+    else tilt_go<float, 128, 3>(pl, b, kps, tb, st);
   }
   MUSE_KT_POST("tilt", st);
   return hipGetLastError();
