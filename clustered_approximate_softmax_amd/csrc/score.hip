@@ -100,13 +100,114 @@ __global__ void __launch_bounds__(256) score_topk_kernel(Plan pl, AttnBufs b) {
   for (int q = base + lane; q < pl.k1w; q += 64) R[q] = -1;
 }
 
+// Same scores and sets for top-k1 <= KMAX: one workgroup per attention
+// problem and one thread per query cluster.  The key centroids are staged in
+// LDS once (fp32) and read by every thread as broadcasts; each thread forms
+// its scores in the same order of operations as above and keeps its KMAX
+// best in registers (clusters visited in ascending order, a later cluster
+// displaces only a strictly smaller score, so ties keep the lower index).
+template <int D, int KMAX>
+__global__ void __launch_bounds__(256) score_topk_rows_kernel(Plan pl, AttnBufs b) {
+  extern __shared__ __align__(16) float mus[];   // [C][D] centroids of the key problem
+  const int C = pl.C;
+  const int ap = blockIdx.x;
+  const int bh = ap / pl.P, p = ap % pl.P;
+  const int bq = bh / pl.Hq, hq = bh % pl.Hq;
+  const int kv = bq * pl.Hkv + (hq * pl.Hkv) / pl.Hq;
+  const size_t kp = (size_t)kv * pl.P + p;
+  const Geom gm = prob_geom(pl, p);
+  const int Cq = min(C, gm.qn), Ck = min(C, gm.kn);
+  const int32_t* koffs = b.ks.offs + kp * (C + 1);
+  const float* mu = b.kst.mu + kp * (size_t)C * D;
+  for (int idx = threadIdx.x; idx < Ck * (D / 4); idx += blockDim.x)
+    reinterpret_cast<f32x4*>(mus)[idx] = reinterpret_cast<const f32x4*>(mu)[idx];
+  __syncthreads();
+  for (int I = threadIdx.x; I < C; I += blockDim.x) {
+    int32_t* R = b.R + ((size_t)ap * C + I) * pl.k1w;
+    const int32_t* qoffs = b.qs.offs + (size_t)ap * (C + 1);
+    const int mI = I < Cq ? qoffs[I + 1] - qoffs[I] : 0;
+    if (mI == 0 || pl.topk <= 0) {
+      for (int q = 0; q < pl.k1w; ++q) R[q] = -1;
+      continue;
+    }
+    const float s = pl.scale;
+    const float* nu = b.qs.cent + ((size_t)ap * C + I) * D;
+    f32x4 nv[D / 4];
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) nv[e] = reinterpret_cast<const f32x4*>(nu)[e];
+    float bv[KMAX];
+    int bc[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) { bv[j] = -INFINITY; bc[j] = -1; }
+    const int k1 = min(pl.topk, KMAX);
+    for (int c = 0; c < Ck; ++c) {
+      const int nc = koffs[c + 1] - koffs[c];
+      if (nc <= 0) continue;
+      float dot = 0.f;
+      const f32x4* mr = reinterpret_cast<const f32x4*>(mus + (size_t)c * D);
+#pragma unroll
+      for (int e = 0; e < D / 4; ++e) {
+        const f32x4 mv = mr[e];
+        dot = fmaf(nv[e][0], mv[0], fmaf(nv[e][1], mv[1], fmaf(nv[e][2], mv[2], fmaf(nv[e][3], mv[3], dot))));
+      }
+      const float x = s * dot + logf((float)nc);
+      // insert into the descending list (slots >= k1 stay empty)
+      if (x > bv[k1 - 1]) {
+#pragma unroll
+        for (int j = KMAX - 1; j > 0; --j) {
+          const bool up = x > bv[j - 1];          // x goes above slot j-1: shift it down
+          const bool here = !up && x > bv[j];     // x lands in slot j
+          if (j < k1) {
+            bv[j] = up ? bv[j - 1] : here ? x : bv[j];
+            bc[j] = up ? bc[j - 1] : here ? c : bc[j];
+          }
+        }
+        if (x > bv[0]) { bv[0] = x; bc[0] = c; }
+      }
+    }
+    // ascending cluster order
+#pragma unroll
+    for (int i = 1; i < KMAX; ++i)
+#pragma unroll
+      for (int j = KMAX - 1; j >= i; --j) {
+        const int lo = bc[j - 1], hi = bc[j];
+        const bool sw = (unsigned)lo > (unsigned)hi;   // -1 (empty) sorts last
+        bc[j - 1] = sw ? hi : lo;
+        bc[j] = sw ? lo : hi;
+      }
+    for (int q = 0; q < pl.k1w; ++q) R[q] = q < KMAX ? bc[q] : -1;
+  }
+}
+
+template <int D>
+static hipError_t score_rows(const Plan& pl, const AttnBufs& b, hipStream_t st) {
+  const long long nprob = (long long)pl.B * pl.Hq * pl.P;
+  const size_t smem = (size_t)pl.C * D * sizeof(float);
+  const int nt = pl.C <= 64 ? 64 : pl.C <= 128 ? 128 : 256;
+  if (pl.topk <= 8) {
+    set_smem_once((const void*)score_topk_rows_kernel<D, 8>, (size_t)MUSE_MAXC * D * sizeof(float));
+    score_topk_rows_kernel<D, 8><<<(unsigned)nprob, nt, smem, st>>>(pl, b);
+  } else {
+    set_smem_once((const void*)score_topk_rows_kernel<D, 16>, (size_t)MUSE_MAXC * D * sizeof(float));
+    score_topk_rows_kernel<D, 16><<<(unsigned)nprob, nt, smem, st>>>(pl, b);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_score_topk(const Plan& pl, const AttnBufs& b, hipStream_t st) {
   const long long waves = (long long)pl.B * pl.Hq * pl.P * pl.C;
   if (waves == 0) return hipSuccess;
   MUSE_KT_PRE(st);
-  score_topk_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(pl, b);
+  hipError_t e;
+  // one workgroup per problem needs enough problems to fill the chip
+  if (pl.topk <= 16 && (long long)pl.B * pl.Hq * pl.P >= 512) {
+    e = pl.D == 64 ? score_rows<64>(pl, b, st) : score_rows<128>(pl, b, st);
+  } else {
+    score_topk_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(pl, b);
+    e = hipGetLastError();
+  }
   MUSE_KT_POST("score_topk", st);
-  return hipGetLastError();
+  return e;
 }
 
 // ---------------------------------------------------------------------------

@@ -97,6 +97,14 @@ def test_causal_ragged_length_tiny_blocks():
     run_case(1, 2, 2, 1000, 64, "bf16", 32, 3, 1, causal=True, block=16, seed=7)
 
 
+@pytest.mark.parametrize("topk", [3, 12])
+def test_causal_many_problems_retrieval(topk):
+    # 16 heads x 63 problems: enough attention problems for the per-problem
+    # score / top-k kernel (one thread per query cluster); sets checked as
+    # valid top-k sets of the oracle's scores
+    run_case(1, 16, 4, 2048, 64, "bf16", 16, 2, topk, causal=True, block=32, seed=13 + topk)
+
+
 def test_causal_retrieve_all_is_exact_causal():
     r = run_case(1, 1, 1, 777, 64, "bf16", 8, 2, 8, causal=True, block=64, seed=8)
     x = r["x"]
