@@ -349,7 +349,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
   constexpr int NT = 64 * WAVES, QT = 16 * QG * WAVES;
   constexpr int KS = D / 32, DT = D / 16;
-  constexpr int ST = G::ST, PD = ST - 1;
+  // one-wave workgroups (small query clusters) keep two stages: more of them fit per CU
+  constexpr int ST = WAVES == 1 ? 2 : G::ST, PD = ST - 1;
   constexpr int LPT = (AT_KT * G::CHK + D * G::CHV) / NT;   // copies per thread per tile
   static_assert(PD * LPT <= 63, "copies in flight exceed the counter");
   __shared__ SM sm;
