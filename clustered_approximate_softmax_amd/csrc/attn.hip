@@ -172,6 +172,178 @@ __device__ __forceinline__ void issue_tile(unsigned char* stg, const TileSrc& sr
   }
 }
 
+// Gathered tiles (small clusters).  A tile is 8 chunks of 8 consecutive rows.  Far tile t: clusters 64t ..
+// 64t+63.  Exact tile: the next 8 chunks of the retrieved clusters, each
+// chunk 8 rows from a multiple of 8 inside one cluster's rows (rows outside
+// the cluster are masked), so small clusters share a tile.  All fields are
+// wave-uniform.
+struct TDesc {
+  int far;
+  int base[8];         // first row (exact) or cluster (far) of each chunk
+  uint32_t vlo, vhi;   // exact: valid items 0..31, 32..63
+};
+
+// Position in the chunk list: next tile, current cluster and next chunk row.
+struct Chunks {
+  int t, j, base, lo, hi;
+};
+
+template <typename SM>
+__device__ __forceinline__ Chunks chunks_first(const SM& sm, const TileSrc& src) {
+  Chunks c;
+  const bool ok = src.nseg > 0;
+  c.t = 0;
+  c.j = 0;
+  c.lo = ok ? __builtin_amdgcn_readfirstlane(sm.seg_lo[0]) : 0;
+  c.hi = ok ? __builtin_amdgcn_readfirstlane(sm.seg_hi[0]) : 0;
+  c.base = c.lo & ~7;
+  return c;
+}
+
+// Descriptor of the next tile; advances c.  Past the end, chunks read rows
+// 0..7 with no valid item.
+template <typename SM>
+__device__ __forceinline__ TDesc take_tile(const SM& sm, const TileSrc& src, Chunks& c) {
+  TDesc d;
+  const int t = c.t;
+  c.t = t + 1;
+  d.far = t < src.nfar;
+  if (d.far) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) d.base[k] = AT_KT * t + 8 * k;
+    d.vlo = ~0u;
+    d.vhi = ~0u;
+    return d;
+  }
+  int j = c.j, base = c.base, lo = c.lo, hi = c.hi;
+  uint32_t vm0 = 0, vm1 = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (base >= hi && j < src.nseg) {   // next cluster (non-empty by construction)
+      ++j;
+      const bool ok = j < src.nseg;
+      const int nlo = __builtin_amdgcn_readfirstlane(sm.seg_lo[ok ? j : 0]);
+      const int nhi = __builtin_amdgcn_readfirstlane(sm.seg_hi[ok ? j : 0]);
+      lo = ok ? nlo : 0;
+      hi = ok ? nhi : 0;
+      base = lo & ~7;
+    }
+    // past the last cluster every chunk stays on rows 0..7 (rows every
+    // sorted copy holds), with no valid item
+    if (j >= src.nseg) base = 0;
+    d.base[k] = base;
+    const int a = max(lo - base, 0), b = min(hi - base, 8);
+    const uint32_t bits = b > a ? (1u << b) - (1u << a) : 0u;
+    if (k < 4) vm0 |= bits << (8 * k);
+    else vm1 |= bits << (8 * (k - 4));
+    base += 8;
+  }
+  c.j = j;
+  c.base = base;
+  c.lo = lo;
+  c.hi = hi;
+  d.vlo = vm0;
+  d.vhi = vm1;
+  return d;
+}
+
+// base[k] for a wave-uniform or per-lane chunk index k
+// (a select tree on the bits of k, so that base[] is never indexed at run time)
+__device__ __forceinline__ int pick8(const TDesc& d, int k) {
+  const bool b0 = k & 1, b1 = k & 2, b2 = k & 4;
+  const int x01 = b0 ? d.base[1] : d.base[0], x23 = b0 ? d.base[3] : d.base[2];
+  const int x45 = b0 ? d.base[5] : d.base[4], x67 = b0 ? d.base[7] : d.base[6];
+  const int x03 = b1 ? x23 : x01, x47 = b1 ? x67 : x45;
+  return b2 ? x47 : x03;
+}
+
+// Copy tile d into stage stg: every thread issues the same number of
+// 16-byte direct-to-LDS loads; rows past the end read clamped, valid rows.
+// One load instruction of a wave covers 1 KB of key rows, never more than
+// one chunk, so the key chunk of an instruction is wave-uniform; each lane's
+// 16 bytes of a value row hold items of a single chunk.
+template <typename TIn, int D, int WAVES>
+__device__ __forceinline__ void issue_tile_g(unsigned char* stg, const TileSrc& src, const TDesc& d) {
+  using G = AtGeo<TIn, D>;
+  constexpr int NT = 64 * WAVES;
+  static_assert(AT_KT * G::CHK % NT == 0 && D * G::CHV % NT == 0, "copies must cover the workgroup");
+  static_assert(8 * G::CHK >= 64, "a 1 KB copy must stay inside one chunk");
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  unsigned char* kst = stg;
+  unsigned char* vst = stg + G::KB;
+  // (fields read into values first: a select between field addresses would
+  // keep the source descriptor in memory)
+  const bool far = d.far;
+  const TIn *mu = reinterpret_cast<const TIn*>(src.mu), *kx = reinterpret_cast<const TIn*>(src.Kx);
+  const TIn *tt = reinterpret_cast<const TIn*>(src.T), *vt = reinterpret_cast<const TIn*>(src.Vt);
+  const int ck = src.Ck, kmax = src.kmax, cp = src.Cp, nv = src.nv;
+  const TIn* kb = far ? mu : kx;
+  const int kcap = far ? ck - 1 : kmax;
+#pragma unroll
+  for (int m = 0; m < AT_KT * G::CHK / NT; ++m) {
+    const int ci = m * NT + tid;
+    const int r = ci / G::CHK, pos = ci % G::CHK;
+    const int kchunk = (m * NT + 64 * w) / (8 * G::CHK);   // wave-uniform
+    const int row = min(pick8(d, kchunk) + (r & 7), kcap);
+    const TIn* p = kb + (size_t)row * D + (pos ^ keyk(r)) * G::E;
+    lds_copy16(p, kst + (m * NT + 64 * w) * 16);
+  }
+  const TIn* vb = far ? tt : vt;
+  const int vstride = far ? cp : nv;
+  const int vcap = (far ? cp : nv) - G::E;
+#pragma unroll
+  for (int m = 0; m < D * G::CHV / NT; ++m) {
+    const int ci = m * NT + tid;
+    const int dd = ci / G::CHV, pos = ci % G::CHV;
+    const int lj = pos ^ keyv(dd);             // logical 16-byte chunk of the row
+    const int kc = lj * G::E / 8;              // its 8-item chunk
+    const int col = min(pick8(d, kc) + (lj * G::E) % 8, vcap);
+    const TIn* p = vb + (size_t)dd * vstride + col;
+    lds_copy16(p, vst + (m * NT + 64 * w) * 16);
+  }
+}
+
+// What consume_tile needs to know of a tile: far or exact, plain (no mask
+// at all), its first row (far: first cluster; local: first key row) and the
+// lane's valid items (bit rt*4 + i for item 32(rt/2) + 8g + 4(rt%2) + i).
+struct TileView {
+  int far, plain, row0;
+  uint32_t okm;
+};
+
+__device__ __forceinline__ TileView view_of(const TDesc& d) {
+  TileView v;
+  const int g = (threadIdx.x & 63) >> 4;
+  v.far = d.far;
+  v.row0 = d.base[0];
+  v.plain = !d.far && d.vlo == ~0u && d.vhi == ~0u;
+  v.okm = ((d.vlo >> (8 * g)) & 0xffu) | (((d.vhi >> (8 * g)) & 0xffu) << 8);
+  return v;
+}
+
+template <bool CAUSAL>
+__device__ __forceinline__ TileView view_of(const TileSrc& src, const Cursor& c, int qmin) {
+  TileView v;
+  v.far = c.t < src.nfar;
+  v.row0 = c.row0;
+  // a plain tile lies inside [lo, hi) and (causal) below every query row of the workgroup
+  v.plain = !v.far && c.row0 >= c.lo && c.row0 + AT_KT <= c.hi && (!CAUSAL || c.row0 + AT_KT - 1 <= qmin);
+  uint32_t ok = 0xffffu;
+  if (!v.far && !v.plain) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int rt = 0; rt < AT_KT / 16; ++rt) {
+      const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((unsigned)(c.row0 + it0 + i - c.lo) >= (unsigned)(c.hi - c.lo)) ok &= ~(1u << (rt * 4 + i));
+    }
+  }
+  v.okm = ok;
+  return v;
+}
+
 // 8 consecutive elements (logical 8-element group lg of a row) as NS bf16 parts.
 template <typename TIn, int NS>
 __device__ __forceinline__ void lds_frag(const unsigned char* row, int lg, int key, u16x8* out) {
@@ -209,11 +381,9 @@ struct AtState {
 // 32(rt/2) + 8g + 4(rt%2) + i of the tile.
 template <typename TIn, int D, int WAVES, int QG, bool CAUSAL>
 __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm, const unsigned char* stg,
-                                             const Cursor& c,
-                                             bool far,
+                                             const TileView& tv,
                                              const u16x8 (&qf)[QG][D / 32][sizeof(TIn) == 2 ? 1 : 3],
-                                             AtState<D> (&st)[QG], float s2, const int (&qrow)[QG],
-                                             int qmin) {
+                                             AtState<D> (&st)[QG], float s2, const int (&qrow)[QG]) {
   using G = AtGeo<TIn, D>;
   constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
   constexpr int KS = D / 32, DT = D / 16;
@@ -236,26 +406,18 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
       for (int qg = 0; qg < QG; ++qg) sc[qg][rt] = mfma_split<NS, NS>(a, qf[qg][k], sc[qg][rt]);
     }
   }
-  // A plain tile lies inside [lo, hi) and (causal) below every query row of
-  // the workgroup: no mask, unit weights.
-  const bool plain = !far && c.row0 >= c.lo && c.row0 + AT_KT <= c.hi && (!CAUSAL || c.row0 + AT_KT - 1 <= qmin);
-  // otherwise: log-weights of the lane's items (far), or which rows lie in
-  // [lo, hi) (a masked row's logit is replaced, not offset, since rows outside
-  // the key segments of a level hold unspecified values)
+  // far: log-weights of the lane's items; exact: the lane's valid items (a
+  // masked row's logit is replaced, not offset, since rows outside the key
+  // segments of a level hold unspecified values); plain: neither
+  const bool far = tv.far, plain = tv.plain;
   f32x4 bv[RT];
-  uint32_t ok = 0xffffu;
+  const uint32_t ok = far ? 0xffffu : tv.okm;
   if (!plain) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
-      if (far) {
-        bv[rt] = *reinterpret_cast<const f32x4*>(&sm.far_bias[c.row0 + it0]);
-      } else {
-        bv[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if ((unsigned)(c.row0 + it0 + i - c.lo) >= (unsigned)(c.hi - c.lo)) ok &= ~(1u << (rt * 4 + i));
-      }
+      if (far) bv[rt] = *reinterpret_cast<const f32x4*>(&sm.far_bias[tv.row0 + it0]);
+      else bv[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 #pragma unroll
@@ -275,7 +437,7 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = (ok >> (rt * 4 + i)) & 1u ? fmaf(s2, sc[qg][rt][i], bv[rt][i]) : -INFINITY;
-          if (CAUSAL && c.row0 + it0 + i > qrow[qg]) v = -INFINITY;
+          if (CAUSAL && tv.row0 + it0 + i > qrow[qg]) v = -INFINITY;
           x[rt * 4 + i] = v;
           mloc = fmaxf(mloc, v);
         }
@@ -351,6 +513,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   constexpr int KS = D / 32, DT = D / 16;
   // one-wave workgroups (small query clusters) keep two stages: more of them fit per CU
   constexpr int ST = WAVES == 1 ? 2 : G::ST, PD = ST - 1;
+  // small query clusters (one-wave workgroups): tiles gathered from 8-row chunks
+  constexpr bool GATHER = WAVES == 1 && MODE != MODE_LOCAL;
   constexpr int LPT = (AT_KT * G::CHK + D * G::CHV) / NT;   // copies per thread per tile
   static_assert(PD * LPT <= 63, "copies in flight exceed the counter");
   __shared__ SM sm;
@@ -495,7 +659,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
           const int alo = k0 + lo[q], ahi = k0 + hi[q];
           sm.seg_lo[run] = alo;
           sm.seg_hi[run] = ahi;
-          ntl += (ahi - (alo & ~7) + AT_KT - 1) / AT_KT;
+          ntl += GATHER ? (ahi - (alo & ~7) + 7) >> 3                // 8-row chunks
+                        : (ahi - (alo & ~7) + AT_KT - 1) / AT_KT;  // tiles
           ++run;
         }
       }
@@ -530,18 +695,38 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     src.Vt = reinterpret_cast<const unsigned char*>(b.Vt) + slice * D * (size_t)b.Nv * esz;
   }
   __syncthreads();
-  const int ntiles = MODE == MODE_LOCAL ? (qhi - (k0 & ~7) + AT_KT - 1) / AT_KT
-                                        : src.nfar + __builtin_amdgcn_readfirstlane(sm.sel[5]);
+  // exact part: tiles (contiguous) or 8-row chunks, 8 to a tile (gathered)
+  const int nex = MODE == MODE_LOCAL ? (qhi - (k0 & ~7) + AT_KT - 1) / AT_KT
+                                     : __builtin_amdgcn_readfirstlane(sm.sel[5]);
+  const int ntiles = (MODE == MODE_LOCAL ? 0 : src.nfar) + (GATHER ? (nex + 7) / 8 : nex);
 
   // ---- tile loop ----
+  // two cursors: copies run PD tiles ahead of consumption.  Contiguous tiles
+  // step through each cluster 64 rows at a time, gathered tiles 8 at a time.
   Cursor lc = cur_first(sm, src), cc = lc;
-#pragma unroll
-  for (int p = 0; p < PD; ++p) {
-    if (p < ntiles) {
-      issue_tile<TIn, D, WAVES>(stg[p], src, lc);
+  Chunks lgc = chunks_first(sm, src), cgc = lgc;
+  auto issue_next = [&](unsigned char* dst) __attribute__((always_inline)) {
+    if constexpr (GATHER) {
+      const TDesc d = take_tile(sm, src, lgc);
+      issue_tile_g<TIn, D, WAVES>(dst, src, d);
+    } else {
+      issue_tile<TIn, D, WAVES>(dst, src, lc);
       lc = cur_next(sm, src, lc);
     }
-  }
+  };
+  auto view_next = [&]() __attribute__((always_inline)) -> TileView {
+    if constexpr (GATHER) {
+      const TDesc d = take_tile(sm, src, cgc);
+      return view_of(d);
+    } else {
+      const TileView v = view_of<MODE == MODE_LOCAL>(src, cc, qlo);
+      cc = cur_next(sm, src, cc);
+      return v;
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < PD; ++p)
+    if (p < ntiles) issue_next(stg[p]);
   // query fragments (loaded after the first copies are on their way)
   int myq[QG];
   u16x8 qf[QG][KS][NS];
@@ -577,13 +762,9 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     else __builtin_amdgcn_s_waitcnt(at_wait(0, 0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (t + PD < ntiles) {
-      issue_tile<TIn, D, WAVES>(stg[sl], src, lc);
-      lc = cur_next(sm, src, lc);
-    }
-    consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, stg[sc_], cc, cc.t < src.nfar, qf, st, s2, qmask,
-                                                       qlo);
-    cc = cur_next(sm, src, cc);
+    if (t + PD < ntiles) issue_next(stg[sl]);
+    const TileView tv = view_next();
+    consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, stg[sc_], tv, qf, st, s2, qmask);
     sl = sl + 1 == ST ? 0 : sl + 1;
     sc_ = sc_ + 1 == ST ? 0 : sc_ + 1;
   }
@@ -657,14 +838,16 @@ __global__ void __launch_bounds__(256) vt_kernel(Plan pl, const void* Vp, const 
                                : reinterpret_cast<const TIn*>(V) + (size_t)(s - nsorted) * N * D;
   TIn* dst = reinterpret_cast<TIn*>(Vt) + (size_t)s * D * Nv;
   const int j0 = blk * AT_KT;
-  // causal levels: only the key segments [2tm, 2tm + m) of a level's sorted
-  // copy are written; every other column becomes zero
-  const int m = s < nsorted && pl.causal ? pl.lev_m[s / (pl.B * pl.Hkv)] : 0;
+  // causal levels: only the key segments [2tm, 2tm + m), t < nseg, of a
+  // level's sorted copy are written; every other column becomes zero
+  const int lev = s < nsorted && pl.causal ? s / (pl.B * pl.Hkv) : -1;
+  const int m = lev >= 0 ? pl.lev_m[lev] : 0, nseg = lev >= 0 ? pl.lev_nseg[lev] : 0;
   for (int idx = threadIdx.x; idx < AT_KT * CH; idx += 256) {
     const int r = idx / CH, e0 = (idx % CH) * E;
     const int j = j0 + r;
     V16 v{};
-    if (j < N && (m == 0 || (j / m) % 2 == 0)) v = *reinterpret_cast<const V16*>(src + (size_t)j * D + e0);
+    if (j < N && (m == 0 || ((j / m) % 2 == 0 && j / (2 * m) < nseg)))
+      v = *reinterpret_cast<const V16*>(src + (size_t)j * D + e0);
 #pragma unroll
     for (int e = 0; e < E; ++e) tile[r][e0 + e] = v[e];
   }
