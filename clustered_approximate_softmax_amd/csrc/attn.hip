@@ -20,6 +20,10 @@
 // from a dim-major copy of the same rows (built by vt_kernel), so both halves
 // of a tile are 64 x 16-byte row segments: they are copied global -> LDS by
 // the direct-to-LDS loads, with no register staging and no transposition.
+// One-wave workgroups (query clusters of under 48 rows, where key clusters
+// are as small) gather their exact tiles instead: a tile is 8 chunks of 8
+// rows, each chunk from a multiple of 8 inside one retrieved cluster, so
+// several small clusters share a tile rather than each padding its own.
 //
 // Pipeline: ST LDS stages, tile t+ST-1 is in flight while tile t is
 // consumed; one barrier per tile.  The waits on the copies are explicit
