@@ -26,7 +26,9 @@
 // several small clusters share a tile rather than each padding its own.
 //
 // Pipeline: ST LDS stages, tile t+ST-1 is in flight while tile t is
-// consumed; one barrier per tile.  The waits on the copies are explicit
+// consumed; one barrier per tile.  One-wave workgroups use a single stage
+// (copy, wait, consume): at half the LDS twice as many run per CU, and their
+// copies overlap each other's work.  The waits on the copies are explicit
 // (s_waitcnt vmcnt with the number of copies issued after the tile), so the
 // loop holds no other global loads.  LDS rows are 16-byte-chunk swizzled so
 // that the fragment reads are free of bank conflicts.
@@ -515,8 +517,9 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
   constexpr int NT = 64 * WAVES, QT = 16 * QG * WAVES;
   constexpr int KS = D / 32, DT = D / 16;
-  // one-wave workgroups (small query clusters) keep two stages: more of them fit per CU
-  constexpr int ST = WAVES == 1 ? 2 : G::ST, PD = ST - 1;
+  // one-wave workgroups (small query clusters) keep one stage: twice as many
+  // fit per CU, and the copy latency of one hides behind the others' work
+  constexpr int ST = WAVES == 1 ? 1 : G::ST, PD = ST - 1;
   // small query clusters (one-wave workgroups): tiles gathered from 8-row chunks
   constexpr bool GATHER = WAVES == 1 && MODE != MODE_LOCAL;
   constexpr int LPT = (AT_KT * G::CHK + D * G::CHV) / NT;   // copies per thread per tile
@@ -762,11 +765,21 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     // they exist, may be in flight); after the barrier every thread's have,
     // and tile t-1 is consumed.  Only real tiles are copied.
     asm volatile("" ::: "memory");
-    if (t + PD - 1 < ntiles) __builtin_amdgcn_s_waitcnt(at_wait((PD - 1) * LPT, 0));
-    else __builtin_amdgcn_s_waitcnt(at_wait(0, 0));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (t + PD < ntiles) issue_next(stg[sl]);
+    if constexpr (PD == 0) {
+      // one stage: after every wave is done with tile t-1, copy tile t and wait for it
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue_next(stg[0]);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(at_wait(0, 0));
+      __builtin_amdgcn_s_barrier();
+    } else {
+      if (t + PD - 1 < ntiles) __builtin_amdgcn_s_waitcnt(at_wait((PD - 1) * LPT, 0));
+      else __builtin_amdgcn_s_waitcnt(at_wait(0, 0));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + PD < ntiles) issue_next(stg[sl]);
+    }
     const TileView tv = view_next();
     consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, stg[sc_], tv, qf, st, s2, qmask);
     sl = sl + 1 == ST ? 0 : sl + 1;
