@@ -518,8 +518,9 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   constexpr int NT = 64 * WAVES, QT = 16 * QG * WAVES;
   constexpr int KS = D / 32, DT = D / 16;
   // one-wave workgroups (small query clusters) keep one stage: twice as many
-  // fit per CU, and the copy latency of one hides behind the others' work
-  constexpr int ST = WAVES == 1 ? 1 : G::ST, PD = ST - 1;
+  // fit per CU, and the copy latency of one hides behind the others' work;
+  // four waves with one query group keep two (four workgroups per CU)
+  constexpr int ST = WAVES == 1 ? 1 : QG == 1 ? 2 : G::ST, PD = ST - 1;
   // small query clusters (one-wave workgroups): tiles gathered from 8-row chunks
   constexpr bool GATHER = WAVES == 1 && MODE != MODE_LOCAL;
   constexpr int LPT = (AT_KT * G::CHK + D * G::CHV) / NT;   // copies per thread per tile
