@@ -213,44 +213,118 @@ __device__ __forceinline__ void km_screen_batch(const SM& sm, const V8 (&x)[D / 
   for (int u = 0; u < TB; ++u) acc[u] = mfma(as_bf(fnm[u]), as_bf(bn), acc[u]);
 }
 
+// The same screening sums for the two 16-point groups of a wave at once:
+// each centroid fragment is read from LDS once and feeds both groups'
+// MFMAs (every accumulator sees the same operations in the same order as
+// in km_screen_batch, so the sums are identical).
+template <int D, int TB, typename SM, typename V8>
+__device__ __forceinline__ void km_screen_batch2(const SM& sm, const V8 (&x)[2][D / 32], const u16x8 (&bn)[2],
+                                                 int t0, f32x4 (&acc)[2][TB]) {
+  constexpr int KS = D / 32;
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+  u16x8 flo[TB][KS], fhi[TB][KS], fnm[TB];
+#pragma unroll
+  for (int u = 0; u < TB; ++u) {
+    const int row = 16 * (t0 + u) + col;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      flo[u][k] = *reinterpret_cast<const u16x8*>(&sm.mu_hat[1][row][32 * k + 8 * g]);
+      fhi[u][k] = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][row][32 * k + 8 * g]);
+    }
+    fnm[u] = *reinterpret_cast<const u16x8*>(&sm.mu_hat[0][row][D]);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int u = 0; u < TB; ++u) acc[q][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) acc[q][u] = mfma(as_bf(flo[u][k]), as_bf(x[q][k]), acc[q][u]);
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) acc[q][u] = mfma(as_bf(fhi[u][k]), as_bf(x[q][k]), acc[q][u]);
+#pragma unroll
+  for (int u = 0; u < TB; ++u)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) acc[q][u] = mfma(as_bf(fnm[u]), as_bf(bn[q]), acc[q][u]);
+}
+
+// Stage group grp of the wave's points (transposed, in LDS) and form its
+// squared norm and the point side of the norm k-step.
+template <typename TIn, int D, typename SM>
+__device__ __forceinline__ void km_stage_group(SM& sm, const XRegs<TIn, D>& xr, int grp, float& xsq_out,
+                                               u16x8& bn) {
+  using S = KmShape<TIn, D>;
+  constexpr int KS = D / 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
+  const int pl = w * (S::SUB / 4) + grp * 16 + col;
+  float xsq = 0.f;
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = xval(xr.x[grp][k], j);
+      xsq = fmaf(v, v, xsq);
+      sm.xt[0][32 * k + 8 * g + j][pl] = xr.x[grp][k][j];
+    }
+  }
+  xsq += __shfl_xor(xsq, 16, 64);
+  xsq += __shfl_xor(xsq, 32, 64);
+  xsq_out = xsq;
+  bn = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  if (g == 0) {
+    const uint16_t xh = f2bf(xsq);
+    bn[0] = xh;
+    bn[1] = 0x3F80;
+    bn[2] = 0x3F80;
+    bn[3] = f2bf(xsq - bf2f(xh));
+  }
+}
+
+// Decide the label of each point of group grp from its screened best and
+// runner-up keys (this lane's share; merged over the wave here), refine the
+// near-ties in fp32, write the label to LDS and to glab.
 template <typename TIn, int D, int CT, typename SM>
-__device__ void km_assign_bf16(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nvalid, const float* cent,
-                               int Ceff, float Rmax, int32_t* glab) {
-  constexpr int TB = CT < 4 ? CT : 4;   // cluster tiles per screening batch
+__device__ __forceinline__ void km_finish_group(SM& sm, const XRegs<TIn, D>& xr, int grp, int m1, int m2,
+                                                float xsq, const u16x8& bn, int sub0, int nvalid,
+                                                const float* cent, int Ceff, float Rmax, int32_t* glab) {
+  constexpr int TB = CT < 4 ? CT : 4;
   using S = KmShape<TIn, D>;
   constexpr int KS = D / 32;
   constexpr int IB = CT <= 8 ? 7 : 8;
   constexpr int KMASK = ~((1 << IB) - 1);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int col = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
+  const int pl = w * (S::SUB / 4) + grp * 16 + col;
+  const bool valid = pl < nvalid;
+  m1 |= 4 * g;
 #pragma unroll
-  for (int grp = 0; grp < S::G16; ++grp) {
-    const int pl = w * (S::SUB / 4) + grp * 16 + col;
-    const bool valid = pl < nvalid;
-    float xsq = 0.f;
+  for (int m = 16; m <= 32; m <<= 1) {
+    const int b1 = __shfl_xor(m1, m, 64), b2 = __shfl_xor(m2, m, 64);
+    m2 = min(max(m1, b1), min(m2, b2));
+    m1 = min(m1, b1);
+  }
+  int label = m1 & ((1 << IB) - 1);
+  const float f1 = __int_as_float(m1 & KMASK), f2 = __int_as_float(m2 & KMASK);
+  const float xn = sqrtf(xsq);
+  // screening error (split residual, accumulation, norm split) plus key truncation
+  const float margin = 2.44140625e-4f * xn * Rmax + 1.220703125e-4f * (xsq + Rmax * Rmax) +
+                       (IB == 7 ? 3.0517578125e-05f : 6.103515625e-05f) * (fabsf(f1) + fabsf(f2));
+  const bool need = valid && Ceff > 1 && (f2 - f1 <= margin);
+  if (__any(need)) {
+    // candidates within the margin; the screening MFMAs are recomputed by the
+    // whole wave (an MFMA reads its operands from every lane, active or not)
+    const float thr = f1 + margin;
+    constexpr int NW = (CT * 16 + 63) / 64;
+    unsigned long long cm[NW];
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = xval(xr.x[grp][k], j);
-        xsq = fmaf(v, v, xsq);
-        sm.xt[0][32 * k + 8 * g + j][pl] = xr.x[grp][k][j];
-      }
-    }
-    xsq += __shfl_xor(xsq, 16, 64);
-    xsq += __shfl_xor(xsq, 32, 64);
-    u16x8 bn = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (g == 0) {
-      const uint16_t xh = f2bf(xsq);
-      bn[0] = xh;
-      bn[1] = 0x3F80;
-      bn[2] = 0x3F80;
-      bn[3] = f2bf(xsq - bf2f(xh));
-    }
-    int m1 = 0x7fffffff, m2 = 0x7fffffff;
-    // batches of up to TB cluster tiles; a batch with 1 or 2 live tiles runs
-    // at that width (rows of absent clusters carry a huge norm and never win)
-    auto keys = [&](auto tbc, int t0) {
+    for (int q = 0; q < NW; ++q) cm[q] = 0ull;
+    auto cands = [&](auto tbc, int t0) {
       constexpr int TBX = decltype(tbc)::value;
       f32x4 acc[TBX];
       km_screen_batch<D, TBX>(sm, xr.x[grp], bn, t0, acc);
@@ -258,42 +332,121 @@ __device__ void km_assign_bf16(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nv
       for (int u = 0; u < TBX; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = (__float_as_int(acc[u][i]) & KMASK) | (16 * (t0 + u) + i);
-          const int n2 = med3i(m1, m2, key);
-          m1 = min(m1, key);
-          m2 = n2;
+          const int c = 16 * (t0 + u) + 4 * g + i;
+          if (need && c < Ceff && acc[u][i] <= thr) cm[c >> 6] |= 1ull << (c & 63);
         }
     };
 #pragma unroll
     for (int t0 = 0; t0 < CT; t0 += TB) {
       const int live = min(TB, (Ceff - 16 * t0 + 15) / 16);
-      if (live > 2) keys(std::integral_constant<int, TB>{}, t0);
-      else if (live == 2) keys(std::integral_constant<int, TB < 2 ? TB : 2>{}, t0);
+      if (live > 2) cands(std::integral_constant<int, TB>{}, t0);
+      else if (live == 2) cands(std::integral_constant<int, TB < 2 ? TB : 2>{}, t0);
+      else if (live == 1) cands(std::integral_constant<int, 1>{}, t0);
+    }
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      cm[q] |= __shfl_xor(cm[q], 16, 64);
+      cm[q] |= __shfl_xor(cm[q], 32, 64);
+    }
+    // exact fp32 distances of the candidates (lanes of points that need no
+    // refinement have an empty mask)
+    float bd = INFINITY;
+    int bc = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      unsigned long long mword = cm[q];
+      while (mword) {
+        const int c = 64 * q + __builtin_ctzll(mword);
+        mword &= mword - 1;
+        float part = 0.f;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          float mv[8];
+          if constexpr (SM::KEEP32) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mv[j] = sm.mu32[c][32 * k + 8 * g + j];
+          } else {
+            const float* mr = cent + (size_t)c * D + 32 * k + 8 * g;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mv[j] = mr[j];
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float df = xval(xr.x[grp][k], j) - mv[j];
+            part = fmaf(df, df, part);
+          }
+        }
+        part += __shfl_xor(part, 16, 64);
+        part += __shfl_xor(part, 32, 64);
+        if (part < bd || (part == bd && c < bc)) { bd = part; bc = c; }
+      }
+    }
+    if (need) label = bc;
+  }
+  if (g == 0) {
+    sm.lab[pl] = valid ? label : -1;
+    if (valid) glab[sub0 + pl] = label;
+  }
+}
+
+// bf16 inputs: assignment of one sub-tile (two 16-point groups per wave).
+// From four cluster tiles up (eight at D = 128), both groups are screened together so that
+// every centroid fragment read from LDS feeds two MFMAs; with fewer, each
+// group is screened on its own (fewer live registers, more workgroups).
+template <typename TIn, int D, int CT, typename SM>
+__device__ void km_assign_bf16(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nvalid, const float* cent,
+                               int Ceff, float Rmax, int32_t* glab) {
+  constexpr int TB = CT < 4 ? CT : 4;   // cluster tiles per screening batch
+  using S = KmShape<TIn, D>;
+  constexpr int IB = CT <= 8 ? 7 : 8;
+  constexpr int KMASK = ~((1 << IB) - 1);
+  static_assert(S::G16 == 2, "two 16-point groups per wave");
+  // (at D = 128 with four tiles the paired path would need more than 256 VGPRs)
+  if constexpr (CT >= 4 && (D == 64 || CT >= 8)) {
+    float xsq[2];
+    u16x8 bn[2];
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) km_stage_group<TIn, D>(sm, xr, grp, xsq[grp], bn[grp]);
+    int m1[2] = {0x7fffffff, 0x7fffffff}, m2[2] = {0x7fffffff, 0x7fffffff};
+    // batches of two cluster tiles for both groups (the same four
+    // accumulators in flight as four tiles of one group); a batch with one
+    // live tile runs at that width (absent clusters carry a huge norm)
+    auto keys = [&](auto tbc, int t0) __attribute__((always_inline)) {
+      constexpr int TBX = decltype(tbc)::value;
+      f32x4 acc[2][TBX];
+      km_screen_batch2<D, TBX>(sm, xr.x, bn, t0, acc);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int u = 0; u < TBX; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = (__float_as_int(acc[q][u][i]) & KMASK) | (16 * (t0 + u) + i);
+            const int n2 = med3i(m1[q], m2[q], key);
+            m1[q] = min(m1[q], key);
+            m2[q] = n2;
+          }
+    };
+#pragma unroll
+    for (int t0 = 0; t0 < CT; t0 += 2) {
+      const int live = min(2, (Ceff - 16 * t0 + 15) / 16);
+      if (live == 2) keys(std::integral_constant<int, 2>{}, t0);
       else if (live == 1) keys(std::integral_constant<int, 1>{}, t0);
     }
-    m1 |= 4 * g;
 #pragma unroll
-    for (int m = 16; m <= 32; m <<= 1) {
-      const int b1 = __shfl_xor(m1, m, 64), b2 = __shfl_xor(m2, m, 64);
-      m2 = min(max(m1, b1), min(m2, b2));
-      m1 = min(m1, b1);
-    }
-    int label = m1 & ((1 << IB) - 1);
-    const float f1 = __int_as_float(m1 & KMASK), f2 = __int_as_float(m2 & KMASK);
-    const float xn = sqrtf(xsq);
-    // screening error (split residual, accumulation, norm split) plus key truncation
-    const float margin = 2.44140625e-4f * xn * Rmax + 1.220703125e-4f * (xsq + Rmax * Rmax) +
-                         (IB == 7 ? 3.0517578125e-05f : 6.103515625e-05f) * (fabsf(f1) + fabsf(f2));
-    const bool need = valid && Ceff > 1 && (f2 - f1 <= margin);
-    if (__any(need)) {
-      // candidates within the margin; the screening MFMAs are recomputed by the
-      // whole wave (an MFMA reads its operands from every lane, active or not)
-      const float thr = f1 + margin;
-      constexpr int NW = (CT * 16 + 63) / 64;
-      unsigned long long cm[NW];
+    for (int grp = 0; grp < 2; ++grp)
+      km_finish_group<TIn, D, CT>(sm, xr, grp, m1[grp], m2[grp], xsq[grp], bn[grp], sub0, nvalid, cent, Ceff,
+                                  Rmax, glab);
+  } else {
 #pragma unroll
-      for (int q = 0; q < NW; ++q) cm[q] = 0ull;
-      auto cands = [&](auto tbc, int t0) {
+    for (int grp = 0; grp < 2; ++grp) {
+      float xsq;
+      u16x8 bn;
+      km_stage_group<TIn, D>(sm, xr, grp, xsq, bn);
+      int m1 = 0x7fffffff, m2 = 0x7fffffff;
+      // batches of up to TB cluster tiles; a batch with 1 or 2 live tiles
+      // runs at that width (rows of absent clusters carry a huge norm)
+      auto keys = [&](auto tbc, int t0) __attribute__((always_inline)) {
         constexpr int TBX = decltype(tbc)::value;
         f32x4 acc[TBX];
         km_screen_batch<D, TBX>(sm, xr.x[grp], bn, t0, acc);
@@ -301,60 +454,20 @@ __device__ void km_assign_bf16(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nv
         for (int u = 0; u < TBX; ++u)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int c = 16 * (t0 + u) + 4 * g + i;
-            if (need && c < Ceff && acc[u][i] <= thr) cm[c >> 6] |= 1ull << (c & 63);
+            const int key = (__float_as_int(acc[u][i]) & KMASK) | (16 * (t0 + u) + i);
+            const int n2 = med3i(m1, m2, key);
+            m1 = min(m1, key);
+            m2 = n2;
           }
       };
 #pragma unroll
       for (int t0 = 0; t0 < CT; t0 += TB) {
         const int live = min(TB, (Ceff - 16 * t0 + 15) / 16);
-        if (live > 2) cands(std::integral_constant<int, TB>{}, t0);
-        else if (live == 2) cands(std::integral_constant<int, TB < 2 ? TB : 2>{}, t0);
-        else if (live == 1) cands(std::integral_constant<int, 1>{}, t0);
+        if (live > 2) keys(std::integral_constant<int, TB>{}, t0);
+        else if (live == 2) keys(std::integral_constant<int, TB < 2 ? TB : 2>{}, t0);
+        else if (live == 1) keys(std::integral_constant<int, 1>{}, t0);
       }
-#pragma unroll
-      for (int q = 0; q < NW; ++q) {
-        cm[q] |= __shfl_xor(cm[q], 16, 64);
-        cm[q] |= __shfl_xor(cm[q], 32, 64);
-      }
-      // exact fp32 distances of the candidates (lanes of points that need no
-      // refinement have an empty mask)
-      float bd = INFINITY;
-      int bc = 0x7fffffff;
-#pragma unroll
-      for (int q = 0; q < NW; ++q) {
-        unsigned long long mword = cm[q];
-        while (mword) {
-          const int c = 64 * q + __builtin_ctzll(mword);
-          mword &= mword - 1;
-          float part = 0.f;
-#pragma unroll
-          for (int k = 0; k < KS; ++k) {
-            float mv[8];
-            if constexpr (SM::KEEP32) {
-#pragma unroll
-              for (int j = 0; j < 8; ++j) mv[j] = sm.mu32[c][32 * k + 8 * g + j];
-            } else {
-              const float* mr = cent + (size_t)c * D + 32 * k + 8 * g;
-#pragma unroll
-              for (int j = 0; j < 8; ++j) mv[j] = mr[j];
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float df = xval(xr.x[grp][k], j) - mv[j];
-              part = fmaf(df, df, part);
-            }
-          }
-          part += __shfl_xor(part, 16, 64);
-          part += __shfl_xor(part, 32, 64);
-          if (part < bd || (part == bd && c < bc)) { bd = part; bc = c; }
-        }
-      }
-      if (need) label = bc;
-    }
-    if (g == 0) {
-      sm.lab[pl] = valid ? label : -1;
-      if (valid) glab[sub0 + pl] = label;
+      km_finish_group<TIn, D, CT>(sm, xr, grp, m1, m2, xsq, bn, sub0, nvalid, cent, Ceff, Rmax, glab);
     }
   }
 }
