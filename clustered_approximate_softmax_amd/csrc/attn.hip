@@ -412,18 +412,19 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
       for (int qg = 0; qg < QG; ++qg) sc[qg][rt] = mfma_split<NS, NS>(a, qf[qg][k], sc[qg][rt]);
     }
   }
-  // far: log-weights of the lane's items; exact: the lane's valid items (a
-  // masked row's logit is replaced, not offset, since rows outside the key
-  // segments of a level hold unspecified values); plain: neither
+  // far: every item is a real cluster row with a finite score, weighted by
+  // its log-count bias (minus infinity for retrieved and empty clusters);
+  // exact: the lane's valid items (a masked row's logit is replaced, not
+  // offset, since rows outside the key segments of a level hold unspecified
+  // values); plain: neither
   const bool far = tv.far, plain = tv.plain;
+  const uint32_t ok = tv.okm;
   f32x4 bv[RT];
-  const uint32_t ok = far ? 0xffffu : tv.okm;
-  if (!plain) {
+  if (far) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
-      if (far) bv[rt] = *reinterpret_cast<const f32x4*>(&sm.far_bias[tv.row0 + it0]);
-      else bv[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bv[rt] = *reinterpret_cast<const f32x4*>(&sm.far_bias[tv.row0 + it0]);
     }
   }
 #pragma unroll
@@ -436,13 +437,22 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
 #pragma unroll
         for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sc[qg][rt][i]);
       mloc *= s2;
+    } else if (far) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = fmaf(s2, sc[qg][rt][i], bv[rt][i]);
+          x[rt * 4 + i] = v;
+          mloc = fmaxf(mloc, v);
+        }
     } else {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = (ok >> (rt * 4 + i)) & 1u ? fmaf(s2, sc[qg][rt][i], bv[rt][i]) : -INFINITY;
+          float v = (ok >> (rt * 4 + i)) & 1u ? s2 * sc[qg][rt][i] : -INFINITY;
           if (CAUSAL && tv.row0 + it0 + i > qrow[qg]) v = -INFINITY;
           x[rt * 4 + i] = v;
           mloc = fmaxf(mloc, v);
