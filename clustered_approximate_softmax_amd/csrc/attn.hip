@@ -937,13 +937,16 @@ template <typename TIn, int D>
 static hipError_t attn_all(const Plan& pl, const AttnBufs& b, hipStream_t st) {
   hipError_t e = launch_vt<TIn, D>(pl, b, st);
   if (e != hipSuccess) return e;
-  constexpr int QG = sizeof(TIn) == 2 ? 2 : 1;
+  // Every launch keeps one group of 16 queries per wave: two groups halve the
+  // LDS fragment reads per MFMA but need about 200 VGPRs (285 at D = 128),
+  // and the lost workgroups per CU cost more than the reads save.
   if (pl.causal) {
-    constexpr int WAVES = 4, QT = 16 * QG * 4;
+    // local blocks: 64-row query tiles
+    constexpr int WAVES = 4, QT = 16 * 4;
     const int nblk = (pl.N + pl.blk - 1) / pl.blk;
     const long long grid = (long long)pl.B * pl.Hq * nblk * ((pl.blk + QT - 1) / QT);
     MUSE_KT_PRE(st);
-    attn_kernel<TIn, TIn, D, WAVES, QG, MODE_LOCAL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, 0);
+    attn_kernel<TIn, TIn, D, WAVES, 1, MODE_LOCAL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, 0);
     MUSE_KT_POST("attn_local", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -951,8 +954,7 @@ static hipError_t attn_all(const Plan& pl, const AttnBufs& b, hipStream_t st) {
     // query clusters of ~m/C rows: the query tile (rows per workgroup) follows
     // the mean cluster size so that ragged clusters waste few tile rows
     const int avg = pl.lev_m[lev] / (pl.C > 0 ? pl.C : 1);
-    if (QG == 2 && avg >= 160) e = attn_level<TIn, D, 4, QG>(pl, b, lev, st);
-    else if (avg >= 48) e = attn_level<TIn, D, 4, 1>(pl, b, lev, st);
+    if (avg >= 48) e = attn_level<TIn, D, 4, 1>(pl, b, lev, st);
     else if constexpr (sizeof(TIn) == 2 || D == 64) e = attn_level<TIn, D, 1, 1>(pl, b, lev, st);
     else e = attn_level<TIn, D, 4, 1>(pl, b, lev, st);   // one wave could not keep a tile's copies counted
     if (e != hipSuccess) return e;
