@@ -350,6 +350,18 @@ __device__ __forceinline__ TileView view_of(const TileSrc& src, const Cursor& c,
   return v;
 }
 
+// The highest causal level whose query half holds row i, or -1 when only
+// the local block does.  Level l has span m = blk 2^l and its t-th segment
+// takes queries [2tm + m, 2tm + 2m): the rows whose local block index
+// q = floor(i / blk) has bit l set (and segment q >> (l+1) exists).
+__device__ __forceinline__ int last_level(const Plan& pl, int i) {
+  const int q = i / pl.blk;
+  int last = -1;
+  for (int l = 0; l < pl.nlev; ++l)
+    if (((q >> l) & 1) && (q >> (l + 1)) < pl.lev_nseg[l]) last = l;
+  return last;
+}
+
 // 8 consecutive elements (logical 8-element group lg of a row) as NS bf16 parts.
 template <typename TIn, int NS>
 __device__ __forceinline__ void lds_frag(const unsigned char* row, int lg, int key, u16x8* out) {
@@ -809,41 +821,64 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     if (row < 0) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const float lse = l > 0.f ? (st[qg].m + __log2f(l)) * LN2 : -INFINITY;
-    if (MODE == MODE_ACAUSAL) {
+    // the output row in the output dtype (16 dims per dt, 4 per lane)
+    auto write_out = [&](const f32x4 (&v)[DT], float lse_out) __attribute__((always_inline)) {
       TOut* O = reinterpret_cast<TOut*>(b.O) + ((size_t)bh * pl.N + row) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         if constexpr (sizeof(TOut) == 2) {
           typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          u32x2 wv = {pk_bf16(st[qg].o[dt][0] * inv, st[qg].o[dt][1] * inv),
-                      pk_bf16(st[qg].o[dt][2] * inv, st[qg].o[dt][3] * inv)};
+          u32x2 wv = {pk_bf16(v[dt][0], v[dt][1]), pk_bf16(v[dt][2], v[dt][3])};
           *reinterpret_cast<u32x2*>(O + 16 * dt + 4 * g) = wv;
         } else {
-          *reinterpret_cast<f32x4*>(O + 16 * dt + 4 * g) = st[qg].o[dt] * inv;
+          *reinterpret_cast<f32x4*>(O + 16 * dt + 4 * g) = v[dt];
         }
       }
-      if (g == 0) b.lse[(size_t)bh * pl.N + row] = lse;
+      if (g == 0) b.lse[(size_t)bh * pl.N + row] = lse_out;
+    };
+    f32x4 on[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) on[dt] = st[qg].o[dt] * inv;
+    if (MODE == MODE_ACAUSAL) {
+      write_out(on, lse);
     } else {
+      // causal: partials of the local block and of each level a row belongs
+      // to are merged in fp32; the last of them writes the output itself
       float* oa = b.oacc + ((size_t)bh * pl.N + row) * D;
       float* la = b.lacc + (size_t)bh * pl.N + row;
+      const bool fin = last_level(pl, row) == (MODE == MODE_LOCAL ? -1 : lev);
       if (MODE == MODE_LOCAL) {
+        if (fin) {
+          write_out(on, lse);
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(oa + 16 * dt + 4 * g) = on[dt];
+          if (g == 0) *la = lse;
+        }
+      } else {
+        if (!(l > 0.f) && !fin) continue;
+        const float lold = *la;
+        float fo = 1.f, fn = 0.f, lnew = lold;
+        if (l > 0.f) {
+          const float L = fmaxf(lold, lse);
+          const float wo = __expf(lold - L), wn = __expf(lse - L);
+          const float tot = wo + wn;
+          fo = wo / tot;
+          fn = 1.f / tot;
+          lnew = L + logf(tot);
+          fn *= wn;
+        }
+        f32x4 mv[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<f32x4*>(oa + 16 * dt + 4 * g) = st[qg].o[dt] * inv;
-        if (g == 0) *la = lse;
-      } else {
-        if (!(l > 0.f)) continue;
-        const float lold = *la;
-        const float L = fmaxf(lold, lse);
-        const float wo = __expf(lold - L), wn = __expf(lse - L);
-        const float tot = wo + wn;
-        const float fo = wo / tot, fn = wn * inv / tot;
+          mv[dt] = *reinterpret_cast<const f32x4*>(oa + 16 * dt + 4 * g) * fo + on[dt] * fn;
+        if (fin) {
+          write_out(mv, lnew);
+        } else {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          f32x4 prev = *reinterpret_cast<const f32x4*>(oa + 16 * dt + 4 * g);
-          *reinterpret_cast<f32x4*>(oa + 16 * dt + 4 * g) = prev * fo + st[qg].o[dt] * fn;
+          for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(oa + 16 * dt + 4 * g) = mv[dt];
+          if (g == 0) *la = lnew;
         }
-        if (g == 0) *la = L + logf(tot);
       }
     }
   }
@@ -888,15 +923,6 @@ __global__ void __launch_bounds__(256) vt_kernel(Plan pl, const void* Vp, const 
     for (int e = 0; e < E; ++e) v[e] = tile[jj + e][d];
     *reinterpret_cast<V16*>(dst + (size_t)d * Nv + j0 + jj) = v;
   }
-}
-
-template <typename TOut>
-__global__ void finalize_kernel(const float* oacc, const float* lacc, TOut* O, float* lse,
-                                long long rows, int D) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long n = rows * D;
-  if (i < n) store1<TOut>(O + i, oacc[i]);
-  if (i < rows) lse[i] = lacc[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -958,15 +984,6 @@ static hipError_t attn_all(const Plan& pl, const AttnBufs& b, hipStream_t st) {
     else if constexpr (sizeof(TIn) == 2 || D == 64) e = attn_level<TIn, D, 1, 1>(pl, b, lev, st);
     else e = attn_level<TIn, D, 4, 1>(pl, b, lev, st);   // one wave could not keep a tile's copies counted
     if (e != hipSuccess) return e;
-  }
-  if (pl.causal) {
-    const long long rows = (long long)pl.B * pl.Hq * pl.N;
-    const long long n = rows * pl.D;
-    MUSE_KT_PRE(st);
-    finalize_kernel<TIn><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
-        b.oacc, b.lacc, reinterpret_cast<TIn*>(b.O), b.lse, rows, pl.D);
-    MUSE_KT_POST("finalize", st);
-    e = hipGetLastError();
   }
   return e;
 }
