@@ -471,8 +471,7 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
         }
       }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    mloc = max4_lanes(mloc);
     // lazy rescale: the running max of a row moves only when the tile's max
     // exceeds it by more than 8 (weights stay below 2^8, exact in the end
     // since output and normaliser share the same max)

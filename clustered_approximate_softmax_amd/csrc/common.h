@@ -88,6 +88,30 @@ __host__ __device__ inline void cset_rows(const Plan& pl, const CSet& s, int p, 
 // ---------------------------------------------------------------------------
 // bf16 helpers (round to nearest even; inputs are finite)
 // ---------------------------------------------------------------------------
+// The value of lane l ^ 16 (or l ^ 32) of a wave, through the lane-swap
+// instructions (VALU; no LDS round trip).  With the same register in both
+// operands, the swap leaves the values of lanes l & ~B and l | B in its two
+// results on every lane l (B = 16 or 32); the partner's is the other one.
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return (threadIdx.x & 16) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float lane_xor16(float x) { return __uint_as_float(lane_xor16(__float_as_uint(x))); }
+__device__ __forceinline__ float lane_xor32(float x) { return __uint_as_float(lane_xor32(__float_as_uint(x))); }
+__device__ __forceinline__ int lane_xor16(int x) { return (int)lane_xor16((uint32_t)x); }
+__device__ __forceinline__ int lane_xor32(int x) { return (int)lane_xor32((uint32_t)x); }
+// max of the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the same on all four)
+__device__ __forceinline__ float max4_lanes(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ uint16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
