@@ -866,9 +866,13 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
 
 // ===========================================================================
 // Batched fp32 contraction on split-bf16 MFMA: C[m][n] = sum_k A[m][k] B[k][n]
-// per batch, 64 x 64 output tile per workgroup, k in steps of 32.  The
-// problem type supplies the batch view, the element loads and the store;
-// B is read along n, A along k (A_KC) or along m.
+// per batch, for the whole n range (N = D) and 128 rows of m per workgroup,
+// k in steps of 32, so that the large operand is read once.  Each thread
+// loads 16 consecutive floats of A (along k, or along m) and N/8 of B (along
+// n) per step; the next step's loads are in flight while the current step
+// is contracted.  The problem type supplies the batch view and the row
+// loads (zeros outside the operand); per output element the k order is
+// ascending in steps of 32, the same for every tiling.
 // ===========================================================================
 template <int NS>
 __device__ __forceinline__ void split_parts(float x, uint16_t* dst, int stride) {
@@ -883,80 +887,96 @@ __device__ __forceinline__ void split_parts(float x, uint16_t* dst, int stride) 
   }
 }
 
-template <class P, int NS>
+__device__ __forceinline__ void load4x(const float* p, int n4, float* out) {
+  for (int q = 0; q < n4; ++q) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * q);
+    out[4 * q] = x[0]; out[4 * q + 1] = x[1]; out[4 * q + 2] = x[2]; out[4 * q + 3] = x[3];
+  }
+}
+
+constexpr int BG_TM = 128, BG_KT = 32;
+
+template <class P, int NS, int N>
 __global__ void __launch_bounds__(256) bwd_gemm_kernel(P prob) {
-  __shared__ __align__(16) uint16_t As[NS][64][40];
-  __shared__ __align__(16) uint16_t Bs[NS][64][40];
+  static_assert(N == 64 || N == 128, "N is the head dim");
+  constexpr int TM = BG_TM, KT = BG_KT, BF = KT * N / 256;   // B floats per thread
+  __shared__ __align__(16) uint16_t As[NS][TM][KT + 8];
+  __shared__ __align__(16) uint16_t Bs[NS][N][KT + 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
   int id = blockIdx.x;
-  const int tn = id % prob.ntiles; id /= prob.ntiles;
-  const int tm = id % prob.mtiles; id /= prob.mtiles;
+  const int tm = id % prob.mtiles;
+  id /= prob.mtiles;
   typename P::View v;
   prob.view(id, v);
-  const int m0 = tm * 64, n0 = tn * 64;
-  if (m0 >= v.M || n0 >= v.N) return;
-  f32x4 acc[4];
+  const int m0 = tm * TM;
+  if (m0 >= v.M) return;
+  float ra[16], rb[BF];
+  auto load = [&](int k0) __attribute__((always_inline)) {
+    if constexpr (P::A_KC) prob.a16(v, m0 + tid / 2, k0 + (tid % 2) * 16, ra);   // row m, 16 k
+    else prob.a16(v, m0 + (tid % 8) * 16, k0 + tid / 8, ra);                    // 16 m, column k
+    prob.bn(v, k0 + tid / 8, (tid % 8) * BF, rb);
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
+    if constexpr (P::A_KC) {
+      const int m = tid / 2, kk = (tid % 2) * 16;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < v.K; k0 += 32) {
-    {
-      float x[8];
-      if constexpr (P::A_KC) {
-        const int m = tid / 4, kk = (tid % 4) * 8;
+      for (int j = 0; j < 16; ++j) split_parts<NS>(ra[j], &As[0][m][kk + j], TM * (KT + 8));
+    } else {
+      const int mm = (tid % 8) * 16, kk = tid / 8;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          x[j] = (m0 + m < v.M && k0 + kk + j < v.K) ? prob.a(v, m0 + m, k0 + kk + j) : 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) split_parts<NS>(x[j], &As[0][m][kk + j], 64 * 40);
-      } else {
-        const int kk = tid / 8, mm = (tid % 8) * 8;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          x[j] = (m0 + mm + j < v.M && k0 + kk < v.K) ? prob.a(v, m0 + mm + j, k0 + kk) : 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) split_parts<NS>(x[j], &As[0][mm + j][kk], 64 * 40);
-      }
+      for (int j = 0; j < 16; ++j) split_parts<NS>(ra[j], &As[0][mm + j][kk], TM * (KT + 8));
     }
-    {
-      float x[8];
-      const int kk = tid / 8, nn = (tid % 8) * 8;
+    const int kk = tid / 8, nn = (tid % 8) * BF;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        x[j] = (n0 + nn + j < v.N && k0 + kk < v.K) ? prob.b(v, k0 + kk, n0 + nn + j) : 0.f;
+    for (int j = 0; j < BF; ++j) split_parts<NS>(rb[j], &Bs[0][nn + j][kk], N * (KT + 8));
+  };
+  // wave w owns rows 32w .. 32w+31 (two row tiles) and every column tile
+  f32x4 acc[2][N / 16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) split_parts<NS>(x[j], &Bs[0][nn + j][kk], 64 * 40);
-    }
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int q = 0; q < N / 16; ++q) acc[r][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load(0);
+  for (int k0 = 0; k0 < v.K; k0 += KT) {
+    stage();
     __syncthreads();
-    u16x8 a[NS];
+    if (k0 + KT < v.K) load(k0 + KT);
+    u16x8 a[2][NS];
 #pragma unroll
-    for (int sp = 0; sp < NS; ++sp) a[sp] = *reinterpret_cast<const u16x8*>(&As[sp][16 * w + col][8 * g]);
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+      for (int sp = 0; sp < NS; ++sp)
+        a[r][sp] = *reinterpret_cast<const u16x8*>(&As[sp][32 * w + 16 * r + col][8 * g]);
+#pragma unroll
+    for (int q = 0; q < N / 16; ++q) {
       u16x8 bb[NS];
 #pragma unroll
       for (int sp = 0; sp < NS; ++sp) bb[sp] = *reinterpret_cast<const u16x8*>(&Bs[sp][16 * q + col][8 * g]);
-      acc[q] = mfma_split<NS, NS>(a, bb, acc[q]);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) acc[r][q] = mfma_split<NS, NS>(a[r], bb, acc[r][q]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 16 * w + 4 * g + i, n = n0 + 16 * q + col;
-      if (m < v.M && n < v.N) prob.c(v, m, n, acc[q][i]);
-    }
+    for (int q = 0; q < N / 16; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 32 * w + 16 * r + 4 * g + i, n = 16 * q + col;
+        if (m < v.M) prob.c(v, m, n, acc[r][q][i]);
+      }
 }
 
 // dnu_I[e] = s sum_{d,c} dT_I[d][c] M[d][c][e]; batch = lp = bh * nseg + t
 struct GemmDnu {
   static constexpr bool A_KC = true;
   Plan pl;
-  int lev, mtiles, ntiles;
+  int lev, mtiles;
   const float* dT;
   const float* Mst;
   float* dnu;
-  struct View { int M, N, K; const float* A; const float* B; float* C; };
+  struct View { int M, K; const float* A; const float* B; float* C; };
   __device__ void view(int batch, View& v) const {
     const int nseg = pl.lev_nseg[lev];
     const int t = batch % nseg, bh = batch / nseg;
@@ -965,14 +985,21 @@ struct GemmDnu {
     const int kvh = (bh / pl.Hq) * pl.Hkv + ((bh % pl.Hq) * pl.Hkv) / pl.Hq;
     const size_t kp = (size_t)kvh * pl.P + p;
     v.M = min(pl.C, gm.qn);
-    v.N = pl.D;
     v.K = pl.D * pl.C;
     v.A = dT + (size_t)batch * pl.C * pl.D * pl.C;
     v.B = Mst + kp * pl.D * pl.C * pl.D;
     v.C = dnu + (size_t)batch * pl.C * pl.D;
   }
-  __device__ float a(const View& v, int m, int k) const { return v.A[(size_t)m * v.K + k]; }
-  __device__ float b(const View& v, int k, int n) const { return v.B[(size_t)k * pl.D + n]; }
+  // A row m, k .. k+15 (K is a multiple of 64)
+  __device__ void a16(const View& v, int m, int k, float* out) const {
+    if (m < v.M && k < v.K) load4x(v.A + (size_t)m * v.K + k, 4, out);
+    else for (int j = 0; j < 16; ++j) out[j] = 0.f;
+  }
+  template <int BF>
+  __device__ void bn(const View& v, int k, int n, float (&out)[BF]) const {
+    if (k < v.K) load4x(v.B + (size_t)k * pl.D + n, BF / 4, out);
+    else for (int j = 0; j < BF; ++j) out[j] = 0.f;
+  }
   __device__ void c(const View& v, int m, int n, float x) const { v.C[(size_t)m * pl.D + n] = pl.scale * x; }
 };
 
@@ -980,11 +1007,11 @@ struct GemmDnu {
 struct GemmDm {
   static constexpr bool A_KC = false;
   Plan pl;
-  int lev, mtiles, ntiles;
+  int lev, mtiles;
   const float* dT;
   const float* nu;   // query centroids [B*Hq][P][C][D]
   float* dM;
-  struct View { int M, N, K, Cq, t, p, bh0; float* C; };
+  struct View { int M, K, Cq, t, p, bh0; float* C; };
   __device__ void view(int batch, View& v) const {
     const int nseg = pl.lev_nseg[lev];
     const int t = batch % nseg, kvh = batch / nseg;
@@ -993,24 +1020,31 @@ struct GemmDm {
     const int Gq = pl.Hq / pl.Hkv;
     v.Cq = min(pl.C, gm.qn);
     v.M = pl.D * pl.C;
-    v.N = pl.D;
     v.K = Gq * pl.C;
     v.t = t;
     v.p = p;
     v.bh0 = (kvh / pl.Hkv) * pl.Hq + (kvh % pl.Hkv) * Gq;
     v.C = dM + (size_t)batch * pl.D * pl.C * pl.D;
   }
-  __device__ float a(const View& v, int m, int k) const {
+  // A rows m .. m+15 of column k = (query head h, query cluster I) (M is a multiple of 64)
+  __device__ void a16(const View& v, int m, int k, float* out) const {
     const int h = k / pl.C, I = k % pl.C;
-    if (I >= v.Cq) return 0.f;
-    const size_t lp = (size_t)(v.bh0 + h) * pl.lev_nseg[lev] + v.t;
-    return dT[(lp * pl.C + I) * (size_t)pl.D * pl.C + m];
+    if (k < v.K && I < v.Cq && m < v.M) {
+      const size_t lp = (size_t)(v.bh0 + h) * pl.lev_nseg[lev] + v.t;
+      load4x(dT + (lp * pl.C + I) * (size_t)pl.D * pl.C + m, 4, out);
+    } else {
+      for (int j = 0; j < 16; ++j) out[j] = 0.f;
+    }
   }
-  __device__ float b(const View& v, int k, int n) const {
+  template <int BF>
+  __device__ void bn(const View& v, int k, int n, float (&out)[BF]) const {
     const int h = k / pl.C, I = k % pl.C;
-    if (I >= v.Cq) return 0.f;
-    const size_t ap = (size_t)(v.bh0 + h) * pl.P + v.p;
-    return nu[(ap * pl.C + I) * pl.D + n];
+    if (k < v.K && I < v.Cq) {
+      const size_t ap = (size_t)(v.bh0 + h) * pl.P + v.p;
+      load4x(nu + (ap * pl.C + I) * pl.D + n, BF / 4, out);
+    } else {
+      for (int j = 0; j < BF; ++j) out[j] = 0.f;
+    }
   }
   __device__ void c(const View& v, int m, int n, float x) const { v.C[(size_t)m * pl.D + n] = pl.scale * x; }
 };
@@ -1241,15 +1275,13 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
     bwd_reduce_k_kernel<<<(unsigned)(pl.B * pl.Hkv * nseg * ((C * D + 255) / 256)), 256, 0, st>>>(A, lev);
     MUSE_KT_POST("bwd_reduce_k", st);
     if (pl.dipole) {
-      GemmDm gdm{pl, lev, (D * C + 63) / 64, (D + 63) / 64, A.dT, A.a.qs.cent, A.dM};
+      GemmDm gdm{pl, lev, (D * C + BG_TM - 1) / BG_TM, A.dT, A.a.qs.cent, A.dM};
       MUSE_KT_PRE(st);
-      bwd_gemm_kernel<GemmDm, NSG>
-          <<<(unsigned)(pl.B * pl.Hkv * nseg * gdm.mtiles * gdm.ntiles), 256, 0, st>>>(gdm);
+      bwd_gemm_kernel<GemmDm, NSG, D><<<(unsigned)(pl.B * pl.Hkv * nseg * gdm.mtiles), 256, 0, st>>>(gdm);
       MUSE_KT_POST("bwd_dM", st);
-      GemmDnu gdn{pl, lev, (C + 63) / 64, (D + 63) / 64, A.dT, A.a.kst.M, A.dnu};
+      GemmDnu gdn{pl, lev, (C + BG_TM - 1) / BG_TM, A.dT, A.a.kst.M, A.dnu};
       MUSE_KT_PRE(st);
-      bwd_gemm_kernel<GemmDnu, NSG>
-          <<<(unsigned)(pl.B * pl.Hq * nseg * gdn.mtiles * gdn.ntiles), 256, 0, st>>>(gdn);
+      bwd_gemm_kernel<GemmDnu, NSG, D><<<(unsigned)(pl.B * pl.Hq * nseg * gdn.mtiles), 256, 0, st>>>(gdn);
       MUSE_KT_POST("bwd_dnu", st);
       MUSE_KT_PRE(st);
       bwd_spread_q_kernel<<<(unsigned)((nq * (D / 4) + 255) / 256), 256, 0, st>>>(A, lev);
