@@ -1123,8 +1123,8 @@ struct alignas(16) BcSmem {
   int32_t sel[4];
 };
 
-template <typename TIn, int D>
-__global__ void __launch_bounds__(256) bwd_bcast_k_kernel(BwdArgs A, int lev) {
+template <typename TIn, int D, int NT>
+__global__ void __launch_bounds__(NT) bwd_bcast_k_kernel(BwdArgs A, int lev) {
   using SM = BcSmem<TIn, D>;
   extern __shared__ __align__(16) unsigned char bc_raw[];
   SM& sm = *reinterpret_cast<SM*>(bc_raw);
@@ -1151,12 +1151,23 @@ __global__ void __launch_bounds__(256) bwd_bcast_k_kernel(BwdArgs A, int lev) {
   const int beg = koffs[c] + sm.sel[1] * 64, cnt = min(koffs[c + 1], beg + 64) - beg;
   const float inv = 1.f / (float)(koffs[c + 1] - koffs[c]);
   const bool dip = pl.dipole != 0;
-  if (dip)
-    for (int idx = tid; idx < D * D; idx += 256) {
-      const int d = idx / D, e = idx % D;
-      sm.dM[d][e] = A.dM[((kl * D + d) * C + c) * D + e];
+  if (dip) {
+    // D x D floats as 16-byte loads, all of a thread's in flight at once
+    constexpr int NL = D * D / 4 / NT;
+    f32x4 mv[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int idx = (u * NT + tid) * 4, d = idx / D, e = idx % D;
+      mv[u] = *reinterpret_cast<const f32x4*>(&A.dM[((kl * D + d) * C + c) * D + e]);
     }
-  for (int e = tid; e < D; e += 256) {
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int idx = (u * NT + tid) * 4, d = idx / D, e = idx % D;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sm.dM[d][e + q] = mv[u][q];
+    }
+  }
+  for (int e = tid; e < D; e += NT) {
     sm.aux[0][e] = A.dS[(kl * C + c) * D + e];
     sm.aux[1][e] = A.dmu[(kl * C + c) * D + e] * inv;
   }
@@ -1165,7 +1176,7 @@ __global__ void __launch_bounds__(256) bwd_bcast_k_kernel(BwdArgs A, int lev) {
   const TIn* Vp = reinterpret_cast<const TIn*>(b.kst.Vp) + rb * D;
   const float* Sc = b.kst.S + (kp * C + c) * D;
   const float* muc = b.kst.mu + (kp * C + c) * D;
-  for (int idx = tid; idx < 64 * (D / 8); idx += 256) {
+  for (int idx = tid; idx < 64 * (D / 8); idx += NT) {
     const int j = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
     float kv[8], vv[8];
     if (j < cnt) {
@@ -1184,18 +1195,21 @@ __global__ void __launch_bounds__(256) bwd_bcast_k_kernel(BwdArgs A, int lev) {
   if (tid < 64) sm.rows[tid] = tid < cnt ? b.ks.perm[rb + tid] : -1;
   __syncthreads();
   // thread -> output dim e, keys j = grp, grp + NG, ...
-  constexpr int NG = 256 / D, NJ = 64 / NG;
+  constexpr int NG = NT / D, NJ = 64 / NG;
   const int e = tid % D, grp = tid / D;
   float gk[NJ], gv[NJ];
 #pragma unroll
   for (int q = 0; q < NJ; ++q) { gk[q] = sm.aux[1][e]; gv[q] = sm.aux[0][e]; }
-  if (dip) {
+  // keys of this thread's group that exist (the rest of the 64 slots are skipped)
+  const int nqv = cnt > grp ? (cnt - grp + NG - 1) / NG : 0;
+  if (dip && nqv > 0) {
     for (int d = 0; d < D; d += 4) {
       float mc[4], mr[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) { mc[u] = sm.dM[d + u][e]; mr[u] = sm.dM[e][d + u]; }
 #pragma unroll
       for (int q = 0; q < NJ; ++q) {
+        if (q >= nqv) break;
         const int j = grp + NG * q;
         const f32x4 vj = *reinterpret_cast<const f32x4*>(&sm.vc[j][d]);
         const f32x4 kj = *reinterpret_cast<const f32x4*>(&sm.kc[j][d]);
@@ -1231,7 +1245,7 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
   set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_LOCAL, 4>, bk_smem);
   set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_EXACT, 4>, bk_smem);
   set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_FAR, 4>, bk_smem);
-  set_smem_once((const void*)bwd_bcast_k_kernel<TIn, D>, bc_smem);
+  set_smem_once((const void*)bwd_bcast_k_kernel<TIn, D, 1024>, bc_smem);
   MUSE_KT_PRE(st);
   bwd_zero_kernel<<<(unsigned)((nq * D / 4 + 255) / 256), 256, 0, st>>>(A.dq, nq * D);
   bwd_zero_kernel<<<(unsigned)((nk * D / 4 + 255) / 256), 256, 0, st>>>(A.dk, nk * D);
@@ -1288,7 +1302,9 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
       MUSE_KT_POST("bwd_spread_q", st);
     }
     MUSE_KT_PRE(st);
-    bwd_bcast_k_kernel<TIn, D><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 256, bc_smem, st>>>(A, lev);
+    // 1024 threads: a workgroup holds a cluster's dM (up to 66 KB) and key
+    // rows in LDS, so one fits per CU; its 16 waves hide each other's LDS latency
+    bwd_bcast_k_kernel<TIn, D, 1024><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 1024, bc_smem, st>>>(A, lev);
     MUSE_KT_POST("bwd_bcast_k", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
