@@ -632,6 +632,9 @@ __device__ __forceinline__ void bk_consume(const BkSmem<TIn, D>& sm,
 }
 
 // Queries rows[qa .. qb) of head bh (rows == nullptr: rows qa .. qb themselves).
+// bf16: software-pipelined.  While tile t is contracted, the Q / dO rows and
+// the lse / Delta of tile t+1 are in flight, and the row indices of tile t+2
+// (so that no load waits on another inside an iteration).
 template <typename TIn, int D, bool CAUSAL, int NT>
 __device__ __forceinline__ void bk_query_range(BkSmem<TIn, D>& sm, const BwdArgs& A, int bh, const int32_t* rows,
                                                int qa, int qb, const u16x8 (&kf)[D / 32][BwdTraits<TIn>::NS],
@@ -640,13 +643,85 @@ __device__ __forceinline__ void bk_query_range(BkSmem<TIn, D>& sm, const BwdArgs
   const Plan& pl = A.pl;
   const TIn* Qh = reinterpret_cast<const TIn*>(A.a.Q) + (size_t)bh * pl.N * D;
   const TIn* dOh = reinterpret_cast<const TIn*>(A.dO) + (size_t)bh * pl.N * D;
+  const float* lse = A.lse + (size_t)bh * pl.N;
+  const float* delta = A.delta + (size_t)bh * pl.N;
+  if constexpr (BkSmem<TIn, D>::NS == 1) {
+    // staging layout: thread -> 4 queries (block qb4) x 8 dims (e0); the first QB
+    // threads also own one query's row index, lse and Delta
+    constexpr int NSTG = (QB / 4) * (D / 8);
+    static_assert(NSTG <= NT && QB <= NT, "one staging item per thread");
+    const int tid = threadIdx.x;
+    const bool stg = tid < NSTG;
+    const int qb4 = tid % (QB / 4), e0 = (tid / (QB / 4)) * 8;
+    const int ntile = (qb - qa + QB - 1) / QB;
+    auto row_at = [&](int q) __attribute__((always_inline)) -> int {
+      return q < qb ? (rows ? rows[q] : q) : -1;
+    };
+    int r1[4], r2[4], s1 = -1, s2r = -1;
+    u16x8 qd[4], od[4];
+    float l1 = 0.f, d1 = 0.f;
+    auto load_rows = [&](int q0, int (&rr)[4], int& sr) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rr[r] = stg ? row_at(q0 + 4 * qb4 + r) : -1;
+      sr = tid < QB ? row_at(q0 + tid) : -1;
+    };
+    auto load_data = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        qd[r] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        od[r] = qd[r];
+        if (r1[r] >= 0) {
+          qd[r] = *reinterpret_cast<const u16x8*>(Qh + (size_t)r1[r] * D + e0);
+          od[r] = *reinterpret_cast<const u16x8*>(dOh + (size_t)r1[r] * D + e0);
+        }
+      }
+      l1 = s1 >= 0 ? lse[s1] * B_LOG2E : 0.f;
+      d1 = s1 >= 0 ? delta[s1] : 0.f;
+    };
+    load_rows(qa, r1, s1);
+    load_data();
+    if (ntile > 1) load_rows(qa + QB, r2, s2r);
+    for (int t = 0; t < ntile; ++t) {
+      // tile t into LDS
+      if (stg) {
+        const int pos = slot_of(4 * qb4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          *reinterpret_cast<u16x8*>(&sm.qs[0][4 * qb4 + r][e0]) = qd[r];
+          *reinterpret_cast<u16x8*>(&sm.os[0][4 * qb4 + r][e0]) = od[r];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          *reinterpret_cast<u16x4*>(&sm.qt[0][e0 + j][pos]) = u16x4{qd[0][j], qd[1][j], qd[2][j], qd[3][j]};
+          *reinterpret_cast<u16x4*>(&sm.ot[0][e0 + j][pos]) = u16x4{od[0][j], od[1][j], od[2][j], od[3][j]};
+        }
+      }
+      if (tid < QB) {
+        sm.qrow[tid] = s1;
+        sm.lse2[tid] = l1;
+        sm.dlt[tid] = d1;
+      }
+      __syncthreads();
+      // tile t+1's rows and scalars, tile t+2's row indices: in flight during the contraction
+      if (t + 1 < ntile) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) r1[r] = r2[r];
+        s1 = s2r;
+        load_data();
+        if (t + 2 < ntile) load_rows(qa + (t + 2) * QB, r2, s2r);
+      }
+      bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
+      __syncthreads();
+    }
+    return;
+  }
   for (int q0 = qa; q0 < qb; q0 += QB) {
     if (threadIdx.x < QB) {
       const int q = q0 + threadIdx.x;
       sm.qrow[threadIdx.x] = q < qb ? (rows ? rows[q] : q) : -1;
     }
     __syncthreads();
-    bk_stage_queries<TIn, D, NT>(sm, Qh, dOh, A.lse + (size_t)bh * pl.N, A.delta + (size_t)bh * pl.N);
+    bk_stage_queries<TIn, D, NT>(sm, Qh, dOh, lse, delta);
     __syncthreads();
     bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
     __syncthreads();
