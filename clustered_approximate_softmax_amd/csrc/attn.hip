@@ -75,8 +75,15 @@ struct AtGeo {
   static constexpr int ST = SB <= 16384 ? 3 : 2;              // stages
 };
 
-// chunk swizzles (chunk position = logical chunk ^ key)
-__device__ __forceinline__ int keyk(int r) { return (r & 3) | ((r >> 1) & 4); }
+// chunk swizzles (chunk position = logical chunk ^ key).  The 16 key rows of
+// one fragment read differ in bits 0, 1, 3 and 4 of r: with 8 chunks a row
+// (128 bytes, rows alternating bank halves) 3 key bits spread them over
+// distinct banks; with 16 or more (256-byte rows, all starting on bank 0)
+// it takes 4.
+template <int CHK>
+__device__ __forceinline__ int keyk(int r) {
+  return CHK >= 16 ? (r & 3) | ((r >> 1) & 12) : (r & 3) | ((r >> 1) & 4);
+}
 __device__ __forceinline__ int keyv(int d) { return d & 7; }
 
 // Everything in LDS but the tile stages, which are a __shared__ array of
@@ -162,7 +169,7 @@ __device__ __forceinline__ void issue_tile(unsigned char* stg, const TileSrc& sr
     const int ci = m * NT + tid;
     const int r = ci / G::CHK, pos = ci % G::CHK;
     const int row = min(c.row0 + r, kcap);
-    const TIn* p = kb + (size_t)row * D + (pos ^ keyk(r)) * G::E;
+    const TIn* p = kb + (size_t)row * D + (pos ^ keyk<G::CHK>(r)) * G::E;
     lds_copy16(p, kst + (m * NT + 64 * w) * 16);
   }
   const TIn* vb = reinterpret_cast<const TIn*>(far ? src.T : src.Vt);
@@ -292,7 +299,7 @@ __device__ __forceinline__ void issue_tile_g(unsigned char* stg, const TileSrc& 
     const int r = ci / G::CHK, pos = ci % G::CHK;
     const int kchunk = (m * NT + 64 * w) / (8 * G::CHK);   // wave-uniform
     const int row = min(pick8(d, kchunk) + (r & 7), kcap);
-    const TIn* p = kb + (size_t)row * D + (pos ^ keyk(r)) * G::E;
+    const TIn* p = kb + (size_t)row * D + (pos ^ keyk<G::CHK>(r)) * G::E;
     lds_copy16(p, kst + (m * NT + 64 * w) * 16);
   }
   const TIn* vb = far ? tt : vt;
@@ -419,7 +426,7 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       u16x8 a[NS];
-      lds_frag<TIn, NS>(kst + r * KROW, 4 * k + g, keyk(r), a);
+      lds_frag<TIn, NS>(kst + r * KROW, 4 * k + g, keyk<G::CHK>(r), a);
 #pragma unroll
       for (int qg = 0; qg < QG; ++qg) sc[qg][rt] = mfma_split<NS, NS>(a, qf[qg][k], sc[qg][rt]);
     }
