@@ -18,9 +18,10 @@
 // depend on scheduling):
 //   bwd_q       query-centric: dq_i over far, retrieved and local items
 //   bwd_kv      item-centric: dk, dv of retrieved keys (gathered over every
-//               query cluster of the query-head group that retrieved them),
-//               of local causal blocks, and dT / mu-gradient partials of the
-//               far items of each query cluster
+//               query cluster of the query-head group that retrieved them)
+//               and of local causal blocks
+//   bwd_far     dT / mu-gradient partials of the far items, one workgroup
+//               per block of clusters looping over several query clusters
 //   reduce_k    dS_c = sum_I dT_Ic, dmu_c (far logits) per key cluster
 //   gemm dM     dM_c = s sum_I dT_Ic nu_I^T         (split-bf16 MFMA)
 //   gemm dnu    dnu_I = s sum_c M_c^T dT_Ic          (split-bf16 MFMA)
@@ -498,7 +499,7 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_q_kernel(BwdArgs A, int lev) {
 // the queries that see them in tiles of QB.  S = Q K^T, dP = dO V^T (queries
 // as rows), dS = P (dP - Delta), dV^T += dO^T P, dK^T += Q^T dS.
 // ===========================================================================
-enum { BK_EXACT = 0, BK_FAR = 1, BK_LOCAL = 2 };
+enum { BK_EXACT = 0, BK_LOCAL = 2 };   // far items have a kernel of their own
 
 template <typename TIn, int D>
 struct alignas(16) BkSmem {
@@ -741,8 +742,8 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
   const float s = pl.scale, s2 = pl.scale * B_LOG2E;
   const int C = pl.C, Gq = pl.Hq / pl.Hkv;
-  int bq = 0, kvh = 0, p = 0, t = 0, nseg = 1, kp = 0, Ck = 0, c = 0, ibeg = 0, iend = 0, ap = 0, I = 0;
-  int bh = 0, blk1 = 0;
+  int bq = 0, kvh = 0, p = 0, t = 0, nseg = 1, kp = 0, Ck = 0, c = 0, ibeg = 0, iend = 0;
+  int blk1 = 0;
   Geom gm{};
   if (KIND == BK_LOCAL) {
     const int nblk = (pl.N + pl.blk - 1) / pl.blk, tpb = (pl.blk + IT - 1) / IT;
@@ -776,24 +777,6 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
     c = sm.sel[0];
     ibeg = koffs[c] + sm.sel[1] * IT;
     iend = min(koffs[c + 1], ibeg + IT);
-  } else {  // BK_FAR: items are the key clusters ct*64 .. ct*64+63 seen from query cluster I
-    nseg = pl.lev_nseg[lev];
-    const int nct = (C + 63) / 64;
-    int id = blockIdx.x;
-    const int ct = id % nct; id /= nct;
-    I = id % C; id /= C;
-    t = id % nseg;
-    bh = id / nseg;
-    bq = bh / pl.Hq;
-    kvh = bq * pl.Hkv + ((bh % pl.Hq) * pl.Hkv) / pl.Hq;
-    p = pl.lev_pfirst[lev] + t;
-    ap = bh * pl.P + p;
-    kp = kvh * pl.P + p;
-    gm = prob_geom(pl, p);
-    Ck = min(C, gm.kn);
-    if (I >= min(C, gm.qn)) return;
-    ibeg = ct * IT;
-    iend = min(C, ibeg + IT);
   }
 
   // ---- this lane's item (wave w owns items 16w .. 16w+15) ----
@@ -820,36 +803,13 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
         irow = b.ks.perm[((size_t)lev * pl.B * pl.Hkv + kvh) * pl.N + gm.k0 + item];
         ibias = 0.f;
       }
-    } else if (ivalid && item < Ck) {
-      const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
-      const int nc = koffs[item + 1] - koffs[item];
-      bool ret = false;
-      const int32_t* Rr = b.R + ((size_t)ap * C + I) * pl.k1w;
-      for (int r = 0; r < pl.k1w; ++r) ret |= (Rr[r] == item);
-      if (nc > 0 && !ret) ibias = __log2f((float)nc);
-      kp_ = reinterpret_cast<const TIn*>(b.kst.mu_in) + ((size_t)kp * C + item) * D;
     }
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       if (kp_) load8_split<TIn, NS>(kp_ + 32 * k + 8 * g, kf[k]);
       else zero8<NS>(kf[k]);
-      if (KIND == BK_FAR) {
-        // value of a far item: column `item` of T_I / n_c, stored (d, c)
-        const TIn* T = reinterpret_cast<const TIn*>(b.T) + ((size_t)ap * C + I) * D * b.Cp32;
-        float v8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          v8[j] = kp_ ? load1_f32<TIn>(T + (size_t)(32 * k + 8 * g + j) * b.Cp32 + item) : 0.f;
-        if constexpr (NS == 1) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) vf[k][0][j] = f2bf(v8[j]);
-        } else {
-          pack8<NS>(v8, vf[k]);
-        }
-      } else {
-        if (vp_) load8_split<TIn, NS>(vp_ + 32 * k + 8 * g, vf[k]);
-        else zero8<NS>(vf[k]);
-      }
+      if (vp_) load8_split<TIn, NS>(vp_ + 32 * k + 8 * g, vf[k]);
+      else zero8<NS>(vf[k]);
     }
   }
   f32x4 dvt[DT], dkt[DT];
@@ -896,11 +856,6 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
       }
       __syncthreads();
     }
-  } else if (KIND == BK_FAR) {
-    const int32_t* qoffs = b.qs.offs + (size_t)ap * (C + 1);
-    const int32_t* qperm = b.qs.perm + ((size_t)lev * pl.B * pl.Hq + bh) * pl.N + gm.q0;
-    bk_query_range<TIn, D, false, NT>(sm, A, bh, qperm, qoffs[I], qoffs[I + 1], kf, vf, ibias, -1, s2, dvt,
-                                      dkt);
   } else {
     // local causal block: the queries from the tile's first row to the block end, every head of the group
     for (int hl = 0; hl < Gq; ++hl) {
@@ -910,23 +865,7 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
   }
   if (!ivalid) return;
   // ---- outputs: lane holds dims d = 16dt + 4g + i of its item ----
-  if (KIND == BK_FAR) {
-    float inv = 0.f;
-    if (item < Ck) {
-      const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
-      const int nc = koffs[item + 1] - koffs[item];
-      inv = nc > 0 ? 1.f / (float)nc : 0.f;
-    }
-    const size_t lp = (size_t)bh * nseg + t;
-    float* dT = A.dT + (lp * C + I) * (size_t)D * C;          // (d, c)
-    float* G = A.G + ((lp * C + I) * C + item) * (size_t)D;    // (c, e)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dT[(size_t)(16 * dt + 4 * g + i) * C + item] = dvt[dt][i] * inv;
-      *reinterpret_cast<f32x4*>(G + 16 * dt + 4 * g) = dkt[dt] * s;
-    }
-  } else {
+  {
     float* dk = A.dk + ((size_t)kvh * pl.N + irow) * D;
     float* dv = A.dv + ((size_t)kvh * pl.N + irow) * D;
 #pragma unroll
@@ -935,6 +874,110 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
       const f32x4 pv = *reinterpret_cast<const f32x4*>(dv + 16 * dt + 4 * g);
       *reinterpret_cast<f32x4*>(dk + 16 * dt + 4 * g) = pk + dkt[dt] * s;
       *reinterpret_cast<f32x4*>(dv + 16 * dt + 4 * g) = pv + dvt[dt];
+    }
+  }
+}
+
+// Far items: key clusters cb*IT .. cb*IT+IT-1 (row mu_c, value T_Ic / n_c,
+// log-weight log n_c, none for retrieved or empty clusters) seen from the
+// query clusters I0 .. I0+ig-1 of one (query head, segment).  The clusters'
+// centroid rows are loaded once; per query cluster the retrieval bias and
+// the value column change, and the cluster's queries stream through LDS.
+// Writes dT_Ic (d, c) and G_Ic = s sum_i dl_ic q_i (c, e).
+template <typename TIn, int D, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, sizeof(TIn) == 2 ? 2 : 1) bwd_far_kernel(BwdArgs A, int lev, int ig) {
+  using SM = BkSmem<TIn, D>;
+  constexpr int NS = SM::NS, KS = D / 32, DT = D / 16;
+  constexpr int NT = 64 * WAVES, IT = 16 * WAVES;
+  extern __shared__ __align__(16) unsigned char bf_raw[];
+  SM& sm = *reinterpret_cast<SM*>(bf_raw);
+  // value columns of the block for one query cluster (bf16), item-major
+  __shared__ __align__(16) uint16_t tcol[NS == 1 ? IT : 1][D + 8];
+  const Plan& pl = A.pl;
+  const AttnBufs& b = A.a;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
+  const float s = pl.scale, s2 = pl.scale * B_LOG2E;
+  const int C = pl.C, nseg = pl.lev_nseg[lev];
+  const int nct = (C + IT - 1) / IT, nib = (C + ig - 1) / ig;
+  int id = blockIdx.x;
+  const int cb = id % nct; id /= nct;
+  const int ib = id % nib; id /= nib;
+  const int t = id % nseg, bh = id / nseg;
+  const int bq = bh / pl.Hq;
+  const int kvh = bq * pl.Hkv + ((bh % pl.Hq) * pl.Hkv) / pl.Hq;
+  const int p = pl.lev_pfirst[lev] + t;
+  const size_t ap = (size_t)bh * pl.P + p, kp = (size_t)kvh * pl.P + p;
+  const Geom gm = prob_geom(pl, p);
+  const int Ck = min(C, gm.kn), Cq = min(C, gm.qn);
+  const int I0 = ib * ig, I1 = min(Cq, I0 + ig);
+  if (I0 >= I1) return;
+  // this lane's item (wave w owns items 16w .. 16w+15 of the block)
+  const int item = cb * IT + 16 * w + col;
+  const bool ivalid = item < C;
+  const bool real = item < Ck;
+  const int32_t* koffs = b.ks.offs + kp * (C + 1);
+  const int nc = real ? koffs[item + 1] - koffs[item] : 0;
+  const float inv = nc > 0 ? 1.f / (float)nc : 0.f;
+  const float lw = nc > 0 ? __log2f((float)nc) : -INFINITY;
+  u16x8 kf[KS][NS], vf[KS][NS];
+  {
+    const TIn* kr = reinterpret_cast<const TIn*>(b.kst.mu_in) + (kp * C + item) * D;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      if (real) load8_split<TIn, NS>(kr + 32 * k + 8 * g, kf[k]);
+      else zero8<NS>(kf[k]);
+    }
+  }
+  const int32_t* qoffs = b.qs.offs + ap * (C + 1);
+  const int32_t* qperm = b.qs.perm + ((size_t)lev * pl.B * pl.Hq + bh) * pl.N + gm.q0;
+  const size_t lp = (size_t)bh * nseg + t;
+#pragma nounroll
+  for (int I = I0; I < I1; ++I) {
+    // retrieved clusters leave the far field of I
+    bool ret = false;
+    const int32_t* Rr = b.R + (ap * C + I) * pl.k1w;
+    for (int r = 0; r < pl.k1w; ++r) ret |= (Rr[r] == item);
+    const float ibias = ret ? -INFINITY : lw;
+    // value: column `item` of T_I / n_c, stored (d, c)
+    const TIn* T = reinterpret_cast<const TIn*>(b.T) + (ap * C + I) * D * b.Cp32;
+    if constexpr (NS == 1) {
+      // the block's D x IT values: 16-byte row loads, transposed into LDS
+      // (item rows), then 16-byte fragment reads (columns C .. Cp-1 of T are zero)
+      const uint16_t* T16 = reinterpret_cast<const uint16_t*>(T) + cb * IT;
+      for (int idx = threadIdx.x; idx < D * (IT / 8); idx += NT) {
+        const int d = idx / (IT / 8), i0 = (idx % (IT / 8)) * 8;
+        const u16x8 v = *reinterpret_cast<const u16x8*>(T16 + (size_t)d * b.Cp32 + i0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) tcol[i0 + q][d] = v[q];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < KS; ++k) vf[k][0] = *reinterpret_cast<const u16x8*>(&tcol[16 * w + col][32 * k + 8 * g]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        float v8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v8[j] = real ? load1_f32<TIn>(T + (size_t)(32 * k + 8 * g + j) * b.Cp32 + item) : 0.f;
+        pack8<NS>(v8, vf[k]);
+      }
+    }
+    f32x4 dvt[DT], dkt[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      dvt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dkt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    bk_query_range<TIn, D, false, NT>(sm, A, bh, qperm, qoffs[I], qoffs[I + 1], kf, vf, ibias, -1, s2, dvt, dkt);
+    if (ivalid) {
+      float* dT = A.dT + (lp * C + I) * (size_t)D * C;          // (d, c)
+      float* G = A.G + ((lp * C + I) * C + item) * (size_t)D;    // (c, e)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dT[(size_t)(16 * dt + 4 * g + i) * C + item] = dvt[dt][i] * inv;
+        *reinterpret_cast<f32x4*>(G + 16 * dt + 4 * g) = dkt[dt] * s;
+      }
     }
   }
 }
@@ -1319,7 +1362,7 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
   set_smem_once((const void*)bwd_q_kernel<TIn, D, BQ_PROBLEM, 4>, bq_smem);
   set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_LOCAL, 4>, bk_smem);
   set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_EXACT, 4>, bk_smem);
-  set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_FAR, 4>, bk_smem);
+  set_smem_once((const void*)bwd_far_kernel<TIn, D, 4>, bk_smem);
   set_smem_once((const void*)bwd_bcast_k_kernel<TIn, D, 1024>, bc_smem);
   MUSE_KT_PRE(st);
   bwd_zero_kernel<<<(unsigned)((nq * D / 4 + 255) / 256), 256, 0, st>>>(A.dq, nq * D);
@@ -1356,8 +1399,13 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
     bwd_kv_kernel<TIn, D, BK_EXACT, 4><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 256, bk_smem, st>>>(A, lev);
     MUSE_KT_POST(kn[lev < 7 ? lev : 7], st);
     MUSE_KT_PRE(st);
-    bwd_kv_kernel<TIn, D, BK_FAR, 4>
-        <<<(unsigned)(pl.B * pl.Hq * nseg * C * ((C + 63) / 64)), 256, bk_smem, st>>>(A, lev);
+    {
+      // query clusters per workgroup: enough workgroups (about 4096) to fill the chip
+      const long long pairs = (long long)pl.B * pl.Hq * nseg * ((C + 63) / 64) * C;
+      const int ig = (int)std::min<long long>(C, std::max<long long>(1, pairs / 4096));
+      bwd_far_kernel<TIn, D, 4><<<(unsigned)(pl.B * pl.Hq * nseg * ((C + 63) / 64) * ((C + ig - 1) / ig)), 256,
+                                  bk_smem, st>>>(A, lev, ig);
+    }
     MUSE_KT_POST("bwd_far", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     MUSE_KT_PRE(st);

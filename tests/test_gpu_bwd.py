@@ -98,6 +98,12 @@ def test_causal_ragged_tiny_blocks_f32():
     run_bwd(1, 1, 1, 333, 64, "f32", 12, 2, 1, causal=True, block=20, seed=9)
 
 
+def test_causal_many_problems_far_groups():
+    # enough (head, segment, query cluster) triples that a far-item workgroup
+    # loops over several query clusters at the lowest levels
+    run_bwd(1, 16, 4, 2048, 64, "bf16", 16, 2, 3, causal=True, block=32, seed=23)
+
+
 def test_causal_block_covers_sequence():
     run_bwd(1, 2, 2, 200, 64, "bf16", 8, 2, 1, causal=True, block=256, seed=10)
 
