@@ -22,8 +22,10 @@
 //               and of local causal blocks
 //   bwd_far     dT / mu-gradient partials of the far items, one workgroup
 //               per block of clusters looping over several query clusters
-//   reduce_k    dS_c = sum_I dT_Ic, dmu_c (far logits) per key cluster
-//   gemm dM     dM_c = s sum_I dT_Ic nu_I^T         (split-bf16 MFMA)
+//   reduce_k    dmu_c (far logits) per key cluster from the far pass's
+//               per-block partials (and dS_c without the dipole term)
+//   gemm dM     dM_c = s sum_I dT_Ic nu_I^T         (split-bf16 MFMA),
+//               and dS_c = sum_I dT_Ic from the same pass over dT
 //   gemm dnu    dnu_I = s sum_c M_c^T dT_Ic          (split-bf16 MFMA)
 //   spread_q    dq_i += dnu_I / m_I
 //   bcast_k     dk_j += dM_c^T (v_j - S_c/n_c) + dmu_c / n_c,
@@ -122,7 +124,7 @@ struct BwdArgs {
   float* dv;
   // per-level buffers; lp = bh * nseg + t, kl = kvh * nseg + t
   float* dT;      // [lp][C][D][C]   (I, d, c): sum_i p dO_i / n_c over far items
-  float* G;       // [lp][C][C][D]   (I, c, e): s sum_i dl q_i over far items
+  float* G;       // [lp][nib][C][D] (block of query clusters, c, e): s sum_{I in block} sum_i dl q_i over far items
   float* dnu;     // [lp][C][D]
   float* dS;      // [kl][C][D]
   float* dmu;     // [kl][C][D]
@@ -883,7 +885,9 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
 // query clusters I0 .. I0+ig-1 of one (query head, segment).  The clusters'
 // centroid rows are loaded once; per query cluster the retrieval bias and
 // the value column change, and the cluster's queries stream through LDS.
-// Writes dT_Ic (d, c) and G_Ic = s sum_i dl_ic q_i (c, e).
+// Writes dT_Ic (d, c) per query cluster and, for the whole block of query
+// clusters, G = s sum_I sum_{i in I} dl_ic q_i (c, e): the mu-gradient is only
+// ever needed summed over query clusters.
 template <typename TIn, int D, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES, sizeof(TIn) == 2 ? 2 : 1) bwd_far_kernel(BwdArgs A, int lev, int ig) {
   using SM = BkSmem<TIn, D>;
@@ -931,6 +935,9 @@ __global__ void __launch_bounds__(64 * WAVES, sizeof(TIn) == 2 ? 2 : 1) bwd_far_
   const int32_t* qoffs = b.qs.offs + ap * (C + 1);
   const int32_t* qperm = b.qs.perm + ((size_t)lev * pl.B * pl.Hq + bh) * pl.N + gm.q0;
   const size_t lp = (size_t)bh * nseg + t;
+  f32x4 dvt[DT], dkt[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dkt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma nounroll
   for (int I = I0; I < I1; ++I) {
     // retrieved clusters leave the far field of I
@@ -962,23 +969,21 @@ __global__ void __launch_bounds__(64 * WAVES, sizeof(TIn) == 2 ? 2 : 1) bwd_far_
         pack8<NS>(v8, vf[k]);
       }
     }
-    f32x4 dvt[DT], dkt[DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      dvt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dkt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int dt = 0; dt < DT; ++dt) dvt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     bk_query_range<TIn, D, false, NT>(sm, A, bh, qperm, qoffs[I], qoffs[I + 1], kf, vf, ibias, -1, s2, dvt, dkt);
     if (ivalid) {
       float* dT = A.dT + (lp * C + I) * (size_t)D * C;          // (d, c)
-      float* G = A.G + ((lp * C + I) * C + item) * (size_t)D;    // (c, e)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) dT[(size_t)(16 * dt + 4 * g + i) * C + item] = dvt[dt][i] * inv;
-        *reinterpret_cast<f32x4*>(G + 16 * dt + 4 * g) = dkt[dt] * s;
-      }
     }
+  }
+  if (ivalid) {
+    float* G = A.G + ((lp * nib + ib) * C + item) * (size_t)D;    // (c, e)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(G + 16 * dt + 4 * g) = dkt[dt] * s;
   }
 }
 
@@ -1054,8 +1059,16 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(P prob) {
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int q = 0; q < N / 16; ++q) acc[r][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // row sums of A (problems with ROWSUM): this thread's 16 rows over its k
+  float rsum[P::ROWSUM ? 16 : 1];
+#pragma unroll
+  for (int j = 0; j < (P::ROWSUM ? 16 : 1); ++j) rsum[j] = 0.f;
   load(0);
   for (int k0 = 0; k0 < v.K; k0 += KT) {
+    if constexpr (P::ROWSUM) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) rsum[j] += ra[j];
+    }
     stage();
     __syncthreads();
     if (k0 + KT < v.K) load(k0 + KT);
@@ -1084,11 +1097,25 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(P prob) {
         const int m = m0 + 32 * w + 16 * r + 4 * g + i, n = 16 * q + col;
         if (m < v.M) prob.c(v, m, n, acc[r][q][i]);
       }
+  if constexpr (P::ROWSUM) {
+    // the 32 threads of a row range (k = tid / 8 mod 32) combine through LDS
+    static_assert(!P::A_KC && 32 * TM * 4 <= (int)sizeof(As), "row sums reuse the A stage");
+    float* red = reinterpret_cast<float*>(&As[0][0][0]);
+    const int mm = (tid % 8) * 16, kq = tid / 8;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) red[kq * TM + mm + j] = rsum[j];
+    __syncthreads();
+    if (tid < TM && m0 + tid < v.M) {
+      float sum = 0.f;
+      for (int q = 0; q < 32; ++q) sum += red[q * TM + tid];
+      prob.rowsum(v, m0 + tid, sum);
+    }
+  }
 }
 
 // dnu_I[e] = s sum_{d,c} dT_I[d][c] M[d][c][e]; batch = lp = bh * nseg + t
 struct GemmDnu {
-  static constexpr bool A_KC = true;
+  static constexpr bool A_KC = true, ROWSUM = false;
   Plan pl;
   int lev, mtiles;
   const float* dT;
@@ -1123,13 +1150,15 @@ struct GemmDnu {
 
 // dM[d][c][e] = s sum_{h,I} dT_{h,I}[d][c] nu_{h,I}[e]; batch = kl = kvh * nseg + t
 struct GemmDm {
-  static constexpr bool A_KC = false;
+  // also the row sums of dT over (h, I): dS_c[d] for m = (d, c)
+  static constexpr bool A_KC = false, ROWSUM = true;
   Plan pl;
   int lev, mtiles;
   const float* dT;
   const float* nu;   // query centroids [B*Hq][P][C][D]
   float* dM;
-  struct View { int M, K, Cq, t, p, bh0; float* C; };
+  float* dS;         // [kl][C][D]
+  struct View { int M, K, Cq, t, p, bh0, kl; float* C; };
   __device__ void view(int batch, View& v) const {
     const int nseg = pl.lev_nseg[lev];
     const int t = batch % nseg, kvh = batch / nseg;
@@ -1142,6 +1171,7 @@ struct GemmDm {
     v.t = t;
     v.p = p;
     v.bh0 = (kvh / pl.Hkv) * pl.Hq + (kvh % pl.Hkv) * Gq;
+    v.kl = batch;
     v.C = dM + (size_t)batch * pl.D * pl.C * pl.D;
   }
   // A rows m .. m+15 of column k = (query head h, query cluster I) (M is a multiple of 64)
@@ -1165,13 +1195,18 @@ struct GemmDm {
     }
   }
   __device__ void c(const View& v, int m, int n, float x) const { v.C[(size_t)m * pl.D + n] = pl.scale * x; }
+  __device__ void rowsum(const View& v, int m, float x) const {
+    const int d = m / pl.C, c = m % pl.C;
+    dS[((size_t)v.kl * pl.C + c) * pl.D + d] = x;
+  }
 };
 
 // ===========================================================================
-// dS_c[d] = sum_{h,I} dT_{h,I}[d][c] ; dmu_c[e] = sum_{h,I} G_{h,I}[c][e]
+// dmu_c[e] = sum_{h, blocks} G[c][e] and, when no dM contraction runs (no
+// dipole term), dS_c[d] = sum_{h,I} dT_{h,I}[d][c]
 // one thread per (kl, index in C*D)
 // ===========================================================================
-__global__ void __launch_bounds__(256) bwd_reduce_k_kernel(BwdArgs A, int lev) {
+__global__ void __launch_bounds__(256) bwd_reduce_k_kernel(BwdArgs A, int lev, int ig, int with_ds) {
   const Plan& pl = A.pl;
   const int C = pl.C, D = pl.D, Gq = pl.Hq / pl.Hkv;
   const int nseg = pl.lev_nseg[lev];
@@ -1184,16 +1219,17 @@ __global__ void __launch_bounds__(256) bwd_reduce_k_kernel(BwdArgs A, int lev) {
   const Geom gm = prob_geom(pl, p);
   const int Cq = min(C, gm.qn);
   const int bh0 = (kvh / pl.Hkv) * pl.Hq + (kvh % pl.Hkv) * Gq;
+  // G holds one partial per block of ig query clusters (blocks that exist)
+  const int nib = (C + ig - 1) / ig, nibq = (Cq + ig - 1) / ig;
   float sS = 0.f, sMu = 0.f;
   for (int h = 0; h < Gq; ++h) {
     const size_t lp = (size_t)(bh0 + h) * nseg + t;
-    for (int I = 0; I < Cq; ++I) {
-      sS += A.dT[(lp * C + I) * (size_t)D * C + idx];
-      sMu += A.G[(lp * C + I) * (size_t)C * D + idx];
-    }
+    if (with_ds)
+      for (int I = 0; I < Cq; ++I) sS += A.dT[(lp * C + I) * (size_t)D * C + idx];
+    for (int q = 0; q < nibq; ++q) sMu += A.G[(lp * nib + q) * (size_t)C * D + idx];
   }
   const int d = idx / C, c = idx % C;   // the dT index is (d, c)
-  A.dS[((size_t)kl * C + c) * D + d] = sS;
+  if (with_ds) A.dS[((size_t)kl * C + c) * D + d] = sS;
   A.dmu[(size_t)kl * C * D + idx] = sMu;
 }
 
@@ -1399,20 +1435,20 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
     bwd_kv_kernel<TIn, D, BK_EXACT, 4><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 256, bk_smem, st>>>(A, lev);
     MUSE_KT_POST(kn[lev < 7 ? lev : 7], st);
     MUSE_KT_PRE(st);
-    {
-      // query clusters per workgroup: enough workgroups (about 4096) to fill the chip
-      const long long pairs = (long long)pl.B * pl.Hq * nseg * ((C + 63) / 64) * C;
-      const int ig = (int)std::min<long long>(C, std::max<long long>(1, pairs / 4096));
-      bwd_far_kernel<TIn, D, 4><<<(unsigned)(pl.B * pl.Hq * nseg * ((C + 63) / 64) * ((C + ig - 1) / ig)), 256,
-                                  bk_smem, st>>>(A, lev, ig);
-    }
+    // query clusters per far workgroup: enough workgroups (about 4096) to fill the chip
+    const long long pairs = (long long)pl.B * pl.Hq * nseg * ((C + 63) / 64) * C;
+    const int ig = (int)std::min<long long>(C, std::max<long long>(1, pairs / 4096));
+    bwd_far_kernel<TIn, D, 4><<<(unsigned)(pl.B * pl.Hq * nseg * ((C + 63) / 64) * ((C + ig - 1) / ig)), 256,
+                                bk_smem, st>>>(A, lev, ig);
     MUSE_KT_POST("bwd_far", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     MUSE_KT_PRE(st);
-    bwd_reduce_k_kernel<<<(unsigned)(pl.B * pl.Hkv * nseg * ((C * D + 255) / 256)), 256, 0, st>>>(A, lev);
+    // dS_c comes from the dM contraction when there is one (it reads every dT anyway)
+    bwd_reduce_k_kernel<<<(unsigned)(pl.B * pl.Hkv * nseg * ((C * D + 255) / 256)), 256, 0, st>>>(A, lev, ig,
+                                                                                                  pl.dipole ? 0 : 1);
     MUSE_KT_POST("bwd_reduce_k", st);
     if (pl.dipole) {
-      GemmDm gdm{pl, lev, (D * C + BG_TM - 1) / BG_TM, A.dT, A.a.qs.cent, A.dM};
+      GemmDm gdm{pl, lev, (D * C + BG_TM - 1) / BG_TM, A.dT, A.a.qs.cent, A.dM, A.dS};
       MUSE_KT_PRE(st);
       bwd_gemm_kernel<GemmDm, NSG, D><<<(unsigned)(pl.B * pl.Hkv * nseg * gdm.mtiles), 256, 0, st>>>(gdm);
       MUSE_KT_POST("bwd_dM", st);
