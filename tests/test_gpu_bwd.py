@@ -104,6 +104,13 @@ def test_causal_many_problems_far_groups():
     run_bwd(1, 16, 4, 2048, 64, "bf16", 16, 2, 3, causal=True, block=32, seed=23)
 
 
+def test_many_pairs_per_key_cluster():
+    # every key cluster is retrieved by all 8 x 128 (query head, query cluster)
+    # pairs, more than one query stream of the item-centric kernel holds, and the
+    # 8-key clusters take one-wave workgroups
+    run_bwd(1, 8, 1, 1024, 64, "bf16", 128, 2, 128, seed=24)
+
+
 def test_causal_block_covers_sequence():
     run_bwd(1, 2, 2, 200, 64, "bf16", 8, 2, 1, causal=True, block=256, seed=10)
 
