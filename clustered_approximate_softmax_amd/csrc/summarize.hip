@@ -4,36 +4,64 @@
 // M_c = sum_j v_j (k_j - mu_c)^T = sum_j v_j k_j^T - S_c mu_c^T.
 //
 // One workgroup per (key problem, cluster).  The cluster's rows are read
-// through the permutation (cluster-contiguous order) in tiles of 32 keys,
-// staged transposed in LDS, and sum_j v_j k_j^T is a 32-key MFMA
-// contraction per tile (exact products of bf16 inputs, fp32 accumulation,
-// fixed order: no atomics).
+// through the permutation (cluster-contiguous order) in tiles of KT keys,
+// staged transposed in LDS, and sum_j v_j k_j^T is an MFMA contraction over
+// the tile's keys (exact products of bf16 inputs, fp32 accumulation, fixed
+// order: no atomics).  The rows of tile t+1 are in flight while tile t is
+// contracted, and the permutation entries of tile t+2, so that a large
+// cluster's tiles do not each wait for two dependent loads.
 #include "common.h"
 #include "launch.h"
 
 namespace muse {
 
 constexpr int SU_NT = 256;
-constexpr int SU_KT = 32;
-constexpr int SU_KP = SU_KT + 8;
 
 template <typename TIn, int D>
 struct alignas(16) SuSmem {
   static constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
-  uint16_t kt[NS][D][SU_KP];
-  uint16_t vt[NS][D][SU_KP];
-  int32_t rows[SU_KT];
+  static constexpr int KT = sizeof(TIn) == 2 && D == 64 ? 64 : 32;   // keys per tile (registers at D = 128)
+  static constexpr int KP = KT + 8;
+  uint16_t kt[NS][D][KP];
+  uint16_t vt[NS][D][KP];
   float red[SU_NT / (D / 8)][2][D];   // [key slot][k sum | v sum][dim]
 };
 
+// 8 consecutive input elements held as loaded (bf16: one 16-byte vector)
+template <typename TIn>
+struct Raw8 {
+  static constexpr int W = sizeof(TIn) == 2 ? 1 : 2;
+  typedef typename std::conditional<sizeof(TIn) == 2, u16x8, f32x4>::type V;
+  V v[W];
+  __device__ __forceinline__ void load(const TIn* p) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) v[i] = *reinterpret_cast<const V*>(p + i * (8 / W));
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < W; ++i) v[i] = V{};
+  }
+  __device__ __forceinline__ void store(TIn* p) const {
+#pragma unroll
+    for (int i = 0; i < W; ++i) *reinterpret_cast<V*>(p + i * (8 / W)) = v[i];
+  }
+  __device__ __forceinline__ float at(int j) const {
+    if constexpr (sizeof(TIn) == 2) return bf2f(v[0][j]);
+    else return v[j / 4][j % 4];
+  }
+};
+
 template <typename TIn, int D>
-__global__ void __launch_bounds__(SU_NT) summarize_kernel(Plan pl, CSet ks, const void* Vv, KStats out) {
-  constexpr int NS = SuSmem<TIn, D>::NS;
+__global__ void __launch_bounds__(SU_NT, 2) summarize_kernel(Plan pl, CSet ks, const void* Vv, KStats out) {
+  using SM = SuSmem<TIn, D>;
+  constexpr int NS = SM::NS, KT = SM::KT;
   constexpr int DT = D / 16;
   constexpr int U = DT * DT / 4;
   constexpr int TPK = D / 8;          // threads per key row
   constexpr int KPP = SU_NT / TPK;    // keys per load pass
-  __shared__ SuSmem<TIn, D> sm;
+  constexpr int NP = KT / KPP;        // passes per tile
+  static_assert(KT % KPP == 0 && KT % 32 == 0, "tile shape");
+  __shared__ SM sm;
   const int C = pl.C;
   const int c = blockIdx.x % C;
   const int hp = blockIdx.x / C;      // head * P + p
@@ -62,7 +90,7 @@ __global__ void __launch_bounds__(SU_NT) summarize_kernel(Plan pl, CSet ks, cons
     }
     return;
   }
-  const int32_t* perm = ks.perm + ((size_t)lev * ks.heads + head) * pl.N + r0;
+  const int32_t* perm = ks.perm + ((size_t)lev * ks.heads + head) * pl.N + r0 + beg;
   const TIn* K = reinterpret_cast<const TIn*>(ks.X) + (size_t)head * pl.N * D;
   const TIn* V = reinterpret_cast<const TIn*>(Vv) + (size_t)head * pl.N * D;
   // cluster-contiguous copies: sorted position q of the problem -> row r0 + q
@@ -76,65 +104,77 @@ __global__ void __launch_bounds__(SU_NT) summarize_kernel(Plan pl, CSet ks, cons
   float sk[8], sv[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) { sk[j] = 0.f; sv[j] = 0.f; }
-  const int e0 = (tid % TPK) * 8;
+  const int e0 = (tid % TPK) * 8, ks0 = tid / TPK;   // dims e0..e0+7 of keys ks0 + KPP * pass
 
-  for (int t0 = 0; t0 < cnt; t0 += SU_KT) {
-    if (tid < SU_KT) sm.rows[tid] = (t0 + tid < cnt) ? perm[beg + t0 + tid] : -1;
-    __syncthreads();
+  int rn[NP];            // rows of the next tile
+  Raw8<TIn> kd[NP], vd[NP];
+  auto rows_of = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int pass = 0; pass < SU_KT / KPP; ++pass) {
-      const int key = pass * KPP + tid / TPK;
-      const int row = sm.rows[key];
-      float kv[8], vv[8];
-      if (row >= 0) {
-        load8_f32<TIn>(K + (size_t)row * D + e0, kv);
-        load8_f32<TIn>(V + (size_t)row * D + e0, vv);
-        if (Kp) {
-          TIn* kd = Kp + (size_t)(t0 + key) * D + e0;
-          TIn* vd = Vp + (size_t)(t0 + key) * D + e0;
-          if constexpr (sizeof(TIn) == 2) {
-            *reinterpret_cast<u16x8*>(kd) = *reinterpret_cast<const u16x8*>(K + (size_t)row * D + e0);
-            *reinterpret_cast<u16x8*>(vd) = *reinterpret_cast<const u16x8*>(V + (size_t)row * D + e0);
-          } else {
-            *reinterpret_cast<f32x4*>(kd) = f32x4{kv[0], kv[1], kv[2], kv[3]};
-            *reinterpret_cast<f32x4*>(kd + 4) = f32x4{kv[4], kv[5], kv[6], kv[7]};
-            *reinterpret_cast<f32x4*>(vd) = f32x4{vv[0], vv[1], vv[2], vv[3]};
-            *reinterpret_cast<f32x4*>(vd + 4) = f32x4{vv[4], vv[5], vv[6], vv[7]};
-          }
-        }
+    for (int q = 0; q < NP; ++q) {
+      const int key = t0 + q * KPP + ks0;
+      rn[q] = key < cnt ? perm[key] : -1;
+    }
+  };
+  auto load_tile = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      if (rn[q] >= 0) {
+        kd[q].load(K + (size_t)rn[q] * D + e0);
+        vd[q].load(V + (size_t)rn[q] * D + e0);
       } else {
+        kd[q].zero();
+        vd[q].zero();
+      }
+    }
+  };
+  rows_of(0);
+  load_tile();
+  if (KT < cnt) rows_of(KT);
+  for (int t0 = 0; t0 < cnt; t0 += KT) {
+    // tile t0 from registers: sums, cluster-contiguous copies, transposed LDS stage
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { kv[j] = 0.f; vv[j] = 0.f; }
+    for (int q = 0; q < NP; ++q) {
+      const int key = q * KPP + ks0;
+      if (Kp && t0 + key < cnt) {
+        kd[q].store(Kp + (size_t)(t0 + key) * D + e0);
+        vd[q].store(Vp + (size_t)(t0 + key) * D + e0);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        sk[j] += kv[j];
-        sv[j] += vv[j];
-        split_store<NS>(kv[j], &sm.kt[0][e0 + j][key], D * SU_KP);
-        split_store<NS>(vv[j], &sm.vt[0][e0 + j][key], D * SU_KP);
+        const float kv = kd[q].at(j), vv = vd[q].at(j);
+        sk[j] += kv;
+        sv[j] += vv;
+        split_store<NS>(kv, &sm.kt[0][e0 + j][key], D * SM::KP);
+        split_store<NS>(vv, &sm.vt[0][e0 + j][key], D * SM::KP);
       }
     }
     __syncthreads();
+    if (t0 + KT < cnt) {
+      load_tile();
+      if (t0 + 2 * KT < cnt) rows_of(t0 + 2 * KT);
+    }
     if (pl.dipole) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int tau = w + 4 * u, dt = tau / DT, et = tau % DT;
-        u16x8 a[NS], b[NS];
+      for (int kk = 0; kk < KT / 32; ++kk)
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          a[s] = *reinterpret_cast<const u16x8*>(&sm.vt[s][16 * dt + col][8 * g]);
-          b[s] = *reinterpret_cast<const u16x8*>(&sm.kt[s][16 * et + col][8 * g]);
+        for (int u = 0; u < U; ++u) {
+          const int tau = w + 4 * u, dt = tau / DT, et = tau % DT;
+          u16x8 a[NS], b[NS];
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            a[s] = *reinterpret_cast<const u16x8*>(&sm.vt[s][16 * dt + col][32 * kk + 8 * g]);
+            b[s] = *reinterpret_cast<const u16x8*>(&sm.kt[s][16 * et + col][32 * kk + 8 * g]);
+          }
+          acc[u] = mfma_split<NS, NS>(a, b, acc[u]);
         }
-        acc[u] = mfma_split<NS, NS>(a, b, acc[u]);
-      }
     }
     __syncthreads();
   }
   // column sums over the key slots held by threads sharing e0 (fixed order)
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    sm.red[tid / TPK][0][e0 + j] = sk[j];
-    sm.red[tid / TPK][1][e0 + j] = sv[j];
+    sm.red[ks0][0][e0 + j] = sk[j];
+    sm.red[ks0][1][e0 + j] = sv[j];
   }
   // reuse kt as fp32 scratch for the sums: [2][D]
   __syncthreads();

@@ -83,7 +83,10 @@ def test_kmeans_default_init_and_determinism():
 
 
 @pytest.mark.parametrize("G,n,D,C,dtype", [(2, 700, 64, 16, "f32"), (2, 3000, 64, 64, "bf16"),
-                                           (1, 500, 128, 100, "bf16"), (1, 64, 64, 32, "f32")])
+                                           (1, 500, 128, 100, "bf16"), (1, 64, 64, 32, "f32"),
+                                           # clusters of over a thousand keys: many tiles, ragged tail
+                                           (1, 5001, 64, 6, "bf16"), (1, 2049, 128, 6, "bf16"),
+                                           (1, 1500, 128, 4, "f32")])
 def test_summarize_matches_oracle(G, n, D, C, dtype):
     import torch
     r = np.random.default_rng(n)
