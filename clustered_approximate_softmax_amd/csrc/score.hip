@@ -217,9 +217,8 @@ hipError_t launch_score_topk(const Plan& pl, const AttnBufs& b, hipStream_t st) 
 // over the key dim e, with A = rows of M (registers) and B = nu^T (staged in
 // LDS).  Small workgroups keep many in flight per CU, which hides the load
 // latency of each; the workgroups of one key problem run on one XCD, so the
-// query heads of its group re-read M from that XCD's L2.  A lane's result is
-// four consecutive clusters of one query cluster, stored as one contiguous
-// run.  Columns c in [C, Cp) are written as zeros.
+// query heads of its group re-read M from that XCD's L2.  Columns c in
+// [C, Cp) are written as zeros.
 // ---------------------------------------------------------------------------
 constexpr int TILT_IC = 128;   // query clusters staged at a time
 
@@ -228,12 +227,130 @@ struct alignas(16) TiltSmem {
   uint16_t nu[NS][TILT_IC][D + 8];   // nu rows of one query problem, bf16 parts
 };
 
+// One value dim d of T for the staged query clusters [i0, i0 + 16 nit):
+// jobs of NT2 adjacent 16-cluster tiles (A = rows of M in registers).  With
+// NT2 = 2 two lane exchanges give each lane eight consecutive clusters, so a
+// store writes 64 contiguous bytes of each of 16 rows (bf16); with NT2 = 1 a
+// lane stores its four clusters.  When there are fewer pairs than waves, pairs
+// would split the query clusters between waves and load each M row twice, so
+// small cluster counts take NT2 = 1.
+template <typename TIn, int D, int NS, int NT2, typename SM>
+__device__ __forceinline__ void tilt_dim(const SM& sm, const float* Mk, const float* Sk, const int32_t* koffs,
+                                         TIn* T, int d, int C, int Ck, int Cp, int Cq, int i0, int nit, float s) {
+  constexpr int KS = D / 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
+  const int njob = Cp / (16 * NT2);
+  for (int job = w; job < njob; job += 4) {
+    u16x8 a[NT2][KS][NS];
+    float sv[NT2][4], inv[NT2][4];
+#pragma unroll
+    for (int h = 0; h < NT2; ++h) {
+      const int cr = 16 * (NT2 * job + h) + col;   // A row: cluster
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        float v[8];
+        if (cr < Ck) {
+          const float* src = Mk + ((size_t)d * C + cr) * D + 32 * k + 8 * g;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+          v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
+          v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          uint16_t hh, m, l;
+          split3(v[j], hh, m, l);
+          a[h][k][0][j] = NS == 1 ? f2bf(v[j]) : hh;
+          if (NS > 1) { a[h][k][NS > 1 ? 1 : 0][j] = m; a[h][k][NS > 2 ? 2 : 0][j] = l; }
+        }
+      }
+      // the lane's four clusters of this tile: value sum and 1 / n_c
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * (NT2 * job + h) + 4 * g + i;
+        const int nc = c < Ck ? koffs[c + 1] - koffs[c] : 0;
+        inv[h][i] = nc > 0 ? 1.f / (float)nc : 0.f;
+        sv[h][i] = nc > 0 ? Sk[(size_t)c * D + d] : 0.f;
+      }
+    }
+    for (int it = 0; it < nit; ++it) {
+      f32x4 acc[NT2];
+#pragma unroll
+      for (int h = 0; h < NT2; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        u16x8 bb[NS];
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp)
+          bb[sp] = *reinterpret_cast<const u16x8*>(&sm.nu[sp][16 * it + col][32 * k + 8 * g]);
+#pragma unroll
+        for (int h = 0; h < NT2; ++h) acc[h] = mfma_split<NS, NS>(a[h][k], bb, acc[h]);
+      }
+      // lane (col, g) holds clusters 16h + 4g + i of the job, WB dwords per tile
+      constexpr int WB = sizeof(TIn) == 2 ? 2 : 4;
+      uint32_t pw[NT2][WB];
+#pragma unroll
+      for (int h = 0; h < NT2; ++h) {
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (sv[h][i] + s * acc[h][i]) * inv[h][i];
+        if constexpr (sizeof(TIn) == 2) {
+          pw[h][0] = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
+          pw[h][1] = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pw[h][i] = __float_as_uint(o[i]);
+        }
+      }
+      const int I = i0 + 16 * it + col;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      if constexpr (NT2 == 1) {
+        if (I < Cq) {
+          TIn* dst = T + ((size_t)I * D + d) * Cp + 16 * job + 4 * g;
+          if constexpr (sizeof(TIn) == 2) *reinterpret_cast<u32x2*>(dst) = u32x2{pw[0][0], pw[0][1]};
+          else *reinterpret_cast<u32x4*>(dst) = u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]};
+        }
+      } else {
+        // across lane bit 5: groups 0, 1 keep tile 0 and take tile 0 of group g + 2;
+        // groups 2, 3 keep tile 1 and take tile 1 of group g - 2
+        const bool hi2 = g >= 2, odd = g & 1;
+        uint32_t e[2][WB], f[2][WB];
+#pragma unroll
+        for (int q = 0; q < WB; ++q) {
+          const uint32_t r = lane_xor32(hi2 ? pw[0][q] : pw[NT2 - 1][q]);
+          e[0][q] = hi2 ? r : pw[0][q];
+          e[1][q] = hi2 ? pw[NT2 - 1][q] : r;
+        }
+        // across lane bit 4: even groups keep their first half, odd groups their second
+#pragma unroll
+        for (int q = 0; q < WB; ++q) {
+          const uint32_t r = lane_xor16(odd ? e[0][q] : e[1][q]);
+          f[0][q] = odd ? r : e[0][q];
+          f[1][q] = odd ? e[1][q] : r;
+        }
+        if (I < Cq) {
+          TIn* dst = T + ((size_t)I * D + d) * Cp + 32 * job + 8 * g;
+          if constexpr (sizeof(TIn) == 2) {
+            *reinterpret_cast<u32x4*>(dst) = u32x4{f[0][0], f[0][1], f[1][0], f[1][1]};
+          } else {
+            *reinterpret_cast<u32x4*>(dst) = u32x4{f[0][0], f[0][1], f[0][2], f[0][3]};
+            *reinterpret_cast<u32x4*>(dst + 4) = u32x4{f[1][0], f[1][1], f[1][2], f[1][3]};
+          }
+        }
+      }
+    }
+  }
+}
+
 template <typename TIn, int D, int NS>
 __global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b, int tb, long long kps) {
   using SM = TiltSmem<TIn, D, NS>;
   extern __shared__ __align__(16) unsigned char tilt_raw[];
   SM& sm = *reinterpret_cast<SM*>(tilt_raw);
-  constexpr int KS = D / 32;
   const int NDB = D / tb;
   const int C = pl.C, Cp = b.Cp32, Gq = pl.Hq / pl.Hkv;
   const int per = Gq * NDB;                       // workgroups per key problem
@@ -246,13 +363,11 @@ __global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b, int tb, 
   const int bq = kvh / pl.Hkv, kh = kvh % pl.Hkv;
   const Geom gm = prob_geom(pl, p);
   const int Cq = min(C, gm.qn), Ck = min(C, gm.kn);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int col = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x;
   const float s = pl.dipole ? pl.scale : 0.f;
   const float* Mk = b.kst.M + kp * (size_t)D * C * D;     // [d][c][e]
   const float* Sk = b.kst.S + kp * (size_t)C * D;         // [c][d]
   const int32_t* koffs = b.ks.offs + kp * (C + 1);
-  const int nct = Cp / 16;
   const size_t ap = (size_t)(bq * pl.Hq + kh * Gq + hl) * pl.P + p;
   const float* nu = b.qs.cent + ap * (size_t)C * D;        // [I][e]
   TIn* T = reinterpret_cast<TIn*>(b.T) + ap * (size_t)C * D * Cp;   // [I][d][c]
@@ -278,66 +393,8 @@ __global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b, int tb, 
     __syncthreads();
     for (int dd = 0; dd < tb; ++dd) {
       const int d = db * tb + dd;
-      for (int ct = w; ct < nct; ct += 4) {
-        const int cr = 16 * ct + col;          // A row: cluster
-        u16x8 a[KS][NS];
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          float v[8];
-          if (cr < Ck) {
-            const float* src = Mk + ((size_t)d * C + cr) * D + 32 * k + 8 * g;
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-            v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
-            v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = 0.f;
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            uint16_t h, m, l;
-            split3(v[j], h, m, l);
-            a[k][0][j] = NS == 1 ? f2bf(v[j]) : h;
-            if (NS > 1) { a[k][NS > 1 ? 1 : 0][j] = m; a[k][NS > 2 ? 2 : 0][j] = l; }
-          }
-        }
-        // the lane's four clusters: value sum and 1 / n_c
-        float sv[4], inv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = 16 * ct + 4 * g + i;
-          const int nc = c < Ck ? koffs[c + 1] - koffs[c] : 0;
-          inv[i] = nc > 0 ? 1.f / (float)nc : 0.f;
-          sv[i] = nc > 0 ? Sk[(size_t)c * D + d] : 0.f;
-        }
-        for (int it = 0; it < nit; ++it) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k = 0; k < KS; ++k) {
-            u16x8 bb[NS];
-#pragma unroll
-            for (int sp = 0; sp < NS; ++sp)
-              bb[sp] = *reinterpret_cast<const u16x8*>(&sm.nu[sp][16 * it + col][32 * k + 8 * g]);
-            acc = mfma_split<NS, NS>(a[k], bb, acc);
-          }
-          const int I = i0 + 16 * it + col;
-          if (I < Cq) {
-            TIn* dst = T + ((size_t)I * D + d) * Cp + 16 * ct + 4 * g;
-            float o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (sv[i] + s * acc[i]) * inv[i];
-            if constexpr (sizeof(TIn) == 2) {
-              typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-              u32x2 wv = {(uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16),
-                          (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16)};
-              *reinterpret_cast<u32x2*>(dst) = wv;
-            } else {
-              *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
-            }
-          }
-        }
-      }
+      if (Cp >= 128) tilt_dim<TIn, D, NS, 2>(sm, Mk, Sk, koffs, T, d, C, Ck, Cp, Cq, i0, nit, s);
+      else tilt_dim<TIn, D, NS, 1>(sm, Mk, Sk, koffs, T, d, C, Ck, Cp, Cq, i0, nit, s);
     }
   }
 }
