@@ -123,7 +123,7 @@ struct BwdArgs {
   float* dk;      // [B*Hkv][N][D]
   float* dv;
   // per-level buffers; lp = bh * nseg + t, kl = kvh * nseg + t
-  float* dT;      // [lp][C][D][C]   (I, d, c): sum_i p dO_i / n_c over far items
+  void* dT;       // [lp][C][D][C]   (I, d, c): sum_i p dO_i / n_c over far items, input dtype
   float* G;       // [lp][nib][C][D] (block of query clusters, c, e): s sum_{I in block} sum_i dl q_i over far items
   float* dnu;     // [lp][C][D]
   float* dS;      // [kl][C][D]
@@ -973,11 +973,11 @@ __global__ void __launch_bounds__(64 * WAVES, sizeof(TIn) == 2 ? 2 : 1) bwd_far_
     for (int dt = 0; dt < DT; ++dt) dvt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     bk_query_range<TIn, D, false, NT>(sm, A, bh, qperm, qoffs[I], qoffs[I + 1], kf, vf, ibias, -1, s2, dvt, dkt);
     if (ivalid) {
-      float* dT = A.dT + (lp * C + I) * (size_t)D * C;          // (d, c)
+      TIn* dT = reinterpret_cast<TIn*>(A.dT) + (lp * C + I) * (size_t)D * C;   // (d, c)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dT[(size_t)(16 * dt + 4 * g + i) * C + item] = dvt[dt][i] * inv;
+        for (int i = 0; i < 4; ++i) store1<TIn>(dT + (size_t)(16 * dt + 4 * g + i) * C + item, dvt[dt][i] * inv);
     }
   }
   if (ivalid) {
@@ -1014,6 +1014,21 @@ __device__ __forceinline__ void load4x(const float* p, int n4, float* out) {
   for (int q = 0; q < n4; ++q) {
     const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * q);
     out[4 * q] = x[0]; out[4 * q + 1] = x[1]; out[4 * q + 2] = x[2]; out[4 * q + 3] = x[3];
+  }
+}
+
+// 16 consecutive elements of dT (fp32, or bf16 for bf16 inputs) as floats
+template <typename DT>
+__device__ __forceinline__ void load16(const DT* p, float* out) {
+  if constexpr (sizeof(DT) == 2) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u16x8 x = *reinterpret_cast<const u16x8*>(p + 8 * q);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out[8 * q + j] = bf2f(x[j]);
+    }
+  } else {
+    load4x(p, 4, out);
   }
 }
 
@@ -1114,14 +1129,15 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(P prob) {
 }
 
 // dnu_I[e] = s sum_{d,c} dT_I[d][c] M[d][c][e]; batch = lp = bh * nseg + t
+template <typename DT>
 struct GemmDnu {
   static constexpr bool A_KC = true, ROWSUM = false;
   Plan pl;
   int lev, mtiles;
-  const float* dT;
+  const DT* dT;
   const float* Mst;
   float* dnu;
-  struct View { int M, K; const float* A; const float* B; float* C; };
+  struct View { int M, K; const DT* A; const float* B; float* C; };
   __device__ void view(int batch, View& v) const {
     const int nseg = pl.lev_nseg[lev];
     const int t = batch % nseg, bh = batch / nseg;
@@ -1137,7 +1153,7 @@ struct GemmDnu {
   }
   // A row m, k .. k+15 (K is a multiple of 64)
   __device__ void a16(const View& v, int m, int k, float* out) const {
-    if (m < v.M && k < v.K) load4x(v.A + (size_t)m * v.K + k, 4, out);
+    if (m < v.M && k < v.K) load16<DT>(v.A + (size_t)m * v.K + k, out);
     else for (int j = 0; j < 16; ++j) out[j] = 0.f;
   }
   template <int BF>
@@ -1149,12 +1165,13 @@ struct GemmDnu {
 };
 
 // dM[d][c][e] = s sum_{h,I} dT_{h,I}[d][c] nu_{h,I}[e]; batch = kl = kvh * nseg + t
+template <typename DT>
 struct GemmDm {
   // also the row sums of dT over (h, I): dS_c[d] for m = (d, c)
   static constexpr bool A_KC = false, ROWSUM = true;
   Plan pl;
   int lev, mtiles;
-  const float* dT;
+  const DT* dT;
   const float* nu;   // query centroids [B*Hq][P][C][D]
   float* dM;
   float* dS;         // [kl][C][D]
@@ -1179,7 +1196,7 @@ struct GemmDm {
     const int h = k / pl.C, I = k % pl.C;
     if (k < v.K && I < v.Cq && m < v.M) {
       const size_t lp = (size_t)(v.bh0 + h) * pl.lev_nseg[lev] + v.t;
-      load4x(dT + (lp * pl.C + I) * (size_t)pl.D * pl.C + m, 4, out);
+      load16<DT>(dT + (lp * pl.C + I) * (size_t)pl.D * pl.C + m, out);
     } else {
       for (int j = 0; j < 16; ++j) out[j] = 0.f;
     }
@@ -1206,6 +1223,7 @@ struct GemmDm {
 // dipole term), dS_c[d] = sum_{h,I} dT_{h,I}[d][c]
 // one thread per (kl, index in C*D)
 // ===========================================================================
+template <typename TIn>
 __global__ void __launch_bounds__(256) bwd_reduce_k_kernel(BwdArgs A, int lev, int ig, int with_ds) {
   const Plan& pl = A.pl;
   const int C = pl.C, D = pl.D, Gq = pl.Hq / pl.Hkv;
@@ -1225,7 +1243,8 @@ __global__ void __launch_bounds__(256) bwd_reduce_k_kernel(BwdArgs A, int lev, i
   for (int h = 0; h < Gq; ++h) {
     const size_t lp = (size_t)(bh0 + h) * nseg + t;
     if (with_ds)
-      for (int I = 0; I < Cq; ++I) sS += A.dT[(lp * C + I) * (size_t)D * C + idx];
+      for (int I = 0; I < Cq; ++I)
+        sS += load1_f32<TIn>(reinterpret_cast<const TIn*>(A.dT) + (lp * C + I) * (size_t)D * C + idx);
     for (int q = 0; q < nibq; ++q) sMu += A.G[(lp * nib + q) * (size_t)C * D + idx];
   }
   const int d = idx / C, c = idx % C;   // the dT index is (d, c)
@@ -1444,17 +1463,18 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
     if ((e = hipGetLastError()) != hipSuccess) return e;
     MUSE_KT_PRE(st);
     // dS_c comes from the dM contraction when there is one (it reads every dT anyway)
-    bwd_reduce_k_kernel<<<(unsigned)(pl.B * pl.Hkv * nseg * ((C * D + 255) / 256)), 256, 0, st>>>(A, lev, ig,
+    bwd_reduce_k_kernel<TIn><<<(unsigned)(pl.B * pl.Hkv * nseg * ((C * D + 255) / 256)), 256, 0, st>>>(A, lev, ig,
                                                                                                   pl.dipole ? 0 : 1);
     MUSE_KT_POST("bwd_reduce_k", st);
     if (pl.dipole) {
-      GemmDm gdm{pl, lev, (D * C + BG_TM - 1) / BG_TM, A.dT, A.a.qs.cent, A.dM, A.dS};
+      GemmDm<TIn> gdm{pl, lev, (D * C + BG_TM - 1) / BG_TM, reinterpret_cast<const TIn*>(A.dT), A.a.qs.cent, A.dM,
+                      A.dS};
       MUSE_KT_PRE(st);
-      bwd_gemm_kernel<GemmDm, NSG, D><<<(unsigned)(pl.B * pl.Hkv * nseg * gdm.mtiles), 256, 0, st>>>(gdm);
+      bwd_gemm_kernel<GemmDm<TIn>, NSG, D><<<(unsigned)(pl.B * pl.Hkv * nseg * gdm.mtiles), 256, 0, st>>>(gdm);
       MUSE_KT_POST("bwd_dM", st);
-      GemmDnu gdn{pl, lev, (C + BG_TM - 1) / BG_TM, A.dT, A.a.kst.M, A.dnu};
+      GemmDnu<TIn> gdn{pl, lev, (C + BG_TM - 1) / BG_TM, reinterpret_cast<const TIn*>(A.dT), A.a.kst.M, A.dnu};
       MUSE_KT_PRE(st);
-      bwd_gemm_kernel<GemmDnu, NSG, D><<<(unsigned)(pl.B * pl.Hq * nseg * gdn.mtiles), 256, 0, st>>>(gdn);
+      bwd_gemm_kernel<GemmDnu<TIn>, NSG, D><<<(unsigned)(pl.B * pl.Hq * nseg * gdn.mtiles), 256, 0, st>>>(gdn);
       MUSE_KT_POST("bwd_dnu", st);
       MUSE_KT_PRE(st);
       bwd_spread_q_kernel<<<(unsigned)((nq * (D / 4) + 255) / 256), 256, 0, st>>>(A, lev);

@@ -234,7 +234,7 @@ static void build_bwd_layout(const Plan& pl, int dtype, BwdLayout& o) {
   o.dq = w; w = al(w + BHq * N * D * 4);
   o.dk = w; w = al(w + BHk * N * D * 4);
   o.dv = w; w = al(w + BHk * N * D * 4);
-  o.dT = w; w = al(w + BHq * ms * C * D * C * 4);
+  o.dT = w; w = al(w + BHq * ms * C * D * C * eb);
   o.G = w; w = al(w + BHq * ms * C * C * D * 4);
   o.dnu = w; w = al(w + BHq * ms * C * D * 4);
   o.dS = w; w = al(w + BHk * ms * C * D * 4);
@@ -457,7 +457,7 @@ int museattn_bwd(const void* Q, const void* K, const void* V, const void* O, con
   bw.dq = (float*)(wb + bl.dq);
   bw.dk = (float*)(wb + bl.dk);
   bw.dv = (float*)(wb + bl.dv);
-  bw.dT = (float*)(wb + bl.dT);
+  bw.dT = (void*)(wb + bl.dT);
   bw.G = (float*)(wb + bl.G);
   bw.dnu = (float*)(wb + bl.dnu);
   bw.dS = (float*)(wb + bl.dS);

@@ -71,7 +71,7 @@ struct BwdLaunch {
   const float* lse;
   float* delta;           // [B*Hq][N]
   float* dq; float* dk; float* dv;   // fp32 accumulators, [heads][N][D]
-  float* dT;              // per-level scratch, see bwd.hip
+  void* dT;               // per-level scratch in the input dtype, see bwd.hip
   float* G;
   float* dnu;
   float* dS;
