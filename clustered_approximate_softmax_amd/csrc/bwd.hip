@@ -1078,8 +1078,8 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(P prob) {
   float rsum[P::ROWSUM ? 16 : 1];
 #pragma unroll
   for (int j = 0; j < (P::ROWSUM ? 16 : 1); ++j) rsum[j] = 0.f;
-  load(0);
-  for (int k0 = 0; k0 < v.K; k0 += KT) {
+  load(v.K0);
+  for (int k0 = v.K0; k0 < v.K; k0 += KT) {
     if constexpr (P::ROWSUM) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) rsum[j] += ra[j];
@@ -1128,17 +1128,21 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(P prob) {
   }
 }
 
-// dnu_I[e] = s sum_{d,c} dT_I[d][c] M[d][c][e]; batch = lp = bh * nseg + t
+// dnu_I[e] = s sum_{d,c} dT_I[d][c] M[d][c][e]; batch = lp = bh * nseg + t.
+// With ksplit > 1 each workgroup contracts one of ksplit ranges of k = (d, c)
+// and writes its partial to slab ks of dnu ([ks][lp][I][e]); bwd_dnu_sum then
+// adds the slabs into slab 0 in order.
 template <typename DT>
 struct GemmDnu {
   static constexpr bool A_KC = true, ROWSUM = false;
   Plan pl;
-  int lev, mtiles;
+  int lev, mtiles, ksplit;
   const DT* dT;
   const float* Mst;
   float* dnu;
-  struct View { int M, K; const DT* A; const float* B; float* C; };
-  __device__ void view(int batch, View& v) const {
+  struct View { int M, K0, K; const DT* A; const float* B; float* C; };
+  __device__ void view(int id, View& v) const {
+    const int ks = id % ksplit, batch = id / ksplit;
     const int nseg = pl.lev_nseg[lev];
     const int t = batch % nseg, bh = batch / nseg;
     const int p = pl.lev_pfirst[lev] + t;
@@ -1146,14 +1150,16 @@ struct GemmDnu {
     const int kvh = (bh / pl.Hq) * pl.Hkv + ((bh % pl.Hq) * pl.Hkv) / pl.Hq;
     const size_t kp = (size_t)kvh * pl.P + p;
     v.M = min(pl.C, gm.qn);
-    v.K = pl.D * pl.C;
+    const int kc = pl.D * pl.C / ksplit;   // a multiple of 32
+    v.K0 = ks * kc;
+    v.K = v.K0 + kc;
     v.A = dT + (size_t)batch * pl.C * pl.D * pl.C;
     v.B = Mst + kp * pl.D * pl.C * pl.D;
-    v.C = dnu + (size_t)batch * pl.C * pl.D;
+    v.C = dnu + ((size_t)ks * pl.B * pl.Hq * nseg + batch) * pl.C * pl.D;
   }
   // A row m, k .. k+15 (K is a multiple of 64)
   __device__ void a16(const View& v, int m, int k, float* out) const {
-    if (m < v.M && k < v.K) load16<DT>(v.A + (size_t)m * v.K + k, out);
+    if (m < v.M && k < v.K) load16<DT>(v.A + (size_t)m * pl.D * pl.C + k, out);   // rows of D * C
     else for (int j = 0; j < 16; ++j) out[j] = 0.f;
   }
   template <int BF>
@@ -1175,7 +1181,7 @@ struct GemmDm {
   const float* nu;   // query centroids [B*Hq][P][C][D]
   float* dM;
   float* dS;         // [kl][C][D]
-  struct View { int M, K, Cq, t, p, bh0, kl; float* C; };
+  struct View { int M, K0, K, Cq, t, p, bh0, kl; float* C; };
   __device__ void view(int batch, View& v) const {
     const int nseg = pl.lev_nseg[lev];
     const int t = batch % nseg, kvh = batch / nseg;
@@ -1184,6 +1190,7 @@ struct GemmDm {
     const int Gq = pl.Hq / pl.Hkv;
     v.Cq = min(pl.C, gm.qn);
     v.M = pl.D * pl.C;
+    v.K0 = 0;
     v.K = Gq * pl.C;
     v.t = t;
     v.p = p;
@@ -1250,6 +1257,16 @@ __global__ void __launch_bounds__(256) bwd_reduce_k_kernel(BwdArgs A, int lev, i
   const int d = idx / C, c = idx % C;   // the dT index is (d, c)
   if (with_ds) A.dS[((size_t)kl * C + c) * D + d] = sS;
   A.dmu[(size_t)kl * C * D + idx] = sMu;
+}
+
+// dnu partial slabs (split contraction) summed into slab 0 in order; one
+// thread per 4 values of a slab
+__global__ void __launch_bounds__(256) bwd_dnu_sum_kernel(float* dnu, long long n4, long long slab, int ksplit) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 v = *reinterpret_cast<const f32x4*>(dnu + 4 * i);
+  for (int q = 1; q < ksplit; ++q) v += *reinterpret_cast<const f32x4*>(dnu + q * slab + 4 * i);
+  *reinterpret_cast<f32x4*>(dnu + 4 * i) = v;
 }
 
 // dq_i += dnu_I / m_I for every query of the level; one thread per (row, 4 dims)
@@ -1438,6 +1455,8 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int C = pl.C;
+  int msegs = 0;   // the most segments of any level: the per-level buffers hold that many
+  for (int l = 0; l < pl.nlev; ++l) msegs = std::max(msegs, pl.lev_nseg[l]);
   for (int lev = 0; lev < pl.nlev; ++lev) {
     const long long nseg = pl.lev_nseg[lev];
     if (nseg == 0) continue;
@@ -1472,9 +1491,20 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
       MUSE_KT_PRE(st);
       bwd_gemm_kernel<GemmDm<TIn>, NSG, D><<<(unsigned)(pl.B * pl.Hkv * nseg * gdm.mtiles), 256, 0, st>>>(gdm);
       MUSE_KT_POST("bwd_dM", st);
-      GemmDnu<TIn> gdn{pl, lev, (C + BG_TM - 1) / BG_TM, reinterpret_cast<const TIn*>(A.dT), A.a.kst.M, A.dnu};
+      // split k = (d, c) while the level has few (head, segment) batches: partial
+      // slabs fit the buffer (sized for the most segments) and ranges stay whole k steps
+      const long long nbat = (long long)pl.B * pl.Hq * nseg * ((C + BG_TM - 1) / BG_TM);
+      int ksplit = 1;
+      while (nseg * ksplit * 2 <= msegs && nbat * ksplit * 2 <= 1024 && (D * C) % (BG_KT * ksplit * 2) == 0)
+        ksplit *= 2;
+      GemmDnu<TIn> gdn{pl, lev, (C + BG_TM - 1) / BG_TM, ksplit, reinterpret_cast<const TIn*>(A.dT), A.a.kst.M,
+                       A.dnu};
       MUSE_KT_PRE(st);
-      bwd_gemm_kernel<GemmDnu<TIn>, NSG, D><<<(unsigned)(pl.B * pl.Hq * nseg * gdn.mtiles), 256, 0, st>>>(gdn);
+      bwd_gemm_kernel<GemmDnu<TIn>, NSG, D><<<(unsigned)(nbat * ksplit), 256, 0, st>>>(gdn);
+      if (ksplit > 1) {
+        const long long slab = (long long)pl.B * pl.Hq * nseg * C * D;
+        bwd_dnu_sum_kernel<<<(unsigned)((slab / 4 + 255) / 256), 256, 0, st>>>(A.dnu, slab / 4, slab, ksplit);
+      }
       MUSE_KT_POST("bwd_dnu", st);
       MUSE_KT_PRE(st);
       bwd_spread_q_kernel<<<(unsigned)((nq * (D / 4) + 255) / 256), 256, 0, st>>>(A, lev);

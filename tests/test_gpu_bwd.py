@@ -15,8 +15,9 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 # gradient tolerances (max-normalised): fp32 inputs use 3-part split products
-# throughout (observed <= 1.3e-6); bf16 rounds P, dS and the staged operands to
-# bf16 (2^-9) and the outputs themselves (observed <= 4.7e-3)
+# throughout (observed <= 1.3e-6); bf16 rounds P, dS, the far-field value
+# gradients dT and the staged operands to bf16 (2^-9) and the outputs themselves
+# (observed <= 6.2e-3)
 GTOL = {"f32": 2e-5, "bf16": 1e-2}
 
 
