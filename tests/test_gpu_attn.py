@@ -119,6 +119,28 @@ def test_causal_block_covers_sequence():
     assert gu.max_rel(r["O"][0, 0], o) < 2e-2
 
 
+def test_fewer_rows_than_clusters():
+    # N < C: C_eff = N clusters of one row each; k1 = 3 of them exact, the rest far
+    run_case(1, 2, 1, 5, 64, "bf16", 16, 3, 3, seed=11)
+
+
+def test_single_row():
+    run_case(1, 1, 1, 1, 64, "f32", 4, 2, 1, seed=12)
+
+
+def test_causal_one_block_and_one_row():
+    # one level whose only segment has a full key block and a single query row
+    run_case(1, 2, 2, 65, 128, "bf16", 8, 2, 2, causal=True, block=64, seed=13)
+
+
+def test_topk_above_cluster_count_clamps():
+    # k1 > C retrieves every non-empty cluster: exact attention
+    r = run_case(1, 1, 1, 300, 64, "bf16", 8, 2, 50, seed=14)
+    x = r["x"]
+    o, _ = mo.exact_attention(x["Q"][0, 0], x["K"][0, 0], x["V"][0, 0], 1 / 8)
+    assert gu.max_rel(r["O"][0, 0], o) < 2e-2
+
+
 def test_forward_is_deterministic():
     import torch
     x = gu.gaussian_inputs(1, 2, 2, 2048, 64, "bf16", comps=32, seed=10)

@@ -112,6 +112,15 @@ def test_many_pairs_per_key_cluster():
     run_bwd(1, 8, 1, 1024, 64, "bf16", 128, 2, 128, seed=24)
 
 
+def test_fewer_rows_than_clusters():
+    # N < C: single-row clusters, far and retrieved
+    run_bwd(1, 2, 1, 5, 64, "bf16", 16, 2, 3, seed=25)
+
+
+def test_causal_one_block_and_one_row():
+    run_bwd(1, 2, 2, 65, 128, "bf16", 8, 2, 2, causal=True, block=64, seed=26)
+
+
 def test_causal_block_covers_sequence():
     run_bwd(1, 2, 2, 200, 64, "bf16", 8, 2, 1, causal=True, block=256, seed=10)
 
