@@ -518,45 +518,14 @@ struct alignas(16) BkSmem {
   int32_t sel[4];
 };
 
+// fp32 inputs: rows sm.qrow[0 .. QB) of Qh / dOh (-1 for none) into LDS as
+// split-bf16 parts, rows and slot-order transposes (bf16 inputs stage through
+// the software-pipelined path of bk_query_range)
 template <typename TIn, int D, int NT>
 __device__ __forceinline__ void bk_stage_queries(BkSmem<TIn, D>& sm, const TIn* Qh, const TIn* dOh,
                                                  const float* lse, const float* delta) {
   constexpr int NS = BkSmem<TIn, D>::NS;
-  if constexpr (NS == 1) {
-    // bf16: 4 queries x 8 dims per thread; rows as 16-byte chunks, the
-    // transposes as 4-query runs in slot order
-    for (int idx = threadIdx.x; idx < (QB / 4) * (D / 8); idx += NT) {
-      const int qb = idx % (QB / 4), e0 = (idx / (QB / 4)) * 8;
-      u16x8 qr[4], orr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = sm.qrow[4 * qb + r];
-        qr[r] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        orr[r] = qr[r];
-        if (row >= 0) {
-          qr[r] = *reinterpret_cast<const u16x8*>(Qh + (size_t)row * D + e0);
-          orr[r] = *reinterpret_cast<const u16x8*>(dOh + (size_t)row * D + e0);
-        }
-      }
-      const int pos = slot_of(4 * qb);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<u16x8*>(&sm.qs[0][4 * qb + r][e0]) = qr[r];
-        *reinterpret_cast<u16x8*>(&sm.os[0][4 * qb + r][e0]) = orr[r];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        *reinterpret_cast<u16x4*>(&sm.qt[0][e0 + j][pos]) = u16x4{qr[0][j], qr[1][j], qr[2][j], qr[3][j]};
-        *reinterpret_cast<u16x4*>(&sm.ot[0][e0 + j][pos]) = u16x4{orr[0][j], orr[1][j], orr[2][j], orr[3][j]};
-      }
-    }
-    if (threadIdx.x < QB) {
-      const int row = sm.qrow[threadIdx.x];
-      sm.lse2[threadIdx.x] = row >= 0 ? lse[row] * B_LOG2E : 0.f;
-      sm.dlt[threadIdx.x] = row >= 0 ? delta[row] : 0.f;
-    }
-    return;
-  }
+  static_assert(NS > 1, "bf16 inputs take the pipelined staging");
   for (int idx = threadIdx.x; idx < QB * (D / 8); idx += NT) {
     const int q = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
     const int row = sm.qrow[q];
@@ -716,18 +685,18 @@ __device__ __forceinline__ void bk_query_range(BkSmem<TIn, D>& sm, const BwdArgs
       bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
       __syncthreads();
     }
-    return;
-  }
-  for (int q0 = qa; q0 < qb; q0 += QB) {
-    if (threadIdx.x < QB) {
-      const int q = q0 + threadIdx.x;
-      sm.qrow[threadIdx.x] = q < qb ? (rows ? rows[q] : q) : -1;
+  } else {
+    for (int q0 = qa; q0 < qb; q0 += QB) {
+      if (threadIdx.x < QB) {
+        const int q = q0 + threadIdx.x;
+        sm.qrow[threadIdx.x] = q < qb ? (rows ? rows[q] : q) : -1;
+      }
+      __syncthreads();
+      bk_stage_queries<TIn, D, NT>(sm, Qh, dOh, lse, delta);
+      __syncthreads();
+      bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
+      __syncthreads();
     }
-    __syncthreads();
-    bk_stage_queries<TIn, D, NT>(sm, Qh, dOh, lse, delta);
-    __syncthreads();
-    bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
-    __syncthreads();
   }
 }
 

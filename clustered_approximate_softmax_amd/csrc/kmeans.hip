@@ -648,7 +648,6 @@ __device__ void km_update_sub(SM& sm, KmAcc<TIn, D, CT>& acc, int Ceff) {
   using S = KmShape<TIn, D>;
   constexpr int NS = S::NS;
   constexpr int DT = D / 16;
-  constexpr int U = KmAcc<TIn, D, CT>::U;
   constexpr int NCT = CT >= 4 ? CT / 4 : 1;                          // cluster tiles per wave
   constexpr int NDT = CT >= 4 ? DT : CT == 2 ? DT / 2 : DT / 4;      // dim tiles per wave
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
