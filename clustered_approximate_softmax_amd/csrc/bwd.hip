@@ -134,19 +134,25 @@ struct BwdArgs {
 // ===========================================================================
 // Delta_i = dO_i . O_i ; zero fill ; fp32 -> output dtype
 // ===========================================================================
-template <typename TIn>
-__global__ void bwd_delta_kernel(const TIn* O, const TIn* dO, float* delta, long long rows, int D) {
-  const long long r = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= rows) return;
+// D / 8 consecutive lanes per row, 8 elements each (coalesced rows), summed
+// across the row's lanes by shuffles in a fixed order
+template <typename TIn, int D>
+__global__ void __launch_bounds__(256) bwd_delta_kernel(const TIn* O, const TIn* dO, float* delta, long long rows) {
+  constexpr int TPR = D / 8;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long r = gid / TPR;
+  const int e = (int)(gid % TPR) * 8;
   float s = 0.f;
-  for (int e = 0; e < D; e += 8) {
+  if (r < rows) {
     float a[8], b[8];
     load8_f32<TIn>(O + r * D + e, a);
     load8_f32<TIn>(dO + r * D + e, b);
 #pragma unroll
     for (int j = 0; j < 8; ++j) s = fmaf(a[j], b[j], s);
   }
-  delta[r] = s;
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (r < rows && e == 0) delta[r] = s;
 }
 
 __global__ void bwd_zero_kernel(float* p, long long n) {
@@ -155,10 +161,20 @@ __global__ void bwd_zero_kernel(float* p, long long n) {
   else for (long long k = i; k < n; ++k) p[k] = 0.f;
 }
 
+// fp32 accumulators to the output dtype, 8 elements per thread (n8 = n / 8)
 template <typename TOut>
-__global__ void bwd_out_kernel(const float* src, TOut* dst, long long n) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) store1<TOut>(dst + i, src[i]);
+__global__ void __launch_bounds__(256) bwd_out_kernel(const float* src, TOut* dst, long long n8) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(src + 8 * i);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(src + 8 * i + 4);
+  if constexpr (sizeof(TOut) == 2) {
+    *reinterpret_cast<u16x8*>(dst + 8 * i) =
+        u16x8{f2bf(a[0]), f2bf(a[1]), f2bf(a[2]), f2bf(a[3]), f2bf(b[0]), f2bf(b[1]), f2bf(b[2]), f2bf(b[3])};
+  } else {
+    *reinterpret_cast<f32x4*>(dst + 8 * i) = a;
+    *reinterpret_cast<f32x4*>(dst + 8 * i + 4) = b;
+  }
 }
 
 // ===========================================================================
@@ -1409,8 +1425,8 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
   bwd_zero_kernel<<<(unsigned)((nq * D / 4 + 255) / 256), 256, 0, st>>>(A.dq, nq * D);
   bwd_zero_kernel<<<(unsigned)((nk * D / 4 + 255) / 256), 256, 0, st>>>(A.dk, nk * D);
   bwd_zero_kernel<<<(unsigned)((nk * D / 4 + 255) / 256), 256, 0, st>>>(A.dv, nk * D);
-  bwd_delta_kernel<TIn><<<(unsigned)((nq + 255) / 256), 256, 0, st>>>(
-      reinterpret_cast<const TIn*>(A.a.O), reinterpret_cast<const TIn*>(A.dO), A.delta, nq, D);
+  bwd_delta_kernel<TIn, D><<<(unsigned)((nq * (D / 8) + 255) / 256), 256, 0, st>>>(
+      reinterpret_cast<const TIn*>(A.a.O), reinterpret_cast<const TIn*>(A.dO), A.delta, nq);
   MUSE_KT_POST("bwd_prep", st);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (pl.causal) {
@@ -1487,9 +1503,13 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   MUSE_KT_PRE(st);
-  bwd_out_kernel<TIn><<<(unsigned)((nq * D + 255) / 256), 256, 0, st>>>(A.dq, reinterpret_cast<TIn*>(dQo), nq * D);
-  bwd_out_kernel<TIn><<<(unsigned)((nk * D + 255) / 256), 256, 0, st>>>(A.dk, reinterpret_cast<TIn*>(dKo), nk * D);
-  bwd_out_kernel<TIn><<<(unsigned)((nk * D + 255) / 256), 256, 0, st>>>(A.dv, reinterpret_cast<TIn*>(dVo), nk * D);
+  // rows of D elements: counts of 8-element groups
+  bwd_out_kernel<TIn><<<(unsigned)((nq * D / 8 + 255) / 256), 256, 0, st>>>(A.dq, reinterpret_cast<TIn*>(dQo),
+                                                                           nq * D / 8);
+  bwd_out_kernel<TIn><<<(unsigned)((nk * D / 8 + 255) / 256), 256, 0, st>>>(A.dk, reinterpret_cast<TIn*>(dKo),
+                                                                           nk * D / 8);
+  bwd_out_kernel<TIn><<<(unsigned)((nk * D / 8 + 255) / 256), 256, 0, st>>>(A.dv, reinterpret_cast<TIn*>(dVo),
+                                                                           nk * D / 8);
   MUSE_KT_POST("bwd_out", st);
   return hipGetLastError();
 }

@@ -121,6 +121,9 @@ static int build_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, 
 
 static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// the kernels move tensor rows, state and workspace with 16-byte vector accesses
+static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 struct Layout {
   muse_layout L;
   int plocal;
@@ -301,6 +304,7 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
                  const int32_t* init_k, void* O, float* lse, void* state, size_t state_bytes,
                  void* ws, size_t ws_bytes, void* stream) {
   if (!Q || !K || !V || !O || !lse || !state || !ws) return MUSE_EINVAL;
+  if (!al16(Q) || !al16(K) || !al16(V) || !al16(O) || !al16(state) || !al16(ws)) return MUSE_EINVAL;
   if (dtype != MUSE_F32 && dtype != MUSE_BF16) return MUSE_EINVAL;
   Plan pl;
   int rc = build_plan(B, Hq, Hkv, N, D, cfg, pl);
@@ -361,6 +365,7 @@ int musecluster(const void* X, muse_dtype dtype, int64_t G, int64_t n, int64_t D
                 int32_t iters, const int32_t* init_idx, int32_t* assign, float* centroids,
                 int32_t* perm, int32_t* offs, void* ws, size_t ws_bytes, void* stream) {
   if (!X || !assign || !centroids || !perm || !offs) return MUSE_EINVAL;
+  if (!al16(X) || !al16(centroids) || (ws && !al16(ws))) return MUSE_EINVAL;
   if (dtype != MUSE_F32 && dtype != MUSE_BF16) return MUSE_EINVAL;
   muse_cfg cfg{C, C, iters, 0, 0, 0, 1, 0, 0.f};
   Plan pl;
@@ -387,6 +392,7 @@ int musesummarize(const void* K, const void* V, muse_dtype dtype, int64_t G, int
                   int32_t C, const int32_t* assign, int32_t* perm, int32_t* offs, float* mu,
                   float* S, float* M, void* stream) {
   if (!K || !V || !assign || !perm || !offs || !mu || !S || !M) return MUSE_EINVAL;
+  if (!al16(K) || !al16(V)) return MUSE_EINVAL;
   if (dtype != MUSE_F32 && dtype != MUSE_BF16) return MUSE_EINVAL;
   muse_cfg cfg{C, C, 1, 0, 0, 0, 1, 0, 0.f};
   Plan pl;
@@ -417,6 +423,9 @@ int museattn_bwd(const void* Q, const void* K, const void* V, const void* O, con
                  int64_t D, const muse_cfg* cfg, const void* state, size_t state_bytes, void* dQ,
                  void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
   if (!Q || !K || !V || !O || !lse || !dO || !state || !dQ || !dK || !dV || !ws) return MUSE_EINVAL;
+  const void* vec[] = {Q, K, V, O, dO, dQ, dK, dV, state, ws};
+  for (const void* p : vec)
+    if (!al16(p)) return MUSE_EINVAL;
   if (dtype != MUSE_F32 && dtype != MUSE_BF16) return MUSE_EINVAL;
   Plan pl;
   int rc = build_plan(B, Hq, Hkv, N, D, cfg, pl);

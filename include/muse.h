@@ -25,6 +25,9 @@
  *   checks happen on the host before the first launch, so an error return
  *   means nothing was queued, except MUSE_EHIP (a launch failed; the HIP
  *   error string is available from muse_last_hip_error()).
+ * - Alignment: Q, K, V, O, dO, dQ, dK, dV, X, centroids and the state and
+ *   workspace buffers must be 16-byte aligned (MUSE_EINVAL otherwise); the
+ *   kernels move their rows with 16-byte vector accesses.
  * - Clamping (documented, not errors): a problem with n < C points uses
  *   C_eff = n clusters; k1 is clamped to the number of non-empty key
  *   clusters of each problem.

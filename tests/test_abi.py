@@ -99,9 +99,16 @@ def test_cluster_and_summarize_reject_bad_arguments():
     assert L.musesummarize(FAKE, FAKE, 1, 2, 100, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
 
 
-def test_backward_reports_unsupported_until_built():
-    # fixed-assignment backward entry point exists in the ABI
+def test_backward_entry_point_exported():
     assert hasattr(M.lib(), "museattn_bwd")
+
+
+def test_entry_points_reject_misaligned_tensors():
+    odd = ctypes.c_void_p(0x1008)   # 8-byte aligned only
+    assert _fwd(M.make_cfg(16, 3, 1), ptr=odd) == -1
+    L = M.lib()
+    assert L.musecluster(odd, 1, 2, 100, 64, 8, 3, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert L.musesummarize(odd, FAKE, 1, 2, 100, 64, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
 
 
 def test_bwd_ws_size_and_null_checks():
