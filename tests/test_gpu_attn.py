@@ -119,6 +119,10 @@ def test_causal_block_covers_sequence():
     assert gu.max_rel(r["O"][0, 0], o) < 2e-2
 
 
+def test_causal_monopole():
+    run_case(1, 2, 1, 1000, 64, "bf16", 16, 2, 2, causal=True, block=64, dipole=False, seed=15)
+
+
 def test_fewer_rows_than_clusters():
     # N < C: C_eff = N clusters of one row each; k1 = 3 of them exact, the rest far
     run_case(1, 2, 1, 5, 64, "bf16", 16, 3, 3, seed=11)

@@ -112,6 +112,15 @@ def test_many_pairs_per_key_cluster():
     run_bwd(1, 8, 1, 1024, 64, "bf16", 128, 2, 128, seed=24)
 
 
+def test_causal_monopole():
+    # without the dipole term dS comes from the cluster reduction, not the dM contraction
+    run_bwd(1, 2, 1, 1000, 64, "bf16", 16, 2, 2, causal=True, block=64, dipole=False, seed=27)
+
+
+def test_causal_d128_f32():
+    run_bwd(1, 2, 1, 600, 128, "f32", 8, 2, 2, causal=True, block=64, seed=28)
+
+
 def test_fewer_rows_than_clusters():
     # N < C: single-row clusters, far and retrieved
     run_bwd(1, 2, 1, 5, 64, "bf16", 16, 2, 3, seed=25)
