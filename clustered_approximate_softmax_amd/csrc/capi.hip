@@ -342,8 +342,7 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
                            (int32_t*)(wb + L.ws_pcnt), st)) != hipSuccess)
       return hip_fail(e);
     if ((e = launch_summarize(pl, (int)dtype, ks, V, ab.kst, st)) != hipSuccess) return hip_fail(e);
-    if ((e = launch_score_topk(pl, ab, st)) != hipSuccess) return hip_fail(e);
-    if ((e = launch_tilt(pl, (int)dtype, ab, st)) != hipSuccess) return hip_fail(e);
+    if ((e = launch_score_tilt(pl, (int)dtype, ab, st)) != hipSuccess) return hip_fail(e);
   }
   if ((e = launch_attn(pl, (int)dtype, ab, st)) != hipSuccess) return hip_fail(e);
   return MUSE_OK;

@@ -60,6 +60,7 @@ struct AttnBufs {
 };
 hipError_t launch_score_topk(const Plan& pl, const AttnBufs& b, hipStream_t st);
 hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
+hipError_t launch_score_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
 hipError_t launch_attn(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
 
 // Backward with the forward's clustering state held fixed.

@@ -12,9 +12,9 @@
 
 namespace muse {
 
-// One wave per (attention problem, query cluster).
-__global__ void __launch_bounds__(256) score_topk_kernel(Plan pl, AttnBufs b) {
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+// One wave per (attention problem, query cluster); wave-level only (no
+// workgroup barriers), so any workgroup can run it.
+__device__ __forceinline__ void score_topk_wave(const Plan& pl, const AttnBufs& b, int wave) {
   const int lane = threadIdx.x & 63;
   const int C = pl.C, D = pl.D;
   const int nprob = pl.B * pl.Hq * pl.P;
@@ -98,6 +98,10 @@ __global__ void __launch_bounds__(256) score_topk_kernel(Plan pl, AttnBufs b) {
     base += __popcll(bal);
   }
   for (int q = base + lane; q < pl.k1w; q += 64) R[q] = -1;
+}
+
+__global__ void __launch_bounds__(256) score_topk_kernel(Plan pl, AttnBufs b) {
+  score_topk_wave(pl, b, blockIdx.x * 4 + (threadIdx.x >> 6));
 }
 
 // Same scores and sets for top-k1 <= KMAX: one workgroup per attention
@@ -346,15 +350,14 @@ __device__ __forceinline__ void tilt_dim(const SM& sm, const float* Mk, const fl
   }
 }
 
+// Workgroup blk of the tilt grid (the grid's XCD order: blk % 8 = XCD).
 template <typename TIn, int D, int NS>
-__global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b, int tb, long long kps) {
-  using SM = TiltSmem<TIn, D, NS>;
-  extern __shared__ __align__(16) unsigned char tilt_raw[];
-  SM& sm = *reinterpret_cast<SM*>(tilt_raw);
+__device__ __forceinline__ void tilt_block(const Plan& pl, const AttnBufs& b, int tb, long long kps, int blk,
+                                           TiltSmem<TIn, D, NS>& sm) {
   const int NDB = D / tb;
   const int C = pl.C, Cp = b.Cp32, Gq = pl.Hq / pl.Hkv;
   const int per = Gq * NDB;                       // workgroups per key problem
-  const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
+  const int xcd = blk % 8, loc = blk / 8;
   const long long kp = (long long)(loc / per) * 8 + xcd;
   if (kp >= kps) return;
   const int u = loc % per;
@@ -400,6 +403,25 @@ __global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b, int tb, 
 }
 
 template <typename TIn, int D, int NS>
+__global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b, int tb, long long kps) {
+  extern __shared__ __align__(16) unsigned char tilt_raw[];
+  tilt_block<TIn, D, NS>(pl, b, tb, kps, (int)blockIdx.x, *reinterpret_cast<TiltSmem<TIn, D, NS>*>(tilt_raw));
+}
+
+// Scores / top-k and tilted summaries in one launch (they are independent):
+// the first nsb workgroups score (4 waves each), the rest tilt.  nsb is a
+// multiple of 8, so the tilt workgroups keep their XCD order.
+template <typename TIn, int D, int NS>
+__global__ void __launch_bounds__(256) score_tilt_kernel(Plan pl, AttnBufs b, int tb, long long kps, int nsb) {
+  extern __shared__ __align__(16) unsigned char st_raw[];
+  if ((int)blockIdx.x < nsb) {
+    score_topk_wave(pl, b, blockIdx.x * 4 + (threadIdx.x >> 6));
+    return;
+  }
+  tilt_block<TIn, D, NS>(pl, b, tb, kps, (int)blockIdx.x - nsb, *reinterpret_cast<TiltSmem<TIn, D, NS>*>(st_raw));
+}
+
+template <typename TIn, int D, int NS>
 static void tilt_go(const Plan& pl, const AttnBufs& b, long long kps, int tb, hipStream_t st) {
   using SM = TiltSmem<TIn, D, NS>;
   const int per = (pl.Hq / pl.Hkv) * (pl.D / tb);
@@ -408,13 +430,27 @@ static void tilt_go(const Plan& pl, const AttnBufs& b, long long kps, int tb, hi
   tilt_kernel<TIn, D, NS><<<grid, 256, sizeof(SM), st>>>(pl, b, tb, kps);
 }
 
-hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st) {
-  const long long kps = (long long)pl.B * pl.Hkv * pl.P;
-  if (kps == 0) return hipSuccess;
-  // dims per workgroup: up to 4, fewer when that leaves the chip under-filled
+// value dims per tilt workgroup: up to 4, fewer when that leaves the chip under-filled
+static int tilt_dims(const Plan& pl, long long kps) {
   const long long heads = kps * (pl.Hq / pl.Hkv);
   int tb = 4;
   while (tb > 1 && heads * (pl.D / tb) < 2048) tb /= 2;
+  return tb;
+}
+
+template <typename TIn, int D, int NS>
+static void score_tilt_go(const Plan& pl, const AttnBufs& b, long long kps, int tb, int nsb, hipStream_t st) {
+  using SM = TiltSmem<TIn, D, NS>;
+  const int per = (pl.Hq / pl.Hkv) * (pl.D / tb);
+  const unsigned grid = (unsigned)(nsb + ((kps + 7) / 8) * 8 * per);
+  set_smem_once((const void*)score_tilt_kernel<TIn, D, NS>, sizeof(SM));
+  score_tilt_kernel<TIn, D, NS><<<grid, 256, sizeof(SM), st>>>(pl, b, tb, kps, nsb);
+}
+
+hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st) {
+  const long long kps = (long long)pl.B * pl.Hkv * pl.P;
+  if (kps == 0) return hipSuccess;
+  const int tb = tilt_dims(pl, kps);
   MUSE_KT_PRE(st);
   if (dtype == 1) {
     if (pl.D == 64) tilt_go<uint16_t, 64, 1>(pl, b, kps, tb, st);
@@ -424,6 +460,31 @@ hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t
     else tilt_go<float, 128, 3>(pl, b, kps, tb, st);
   }
   MUSE_KT_POST("tilt", st);
+  return hipGetLastError();
+}
+
+// Scores / top-k and tilted summaries of a forward.  They are independent, so
+// they share one launch, except when the per-problem score kernel applies.
+hipError_t launch_score_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st) {
+  const long long waves = (long long)pl.B * pl.Hq * pl.P * pl.C;
+  const long long kps = (long long)pl.B * pl.Hkv * pl.P;
+  const bool rows = pl.topk <= 16 && (long long)pl.B * pl.Hq * pl.P >= 512;
+  if (rows || waves == 0 || kps == 0) {
+    const hipError_t e = launch_score_topk(pl, b, st);
+    if (e != hipSuccess) return e;
+    return launch_tilt(pl, dtype, b, st);
+  }
+  const int tb = tilt_dims(pl, kps);
+  const int nsb = (int)(((waves + 3) / 4 + 7) / 8 * 8);   // score workgroups, a multiple of 8
+  MUSE_KT_PRE(st);
+  if (dtype == 1) {
+    if (pl.D == 64) score_tilt_go<uint16_t, 64, 1>(pl, b, kps, tb, nsb, st);
+    else score_tilt_go<uint16_t, 128, 1>(pl, b, kps, tb, nsb, st);
+  } else {
+    if (pl.D == 64) score_tilt_go<float, 64, 3>(pl, b, kps, tb, nsb, st);
+    else score_tilt_go<float, 128, 3>(pl, b, kps, tb, nsb, st);
+  }
+  MUSE_KT_POST("score_tilt", st);
   return hipGetLastError();
 }
 
