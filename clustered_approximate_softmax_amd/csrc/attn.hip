@@ -42,6 +42,7 @@
 // LDS feeds QG matrix instructions.
 #include "common.h"
 #include "launch.h"
+#include "vt.h"
 
 namespace muse {
 
@@ -890,59 +891,21 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   }
 }
 
-// Dim-major copies of the values: slice s < nsorted is the cluster-contiguous
-// copy of level/head s, the next B*Hkv slices are the input V.  Vt[s][d][j]
-// = V_s[j][d] for the rows j that hold values, zero for the others and for
-// N <= j < Nv.
 template <typename TIn, int D>
 __global__ void __launch_bounds__(256) vt_kernel(Plan pl, const void* Vp, const void* V, void* Vt, int Nv,
                                                  int nsorted, int sfirst) {
-  const int N = pl.N;
-  constexpr int E = 16 / (int)sizeof(TIn), CH = D / E;
-  using V16 = typename std::conditional<sizeof(TIn) == 2, u16x8, f32x4>::type;
-  __shared__ TIn tile[AT_KT][D + 2];
-  const int nb = (Nv + AT_KT - 1) / AT_KT;
-  const int s = sfirst + (int)(blockIdx.x / nb), blk = blockIdx.x % nb;
-  const TIn* src = s < nsorted ? reinterpret_cast<const TIn*>(Vp) + (size_t)s * N * D
-                               : reinterpret_cast<const TIn*>(V) + (size_t)(s - nsorted) * N * D;
-  TIn* dst = reinterpret_cast<TIn*>(Vt) + (size_t)s * D * Nv;
-  const int j0 = blk * AT_KT;
-  // causal levels: only the key segments [2tm, 2tm + m), t < nseg, of a
-  // level's sorted copy are written; every other column becomes zero
-  const int lev = s < nsorted && pl.causal ? s / (pl.B * pl.Hkv) : -1;
-  const int m = lev >= 0 ? pl.lev_m[lev] : 0, nseg = lev >= 0 ? pl.lev_nseg[lev] : 0;
-  for (int idx = threadIdx.x; idx < AT_KT * CH; idx += 256) {
-    const int r = idx / CH, e0 = (idx % CH) * E;
-    const int j = j0 + r;
-    V16 v{};
-    if (j < N && (m == 0 || ((j / m) % 2 == 0 && j / (2 * m) < nseg)))
-      v = *reinterpret_cast<const V16*>(src + (size_t)j * D + e0);
-#pragma unroll
-    for (int e = 0; e < E; ++e) tile[r][e0 + e] = v[e];
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < D * (AT_KT / E); idx += 256) {
-    const int d = idx / (AT_KT / E), jj = (idx % (AT_KT / E)) * E;
-    if (j0 + jj >= Nv) continue;
-    V16 v;
-#pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = tile[jj + e][d];
-    *reinterpret_cast<V16*>(dst + (size_t)d * Nv + j0 + jj) = v;
-  }
+  __shared__ TIn tile[VT_ROWS][D + 2];
+  vt_block<TIn, D>(pl, Vp, V, Vt, Nv, nsorted, sfirst, (int)blockIdx.x, tile);
 }
 
 // ---------------------------------------------------------------------------
 template <typename TIn, int D>
 static hipError_t launch_vt(const Plan& pl, const AttnBufs& b, hipStream_t st) {
-  const int nsorted = pl.nlev * pl.B * pl.Hkv;
-  // without retrieval no tile reads the sorted copies: only the input-order
-  // slices (causal local blocks) are needed
-  const int sfirst = pl.topk > 0 ? 0 : nsorted;
-  const int nslice = nsorted + (pl.causal ? pl.B * pl.Hkv : 0) - sfirst;
-  const long long grid = (long long)nslice * ((b.Nv + AT_KT - 1) / AT_KT);
+  const VtGeo g = vt_geo(pl, b.Nv);
+  const long long grid = (long long)g.nslice * g.nb;
   if (grid == 0) return hipSuccess;
   MUSE_KT_PRE(st);
-  vt_kernel<TIn, D><<<(unsigned)grid, 256, 0, st>>>(pl, b.kst.Vp, b.V, b.Vt, b.Nv, nsorted, sfirst);
+  vt_kernel<TIn, D><<<(unsigned)grid, 256, 0, st>>>(pl, b.kst.Vp, b.V, b.Vt, b.Nv, g.nsorted, g.sfirst);
   MUSE_KT_POST("value_transpose", st);
   return hipGetLastError();
 }
@@ -966,8 +929,8 @@ static hipError_t attn_level(const Plan& pl, const AttnBufs& b, int lev, hipStre
 }
 
 template <typename TIn, int D>
-static hipError_t attn_all(const Plan& pl, const AttnBufs& b, hipStream_t st) {
-  hipError_t e = launch_vt<TIn, D>(pl, b, st);
+static hipError_t attn_all(const Plan& pl, const AttnBufs& b, bool vt_done, hipStream_t st) {
+  hipError_t e = vt_done ? hipSuccess : launch_vt<TIn, D>(pl, b, st);
   if (e != hipSuccess) return e;
   // Every launch keeps one group of 16 queries per wave: two groups halve the
   // LDS fragment reads per MFMA but need about 200 VGPRs (285 at D = 128),
@@ -994,9 +957,10 @@ static hipError_t attn_all(const Plan& pl, const AttnBufs& b, hipStream_t st) {
   return e;
 }
 
-hipError_t launch_attn(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st) {
-  if (dtype == 1) return pl.D == 64 ? attn_all<uint16_t, 64>(pl, b, st) : attn_all<uint16_t, 128>(pl, b, st);
-  return pl.D == 64 ? attn_all<float, 64>(pl, b, st) : attn_all<float, 128>(pl, b, st);
+hipError_t launch_attn(const Plan& pl, int dtype, const AttnBufs& b, bool vt_done, hipStream_t st) {
+  if (dtype == 1)
+    return pl.D == 64 ? attn_all<uint16_t, 64>(pl, b, vt_done, st) : attn_all<uint16_t, 128>(pl, b, vt_done, st);
+  return pl.D == 64 ? attn_all<float, 64>(pl, b, vt_done, st) : attn_all<float, 128>(pl, b, vt_done, st);
 }
 
 }  // namespace muse

@@ -337,14 +337,15 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
   ab.lse = lse;
   hipError_t e = hipGetLastError();  // clear stale errors from earlier calls
   (void)e;
+  bool vt_done = false;   // the value copies built with the scores
   if (pl.P > 0) {
     if ((e = launch_kmeans(pl, (int)dtype, qs, ks, lay.plocal, lay.lg, (float*)(wb + L.ws_part),
                            (int32_t*)(wb + L.ws_pcnt), st)) != hipSuccess)
       return hip_fail(e);
     if ((e = launch_summarize(pl, (int)dtype, ks, V, ab.kst, st)) != hipSuccess) return hip_fail(e);
-    if ((e = launch_score_tilt(pl, (int)dtype, ab, st)) != hipSuccess) return hip_fail(e);
+    if ((e = launch_score_tilt(pl, (int)dtype, ab, vt_done, st)) != hipSuccess) return hip_fail(e);
   }
-  if ((e = launch_attn(pl, (int)dtype, ab, st)) != hipSuccess) return hip_fail(e);
+  if ((e = launch_attn(pl, (int)dtype, ab, vt_done, st)) != hipSuccess) return hip_fail(e);
   return MUSE_OK;
 }
 

@@ -60,8 +60,8 @@ struct AttnBufs {
 };
 hipError_t launch_score_topk(const Plan& pl, const AttnBufs& b, hipStream_t st);
 hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
-hipError_t launch_score_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
-hipError_t launch_attn(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
+hipError_t launch_score_tilt(const Plan& pl, int dtype, const AttnBufs& b, bool& vt_done, hipStream_t st);
+hipError_t launch_attn(const Plan& pl, int dtype, const AttnBufs& b, bool vt_done, hipStream_t st);
 
 // Backward with the forward's clustering state held fixed.
 struct BwdLaunch {

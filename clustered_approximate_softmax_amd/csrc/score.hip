@@ -9,6 +9,7 @@
 //     query-cluster centroid; newx.sg page, Abstract).
 #include "common.h"
 #include "launch.h"
+#include "vt.h"
 
 namespace muse {
 
@@ -408,17 +409,25 @@ __global__ void __launch_bounds__(256) tilt_kernel(Plan pl, AttnBufs b, int tb, 
   tilt_block<TIn, D, NS>(pl, b, tb, kps, (int)blockIdx.x, *reinterpret_cast<TiltSmem<TIn, D, NS>*>(tilt_raw));
 }
 
-// Scores / top-k and tilted summaries in one launch (they are independent):
-// the first nsb workgroups score (4 waves each), the rest tilt.  nsb is a
-// multiple of 8, so the tilt workgroups keep their XCD order.
+// Scores / top-k, tilted summaries and the dim-major value copies in one
+// launch (they are independent): the first nsb workgroups score (4 waves
+// each), the next ntb tilt, the rest transpose values through the same LDS.
+// nsb is a multiple of 8, so the tilt workgroups keep their XCD order.
 template <typename TIn, int D, int NS>
-__global__ void __launch_bounds__(256) score_tilt_kernel(Plan pl, AttnBufs b, int tb, long long kps, int nsb) {
+__global__ void __launch_bounds__(256) score_tilt_kernel(Plan pl, AttnBufs b, int tb, long long kps, int nsb,
+                                                         int ntb, int nsorted, int sfirst) {
   extern __shared__ __align__(16) unsigned char st_raw[];
-  if ((int)blockIdx.x < nsb) {
-    score_topk_wave(pl, b, blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int blk = (int)blockIdx.x;
+  if (blk < nsb) {
+    score_topk_wave(pl, b, blk * 4 + (threadIdx.x >> 6));
     return;
   }
-  tilt_block<TIn, D, NS>(pl, b, tb, kps, (int)blockIdx.x - nsb, *reinterpret_cast<TiltSmem<TIn, D, NS>*>(st_raw));
+  if (blk < nsb + ntb) {
+    tilt_block<TIn, D, NS>(pl, b, tb, kps, blk - nsb, *reinterpret_cast<TiltSmem<TIn, D, NS>*>(st_raw));
+    return;
+  }
+  vt_block<TIn, D>(pl, b.kst.Vp, b.V, b.Vt, b.Nv, nsorted, sfirst, blk - nsb - ntb,
+                   reinterpret_cast<TIn(*)[D + 2]>(st_raw));
 }
 
 template <typename TIn, int D, int NS>
@@ -440,11 +449,13 @@ static int tilt_dims(const Plan& pl, long long kps) {
 
 template <typename TIn, int D, int NS>
 static void score_tilt_go(const Plan& pl, const AttnBufs& b, long long kps, int tb, int nsb, hipStream_t st) {
-  using SM = TiltSmem<TIn, D, NS>;
+  constexpr size_t smem = std::max(sizeof(TiltSmem<TIn, D, NS>), sizeof(TIn) * VT_ROWS * (D + 2));
   const int per = (pl.Hq / pl.Hkv) * (pl.D / tb);
-  const unsigned grid = (unsigned)(nsb + ((kps + 7) / 8) * 8 * per);
-  set_smem_once((const void*)score_tilt_kernel<TIn, D, NS>, sizeof(SM));
-  score_tilt_kernel<TIn, D, NS><<<grid, 256, sizeof(SM), st>>>(pl, b, tb, kps, nsb);
+  const int ntb = (int)(((kps + 7) / 8) * 8 * per);
+  const VtGeo g = vt_geo(pl, b.Nv);
+  const unsigned grid = (unsigned)(nsb + ntb + (long long)g.nslice * g.nb);
+  set_smem_once((const void*)score_tilt_kernel<TIn, D, NS>, smem);
+  score_tilt_kernel<TIn, D, NS><<<grid, 256, smem, st>>>(pl, b, tb, kps, nsb, ntb, g.nsorted, g.sfirst);
 }
 
 hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st) {
@@ -463,9 +474,11 @@ hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t
   return hipGetLastError();
 }
 
-// Scores / top-k and tilted summaries of a forward.  They are independent, so
-// they share one launch, except when the per-problem score kernel applies.
-hipError_t launch_score_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st) {
+// Scores / top-k, tilted summaries and (vt_done) the dim-major value copies of
+// a forward.  They are independent, so they share one launch, except when the
+// per-problem score kernel applies.
+hipError_t launch_score_tilt(const Plan& pl, int dtype, const AttnBufs& b, bool& vt_done, hipStream_t st) {
+  vt_done = false;
   const long long waves = (long long)pl.B * pl.Hq * pl.P * pl.C;
   const long long kps = (long long)pl.B * pl.Hkv * pl.P;
   const bool rows = pl.topk <= 16 && (long long)pl.B * pl.Hq * pl.P >= 512;
@@ -485,6 +498,7 @@ hipError_t launch_score_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipSt
     else score_tilt_go<float, 128, 3>(pl, b, kps, tb, nsb, st);
   }
   MUSE_KT_POST("score_tilt", st);
+  vt_done = true;
   return hipGetLastError();
 }
 
