@@ -82,6 +82,19 @@ def test_kmeans_default_init_and_determinism():
     gu.check_labels(X[0], X[0][mo.default_init(4096, 32)], a1[0])
 
 
+@pytest.mark.parametrize("n,C,D,dtype", [(3001, 48, 64, "bf16"), (1000, 7, 128, "f32"), (10, 4, 64, "bf16")])
+def test_kmeans_default_init_where_rounding_order_matters(n, C, D, dtype):
+    """No initial indices: the library starts from the points floor(c n / C)
+    (c * floor(n / C) would differ at these sizes); the first assignment and
+    update then match one oracle Lloyd step from those points."""
+    X = _points(1, n, D, dtype, comps=max(4, C // 2), seed=n + C)
+    a, cent, _, _ = (t.cpu().numpy() for t in M.musecluster(gu.to_dev(X, dtype), C, 1))
+    start = X[0][mo.default_init(n, C)].astype(np.float64)
+    gu.check_labels(X[0], start, a[0])
+    want = mo.update_step(X[0], a[0], start)
+    np.testing.assert_allclose(cent[0, :C], want, rtol=0, atol=2e-6 * np.abs(X[0]).max())
+
+
 @pytest.mark.parametrize("G,n,D,C,dtype", [(2, 700, 64, 16, "f32"), (2, 3000, 64, 64, "bf16"),
                                            (1, 500, 128, 100, "bf16"), (1, 64, 64, 32, "f32"),
                                            # clusters of over a thousand keys: many tiles, ragged tail

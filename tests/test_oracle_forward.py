@@ -47,6 +47,64 @@ def test_hand_derived_cases(case):
     np.testing.assert_allclose(r.lse, want_l, rtol=1e-13, atol=1e-13)
 
 
+def _golden_retrieval():
+    with open(os.path.join(HERE, "golden", "hand_retrieval_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_retrieval(), ids=lambda c: c["name"])
+def test_hand_derived_retrieval_cases(case):
+    """The cluster score's log-count and scale each decide a retrieval."""
+    env = {"exp": math.exp, "log": math.log, "__builtins__": {}}
+    Q, K, V = (np.array(case[k], float) for k in ("Q", "K", "V"))
+    r = mo.solve_problem(Q, K, V, case["scale"], case["cq"], case["ck"], case["topk"],
+                         case["iters"], case["init_q"], case["init_k"])
+    assert r.ak.tolist() == case["labels_k"]
+    want_sig = np.array([[eval(e, env) for e in row] for row in case["sigma"]])
+    np.testing.assert_allclose(r.sigma, want_sig, rtol=1e-14, atol=1e-14)
+    assert [sorted(x.tolist()) for x in r.R] == case["retrieved"]
+    want_o = np.array([[eval(e, env) for e in row] for row in case["o"]])
+    want_l = np.array([eval(e, env) for e in case["lse"]])
+    np.testing.assert_allclose(r.o, want_o, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(r.lse, want_l, rtol=1e-13, atol=1e-13)
+
+
+# -- the retrieval score is the log of the monopole tilted mass -------------------
+@pytest.mark.parametrize("seed", range(3))
+def test_cluster_score_is_log_tilted_mass_at_zero_spread(seed):
+    """With every key of a cluster at its centroid, sigma_Ic is exactly the
+    brute-force log sum_{j in c} exp(s nu_I.k_j); with spread, Jensen's
+    inequality makes sigma_Ic a lower bound of it."""
+    rng = np.random.default_rng(100 + seed)
+    D, Ck, Cq = 5, 6, 4
+    s = [0.3, 1.0, 2.5][seed]
+    centres = rng.standard_normal((Ck, D))
+    sizes = rng.integers(1, 9, Ck)
+    lab = np.repeat(np.arange(Ck), sizes)
+    nu = rng.standard_normal((Cq, D))
+    for spread in (0.0, 0.4):
+        K = centres[lab] + spread * rng.standard_normal((len(lab), D))
+        n, mu, _, _ = mo.key_stats(K, np.zeros_like(K), lab, Ck)
+        sig = mo.cluster_scores(nu, mu, n, s)
+        for I in range(Cq):
+            for c in range(Ck):
+                lg = s * (K[lab == c] @ nu[I])
+                brute = lg.max() + math.log(np.exp(lg - lg.max()).sum())
+                if spread == 0.0:
+                    assert abs(sig[I, c] - brute) <= 1e-12 * max(1.0, abs(brute))
+                else:
+                    assert sig[I, c] <= brute + 1e-12
+
+
+def test_cluster_score_empty_cluster_is_never_selected():
+    n = np.array([3, 0, 2])
+    mu = np.array([[0.0, 0.0], [50.0, 0.0], [1.0, 0.0]])
+    sig = mo.cluster_scores(np.array([[1.0, 0.0]]), mu, n, 1.0)
+    assert sig[0, 1] == -np.inf
+    assert mo.select_topk(sig[0], 2).tolist() == [0, 2]
+    assert mo.select_topk(sig[0], 5).tolist() == [0, 2]
+
+
 # -- (a) singleton key clusters reproduce brute-force softmax ---------------------
 @pytest.mark.parametrize("seed", range(4))
 def test_singleton_key_clusters_are_exact(seed):

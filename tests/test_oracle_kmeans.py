@@ -77,3 +77,13 @@ def test_default_init_is_distinct_and_in_range():
     for n, C in [(1, 1), (5, 5), (1000, 16), (1024, 128), (17, 16)]:
         ii = mo.default_init(n, C)
         assert len(set(ii.tolist())) == C and ii.min() >= 0 and ii.max() < n
+
+
+def test_default_init_is_floor_of_c_n_over_C():
+    """The default starting points are evenly spread, floor(c n / C); the
+    values below are written out by hand at sizes where the rounding order
+    matters (c * floor(n / C) gives 0, 2, 4, 6 for n = 10, C = 4)."""
+    assert mo.default_init(10, 4).tolist() == [0, 2, 5, 7]
+    assert mo.default_init(1000, 7).tolist() == [0, 142, 285, 428, 571, 714, 857]
+    assert mo.default_init(5, 3).tolist() == [0, 1, 3]
+    assert mo.default_init(4, 4).tolist() == [0, 1, 2, 3]
