@@ -641,3 +641,101 @@ def backward_query_rows(Qh, Kh, Vh, dOh, cfg: MuseConfig, O, lse, shared, rows):
             dl = pe * (Vh[b0:i + 1] @ dOh[i] - np.dot(dOh[i], O[i]))
             out[k] += s * (dl @ Kh[b0:i + 1])
     return out
+
+
+def rows_read_by_key_backward(N, cfg: MuseConfig, rows):
+    """The query rows whose O and lse ``backward_key_rows`` reads for the
+    given key rows: every query of each problem holding one of them as a
+    key (the far-field gradients of a key cluster sum over all queries of
+    its problem) and, when causal, the rows of its local block at or after
+    it."""
+    plan = causal_plan(N, cfg.block) if cfg.causal else acausal_plan(N)
+    need = set()
+    for pr in plan:
+        k0, kn, q0, qn = pr["k0"], pr["kn"], pr["q0"], pr["qn"]
+        if any(k0 <= int(j) < k0 + kn for j in rows):
+            need.update(range(q0, q0 + qn))
+    if cfg.causal:
+        for j in rows:
+            j = int(j)
+            b1 = min((j // cfg.block + 1) * cfg.block, N)
+            need.update(range(j, b1))
+    return np.array(sorted(need), np.int64)
+
+
+def backward_key_rows(Qg, Kh, Vh, dOg, cfg: MuseConfig, Og, lseg, shared_g, rows):
+    """dK and dV of one KV head at key ``rows`` only, summed over the query
+    heads that read it, from the same formulas as ``backward_problem`` and
+    ``local_backward`` (O9, with assignments, retrieval sets and counts
+    fixed as in ``shared_g``).
+
+    Qg, dOg, Og: [G, N, D] of the G query heads of the group; lseg [G, N];
+    shared_g: list over those heads of dicts problem -> (aq, ak, R).  O and
+    lse are read only at ``rows_read_by_key_backward``.  For key j of cluster
+    c in a problem: dV_j = sum_i p_ij dO_i + dS_c + dM_c (k_j - mu_c) and
+    dK_j = s sum_i dl_ij q_i + dM_c^T (v_j - S_c / n_c) + dmu_c / n_c, the
+    exact sums over the queries whose cluster retrieved c, the cluster
+    gradients dS_c, dM_c, dmu_c over the queries that see c as a far item.
+    """
+    Kh = np.asarray(Kh, np.float64)
+    Vh = np.asarray(Vh, np.float64)
+    N, D = Kh.shape
+    s = cfg.s(D)
+    rows = np.asarray(rows, np.int64)
+    dK = np.zeros((len(rows), D))
+    dV = np.zeros((len(rows), Vh.shape[1]))
+    plan = causal_plan(N, cfg.block) if cfg.causal else acausal_plan(N)
+    for hq in range(len(Qg)):
+        Qh = np.asarray(Qg[hq], np.float64)
+        dOh = np.asarray(dOg[hq], np.float64)
+        Oh = np.asarray(Og[hq], np.float64)
+        lse = np.asarray(lseg[hq], np.float64)
+        for p, pr in enumerate(plan):
+            q0, qn, k0, kn = pr["q0"], pr["qn"], pr["k0"], pr["kn"]
+            here = [(k, int(j) - k0) for k, j in enumerate(rows) if k0 <= j < k0 + kn]
+            if not here:
+                continue
+            aq, ak, R = shared_g[hq][p]
+            aq, ak = np.asarray(aq), np.asarray(ak)
+            Cq, Ck = min(cfg.cq, qn), min(cfg.ck, kn)
+            K, V, Q = Kh[k0:k0 + kn], Vh[k0:k0 + kn], Qh[q0:q0 + qn]
+            dO = dOh[q0:q0 + qn]
+            L = lse[q0:q0 + qn]
+            Delta = np.sum(dO * Oh[q0:q0 + qn], axis=1)
+            n, mu, S, M = key_stats(K, V, ak, Ck)
+            m, nu = query_stats(Q, aq, Cq)
+            T = tilted_summaries(S, M, nu, s, cfg.dipole)
+            for c in sorted(set(int(ak[j]) for _, j in here)):
+                # queries that retrieved c (exact) and those that see it far
+                ret = np.array([I for I in range(Cq) if m[I] > 0 and c in set(int(x) for x in R[I])],
+                               np.int64)
+                far = np.array([I for I in range(Cq) if m[I] > 0 and I not in set(ret.tolist())],
+                               np.int64)
+                qe = np.nonzero(np.isin(aq, ret))[0]
+                dT = np.zeros((Cq, V.shape[1]))
+                dmu = np.zeros(D)
+                for I in far:
+                    mem = np.nonzero(aq == I)[0]
+                    rho = np.exp(s * (Q[mem] @ mu[c]) - L[mem])
+                    dlam = rho * (dO[mem] @ T[I, c] - n[c] * Delta[mem])
+                    dT[I] = rho @ dO[mem]
+                    dmu += s * (dlam @ Q[mem])
+                dS = dT.sum(axis=0)
+                dM = s * (dT.T @ nu) if cfg.dipole else np.zeros((V.shape[1], D))
+                for k, j in here:
+                    if ak[j] != c:
+                        continue
+                    pe = np.exp(s * (Q[qe] @ K[j]) - L[qe])
+                    dl = pe * (dO[qe] @ V[j] - Delta[qe])
+                    dV[k] += pe @ dO[qe] + dS + dM @ (K[j] - mu[c])
+                    dK[k] += s * (dl @ Q[qe]) + dM.T @ (V[j] - S[c] / n[c]) + dmu / n[c]
+        if cfg.causal:
+            for k, j in enumerate(rows):
+                j = int(j)
+                b1 = min((j // cfg.block + 1) * cfg.block, N)
+                qi = np.arange(j, b1)
+                pe = np.exp(s * (Qh[qi] @ Kh[j]) - lse[qi])
+                dl = pe * (dOh[qi] @ Vh[j] - np.sum(dOh[qi] * Oh[qi], axis=1))
+                dV[k] += pe @ dOh[qi]
+                dK[k] += s * (dl @ Qh[qi])
+    return dK, dV

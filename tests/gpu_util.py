@@ -35,7 +35,9 @@ def check_labels(X, mu_prev, labels, tie=TIE):
     relative distance ties; returns the number of tie-tolerated flips."""
     X = np.asarray(X, np.float64)
     mu_prev = np.asarray(mu_prev, np.float64)
-    d = ((X[:, None, :] - mu_prev[None]) ** 2).sum(-1)
+    d = np.empty((X.shape[0], mu_prev.shape[0]))
+    for r0 in range(0, X.shape[0], 512):
+        d[r0:r0 + 512] = ((X[r0:r0 + 512, None, :] - mu_prev[None]) ** 2).sum(-1)
     want = np.argmin(d, axis=1)
     bad = np.nonzero(labels != want)[0]
     for j in bad:
@@ -83,6 +85,17 @@ def check_retrieval(results, shared, k1, tie=TIE):
                 lo = min(sig[c] for c in sel)
                 hi = max(sig[c] for c in valid if c not in sel)
                 assert hi <= lo + tie * max(abs(lo), abs(hi), 1.0), (bh, p, I, lo, hi)
+
+
+def check_lse(got, ref, dtype, what=""):
+    """lse per (batch, head) within the output tolerance relative to the
+    largest |lse| of that head: |lse_gpu - lse_ref| <= TOL * max |lse_ref|."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bound = TOL[dtype] * max(float(np.max(np.abs(ref))), 1e-30)
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= bound, (what, err, bound)
+    return err
 
 
 def max_rel(a, b):

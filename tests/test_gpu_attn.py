@@ -44,7 +44,7 @@ def run_case(B, Hq, Hkv, N, D, dtype, C, iters, topk, causal=False, block=0, dip
         for h in range(Hq):
             e = gu.max_rel(O[b, h], Or[b, h])
             assert e <= gu.TOL[dtype], (b, h, e)
-            np.testing.assert_allclose(lse[b, h], Lr[b, h], atol=50 * gu.TOL[dtype])
+            gu.check_lse(lse[b, h], Lr[b, h], dtype, (b, h))
     gu.check_retrieval(res, shared, topk)
     return dict(x=x, O=O, lse=lse, state=st, shared=shared, res=res, cfg=cfg, ocfg=ocfg, rows=rows,
                 inits=inits, Or=Or)

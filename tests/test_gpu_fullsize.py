@@ -48,7 +48,7 @@ def _run_full(name, heads, nrows):
         Og = O[b, h].float().cpu().numpy()
         err = gu.max_rel(Og[qrows], o_ref[qrows])
         assert err <= gu.TOL[w.dtype], (name, b, h, err)
-        np.testing.assert_allclose(lse[b, h].cpu().numpy()[qrows], l_ref[qrows], atol=50 * gu.TOL[w.dtype])
+        gu.check_lse(lse[b, h].cpu().numpy()[qrows], l_ref[qrows], w.dtype, (name, b, h))
         # retrieval validity, integer outputs and centroids of the problems touched
         for p, r in enumerate(res):
             if r is None:
@@ -91,22 +91,79 @@ def test_full_c5_causal_64k_gqa_d128_forward():
     _run_full("c5", [(0, 5)], 64)
 
 
-def test_full_c5_causal_64k_gqa_d128_backward():
-    """Fwd + bwd at 64k, D=128, GQA 32/8.  dQ at sampled rows (rows whose
-    causal levels differ) against the oracle's row-restricted backward; dK
-    and dV over whole KV heads through identities of the fixed-assignment
-    map that hold at any size: sum_j dV_j = sum_i dO_i, <dV, V> = sum_i
-    dO_i . O_i, sum_j dK_j = 0 and <dQ, Q> = <dK, K> per KV group."""
-    import time
+def test_full_c4_forward_clustering_lockstep():
+    """The forward's own clustering at the 64k GQA shape, every level: one
+    run with 9 Lloyd iterations and one with 10 (default starting points);
+    the oracle takes one Lloyd step from the 9-iteration centroids of two
+    query heads and two KV heads over all 63 problems each, and the GPU's
+    10th labels must be its nearest centroids except at 1e-5 distance
+    ties, its centroids the fp64 means of its members."""
+    import torch
+    w = synth.WORKLOADS["c4"]
+    x = synth.make_inputs(w, with_do=False)
+    Q, K, V = (torch.from_numpy(x[k]).to(torch.bfloat16).cuda() for k in "QKV")
+    rows_plan = M.plan(w.N, M.make_cfg(w.C, 1, w.topk, True, w.block))
+    got = {}
+    for t in (w.iters - 1, w.iters):
+        cfg = M.make_cfg(w.C, t, w.topk, True, w.block)
+        _, _, st = M.museattn_fwd(Q, K, V, cfg)
+        torch.cuda.synchronize()
+        got[t] = {f: st.field(f).cpu().numpy() for f in ("q_labels", "k_labels", "q_cent", "k_cent")}
+        del st
+    flips = 0
+    for side, h in (("q", 0), ("q", 31), ("k", 0), ("k", 7)):
+        X_all = (x["Q"] if side == "q" else x["K"])[0, h]
+        for p, (lev, t_, k0, kn, q0, qn) in enumerate(rows_plan):
+            r0, n = (q0, qn) if side == "q" else (k0, kn)
+            X = X_all[r0:r0 + n]
+            prev = got[w.iters - 1][f"{side}_cent"][h, p].astype(np.float64)
+            a = got[w.iters][f"{side}_labels"][lev, h, r0:r0 + n].astype(np.int64)
+            flips += gu.check_labels(X, prev, a)
+            want = mo.update_step(X, a, prev)
+            np.testing.assert_allclose(got[w.iters][f"{side}_cent"][h, p].astype(np.float64), want, rtol=0,
+                                       atol=3e-6 * max(1.0, np.abs(X).max()), err_msg=f"{side}{h} p{p}")
+    print("c4 lockstep, tie-tolerated flips:", flips)
 
+
+@pytest.fixture(scope="module")
+def c5_run():
+    """Fwd + bwd at 64k, D=128, GQA 32/8 (the training workload), once."""
     import torch
     w = synth.WORKLOADS["c5"]
+    print("c5: generating inputs", flush=True)
     x = synth.make_inputs(w, with_do=True)
     Q, K, V, dO = (torch.from_numpy(x[k]).to(torch.bfloat16).cuda() for k in ("Q", "K", "V", "dO"))
     cfg = M.make_cfg(w.C, w.iters, w.topk, w.causal, w.block)
+    print("c5: forward + backward on the GPU", flush=True)
     O, lse, st = M.museattn_fwd(Q, K, V, cfg)
     dQ, dK, dV = M.museattn_bwd(Q, K, V, O, lse, dO, cfg, st)
     torch.cuda.synchronize()
+    rows_plan = M.plan(w.N, cfg)
+    ql, kl, R = (st.field(f).cpu().numpy() for f in ("q_labels", "k_labels", "R"))
+    ocfg = mo.MuseConfig(cq=w.C, ck=w.C, iters=w.iters, topk=w.topk, block=w.block, causal=w.causal)
+
+    def shared_of(h):
+        g = (h * w.Hkv) // w.Hq
+        d = {}
+        for p, (lev, t, k0, kn, q0, qn) in enumerate(rows_plan):
+            Cq = min(w.C, qn)
+            Rp = [np.array(sorted(c for c in R[h, p, I] if c >= 0), np.int64) for I in range(Cq)]
+            d[p] = (ql[lev, h, q0:q0 + qn].astype(np.int64), kl[lev, g, k0:k0 + kn].astype(np.int64), Rp)
+        return d
+    out = dict(w=w, x=x, dev=(Q, K, V, dO, O), grads=(dQ, dK, dV), shared_of=shared_of, ocfg=ocfg)
+    yield out
+    del out, Q, K, V, dO, O, lse, st, dQ, dK, dV
+
+
+def test_full_c5_backward_identities(c5_run):
+    """dK and dV over whole KV heads through identities of the
+    fixed-assignment map that hold at any size: sum_j dV_j = sum_i dO_i,
+    <dV, V> = sum_i dO_i . O_i, sum_j dK_j = 0 and <dQ, Q> = <dK, K> per
+    KV group."""
+    import torch
+    w = c5_run["w"]
+    Q, K, V, dO, O = c5_run["dev"]
+    dQ, dK, dV = c5_run["grads"]
     for t in (dQ, dK, dV):
         assert bool(torch.isfinite(t.float()).all())
     Gq = w.Hq // w.Hkv
@@ -126,20 +183,21 @@ def test_full_c5_causal_64k_gqa_d128_backward():
         # O(lam Q, K / lam) = O(Q, K)
         a, b = float((dQ[0, hs].to(f64) * Q[0, hs].to(f64)).sum()), float((dk * kk).sum())
         assert abs(a - b) <= 2e-3 * float((dk * kk).abs().sum()), (g, a, b)
-    # sampled dQ rows of one head against the oracle
-    b, h = 0, 5
+
+
+@pytest.mark.parametrize("h", [5, 30])
+def test_full_c5_backward_dq_rows(c5_run, h):
+    """Sampled dQ rows of one query head (rows whose causal levels differ)
+    against the oracle's row-restricted backward, element by element."""
+    import time
+    w, x, ocfg = c5_run["w"], c5_run["x"], c5_run["ocfg"]
+    dQ = c5_run["grads"][0]
+    b = 0
     g = (h * w.Hkv) // w.Hq
-    rows_plan = M.plan(w.N, cfg)
-    ql, kl, R = (st.field(f).cpu().numpy() for f in ("q_labels", "k_labels", "R"))
-    shared = {}
-    for p, (lev, t, k0, kn, q0, qn) in enumerate(rows_plan):
-        Cq = min(w.C, qn)
-        Rp = [np.array(sorted(c for c in R[h, p, I] if c >= 0), np.int64) for I in range(Cq)]
-        shared[p] = (ql[lev, h, q0:q0 + qn].astype(np.int64), kl[lev, g, k0:k0 + kn].astype(np.int64), Rp)
-    ocfg = mo.MuseConfig(cq=w.C, ck=w.C, iters=w.iters, topk=w.topk, block=w.block, causal=w.causal)
+    shared = c5_run["shared_of"](h)
     # block indices 63, 42, 21, 1 take part in levels {0..5}, {1,3,5}, {0,2,4}, {0}
     rows = np.array([63 * 1024 + 1000, 42 * 1024 + 5, 21 * 1024 + 511, 1 * 1024 + 1023])
-    rows = np.concatenate([rows, np.random.default_rng(11).choice(w.N, 8, replace=False)])
+    rows = np.concatenate([rows, np.random.default_rng(11 + h).choice(w.N, 8, replace=False)])
     need = mo.rows_read_by_query_backward(w.N, ocfg, shared, rows)
     t0 = time.perf_counter()
     Qh, Kh, Vh, dOh = x["Q"][b, h], x["K"][b, g], x["V"][b, g], x["dO"][b, h]
@@ -147,6 +205,40 @@ def test_full_c5_causal_64k_gqa_d128_backward():
     dq_ref = mo.backward_query_rows(Qh, Kh, Vh, dOh, ocfg, o_ref, l_ref, shared, rows)
     got = dQ[b, h].float().cpu().numpy()[rows]
     err = gu.max_rel(got, dq_ref)
-    print(f"c5 dQ rows {rows.tolist()} ({len(need)} rows read, oracle {time.perf_counter() - t0:.1f} s): "
+    print(f"c5 dQ head {h} rows {rows.tolist()} ({len(need)} rows read, oracle {time.perf_counter() - t0:.1f} s): "
           f"max rel err {err:.3e}")
-    assert err <= 2e-2, err
+    assert err <= 1e-2, err
+
+
+@pytest.mark.parametrize("g", [0, 7])
+def test_full_c5_backward_dk_dv_rows(c5_run, g):
+    """dK and dV of sampled key rows of one KV head, summed over its four
+    query heads, element by element against the oracle's key-row-restricted
+    backward.  The rows are keys at levels 0 (block 62), 1 (block 61), 2
+    (block 59) and 3 (block 55), and a key of the last block that only its
+    local block reads; the oracle's O and lse of every query row they need
+    come from its own row-restricted forward."""
+    import time
+    w, x, ocfg = c5_run["w"], c5_run["x"], c5_run["ocfg"]
+    dK, dV = c5_run["grads"][1], c5_run["grads"][2]
+    Gq = w.Hq // w.Hkv
+    hs = list(range(g * Gq, (g + 1) * Gq))
+    rows = np.array([62 * 1024 + 5, 62 * 1024 + 1000, 61 * 1024 + 17, 59 * 1024 + 600, 55 * 1024 + 1023,
+                     63 * 1024 + 3])
+    need = mo.rows_read_by_key_backward(w.N, ocfg, rows)
+    t0 = time.perf_counter()
+    Og = np.zeros((Gq, w.N, w.D))
+    Lg = np.zeros((Gq, w.N))
+    shared = []
+    for k, h in enumerate(hs):
+        sh = c5_run["shared_of"](h)
+        shared.append(sh)
+        o_ref, l_ref, _ = mo.forward_head(x["Q"][0, h], x["K"][0, g], x["V"][0, g], ocfg, shared=sh, qrows=need)
+        Og[k], Lg[k] = o_ref, l_ref
+    gk, gv = mo.backward_key_rows(x["Q"][0, hs], x["K"][0, g], x["V"][0, g], x["dO"][0, hs], ocfg, Og, Lg,
+                                  shared, rows)
+    ek = gu.max_rel(dK[0, g].float().cpu().numpy()[rows], gk)
+    ev = gu.max_rel(dV[0, g].float().cpu().numpy()[rows], gv)
+    print(f"c5 KV head {g} key rows {rows.tolist()} ({len(need)} query rows read, oracle "
+          f"{time.perf_counter() - t0:.1f} s): max rel err dK {ek:.3e} dV {ev:.3e}")
+    assert ek <= 2e-2 and ev <= 2e-2, (ek, ev)

@@ -190,3 +190,25 @@ def test_backward_global_identities(causal):
                                    rtol=1e-10)
         np.testing.assert_allclose(sum(np.sum(dQ[0, h] * Q[0, h]) for h in hs), np.sum(dK[0, g] * K[0, g]),
                                    rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("causal,dipole", [(False, True), (True, True), (True, False)])
+def test_key_row_restricted_backward_equals_full_backward(causal, dipole):
+    """dK and dV at chosen key rows, summed over a GQA group, equal the full
+    backward's rows, with O and lse poisoned outside the rows it reads."""
+    Q, K, V, dO = _rand(13, B=1, Hq=4, Hkv=2, N=83, D=4)
+    cfg = mo.MuseConfig(cq=4, ck=3, iters=3, topk=1, block=8, causal=causal, scale=0.8, dipole=dipole)
+    O, L, res = mo.forward(Q, K, V, cfg)
+    _, dK, dV = mo.backward(Q, K, V, dO, cfg, O, L, res)
+    rows = [0, 7, 8, 31, 47, 64, 82]
+    need = mo.rows_read_by_key_backward(83, cfg, rows)
+    for g in range(2):
+        hs = [h for h in range(4) if (h * 2) // 4 == g]
+        Op = np.full((len(hs), 83, 4), np.nan)
+        Lp = np.full((len(hs), 83), np.nan)
+        for k, h in enumerate(hs):
+            Op[k, need], Lp[k, need] = O[0, h][need], L[0, h][need]
+        shared = [{p: (r.aq, r.ak, r.R) for p, r in enumerate(res[(0, h)])} for h in hs]
+        gk, gv = mo.backward_key_rows(Q[0, hs], K[0, g], V[0, g], dO[0, hs], cfg, Op, Lp, shared, rows)
+        np.testing.assert_allclose(gk, dK[0, g][rows], atol=1e-12)
+        np.testing.assert_allclose(gv, dV[0, g][rows], atol=1e-12)
