@@ -2,19 +2,24 @@
 
 A step is one museattn_fwd call over the whole workload tensor (all batch x
 heads, clustering included; input generation excluded), inputs resident in
-HBM; for the training workload (--config c5) a step is museattn_fwd followed
-by museattn_bwd.  Default workload: acausal bf16, batch 1, 8 heads, N=8192, D=64, 64
-query and 64 key clusters, 10 Lloyd iterations, top-4 retrieval.
+HBM; for the training workload (c5) a step is museattn_fwd followed by
+museattn_bwd.  Headline workload (default): causal bf16 at the Llama-3.2-1B
+attention shape, batch 1, 32 query heads over 8 KV heads, N=65536, D=64,
+RoPE, local blocks of 1024, 128 clusters per block level, top-8 retrieval.
 
-Prints one JSON line: ms per layer, effective TFLOP/s (exact-attention
-FLOPs / time), the roofline of the dominant kernel (algorithmic work per
-launch / mean launch time from HIP events on the launch stream), exact
-attention timed on the same GPU (torch SDPA, and this library's own
-kernels with every cluster retrieved), the approximation error (aggregate
-and mean per-row RSE on sampled rows), and the fp64 oracle timed on a
-bounded sample on the host cores.
+Prints one JSON line: ms per layer (median of the timed steps, each
+bracketed by HIP events on the launch stream), effective TFLOP/s
+(exact-attention FLOPs / time), the roofline of the dominant kernel
+(algorithmic work per launch / mean launch time from HIP events around each
+launch), exact attention timed on the same GPU (torch SDPA, and this
+library's own kernels with every cluster retrieved), the approximation
+error (aggregate and mean per-row RSE on sampled rows), the fp64 oracle
+timed on a bounded sample on the host cores, and a sweep over the other
+workloads (8k acausal, 16k causal batch 4, 64k D=128 forward + backward)
+with the same timing, SDPA, RSE and CPU-baseline figures.
 """
 import argparse
+import gc
 import json
 import re
 import math
@@ -31,16 +36,27 @@ METRIC = "MuSe attn ms/layer + effective TFLOP/s (% of MFMA peak) at N=8k..64k, 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+HEADLINE = "c4"
+SWEEP = ("c2", "c3", "c5")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default=HEADLINE, choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-sweep", action="store_true", help="time the headline workload only")
+    ap.add_argument("--sweep-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work per workload (bounded sample)")
     ap.add_argument("--no-exact", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain copy of this many MiB (for PMC byte-counter scaling)")
     return ap.parse_args()
@@ -132,19 +148,29 @@ def measured_traffic(w, kernel):
     return int(rec["bytes_per_dispatch"])
 
 
-def time_calls(fn, steps, torch):
+def time_steps(fn, steps, torch):
+    """Run `steps` calls of fn, each bracketed by HIP events on the current
+    (launch) stream, the whole region bracketed by device synchronisation.
+    Returns (median ms per call from the events, mean ms per call from the
+    host clock around the region)."""
     torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for a, b in evs:
+        a.record()
         fn()
+        b.record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [a.elapsed_time(b) for a, b in evs]
+    return float(np.median(per)), wall
 
 
 def exact_attention_ms(Q, K, V, w, steps, torch):
     """torch SDPA on the same tensors (KV heads repeated for GQA); for the
     training workload forward + backward, restricted to the fused flash /
-    memory-efficient kernels (no math fallback)."""
+    memory-efficient kernels (no math fallback).  Median ms per call."""
     import torch.nn.functional as F
     from torch.nn.attention import SDPBackend, sdpa_kernel
     Hq, Hkv = w.Hq, w.Hkv
@@ -163,13 +189,13 @@ def exact_attention_ms(Q, K, V, w, steps, torch):
             F.scaled_dot_product_attention(Q, Kx, Vx, is_causal=w.causal)
     for _ in range(2):
         f()
-    return time_calls(f, steps, torch)
+    return time_steps(f, steps, torch)[0]
 
 
 def own_exact_ms(Q, K, V, w, M, steps, torch):
     """The same forward with k1 = C: every key cluster is retrieved, so the
     gathered exact kernels compute plain softmax attention (clustering and
-    summaries included).  Returns (ms per call, O)."""
+    summaries included).  Returns (median ms per call, O)."""
     cfg = M.make_cfg(w.C, w.iters, w.C, w.causal, w.block)
     O, lse, st = M.museattn_fwd(Q, K, V, cfg)
     ws = torch.empty(M.layout(w.B, w.Hq, w.Hkv, w.N, w.D, M._dt(Q), cfg)["ws_bytes"], dtype=torch.uint8,
@@ -178,7 +204,8 @@ def own_exact_ms(Q, K, V, w, M, steps, torch):
     def f():
         M.museattn_fwd(Q, K, V, cfg, state=st, ws=ws, out=(O, lse))
     f()
-    ms = time_calls(f, steps, torch)
+    ms = time_steps(f, steps, torch)[0]
+    del ws, st, lse
     return ms, O
 
 
@@ -209,72 +236,108 @@ def rse_vs_exact(Q, K, V, O, w, torch, rows_per_head=1024):
     return num / den, float(torch.cat(rows).mean())
 
 
-def cpu_baseline(w, x, budget_s=25.0):
-    """Oracle on a bounded sample: one (batch, KV group) slice, or fewer of
-    its problems, extrapolated linearly to the whole layer."""
-    from oracle import muse_oracle as mo
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        return 1
+
+
+def cpu_baseline(w, x, budget_s):
+    """The fp64 oracle timed on a bounded sample of the workload, scaled to
+    the whole layer.
+
+    Acausal: whole (batch, query head) problems until the budget is spent,
+    extrapolated linearly in the number of heads.  Causal: the first segment
+    of each block level of head 0 (forward, plus the backward for a training
+    workload), timed for spans up to 8192 rows while the budget is predicted
+    to last (a level costs about twice the one below it); each
+    larger level is extrapolated from the largest measured one linearly in
+    the span (every step of a problem, k-means, statistics and attention, is
+    linear in its row count at fixed C and D); each level's time is
+    multiplied by its segment count, the exact local blocks by the block
+    count from four timed blocks, and the head by B * Hq."""
+    from oracle import muse_oracle as mo
     cfg = mo.MuseConfig(cq=w.C, ck=w.C, iters=w.iters, topk=w.topk, block=w.block, causal=w.causal)
     Q, K, V = x["Q"], x["K"], x["V"]
-    heads_done = 0
-    t0 = time.perf_counter()
-    for h in range(w.Hq):
-        kv = h * w.Hkv // w.Hq
-        mo.forward_head(Q[0, h], K[0, kv], V[0, kv], cfg)
-        heads_done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    per_layer_ms = dt / heads_done * (w.B * w.Hq) * 1e3
-    return {"value": round(per_layer_ms, 1), "unit": "ms/layer", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{heads_done} of {w.B * w.Hq} (batch, query head) problems in {dt:.1f} s, "
-                      f"extrapolated linearly to the layer; host os.cpu_count()={os.cpu_count()}"}
+    dO = x.get("dO")
+    s = cfg.s(w.D)
+    heads = w.B * w.Hq
+
+    def one_problem(q, k, v, do):
+        r = mo.solve_problem(q, k, v, s, cfg.cq, cfg.ck, cfg.topk, cfg.iters)
+        if do is not None:
+            delta = np.einsum("nd,nd->n", do.astype(np.float64), r.o)
+            mo.backward_problem(q, k, v, s, r.aq, r.ak, r.R, min(cfg.cq, len(q)), min(cfg.ck, len(k)),
+                                r.lse, delta, do, cfg.dipole)
+
+    t_all = time.perf_counter()
+    if not w.causal:
+        done = 0
+        for h in range(w.Hq):
+            g = h * w.Hkv // w.Hq
+            one_problem(Q[0, h], K[0, g], V[0, g], None if dO is None else dO[0, h])
+            done += 1
+            if time.perf_counter() - t_all > budget_s:
+                break
+        dt = time.perf_counter() - t_all
+        value = dt / done * heads * 1e3
+        sample = (f"{done} of {heads} whole (batch, query head) problems in {dt:.1f} s, "
+                  f"extrapolated linearly in heads")
+    else:
+        plan = mo.causal_plan(w.N, w.block)
+        first = {}
+        for pr in plan:
+            first.setdefault(pr["level"], pr)
+        nseg = {l: sum(1 for pr in plan if pr["level"] == l) for l in first}
+        measured, per_level = {}, {}
+        for l in sorted(first):
+            pr = first[l]
+            if pr["kn"] > 8192:
+                break
+            if measured:
+                last = max(measured)
+                predicted = measured[last] * pr["kn"] / first[last]["kn"]
+                if time.perf_counter() - t_all + predicted > budget_s:
+                    break
+            q0, qn, k0, kn = pr["q0"], pr["qn"], pr["k0"], pr["kn"]
+            t0 = time.perf_counter()
+            one_problem(Q[0, 0, q0:q0 + qn], K[0, 0, k0:k0 + kn], V[0, 0, k0:k0 + kn],
+                        None if dO is None else dO[0, 0, q0:q0 + qn])
+            measured[l] = time.perf_counter() - t0
+        lmax = max(measured)
+        for l in first:
+            per_level[l] = measured[l] if l in measured else measured[lmax] * first[l]["kn"] / first[lmax]["kn"]
+        nb = -(-w.N // w.block)
+        nloc = min(4, nb)
+        t0 = time.perf_counter()
+        span = nloc * w.block
+        lo, ll = mo.local_causal(Q[0, 0, :span], K[0, 0, :span], V[0, 0, :span], s, w.block)
+        if dO is not None:
+            delta = np.einsum("nd,nd->n", dO[0, 0, :span].astype(np.float64), lo)
+            mo.local_backward(Q[0, 0, :span], K[0, 0, :span], V[0, 0, :span], s, w.block, ll, delta,
+                              dO[0, 0, :span])
+        t_loc = (time.perf_counter() - t0) * nb / nloc
+        per_head = sum(per_level[l] * nseg[l] for l in first) + t_loc
+        value = per_head * heads * 1e3
+        dt = time.perf_counter() - t_all
+        sample = (f"head 0: the first segment of levels {sorted(measured)} timed "
+                  f"({', '.join(f'{measured[l]:.2f} s' for l in sorted(measured))}), "
+                  f"levels {sorted(set(first) - set(measured))} extrapolated linearly in span, "
+                  f"{nloc} of {nb} local blocks timed; {dt:.1f} s of oracle work, scaled by segment "
+                  f"counts and {heads} (batch, query head) pairs"
+                  + ("; forward + backward" if dO is not None else ""))
+    return {"value": round(value, 1), "unit": "ms/layer", "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": sample + f"; host os.cpu_count()={os.cpu_count()}"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-    import torch
-
-    from clustered_approximate_softmax_amd import muse as M
-    from clustered_approximate_softmax_amd import synth
-
-    w = synth.WORKLOADS[args.config]
-    x = synth.make_inputs(w)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    Q, K, V = (torch.from_numpy(x[k]).to(tdt).cuda() for k in ("Q", "K", "V"))
-    cfg = M.make_cfg(w.C, w.iters, w.topk, w.causal, w.block)
-    rows = M.plan(w.N, cfg)
-    O, lse, st = M.museattn_fwd(Q, K, V, cfg)
-    ws = torch.empty(M.layout(w.B, w.Hq, w.Hkv, w.N, w.D, M._dt(Q), cfg)["ws_bytes"], dtype=torch.uint8,
-                     device="cuda")
-    if w.backward:
-        dO = torch.from_numpy(x["dO"]).to(tdt).cuda()
-        bws = torch.empty(M.bwd_ws_size(w.B, w.Hq, w.Hkv, w.N, w.D, M._dt(Q), cfg), dtype=torch.uint8,
-                          device="cuda")
-        grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
-
-    def step():
-        M.museattn_fwd(Q, K, V, cfg, state=st, ws=ws, out=(O, lse))
-        if w.backward:
-            M.museattn_bwd(Q, K, V, O, lse, dO, cfg, st, ws=bws, out=grads)
-
-    for _ in range(args.warmup):
-        step()
-    ms = time_calls(step, args.steps, torch)
-
-    # per-kernel HIP-event timing on the launch stream (separate pass)
+def kernel_roofline(w, M, st, rows, step, steps, torch):
+    """Per-kernel HIP-event timing (a separate pass of `steps` steps) and the
+    roofline of the kernel with the most time per step."""
     M.timing_reset()
     M.timing_enable(True)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     kt = M.timing_read()
@@ -288,11 +351,11 @@ def main():
         a[0] += tot
         a[1] += n
         if base != name:
-            levels[name] = {"ms_per_launch": tot / n, "launches_per_step": n / args.steps}
+            levels[name] = {"ms_per_launch": tot / n, "launches_per_step": n / steps}
     per_kernel = {}
     for name, (tot, n) in agg.items():
-        per_kernel[name] = {"ms_per_launch": tot / n, "launches_per_step": n / args.steps,
-                            "ms_per_step": tot / args.steps}
+        per_kernel[name] = {"ms_per_launch": tot / n, "launches_per_step": n / steps,
+                            "ms_per_step": tot / steps}
     dom = max(per_kernel, key=lambda k: per_kernel[k]["ms_per_step"])
     launches = per_kernel[dom]["launches_per_step"]
     fl, by, bound = models.get(dom, (0.0, 0.0, "hbm"))
@@ -310,38 +373,114 @@ def main():
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = {"flops": fl / launches, "bytes": by / launches}
     roof["avg_launch_ms"] = round(avg_s * 1e3, 4)
+    kernels = {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in per_kernel.items()}
+    lev = {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in levels.items()}
+    return roof, kernels, lev
 
+
+def run_workload(name, args, torch, M, synth, steps, warmup, headline):
+    """Time one workload; returns the figures of its JSON entry."""
+    w = synth.WORKLOADS[name]
+    log(f"{name} ({w.name}): generating inputs")
+    x = synth.make_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    Q, K, V = (torch.from_numpy(x[k]).to(tdt).cuda() for k in ("Q", "K", "V"))
+    cfg = M.make_cfg(w.C, w.iters, w.topk, w.causal, w.block)
+    rows = M.plan(w.N, cfg)
+    O, lse, st = M.museattn_fwd(Q, K, V, cfg)
+    ws = torch.empty(M.layout(w.B, w.Hq, w.Hkv, w.N, w.D, M._dt(Q), cfg)["ws_bytes"], dtype=torch.uint8,
+                     device="cuda")
+    dO = bws = grads = None
+    if w.backward:
+        dO = torch.from_numpy(x["dO"]).to(tdt).cuda()
+        bws = torch.empty(M.bwd_ws_size(w.B, w.Hq, w.Hkv, w.N, w.D, M._dt(Q), cfg), dtype=torch.uint8,
+                          device="cuda")
+        grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+
+    def step():
+        M.museattn_fwd(Q, K, V, cfg, state=st, ws=ws, out=(O, lse))
+        if w.backward:
+            M.museattn_bwd(Q, K, V, O, lse, dO, cfg, st, ws=bws, out=grads)
+
+    for _ in range(warmup):
+        step()
+    log(f"{name}: timing {steps} steps")
+    ms, wall = time_steps(step, steps, torch)
     eff = exact_flops(w) / (ms / 1e3) / 1e12
-    out = {
-        "metric": METRIC, "value": round(ms, 4), "unit": "ms/layer", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
-        "data": "synthetic (seeded Gaussian-mixture Q/K, normal V)",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "D": w.D,
-                   "clusters": w.C, "lloyd_iters": w.iters, "topk": w.topk, "causal": w.causal,
-                   "local_block": w.block},
-        "effective_tflops": round(eff, 2),
-        "effective_pct_of_mfma_peak": round(100 * eff / (PEAK_BF16_TFLOPS if w.dtype == "bf16"
-                                                           else PEAK_F32_TFLOPS), 2),
-        "roofline": roof,
-        "kernels": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in per_kernel.items()},
-        "levels": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in levels.items()},
-    }
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    res = {"workload": w.name, "ms": round(ms, 4), "ms_mean_wall": round(wall, 4),
+           "effective_tflops": round(eff, 2), "effective_pct_of_mfma_peak": round(100 * eff / peak, 2),
+           "step": "museattn_fwd + museattn_bwd" if w.backward else "museattn_fwd"}
+    if headline and not args.no_kernel_timing:
+        log(f"{name}: per-kernel timing pass")
+        res["roofline"], res["kernels"], res["levels"] = kernel_roofline(w, M, st, rows, step, steps, torch)
     if not args.no_exact:
-        ex_ms = exact_attention_ms(Q, K, V, w, max(3, args.steps // 2), torch)
-        out["exact_attention_same_gpu"] = {"impl": "torch.nn.functional.scaled_dot_product_attention",
+        log(f"{name}: exact attention (SDPA) and RSE")
+        ex_ms = exact_attention_ms(Q, K, V, w, max(3, steps // 2), torch)
+        res["exact_attention_same_gpu"] = {"impl": "torch.nn.functional.scaled_dot_product_attention",
                                            "ms": round(ex_ms, 4),
                                            "tflops": round(exact_flops(w) / ex_ms / 1e9, 1),
                                            "speedup_muse_vs_exact": round(ex_ms / ms, 3)}
         rse, rse_row = rse_vs_exact(Q, K, V, O, w, torch)
-        out["rse_vs_exact"] = round(rse, 5)
-        out["rse_row_mean"] = round(rse_row, 5)
-        # the build's own exact attention: every cluster retrieved (forward only)
-        own_ms, O_own = own_exact_ms(Q, K, V, w, M, max(2, args.steps // 4), torch)
-        out["exact_attention_own_kernels"] = {
-            "impl": "museattn_fwd with k1 = C (all key clusters retrieved; forward only, clustering included)",
-            "ms": round(own_ms, 4), "rse_vs_exact": float(f"{rse_vs_exact(Q, K, V, O_own, w, torch)[0]:.3g}")}
-        del O_own
+        res["rse_vs_exact"] = round(rse, 5)
+        res["rse_row_mean"] = round(rse_row, 5)
+        if headline:
+            # the build's own exact attention: every cluster retrieved (forward only)
+            own_ms, O_own = own_exact_ms(Q, K, V, w, M, max(2, min(steps // 4, 5)), torch)
+            res["exact_attention_own_kernels"] = {
+                "impl": "museattn_fwd with k1 = C (all key clusters retrieved; forward only, clustering included)",
+                "ms": round(own_ms, 4), "rse_vs_exact": float(f"{rse_vs_exact(Q, K, V, O_own, w, torch)[0]:.3g}")}
+            del O_own
+    del Q, K, V, O, lse, st, ws, dO, bws, grads
+    gc.collect()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log(f"{name}: oracle on the host (budget {args.cpu_budget:.0f} s)")
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    del x
+    gc.collect()
+    return w, res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    from clustered_approximate_softmax_amd import muse as M
+    from clustered_approximate_softmax_amd import synth
+
+    M.lib()   # fail loudly before any work when the HIP library is missing
+    w, head = run_workload(args.config, args, torch, M, synth, args.steps, args.warmup, True)
+    out = {
+        "metric": METRIC, "value": head["ms"], "unit": "ms/layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms"],
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian-mixture Q/K, normal V)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "D": w.D,
+                   "clusters": w.C, "lloyd_iters": w.iters, "topk": w.topk, "causal": w.causal,
+                   "local_block": w.block, "rope": w.rope, "step": head["step"]},
+        "timing": "median of the timed steps by HIP events around each step; ms_mean_wall is the "
+                  "host-clock mean over the synchronised region",
+        "ms_mean_wall": head["ms_mean_wall"],
+        "effective_tflops": head["effective_tflops"],
+        "effective_pct_of_mfma_peak": head["effective_pct_of_mfma_peak"],
+    }
+    for k in ("roofline", "kernels", "levels", "exact_attention_same_gpu", "rse_vs_exact", "rse_row_mean",
+              "exact_attention_own_kernels", "cpu_baseline"):
+        if k in head:
+            out[k] = head[k]
+    if not args.no_sweep:
+        sweep = {}
+        for name in SWEEP:
+            if name == args.config:
+                continue
+            ww, r = run_workload(name, args, torch, M, synth, args.sweep_steps, 2, False)
+            sweep[name] = r
+        out["sweep"] = sweep
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device="cuda").normal_()
@@ -350,8 +489,6 @@ def main():
             bbuf.copy_(a)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = n * 4
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(out), flush=True)
 
 
