@@ -77,17 +77,22 @@ static int build_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, 
   if (!cfg) return MUSE_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || (D != 64 && D != 128)) return MUSE_EINVAL;
   if (Hq % Hkv != 0) return MUSE_EINVAL;
-  if (cfg->cq < 1 || cfg->cq > MUSE_MAX_CLUSTERS || cfg->ck != cfg->cq) return MUSE_EINVAL;
+  if (cfg->cq < 1 || cfg->cq > MUSE_MAX_CLUSTERS || cfg->ck < 1 || cfg->ck > MUSE_MAX_CLUSTERS)
+    return MUSE_EINVAL;
   if (cfg->iters < 1 || cfg->topk < 0) return MUSE_EINVAL;
   if (cfg->causal != 0 && cfg->causal != 1) return MUSE_EINVAL;
+  if (cfg->init_mode != 0 && cfg->init_mode != 1) return MUSE_EINVAL;
   if (cfg->causal && cfg->block < 1) return MUSE_EINVAL;
   if (B * Hq * N * D >= (int64_t)1 << 40 || N >= ((int64_t)1 << 30)) return MUSE_EUNSUPPORTED;
   pl.B = (int)B; pl.Hq = (int)Hq; pl.Hkv = (int)Hkv; pl.N = (int)N; pl.D = (int)D;
-  pl.C = cfg->cq;
+  pl.Cq = cfg->cq;
+  pl.Ck = cfg->ck;
+  pl.C = std::max(cfg->cq, cfg->ck);
   pl.iters = cfg->iters;
   pl.topk = cfg->topk;
-  pl.k1w = std::max(1, std::min(cfg->topk, cfg->cq));
+  pl.k1w = std::max(1, std::min(cfg->topk, cfg->ck));
   pl.dipole = cfg->dipole ? 1 : 0;
+  pl.warm = cfg->init_mode;
   pl.causal = cfg->causal;
   pl.blk = cfg->causal ? cfg->block : 0;
   pl.scale = cfg->scale > 0.f ? cfg->scale : (float)(1.0 / sqrt((double)D));
@@ -317,9 +322,9 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
   char* sb = (char*)state;
   char* wb = (char*)ws;
   CSet qs{Q, pl.B * pl.Hq, 1, init_q, (int32_t*)(sb + L.q_labels), (int32_t*)(sb + L.q_perm),
-          (int32_t*)(sb + L.q_offs), (float*)(sb + L.q_cent)};
+          (int32_t*)(sb + L.q_offs), (float*)(sb + L.q_cent), pl.Cq};
   CSet ks{K, pl.B * pl.Hkv, 0, init_k, (int32_t*)(sb + L.k_labels), (int32_t*)(sb + L.k_perm),
-          (int32_t*)(sb + L.k_offs), (float*)(sb + L.k_cent)};
+          (int32_t*)(sb + L.k_offs), (float*)(sb + L.k_cent), pl.Ck};
   AttnBufs ab;
   memset(&ab, 0, sizeof(ab));
   ab.Q = Q; ab.K = K; ab.V = V;
@@ -376,8 +381,8 @@ int musecluster(const void* X, muse_dtype dtype, int64_t G, int64_t n, int64_t D
   build_kmlarge(pl, (int)G, (int)dtype, plocal, lg);
   const size_t need = muse_cluster_ws_size(G, n, D, dtype, C);
   if (lg.nl > 0 && (!ws || ws_bytes < need)) return MUSE_EWORKSPACE;
-  CSet s0{X, (int)G, 1, init_idx, assign, perm, offs, centroids};
-  CSet s1{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
+  CSet s0{X, (int)G, 1, init_idx, assign, perm, offs, centroids, C};
+  CSet s1{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, C};
   size_t kp_bytes, kc_bytes;
   km_ws_bytes(lg, C, (int)D, kp_bytes, kc_bytes);
   float* part = (float*)ws;
@@ -398,7 +403,7 @@ int musesummarize(const void* K, const void* V, muse_dtype dtype, int64_t G, int
   Plan pl;
   int rc = build_plan(1, G, G, n, D, &cfg, pl);
   if (rc) return rc;
-  CSet ks{K, (int)G, 0, nullptr, const_cast<int32_t*>(assign), perm, offs, nullptr};
+  CSet ks{K, (int)G, 0, nullptr, const_cast<int32_t*>(assign), perm, offs, nullptr, C};
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   hipError_t e = launch_perm_only(pl, ks, st);
@@ -443,9 +448,9 @@ int museattn_bwd(const void* Q, const void* K, const void* V, const void* O, con
   memset(&ab, 0, sizeof(ab));
   ab.Q = Q; ab.K = K; ab.V = V;
   ab.qs = CSet{Q, pl.B * pl.Hq, 1, nullptr, (int32_t*)(sb + L.q_labels), (int32_t*)(sb + L.q_perm),
-               (int32_t*)(sb + L.q_offs), (float*)(sb + L.q_cent)};
+               (int32_t*)(sb + L.q_offs), (float*)(sb + L.q_cent), pl.Cq};
   ab.ks = CSet{K, pl.B * pl.Hkv, 0, nullptr, (int32_t*)(sb + L.k_labels), (int32_t*)(sb + L.k_perm),
-               (int32_t*)(sb + L.k_offs), (float*)(sb + L.k_cent)};
+               (int32_t*)(sb + L.k_offs), (float*)(sb + L.k_cent), pl.Ck};
   ab.kst = KStats{(float*)(sb + L.mu), (float*)(sb + L.S), (float*)(sb + L.M), sb + L.mu_in,
                   sb + L.Kp, sb + L.Vp};
   ab.R = (int32_t*)(sb + L.R);

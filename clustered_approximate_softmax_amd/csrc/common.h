@@ -34,10 +34,13 @@ namespace muse {
 // [2mt + m, min(2mt + 2m, N)).  (Hierarchical block decomposition of the
 // causal case: newx.sg page, Abstract.)
 // ---------------------------------------------------------------------------
+// C is the storage count of every per-cluster array, max(cq, ck): the
+// side with fewer clusters simply has empty clusters beyond its own count.
 struct Plan {
-  int32_t B, Hq, Hkv, N, D, C;
+  int32_t B, Hq, Hkv, N, D, C, Cq, Ck;
   int32_t nlev, P;          // levels, problems per head
   int32_t causal, blk, iters, topk, k1w, dipole;
+  int32_t warm;             // 1: k-means starts from the centroids already in the state
   float scale;
   int32_t lev_m[MUSE_MAXLEV];
   int32_t lev_nseg[MUSE_MAXLEV];
@@ -71,11 +74,12 @@ struct CSet {
   const void* X;        // [heads][N][D] in the input dtype
   int32_t heads;        // B*Hq or B*Hkv
   int32_t is_q;         // 1: query geometry (q0, qn), 0: key geometry
-  const int32_t* init;  // [heads][P][C] or null (floor(c n / C))
+  const int32_t* init;  // [heads][P][this set's C] or null (floor(c n / C_eff))
   int32_t* labels;      // [nlev][heads][N]
   int32_t* perm;        // [nlev][heads][N]: sorted position -> row
   int32_t* offs;        // [heads][P][C+1], relative to the problem start
   float* cent;          // [heads][P][C][D] k-means centroids
+  int32_t C;            // clusters of this set (cq or ck; at most the storage count Plan::C)
 };
 
 __host__ __device__ inline void cset_rows(const Plan& pl, const CSet& s, int p, int& lev, int& r0,

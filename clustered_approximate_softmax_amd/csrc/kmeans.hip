@@ -775,11 +775,11 @@ __global__ void __launch_bounds__(KM_NT) km_init_kernel(Plan pl, CSet s0, CSet s
   const int head = (int)(id / pl.P);
   int lev, r0, n;
   cset_rows(pl, s, p, lev, r0, n);
-  const int Ceff = min(C, n);
+  const int Ceff = min(s.C, n);
   float* dst = s.cent + (cp_index(pl, head, p) * C + c) * D + e0;
   float v[8];
   if (c < Ceff) {
-    const int32_t* init = s.init ? s.init + cp_index(pl, head, p) * C : nullptr;
+    const int32_t* init = s.init ? s.init + cp_index(pl, head, p) * s.C : nullptr;
     int r = init ? init[c] : (int)(((long long)c * n) / Ceff);
     r = min(max(r, 0), n - 1);
     load8_f32<TIn>(reinterpret_cast<const TIn*>(s.X) + ((size_t)head * pl.N + r0 + r) * D + e0, v);
@@ -805,7 +805,7 @@ __global__ void __launch_bounds__(KM_NT) km_local_kernel(Plan pl, CSet s0, CSet 
   const int p = plocal - 1 - id / s.heads;
   int lev, r0, n;
   cset_rows(pl, s, p, lev, r0, n);
-  const int C = pl.C, Ceff = min(C, n);
+  const int C = pl.C, Ceff = min(s.C, n);
   const TIn* Xp = reinterpret_cast<const TIn*>(s.X) + ((size_t)head * pl.N + r0) * D;
   float* cent = s.cent + cp_index(pl, head, p) * C * D;
   int32_t* glab = s.labels + ((size_t)lev * s.heads + head) * pl.N + r0;
@@ -879,7 +879,7 @@ __global__ void __launch_bounds__(KM_NT) km_assign_kernel(Plan pl, CSet s0, CSet
   const int p = pl.lev_pfirst[lev] + t;
   int lv, r0, n;
   cset_rows(pl, s, p, lv, r0, n);
-  const int C = pl.C, Ceff = min(C, n);
+  const int C = pl.C, Ceff = min(s.C, n);
   const int c0 = ci * lg.ch, c1 = min(n, c0 + lg.ch);
   const TIn* Xp = reinterpret_cast<const TIn*>(s.X) + ((size_t)head * pl.N + r0) * D;
   const float* cent = s.cent + cp_index(pl, head, p) * C * D;
@@ -944,7 +944,7 @@ __global__ void __launch_bounds__(256) km_reduce_kernel(Plan pl, CSet s0, CSet s
   const int p = pl.lev_pfirst[lev] + t;
   int lv, r0, n;
   cset_rows(pl, s, p, lv, r0, n);
-  const int C = pl.C, Ceff = min(C, n);
+  const int C = pl.C, Ceff = min(s.C, n);
   const int c = cb * cpb + threadIdx.x / D, e = threadIdx.x % D;
   if (c >= Ceff) return;
   const int nchp = (n + lg.ch - 1) / lg.ch;
@@ -996,7 +996,7 @@ __global__ void __launch_bounds__(KM_NT) km_perm_chunk_kernel(Plan pl, CSet s0, 
   const int p = pl.lev_pfirst[lev] + t;
   int lv, r0, n;
   cset_rows(pl, s, p, lv, r0, n);
-  const int C = pl.C, Ceff = min(C, n);
+  const int C = pl.C, Ceff = min(s.C, n);
   const int nchp = (n + lg.ch - 1) / lg.ch;
   const int c0 = ci * lg.ch, c1 = min(n, c0 + lg.ch);
   if (c0 >= c1) return;
@@ -1087,7 +1087,7 @@ __global__ void __launch_bounds__(KM_NT) km_perm_kernel(Plan pl, CSet s0, CSet s
   const int head = id / nl, p = plocal + id % nl;
   int lev, r0, n;
   cset_rows(pl, s, p, lev, r0, n);
-  const int C = pl.C, Ceff = min(C, n);
+  const int C = pl.C, Ceff = min(s.C, n);
   const int32_t* glab = s.labels + ((size_t)lev * s.heads + head) * pl.N + r0;
   int32_t* perm = s.perm + ((size_t)lev * s.heads + head) * pl.N + r0;
   int32_t* offs = s.offs + cp_index(pl, head, p) * (C + 1);
@@ -1104,7 +1104,7 @@ static hipError_t km_run_t(const Plan& pl, const CSet& s0, const CSet& s1, int p
   const int nsets_heads = s0.heads + s1.heads;
   const size_t smem = sizeof(KmSmem<TIn, D, CT>);
   if (nsets_heads == 0) return hipSuccess;
-  {
+  if (!pl.warm) {   // a warm start keeps the centroids the state already holds
     const long long thr = (long long)nsets_heads * pl.P * pl.C * (D / 8);
     MUSE_KT_PRE(st);
     km_init_kernel<TIn><<<(unsigned)((thr + KM_NT - 1) / KM_NT), KM_NT, 0, st>>>(pl, s0, s1, D);
@@ -1156,7 +1156,7 @@ hipError_t launch_kmeans(const Plan& pl, int dtype, const CSet& s0, const CSet& 
 }
 
 hipError_t launch_perm_only(const Plan& pl, const CSet& s0, hipStream_t st) {
-  CSet s1{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
+  CSet s1{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0};
   if (s0.heads * pl.P == 0) return hipSuccess;
   MUSE_KT_PRE(st);
   km_perm_kernel<<<s0.heads * pl.P, KM_NT, 0, st>>>(pl, s0, s1, 0);

@@ -37,7 +37,7 @@ class MuseError(RuntimeError):
 class muse_cfg(ctypes.Structure):
     _fields_ = [("cq", ctypes.c_int32), ("ck", ctypes.c_int32), ("iters", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("block", ctypes.c_int32), ("causal", ctypes.c_int32),
-                ("dipole", ctypes.c_int32), ("reserved", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("dipole", ctypes.c_int32), ("init_mode", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
 LAYOUT_FIELDS = ["P", "L", "C", "k1w", "Cp32", "Nv"]
@@ -103,9 +103,11 @@ def _check(fn, rc):
         raise MuseError(fn, rc, detail)
 
 
-def make_cfg(C, iters=10, topk=0, causal=False, block=0, dipole=True, scale=0.0):
-    return muse_cfg(int(C), int(C), int(iters), int(topk), int(block), int(bool(causal)),
-                    int(bool(dipole)), 0, float(scale))
+def make_cfg(C, iters=10, topk=0, causal=False, block=0, dipole=True, scale=0.0, ck=None, warm=False):
+    """C query clusters (and key clusters unless ck is given); warm: the
+    k-means continues from the centroids of the state passed to the call."""
+    return muse_cfg(int(C), int(C if ck is None else ck), int(iters), int(topk), int(block),
+                    int(bool(causal)), int(bool(dipole)), int(bool(warm)), float(scale))
 
 
 def plan(N, cfg: muse_cfg):

@@ -59,8 +59,11 @@ enum {
  * and no architectural change [NEWX]: the cluster counts, the number of
  * retrieved clusters k1 ([GIST] Retrieval-Augmented Approximation), the
  * causal flag and the local block size of the causal hierarchy [NEWX].
- *   cq, ck   clusters per query / key problem, 1..256.  This build uses one
- *            count for both sides and requires cq == ck.
+ *   cq, ck   clusters per query / key problem, 1..256 each ([GIST]
+ *            Bidirectional Semantic Clustering: queries and keys are
+ *            clustered separately).  Per-cluster arrays of the state are
+ *            laid out with C = max(cq, ck) clusters per problem; the side
+ *            with fewer clusters has empty clusters beyond its own count.
  *   iters    Lloyd iterations, >= 1.
  *   topk     k1, clusters per query cluster attended exactly, >= 0.
  *   block    causal local block size (>= 1); ignored when causal == 0.
@@ -68,10 +71,18 @@ enum {
  *            `block`, approximated off-diagonal blocks on ceil(log2(
  *            ceil(N/block))) dyadic levels).
  *   dipole   1: monopole + dipole summaries; 0: monopole only.
+ *   init_mode  0: the k-means of every problem starts from the points given
+ *            by init_q / init_k (or the default points); 1: warm start, the
+ *            Lloyd iterations continue from the centroids already held in
+ *            `state` (q_cent, k_cent), which must come from an earlier
+ *            museattn_fwd with the same shapes and cq, ck, block and causal
+ *            (for example the previous training step on the same layer);
+ *            init_q / init_k are then ignored.  The library cannot check
+ *            where those centroids came from.
  *   scale    softmax scale s applied to q.k; <= 0 means 1/sqrt(D).
  */
 typedef struct {
-  int32_t cq, ck, iters, topk, block, causal, dipole, reserved;
+  int32_t cq, ck, iters, topk, block, causal, dipole, init_mode;
   float scale;
 } muse_cfg;
 
@@ -79,7 +90,8 @@ typedef struct {
  * Byte offsets of the arrays held in the `state` buffer that museattn_fwd
  * fills and museattn_bwd reads (the fixed assignments of the backward).
  * P = problems per head (1 when acausal), L = levels (1 when acausal),
- * C = cq, k1w = max(1, min(topk, C)), Cp32 = C rounded up to a multiple of 64,
+ * C = max(cq, ck), k1w = max(1, min(topk, ck)), Cp32 = C rounded up to a
+ * multiple of 64,
  * Nv = N rounded up to a multiple of 8.
  *   q_labels  int32 [L][B*Hq][N]      query cluster of each row per level
  *   k_labels  int32 [L][B*Hkv][N]
@@ -180,10 +192,10 @@ int musesummarize(const void* K, const void* V, muse_dtype dtype, int64_t G, int
  * Two-Stage Attention, Exponential Tilting, Retrieval-Augmented
  * Approximation; [NEWX] monopole + dipole, causal hierarchy).
  *   Q [B,Hq,N,D], K, V [B,Hkv,N,D]  inputs (dtype)
- *   init_q     int32 [B*Hq][P][C] starting indices of the query k-means of
+ *   init_q     int32 [B*Hq][P][cq] starting indices of the query k-means of
  *              every problem (relative to the problem's first query row) or
  *              NULL for floor(c n / C_eff)
- *   init_k     int32 [B*Hkv][P][C] same for keys, or NULL
+ *   init_k     int32 [B*Hkv][P][ck] same for keys, or NULL
  *   O          [B,Hq,N,D] out (dtype)
  *   lse        fp32 [B,Hq,N] out: log of each row's softmax normaliser
  *   state      out: assignments and statistics (muse_layout), state_bytes

@@ -116,7 +116,15 @@ def kmeans(X, C: int, iters: int, init_idx, history: bool = False):
     X = np.asarray(X, np.float64)
     init_idx = np.asarray(init_idx, np.int64)[:C]
     assert len(set(init_idx.tolist())) == C, "initial indices must be distinct"
-    mu = X[init_idx].copy()
+    return kmeans_from(X, X[init_idx], iters, history)
+
+
+def kmeans_from(X, mu0, iters: int, history: bool = False):
+    """Lloyd's algorithm from given starting centroids mu0 [C, D]: the
+    warm start of a clustering that continues from an earlier call's
+    centroids (empty clusters keep their centroid, as in every step)."""
+    X = np.asarray(X, np.float64)
+    mu = np.array(mu0, np.float64, copy=True)
     labels = np.zeros(X.shape[0], np.int64)
     hist = []
     for _ in range(iters):

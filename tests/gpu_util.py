@@ -46,9 +46,10 @@ def check_labels(X, mu_prev, labels, tie=TIE):
     return len(bad)
 
 
-def shared_state(state, plan_rows, B, Hq, Hkv, k1w):
+def shared_state(state, plan_rows, B, Hq, Hkv, k1w, cq=None):
     """Per-(b, h) dict problem -> (aq, ak, R) read from the GPU state, in the
-    form the oracle's forward(shared=...) takes."""
+    form the oracle's forward(shared=...) takes (cq: query clusters, default
+    the state's per-problem cluster count)."""
     ql = state.field("q_labels").cpu().numpy()
     kl = state.field("k_labels").cpu().numpy()
     R = state.field("R").cpu().numpy()
@@ -60,7 +61,7 @@ def shared_state(state, plan_rows, B, Hq, Hkv, k1w):
             for p, (lev, t, k0, kn, q0, qn) in enumerate(plan_rows):
                 aq = ql[lev, b * Hq + h, q0:q0 + qn].astype(np.int64)
                 ak = kl[lev, b * Hkv + g, k0:k0 + kn].astype(np.int64)
-                Cq = min(R.shape[2], qn)
+                Cq = min(R.shape[2] if cq is None else cq, qn)
                 Rp = [np.array(sorted(x for x in R[b * Hq + h, p, I] if x >= 0), np.int64) for I in range(Cq)]
                 d[p] = (aq, ak, Rp)
             out[(b, h)] = d

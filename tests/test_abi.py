@@ -75,11 +75,19 @@ def test_fwd_rejects_bad_arguments(kw, cfgkw):
     assert _fwd(M.make_cfg(**c), **kw) == -1
 
 
-def test_fwd_rejects_unequal_cluster_counts_and_nulls():
-    cfg = M.make_cfg(16, 3, 1)
-    cfg.ck = 8
-    assert _fwd(cfg) == -1
+def test_fwd_rejects_bad_key_cluster_count_and_nulls():
+    for ck in (0, 257):
+        assert _fwd(M.make_cfg(16, 3, 1, ck=ck)) == -1
     assert _fwd(M.make_cfg(16, 3, 1), ptr=None) == -1
+
+
+def test_layout_with_separate_cluster_counts():
+    """Per-cluster arrays use max(cq, ck) clusters; the retrieval width
+    follows the key clusters."""
+    lay = M.layout(1, 2, 1, 4096, 64, M.MUSE_BF16, M.make_cfg(24, 3, 40, ck=80))
+    assert lay["C"] == 80 and lay["k1w"] == 40 and lay["Cp32"] == 128
+    lay = M.layout(1, 2, 1, 4096, 64, M.MUSE_BF16, M.make_cfg(96, 3, 40, ck=16))
+    assert lay["C"] == 96 and lay["k1w"] == 16
 
 
 def test_fwd_rejects_small_buffers():
@@ -123,3 +131,4 @@ def test_bwd_ws_size_and_null_checks():
     rc = L.museattn_bwd(None, None, None, None, None, None, 1, 1, 4, 2, 1000, 64, ctypes.byref(cfg),
                         None, 0, None, None, None, None, 0, None)
     assert rc == -1
+

@@ -18,11 +18,13 @@ pytestmark = pytest.mark.gpu
 
 
 def run_case(B, Hq, Hkv, N, D, dtype, C, iters, topk, causal=False, block=0, dipole=True, seed=0,
-             comps=16, init=False, rope=False):
+             comps=16, init=False, rope=False, ck=None):
+    """C query clusters and ck key clusters (default C)."""
     import torch
+    ck = C if ck is None else ck
     x = gu.gaussian_inputs(B, Hq, Hkv, N, D, dtype, comps=comps, seed=seed, rope=rope)
-    cfg = M.make_cfg(C, iters, topk, causal, block, dipole)
-    ocfg = mo.MuseConfig(cq=C, ck=C, iters=iters, topk=topk, block=block, causal=causal, dipole=dipole)
+    cfg = M.make_cfg(C, iters, topk, causal, block, dipole, ck=ck)
+    ocfg = mo.MuseConfig(cq=C, ck=ck, iters=iters, topk=topk, block=block, causal=causal, dipole=dipole)
     Qd, Kd, Vd = (gu.to_dev(x[k], dtype) for k in "QKV")
     rows = M.plan(N, cfg)
     iq = ik = None
@@ -30,7 +32,7 @@ def run_case(B, Hq, Hkv, N, D, dtype, C, iters, topk, causal=False, block=0, dip
     if init:
         rng = np.random.default_rng(seed + 77)
         iqa = np.stack([gu.synth.draw_inits(rng, [r[5] for r in rows], C) for _ in range(B * Hq)])
-        ika = np.stack([gu.synth.draw_inits(rng, [r[3] for r in rows], C) for _ in range(B * Hkv)])
+        ika = np.stack([gu.synth.draw_inits(rng, [r[3] for r in rows], ck) for _ in range(B * Hkv)])
         iq, ik = torch.from_numpy(iqa).cuda(), torch.from_numpy(ika).cuda()
         inits = {(b, h): {p: (iqa[b * Hq + h, p], ika[b * Hkv + (h * Hkv) // Hq, p])
                           for p in range(len(rows))} for b in range(B) for h in range(Hq)}
@@ -38,7 +40,7 @@ def run_case(B, Hq, Hkv, N, D, dtype, C, iters, topk, causal=False, block=0, dip
     torch.cuda.synchronize()
     O = O.float().cpu().numpy()
     lse = lse.cpu().numpy()
-    shared = gu.shared_state(st, rows, B, Hq, Hkv, max(1, min(topk, C)))
+    shared = gu.shared_state(st, rows, B, Hq, Hkv, max(1, min(topk, ck)), cq=C)
     Or, Lr, res = mo.forward(x["Q"], x["K"], x["V"], ocfg, shared=shared)
     for b in range(B):
         for h in range(Hq):
@@ -154,3 +156,12 @@ def test_forward_is_deterministic():
     O2, l2, _ = M.museattn_fwd(Qd, Kd, Vd, cfg)
     torch.cuda.synchronize()
     assert torch.equal(O1, O2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("cq,ck,causal,dtype", [(16, 48, False, "bf16"), (64, 24, False, "f32"),
+                                                (24, 80, True, "bf16"), (40, 12, True, "bf16")])
+def test_separate_query_and_key_cluster_counts(cq, ck, causal, dtype):
+    """Queries and keys clustered with their own counts (seeded starting
+    points of each side's length), acausal and causal."""
+    run_case(1, 4, 2, 3000 if not causal else 2500, 64, dtype, cq, 3, 3, causal=causal,
+             block=256 if causal else 0, seed=40 + cq, comps=24, init=True, ck=ck)

@@ -22,11 +22,12 @@ GTOL = {"f32": 2e-5, "bf16": 1e-2}
 
 
 def run_bwd(B, Hq, Hkv, N, D, dtype, C, iters, topk, causal=False, block=0, dipole=True, seed=0, comps=16,
-            rope=False):
+            rope=False, ck=None):
     import torch
+    ck = C if ck is None else ck
     x = gu.gaussian_inputs(B, Hq, Hkv, N, D, dtype, comps=comps, seed=seed, rope=rope)
-    cfg = M.make_cfg(C, iters, topk, causal, block, dipole)
-    ocfg = mo.MuseConfig(cq=C, ck=C, iters=iters, topk=topk, block=block, causal=causal, dipole=dipole)
+    cfg = M.make_cfg(C, iters, topk, causal, block, dipole, ck=ck)
+    ocfg = mo.MuseConfig(cq=C, ck=ck, iters=iters, topk=topk, block=block, causal=causal, dipole=dipole)
     Qd, Kd, Vd, dOd = (gu.to_dev(x[k], dtype) for k in ("Q", "K", "V", "dO"))
     print(f"case B={B} Hq={Hq} Hkv={Hkv} N={N} D={D} {dtype} C={C} topk={topk} causal={causal} "
           f"block={block} dipole={dipole} seed={seed}", flush=True)
@@ -34,7 +35,7 @@ def run_bwd(B, Hq, Hkv, N, D, dtype, C, iters, topk, causal=False, block=0, dipo
     dQ, dK, dV = M.museattn_bwd(Qd, Kd, Vd, O, lse, dOd, cfg, st)
     torch.cuda.synchronize()
     rows = M.plan(N, cfg)
-    shared = gu.shared_state(st, rows, B, Hq, Hkv, max(1, min(topk, C)))
+    shared = gu.shared_state(st, rows, B, Hq, Hkv, max(1, min(topk, ck)), cq=C)
     Or, Lr, res = mo.forward(x["Q"], x["K"], x["V"], ocfg, shared=shared)
     gQ, gK, gV = mo.backward(x["Q"], x["K"], x["V"], x["dO"], ocfg, Or, Lr, res)
     out = dict(dQ=dQ.float().cpu().numpy(), dK=dK.float().cpu().numpy(), dV=dV.float().cpu().numpy())
@@ -143,3 +144,10 @@ def test_backward_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("cq,ck,causal,dtype", [(12, 40, False, "bf16"), (48, 16, False, "f32"),
+                                                (20, 6, True, "bf16"), (8, 32, True, "f32")])
+def test_separate_query_and_key_cluster_counts(cq, ck, causal, dtype):
+    run_bwd(1, 4, 2, 900, 64, dtype, cq, 3, 2, causal=causal, block=64 if causal else 0, seed=50 + cq,
+            comps=16, ck=ck)

@@ -25,15 +25,17 @@ def _inits(rng, rows, C, heads, side):
 
 
 def lockstep_forward(x, B, Hq, Hkv, N, D, dtype, C, iters, topk, causal=False, block=0, heads=None,
-                     seed=0):
+                     seed=0, ck=None):
     """Runs the lockstep comparison; returns the number of tie-tolerated
-    label flips.  heads: optional list of (side, head) pairs to check
-    (default: all)."""
+    label flips.  C query clusters, ck key clusters (default C).  heads:
+    optional list of (side, head) pairs to check (default: all)."""
     import torch
-    cfg_rows = M.plan(N, M.make_cfg(C, 1, topk, causal, block))
+    ck = C if ck is None else ck
+    cnt = {"q": C, "k": ck}
+    cfg_rows = M.plan(N, M.make_cfg(C, 1, topk, causal, block, ck=ck))
     rng = np.random.default_rng(seed + 500)
     iq = _inits(rng, cfg_rows, C, B * Hq, "q")
-    ik = _inits(rng, cfg_rows, C, B * Hkv, "k")
+    ik = _inits(rng, cfg_rows, ck, B * Hkv, "k")
     iqd, ikd = torch.from_numpy(iq).cuda(), torch.from_numpy(ik).cuda()
     Qd, Kd, Vd = (gu.to_dev(x[k], dtype) for k in "QKV")
     Xs = {"q": x["Q"].reshape(B * Hq, N, D), "k": x["K"].reshape(B * Hkv, N, D)}
@@ -44,11 +46,11 @@ def lockstep_forward(x, B, Hq, Hkv, N, D, dtype, C, iters, topk, causal=False, b
     for side, h in heads:
         for p, r in enumerate(cfg_rows):
             r0, n = (int(r[4]), int(r[5])) if side == "q" else (int(r[2]), int(r[3]))
-            Ce = min(C, n)
+            Ce = min(cnt[side], n)
             prev[(side, h, p)] = Xs[side][h, r0:r0 + n][inits[side][h, p, :Ce]].astype(np.float64)
     flips = 0
     for t in range(1, iters + 1):
-        cfg = M.make_cfg(C, t, topk, causal, block)
+        cfg = M.make_cfg(C, t, topk, causal, block, ck=ck)
         O, lse, st = M.museattn_fwd(Qd, Kd, Vd, cfg, iqd, ikd)
         torch.cuda.synchronize()
         lab = {"q": st.field("q_labels").cpu().numpy(), "k": st.field("k_labels").cpu().numpy()}
@@ -57,7 +59,7 @@ def lockstep_forward(x, B, Hq, Hkv, N, D, dtype, C, iters, topk, causal=False, b
             for p, r in enumerate(cfg_rows):
                 lev = int(r[0])
                 r0, n = (int(r[4]), int(r[5])) if side == "q" else (int(r[2]), int(r[3]))
-                Ce = min(C, n)
+                Ce = min(cnt[side], n)
                 X = Xs[side][h, r0:r0 + n]
                 a = lab[side][lev, h, r0:r0 + n].astype(np.int64)
                 assert a.min() >= 0 and a.max() < Ce, (side, h, p, t)
@@ -87,3 +89,12 @@ def test_forward_clustering_lockstep(B, Hq, Hkv, N, D, dtype, C, iters, topk, ca
     x = gu.gaussian_inputs(B, Hq, Hkv, N, D, dtype, comps=max(8, C // 2), seed=N + C)
     flips = lockstep_forward(x, B, Hq, Hkv, N, D, dtype, C, iters, topk, causal, block, seed=N)
     print("tie-tolerated label flips:", flips)
+
+
+@pytest.mark.parametrize("cq,ck,causal", [(16, 48, False), (40, 12, True)])
+def test_forward_clustering_lockstep_separate_counts(cq, ck, causal):
+    """Each side clusters with its own count: query labels stay below cq,
+    key labels below ck, and both match one oracle Lloyd step."""
+    N = 3000
+    x = gu.gaussian_inputs(1, 2, 1, N, 64, "bf16", comps=24, seed=cq * ck)
+    lockstep_forward(x, 1, 2, 1, N, 64, "bf16", cq, 3, 2, causal, 256 if causal else 0, seed=cq, ck=ck)

@@ -87,3 +87,35 @@ def test_default_init_is_floor_of_c_n_over_C():
     assert mo.default_init(1000, 7).tolist() == [0, 142, 285, 428, 571, 714, 857]
     assert mo.default_init(5, 3).tolist() == [0, 1, 3]
     assert mo.default_init(4, 4).tolist() == [0, 1, 2, 3]
+
+
+@pytest.mark.parametrize("trial", range(12))
+def test_warm_started_kmeans_matches_scipy_from_the_same_centroids(trial):
+    """A warm start continues Lloyd from given centroids: scipy's kmeans2
+    with those centroids as its starting matrix agrees, including from
+    centroids that are no data point and with clusters that end empty."""
+    rng = np.random.default_rng(2000 + trial)
+    n, D, C = int(rng.integers(30, 200)), int(rng.integers(1, 7)), int(rng.integers(2, 12))
+    X = rng.standard_normal((n, D))
+    mu0 = rng.standard_normal((C, D)) * (3.0 if trial % 3 == 0 else 1.0)
+    iters = int(rng.integers(1, 6))
+    lab, mu = mo.kmeans_from(X, mu0, iters)
+    from scipy.cluster.vq import kmeans2
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        smu, slab = kmeans2(X, mu0.copy(), iter=iters, minit="matrix", missing="warn")
+    assert np.array_equal(lab, slab)
+    np.testing.assert_allclose(mu, smu, rtol=0, atol=1e-12)
+
+
+def test_warm_start_continues_a_clustering():
+    """T1 iterations, then T2 more from the resulting centroids, is T1 + T2
+    iterations from the start."""
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((400, 5))
+    init = rng.choice(400, 9, replace=False)
+    _, mu1 = mo.kmeans(X, 9, 3, init)
+    lab2, mu2 = mo.kmeans_from(X, mu1, 4)
+    lab7, mu7 = mo.kmeans(X, 9, 7, init)
+    assert np.array_equal(lab2, lab7)
+    np.testing.assert_array_equal(mu2, mu7)
