@@ -72,6 +72,7 @@ class MuseConfig:
     causal: bool = False
     dipole: bool = True   # False: monopole only (T_Ic = S_c)
     scale: float = 0.0    # <= 0 means 1/sqrt(D)
+    exact_tilt: bool = False  # True: far items from the exactly tilted summaries (overrides dipole)
 
     def s(self, D: int) -> float:
         return self.scale if self.scale > 0 else 1.0 / math.sqrt(D)
@@ -209,6 +210,37 @@ def tilted_summaries(S, M, nu, s, dipole=True):
     return T
 
 
+def exact_tilt_stats(K, V, labels, Ck, nu, s):
+    """Exponentially tilted statistics of every key cluster c seen from every
+    query-cluster centroid nu_I (gist.science page, Technical Summary, Core
+    Mechanisms, Exponential Tilting: centroids weighted by the attention of
+    the query centroid instead of plain averages).  With the tilt weights
+    w_j = exp(s nu_I.k_j) over j in c:
+      lnZ_Ic   = log sum_j w_j                     (exact log tilted mass)
+      kappa_Ic = sum_j w_j k_j / sum_j w_j         (tilted key centroid)
+      U_Ic     = sum_j w_j v_j / sum_j w_j         (tilted value mean)
+    lnZ is -inf and kappa, U are zero for an empty cluster."""
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    nu = np.asarray(nu, np.float64)
+    Cq = nu.shape[0]
+    lnZ = np.full((Cq, Ck), -np.inf)
+    kap = np.zeros((Cq, Ck, K.shape[1]))
+    U = np.zeros((Cq, Ck, V.shape[1]))
+    for c in range(Ck):
+        idx = np.nonzero(labels == c)[0]
+        if len(idx) == 0:
+            continue
+        lg = s * (nu @ K[idx].T)                     # [Cq, n_c]
+        mx = lg.max(axis=1, keepdims=True)
+        w = np.exp(lg - mx)
+        z = w.sum(axis=1)
+        lnZ[:, c] = mx[:, 0] + np.log(z)
+        kap[:, c] = (w @ K[idx]) / z[:, None]
+        U[:, c] = (w @ V[idx]) / z[:, None]
+    return lnZ, kap, U
+
+
 # ----------------------------------------------------------------------------
 # O5: one acausal problem (two stages: far field + exact retrieval)
 # ----------------------------------------------------------------------------
@@ -232,7 +264,7 @@ class ProblemResult:
 
 
 def solve_problem(Q, K, V, s, Cq, Ck, k1, iters, init_q=None, init_k=None,
-                  aq=None, ak=None, R=None, dipole=True, qrows=None):
+                  aq=None, ak=None, R=None, dipole=True, qrows=None, exact_tilt=False):
     """One acausal MuSe problem: queries Q [n_q, D] against keys K, V.
 
     aq/ak/R, when given, replace the clustering and the retrieval (the
@@ -240,6 +272,15 @@ def solve_problem(Q, K, V, s, Cq, Ck, k1, iters, init_q=None, init_k=None,
     qrows, when given, limits the per-query outputs to those rows (every
     cluster statistic is still taken over the whole problem); the other
     rows of o and lse stay zero.
+
+    exact_tilt: far items use the exactly tilted statistics of
+    ``exact_tilt_stats`` instead of the first-order (dipole) summary: for
+    query i of cluster I and far cluster c the item has log-weight
+    lnZ_Ic + s (q_i - nu_I).kappa_Ic and value U_Ic.  This is the
+    decomposition about the query centroid with the key residuals taken
+    about the tilted centroid, dropping only the residual cross term
+    (q_i - nu_I).(k_j - kappa_Ic); retrieval ranks clusters by the exact
+    tilted mass lnZ_Ic.
     """
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
@@ -257,7 +298,11 @@ def solve_problem(Q, K, V, s, Cq, Ck, k1, iters, init_q=None, init_k=None,
     aq = np.asarray(aq, np.int64)
     n, mu, S, M = key_stats(K, V, ak, Ck)
     m, nu = query_stats(Q, aq, Cq)
-    sig = cluster_scores(nu, mu, n, s)
+    if exact_tilt:
+        lnZ, kap, U = exact_tilt_stats(K, V, ak, Ck, nu, s)
+        sig = lnZ.copy()
+    else:
+        sig = cluster_scores(nu, mu, n, s)
     if R is None:
         R = [select_topk(sig[I], k1) if m[I] > 0 else np.zeros(0, np.int64)
              for I in range(Cq)]
@@ -265,7 +310,9 @@ def solve_problem(Q, K, V, s, Cq, Ck, k1, iters, init_q=None, init_k=None,
     if want is not None:
         want[np.asarray(qrows, np.int64)] = True
     need = None if want is None else sorted(set(aq[want].tolist()))
-    if need is None:
+    if exact_tilt:
+        T = U
+    elif need is None:
         T = tilted_summaries(S, M, nu, s, dipole)
     else:
         T = np.zeros((Cq, Ck, S.shape[1]))
@@ -287,6 +334,20 @@ def solve_problem(Q, K, V, s, Cq, Ck, k1, iters, init_q=None, init_k=None,
         # centroid term, q_i.mu_c and nu_I.(k_j - mu_c) are kept; the residual
         # cross term (q_i - nu_I).(k_j - mu_c) is dropped.
         ell = s * (Q[rows] @ K[ek].T)                      # [r, |ek|]
+        if exact_tilt:
+            # far items: log-weight lnZ_Ic + s (q_i - nu_I).kappa_Ic, value U_Ic
+            lamw = s * ((Q[rows] - nu[I]) @ kap[I, far].T) + lnZ[I, far][None, :]
+            logw = np.concatenate([ell, lamw], axis=1)
+            if logw.shape[1] == 0:
+                continue
+            mx = logw.max(axis=1, keepdims=True)
+            we = np.exp(ell - mx)
+            wf = np.exp(lamw - mx)
+            den = we.sum(axis=1) + wf.sum(axis=1)
+            num = we @ V[ek] + wf @ U[I, far]
+            o[rows] = num / den[:, None]
+            lse[rows] = mx[:, 0] + np.log(den)
+            continue
         lam = s * (Q[rows] @ mu[far].T)                    # [r, |far|]
         logw = np.concatenate([ell, lam + np.log(n[far].astype(np.float64))[None, :]], axis=1)
         if logw.shape[1] == 0:
@@ -298,8 +359,11 @@ def solve_problem(Q, K, V, s, Cq, Ck, k1, iters, init_q=None, init_k=None,
         num = we @ V[ek] + wf @ T[I, far]
         o[rows] = num / den[:, None]
         lse[rows] = mx[:, 0] + np.log(den)
-    return ProblemResult(o=o, lse=lse, aq=aq, ak=ak, R=R, n=n, mu=mu, S=S, M=M,
-                         m=m, nu=nu, T=T, sigma=sig, mu_q=mu_q)
+    res = ProblemResult(o=o, lse=lse, aq=aq, ak=ak, R=R, n=n, mu=mu, S=S, M=M,
+                        m=m, nu=nu, T=T, sigma=sig, mu_q=mu_q)
+    if exact_tilt:
+        res.extra.update(lnZ=lnZ, kappa=kap, U=U)
+    return res
 
 
 # ----------------------------------------------------------------------------
@@ -401,7 +465,7 @@ def forward_head(Qh, Kh, Vh, cfg: MuseConfig, inits=None, shared=None, qrows=Non
                 continue
         r = solve_problem(Qh[q0:q0 + qn], Kh[k0:k0 + kn], Vh[k0:k0 + kn], s,
                           cfg.cq, cfg.ck, cfg.topk, cfg.iters, iq, ik, aq, ak, R,
-                          cfg.dipole, qrows=sub)
+                          cfg.dipole, qrows=sub, exact_tilt=cfg.exact_tilt)
         parts_o[p, q0:q0 + qn] = r.o
         parts_l[p, q0:q0 + qn] = r.lse
         results.append(r)
