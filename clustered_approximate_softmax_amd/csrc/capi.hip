@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <unordered_set>
 #include <vector>
@@ -256,6 +257,36 @@ static int hip_fail(hipError_t e) {
   return MUSE_EHIP;
 }
 
+// Forward workspace for callers that cannot allocate (museattn_fwd_noalloc):
+// one array per GPU, held until the process ends.  In host code the name
+// `scratch` is only a host-side stand-in; kernels and copies take the device
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MUSE_NOALLOC_WS_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // indexed by HIP device ordinal
+}  // namespace
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+static int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p) return MUSE_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MUSE_OK;
+}
+
 }  // namespace muse
 
 using namespace muse;
@@ -352,6 +383,23 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
   }
   if ((e = launch_attn(pl, (int)dtype, ab, vt_done, st)) != hipSuccess) return hip_fail(e);
   return MUSE_OK;
+}
+
+int museattn_fwd_noalloc(const void* Q, const void* K, const void* V, muse_dtype dtype, int64_t B,
+                         int64_t Hq, int64_t Hkv, int64_t N, int64_t D, const muse_cfg* cfg,
+                         const int32_t* init_q, const int32_t* init_k, void* O, float* lse, void* state,
+                         size_t state_bytes, void* stream) {
+  if (dtype != MUSE_F32 && dtype != MUSE_BF16) return MUSE_EINVAL;
+  Plan pl;
+  int rc = build_plan(B, Hq, Hkv, N, D, cfg, pl);
+  if (rc) return rc;
+  Layout lay;
+  build_layout(pl, (int)dtype, lay);
+  if (lay.L.ws_bytes > (size_t)MUSE_NOALLOC_WS_BYTES) return MUSE_EWORKSPACE;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws)) != MUSE_OK) return rc;
+  return museattn_fwd(Q, K, V, dtype, B, Hq, Hkv, N, D, cfg, init_q, init_k, O, lse, state, state_bytes, ws,
+                      (size_t)MUSE_NOALLOC_WS_BYTES, stream);
 }
 
 size_t muse_cluster_ws_size(int64_t G, int64_t n, int64_t D, muse_dtype dtype, int32_t C) {

@@ -79,6 +79,8 @@ def lib():
     L.museattn_fwd.argtypes = [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64,
                                ctypes.POINTER(muse_cfg), _P, _P, _P, _P, _P, ctypes.c_size_t, _P,
                                ctypes.c_size_t, _P]
+    L.museattn_fwd_noalloc.argtypes = [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64,
+                                       ctypes.POINTER(muse_cfg), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.muse_bwd_ws_size.restype = ctypes.c_size_t
     L.muse_bwd_ws_size.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.POINTER(muse_cfg)]
     L.museattn_bwd.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64,
@@ -251,6 +253,20 @@ def museattn_fwd(Q, K, V, cfg: muse_cfg, init_q=None, init_k=None, state=None, w
                             _ptr(init_k), _ptr(O), _ptr(lse), _ptr(state.buf), state.buf.numel(), _ptr(ws),
                             ws.numel(), _stream())
     _check("museattn_fwd", rc)
+    return O, lse, state
+
+
+def museattn_fwd_noalloc(Q, K, V, cfg: muse_cfg, state: "State", out, init_q=None, init_k=None):
+    """museattn_fwd on the library's own per-GPU workspace: state and
+    out=(O, lse) are given by the caller, nothing is allocated."""
+    _dev_check(Q, K, V, init_q, init_k)
+    B, Hq, N, D = Q.shape
+    Hkv = K.shape[1]
+    O, lse = out
+    rc = lib().museattn_fwd_noalloc(_ptr(Q), _ptr(K), _ptr(V), _dt(Q), B, Hq, Hkv, N, D, ctypes.byref(cfg),
+                                    _ptr(init_q), _ptr(init_k), _ptr(O), _ptr(lse), _ptr(state.buf),
+                                    state.buf.numel(), _stream())
+    _check("museattn_fwd_noalloc", rc)
     return O, lse, state
 
 

@@ -207,6 +207,30 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * museattn_fwd_noalloc - museattn_fwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * kernels and results as museattn_fwd; the workspace is a file-scope device
+ * array of MUSE_NOALLOC_WS_BYTES (64 MiB) in the library, one per GPU,
+ * held until the process ends.  The caller still passes inputs, outputs and
+ * `state`.  The call allocates and frees nothing (per-kernel timing, when
+ * switched on with muse_timing_enable, creates HIP events: leave it off).
+ *   Returns MUSE_EWORKSPACE when the call's workspace (muse_layout.ws_bytes)
+ *   exceeds MUSE_NOALLOC_WS_BYTES (e.g. the 8k acausal workload with 8 heads
+ *   and 64 clusters needs about 20 MiB; the 64k causal workloads do not fit),
+ *   MUSE_EHIP when the array's device address cannot be found, otherwise as
+ *   museattn_fwd.
+ * Every call on one GPU uses that GPU's single array and leaves its
+ * contents behind: calls that overlap on one GPU (on different streams, or
+ * from different host threads) race and must be serialised by the caller.
+ */
+#define MUSE_NOALLOC_WS_BYTES (64u << 20)
+int museattn_fwd_noalloc(const void* Q, const void* K, const void* V, muse_dtype dtype, int64_t B,
+                         int64_t Hq, int64_t Hkv, int64_t N, int64_t D, const muse_cfg* cfg,
+                         const int32_t* init_q, const int32_t* init_k, void* O, float* lse, void* state,
+                         size_t state_bytes, void* stream);
+
+/*
  * museattn_bwd - gradients of museattn_fwd with the cluster assignments,
  * retrieval sets and counts held fixed (those saved in `state` by the
  * forward on the same Q, K, V and cfg); differentiates through the

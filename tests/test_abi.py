@@ -132,3 +132,16 @@ def test_bwd_ws_size_and_null_checks():
                         None, 0, None, None, None, None, 0, None)
     assert rc == -1
 
+
+def test_noalloc_forward_rejects_workspace_beyond_its_array():
+    """museattn_fwd_noalloc checks the call's workspace against its fixed
+    per-GPU array (64 MiB) before touching the GPU."""
+    L = M.lib()
+    big = M.make_cfg(32, 10, 0, True, 512)          # 16k causal, batch 4, 8 heads: ~770 MiB
+    assert M.layout(4, 8, 8, 16384, 64, M.MUSE_BF16, big)["ws_bytes"] > 64 << 20
+    rc = L.museattn_fwd_noalloc(FAKE, FAKE, FAKE, M.MUSE_BF16, 4, 8, 8, 16384, 64, ctypes.byref(big), None, None,
+                                FAKE, FAKE, FAKE, 1 << 40, None)
+    assert rc == -2
+    rc = L.museattn_fwd_noalloc(FAKE, FAKE, FAKE, M.MUSE_BF16, 1, 2, 2, 256, 32, ctypes.byref(big), None, None,
+                                FAKE, FAKE, FAKE, 1 << 40, None)
+    assert rc == -1
