@@ -13,7 +13,9 @@ bracketed by HIP events on the launch stream), effective TFLOP/s
 (algorithmic work per launch / mean launch time from HIP events around each
 launch), exact attention timed on the same GPU (torch SDPA, and this
 library's own kernels with every cluster retrieved), the approximation
-error (aggregate and mean per-row RSE on sampled rows), the fp64 oracle
+error (aggregate and mean per-row RSE on sampled rows; the same forward
+with the exact exponential tilt in place of the dipole, its time and RSE
+beside them), the fp64 oracle
 timed on a bounded sample on the host cores, and a sweep over the other
 workloads (8k acausal, 16k causal batch 4, 64k D=128 forward + backward)
 with the same timing, SDPA, RSE and CPU-baseline figures.
@@ -424,6 +426,20 @@ def run_workload(name, args, torch, M, synth, steps, warmup, headline):
         rse, rse_row = rse_vs_exact(Q, K, V, O, w, torch)
         res["rse_vs_exact"] = round(rse, 5)
         res["rse_row_mean"] = round(rse_row, 5)
+        # the same forward with the exact exponential tilt in place of the dipole
+        xcfg = M.make_cfg(w.C, w.iters, w.topk, w.causal, w.block, tilt="exact")
+        Ox, lx, stx = M.museattn_fwd(Q, K, V, xcfg)
+        wsx = torch.empty(M.layout(w.B, w.Hq, w.Hkv, w.N, w.D, M._dt(Q), xcfg)["ws_bytes"], dtype=torch.uint8,
+                          device="cuda")
+
+        def fx():
+            M.museattn_fwd(Q, K, V, xcfg, state=stx, ws=wsx, out=(Ox, lx))
+        fx()
+        x_ms = time_steps(fx, max(3, min(steps // 4, 10)), torch)[0]
+        x_rse, x_row = rse_vs_exact(Q, K, V, Ox, w, torch)
+        res["exact_tilt"] = {"impl": "museattn_fwd with the exact exponential tilt (forward only)",
+                             "ms": round(x_ms, 4), "rse_vs_exact": round(x_rse, 5), "rse_row_mean": round(x_row, 5)}
+        del Ox, lx, stx, wsx
         if headline:
             # the build's own exact attention: every cluster retrieved (forward only)
             own_ms, O_own = own_exact_ms(Q, K, V, w, M, max(2, min(steps // 4, 5)), torch)
@@ -470,7 +486,7 @@ def main():
         "effective_pct_of_mfma_peak": head["effective_pct_of_mfma_peak"],
     }
     for k in ("roofline", "kernels", "levels", "exact_attention_same_gpu", "rse_vs_exact", "rse_row_mean",
-              "exact_attention_own_kernels", "cpu_baseline"):
+              "exact_tilt", "exact_attention_own_kernels", "cpu_baseline"):
         if k in head:
             out[k] = head[k]
     if not args.no_sweep:

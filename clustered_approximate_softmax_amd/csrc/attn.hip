@@ -662,11 +662,19 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   if (MODE != MODE_LOCAL) {
     const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
     const int32_t* Rr = b.R + ((size_t)ap * C + I) * pl.k1w;
+    // far items: log2 n_c (value T_Ic / n_c), or with the exact tilt the
+    // bias log2 Z_Ic - s log2(e) nu_I.kappa_Ic (key row kappa_Ic, value U_Ic)
+    const bool xt = pl.dipole == 2;
+    const float* fbI = b.fb + ((size_t)ap * C + I) * b.Cp32;
     for (int c = tid; c < MUSE_MAXC; c += NT) {
       float bias = -INFINITY;
       if (c < Ck) {
-        const int nc = koffs[c + 1] - koffs[c];
-        if (nc > 0) bias = __log2f((float)nc);
+        if (xt) {
+          bias = fbI[c];
+        } else {
+          const int nc = koffs[c + 1] - koffs[c];
+          if (nc > 0) bias = __log2f((float)nc);
+        }
       }
       sm.far_bias[c] = bias;
     }
@@ -715,7 +723,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     src.nseg = __builtin_amdgcn_readfirstlane(sm.sel[4]);
     src.nfar = (Ck + AT_KT - 1) / AT_KT;
     src.Ck = max(Ck, 1);
-    src.mu = reinterpret_cast<const unsigned char*>(b.kst.mu_in) + (size_t)kp * C * D * esz;
+    src.mu = xt ? reinterpret_cast<const unsigned char*>(b.kap) + ((size_t)ap * C + I) * b.Cp32 * D * esz
+                : reinterpret_cast<const unsigned char*>(b.kst.mu_in) + (size_t)kp * C * D * esz;
     src.T = reinterpret_cast<const unsigned char*>(b.T) + ((size_t)ap * C + I) * D * b.Cp32 * esz;
     const size_t slice = (size_t)lev * pl.B * pl.Hkv + kvh;
     src.Kx = reinterpret_cast<const unsigned char*>(b.kst.Kp) + slice * pl.N * D * esz;

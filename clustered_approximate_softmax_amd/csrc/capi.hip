@@ -83,6 +83,7 @@ static int build_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, 
   if (cfg->iters < 1 || cfg->topk < 0) return MUSE_EINVAL;
   if (cfg->causal != 0 && cfg->causal != 1) return MUSE_EINVAL;
   if (cfg->init_mode != 0 && cfg->init_mode != 1) return MUSE_EINVAL;
+  if (cfg->dipole < 0 || cfg->dipole > 2) return MUSE_EINVAL;
   if (cfg->causal && cfg->block < 1) return MUSE_EINVAL;
   if (B * Hq * N * D >= (int64_t)1 << 40 || N >= ((int64_t)1 << 30)) return MUSE_EUNSUPPORTED;
   pl.B = (int)B; pl.Hq = (int)Hq; pl.Hkv = (int)Hkv; pl.N = (int)N; pl.D = (int)D;
@@ -92,7 +93,7 @@ static int build_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, 
   pl.iters = cfg->iters;
   pl.topk = cfg->topk;
   pl.k1w = std::max(1, std::min(cfg->topk, cfg->ck));
-  pl.dipole = cfg->dipole ? 1 : 0;
+  pl.dipole = cfg->dipole;
   pl.warm = cfg->init_mode;
   pl.causal = cfg->causal;
   pl.blk = cfg->causal ? cfg->block : 0;
@@ -221,6 +222,11 @@ static void build_layout(const Plan& pl, int dtype, Layout& out) {
   km_ws_bytes(out.lg, pl.C, pl.D, kp_bytes, kc_bytes);
   L.ws_part = w; w = al(w + kp_bytes);
   L.ws_pcnt = w; w = al(w + kc_bytes);
+  // exact tilt: tilted key centroids per (I, c) and the two per-pair floats
+  const bool xt = pl.dipole == 2;
+  L.ws_kap = w; w = al(w + (xt ? BHq * P * C * L.Cp32 * D * eb : 0));
+  L.ws_lz = w; w = al(w + (xt ? BHq * P * C * L.Cp32 * 4 : 0));
+  L.ws_fb = w; w = al(w + (xt ? BHq * P * C * L.Cp32 * 4 : 0));
   L.ws_bytes = std::max<size_t>(w, 256);
 }
 
@@ -371,6 +377,9 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
   ab.Nv = (int32_t)L.Nv;
   ab.O = O;
   ab.lse = lse;
+  ab.kap = wb + L.ws_kap;
+  ab.lz = (float*)(wb + L.ws_lz);
+  ab.fb = (float*)(wb + L.ws_fb);
   hipError_t e = hipGetLastError();  // clear stale errors from earlier calls
   (void)e;
   bool vt_done = false;   // the value copies built with the scores
@@ -379,7 +388,11 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
                            (int32_t*)(wb + L.ws_pcnt), st)) != hipSuccess)
       return hip_fail(e);
     if ((e = launch_summarize(pl, (int)dtype, ks, V, ab.kst, st)) != hipSuccess) return hip_fail(e);
-    if ((e = launch_score_tilt(pl, (int)dtype, ab, vt_done, st)) != hipSuccess) return hip_fail(e);
+    if (pl.dipole == 2) {
+      if ((e = launch_tilt_exact(pl, (int)dtype, ab, st)) != hipSuccess) return hip_fail(e);
+    } else if ((e = launch_score_tilt(pl, (int)dtype, ab, vt_done, st)) != hipSuccess) {
+      return hip_fail(e);
+    }
   }
   if ((e = launch_attn(pl, (int)dtype, ab, vt_done, st)) != hipSuccess) return hip_fail(e);
   return MUSE_OK;
@@ -483,6 +496,7 @@ int museattn_bwd(const void* Q, const void* K, const void* V, const void* O, con
   Plan pl;
   int rc = build_plan(B, Hq, Hkv, N, D, cfg, pl);
   if (rc) return rc;
+  if (pl.dipole == 2) return MUSE_EUNSUPPORTED;   // the exact tilt has no backward here
   Layout lay;
   build_layout(pl, (int)dtype, lay);
   const muse_layout& L = lay.L;

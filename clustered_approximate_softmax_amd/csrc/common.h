@@ -39,7 +39,7 @@ namespace muse {
 struct Plan {
   int32_t B, Hq, Hkv, N, D, C, Cq, Ck;
   int32_t nlev, P;          // levels, problems per head
-  int32_t causal, blk, iters, topk, k1w, dipole;
+  int32_t causal, blk, iters, topk, k1w, dipole;   // dipole: 0 monopole, 1 dipole, 2 exact tilt
   int32_t warm;             // 1: k-means starts from the centroids already in the state
   float scale;
   int32_t lev_m[MUSE_MAXLEV];

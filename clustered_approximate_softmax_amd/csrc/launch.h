@@ -50,10 +50,13 @@ struct AttnBufs {
   CSet qs, ks;            // query / key clustering (labels, perm, offs, cent)
   KStats kst;
   int32_t* R;             // [B*Hq][P][C][k1w]
-  void* T;                // [B*Hq][P][C][D][Cp32] T_Ic / n_c in the input dtype (I, d, c)
+  void* T;                // [B*Hq][P][C][D][Cp32] T_Ic / n_c (exact tilt: U_Ic) in the input dtype (I, d, c)
   int32_t Cp32;           // C rounded up to 32
   void* Vt;               // value columns: [nlev*B*Hkv sorted copies (+ B*Hkv input V)][D][Nv]
   int32_t Nv;             // N rounded up to 8
+  void* kap;              // exact tilt: tilted key centroids [B*Hq][P][C][Cp32][D] (input dtype)
+  float* lz;              // exact tilt: ln Z_Ic [B*Hq][P][C][Cp32]
+  float* fb;              // exact tilt: far bias log2 Z_Ic - s log2(e) nu_I.kappa_Ic, same layout
   float* oacc;            // causal running output [B*Hq][N][D] (fp32)
   float* lacc;            // causal running lse [B*Hq][N]
   void* O; float* lse;    // outputs
@@ -62,6 +65,9 @@ hipError_t launch_score_topk(const Plan& pl, const AttnBufs& b, hipStream_t st);
 hipError_t launch_tilt(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
 hipError_t launch_score_tilt(const Plan& pl, int dtype, const AttnBufs& b, bool& vt_done, hipStream_t st);
 hipError_t launch_attn(const Plan& pl, int dtype, const AttnBufs& b, bool vt_done, hipStream_t st);
+// Exactly tilted statistics (kap, T = tilted value means, lz, fb) and the
+// retrieval sets ranked by lz.
+hipError_t launch_tilt_exact(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
 
 // Backward with the forward's clustering state held fixed.
 struct BwdLaunch {

@@ -153,7 +153,7 @@ __global__ void __launch_bounds__(SU_NT, 2) summarize_kernel(Plan pl, CSet ks, c
       load_tile();
       if (t0 + 2 * KT < cnt) rows_of(t0 + 2 * KT);
     }
-    if (pl.dipole) {
+    if (pl.dipole == 1) {
 #pragma unroll
       for (int kk = 0; kk < KT / 32; ++kk)
 #pragma unroll
@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(SU_NT, 2) summarize_kernel(Plan pl, CSet ks, c
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 16 * dt + 4 * g + i;
-      const float v = pl.dipole ? acc[u][i] - fs[D + d] * mue : 0.f;
+      const float v = pl.dipole == 1 ? acc[u][i] - fs[D + d] * mue : 0.f;
       M[((size_t)d * C + c) * D + e] = v;
     }
   }

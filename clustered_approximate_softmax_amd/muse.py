@@ -43,7 +43,7 @@ class muse_cfg(ctypes.Structure):
 LAYOUT_FIELDS = ["P", "L", "C", "k1w", "Cp32", "Nv"]
 LAYOUT_OFFS = ["q_labels", "k_labels", "q_perm", "k_perm", "q_offs", "k_offs", "q_cent", "k_cent",
                "mu", "S", "M", "R", "Kp", "Vp", "mu_in", "state_bytes", "ws_T", "ws_oacc", "ws_lacc", "ws_Vt", "ws_part",
-               "ws_pcnt", "ws_bytes"]
+               "ws_pcnt", "ws_bytes", "ws_kap", "ws_lz", "ws_fb"]
 
 
 class muse_layout(ctypes.Structure):
@@ -105,11 +105,17 @@ def _check(fn, rc):
         raise MuseError(fn, rc, detail)
 
 
-def make_cfg(C, iters=10, topk=0, causal=False, block=0, dipole=True, scale=0.0, ck=None, warm=False):
+TILT = {"monopole": 0, "dipole": 1, "exact": 2}
+
+
+def make_cfg(C, iters=10, topk=0, causal=False, block=0, dipole=True, scale=0.0, ck=None, warm=False,
+             tilt=None):
     """C query clusters (and key clusters unless ck is given); warm: the
-    k-means continues from the centroids of the state passed to the call."""
+    k-means continues from the centroids of the state passed to the call;
+    tilt: "monopole", "dipole" or "exact" (overrides dipole)."""
+    mode = TILT[tilt] if tilt is not None else int(bool(dipole))
     return muse_cfg(int(C), int(C if ck is None else ck), int(iters), int(topk), int(block),
-                    int(bool(causal)), int(bool(dipole)), int(bool(warm)), float(scale))
+                    int(bool(causal)), mode, int(bool(warm)), float(scale))
 
 
 def plan(N, cfg: muse_cfg):

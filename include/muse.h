@@ -70,7 +70,16 @@ enum {
  *   causal   0: acausal; 1: causal hierarchy (exact local blocks of size
  *            `block`, approximated off-diagonal blocks on ceil(log2(
  *            ceil(N/block))) dyadic levels).
- *   dipole   1: monopole + dipole summaries; 0: monopole only.
+ *   dipole   1: monopole + dipole summaries (first-order tilt: T_Ic =
+ *            S_c + s M_c nu_I, far log-weight s q.mu_c + ln n_c; retrieval
+ *            by s nu_I.mu_c + ln n_c); 0: monopole only (T_Ic = S_c);
+ *            2: exact exponential tilt ([GIST] Exponential Tilting): the far
+ *            item of key cluster c for a query q of query cluster I has
+ *            log-weight ln Z_Ic + s (q - nu_I).kappa_Ic and value U_Ic, with
+ *            Z_Ic = sum_{j in c} exp(s nu_I.k_j), kappa_Ic and U_Ic the
+ *            keys' and values' means under those weights; retrieval ranks
+ *            clusters by ln Z_Ic.  museattn_bwd returns MUSE_EUNSUPPORTED
+ *            for 2.
  *   init_mode  0: the k-means of every problem starts from the points given
  *            by init_q / init_k (or the default points); 1: warm start, the
  *            Lloyd iterations continue from the centroids already held in
@@ -119,7 +128,7 @@ typedef struct {
   size_t Kp, Vp, mu_in;
   size_t state_bytes;
   /* workspace arrays (scratch; valid after museattn_fwd until the next call) */
-  size_t ws_T;      /* dtype [B*Hq][P][C][D][Cp32] T_Ic / n_c, index (I, d, c) */
+  size_t ws_T;      /* dtype [B*Hq][P][C][D][Cp32] T_Ic / n_c (exact tilt: U_Ic), index (I, d, c) */
   size_t ws_oacc;   /* fp32 [B*Hq][N][D] causal running output */
   size_t ws_lacc;   /* fp32 [B*Hq][N] causal running lse */
   size_t ws_Vt;     /* dtype [L*B*Hkv (+ B*Hkv when causal)][D][Nv] value columns of the sorted
@@ -127,6 +136,10 @@ typedef struct {
   size_t ws_part;   /* k-means chunk partial sums */
   size_t ws_pcnt;
   size_t ws_bytes;
+  /* exact tilt only (dipole == 2; zero-sized otherwise) */
+  size_t ws_kap;    /* dtype [B*Hq][P][C][Cp32][D] tilted key centroids kappa_Ic */
+  size_t ws_lz;     /* fp32 [B*Hq][P][C][Cp32] ln Z_Ic (-inf: empty cluster) */
+  size_t ws_fb;     /* fp32 [B*Hq][P][C][Cp32] log2 Z_Ic - s log2(e) nu_I.kappa_Ic */
 } muse_layout;
 
 /*
