@@ -40,6 +40,8 @@
 // 16-byte read of one value column.
 // Each wave holds QG groups of 16 queries so that every fragment read from
 // LDS feeds QG matrix instructions.
+#include <utility>
+
 #include "common.h"
 #include "launch.h"
 #include "vt.h"
@@ -59,6 +61,21 @@ constexpr float LN2 = 0.6931471805599453f;
 __device__ __forceinline__ void lds_copy16(const void* src, const void* lds) {
   const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(a), "v"(src) : "memory", "m0");
+}
+
+// The same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset (the saddr form): a tile's per-lane offsets do not
+// change from tile to tile, so each copy costs no address arithmetic.
+template <int IMM>
+__device__ __forceinline__ void lds_copy16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %0, %3\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds), "v"(voff), "s"(sbase),
+               "i"(IMM) : "memory", "m0");
+}
+// copies M... of one half of a tile: destination l0 + OFF + M * STEP
+template <int OFF, int STEP, size_t... M>
+__device__ __forceinline__ void lds_copies_s(const void* sbase, const uint32_t* voff, uint32_t l0,
+                                             std::index_sequence<M...>) {
+  (lds_copy16_s<OFF + (int)M * STEP>(sbase, voff[M], l0), ...);
 }
 
 // s_waitcnt immediate for vmcnt(v) and lgkmcnt(l), expcnt left alone.
@@ -92,7 +109,7 @@ __device__ __forceinline__ int keyv(int d) { return d & 7; }
 // the copies in flight and does not wait for them.
 template <typename TIn, int D, int WAVES, int QG>
 struct alignas(16) AtSmem {
-  float far_bias[MUSE_MAXC];   // log2 n_c, or -inf (empty or retrieved)
+  float far_bias[MUSE_MAXC];   // (log2 n_c or the tilt bias) / s2, or -inf (empty or retrieved)
   int32_t seg_lo[MUSE_MAXC];   // retrieved clusters (non-empty), absolute rows
   int32_t seg_hi[MUSE_MAXC];
   int32_t qrow[16 * QG * WAVES];
@@ -184,6 +201,44 @@ __device__ __forceinline__ void issue_tile(unsigned char* stg, const TileSrc& sr
     const TIn* p = vb + (size_t)d * vstride + col;
     lds_copy16(p, vst + (m * NT + 64 * w) * 16);
   }
+}
+
+// Per-lane byte offsets of a contiguous tile's copies (issue_tile's layout):
+// key rows (row stride D) and value columns (row stride vstride).
+template <typename TIn, int D, int WAVES>
+struct TileOffs {
+  static constexpr int NT = 64 * WAVES;
+  static constexpr int MK = AT_KT * AtGeo<TIn, D>::CHK / NT, MV = D * AtGeo<TIn, D>::CHV / NT;
+  uint32_t k[MK], vx[MV], vf[MV];
+  __device__ __forceinline__ void init(int tid, int nv, int cp) {
+    using G = AtGeo<TIn, D>;
+    constexpr int esz = (int)sizeof(TIn);
+#pragma unroll
+    for (int m = 0; m < MK; ++m) {
+      const int ci = m * NT + tid, r = ci / G::CHK, pos = ci % G::CHK;
+      k[m] = (uint32_t)((r * D + (pos ^ keyk<G::CHK>(r)) * G::E) * esz);
+    }
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      const int ci = m * NT + tid, d = ci / G::CHV, pos = ci % G::CHV;
+      const int col = (pos ^ keyv(d)) * G::E;
+      vx[m] = (uint32_t)((d * nv + col) * esz);
+      vf[m] = (uint32_t)((d * cp + col) * esz);
+    }
+  }
+};
+
+// issue_tile for a tile whose 64 key rows and value columns all lie inside
+// their arrays (no clamping needed): bases in SGPRs, offsets from TileOffs.
+template <typename TIn, int D, int WAVES>
+__device__ __forceinline__ void issue_tile_fast(unsigned char* stg, const void* kb, const void* vb,
+                                                const uint32_t* koff, const uint32_t* voff, int ws) {
+  using G = AtGeo<TIn, D>;
+  using O = TileOffs<TIn, D, WAVES>;
+  // LDS destinations: one wave-uniform base plus immediate offsets
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stg) + 64 * 16 * ws;
+  lds_copies_s<0, O::NT * 16>(kb, koff, l0, std::make_index_sequence<O::MK>{});
+  lds_copies_s<G::KB, O::NT * 16>(vb, voff, l0, std::make_index_sequence<O::MV>{});
 }
 
 // Gathered tiles (small clusters).  A tile is 8 chunks of 8 consecutive rows.  Far tile t: clusters 64t ..
@@ -345,14 +400,13 @@ __device__ __forceinline__ TileView view_of(const TileSrc& src, const Cursor& c,
   v.plain = !v.far && c.row0 >= c.lo && c.row0 + AT_KT <= c.hi && (!CAUSAL || c.row0 + AT_KT - 1 <= qmin);
   uint32_t ok = 0xffffu;
   if (!v.far && !v.plain) {
-    const int g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-    for (int rt = 0; rt < AT_KT / 16; ++rt) {
-      const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if ((unsigned)(c.row0 + it0 + i - c.lo) >= (unsigned)(c.hi - c.lo)) ok &= ~(1u << (rt * 4 + i));
-    }
+    // tile items [a, b) lie in [lo, hi): a 64-bit range mask (wave-uniform);
+    // the lane's items 8g + 0..7 and 32 + 8g + 0..7 are byte g of each half
+    const int a = min(max(c.lo - c.row0, 0), AT_KT), b = min(max(c.hi - c.row0, 0), AT_KT);
+    const uint64_t below_a = a >= 64 ? ~0ull : (1ull << a) - 1, below_b = b >= 64 ? ~0ull : (1ull << b) - 1;
+    const uint64_t rng = below_b & ~below_a;
+    const int g8 = 8 * ((threadIdx.x & 63) >> 4);
+    ok = (((uint32_t)rng >> g8) & 0xffu) | ((((uint32_t)(rng >> 32)) >> g8) & 0xffu) << 8;
   }
   v.okm = ok;
   return v;
@@ -398,18 +452,31 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 
 template <int D>
 struct AtState {
-  float m, lpart;         // running max (base 2) and this lane's partial sum
+  float m;                // running max (base 2)
+  f32x4 lsum;             // row sums from the matrix cores: element 0 of lanes 0..15 (tile row 0)
   f32x4 o[D / 16];
 };
 
 // Consume the tile (cursor c) staged in stage s for the QG query groups of
 // this wave.  Score slot (rt, 4g + i) of a lane is item
 // 32(rt/2) + 8g + 4(rt%2) + i of the tile.
+// Consume the tile (cursor c) staged in stage s for the QG query groups of
+// this wave.  Score slot (rt, 4g + i) of a lane is item
+// 32(rt/2) + 8g + 4(rt%2) + i of the tile.
+//
+// Every item's logit is s2 (score + b): b = 0 for exact keys, and for far
+// items their bias divided by s2 (the log-count or tilt bias, minus infinity
+// for retrieved and empty clusters).  The raw scores are adjusted in place
+// (far tiles add b; tiles with invalid items replace those scores by minus
+// infinity, not offset them, since rows outside the key segments of a level
+// hold unspecified values), and one softmax step follows for every kind of
+// tile, with the scale folded into the exponent.
 template <typename TIn, int D, int WAVES, int QG, bool CAUSAL>
 __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm, const unsigned char* stg,
                                              const TileView& tv,
                                              const u16x8 (&qf)[QG][D / 32][sizeof(TIn) == 2 ? 1 : 3],
-                                             AtState<D> (&st)[QG], float s2, const int (&qrow)[QG]) {
+                                             AtState<D> (&st)[QG], float s2, const int (&qrow)[QG],
+                                             const u16x8& ones) {
   using G = AtGeo<TIn, D>;
   constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
   constexpr int KS = D / 32, DT = D / 16;
@@ -432,54 +499,40 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
       for (int qg = 0; qg < QG; ++qg) sc[qg][rt] = mfma_split<NS, NS>(a, qf[qg][k], sc[qg][rt]);
     }
   }
-  // far: every item is a real cluster row with a finite score, weighted by
-  // its log-count bias (minus infinity for retrieved and empty clusters);
-  // exact: the lane's valid items (a masked row's logit is replaced, not
-  // offset, since rows outside the key segments of a level hold unspecified
-  // values); plain: neither
-  const bool far = tv.far, plain = tv.plain;
-  const uint32_t ok = tv.okm;
-  f32x4 bv[RT];
-  if (far) {
+  if (tv.far) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
-      bv[rt] = *reinterpret_cast<const f32x4*>(&sm.far_bias[tv.row0 + it0]);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.far_bias[tv.row0 + it0]);
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) sc[qg][rt] += b;
+    }
+  } else if (!tv.plain) {
+    const uint32_t ok = tv.okm;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // an all-ones / all-zeros mask from the item's bit selects the score
+        const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)ok, rt * 4 + i, 1);
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+          float v = __uint_as_float((__float_as_uint(sc[qg][rt][i]) & keep) | (0xff800000u & ~keep));
+          if (CAUSAL && tv.row0 + it0 + i > qrow[qg]) v = -INFINITY;
+          sc[qg][rt][i] = v;
+        }
+      }
     }
   }
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
-    float x[RT * 4];
     float mloc = -INFINITY;
-    if (plain) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sc[qg][rt][i]);
-      mloc *= s2;
-    } else if (far) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = fmaf(s2, sc[qg][rt][i], bv[rt][i]);
-          x[rt * 4 + i] = v;
-          mloc = fmaxf(mloc, v);
-        }
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int it0 = 32 * (rt >> 1) + 8 * g + 4 * (rt & 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = (ok >> (rt * 4 + i)) & 1u ? s2 * sc[qg][rt][i] : -INFINITY;
-          if (CAUSAL && tv.row0 + it0 + i > qrow[qg]) v = -INFINITY;
-          x[rt * 4 + i] = v;
-          mloc = fmaxf(mloc, v);
-        }
-      }
-    }
-    mloc = max4_lanes(mloc);
+      for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sc[qg][rt][i]);
+    mloc = max4_lanes(mloc * s2);
     // lazy rescale: the running max of a row moves only when the tile's max
     // exceeds it by more than 8 (weights stay below 2^8, exact in the end
     // since output and normaliser share the same max)
@@ -487,29 +540,15 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
     const bool grow = mcand > st[qg].m + 8.f;
     if (__any(grow)) {
       const float alpha = grow ? __builtin_amdgcn_exp2f(st[qg].m - mcand) : 1.f;
-      st[qg].lpart *= alpha;
+      st[qg].lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) st[qg].o[dt] *= alpha;
       st[qg].m = grow ? mcand : st[qg].m;
     }
     const float mref = st[qg].m;
-    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
-    if (plain) {
+    float x[RT * 4];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[rt * 4 + i] = __builtin_amdgcn_exp2f(fmaf(sc[qg][rt][i], s2, -mref));
-          ps4[i] += x[rt * 4 + i];
-        }
-    } else {
-#pragma unroll
-      for (int j = 0; j < RT * 4; ++j) {
-        x[j] = __builtin_amdgcn_exp2f(x[j] - mref);
-        ps4[j & 3] += x[j];
-      }
-    }
-    st[qg].lpart += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+    for (int j = 0; j < RT * 4; ++j) x[j] = __builtin_amdgcn_exp2f(fmaf(sc[qg][j / 4][j % 4], s2, -mref));
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) {
       // P^T slots 8g + j: items 32ps + 8g + j
@@ -535,6 +574,8 @@ __device__ __forceinline__ void consume_tile(const AtSmem<TIn, D, WAVES, QG>& sm
         lds_frag<TIn, NS>(vst + d * VROW, 4 * ps + g, keyv(d), va);
         st[qg].o[dt] = mfma_split<NS, NS>(va, pb, st[qg].o[dt]);
       }
+      // the row sums of the same (rounded) weights: a row of ones times P^T
+      st[qg].lsum = mfma_split<1, NS>(&ones, pb, st[qg].lsum);
     }
   }
 }
@@ -557,6 +598,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   __shared__ SM sm;
   __shared__ __attribute__((aligned(16))) unsigned char stg[ST][G::SB];   // tile stages [key rows | value columns]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ws = __builtin_amdgcn_readfirstlane(w);
   const int col = lane & 15, g = lane >> 4;
   const float s2 = pl.scale * LOG2E;
   const int C = pl.C;
@@ -676,7 +718,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
           if (nc > 0) bias = __log2f((float)nc);
         }
       }
-      sm.far_bias[c] = bias;
+      sm.far_bias[c] = bias / s2;   // the logit is s2 (score + bias / s2)
     }
     int cc[4];
     if (tid < 64) {
@@ -750,20 +792,45 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   // two cursors: copies run PD tiles ahead of consumption.  Contiguous tiles
   // step through each cluster 64 rows at a time, gathered tiles 8 at a time.
   Cursor lc = cur_first(sm, src), cc = lc;
-  Chunks lgc = chunks_first(sm, src), cgc = lgc;
+  TileOffs<TIn, D, WAVES> toffs;
+  toffs.init(tid, src.nv, src.Cp);
+  Chunks lgc = chunks_first(sm, src);
+  TDesc gd;   // gathered tiles: the tile just issued (one stage: the next one consumed)
   auto issue_next = [&](unsigned char* dst) __attribute__((always_inline)) {
     if constexpr (GATHER) {
-      const TDesc d = take_tile(sm, src, lgc);
-      issue_tile_g<TIn, D, WAVES>(dst, src, d);
+      gd = take_tile(sm, src, lgc);
+      // far tiles are 64 consecutive clusters: scalar bases when in range
+      if (gd.far && gd.base[0] + AT_KT <= src.Ck && gd.base[0] + AT_KT <= src.Cp) {
+        const size_t r0 = (size_t)gd.base[0] * sizeof(TIn);
+        issue_tile_fast<TIn, D, WAVES>(dst, reinterpret_cast<const unsigned char*>(src.mu) + r0 * D,
+                                       reinterpret_cast<const unsigned char*>(src.T) + r0, toffs.k, toffs.vf, ws);
+      } else {
+        issue_tile_g<TIn, D, WAVES>(dst, src, gd);
+      }
     } else {
-      issue_tile<TIn, D, WAVES>(dst, src, lc);
+      // a tile whose rows and value columns all lie inside their arrays is
+      // copied with scalar bases; tiles at an array's end clamp (issue_tile)
+      const bool far = lc.t < src.nfar;
+      const int kcap = far ? src.Ck - 1 : src.kmax;
+      const int vstride = far ? src.Cp : src.nv;
+      if (lc.row0 + AT_KT - 1 <= kcap && lc.row0 + AT_KT <= vstride) {
+        const size_t r0 = (size_t)lc.row0 * sizeof(TIn);
+        if (far)
+          issue_tile_fast<TIn, D, WAVES>(dst, reinterpret_cast<const unsigned char*>(src.mu) + r0 * D,
+                                         reinterpret_cast<const unsigned char*>(src.T) + r0, toffs.k, toffs.vf, ws);
+        else
+          issue_tile_fast<TIn, D, WAVES>(dst, reinterpret_cast<const unsigned char*>(src.Kx) + r0 * D,
+                                         reinterpret_cast<const unsigned char*>(src.Vt) + r0, toffs.k, toffs.vx, ws);
+      } else {
+        issue_tile<TIn, D, WAVES>(dst, src, lc);
+      }
       lc = cur_next(sm, src, lc);
     }
   };
   auto view_next = [&]() __attribute__((always_inline)) -> TileView {
     if constexpr (GATHER) {
-      const TDesc d = take_tile(sm, src, cgc);
-      return view_of(d);
+      static_assert(!GATHER || PD == 0, "gathered tiles are consumed right after they are issued");
+      return view_of(gd);
     } else {
       const TileView v = view_of<MODE == MODE_LOCAL>(src, cc, qlo);
       cc = cur_next(sm, src, cc);
@@ -790,10 +857,15 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
       for (int sp = 0; sp < NS; ++sp) asm volatile("" : "+v"(qf[qg][k][sp]));
     }
     st[qg].m = -1e30f;
-    st[qg].lpart = 0.f;
+    st[qg].lsum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st[qg].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // A operand of the row sums: row 0 all ones, the other rows zero (lane l
+  // holds row l % 16)
+  u16x8 ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = col == 0 ? (uint16_t)0x3F80 : (uint16_t)0;
   int qmask[QG];
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) qmask[qg] = myq[qg] < 0 ? -1 : myq[qg];
@@ -820,7 +892,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
       if (t + PD < ntiles) issue_next(stg[sl]);
     }
     const TileView tv = view_next();
-    consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, stg[sc_], tv, qf, st, s2, qmask);
+    consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, stg[sc_], tv, qf, st, s2, qmask, ones);
     sl = sl + 1 == ST ? 0 : sl + 1;
     sc_ = sc_ + 1 == ST ? 0 : sc_ + 1;
   }
@@ -830,7 +902,9 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   // ---- finish: normalise, write or merge (lse in natural log units) ----
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
-    float l = st[qg].lpart;
+    // rows 1..15 of the row-sum tile are zero: lanes 16..63 and elements
+    // 1..3 hold nothing, lane col element 0 holds the sum of query col
+    float l = st[qg].lsum[0];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     const int row = myq[qg];

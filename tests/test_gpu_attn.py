@@ -165,3 +165,10 @@ def test_separate_query_and_key_cluster_counts(cq, ck, causal, dtype):
     points of each side's length), acausal and causal."""
     run_case(1, 4, 2, 3000 if not causal else 2500, 64, dtype, cq, 3, 3, causal=causal,
              block=256 if causal else 0, seed=40 + cq, comps=24, init=True, ck=ck)
+
+
+def test_large_clusters():
+    # clusters of ~250 rows (acausal) and ~512 rows (causal level of span 4096):
+    # many contiguous exact tiles per retrieved cluster
+    run_case(1, 2, 1, 4000, 64, "bf16", 16, 3, 2, seed=31, comps=16)
+    run_case(1, 2, 1, 8192, 64, "bf16", 8, 2, 2, causal=True, block=1024, seed=32, comps=8)
