@@ -39,6 +39,7 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "c4"
+BLOCKS_K2 = 4      # blocks retrieved inside each retrieved cluster (spatial-block scheme)
 SWEEP = ("c2", "c3", "c5")
 
 
@@ -59,6 +60,7 @@ def parse():
                     help="seconds of oracle work per workload (bounded sample)")
     ap.add_argument("--no-exact", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-blocks", action="store_true", help="skip the spatial-block scheme entry")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain copy of this many MiB (for PMC byte-counter scaling)")
     return ap.parse_args()
@@ -440,6 +442,27 @@ def run_workload(name, args, torch, M, synth, steps, warmup, headline):
         res["exact_tilt"] = {"impl": "museattn_fwd with the exact exponential tilt (forward only)",
                              "ms": round(x_ms, 4), "rse_vs_exact": round(x_rse, 5), "rse_row_mean": round(x_row, 5)}
         del Ox, lx, stx, wsx
+        if w.causal and not args.no_blocks:
+            # the causal scheme on spatial blocks with accumulated summaries:
+            # coarse query clusters (the block's queries in groups of about
+            # 64), the workload's key clusters and k1, k2 blocks per cluster
+            cq = max(1, w.block // 64)
+            bcfg = M.make_cfg(cq, w.iters, w.topk, True, w.block, ck=w.C, blocks=True, topk2=BLOCKS_K2)
+            Ob, lb, stb = M.museattn_fwd(Q, K, V, bcfg)
+            wsb = torch.empty(M.layout(w.B, w.Hq, w.Hkv, w.N, w.D, M._dt(Q), bcfg)["ws_bytes"],
+                              dtype=torch.uint8, device="cuda")
+
+            def fb():
+                M.museattn_fwd(Q, K, V, bcfg, state=stb, ws=wsb, out=(Ob, lb))
+            fb()
+            b_ms = time_steps(fb, max(3, min(steps // 4, 10)), torch)[0]
+            b_rse, b_row = rse_vs_exact(Q, K, V, Ob, w, torch)
+            res["spatial_blocks"] = {
+                "impl": "museattn_fwd, causal spatial blocks with accumulated summaries and two-level "
+                        "retrieval (exact tilt; forward only)",
+                "query_clusters": cq, "key_clusters": w.C, "k1": w.topk, "k2": BLOCKS_K2,
+                "ms": round(b_ms, 4), "rse_vs_exact": round(b_rse, 5), "rse_row_mean": round(b_row, 5)}
+            del Ob, lb, stb, wsb
         if headline:
             # the build's own exact attention: every cluster retrieved (forward only)
             own_ms, O_own = own_exact_ms(Q, K, V, w, M, max(2, min(steps // 4, 5)), torch)
@@ -486,7 +509,7 @@ def main():
         "effective_pct_of_mfma_peak": head["effective_pct_of_mfma_peak"],
     }
     for k in ("roofline", "kernels", "levels", "exact_attention_same_gpu", "rse_vs_exact", "rse_row_mean",
-              "exact_tilt", "exact_attention_own_kernels", "cpu_baseline"):
+              "exact_tilt", "spatial_blocks", "exact_attention_own_kernels", "cpu_baseline"):
         if k in head:
             out[k] = head[k]
     if not args.no_sweep:

@@ -48,7 +48,7 @@
 
 namespace muse {
 
-enum { MODE_ACAUSAL = 0, MODE_LEVEL = 1, MODE_LOCAL = 2 };
+enum { MODE_ACAUSAL = 0, MODE_LEVEL = 1, MODE_LOCAL = 2, MODE_V4 = 3 };
 constexpr int AT_KT = 64;   // items per tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -418,6 +418,7 @@ __device__ __forceinline__ TileView view_of(const TileSrc& src, const Cursor& c,
 // q = floor(i / blk) has bit l set (and segment q >> (l+1) exists).
 __device__ __forceinline__ int last_level(const Plan& pl, int i) {
   const int q = i / pl.blk;
+  if (pl.v4) return q >= 1 ? 0 : -1;   // spatial blocks: one pass for every block after the first
   int last = -1;
   for (int l = 0; l < pl.nlev; ++l)
     if (((q >> l) & 1) && (q >> (l + 1)) < pl.lev_nseg[l]) last = l;
@@ -603,7 +604,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   const float s2 = pl.scale * LOG2E;
   const int C = pl.C;
 
-  int bh, kvh, ap = 0, I = 0, tile, kp = 0, Ck = 0, q0 = 0, k0 = 0;
+  int bh, kvh, ap = 0, I = 0, tile, kp = 0, Ck = 0, q0 = 0, k0 = 0, vb = 0;
   int qlo = 0, qhi = 0;
   if (MODE == MODE_LOCAL) {
     const int nblk = (pl.N + pl.blk - 1) / pl.blk;
@@ -618,9 +619,14 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     if (qlo >= qhi) return;
     k0 = b0;
   } else {
-    const int nseg = pl.lev_nseg[lev];
-    const int m = pl.lev_m[lev];
-    const int spp = (m + QT - 1) / QT + C;
+    // MODE_V4: problem t is query block t + 1 of a head; its query groups
+    // are the query clusters' runs inside that block (q_perm positions
+    // v4 qb[I][block] .. qb[I][block + 1])
+    constexpr bool V4 = MODE == MODE_V4;
+    const int nseg = V4 ? pl.nb - 1 : pl.lev_nseg[lev];
+    const int m = V4 ? pl.blk : pl.lev_m[lev];
+    const int Cqs = V4 ? min(pl.Cq, pl.N) : C;
+    const int spp = (m + QT - 1) / QT + Cqs;
     // workgroups are dispatched round-robin over the 8 XCDs: keep every
     // problem on one XCD so its keys and values stay in that XCD's L2
     const int nprob = pl.B * pl.Hq * nseg;
@@ -630,20 +636,26 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     if (pid >= nprob) return;
     const int t = pid % nseg;
     bh = pid / nseg;
-    const int p = pl.lev_pfirst[lev] + t;
+    const int p = V4 ? 0 : pl.lev_pfirst[lev] + t;
+    vb = t + 1;
     ap = bh * pl.P + p;
     const Geom gm = prob_geom(pl, p);
-    const int Cq = min(C, gm.qn);
-    Ck = min(C, gm.kn);
+    const int Cq = V4 ? Cqs : min(C, gm.qn);
+    Ck = V4 ? min(pl.Ck, pl.N) : min(C, gm.kn);
     k0 = gm.k0;
     q0 = gm.q0;
-    const int32_t* qoffs = b.qs.offs + (size_t)ap * (C + 1);
+    // query group c of this problem: q_perm positions [qpos(c, 0), qpos(c, 1))
+    const int32_t* qoffs = V4 ? b.qb + (size_t)bh * pl.Cq * (pl.nb + 1) + vb : b.qs.offs + (size_t)ap * (C + 1);
+    const int qstr = V4 ? pl.nb + 1 : 1;
+    auto qpos = [&](int c, int e) __attribute__((always_inline)) {
+      return V4 ? qoffs[c * qstr + e] : qoffs[c + e];
+    };
     if (tid < 64) {
       int v[4], sum = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c = tid * 4 + q;
-        v[q] = c < Cq ? (qoffs[c + 1] - qoffs[c] + QT - 1) / QT : 0;
+        v[q] = c < Cq ? (qpos(c, 1) - qpos(c, 0) + QT - 1) / QT : 0;
         sum += v[q];
       }
       int inc = sum;
@@ -658,7 +670,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
         if (c < Cq && v[q] > 0 && slot >= run && slot < run + v[q]) {
           sm.sel[0] = c;
           sm.sel[1] = slot - run;
-          sm.sel[3] = qoffs[c];
+          sm.sel[3] = qpos(c, 0);
         }
         run += v[q];
       }
@@ -669,7 +681,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     I = sm.sel[0];
     tile = sm.sel[1];
     qlo = sm.sel[3] + tile * QT;
-    qhi = min(qoffs[I + 1], qlo + QT);
+    qhi = min(qpos(I, 1), qlo + QT);
     const int bq = bh / pl.Hq, hq = bh % pl.Hq;
     kvh = bq * pl.Hkv + (hq * pl.Hkv) / pl.Hq;
     kp = kvh * pl.P + p;
@@ -706,8 +718,11 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     const int32_t* Rr = b.R + ((size_t)ap * C + I) * pl.k1w;
     // far items: log2 n_c (value T_Ic / n_c), or with the exact tilt the
     // bias log2 Z_Ic - s log2(e) nu_I.kappa_Ic (key row kappa_Ic, value U_Ic)
+    constexpr bool V4 = MODE == MODE_V4;
     const bool xt = pl.dipole == 2;
-    const float* fbI = b.fb + ((size_t)ap * C + I) * b.Cp32;
+    // MODE_V4: the far items of group (I, block vb), one per key cluster
+    const size_t grp = V4 ? ((size_t)bh * pl.nb + vb) * pl.Cq + I : 0;
+    const float* fbI = V4 ? b.fbias + grp * b.Cp32 : b.fb + ((size_t)ap * C + I) * b.Cp32;
     for (int c = tid; c < MUSE_MAXC; c += NT) {
       float bias = -INFINITY;
       if (c < Ck) {
@@ -727,9 +742,22 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = tid * 4 + q;
-        cc[q] = r < pl.k1w ? Rr[r] : -1;
-        lo[q] = cc[q] >= 0 ? koffs[cc[q]] : 0;
-        hi[q] = cc[q] >= 0 ? koffs[cc[q] + 1] : 0;
+        if constexpr (V4) {
+          // retrieved (cluster, block) pairs: entry r is block slot r % k2w
+          // of retrieved cluster slot r / k2w
+          const size_t g1 = (((size_t)bh * pl.Cq + I) * pl.nb + vb) * pl.k1w;
+          const int j = r / pl.k2w;
+          const int c = r < pl.k1w * pl.k2w ? b.r1[g1 + j] : -1;
+          const int be = c >= 0 ? b.r2[g1 * pl.k2w + r] : -1;
+          const int32_t* kbr = b.kb + ((size_t)kvh * pl.Ck + max(c, 0)) * (pl.nb + 1);
+          cc[q] = -1;   // retrieved clusters keep their far item (the rest of their keys)
+          lo[q] = be >= 0 ? kbr[be] : 0;
+          hi[q] = be >= 0 ? kbr[be + 1] : 0;
+        } else {
+          cc[q] = r < pl.k1w ? Rr[r] : -1;
+          lo[q] = cc[q] >= 0 ? koffs[cc[q]] : 0;
+          hi[q] = cc[q] >= 0 ? koffs[cc[q] + 1] : 0;
+        }
         v[q] = hi[q] > lo[q] ? 1 : 0;
         sum += v[q];
       }
@@ -765,9 +793,14 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     src.nseg = __builtin_amdgcn_readfirstlane(sm.sel[4]);
     src.nfar = (Ck + AT_KT - 1) / AT_KT;
     src.Ck = max(Ck, 1);
-    src.mu = xt ? reinterpret_cast<const unsigned char*>(b.kap) + ((size_t)ap * C + I) * b.Cp32 * D * esz
-                : reinterpret_cast<const unsigned char*>(b.kst.mu_in) + (size_t)kp * C * D * esz;
-    src.T = reinterpret_cast<const unsigned char*>(b.T) + ((size_t)ap * C + I) * D * b.Cp32 * esz;
+    if constexpr (V4) {
+      src.mu = reinterpret_cast<const unsigned char*>(b.fk) + grp * b.Cp32 * D * esz;
+      src.T = reinterpret_cast<const unsigned char*>(b.fv) + grp * D * b.Cp32 * esz;
+    } else {
+      src.mu = xt ? reinterpret_cast<const unsigned char*>(b.kap) + ((size_t)ap * C + I) * b.Cp32 * D * esz
+                  : reinterpret_cast<const unsigned char*>(b.kst.mu_in) + (size_t)kp * C * D * esz;
+      src.T = reinterpret_cast<const unsigned char*>(b.T) + ((size_t)ap * C + I) * D * b.Cp32 * esz;
+    }
     const size_t slice = (size_t)lev * pl.B * pl.Hkv + kvh;
     src.Kx = reinterpret_cast<const unsigned char*>(b.kst.Kp) + slice * pl.N * D * esz;
     src.Vt = reinterpret_cast<const unsigned char*>(b.Vt) + slice * D * (size_t)b.Nv * esz;
@@ -1011,6 +1044,21 @@ static hipError_t attn_level(const Plan& pl, const AttnBufs& b, int lev, hipStre
   return hipGetLastError();
 }
 
+// Spatial blocks: one launch over the groups (query cluster, block) of
+// every block after the first.
+template <typename TIn, int D, int WAVES>
+static hipError_t attn_v4(const Plan& pl, const AttnBufs& b, hipStream_t st) {
+  constexpr int QT = 16 * WAVES;
+  const int spp = (pl.blk + QT - 1) / QT + std::min(pl.Cq, pl.N);
+  const long long nprob = (long long)pl.B * pl.Hq * (pl.nb - 1);
+  const long long grid = ((nprob + 7) / 8) * 8 * spp;
+  if (nprob <= 0) return hipSuccess;
+  MUSE_KT_PRE(st);
+  attn_kernel<TIn, TIn, D, WAVES, 1, MODE_V4><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, 0);
+  MUSE_KT_POST("attn_v4", st);
+  return hipGetLastError();
+}
+
 template <typename TIn, int D>
 static hipError_t attn_all(const Plan& pl, const AttnBufs& b, bool vt_done, hipStream_t st) {
   hipError_t e = vt_done ? hipSuccess : launch_vt<TIn, D>(pl, b, st);
@@ -1027,6 +1075,12 @@ static hipError_t attn_all(const Plan& pl, const AttnBufs& b, bool vt_done, hipS
     attn_kernel<TIn, TIn, D, WAVES, 1, MODE_LOCAL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, 0);
     MUSE_KT_POST("attn_local", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (pl.v4) {
+    const int avg = pl.blk / std::max(1, std::min(pl.Cq, pl.N));
+    if (avg >= 48) return attn_v4<TIn, D, 4>(pl, b, st);
+    if constexpr (sizeof(TIn) == 2 || D == 64) return attn_v4<TIn, D, 1>(pl, b, st);
+    return attn_v4<TIn, D, 4>(pl, b, st);
   }
   for (int lev = 0; lev < pl.nlev; ++lev) {
     // query clusters of ~m/C rows: the query tile (rows per workgroup) follows

@@ -81,7 +81,7 @@ static int build_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, 
   if (cfg->cq < 1 || cfg->cq > MUSE_MAX_CLUSTERS || cfg->ck < 1 || cfg->ck > MUSE_MAX_CLUSTERS)
     return MUSE_EINVAL;
   if (cfg->iters < 1 || cfg->topk < 0) return MUSE_EINVAL;
-  if (cfg->causal != 0 && cfg->causal != 1) return MUSE_EINVAL;
+  if (cfg->causal < 0 || cfg->causal > 2) return MUSE_EINVAL;
   if (cfg->init_mode != 0 && cfg->init_mode != 1) return MUSE_EINVAL;
   if (cfg->dipole < 0 || cfg->dipole > 2) return MUSE_EINVAL;
   if (cfg->causal && cfg->block < 1) return MUSE_EINVAL;
@@ -95,9 +95,30 @@ static int build_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, 
   pl.k1w = std::max(1, std::min(cfg->topk, cfg->ck));
   pl.dipole = cfg->dipole;
   pl.warm = cfg->init_mode;
-  pl.causal = cfg->causal;
+  pl.causal = cfg->causal ? 1 : 0;
   pl.blk = cfg->causal ? cfg->block : 0;
   pl.scale = cfg->scale > 0.f ? cfg->scale : (float)(1.0 / sqrt((double)D));
+  if (cfg->causal == 2) {
+    // spatial blocks with accumulated summaries: one clustering problem per
+    // head over all rows (the acausal geometry), exact local blocks, and one
+    // pass over the groups (query cluster, block) for everything earlier
+    if (cfg->dipole != 2) return MUSE_EUNSUPPORTED;
+    if (cfg->topk2 < 0 || (cfg->topk > 0 && cfg->topk2 < 1)) return MUSE_EINVAL;
+    const int64_t nb = (N + pl.blk - 1) / pl.blk;
+    if (nb > 4096) return MUSE_EUNSUPPORTED;
+    pl.v4 = 1;
+    pl.nb = (int)nb;
+    pl.topk2 = cfg->topk2;
+    pl.k2w = (int)std::max<int64_t>(1, std::min<int64_t>(cfg->topk2, nb));
+    if (pl.k1w * pl.k2w > MUSE_MAXC) return MUSE_EUNSUPPORTED;
+    pl.nlev = 1;
+    pl.lev_m[0] = (int)N;
+    pl.lev_nseg[0] = 1;
+    pl.lev_pfirst[0] = 0;
+    pl.lev_pfirst[1] = 1;
+    pl.P = 1;
+    return MUSE_OK;
+  }
   if (!pl.causal) {
     pl.nlev = 1;
     pl.lev_m[0] = (int)N;
@@ -211,10 +232,18 @@ static void build_layout(const Plan& pl, int dtype, Layout& out) {
   L.Kp = o; o = al(o + nl * BHk * N * D * eb);
   L.Vp = o; o = al(o + nl * BHk * N * D * eb);
   L.mu_in = o; o = al(o + BHk * P * C * D * eb);
+  // spatial-block scheme: retrieval of every group and block bounds
+  const size_t nb = pl.v4 ? pl.nb : 0, Cq = pl.Cq, Ck = pl.Ck;
+  L.nb = (int64_t)nb;
+  L.k2w = pl.v4 ? pl.k2w : 0;
+  L.v4_R1 = o; o = al(o + BHq * Cq * nb * pl.k1w * 4);
+  L.v4_R2 = o; o = al(o + BHq * Cq * nb * pl.k1w * (size_t)L.k2w * 4);
+  L.v4_kb = o; o = al(o + (pl.v4 ? BHk * Ck * (nb + 1) * 4 : 0));
+  L.v4_qb = o; o = al(o + (pl.v4 ? BHq * Cq * (nb + 1) * 4 : 0));
   L.state_bytes = std::max<size_t>(o, 256);
   build_kmlarge(pl, (int)(BHq + BHk), dtype, out.plocal, out.lg);
   size_t w = 0;
-  L.ws_T = w; w = al(w + BHq * P * C * D * L.Cp32 * eb);
+  L.ws_T = w; w = al(w + (pl.v4 ? 0 : BHq * P * C * D * L.Cp32 * eb));
   L.ws_oacc = w; w = al(w + (pl.causal ? BHq * N * D * 4 : 0));
   L.ws_lacc = w; w = al(w + (pl.causal ? BHq * N * 4 : 0));
   L.ws_Vt = w; w = al(w + (nl + (pl.causal ? 1 : 0)) * BHk * D * (size_t)L.Nv * eb);
@@ -223,10 +252,16 @@ static void build_layout(const Plan& pl, int dtype, Layout& out) {
   L.ws_part = w; w = al(w + kp_bytes);
   L.ws_pcnt = w; w = al(w + kc_bytes);
   // exact tilt: tilted key centroids per (I, c) and the two per-pair floats
-  const bool xt = pl.dipole == 2;
+  const bool xt = pl.dipole == 2 && !pl.v4;
   L.ws_kap = w; w = al(w + (xt ? BHq * P * C * L.Cp32 * D * eb : 0));
   L.ws_lz = w; w = al(w + (xt ? BHq * P * C * L.Cp32 * 4 : 0));
   L.ws_fb = w; w = al(w + (xt ? BHq * P * C * L.Cp32 * 4 : 0));
+  L.ws_v4pz = w; w = al(w + BHq * Cq * Ck * nb * 4);
+  L.ws_v4pk = w; w = al(w + BHq * Cq * Ck * nb * D * 4);
+  L.ws_v4pu = w; w = al(w + BHq * Cq * Ck * nb * D * 4);
+  L.ws_v4kap = w; w = al(w + BHq * nb * Cq * L.Cp32 * D * eb);
+  L.ws_v4T = w; w = al(w + BHq * nb * Cq * D * L.Cp32 * eb);
+  L.ws_v4fb = w; w = al(w + BHq * nb * Cq * L.Cp32 * 4);
   L.ws_bytes = std::max<size_t>(w, 256);
 }
 
@@ -380,6 +415,16 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
   ab.kap = wb + L.ws_kap;
   ab.lz = (float*)(wb + L.ws_lz);
   ab.fb = (float*)(wb + L.ws_fb);
+  ab.r1 = (int32_t*)(sb + L.v4_R1);
+  ab.r2 = (int32_t*)(sb + L.v4_R2);
+  ab.kb = (int32_t*)(sb + L.v4_kb);
+  ab.qb = (int32_t*)(sb + L.v4_qb);
+  ab.pz = (float*)(wb + L.ws_v4pz);
+  ab.pk = (float*)(wb + L.ws_v4pk);
+  ab.pu = (float*)(wb + L.ws_v4pu);
+  ab.fk = wb + L.ws_v4kap;
+  ab.fv = wb + L.ws_v4T;
+  ab.fbias = (float*)(wb + L.ws_v4fb);
   hipError_t e = hipGetLastError();  // clear stale errors from earlier calls
   (void)e;
   bool vt_done = false;   // the value copies built with the scores
@@ -388,7 +433,9 @@ int museattn_fwd(const void* Q, const void* K, const void* V, muse_dtype dtype, 
                            (int32_t*)(wb + L.ws_pcnt), st)) != hipSuccess)
       return hip_fail(e);
     if ((e = launch_summarize(pl, (int)dtype, ks, V, ab.kst, st)) != hipSuccess) return hip_fail(e);
-    if (pl.dipole == 2) {
+    if (pl.v4) {
+      if ((e = launch_v4(pl, (int)dtype, ab, st)) != hipSuccess) return hip_fail(e);
+    } else if (pl.dipole == 2) {
       if ((e = launch_tilt_exact(pl, (int)dtype, ab, st)) != hipSuccess) return hip_fail(e);
     } else if ((e = launch_score_tilt(pl, (int)dtype, ab, vt_done, st)) != hipSuccess) {
       return hip_fail(e);

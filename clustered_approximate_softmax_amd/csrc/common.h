@@ -41,6 +41,8 @@ struct Plan {
   int32_t nlev, P;          // levels, problems per head
   int32_t causal, blk, iters, topk, k1w, dipole;   // dipole: 0 monopole, 1 dipole, 2 exact tilt
   int32_t warm;             // 1: k-means starts from the centroids already in the state
+  int32_t v4;               // 1: causal spatial blocks with accumulated summaries (one problem per head)
+  int32_t nb, topk2, k2w;   // v4: blocks, retrieved blocks per retrieved cluster (and its storage width)
   float scale;
   int32_t lev_m[MUSE_MAXLEV];
   int32_t lev_nseg[MUSE_MAXLEV];
@@ -56,7 +58,7 @@ __host__ __device__ inline Geom prob_geom(const Plan& pl, int p) {
   int lev = 0;
   while (lev + 1 < pl.nlev && pl.lev_pfirst[lev + 1] <= p) ++lev;
   g.lev = lev;
-  if (!pl.causal) {
+  if (!pl.causal || pl.v4) {
     g.k0 = 0; g.kn = pl.N; g.q0 = 0; g.qn = pl.N;
     return g;
   }

@@ -57,6 +57,17 @@ struct AttnBufs {
   void* kap;              // exact tilt: tilted key centroids [B*Hq][P][C][Cp32][D] (input dtype)
   float* lz;              // exact tilt: ln Z_Ic [B*Hq][P][C][Cp32]
   float* fb;              // exact tilt: far bias log2 Z_Ic - s log2(e) nu_I.kappa_Ic, same layout
+  // spatial blocks with accumulated summaries (Plan::v4); layouts as in muse.h
+  int32_t* r1;            // [B*Hq][Cq][nb][k1w] retrieved clusters of each group
+  int32_t* r2;            // [B*Hq][Cq][nb][k1w][k2w] retrieved blocks
+  int32_t* kb;            // [B*Hkv][Ck][nb+1] block starts inside each key cluster's run
+  int32_t* qb;            // [B*Hq][Cq][nb+1] same for the query clusters
+  float* pz;              // [B*Hq][Cq][Ck][nb] ln Z of each (c, beta) seen from nu_I
+  float* pk;              // [B*Hq][Cq][Ck][nb][D] tilted key means
+  float* pu;              // [B*Hq][Cq][Ck][nb][D] tilted value means
+  void* fk;               // [B*Hq][nb][Cq][Cp32][D] far key rows of each group (input dtype)
+  void* fv;               // [B*Hq][nb][Cq][D][Cp32] far values (input dtype)
+  float* fbias;           // [B*Hq][nb][Cq][Cp32] far bias (base 2), -inf when empty
   float* oacc;            // causal running output [B*Hq][N][D] (fp32)
   float* lacc;            // causal running lse [B*Hq][N]
   void* O; float* lse;    // outputs
@@ -68,6 +79,11 @@ hipError_t launch_attn(const Plan& pl, int dtype, const AttnBufs& b, bool vt_don
 // Exactly tilted statistics (kap, T = tilted value means, lz, fb) and the
 // retrieval sets ranked by lz.
 hipError_t launch_tilt_exact(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
+
+// Spatial blocks with causally accumulated summaries: block bounds, the
+// exactly tilted statistics of every (query cluster, key cluster, block),
+// the two-level retrieval of every group and its far items.
+hipError_t launch_v4(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st);
 
 // Backward with the forward's clustering state held fixed.
 struct BwdLaunch {

@@ -1,0 +1,506 @@
+// Causal MuSe on spatial blocks with causally accumulated summaries
+// (gist.science page, Technical Summary, Core Mechanisms: Causal
+// Accumulation, Retrieval-Augmented Approximation, Exponential Tilting).
+//
+// Queries and keys are clustered once per head over all N rows (the acausal
+// clustering, so the stable cluster-contiguous order keeps every cluster's
+// rows ascending).  Block b holds rows [b B, (b + 1) B).  For query cluster
+// I (centroid nu_I) and a key set A, the exactly tilted statistics are
+//   lnZ = log sum_{j in A} exp(s nu_I.k_j),
+//   kappa = sum w_j k_j / sum w_j,  U = sum w_j v_j / sum w_j.
+// The group (I, b) -- the queries of cluster I in block b -- retrieves the
+// top-k1 key clusters by lnZ over their keys in blocks < b, inside each the
+// top-k2 blocks by lnZ over that block's keys (largest first, ties to the
+// lower index, empty sets never chosen), attends exactly to those keys and
+// to its own block, and sees every other earlier key through one far item
+// per key cluster: log-weight lnZ + s (q - nu_I).kappa and value U over the
+// cluster's earlier keys minus the retrieved blocks.
+//
+// Kernels, in launch order:
+//   v4_bounds   where each block starts inside every cluster's sorted run
+//   v4_part     lnZ, kappa, U of every (I, c, block): an online base-2
+//               softmax per lane group over the keys of each (c, block)
+//   v4_select   the two-level retrieval of every group: a running prefix
+//               of lnZ per key cluster, ranks for k1, and per retrieved
+//               cluster k2 rounds of a wave-wide argmax over the blocks
+//   v4_far      the far items of every group from the running prefix of
+//               the (I, c, block) statistics, for all key clusters
+//   v4_rem      the far items of the retrieved clusters again, now over
+//               their earlier keys minus the retrieved blocks (a sum of
+//               the remaining blocks' statistics, no subtraction)
+// The attention pass itself is attn_kernel's MODE_V4.
+#include <climits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace muse {
+
+constexpr float PX_LOG2E = 1.4426950408889634f;
+constexpr float PX_LN2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Block starts: bnd[c][beta] = first position of cluster c's run in the
+// sorted order whose row is >= beta B (beta = nb: the run's end).  One
+// thread per (set, head, cluster, beta); keys first, then queries.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) v4_bounds_kernel(Plan pl, CSet ks, CSet qs, int32_t* kb, int32_t* qb) {
+  const long long nk = (long long)ks.heads * pl.Ck * (pl.nb + 1);
+  const long long nq = (long long)qs.heads * pl.Cq * (pl.nb + 1);
+  long long id = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= nk + nq) return;
+  const bool key = id < nk;
+  if (!key) id -= nk;
+  const int Cs = key ? pl.Ck : pl.Cq;
+  const int beta = (int)(id % (pl.nb + 1));
+  const long long hc = id / (pl.nb + 1);
+  const int c = (int)(hc % Cs), head = (int)(hc / Cs);
+  const int32_t* offs = (key ? ks.offs : qs.offs) + (size_t)head * (pl.C + 1);
+  const int32_t* perm = (key ? ks.perm : qs.perm) + (size_t)head * pl.N;
+  int lo = offs[c], hi = offs[c + 1];
+  const long long lim = (long long)beta * pl.blk;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (perm[mid] < lim) lo = mid + 1;
+    else hi = mid;
+  }
+  (key ? kb : qb)[id] = lo;
+}
+
+// E elements of a row as fp32 (E a multiple of 8).
+template <typename TIn, int E>
+__device__ __forceinline__ void px_load(const TIn* p, float* out) {
+  static_assert(E % 8 == 0, "whole 16-byte loads");
+  if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+    for (int i = 0; i < E / 8; ++i) {
+      const u16x8 v = *reinterpret_cast<const u16x8*>(p + 8 * i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out[8 * i + j] = __uint_as_float((uint32_t)v[j] << 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[4 * i + j] = v[j];
+    }
+  }
+}
+
+// fp32 -> input dtype (bf16: round to nearest even), and back.
+template <typename TIn>
+__device__ __forceinline__ TIn px_round(float x) {
+  if constexpr (sizeof(TIn) == 2) {
+    const uint32_t u = __float_as_uint(x);
+    return (TIn)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  } else {
+    return x;
+  }
+}
+template <typename TIn>
+__device__ __forceinline__ float px_float(TIn v) {
+  if constexpr (sizeof(TIn) == 2) return __uint_as_float((uint32_t)v << 16);
+  else return v;
+}
+
+// Log-domain merge of (z, kappa, U) with (z2, kappa2, U2), natural logs;
+// a side with z = -inf is empty.
+template <int E>
+__device__ __forceinline__ void px_merge(float& z, float* k, float* u, float z2, const float* k2,
+                                         const float* u2) {
+  if (!(z2 > -INFINITY)) return;
+  const float zm = fmaxf(z, z2);
+  const float a = __expf(z - zm), w = __expf(z2 - zm);
+  const float inv = 1.f / (a + w);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    k[e] = (a * k[e] + w * k2[e]) * inv;
+    u[e] = (a * u[e] + w * u2[e]) * inv;
+  }
+  z = zm + __logf(a + w);
+}
+
+// ---------------------------------------------------------------------------
+// Statistics of every (I, c, block).  One wave per (q-head, 16 query
+// clusters, key cluster): lane = (query cluster il, quarter ds of the
+// feature dims); the four quarters' partial dot products are summed across
+// lanes, and each lane accumulates its quarter of sum w k and sum w v.
+// ---------------------------------------------------------------------------
+template <typename TIn, int D>
+__global__ void __launch_bounds__(256) v4_part_kernel(Plan pl, AttnBufs b) {
+  constexpr int E = D / 4;
+  const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int Cqe = min(pl.Cq, pl.N), Cke = min(pl.Ck, pl.N);
+  const int nIt = (Cqe + 15) / 16;
+  if (wave >= (long long)pl.B * pl.Hq * nIt * Cke) return;   // whole waves: no barriers below
+  const int c = (int)(wave % Cke);
+  const long long r = wave / Cke;
+  const int it = (int)(r % nIt), bh = (int)(r / nIt);
+  const int bq = bh / pl.Hq, hq = bh % pl.Hq;
+  const int kvh = bq * pl.Hkv + (hq * pl.Hkv) / pl.Hq;
+  const int il = lane & 15, ds = lane >> 4;
+  const int I = it * 16 + il;
+  const bool Iok = I < Cqe;
+  const float s2 = pl.scale * PX_LOG2E;
+  float nu[E];
+  {
+    const float* nup = b.qs.cent + ((size_t)bh * pl.C + (Iok ? I : 0)) * D + ds * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) nu[e] = Iok ? nup[e] * s2 : 0.f;
+  }
+  const int32_t* kbr = b.kb + ((size_t)kvh * pl.Ck + c) * (pl.nb + 1);
+  const TIn* Kp = reinterpret_cast<const TIn*>(b.kst.Kp) + (size_t)kvh * pl.N * D + ds * E;
+  const TIn* Vp = reinterpret_cast<const TIn*>(b.kst.Vp) + (size_t)kvh * pl.N * D + ds * E;
+  const size_t row = ((size_t)bh * pl.Cq + (Iok ? I : 0)) * pl.Ck + c;   // (I, c): nb entries
+  int r1 = kbr[0];
+  for (int beta = 0; beta < pl.nb; ++beta) {
+    const int r0 = r1;
+    r1 = kbr[beta + 1];
+    float m = -INFINITY, z = 0.f, ak[E], au[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) { ak[e] = 0.f; au[e] = 0.f; }
+    for (int j = r0; j < r1; ++j) {
+      float kx[E], vx[E];
+      px_load<TIn, E>(Kp + (size_t)j * D, kx);
+      px_load<TIn, E>(Vp + (size_t)j * D, vx);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) d = fmaf(nu[e], kx[e], d);
+      d += __shfl_xor(d, 16, 64);
+      d += __shfl_xor(d, 32, 64);
+      const float mn = fmaxf(m, d);
+      const float sc = __builtin_amdgcn_exp2f(m - mn), p = __builtin_amdgcn_exp2f(d - mn);
+      z = fmaf(z, sc, p);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        ak[e] = fmaf(ak[e], sc, p * kx[e]);
+        au[e] = fmaf(au[e], sc, p * vx[e]);
+      }
+      m = mn;
+    }
+    if (Iok) {
+      const bool ne = r1 > r0;
+      const float inv = ne ? 1.f / z : 0.f;
+      if (ds == 0) b.pz[row * pl.nb + beta] = ne ? (m + __log2f(z)) * PX_LN2 : -INFINITY;
+      float* pk = b.pk + (row * pl.nb + beta) * D + ds * E;
+      float* pu = b.pu + (row * pl.nb + beta) * D + ds * E;
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        *reinterpret_cast<f32x4*>(pk + e) = f32x4{ak[e], ak[e + 1], ak[e + 2], ak[e + 3]} * inv;
+        *reinterpret_cast<f32x4*>(pu + e) = f32x4{au[e], au[e + 1], au[e + 2], au[e + 3]} * inv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Two-level retrieval of every group (I, b).  One workgroup per (q-head, I);
+// thread c keeps the running lnZ of key cluster c over the blocks before b.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) v4_select_kernel(Plan pl, AttnBufs b) {
+  __shared__ float sz[MUSE_MAXC];
+  __shared__ int32_t selc[MUSE_MAXC];
+  __shared__ int32_t wcnt[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int Cke = min(pl.Ck, pl.N);
+  const int bh = blockIdx.x / pl.Cq, I = blockIdx.x % pl.Cq;
+  const int bq = bh / pl.Hq, hq = bh % pl.Hq;
+  const int kvh = bq * pl.Hkv + (hq * pl.Hkv) / pl.Hq;
+  const int c = tid;
+  const bool cok = c < Cke;
+  const int32_t* kbr = b.kb + ((size_t)kvh * pl.Ck + (cok ? c : 0)) * (pl.nb + 1);
+  const int kb0 = cok ? kbr[0] : 0;
+  const size_t irow = (size_t)bh * pl.Cq + I;
+  const float* pzr = b.pz + (irow * pl.Ck + (cok ? c : 0)) * pl.nb;
+  const int32_t* qbr = b.qb + irow * (pl.nb + 1);
+  const int k1 = min(pl.topk, Cke);
+  const int k12 = pl.k1w * pl.k2w;
+  const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  float run = -INFINITY;
+  for (int bb = 0; bb < pl.nb; ++bb) {
+    if (bb >= 1 && cok) {
+      const float z2 = pzr[bb - 1];
+      if (z2 > -INFINITY) {
+        const float zm = fmaxf(run, z2);
+        run = zm + __logf(__expf(run - zm) + __expf(z2 - zm));
+      }
+    }
+    int32_t* R1 = b.r1 + (irow * pl.nb + bb) * pl.k1w;
+    int32_t* R2 = b.r2 + (irow * pl.nb + bb) * k12;
+    const bool hasq = bb >= 1 && qbr[bb + 1] > qbr[bb];
+    if (!hasq || k1 == 0) {
+      for (int j = tid; j < pl.k1w; j += 256) R1[j] = -1;
+      for (int j = tid; j < k12; j += 256) R2[j] = -1;
+      continue;
+    }
+    // top-k1 clusters among those with keys before block bb
+    const bool valid = cok && kbr[bb] > kb0;
+    const float zc = valid ? run : -INFINITY;
+    sz[tid] = zc;
+    __syncthreads();
+    int rank = 0;
+    if (valid)
+      for (int c2 = 0; c2 < Cke; ++c2) {
+        const float z2 = sz[c2];
+        rank += (z2 > zc) || (z2 == zc && c2 < c);
+      }
+    const bool sel = valid && rank < k1;
+    const unsigned long long bal = __ballot(sel);
+    if (lane == 0) wcnt[w] = __popcll(bal);
+    __syncthreads();
+    int pre = 0;
+    for (int q = 0; q < w; ++q) pre += wcnt[q];
+    const int nsel = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    if (sel) {
+      const int pos = pre + __popcll(bal & lt);
+      R1[pos] = c;
+      selc[pos] = c;
+    }
+    for (int j = nsel + tid; j < pl.k1w; j += 256) R1[j] = -1;
+    __syncthreads();
+    // top-k2 blocks of each retrieved cluster: wave w takes slots w, w + 4, ...
+    // lane l owns blocks l + 64 t; bit t of `mine` marks a chosen one
+    for (int j = w; j < pl.k1w; j += 4) {
+      int32_t* out = R2 + (size_t)j * pl.k2w;
+      if (j >= nsel) {
+        for (int t = lane; t < pl.k2w; t += 64) out[t] = -1;
+        continue;
+      }
+      const int cj = selc[j];
+      const int32_t* kbj = b.kb + ((size_t)kvh * pl.Ck + cj) * (pl.nb + 1);
+      const float* pzj = b.pz + (irow * pl.Ck + cj) * pl.nb;
+      unsigned long long mine = 0;
+      for (int t = 0; t < pl.k2w; ++t) {
+        float best = -INFINITY;
+        int bi = INT_MAX;
+        for (int be = lane, u = 0; be < bb; be += 64, ++u) {
+          if (kbj[be + 1] <= kbj[be] || ((mine >> u) & 1)) continue;
+          const float v = pzj[be];
+          if (bi == INT_MAX || v > best) { best = v; bi = be; }   // blocks ascend per lane
+        }
+        for (int o = 32; o >= 1; o >>= 1) {
+          const float ob = __shfl_xor(best, o, 64);
+          const int oi = __shfl_xor(bi, o, 64);
+          if (oi != INT_MAX && (bi == INT_MAX || ob > best || (ob == best && oi < bi))) { best = ob; bi = oi; }
+        }
+        if (bi == INT_MAX) break;
+        if ((bi & 63) == lane) mine |= 1ull << (bi >> 6);
+      }
+      int pos = 0;
+      for (int t = 0; 64 * t < bb; ++t) {
+        const bool mt = (mine >> t) & 1;
+        const unsigned long long m = __ballot(mt);
+        if (mt) out[pos + __popcll(m & lt)] = 64 * t + lane;
+        pos += __popcll(m);
+      }
+      for (int t = pos + lane; t < pl.k2w; t += 64) out[t] = -1;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Far items of every group from the running prefix over the blocks.  One
+// workgroup per (q-head, I, chunk of CW key clusters) with QN x CW threads:
+// thread (part q, key cluster c) keeps 16 dims of kappa and U of c over the
+// blocks < b, so a wave writes 64 consecutive clusters of one value row of
+// the (d, c) layout at once.
+// ---------------------------------------------------------------------------
+template <int D>
+struct FarGeo {
+  static constexpr int DQ = 16, QN = D / DQ, CW = 1024 / QN;   // dims per thread, parts, clusters per workgroup
+};
+
+template <typename TIn, int D>
+__global__ void __launch_bounds__(1024) v4_far_kernel(Plan pl, AttnBufs b, int cw, int nchunk) {
+  constexpr int DQ = FarGeo<D>::DQ, QN = FarGeo<D>::QN;
+  __shared__ float red[QN][FarGeo<D>::CW];
+  const int tid = threadIdx.x;
+  const int q = tid / cw, cl = tid % cw;
+  const int Cke = min(pl.Ck, pl.N), Cqe = min(pl.Cq, pl.N);
+  const int chunk = blockIdx.x % nchunk;
+  const int bh = blockIdx.x / nchunk / pl.Cq, I = blockIdx.x / nchunk % pl.Cq;
+  const int c = chunk * cw + cl;
+  if (I >= Cqe) return;   // whole workgroup
+  const bool cin = c < (Cke + 63) / 64 * 64;   // columns written (whole far tiles)
+  const bool cok = c < Cke;
+  const float s2 = pl.scale * PX_LOG2E;
+  const size_t irow = (size_t)bh * pl.Cq + I;
+  const int32_t* qbr = b.qb + irow * (pl.nb + 1);
+  const float* nup = b.qs.cent + ((size_t)bh * pl.C + I) * D + q * DQ;   // read where needed
+  const size_t prow = irow * pl.Ck + (cok ? c : 0);
+  float z = -INFINITY, kap[DQ], u[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) { kap[e] = 0.f; u[e] = 0.f; }
+  const int Cp = b.Cp32;
+  for (int bb = 0; bb < pl.nb; ++bb) {
+    if (bb >= 1 && qbr[bb + 1] > qbr[bb]) {
+      const size_t g = ((size_t)bh * pl.nb + bb) * pl.Cq + I;
+      const bool ne = cok && z > -INFINITY;
+      TIn kr[DQ];
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        kr[e] = px_round<TIn>(ne ? kap[e] : 0.f);
+        dot = fmaf(nup[e], px_float<TIn>(kr[e]), dot);
+      }
+      dot *= s2;
+      if (cin) {
+        TIn* fk = reinterpret_cast<TIn*>(b.fk) + (g * Cp + c) * D + q * DQ;
+#pragma unroll
+        for (int e = 0; e < DQ; ++e) fk[e] = kr[e];
+        TIn* fv = reinterpret_cast<TIn*>(b.fv) + (g * D + q * DQ) * Cp + c;
+#pragma unroll
+        for (int e = 0; e < DQ; ++e) fv[(size_t)e * Cp] = px_round<TIn>(ne ? u[e] : 0.f);
+      }
+      red[q][cl] = dot;
+      __syncthreads();
+      if (q == 0 && cin) {
+        float tot = 0.f;
+#pragma unroll
+        for (int i = 0; i < QN; ++i) tot += red[i][cl];
+        b.fbias[g * Cp + c] = ne ? z * PX_LOG2E - tot : -INFINITY;
+      }
+      __syncthreads();
+    }
+    if (cok) {
+      const float z2 = b.pz[prow * pl.nb + bb];
+      if (z2 > -INFINITY) {
+        // merge block bb's statistics, four dims at a time
+        const float zm = fmaxf(z, z2);
+        const float a = __expf(z - zm), wgt = __expf(z2 - zm);
+        const float inv = 1.f / (a + wgt);
+        const float* k2 = b.pk + (prow * pl.nb + bb) * D + q * DQ;
+        const float* u2 = b.pu + (prow * pl.nb + bb) * D + q * DQ;
+#pragma unroll
+        for (int e = 0; e < DQ; e += 4) {
+          const f32x4 kk = *reinterpret_cast<const f32x4*>(k2 + e);
+          const f32x4 uu = *reinterpret_cast<const f32x4*>(u2 + e);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            kap[e + i] = (a * kap[e + i] + wgt * kk[i]) * inv;
+            u[e + i] = (a * u[e + i] + wgt * uu[i]) * inv;
+          }
+        }
+        z = zm + __logf(a + wgt);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Far items of the retrieved clusters: the earlier blocks that were not
+// retrieved, merged in block order.  One workgroup per group (q-head, b >= 1,
+// I), wave w takes retrieved slots w, w + 4, ...; lane = feature dims.
+// ---------------------------------------------------------------------------
+template <typename TIn, int D>
+__global__ void __launch_bounds__(256) v4_rem_kernel(Plan pl, AttnBufs b) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int id = blockIdx.x;
+  const int I = id % pl.Cq;
+  id /= pl.Cq;
+  const int bb = 1 + id % (pl.nb - 1), bh = id / (pl.nb - 1);
+  if (I >= min(pl.Cq, pl.N)) return;
+  const size_t irow = (size_t)bh * pl.Cq + I;
+  const int32_t* qbr = b.qb + irow * (pl.nb + 1);
+  if (qbr[bb + 1] <= qbr[bb]) return;
+  const float s2 = pl.scale * PX_LOG2E;
+  const int32_t* R1 = b.r1 + (irow * pl.nb + bb) * pl.k1w;
+  const int32_t* R2 = b.r2 + (irow * pl.nb + bb) * pl.k1w * pl.k2w;
+  const size_t g = ((size_t)bh * pl.nb + bb) * pl.Cq + I;
+  const int Cp = b.Cp32;
+  float nus[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) nus[e] = b.qs.cent[((size_t)bh * pl.C + I) * D + E * lane + e] * s2;
+  for (int j = w; j < pl.k1w; j += 4) {
+    const int c = R1[j];
+    if (c < 0) break;   // retrieved slots are ascending, padded with -1
+    const int32_t* sel = R2 + (size_t)j * pl.k2w;
+    const size_t prow = irow * pl.Ck + c;
+    float z = -INFINITY, kap[E], u[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) { kap[e] = 0.f; u[e] = 0.f; }
+    int p = 0;
+    for (int be = 0; be < bb; ++be) {
+      if (p < pl.k2w && sel[p] == be) { ++p; continue; }
+      const float z2 = b.pz[prow * pl.nb + be];
+      if (!(z2 > -INFINITY)) continue;
+      float k2[E], u2[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        k2[e] = b.pk[(prow * pl.nb + be) * D + E * lane + e];
+        u2[e] = b.pu[(prow * pl.nb + be) * D + E * lane + e];
+      }
+      px_merge<E>(z, kap, u, z2, k2, u2);
+    }
+    const bool ne = z > -INFINITY;
+    TIn kr[E];
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      kr[e] = px_round<TIn>(ne ? kap[e] : 0.f);
+      dot = fmaf(nus[e], px_float<TIn>(kr[e]), dot);
+    }
+    for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
+    TIn* fk = reinterpret_cast<TIn*>(b.fk) + (g * Cp + c) * D + E * lane;
+    TIn* fv = reinterpret_cast<TIn*>(b.fv) + (g * D + E * lane) * Cp + c;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      fk[e] = kr[e];
+      fv[(size_t)e * Cp] = px_round<TIn>(ne ? u[e] : 0.f);
+    }
+    if (lane == 0) b.fbias[g * Cp + c] = ne ? z * PX_LOG2E - dot : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename TIn, int D>
+static hipError_t v4_go(const Plan& pl, const AttnBufs& b, hipStream_t st) {
+  const int Cqe = std::min(pl.Cq, pl.N), Cke = std::min(pl.Ck, pl.N);
+  const long long BHq = (long long)pl.B * pl.Hq;
+  {
+    const long long n = ((long long)b.ks.heads * pl.Ck + (long long)b.qs.heads * pl.Cq) * (pl.nb + 1);
+    MUSE_KT_PRE(st);
+    v4_bounds_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(pl, b.ks, b.qs, b.kb, b.qb);
+    MUSE_KT_POST("v4_bounds", st);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    const long long waves = BHq * ((Cqe + 15) / 16) * Cke;
+    MUSE_KT_PRE(st);
+    v4_part_kernel<TIn, D><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(pl, b);
+    MUSE_KT_POST("v4_part", st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  MUSE_KT_PRE(st);
+  v4_select_kernel<<<(unsigned)(BHq * pl.Cq), 256, 0, st>>>(pl, b);
+  MUSE_KT_POST("v4_select", st);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    // clusters rounded up to whole waves, in chunks of at most CW
+    const int Cpk = (Cke + 63) / 64 * 64;
+    const int cw = std::min(Cpk, FarGeo<D>::CW), nchunk = (Cpk + cw - 1) / cw;
+    MUSE_KT_PRE(st);
+    v4_far_kernel<TIn, D><<<(unsigned)(BHq * pl.Cq * nchunk), FarGeo<D>::QN * cw, 0, st>>>(pl, b, cw, nchunk);
+    MUSE_KT_POST("v4_far", st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (pl.nb > 1 && pl.topk > 0) {
+    MUSE_KT_PRE(st);
+    v4_rem_kernel<TIn, D><<<(unsigned)(BHq * (pl.nb - 1) * pl.Cq), 256, 0, st>>>(pl, b);
+    MUSE_KT_POST("v4_rem", st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_v4(const Plan& pl, int dtype, const AttnBufs& b, hipStream_t st) {
+  if (dtype == 1) return pl.D == 64 ? v4_go<uint16_t, 64>(pl, b, st) : v4_go<uint16_t, 128>(pl, b, st);
+  return pl.D == 64 ? v4_go<float, 64>(pl, b, st) : v4_go<float, 128>(pl, b, st);
+}
+
+}  // namespace muse

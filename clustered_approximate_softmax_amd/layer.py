@@ -67,7 +67,7 @@ class MuseAttnFunction:
                 st = _new_state(q, k, cfg)
                 warm = cfg.init_mode == 1 and _seed_centroids(st, prev)
                 run = cfg if warm else M.muse_cfg(cfg.cq, cfg.ck, cfg.iters, cfg.topk, cfg.block, cfg.causal,
-                                                  cfg.dipole, 0, cfg.scale)
+                                                  cfg.dipole, 0, cfg.scale, cfg.topk2)
                 O, lse, st = M.museattn_fwd(q, k, v, run, state=st)
                 ctx.save_for_backward(q, k, v, O, lse)
                 ctx.state = st

@@ -37,17 +37,22 @@ class MuseError(RuntimeError):
 class muse_cfg(ctypes.Structure):
     _fields_ = [("cq", ctypes.c_int32), ("ck", ctypes.c_int32), ("iters", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("block", ctypes.c_int32), ("causal", ctypes.c_int32),
-                ("dipole", ctypes.c_int32), ("init_mode", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("dipole", ctypes.c_int32), ("init_mode", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("topk2", ctypes.c_int32)]
 
 
 LAYOUT_FIELDS = ["P", "L", "C", "k1w", "Cp32", "Nv"]
 LAYOUT_OFFS = ["q_labels", "k_labels", "q_perm", "k_perm", "q_offs", "k_offs", "q_cent", "k_cent",
                "mu", "S", "M", "R", "Kp", "Vp", "mu_in", "state_bytes", "ws_T", "ws_oacc", "ws_lacc", "ws_Vt", "ws_part",
                "ws_pcnt", "ws_bytes", "ws_kap", "ws_lz", "ws_fb"]
+LAYOUT_V4_FIELDS = ["nb", "k2w"]
+LAYOUT_V4_OFFS = ["v4_R1", "v4_R2", "v4_kb", "v4_qb", "ws_v4pz", "ws_v4pk", "ws_v4pu", "ws_v4kap", "ws_v4T",
+                  "ws_v4fb"]
 
 
 class muse_layout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int64) for n in LAYOUT_FIELDS] + [(n, ctypes.c_size_t) for n in LAYOUT_OFFS]
+    _fields_ = ([(n, ctypes.c_int64) for n in LAYOUT_FIELDS] + [(n, ctypes.c_size_t) for n in LAYOUT_OFFS]
+                + [(n, ctypes.c_int64) for n in LAYOUT_V4_FIELDS] + [(n, ctypes.c_size_t) for n in LAYOUT_V4_OFFS])
 
 
 _lib = None
@@ -109,13 +114,18 @@ TILT = {"monopole": 0, "dipole": 1, "exact": 2}
 
 
 def make_cfg(C, iters=10, topk=0, causal=False, block=0, dipole=True, scale=0.0, ck=None, warm=False,
-             tilt=None):
+             tilt=None, blocks=False, topk2=0):
     """C query clusters (and key clusters unless ck is given); warm: the
     k-means continues from the centroids of the state passed to the call;
-    tilt: "monopole", "dipole" or "exact" (overrides dipole)."""
+    tilt: "monopole", "dipole" or "exact" (overrides dipole); blocks: the
+    causal scheme on spatial blocks with accumulated summaries (causal = 2,
+    exact tilt, topk2 blocks inside each of the topk retrieved clusters)."""
+    if blocks:
+        tilt = "exact"
     mode = TILT[tilt] if tilt is not None else int(bool(dipole))
+    cz = 2 if blocks else int(bool(causal))
     return muse_cfg(int(C), int(C if ck is None else ck), int(iters), int(topk), int(block),
-                    int(bool(causal)), mode, int(bool(warm)), float(scale))
+                    cz, mode, int(bool(warm)), float(scale), int(topk2))
 
 
 def plan(N, cfg: muse_cfg):
@@ -131,7 +141,9 @@ def layout(B, Hq, Hkv, N, D, dtype, cfg: muse_cfg) -> dict:
     lay = muse_layout()
     _check("muse_layout_query", lib().muse_layout_query(B, Hq, Hkv, N, D, dtype, ctypes.byref(cfg),
                                                         ctypes.byref(lay)))
-    return {n: int(getattr(lay, n)) for n, _ in muse_layout._fields_}
+    out = {n: int(getattr(lay, n)) for n, _ in muse_layout._fields_}
+    out.update(cq=int(cfg.cq), ck=int(cfg.ck))
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -232,6 +244,13 @@ class State:
             "mu": (f32, (BHk, P, C, D)), "S": (f32, (BHk, P, C, D)),
             "M": (f32, (BHk, P, D, C, D)), "R": (i32, (BHq, P, C, k1w)),
         }
+        nb, k2w = self.lay["nb"], self.lay["k2w"]
+        if nb:
+            Cq, Ck = self.lay["cq"], self.lay["ck"]
+            shapes.update({
+                "v4_R1": (i32, (BHq, Cq, nb, k1w)), "v4_R2": (i32, (BHq, Cq, nb, k1w, k2w)),
+                "v4_kb": (i32, (BHk, Ck, nb + 1)), "v4_qb": (i32, (BHq, Cq, nb + 1)),
+            })
         dt, shp = shapes[name]
         return self._view(name, dt, shp)
 

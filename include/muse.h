@@ -69,7 +69,19 @@ enum {
  *   block    causal local block size (>= 1); ignored when causal == 0.
  *   causal   0: acausal; 1: causal hierarchy (exact local blocks of size
  *            `block`, approximated off-diagonal blocks on ceil(log2(
- *            ceil(N/block))) dyadic levels).
+ *            ceil(N/block))) dyadic levels); 2: causal spatial blocks with
+ *            causally accumulated summaries ([GIST] Causal Accumulation,
+ *            Retrieval-Augmented Approximation): queries and keys are
+ *            clustered once per head over all N rows; a query of cluster I
+ *            in block b = floor(i / block) attends exactly to the rows of
+ *            its own block up to itself, to the top-`topk` key clusters by
+ *            ln Z over the keys of earlier blocks and, inside each, to the
+ *            keys of its top-`topk2` earlier blocks by ln Z over that
+ *            block's keys; every other key of an earlier block enters
+ *            through one exactly tilted far item per key cluster (its
+ *            earlier keys minus the retrieved blocks).  Requires dipole == 2
+ *            (MUSE_EUNSUPPORTED otherwise), at most 4096 blocks and
+ *            k1w * k2w <= 256; museattn_bwd returns MUSE_EUNSUPPORTED.
  *   dipole   1: monopole + dipole summaries (first-order tilt: T_Ic =
  *            S_c + s M_c nu_I, far log-weight s q.mu_c + ln n_c; retrieval
  *            by s nu_I.mu_c + ln n_c); 0: monopole only (T_Ic = S_c);
@@ -89,10 +101,14 @@ enum {
  *            init_q / init_k are then ignored.  The library cannot check
  *            where those centroids came from.
  *   scale    softmax scale s applied to q.k; <= 0 means 1/sqrt(D).
+ *   topk2    k2, blocks retrieved inside each retrieved cluster (causal ==
+ *            2 only; >= 1 when topk >= 1, clamped to the number of blocks;
+ *            ignored otherwise).
  */
 typedef struct {
   int32_t cq, ck, iters, topk, block, causal, dipole, init_mode;
   float scale;
+  int32_t topk2;
 } muse_cfg;
 
 /*
@@ -140,6 +156,25 @@ typedef struct {
   size_t ws_kap;    /* dtype [B*Hq][P][C][Cp32][D] tilted key centroids kappa_Ic */
   size_t ws_lz;     /* fp32 [B*Hq][P][C][Cp32] ln Z_Ic (-inf: empty cluster) */
   size_t ws_fb;     /* fp32 [B*Hq][P][C][Cp32] log2 Z_Ic - s log2(e) nu_I.kappa_Ic */
+  /* causal == 2 only (zero-sized otherwise).  nb = ceil(N / block) blocks,
+     k2w = max(1, min(topk2, nb)); group (I, b) = queries of cluster I in
+     block b.  State: */
+  int64_t nb, k2w;
+  size_t v4_R1;     /* int32 [B*Hq][cq][nb][k1w] retrieved key clusters of each group,
+                       ascending, -1 pad (all -1 for groups without queries and b = 0) */
+  size_t v4_R2;     /* int32 [B*Hq][cq][nb][k1w][k2w] retrieved blocks of each retrieved
+                       cluster, ascending, -1 pad */
+  size_t v4_kb;     /* int32 [B*Hkv][ck][nb+1] position in k_perm of the first key of cluster c
+                       in block beta (beta = nb: end of the cluster) */
+  size_t v4_qb;     /* int32 [B*Hq][cq][nb+1] same for the queries in q_perm */
+  /* workspace: */
+  size_t ws_v4pz;   /* fp32 [B*Hq][cq][ck][nb] ln Z of the keys of (c, beta) seen from nu_I */
+  size_t ws_v4pk;   /* fp32 [B*Hq][cq][ck][nb][D] their tilted key mean */
+  size_t ws_v4pu;   /* fp32 [B*Hq][cq][ck][nb][D] their tilted value mean */
+  size_t ws_v4kap;  /* dtype [B*Hq][nb][cq][Cp32][D] far-item key rows kappa of each group */
+  size_t ws_v4T;    /* dtype [B*Hq][nb][cq][D][Cp32] far-item values U, index (d, c) */
+  size_t ws_v4fb;   /* fp32 [B*Hq][nb][cq][Cp32] far-item bias log2 Z - s log2(e) nu_I.kappa,
+                       -inf for an empty far item */
 } muse_layout;
 
 /*

@@ -145,3 +145,32 @@ def test_noalloc_forward_rejects_workspace_beyond_its_array():
     rc = L.museattn_fwd_noalloc(FAKE, FAKE, FAKE, M.MUSE_BF16, 1, 2, 2, 256, 32, ctypes.byref(big), None, None,
                                 FAKE, FAKE, FAKE, 1 << 40, None)
     assert rc == -1
+
+
+def test_spatial_block_scheme_validation_and_layout():
+    """causal = 2 (spatial blocks with accumulated summaries) needs the exact
+    tilt, k2 >= 1 when k1 >= 1, at most 4096 blocks and k1w * k2w <= 256;
+    its state holds the retrieval of every group and the block starts."""
+    L = M.lib()
+    ok = M.make_cfg(16, 3, 4, True, 64, ck=32, blocks=True, topk2=3)
+    lay = M.layout(1, 4, 2, 1000, 64, M.MUSE_BF16, ok)
+    assert lay["P"] == 1 and lay["L"] == 1 and lay["nb"] == 16 and lay["k2w"] == 3 and lay["k1w"] == 4
+    assert lay["v4_R2"] >= lay["v4_R1"] + 4 * 16 * 16 * 4 * 4
+    assert lay["state_bytes"] >= lay["v4_qb"] + 4 * 16 * 17 * 4
+    assert lay["ws_bytes"] >= lay["ws_v4fb"] + 4 * 16 * 16 * lay["Cp32"] * 4
+    assert lay["ws_oacc"] == lay["ws_T"]            # the hierarchy's T is not allocated
+    for bad, code in ((dict(tilt="dipole"), -3), (dict(topk2=0), -1), (dict(topk2=-1), -1)):
+        c = M.make_cfg(16, 3, 4, True, 64, ck=32, blocks=True, topk2=bad.get("topk2", 3))
+        if "tilt" in bad:
+            c.dipole = 1
+        assert L.muse_layout_query(1, 4, 2, 1000, 64, 1, ctypes.byref(c), ctypes.byref(M.muse_layout())) == code
+    many = M.make_cfg(16, 3, 4, True, 4, ck=32, blocks=True, topk2=3)        # 5000 blocks
+    assert L.muse_layout_query(1, 1, 1, 20000, 64, 1, ctypes.byref(many), ctypes.byref(M.muse_layout())) == -3
+    wide = M.make_cfg(16, 3, 32, True, 16, ck=32, blocks=True, topk2=9)     # 32 x 9 > 256 pairs
+    assert L.muse_layout_query(1, 1, 1, 1000, 64, 1, ctypes.byref(wide), ctypes.byref(M.muse_layout())) == -3
+    # no retrieval: k2 may be 0
+    none = M.make_cfg(16, 3, 0, True, 64, ck=32, blocks=True, topk2=0)
+    assert L.muse_layout_query(1, 1, 1, 1000, 64, 1, ctypes.byref(none), ctypes.byref(M.muse_layout())) == 0
+    # the backward does not cover the scheme
+    assert L.museattn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 4, 2, 1000, 64, ctypes.byref(ok), FAKE,
+                          1 << 40, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == -3
