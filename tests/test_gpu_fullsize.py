@@ -91,6 +91,50 @@ def test_full_c5_causal_64k_gqa_d128_forward():
     _run_full("c5", [(0, 5)], 64)
 
 
+def test_full_c4_spatial_blocks_64k():
+    """The causal scheme on spatial blocks at the 64k GQA workload, in the
+    configuration the benchmark times (16 query clusters for blocks of 1024,
+    128 key clusters, k1 = 8, k2 = 4): block starts exact for every head,
+    the retrieval of the sampled rows' groups a valid two-level top-k of the
+    oracle's scores, and the sampled rows equal to the oracle on shared
+    state."""
+    import torch
+
+    from oracle import muse_v4_oracle as v4
+    from tests import test_gpu_v4 as tv
+    w = synth.WORKLOADS["c4"]
+    cq, k2 = w.block // 64, 4
+    x = synth.make_inputs(w, with_do=False)
+    Q, K, V = (torch.from_numpy(x[k]).to(torch.bfloat16).cuda() for k in "QKV")
+    cfg = M.make_cfg(cq, w.iters, w.topk, True, w.block, ck=w.C, blocks=True, topk2=k2)
+    O, lse, st = M.museattn_fwd(Q, K, V, cfg)
+    torch.cuda.synchronize()
+    r = dict(x=x, ql=st.field("q_labels").cpu().numpy()[0], kl=st.field("k_labels").cpu().numpy()[0],
+             qoffs=st.field("q_offs").cpu().numpy()[:, 0], koffs=st.field("k_offs").cpu().numpy()[:, 0])
+    for n in ("v4_R1", "v4_R2", "v4_kb", "v4_qb"):
+        r[n] = st.field(n).cpu().numpy()
+    tv.check_bounds(r, w.B, w.Hq, w.Hkv, w.N, cq, w.C, w.block)
+    ocfg = mo.MuseConfig(cq=cq, ck=w.C, iters=w.iters, topk=w.topk, block=w.block, causal=True,
+                         exact_tilt=True)
+    rng = np.random.default_rng(11)
+    report = []
+    for (b, h) in ((0, 0), (0, 31)):
+        g = (h * w.Hkv) // w.Hq
+        qrows = np.sort(rng.choice(w.N, 40, replace=False))
+        aq = r["ql"][b * w.Hq + h]
+        groups = sorted({(int(aq[i]), int(i // w.block)) for i in qrows if i >= w.block})
+        tv.check_selection(r, b, h, w.Hq, w.Hkv, w.N, w.D, w.block, cq, w.topk, k2, ocfg.s(w.D), groups=groups)
+        sh = tv.shared_for(r, b, h, w.Hq, w.Hkv, w.N, w.block, cq)
+        o_ref, l_ref, _ = v4.forward_head(x["Q"][b, h], x["K"][b, g], x["V"][b, g], ocfg, k2, shared=sh,
+                                          qrows=qrows)
+        Og = O[b, h].float().cpu().numpy()
+        err = gu.max_rel(Og[qrows], o_ref[qrows])
+        assert err <= gu.TOL[w.dtype], (b, h, err)
+        gu.check_lse(lse[b, h].cpu().numpy()[qrows], l_ref[qrows], w.dtype, (b, h))
+        report.append((b, h, err))
+    print("c4 spatial blocks, max rel err vs oracle per sampled head:", report)
+
+
 def test_full_c4_forward_clustering_lockstep():
     """The forward's own clustering at the 64k GQA shape, every level: one
     run with 9 Lloyd iterations and one with 10 (default starting points);

@@ -75,8 +75,9 @@ def shared_for(r, b, h, Hq, Hkv, N, blk, cq):
     return dict(aq=aq, ak=ak, R1=sel)
 
 
-def check_selection(r, b, h, Hq, Hkv, N, D, blk, cq, k1, k2, scale, tie=gu.TIE):
-    """Every group's retrieval is a valid two-level top-k of the fp64 scores."""
+def check_selection(r, b, h, Hq, Hkv, N, D, blk, cq, k1, k2, scale, tie=gu.TIE, groups=None):
+    """Every group's retrieval (or that of the (I, block) pairs in `groups`)
+    is a valid two-level top-k of the fp64 scores."""
     g = (h * Hkv) // Hq
     bh = b * Hq + h
     Qh = r["x"]["Q"][b, h].astype(np.float64)
@@ -97,26 +98,26 @@ def check_selection(r, b, h, Hq, Hkv, N, D, blk, cq, k1, k2, scale, tie=gu.TIE):
             lo, hi = min(scores[i] for i in chosen), max(rest)
             assert hi <= lo + tie * max(abs(lo), abs(hi), 1.0), (what, lo, hi)
 
-    for bb in range(1, nb):
-        for I in range(min(cq, N)):
-            R1 = r["v4_R1"][bh, I, bb]
-            if not np.any(aq[bb * blk:(bb + 1) * blk] == I):
-                assert np.all(R1 == -1)
-                continue
-            pre = np.arange(bb * blk)
-            sig = [v4.set_score(Kh[pre[ak[pre] == c]], nu[I], scale) for c in range(int(ak.max()) + 1)]
-            cl = [int(c) for c in R1 if c >= 0]
-            assert np.all(R1[len(cl):] == -1)
-            ok_topk(sig, cl, k1, ("clusters", bh, I, bb))
-            for j, c in enumerate(cl):
-                bs = [v4.set_score(Kh[np.arange(be * blk, (be + 1) * blk)[ak[be * blk:(be + 1) * blk] == c]],
-                                   nu[I], scale) for be in range(bb)]
-                R2 = r["v4_R2"][bh, I, bb, j]
-                bl = [int(x) for x in R2 if x >= 0]
-                assert np.all(R2[len(bl):] == -1)
-                ok_topk(bs, bl, k2, ("blocks", bh, I, bb, c))
-            for j in range(len(cl), k1w):
-                assert np.all(r["v4_R2"][bh, I, bb, j] == -1)
+    todo = groups if groups is not None else [(I, bb) for bb in range(1, nb) for I in range(min(cq, N))]
+    for I, bb in todo:
+        R1 = r["v4_R1"][bh, I, bb]
+        if not np.any(aq[bb * blk:(bb + 1) * blk] == I):
+            assert np.all(R1 == -1)
+            continue
+        pre = np.arange(bb * blk)
+        sig = [v4.set_score(Kh[pre[ak[pre] == c]], nu[I], scale) for c in range(int(ak.max()) + 1)]
+        cl = [int(c) for c in R1 if c >= 0]
+        assert np.all(R1[len(cl):] == -1)
+        ok_topk(sig, cl, k1, ("clusters", bh, I, bb))
+        for j, c in enumerate(cl):
+            bs = [v4.set_score(Kh[np.arange(be * blk, (be + 1) * blk)[ak[be * blk:(be + 1) * blk] == c]],
+                               nu[I], scale) for be in range(bb)]
+            R2 = r["v4_R2"][bh, I, bb, j]
+            bl = [int(x) for x in R2 if x >= 0]
+            assert np.all(R2[len(bl):] == -1)
+            ok_topk(bs, bl, k2, ("blocks", bh, I, bb, c))
+        for j in range(len(cl), k1w):
+            assert np.all(r["v4_R2"][bh, I, bb, j] == -1)
 
 
 CASES = [
