@@ -588,12 +588,14 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   constexpr int NS = sizeof(TIn) == 2 ? 1 : 3;
   constexpr int NT = 64 * WAVES, QT = 16 * QG * WAVES;
   constexpr int KS = D / 32, DT = D / 16;
-  // one-wave workgroups (small query clusters) keep one stage: twice as many
-  // fit per CU, and the copy latency of one hides behind the others' work;
-  // four waves with one query group keep two (four workgroups per CU)
-  constexpr int ST = WAVES == 1 ? 1 : QG == 1 ? 2 : G::ST, PD = ST - 1;
-  // small query clusters (one-wave workgroups): tiles gathered from 8-row chunks
-  constexpr bool GATHER = WAVES == 1 && MODE != MODE_LOCAL;
+  // small query clusters (one-wave workgroups) and the spatial-block groups,
+  // whose retrieved (cluster, block) ranges hold a few keys each: tiles
+  // gathered from 8-row chunks
+  constexpr bool GATHER = (WAVES == 1 || MODE == MODE_V4) && MODE != MODE_LOCAL;
+  // gathered tiles keep one stage (one-wave workgroups: twice as many fit per
+  // CU, and the copy latency of one hides behind the others' work); four
+  // waves with one query group keep two (four workgroups per CU)
+  constexpr int ST = GATHER ? 1 : QG == 1 ? 2 : G::ST, PD = ST - 1;
   constexpr int LPT = (AT_KT * G::CHK + D * G::CHV) / NT;   // copies per thread per tile
   static_assert(PD * LPT <= 63, "copies in flight exceed the counter");
   __shared__ SM sm;

@@ -24,10 +24,8 @@
 //               of lnZ per key cluster, ranks for k1, and per retrieved
 //               cluster k2 rounds of a wave-wide argmax over the blocks
 //   v4_far      the far items of every group from the running prefix of
-//               the (I, c, block) statistics, for all key clusters
-//   v4_rem      the far items of the retrieved clusters again, now over
-//               their earlier keys minus the retrieved blocks (a sum of
-//               the remaining blocks' statistics, no subtraction)
+//               the (I, c, block) statistics; a retrieved cluster's item
+//               leaves out its retrieved blocks
 // The attention pass itself is attn_kernel's MODE_V4.
 #include <climits>
 
@@ -36,6 +34,7 @@
 
 namespace muse {
 
+constexpr int V4_MAXNB = 4096;   // blocks per sequence (checked on the host)
 constexpr float PX_LOG2E = 1.4426950408889634f;
 constexpr float PX_LN2 = 0.6931471805599453f;
 
@@ -102,23 +101,6 @@ template <typename TIn>
 __device__ __forceinline__ float px_float(TIn v) {
   if constexpr (sizeof(TIn) == 2) return __uint_as_float((uint32_t)v << 16);
   else return v;
-}
-
-// Log-domain merge of (z, kappa, U) with (z2, kappa2, U2), natural logs;
-// a side with z = -inf is empty.
-template <int E>
-__device__ __forceinline__ void px_merge(float& z, float* k, float* u, float z2, const float* k2,
-                                         const float* u2) {
-  if (!(z2 > -INFINITY)) return;
-  const float zm = fmaxf(z, z2);
-  const float a = __expf(z - zm), w = __expf(z2 - zm);
-  const float inv = 1.f / (a + w);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    k[e] = (a * k[e] + w * k2[e]) * inv;
-    u[e] = (a * u[e] + w * u2[e]) * inv;
-  }
-  z = zm + __logf(a + w);
 }
 
 // ---------------------------------------------------------------------------
@@ -200,6 +182,7 @@ __global__ void __launch_bounds__(256) v4_part_kernel(Plan pl, AttnBufs b) {
 // thread c keeps the running lnZ of key cluster c over the blocks before b.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) v4_select_kernel(Plan pl, AttnBufs b) {
+  __shared__ float bsc[4][V4_MAXNB];   // per wave: block scores of the cluster it ranks (-inf: not a candidate)
   __shared__ float sz[MUSE_MAXC];
   __shared__ int32_t selc[MUSE_MAXC];
   __shared__ int32_t wcnt[4];
@@ -219,9 +202,11 @@ __global__ void __launch_bounds__(256) v4_select_kernel(Plan pl, AttnBufs b) {
   const int k12 = pl.k1w * pl.k2w;
   const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   float run = -INFINITY;
+  float znext = cok ? pzr[0] : -INFINITY;   // block bb - 1's ln Z, loaded one block ahead
   for (int bb = 0; bb < pl.nb; ++bb) {
     if (bb >= 1 && cok) {
-      const float z2 = pzr[bb - 1];
+      const float z2 = znext;
+      znext = pzr[bb];
       if (z2 > -INFINITY) {
         const float zm = fmaxf(run, z2);
         run = zm + __logf(__expf(run - zm) + __expf(z2 - zm));
@@ -271,13 +256,16 @@ __global__ void __launch_bounds__(256) v4_select_kernel(Plan pl, AttnBufs b) {
       const int cj = selc[j];
       const int32_t* kbj = b.kb + ((size_t)kvh * pl.Ck + cj) * (pl.nb + 1);
       const float* pzj = b.pz + (irow * pl.Ck + cj) * pl.nb;
+      float* my = bsc[w];
+      // each lane stages and later scans only its own blocks be = lane + 64 u
+      for (int be = lane; be < bb; be += 64) my[be] = kbj[be + 1] > kbj[be] ? pzj[be] : -INFINITY;
       unsigned long long mine = 0;
       for (int t = 0; t < pl.k2w; ++t) {
         float best = -INFINITY;
         int bi = INT_MAX;
         for (int be = lane, u = 0; be < bb; be += 64, ++u) {
-          if (kbj[be + 1] <= kbj[be] || ((mine >> u) & 1)) continue;
-          const float v = pzj[be];
+          const float v = my[be];
+          if (!(v > -INFINITY) || ((mine >> u) & 1)) continue;
           if (bi == INT_MAX || v > best) { best = v; bi = be; }   // blocks ascend per lane
         }
         for (int o = 32; o >= 1; o >>= 1) {
@@ -302,21 +290,53 @@ __global__ void __launch_bounds__(256) v4_select_kernel(Plan pl, AttnBufs b) {
 }
 
 // ---------------------------------------------------------------------------
-// Far items of every group from the running prefix over the blocks.  One
-// workgroup per (q-head, I, chunk of CW key clusters) with QN x CW threads:
-// thread (part q, key cluster c) keeps 16 dims of kappa and U of c over the
-// blocks < b, so a wave writes 64 consecutive clusters of one value row of
-// the (d, c) layout at once.
+// Far items of every group.  One workgroup per (q-head, I, chunk of CW key
+// clusters) with QN x CW threads: thread (part q, key cluster c) keeps 8
+// dims of the running prefix (ln Z, kappa, U) of c over the blocks < b, so a
+// wave writes 64 consecutive clusters of one value row of the (d, c) layout
+// at once.  A cluster the group retrieved gets the prefix without its
+// retrieved blocks: with r = 1 - sum over those blocks of Z_block / Z_prefix,
+// kappa = (kappa_prefix - sum (Z_block / Z_prefix) kappa_block) / r (U alike)
+// and ln Z = ln Z_prefix + ln r.  Rounding is amplified by 1 / r, so when
+// r < 1/256 (the retrieved blocks hold nearly all of the prefix) the other
+// blocks are merged directly instead; an empty remainder (by key count)
+// gives no item.
 // ---------------------------------------------------------------------------
 template <int D>
 struct FarGeo {
-  static constexpr int DQ = 16, QN = D / DQ, CW = 1024 / QN;   // dims per thread, parts, clusters per workgroup
+  static constexpr int DQ = 8, QN = D / DQ, CW = 1024 / QN;   // dims per thread, parts, clusters per workgroup
 };
+
+// Merge the statistics of block be of row prow (dims off .. off + DQ) into (z, k, u).
+template <int D, int DQ>
+__device__ __forceinline__ void far_merge(const AttnBufs& b, size_t prow, int nb, int be, int off, float& z,
+                                          float* k, float* u) {
+  const float z2 = b.pz[prow * nb + be];
+  if (!(z2 > -INFINITY)) return;
+  const float zm = fmaxf(z, z2);
+  const float a = __expf(z - zm), wgt = __expf(z2 - zm);
+  const float inv = 1.f / (a + wgt);
+  const float* k2 = b.pk + (prow * nb + be) * D + off;
+  const float* u2 = b.pu + (prow * nb + be) * D + off;
+#pragma unroll
+  for (int e = 0; e < DQ; e += 4) {
+    const f32x4 kk = *reinterpret_cast<const f32x4*>(k2 + e);
+    const f32x4 uu = *reinterpret_cast<const f32x4*>(u2 + e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      k[e + i] = (a * k[e + i] + wgt * kk[i]) * inv;
+      u[e + i] = (a * u[e + i] + wgt * uu[i]) * inv;
+    }
+  }
+  z = zm + __logf(a + wgt);
+}
 
 template <typename TIn, int D>
 __global__ void __launch_bounds__(1024) v4_far_kernel(Plan pl, AttnBufs b, int cw, int nchunk) {
   constexpr int DQ = FarGeo<D>::DQ, QN = FarGeo<D>::QN;
   __shared__ float red[QN][FarGeo<D>::CW];
+  __shared__ int32_t slot[MUSE_MAXC];   // (block << 8) | retrieved slot, per key cluster
+  __shared__ int32_t r2s[MUSE_MAXC];    // the group's retrieved blocks, [slot][k2w]
   const int tid = threadIdx.x;
   const int q = tid / cw, cl = tid % cw;
   const int Cke = min(pl.Ck, pl.N), Cqe = min(pl.Cq, pl.N);
@@ -326,11 +346,17 @@ __global__ void __launch_bounds__(1024) v4_far_kernel(Plan pl, AttnBufs b, int c
   if (I >= Cqe) return;   // whole workgroup
   const bool cin = c < (Cke + 63) / 64 * 64;   // columns written (whole far tiles)
   const bool cok = c < Cke;
+  const int bq = bh / pl.Hq, hq = bh % pl.Hq;
+  const int kvh = bq * pl.Hkv + (hq * pl.Hkv) / pl.Hq;
   const float s2 = pl.scale * PX_LOG2E;
   const size_t irow = (size_t)bh * pl.Cq + I;
   const int32_t* qbr = b.qb + irow * (pl.nb + 1);
+  const int32_t* kbc = b.kb + ((size_t)kvh * pl.Ck + (cok ? c : 0)) * (pl.nb + 1);
   const float* nup = b.qs.cent + ((size_t)bh * pl.C + I) * D + q * DQ;   // read where needed
   const size_t prow = irow * pl.Ck + (cok ? c : 0);
+  const int k12 = pl.k1w * pl.k2w;
+  for (int t = tid; t < MUSE_MAXC; t += blockDim.x) slot[t] = -1;
+  __syncthreads();
   float z = -INFINITY, kap[DQ], u[DQ];
 #pragma unroll
   for (int e = 0; e < DQ; ++e) { kap[e] = 0.f; u[e] = 0.f; }
@@ -338,12 +364,70 @@ __global__ void __launch_bounds__(1024) v4_far_kernel(Plan pl, AttnBufs b, int c
   for (int bb = 0; bb < pl.nb; ++bb) {
     if (bb >= 1 && qbr[bb + 1] > qbr[bb]) {
       const size_t g = ((size_t)bh * pl.nb + bb) * pl.Cq + I;
-      const bool ne = cok && z > -INFINITY;
+      if (pl.topk > 0) {
+        const int32_t* R1 = b.r1 + (irow * pl.nb + bb) * pl.k1w;
+        const int32_t* R2 = b.r2 + (irow * pl.nb + bb) * k12;
+        if (tid < pl.k1w) {
+          const int cs = R1[tid];
+          if (cs >= 0) slot[cs] = (bb << 8) | tid;
+        }
+        if (tid < k12) r2s[tid] = R2[tid];
+        __syncthreads();
+      }
+      float zf = z, kf[DQ], uf[DQ];
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) { kf[e] = kap[e]; uf[e] = u[e]; }
+      const int sv = cok ? slot[c] : -1;
+      if (sv >= 0 && (sv >> 8) == bb) {
+        const int32_t* sel = r2s + (sv & 255) * pl.k2w;
+        int nrem = kbc[bb] - kbc[0];
+        float rho = 0.f;
+        for (int t = 0; t < pl.k2w; ++t) {
+          const int be = sel[t];
+          if (be < 0) break;
+          nrem -= kbc[be + 1] - kbc[be];
+          const float zb = b.pz[prow * pl.nb + be];
+          if (!(zb > -INFINITY)) continue;
+          const float wgt = __expf(zb - z);
+          rho += wgt;
+          const float* k2 = b.pk + (prow * pl.nb + be) * D + q * DQ;
+          const float* u2 = b.pu + (prow * pl.nb + be) * D + q * DQ;
+#pragma unroll
+          for (int e = 0; e < DQ; e += 4) {
+            const f32x4 kk = *reinterpret_cast<const f32x4*>(k2 + e);
+            const f32x4 uu = *reinterpret_cast<const f32x4*>(u2 + e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              kf[e + i] = fmaf(-wgt, kk[i], kf[e + i]);
+              uf[e + i] = fmaf(-wgt, uu[i], uf[e + i]);
+            }
+          }
+        }
+        const float r = 1.f - rho;
+        if (nrem == 0) {
+          zf = -INFINITY;
+        } else if (r >= 1.f / 256.f) {
+          const float inv = 1.f / r;
+#pragma unroll
+          for (int e = 0; e < DQ; ++e) { kf[e] *= inv; uf[e] *= inv; }
+          zf = z + __logf(r);
+        } else {
+          zf = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < DQ; ++e) { kf[e] = 0.f; uf[e] = 0.f; }
+          int p = 0;
+          for (int be = 0; be < bb; ++be) {
+            if (p < pl.k2w && sel[p] == be) { ++p; continue; }
+            far_merge<D, DQ>(b, prow, pl.nb, be, q * DQ, zf, kf, uf);
+          }
+        }
+      }
+      const bool ne = cok && zf > -INFINITY;
       TIn kr[DQ];
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < DQ; ++e) {
-        kr[e] = px_round<TIn>(ne ? kap[e] : 0.f);
+        kr[e] = px_round<TIn>(ne ? kf[e] : 0.f);
         dot = fmaf(nup[e], px_float<TIn>(kr[e]), dot);
       }
       dot *= s2;
@@ -353,7 +437,7 @@ __global__ void __launch_bounds__(1024) v4_far_kernel(Plan pl, AttnBufs b, int c
         for (int e = 0; e < DQ; ++e) fk[e] = kr[e];
         TIn* fv = reinterpret_cast<TIn*>(b.fv) + (g * D + q * DQ) * Cp + c;
 #pragma unroll
-        for (int e = 0; e < DQ; ++e) fv[(size_t)e * Cp] = px_round<TIn>(ne ? u[e] : 0.f);
+        for (int e = 0; e < DQ; ++e) fv[(size_t)e * Cp] = px_round<TIn>(ne ? uf[e] : 0.f);
       }
       red[q][cl] = dot;
       __syncthreads();
@@ -361,98 +445,11 @@ __global__ void __launch_bounds__(1024) v4_far_kernel(Plan pl, AttnBufs b, int c
         float tot = 0.f;
 #pragma unroll
         for (int i = 0; i < QN; ++i) tot += red[i][cl];
-        b.fbias[g * Cp + c] = ne ? z * PX_LOG2E - tot : -INFINITY;
+        b.fbias[g * Cp + c] = ne ? zf * PX_LOG2E - tot : -INFINITY;
       }
       __syncthreads();
     }
-    if (cok) {
-      const float z2 = b.pz[prow * pl.nb + bb];
-      if (z2 > -INFINITY) {
-        // merge block bb's statistics, four dims at a time
-        const float zm = fmaxf(z, z2);
-        const float a = __expf(z - zm), wgt = __expf(z2 - zm);
-        const float inv = 1.f / (a + wgt);
-        const float* k2 = b.pk + (prow * pl.nb + bb) * D + q * DQ;
-        const float* u2 = b.pu + (prow * pl.nb + bb) * D + q * DQ;
-#pragma unroll
-        for (int e = 0; e < DQ; e += 4) {
-          const f32x4 kk = *reinterpret_cast<const f32x4*>(k2 + e);
-          const f32x4 uu = *reinterpret_cast<const f32x4*>(u2 + e);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            kap[e + i] = (a * kap[e + i] + wgt * kk[i]) * inv;
-            u[e + i] = (a * u[e + i] + wgt * uu[i]) * inv;
-          }
-        }
-        z = zm + __logf(a + wgt);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Far items of the retrieved clusters: the earlier blocks that were not
-// retrieved, merged in block order.  One workgroup per group (q-head, b >= 1,
-// I), wave w takes retrieved slots w, w + 4, ...; lane = feature dims.
-// ---------------------------------------------------------------------------
-template <typename TIn, int D>
-__global__ void __launch_bounds__(256) v4_rem_kernel(Plan pl, AttnBufs b) {
-  constexpr int E = D / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int id = blockIdx.x;
-  const int I = id % pl.Cq;
-  id /= pl.Cq;
-  const int bb = 1 + id % (pl.nb - 1), bh = id / (pl.nb - 1);
-  if (I >= min(pl.Cq, pl.N)) return;
-  const size_t irow = (size_t)bh * pl.Cq + I;
-  const int32_t* qbr = b.qb + irow * (pl.nb + 1);
-  if (qbr[bb + 1] <= qbr[bb]) return;
-  const float s2 = pl.scale * PX_LOG2E;
-  const int32_t* R1 = b.r1 + (irow * pl.nb + bb) * pl.k1w;
-  const int32_t* R2 = b.r2 + (irow * pl.nb + bb) * pl.k1w * pl.k2w;
-  const size_t g = ((size_t)bh * pl.nb + bb) * pl.Cq + I;
-  const int Cp = b.Cp32;
-  float nus[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) nus[e] = b.qs.cent[((size_t)bh * pl.C + I) * D + E * lane + e] * s2;
-  for (int j = w; j < pl.k1w; j += 4) {
-    const int c = R1[j];
-    if (c < 0) break;   // retrieved slots are ascending, padded with -1
-    const int32_t* sel = R2 + (size_t)j * pl.k2w;
-    const size_t prow = irow * pl.Ck + c;
-    float z = -INFINITY, kap[E], u[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) { kap[e] = 0.f; u[e] = 0.f; }
-    int p = 0;
-    for (int be = 0; be < bb; ++be) {
-      if (p < pl.k2w && sel[p] == be) { ++p; continue; }
-      const float z2 = b.pz[prow * pl.nb + be];
-      if (!(z2 > -INFINITY)) continue;
-      float k2[E], u2[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        k2[e] = b.pk[(prow * pl.nb + be) * D + E * lane + e];
-        u2[e] = b.pu[(prow * pl.nb + be) * D + E * lane + e];
-      }
-      px_merge<E>(z, kap, u, z2, k2, u2);
-    }
-    const bool ne = z > -INFINITY;
-    TIn kr[E];
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      kr[e] = px_round<TIn>(ne ? kap[e] : 0.f);
-      dot = fmaf(nus[e], px_float<TIn>(kr[e]), dot);
-    }
-    for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
-    TIn* fk = reinterpret_cast<TIn*>(b.fk) + (g * Cp + c) * D + E * lane;
-    TIn* fv = reinterpret_cast<TIn*>(b.fv) + (g * D + E * lane) * Cp + c;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      fk[e] = kr[e];
-      fv[(size_t)e * Cp] = px_round<TIn>(ne ? u[e] : 0.f);
-    }
-    if (lane == 0) b.fbias[g * Cp + c] = ne ? z * PX_LOG2E - dot : -INFINITY;
+    if (cok) far_merge<D, DQ>(b, prow, pl.nb, bb, q * DQ, z, kap, u);
   }
 }
 
@@ -487,12 +484,6 @@ static hipError_t v4_go(const Plan& pl, const AttnBufs& b, hipStream_t st) {
     MUSE_KT_PRE(st);
     v4_far_kernel<TIn, D><<<(unsigned)(BHq * pl.Cq * nchunk), FarGeo<D>::QN * cw, 0, st>>>(pl, b, cw, nchunk);
     MUSE_KT_POST("v4_far", st);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (pl.nb > 1 && pl.topk > 0) {
-    MUSE_KT_PRE(st);
-    v4_rem_kernel<TIn, D><<<(unsigned)(BHq * (pl.nb - 1) * pl.Cq), 256, 0, st>>>(pl, b);
-    MUSE_KT_POST("v4_rem", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
