@@ -87,6 +87,14 @@ __device__ __forceinline__ void px_load(const TIn* p, float* out) {
   }
 }
 
+// x of lane l ^ 1 and of lane l ^ 2 (DPP quad permutations: no LDS trip).
+__device__ __forceinline__ float px_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float px_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
 // fp32 -> input dtype (bf16: round to nearest even), and back.
 template <typename TIn>
 __device__ __forceinline__ TIn px_round(float x) {
@@ -110,19 +118,24 @@ __device__ __forceinline__ float px_float(TIn v) {
 // lanes, and each lane accumulates its quarter of sum w k and sum w v.
 // ---------------------------------------------------------------------------
 template <typename TIn, int D>
-__global__ void __launch_bounds__(256) v4_part_kernel(Plan pl, AttnBufs b) {
-  constexpr int E = D / 4;
+__global__ void __launch_bounds__(256) v4_part_kernel(Plan pl, AttnBufs b, int nbg) {
+  constexpr int E = D / 4, KU = D == 64 ? 2 : 1;
   const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int Cqe = min(pl.Cq, pl.N), Cke = min(pl.Ck, pl.N);
   const int nIt = (Cqe + 15) / 16;
-  if (wave >= (long long)pl.B * pl.Hq * nIt * Cke) return;   // whole waves: no barriers below
-  const int c = (int)(wave % Cke);
-  const long long r = wave / Cke;
+  if (wave >= (long long)pl.B * pl.Hq * nIt * Cke * nbg) return;   // whole waves: no barriers below
+  // the blocks of one (q-head, query-cluster tile, key cluster) are split
+  // into nbg ranges, one wave each (the blocks are independent)
+  const int bg = (int)(wave % nbg);
+  const int c = (int)(wave / nbg % Cke);
+  const long long r = wave / nbg / Cke;
   const int it = (int)(r % nIt), bh = (int)(r / nIt);
   const int bq = bh / pl.Hq, hq = bh % pl.Hq;
   const int kvh = bq * pl.Hkv + (hq * pl.Hkv) / pl.Hq;
-  const int il = lane & 15, ds = lane >> 4;
+  // lane = 4 il + ds: the four quarters of one query cluster are adjacent
+  // lanes, summed by in-row lane swaps
+  const int il = lane >> 2, ds = lane & 3;
   const int I = it * 16 + il;
   const bool Iok = I < Cqe;
   const float s2 = pl.scale * PX_LOG2E;
@@ -136,31 +149,57 @@ __global__ void __launch_bounds__(256) v4_part_kernel(Plan pl, AttnBufs b) {
   const TIn* Kp = reinterpret_cast<const TIn*>(b.kst.Kp) + (size_t)kvh * pl.N * D + ds * E;
   const TIn* Vp = reinterpret_cast<const TIn*>(b.kst.Vp) + (size_t)kvh * pl.N * D + ds * E;
   const size_t row = ((size_t)bh * pl.Cq + (Iok ? I : 0)) * pl.Ck + c;   // (I, c): nb entries
-  int r1 = kbr[0];
-  for (int beta = 0; beta < pl.nb; ++beta) {
+  const int be0 = (int)((long long)pl.nb * bg / nbg), be1 = (int)((long long)pl.nb * (bg + 1) / nbg);
+  int r1 = kbr[be0];
+  for (int beta = be0; beta < be1; ++beta) {
     const int r0 = r1;
     r1 = kbr[beta + 1];
+    // sums relative to a reference m that moves only when a logit exceeds
+    // it by more than 8 (weights stay below 2^8); KU keys per step
     float m = -INFINITY, z = 0.f, ak[E], au[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) { ak[e] = 0.f; au[e] = 0.f; }
-    for (int j = r0; j < r1; ++j) {
-      float kx[E], vx[E];
-      px_load<TIn, E>(Kp + (size_t)j * D, kx);
-      px_load<TIn, E>(Vp + (size_t)j * D, vx);
-      float d = 0.f;
+    for (int j = r0; j < r1; j += KU) {
+      float kx[KU][E], vx[KU][E], d[KU];
 #pragma unroll
-      for (int e = 0; e < E; ++e) d = fmaf(nu[e], kx[e], d);
-      d += __shfl_xor(d, 16, 64);
-      d += __shfl_xor(d, 32, 64);
-      const float mn = fmaxf(m, d);
-      const float sc = __builtin_amdgcn_exp2f(m - mn), p = __builtin_amdgcn_exp2f(d - mn);
-      z = fmaf(z, sc, p);
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        ak[e] = fmaf(ak[e], sc, p * kx[e]);
-        au[e] = fmaf(au[e], sc, p * vx[e]);
+      for (int k = 0; k < KU; ++k) {
+        const int jr = min(j + k, r1 - 1);
+        px_load<TIn, E>(Kp + (size_t)jr * D, kx[k]);
+        px_load<TIn, E>(Vp + (size_t)jr * D, vx[k]);
       }
-      m = mn;
+#pragma unroll
+      for (int k = 0; k < KU; ++k) {
+        d[k] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) d[k] = fmaf(nu[e], kx[k][e], d[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < KU; ++k) d[k] += px_xor1(d[k]);
+#pragma unroll
+      for (int k = 0; k < KU; ++k) {
+        d[k] += px_xor2(d[k]);
+        if (j + k >= r1) d[k] = -INFINITY;
+      }
+      float dm = d[0];
+#pragma unroll
+      for (int k = 1; k < KU; ++k) dm = fmaxf(dm, d[k]);
+      if (dm > m + 8.f) {
+        const float sc = __builtin_amdgcn_exp2f(m - dm);
+        z *= sc;
+#pragma unroll
+        for (int e = 0; e < E; ++e) { ak[e] *= sc; au[e] *= sc; }
+        m = dm;
+      }
+#pragma unroll
+      for (int k = 0; k < KU; ++k) {
+        const float p = __builtin_amdgcn_exp2f(d[k] - m);
+        z += p;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          ak[e] = fmaf(p, kx[k][e], ak[e]);
+          au[e] = fmaf(p, vx[k][e], au[e]);
+        }
+      }
     }
     if (Iok) {
       const bool ne = r1 > r0;
@@ -254,11 +293,11 @@ __global__ void __launch_bounds__(256) v4_select_kernel(Plan pl, AttnBufs b) {
         continue;
       }
       const int cj = selc[j];
-      const int32_t* kbj = b.kb + ((size_t)kvh * pl.Ck + cj) * (pl.nb + 1);
       const float* pzj = b.pz + (irow * pl.Ck + cj) * pl.nb;
       float* my = bsc[w];
       // each lane stages and later scans only its own blocks be = lane + 64 u
-      for (int be = lane; be < bb; be += 64) my[be] = kbj[be + 1] > kbj[be] ? pzj[be] : -INFINITY;
+      // (an empty (cluster, block) has ln Z = -inf and is never a candidate)
+      for (int be = lane; be < bb; be += 64) my[be] = pzj[be];
       unsigned long long mine = 0;
       for (int t = 0; t < pl.k2w; ++t) {
         float best = -INFINITY;
@@ -355,14 +394,16 @@ __global__ void __launch_bounds__(1024) v4_far_kernel(Plan pl, AttnBufs b, int c
   const float* nup = b.qs.cent + ((size_t)bh * pl.C + I) * D + q * DQ;   // read where needed
   const size_t prow = irow * pl.Ck + (cok ? c : 0);
   const int k12 = pl.k1w * pl.k2w;
+  __shared__ int32_t hasq[V4_MAXNB];   // 1: the group (I, block) has queries
   for (int t = tid; t < MUSE_MAXC; t += blockDim.x) slot[t] = -1;
+  for (int t = tid; t < pl.nb; t += blockDim.x) hasq[t] = t >= 1 && qbr[t + 1] > qbr[t];
   __syncthreads();
   float z = -INFINITY, kap[DQ], u[DQ];
 #pragma unroll
   for (int e = 0; e < DQ; ++e) { kap[e] = 0.f; u[e] = 0.f; }
   const int Cp = b.Cp32;
   for (int bb = 0; bb < pl.nb; ++bb) {
-    if (bb >= 1 && qbr[bb + 1] > qbr[bb]) {
+    if (hasq[bb]) {
       const size_t g = ((size_t)bh * pl.nb + bb) * pl.Cq + I;
       if (pl.topk > 0) {
         const int32_t* R1 = b.r1 + (irow * pl.nb + bb) * pl.k1w;
@@ -372,8 +413,9 @@ __global__ void __launch_bounds__(1024) v4_far_kernel(Plan pl, AttnBufs b, int c
           if (cs >= 0) slot[cs] = (bb << 8) | tid;
         }
         if (tid < k12) r2s[tid] = R2[tid];
-        __syncthreads();
       }
+      // (also orders this group's writes of red after the previous group's reads)
+      __syncthreads();
       float zf = z, kf[DQ], uf[DQ];
 #pragma unroll
       for (int e = 0; e < DQ; ++e) { kf[e] = kap[e]; uf[e] = u[e]; }
@@ -447,7 +489,6 @@ __global__ void __launch_bounds__(1024) v4_far_kernel(Plan pl, AttnBufs b, int c
         for (int i = 0; i < QN; ++i) tot += red[i][cl];
         b.fbias[g * Cp + c] = ne ? zf * PX_LOG2E - tot : -INFINITY;
       }
-      __syncthreads();
     }
     if (cok) far_merge<D, DQ>(b, prow, pl.nb, bb, q * DQ, z, kap, u);
   }
@@ -467,9 +508,12 @@ static hipError_t v4_go(const Plan& pl, const AttnBufs& b, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    const long long waves = BHq * ((Cqe + 15) / 16) * Cke;
+    // about 16 waves per SIMD: split each key cluster's blocks into ranges
+    const long long base = BHq * ((Cqe + 15) / 16) * Cke;
+    const int nbg = (int)std::max<long long>(1, std::min<long long>(pl.nb, 16384 / std::max<long long>(base, 1)));
+    const long long waves = base * nbg;
     MUSE_KT_PRE(st);
-    v4_part_kernel<TIn, D><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(pl, b);
+    v4_part_kernel<TIn, D><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(pl, b, nbg);
     MUSE_KT_POST("v4_part", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

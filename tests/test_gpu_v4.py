@@ -26,12 +26,12 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def run(B, Hq, Hkv, N, D, dtype, cq, ck, k1, k2, blk, seed=0, iters=4, comps=16):
+def run(B, Hq, Hkv, N, D, dtype, cq, ck, k1, k2, blk, seed=0, iters=4, comps=16, scale=0.0):
     import torch
     print(f"case B={B} Hq={Hq} Hkv={Hkv} N={N} D={D} {dtype} cq={cq} ck={ck} k1={k1} k2={k2} "
-          f"block={blk} seed={seed}", flush=True)
+          f"block={blk} seed={seed} scale={scale}", flush=True)
     x = gu.gaussian_inputs(B, Hq, Hkv, N, D, dtype, comps=comps, seed=seed)
-    cfg = M.make_cfg(cq, iters, k1, True, blk, ck=ck, blocks=True, topk2=k2)
+    cfg = M.make_cfg(cq, iters, k1, True, blk, ck=ck, blocks=True, topk2=k2, scale=scale)
     Qd, Kd, Vd = (gu.to_dev(x[k], dtype) for k in "QKV")
     O, lse, st = M.museattn_fwd(Qd, Kd, Vd, cfg)
     torch.cuda.synchronize()
@@ -150,6 +150,27 @@ def test_v4_forward_matches_oracle(B, Hq, Hkv, N, D, dtype, cq, ck, k1, k2, blk)
             assert e <= gu.TOL[dtype], (b, h, e)
             gu.check_lse(r["lse"][b, h], lse, dtype, (b, h))
     print("max rel err per head:", [round(e, 6) for e in errs], flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_v4_peaked_tilt(dtype):
+    """Softmax scale 5: the retrieved blocks often hold nearly all of a
+    retrieved cluster's earlier tilted mass, so its far item is taken both
+    by subtraction from the prefix (when at least 1/256 remains) and by
+    merging the remaining blocks directly (when less does: 17 of the 120
+    retrieved (group, cluster) pairs of the fp32 inputs, by the oracle's
+    count)."""
+    N, D, blk, cq, ck, k1, k2, scale = 1024, 64, 64, 4, 8, 2, 2, 5.0
+    r = run(1, 1, 1, N, D, dtype, cq, ck, k1, k2, blk, seed=5, scale=scale)
+    check_bounds(r, 1, 1, 1, N, cq, ck, blk)
+    check_selection(r, 0, 0, 1, 1, N, D, blk, cq, k1, k2, scale)
+    ocfg = mo.MuseConfig(cq=cq, ck=ck, iters=4, topk=k1, block=blk, causal=True, exact_tilt=True, scale=scale)
+    sh = shared_for(r, 0, 0, 1, 1, N, blk, cq)
+    o, lse, _ = v4.forward_head(r["x"]["Q"][0, 0], r["x"]["K"][0, 0], r["x"]["V"][0, 0], ocfg, k2, shared=sh)
+    e = gu.max_rel(r["O"][0, 0], o)
+    print("max rel err:", e, flush=True)
+    assert e <= gu.TOL[dtype], e
+    gu.check_lse(r["lse"][0, 0], lse, dtype)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
