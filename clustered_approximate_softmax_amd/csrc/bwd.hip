@@ -517,7 +517,11 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_q_kernel(BwdArgs A, int lev) {
 // the queries that see them in tiles of QB.  S = Q K^T, dP = dO V^T (queries
 // as rows), dS = P (dP - Delta), dV^T += dO^T P, dK^T += Q^T dS.
 // ===========================================================================
-enum { BK_EXACT = 0, BK_LOCAL = 2 };   // far items have a kernel of their own
+// far items have a kernel of their own; BK_STREAM is BK_EXACT with the
+// retrieving query clusters' queries as one stream (levels of small query
+// clusters, where one stream per query cluster would leave most of each
+// query tile empty)
+enum { BK_EXACT = 0, BK_STREAM = 1, BK_LOCAL = 2 };
 
 template <typename TIn, int D>
 struct alignas(16) BkSmem {
@@ -530,6 +534,9 @@ struct alignas(16) BkSmem {
   float dlt[QB];
   int32_t qrow[QB];
   int32_t list[256];              // (query head, query cluster) pairs retrieving the cluster
+  int32_t cum[257];               // their first position in the combined query stream
+  int32_t hq0[256];               // their first q_perm position
+  int32_t hbh[256];               // their query head
   int32_t wc[4];
   int32_t sel[4];
 };
@@ -616,6 +623,99 @@ __device__ __forceinline__ void bk_consume(const BkSmem<TIn, D>& sm,
     }
     dvt[dt] = mfma_split<NS, NS>(a, pb, dvt[dt]);
     dkt[dt] = mfma_split<NS, NS>(c, db, dkt[dt]);
+  }
+}
+
+// A stream of n queries: query q < n is row row_at(q) of Qh / dOh / lse /
+// delta (-1: none).  bf16: software-pipelined.  While tile t is contracted,
+// the Q / dO rows and the lse / Delta of tile t+1 are in flight, and the row
+// indices of tile t+2 (so that no load waits on another inside an
+// iteration).
+template <typename TIn, int D, bool CAUSAL, int NT, class RowAt>
+__device__ __forceinline__ void bk_query_stream(BkSmem<TIn, D>& sm, const TIn* Qh, const TIn* dOh, const float* lse,
+                                                const float* delta, int n, RowAt row_of,
+                                                const u16x8 (&kf)[D / 32][BwdTraits<TIn>::NS],
+                                                const u16x8 (&vf)[D / 32][BwdTraits<TIn>::NS], float ibias,
+                                                int irow, float s2, f32x4 (&dvt)[D / 16], f32x4 (&dkt)[D / 16]) {
+  const int qa = 0, qb = n;
+  if constexpr (BkSmem<TIn, D>::NS == 1) {
+    // staging layout: thread -> 4 queries (block qb4) x 8 dims (e0); the first QB
+    // threads also own one query's row index, lse and Delta
+    constexpr int NSTG = (QB / 4) * (D / 8);
+    static_assert(NSTG <= NT && QB <= NT, "one staging item per thread");
+    const int tid = threadIdx.x;
+    const bool stg = tid < NSTG;
+    const int qb4 = tid % (QB / 4), e0 = (tid / (QB / 4)) * 8;
+    const int ntile = (qb - qa + QB - 1) / QB;
+    auto row_at = [&](int q) __attribute__((always_inline)) -> int { return q < qb ? row_of(q) : -1; };
+    int r1[4], r2[4], s1 = -1, s2r = -1;
+    u16x8 qd[4], od[4];
+    float l1 = 0.f, d1 = 0.f;
+    auto load_rows = [&](int q0, int (&rr)[4], int& sr) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rr[r] = stg ? row_at(q0 + 4 * qb4 + r) : -1;
+      sr = tid < QB ? row_at(q0 + tid) : -1;
+    };
+    auto load_data = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        qd[r] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        od[r] = qd[r];
+        if (r1[r] >= 0) {
+          qd[r] = *reinterpret_cast<const u16x8*>(Qh + (size_t)r1[r] * D + e0);
+          od[r] = *reinterpret_cast<const u16x8*>(dOh + (size_t)r1[r] * D + e0);
+        }
+      }
+      l1 = s1 >= 0 ? lse[s1] * B_LOG2E : 0.f;
+      d1 = s1 >= 0 ? delta[s1] : 0.f;
+    };
+    load_rows(qa, r1, s1);
+    load_data();
+    if (ntile > 1) load_rows(qa + QB, r2, s2r);
+    for (int t = 0; t < ntile; ++t) {
+      // tile t into LDS
+      if (stg) {
+        const int pos = slot_of(4 * qb4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          *reinterpret_cast<u16x8*>(&sm.qs[0][4 * qb4 + r][e0]) = qd[r];
+          *reinterpret_cast<u16x8*>(&sm.os[0][4 * qb4 + r][e0]) = od[r];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          *reinterpret_cast<u16x4*>(&sm.qt[0][e0 + j][pos]) = u16x4{qd[0][j], qd[1][j], qd[2][j], qd[3][j]};
+          *reinterpret_cast<u16x4*>(&sm.ot[0][e0 + j][pos]) = u16x4{od[0][j], od[1][j], od[2][j], od[3][j]};
+        }
+      }
+      if (tid < QB) {
+        sm.qrow[tid] = s1;
+        sm.lse2[tid] = l1;
+        sm.dlt[tid] = d1;
+      }
+      __syncthreads();
+      // tile t+1's rows and scalars, tile t+2's row indices: in flight during the contraction
+      if (t + 1 < ntile) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) r1[r] = r2[r];
+        s1 = s2r;
+        load_data();
+        if (t + 2 < ntile) load_rows(qa + (t + 2) * QB, r2, s2r);
+      }
+      bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
+      __syncthreads();
+    }
+  } else {
+    for (int q0 = qa; q0 < qb; q0 += QB) {
+      if (threadIdx.x < QB) {
+        const int q = q0 + threadIdx.x;
+        sm.qrow[threadIdx.x] = q < qb ? row_of(q) : -1;
+      }
+      __syncthreads();
+      bk_stage_queries<TIn, D, NT>(sm, Qh, dOh, lse, delta);
+      __syncthreads();
+      bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
+      __syncthreads();
+    }
   }
 }
 
@@ -744,7 +844,7 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
     ibeg = blk0 + tile * IT;
     iend = min(blk1, ibeg + IT);
     if (ibeg >= iend) return;
-  } else if (KIND == BK_EXACT) {
+  } else {
     nseg = pl.lev_nseg[lev];
     const int m = pl.lev_m[lev];
     const int spp = (m + IT - 1) / IT + C;
@@ -782,7 +882,7 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
         irow = item;
         ibias = 0.f;
       }
-    } else if (KIND == BK_EXACT) {
+    } else {
       if (ivalid) {
         const size_t kb = (((size_t)lev * pl.B * pl.Hkv + kvh) * pl.N + gm.k0 + item) * D;
         kp_ = reinterpret_cast<const TIn*>(b.kst.Kp) + kb;
@@ -807,7 +907,7 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
   }
 
   // ---- the queries that see these items ----
-  if (KIND == BK_EXACT) {
+  if (KIND != BK_LOCAL) {
     // (query head of the group, query cluster) pairs whose retrieval set holds c,
     // scanned in a fixed order, at most 256 per round
     const int Cq = min(C, gm.qn);
@@ -832,14 +932,65 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
 #pragma unroll
       for (int q = 0; q < WAVES; ++q) cnt += sm.wc[q];
       __syncthreads();
-      for (int li = 0; li < cnt; ++li) {
-        const int ent = sm.list[li];
-        const int hl = ent / Cq, Iq = ent % Cq;
-        const int bhx = bq * pl.Hq + (kvh % pl.Hkv) * Gq + hl;
-        const int32_t* qoffs = b.qs.offs + ((size_t)bhx * pl.P + p) * (C + 1);
-        const int32_t* qperm = b.qs.perm + ((size_t)lev * pl.B * pl.Hq + bhx) * pl.N + gm.q0;
-        bk_query_range<TIn, D, false, NT>(sm, A, bhx, qperm, qoffs[Iq], qoffs[Iq + 1], kf, vf, ibias, irow,
-                                          s2, dvt, dkt);
+      // the listed pairs' queries as one stream (small clusters then share
+      // query tiles): pair li holds stream positions [cum[li], cum[li+1]),
+      // its queries at q_perm positions hq0[li] + 0, 1, ... of head hbh[li]
+      if (tid < 64) {
+        int v[4], pos[4], hb[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int li = tid * 4 + q;
+          v[q] = 0;
+          if (li < cnt) {
+            const int ent = sm.list[li];
+            const int hl = ent / Cq, Iq = ent % Cq;
+            hb[q] = bq * pl.Hq + (kvh % pl.Hkv) * Gq + hl;
+            const int32_t* qoffs = b.qs.offs + ((size_t)hb[q] * pl.P + p) * (C + 1);
+            pos[q] = qoffs[Iq];
+            v[q] = qoffs[Iq + 1] - pos[q];
+          }
+          sum += v[q];
+        }
+        int inc = sum;
+        for (int mm = 1; mm < 64; mm <<= 1) {
+          const int o = __shfl_up(inc, mm, 64);
+          if (tid >= mm) inc += o;
+        }
+        int run = inc - sum;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int li = tid * 4 + q;
+          if (li < cnt) {
+            sm.cum[li] = run;
+            sm.hq0[li] = pos[q];
+            sm.hbh[li] = hb[q];
+          }
+          run += v[q];
+        }
+        if (tid == 63) sm.cum[cnt] = inc;
+      }
+      __syncthreads();
+      const int total = sm.cum[cnt];
+      const int32_t* permb = b.qs.perm + (size_t)lev * pl.B * pl.Hq * pl.N + gm.q0;
+      if constexpr (KIND == BK_STREAM) {
+        int hc = 0;   // this thread's cursor: successive lookups move it a few pairs at most
+        auto row_of = [&](int v) __attribute__((always_inline)) -> int {
+          // the pair holding stream position v: the last li with cum[li] <= v
+          while (hc > 0 && sm.cum[hc] > v) --hc;
+          while (hc + 1 < cnt && sm.cum[hc + 1] <= v) ++hc;
+          const int bhx = sm.hbh[hc];
+          return bhx * pl.N + permb[(size_t)bhx * pl.N + sm.hq0[hc] + (v - sm.cum[hc])];
+        };
+        bk_query_stream<TIn, D, false, NT>(sm, reinterpret_cast<const TIn*>(A.a.Q),
+                                           reinterpret_cast<const TIn*>(A.dO), A.lse, A.delta, total, row_of, kf,
+                                           vf, ibias, irow, s2, dvt, dkt);
+      } else {
+        // one stream per pair (row indices read straight from q_perm)
+        for (int li = 0; li < cnt; ++li) {
+          const int bhx = sm.hbh[li], q0 = sm.hq0[li];
+          bk_query_range<TIn, D, false, NT>(sm, A, bhx, permb + (size_t)bhx * pl.N, q0,
+                                            q0 + sm.cum[li + 1] - sm.cum[li], kf, vf, ibias, irow, s2, dvt, dkt);
+        }
       }
       __syncthreads();
     }
@@ -1419,6 +1570,7 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
   set_smem_once((const void*)bwd_q_kernel<TIn, D, BQ_PROBLEM, 4>, bq_smem);
   set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_LOCAL, 4>, bk_smem);
   set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_EXACT, 4>, bk_smem);
+  set_smem_once((const void*)bwd_kv_kernel<TIn, D, BK_STREAM, 4>, bk_smem);
   set_smem_once((const void*)bwd_far_kernel<TIn, D, 4>, bk_smem);
   set_smem_once((const void*)bwd_bcast_k_kernel<TIn, D, 1024>, bc_smem);
   MUSE_KT_PRE(st);
@@ -1455,7 +1607,11 @@ static hipError_t bwd_all(const BwdArgs& A, void* dQo, void* dKo, void* dVo, hip
     bwd_q_kernel<TIn, D, BQ_PROBLEM, 4><<<(unsigned)(pl.B * pl.Hq * nseg * spp), 256, bq_smem, st>>>(A, lev);
     MUSE_KT_POST(qn[lev < 7 ? lev : 7], st);
     MUSE_KT_PRE(st);
-    bwd_kv_kernel<TIn, D, BK_EXACT, 4><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 256, bk_smem, st>>>(A, lev);
+    // query clusters of fewer than a query tile's rows on average: one query stream per key cluster
+    if (m < (long long)QB * C)
+      bwd_kv_kernel<TIn, D, BK_STREAM, 4><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 256, bk_smem, st>>>(A, lev);
+    else
+      bwd_kv_kernel<TIn, D, BK_EXACT, 4><<<(unsigned)(pl.B * pl.Hkv * nseg * spp), 256, bk_smem, st>>>(A, lev);
     MUSE_KT_POST(kn[lev < 7 ? lev : 7], st);
     MUSE_KT_PRE(st);
     // query clusters per far workgroup: enough workgroups (about 4096) to fill the chip

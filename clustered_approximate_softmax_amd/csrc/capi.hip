@@ -544,6 +544,8 @@ int museattn_bwd(const void* Q, const void* K, const void* V, const void* O, con
   int rc = build_plan(B, Hq, Hkv, N, D, cfg, pl);
   if (rc) return rc;
   if (pl.dipole == 2) return MUSE_EUNSUPPORTED;   // the exact tilt has no backward here
+  // the item-centric pass indexes query rows of all heads with 32-bit integers
+  if ((int64_t)pl.B * pl.Hq * pl.N >= ((int64_t)1 << 31)) return MUSE_EUNSUPPORTED;
   Layout lay;
   build_layout(pl, (int)dtype, lay);
   const muse_layout& L = lay.L;
