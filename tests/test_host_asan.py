@@ -5,7 +5,7 @@ code is unchanged) and linked with the in-tree objects of the other sources.
 A child process then runs every host-only path of the ABI under the
 sanitizer runtime: the problem plan and the state/workspace layout for many
 shapes and configurations (causal hierarchy, spatial blocks, separate
-cluster counts, ragged and tiny sizes, the 16-level limit), and the argument
+cluster counts, ragged and tiny sizes, up to 2^20 rows), and the argument
 checks of every entry point that returns before anything is queued.  Any
 out-of-bounds access or use of freed memory in that code aborts the child
 with a sanitizer report.  A tiny program with a planted heap overflow checks
