@@ -255,8 +255,8 @@ def cpu_baseline(w, x, budget_s):
     Acausal: whole (batch, query head) problems until the budget is spent,
     extrapolated linearly in the number of heads.  Causal: the first segment
     of each block level of head 0 (forward, plus the backward for a training
-    workload), timed for spans up to 8192 rows while the budget is predicted
-    to last (a level costs about twice the one below it); each
+    workload), timed level by level while the budget is predicted to last (a
+    level costs about twice the one below it); each
     larger level is extrapolated from the largest measured one linearly in
     the span (every step of a problem, k-means, statistics and attention, is
     linear in its row count at fixed C and D); each level's time is
@@ -298,8 +298,6 @@ def cpu_baseline(w, x, budget_s):
         measured, per_level = {}, {}
         for l in sorted(first):
             pr = first[l]
-            if pr["kn"] > 8192:
-                break
             if measured:
                 last = max(measured)
                 predicted = measured[last] * pr["kn"] / first[last]["kn"]
