@@ -373,6 +373,111 @@ __device__ __forceinline__ void issue_tile_g(unsigned char* stg, const TileSrc& 
   }
 }
 
+// Gathered exact tiles from a chunk table (one-wave workgroups, bf16 at
+// D = 64).  The exact chunks of a workgroup are listed once, in tile order:
+// lane l of tab.b[i] holds the first row of chunk 64i + l, and lane l of
+// tab.m the valid-row bytes of chunks 4l .. 4l+3 (zero past the last chunk).
+// A tile's descriptor is then eight lane reads of the table, and its copies
+// use scalar row bases with per-lane offsets that never change.
+constexpr int GX_MAXCH = 256;   // chunks the table holds (32 tiles)
+struct GxTab {
+  int b0, b1, b2, b3;    // chunk bases (four registers: GX_MAXCH = 256)
+  uint32_t m;
+  uint32_t voff_k[2];   // key-copy byte offsets within a chunk (even, odd copy)
+};
+static_assert(GX_MAXCH == 256, "the table is four registers of chunk bases");
+
+// List the exact chunks of the nseg retrieved segments (row ranges in
+// seg_lo/seg_hi) into scratch LDS (bases at cb[], valid-row bytes at cm[]),
+// then read them into the register table.  nch = total chunks <= GX_MAXCH.
+template <typename SM>
+__device__ __forceinline__ void gx_build(const SM& sm, int nseg, int nch, int32_t* cb, uint8_t* cm, GxTab& tab) {
+  const int lane = threadIdx.x & 63;
+  int run = 0;   // chunks before this round of 64 segments
+  for (int j0 = 0; j0 < nseg; j0 += 64) {
+    const int j = j0 + lane;
+    const int lo = j < nseg ? sm.seg_lo[j] : 0, hi = j < nseg ? sm.seg_hi[j] : 0;
+    const int first = lo & ~7;
+    const int cnt = j < nseg ? (hi - first + 7) >> 3 : 0;
+    int inc = cnt;
+    for (int mm = 1; mm < 64; mm <<= 1) {
+      const int o = __shfl_up(inc, mm, 64);
+      if (lane >= mm) inc += o;
+    }
+    const int start = run + inc - cnt;
+    for (int c = 0; c < cnt; ++c) {
+      const int base = first + 8 * c;
+      const int a = max(lo - base, 0), bb = min(hi - base, 8);
+      if (start + c < GX_MAXCH) {
+        cb[start + c] = base;
+        cm[start + c] = (uint8_t)(bb > a ? (1u << bb) - (1u << a) : 0u);
+      }
+    }
+    run += __shfl(inc, 63, 64);
+  }
+  __syncthreads();
+  tab.b0 = lane < nch ? cb[lane] : 0;
+  tab.b1 = 64 + lane < nch ? cb[64 + lane] : 0;
+  tab.b2 = 128 + lane < nch ? cb[128 + lane] : 0;
+  tab.b3 = 192 + lane < nch ? cb[192 + lane] : 0;
+  uint32_t mw = *reinterpret_cast<const uint32_t*>(cm + 4 * lane);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (4 * lane + q >= nch) mw &= ~(0xffu << (8 * q));
+  tab.m = mw;
+  // key copy of chunk m: lane t takes row (t/8) & 7 of the chunk, 16-byte
+  // piece (t & 7) ^ keyk(8m + t/8) (issue_tile_g's layout)
+  const int r7 = (lane >> 3) & 7;
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+    tab.voff_k[p] = (uint32_t)((r7 * 64 + (((lane & 7) ^ ((r7 & 3) | (p << 2))) * 8)) * 2);
+  // the tile stage is overwritten next: every table read must have returned
+  __builtin_amdgcn_s_waitcnt(at_wait(63, 0));
+  __syncthreads();
+}
+
+// Descriptor of exact tile te (chunks 8te .. 8te+7) from the table.
+__device__ __forceinline__ TDesc gx_tile(const GxTab& tab, int te) {
+  TDesc d;
+  d.far = 0;
+  const int r = te >> 3;
+  const int reg = r == 0 ? tab.b0 : r == 1 ? tab.b1 : r == 2 ? tab.b2 : tab.b3;
+  const int l0 = (8 * te) & 63;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) d.base[k] = __builtin_amdgcn_readlane(reg, l0 + k);
+  d.vlo = (uint32_t)__builtin_amdgcn_readlane((int)tab.m, (2 * te) & 63);
+  d.vhi = (uint32_t)__builtin_amdgcn_readlane((int)tab.m, (2 * te + 1) & 63);
+  return d;
+}
+
+// key copies of chunks M..: row base (scalar) + the lane's fixed offset
+template <size_t... M>
+__device__ __forceinline__ void gx_kcopies(const unsigned char* kx, const TDesc& d, const uint32_t (&vo)[2],
+                                           uint32_t l0, std::index_sequence<M...>) {
+  (lds_copy16_s<(int)M * 1024>(kx + (size_t)d.base[M] * 128, vo[M & 1], l0), ...);
+}
+// value copies M..: value rows 8M + t/8 at the lane's chunk column
+template <size_t... M>
+__device__ __forceinline__ void gx_vcopies(const unsigned char* vt, size_t rstep, uint32_t vo, uint32_t l0,
+                                           std::index_sequence<M...>) {
+  (lds_copy16_s<8192 + (int)M * 1024>(vt + M * rstep, vo, l0), ...);
+}
+
+// issue_tile_g for an exact bf16 D = 64 tile of the table whose rows all lie
+// inside the key array (one wave): 8 key and 8 value copies of 1 KB.
+__device__ __forceinline__ void issue_tile_gx(unsigned char* stg, const TileSrc& src, const TDesc& d,
+                                              const GxTab& tab) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stg);
+  gx_kcopies(reinterpret_cast<const unsigned char*>(src.Kx), d, tab.voff_k, l0, std::make_index_sequence<8>{});
+  // value column chunk of this lane: (t & 7) ^ ((t/8) & 7), fixed per lane
+  const int lj = (lane & 7) ^ ((lane >> 3) & 7);
+  const int col = pick8(d, lj);
+  const uint32_t vo = (uint32_t)((((lane >> 3) & 7) * src.nv + col) * 2);
+  gx_vcopies(reinterpret_cast<const unsigned char*>(src.Vt), (size_t)16 * src.nv, vo, l0,
+             std::make_index_sequence<8>{});
+}
+
 // What consume_tile needs to know of a tile: far or exact, plain (no mask
 // at all), its first row (far: first cluster; local: first key row) and the
 // lane's valid items (bit rt*4 + i for item 32(rt/2) + 8g + 4(rt%2) + i).
@@ -822,6 +927,16 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   const int nex = MODE == MODE_LOCAL ? (qhi - (k0 & ~7) + AT_KT - 1) / AT_KT
                                      : __builtin_amdgcn_readfirstlane(sm.sel[5]);
   const int ntiles = (MODE == MODE_LOCAL ? 0 : src.nfar) + (GATHER ? (nex + 7) / 8 : nex);
+  // one-wave bf16 workgroups at D = 64 list their exact chunks once (the
+  // tile stage is free until the first copy)
+  constexpr bool GXC = GATHER && WAVES == 1 && sizeof(TIn) == 2 && D == 64;
+  GxTab gxt = {0, 0, 0, 0, 0u, {0u, 0u}};
+  const bool gx = GXC && nex <= GX_MAXCH;
+  if constexpr (GXC) {
+    if (gx)
+      gx_build(sm, src.nseg, nex, reinterpret_cast<int32_t*>(&stg[0][0]),
+               reinterpret_cast<uint8_t*>(&stg[0][0]) + 4 * GX_MAXCH, gxt);
+  }
 
   // ---- tile loop ----
   // two cursors: copies run PD tiles ahead of consumption.  Contiguous tiles
@@ -833,6 +948,19 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   TDesc gd;   // gathered tiles: the tile just issued (one stage: the next one consumed)
   auto issue_next = [&](unsigned char* dst) __attribute__((always_inline)) {
     if constexpr (GATHER) {
+      if constexpr (GXC) {
+        if (gx && lgc.t >= src.nfar) {
+          // exact tile from the chunk table
+          gd = gx_tile(gxt, lgc.t - src.nfar);
+          ++lgc.t;
+          int mx = gd.base[0];
+#pragma unroll
+          for (int k = 1; k < 8; ++k) mx = max(mx, gd.base[k]);
+          if (mx + 7 <= src.kmax) issue_tile_gx(dst, src, gd, gxt);
+          else issue_tile_g<TIn, D, WAVES>(dst, src, gd);
+          return;
+        }
+      }
       gd = take_tile(sm, src, lgc);
       // far tiles are 64 consecutive clusters: scalar bases when in range
       if (gd.far && gd.base[0] + AT_KT <= src.Ck && gd.base[0] + AT_KT <= src.Cp) {
