@@ -45,7 +45,7 @@ struct alignas(16) KmSmem {
   uint16_t mu_hat[S::NP][CT * 16][S::MUP];
   float mu_norm[CT * 16];
   uint16_t xt[S::NS][D][S::XTP];
-  int32_t lab[S::SUB];
+  uint16_t lab[S::SUB];      // labels of the sub-tile (0xffff: no point)
   int32_t cnt[MUSE_MAXC];
   int32_t wcnt[4][MUSE_MAXC];
   float red[8];
@@ -162,6 +162,13 @@ __device__ __forceinline__ int med3i(int a, int b, int c) {
   int r;
   asm("v_med3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
+}
+
+// Smallest two of {m1, m2, a, b} (m1 <= m2, all distinct) into m1, m2: the
+// second smallest is min(m2, med3(m1, a, b)).
+__device__ __forceinline__ void top2_pair(int& m1, int& m2, int a, int b) {
+  m2 = min(m2, med3i(m1, a, b));
+  m1 = min(min(m1, a), b);
 }
 
 template <typename V8>
@@ -384,7 +391,7 @@ __device__ __forceinline__ void km_finish_group(SM& sm, const XRegs<TIn, D>& xr,
     if (need) label = bc;
   }
   if (g == 0) {
-    sm.lab[pl] = valid ? label : -1;
+    sm.lab[pl] = valid ? (uint16_t)label : (uint16_t)0xffff;
     if (valid) glab[sub0 + pl] = label;
   }
 }
@@ -420,12 +427,9 @@ __device__ void km_assign_bf16(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nv
 #pragma unroll
         for (int u = 0; u < TBX; ++u)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = (__float_as_int(acc[q][u][i]) & KMASK) | (16 * (t0 + u) + i);
-            const int n2 = med3i(m1[q], m2[q], key);
-            m1[q] = min(m1[q], key);
-            m2[q] = n2;
-          }
+          for (int i = 0; i < 4; i += 2)
+            top2_pair(m1[q], m2[q], (__float_as_int(acc[q][u][i]) & KMASK) | (16 * (t0 + u) + i),
+                      (__float_as_int(acc[q][u][i + 1]) & KMASK) | (16 * (t0 + u) + i + 1));
     };
 #pragma unroll
     for (int t0 = 0; t0 < CT; t0 += 2) {
@@ -453,12 +457,9 @@ __device__ void km_assign_bf16(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nv
 #pragma unroll
         for (int u = 0; u < TBX; ++u)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = (__float_as_int(acc[u][i]) & KMASK) | (16 * (t0 + u) + i);
-            const int n2 = med3i(m1, m2, key);
-            m1 = min(m1, key);
-            m2 = n2;
-          }
+          for (int i = 0; i < 4; i += 2)
+            top2_pair(m1, m2, (__float_as_int(acc[u][i]) & KMASK) | (16 * (t0 + u) + i),
+                      (__float_as_int(acc[u][i + 1]) & KMASK) | (16 * (t0 + u) + i + 1));
       };
 #pragma unroll
       for (int t0 = 0; t0 < CT; t0 += TB) {
@@ -611,10 +612,31 @@ __device__ void km_assign_sub(SM& sm, const XRegs<TIn, D>& xr, int sub0, int nva
       label = bc;
     }
     if (g == 0) {
-      sm.lab[pl] = valid ? label : -1;
+      sm.lab[pl] = valid ? (uint16_t)label : (uint16_t)0xffff;
       if (valid) glab[sub0 + pl] = label;
     }
   }
+}
+
+// bf16 one-hot of 8 labels held two to a register: 1.0 where a label equals
+// the cluster (both halves of clp), else 0.  Per half: x = l ^ c is zero
+// exactly on a match; min(x, 1) is 0 or 1; 0x3F80 - 0x3F80 min(x, 1) (modulo
+// 2^16) is 1.0 or 0.  Three packed 16-bit integer operations per two labels.
+template <typename V>
+__device__ __forceinline__ u16x8 onehot8(const V& lp, uint32_t clp) {
+  // (each constant is given in both halves of a register: an inline constant
+  // would supply only the low half)
+  const uint32_t one1 = 0x00010001u, neg = 0xC080C080u, one = 0x3F803F80u;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t m, o;
+    asm("v_pk_min_u16 %0, %1, %2" : "=v"(m) : "v"((uint32_t)lp[q] ^ clp), "v"(one1));
+    asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(o) : "v"(m), "v"(neg), "v"(one));
+    r[q] = o;
+  }
+  return __builtin_bit_cast(u16x8, r);
 }
 
 // One-hot update: acc += onehot(labels) . X.  Wave w owns the cluster tiles
@@ -654,9 +676,9 @@ __device__ void km_update_sub(SM& sm, KmAcc<TIn, D, CT>& acc, int Ceff) {
   const int col = lane & 15, g = lane >> 4;
 #pragma unroll 2
   for (int ks = 0; ks < S::SUB / 32; ++ks) {
-    const int4 l0 = *reinterpret_cast<const int4*>(&sm.lab[32 * ks + 8 * g]);
-    const int4 l1 = *reinterpret_cast<const int4*>(&sm.lab[32 * ks + 8 * g + 4]);
-    const int labs[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+    // labels of points 32ks + 8g .. +7, two to a register
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 lp = *reinterpret_cast<const u32x4*>(&sm.lab[32 * ks + 8 * g]);
     u16x8 b[NDT][NS];
 #pragma unroll
     for (int d = 0; d < NDT; ++d) {
@@ -669,10 +691,7 @@ __device__ void km_update_sub(SM& sm, KmAcc<TIn, D, CT>& acc, int Ceff) {
     for (int c = 0; c < NCT; ++c) {
       const int ct = CT >= 4 ? w + 4 * c : CT == 2 ? (w & 1) : 0;
       if (ct * 16 >= Ceff) continue;
-      u16x8 a;
-      const int cl = 16 * ct + col;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = (labs[j] == cl) ? (uint16_t)0x3F80 : (uint16_t)0;
+      const u16x8 a = onehot8(lp, (uint32_t)(16 * ct + col) * 0x10001u);
 #pragma unroll
       for (int d = 0; d < NDT; ++d) acc.a[c * NDT + d] = mfma_split<1, NS>(&a, b[d], acc.a[c * NDT + d]);
     }
