@@ -1193,9 +1193,11 @@ template <typename TIn, int D>
 static hipError_t attn_all(const Plan& pl, const AttnBufs& b, bool vt_done, hipStream_t st) {
   hipError_t e = vt_done ? hipSuccess : launch_vt<TIn, D>(pl, b, st);
   if (e != hipSuccess) return e;
-  // Every launch keeps one group of 16 queries per wave: two groups halve the
-  // LDS fragment reads per MFMA but need about 200 VGPRs (285 at D = 128),
-  // and the lost workgroups per CU cost more than the reads save.
+  // One group of 16 queries per wave, except at causal levels of query
+  // clusters of 128 rows and more (bf16, D = 64): there two groups per wave,
+  // which halve the LDS fragment reads per MFMA, measured 1 % faster at 64k
+  // (at 8k, and at smaller clusters, the workgroups lost per CU to their
+  // 200 VGPRs cost more than the reads save; 285 VGPRs at D = 128).
   if (pl.causal) {
     // local blocks: 64-row query tiles
     constexpr int WAVES = 4, QT = 16 * 4;
@@ -1216,7 +1218,8 @@ static hipError_t attn_all(const Plan& pl, const AttnBufs& b, bool vt_done, hipS
     // query clusters of ~m/C rows: the query tile (rows per workgroup) follows
     // the mean cluster size so that ragged clusters waste few tile rows
     const int avg = pl.lev_m[lev] / (pl.C > 0 ? pl.C : 1);
-    if (avg >= 48) e = attn_level<TIn, D, 4, 1>(pl, b, lev, st);
+    if (sizeof(TIn) == 2 && D == 64 && pl.causal && avg >= 128) e = attn_level<TIn, D, 4, 2>(pl, b, lev, st);
+    else if (avg >= 48) e = attn_level<TIn, D, 4, 1>(pl, b, lev, st);
     else if constexpr (sizeof(TIn) == 2 || D == 64) e = attn_level<TIn, D, 1, 1>(pl, b, lev, st);
     else e = attn_level<TIn, D, 4, 1>(pl, b, lev, st);   // one wave could not keep a tile's copies counted
     if (e != hipSuccess) return e;

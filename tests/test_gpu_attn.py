@@ -172,3 +172,18 @@ def test_large_clusters():
     # many contiguous exact tiles per retrieved cluster
     run_case(1, 2, 1, 4000, 64, "bf16", 16, 3, 2, seed=31, comps=16)
     run_case(1, 2, 1, 8192, 64, "bf16", 8, 2, 2, causal=True, block=1024, seed=32, comps=8)
+
+
+def test_causal_launch_shapes_by_level():
+    """Causal GQA levels whose query clusters average 32, 64, 128 and 256
+    rows: one-wave workgroups, four waves of one query group, and four
+    waves of two query groups, with ragged last segments."""
+    run_case(1, 4, 2, 6000, 64, "bf16", 16, 3, 3, causal=True, block=512, seed=51, comps=16)
+
+
+def test_one_wave_more_exact_chunks_than_the_table():
+    """Query clusters of about 32 rows (one-wave workgroups) retrieving six of
+    eight key clusters of about 512 rows: more exact 8-row chunks than the
+    per-workgroup chunk table holds (256), so tiles are walked from the
+    segment list instead."""
+    run_case(1, 2, 1, 4096, 64, "bf16", 128, 3, 6, seed=52, comps=16, ck=8)
