@@ -758,11 +758,18 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
       return V4 ? qoffs[c * qstr + e] : qoffs[c + e];
     };
     if (tid < 64) {
-      int v[4], sum = 0;
+      // every offset is read unconditionally (clusters past Cq read cluster
+      // Cq - 1), so the reads are one round trip
+      int lo[4], hi[4], v[4], sum = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int c = tid * 4 + q;
-        v[q] = c < Cq ? (qpos(c, 1) - qpos(c, 0) + QT - 1) / QT : 0;
+        const int c = max(min(tid * 4 + q, Cq - 1), 0);
+        lo[q] = qpos(c, 0);
+        hi[q] = qpos(c, 1);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = tid * 4 + q < Cq ? (hi[q] - lo[q] + QT - 1) / QT : 0;
         sum += v[q];
       }
       int inc = sum;
@@ -773,11 +780,11 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
       int run = inc - sum;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int c = tid * 4 + q;
-        if (c < Cq && v[q] > 0 && slot >= run && slot < run + v[q]) {
-          sm.sel[0] = c;
+        if (v[q] > 0 && slot >= run && slot < run + v[q]) {
+          sm.sel[0] = tid * 4 + q;
           sm.sel[1] = slot - run;
-          sm.sel[3] = qpos(c, 0);
+          sm.sel[3] = lo[q];
+          sm.sel[6] = hi[q];
         }
         run += v[q];
       }
@@ -785,10 +792,11 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     }
     __syncthreads();
     if (slot >= sm.sel[2]) return;
-    I = sm.sel[0];
-    tile = sm.sel[1];
-    qlo = sm.sel[3] + tile * QT;
-    qhi = min(qpos(I, 1), qlo + QT);
+    // the selection is the workgroup's own (uniform)
+    I = __builtin_amdgcn_readfirstlane(sm.sel[0]);
+    tile = __builtin_amdgcn_readfirstlane(sm.sel[1]);
+    qlo = __builtin_amdgcn_readfirstlane(sm.sel[3]) + tile * QT;
+    qhi = min(__builtin_amdgcn_readfirstlane(sm.sel[6]), qlo + QT);
     const int bq = bh / pl.Hq, hq = bh % pl.Hq;
     kvh = bq * pl.Hkv + (hq * pl.Hkv) / pl.Hq;
     kp = kvh * pl.P + p;
@@ -799,17 +807,17 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
   }
   const TIn* Qh = reinterpret_cast<const TIn*>(b.Q) + (size_t)bh * pl.N * D;
 
-  for (int r = tid; r < QT; r += NT) {
-    int row = -1;
-    if (qlo + r < qhi) {
-      if (MODE == MODE_LOCAL) {
-        row = qlo + r;
-      } else {
-        const int32_t* qperm = b.qs.perm + ((size_t)lev * pl.B * pl.Hq + bh) * pl.N + q0;
-        row = qperm[qlo + r];
-      }
-    }
-    sm.qrow[r] = row;
+  // the workgroup's query rows, one per thread (QT <= NT).  The row list,
+  // far-item and retrieved-cluster reads below are all issued before any of
+  // them is used, every index kept in range, so they overlap in flight.
+  static_assert(QT <= NT, "one query row per thread");
+  int qrow_t;
+  if (MODE == MODE_LOCAL) {
+    qrow_t = qlo + tid < qhi ? qlo + tid : -1;
+  } else {
+    const int32_t* qperm = b.qs.perm + ((size_t)lev * pl.B * pl.Hq + bh) * pl.N + q0;
+    const int v = qperm[min(qlo + tid, qhi - 1)];   // qlo < qhi
+    qrow_t = qlo + tid < qhi ? v : -1;
   }
   const size_t esz = sizeof(TIn);
   TileSrc src;
@@ -830,41 +838,65 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     // MODE_V4: the far items of group (I, block vb), one per key cluster
     const size_t grp = V4 ? ((size_t)bh * pl.nb + vb) * pl.Cq + I : 0;
     const float* fbI = V4 ? b.fbias + grp * b.Cp32 : b.fb + ((size_t)ap * C + I) * b.Cp32;
-    for (int c = tid; c < MUSE_MAXC; c += NT) {
-      float bias = -INFINITY;
-      if (c < Ck) {
-        if (xt) {
-          bias = fbI[c];
-        } else {
-          const int nc = koffs[c + 1] - koffs[c];
-          if (nc > 0) bias = __log2f((float)nc);
-        }
+    // far item c of this thread: c = tid + i NT
+    constexpr int FBN = MUSE_MAXC / NT;
+    float fbv[FBN];
+    int kn0[FBN], kn1[FBN];
+#pragma unroll
+    for (int i = 0; i < FBN; ++i) {
+      const int c = tid + i * NT;
+      if (xt) {
+        fbv[i] = fbI[max(min(c, Ck - 1), 0)];
+        kn0[i] = kn1[i] = 0;
+      } else {
+        fbv[i] = 0.f;
+        kn0[i] = koffs[min(c, Ck)];
+        kn1[i] = koffs[min(c + 1, Ck)];
       }
-      sm.far_bias[c] = bias / s2;   // the logit is s2 (score + bias / s2)
     }
     int cc[4];
     if (tid < 64) {
       // compact the non-empty retrieved clusters into segments of absolute rows
       int lo[4], hi[4], v[4], sum = 0;
+      if constexpr (V4) {
+        // retrieved (cluster, block) pairs: entry r is block slot r % k2w of
+        // retrieved cluster slot r / k2w
+        const size_t g1 = (((size_t)bh * pl.Cq + I) * pl.nb + vb) * pl.k1w;
+        const int nr = pl.k1w * pl.k2w;
+        int c1[4], be[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = min(tid * 4 + q, nr - 1);
+          c1[q] = b.r1[g1 + r / pl.k2w];
+          be[q] = b.r2[g1 * pl.k2w + r];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool ok = tid * 4 + q < nr && c1[q] >= 0 && be[q] >= 0;
+          const int32_t* kbr = b.kb + ((size_t)kvh * pl.Ck + min(max(c1[q], 0), pl.Ck - 1)) * (pl.nb + 1) +
+                               min(max(be[q], 0), pl.nb - 1);
+          const int a = kbr[0], e = kbr[1];
+          cc[q] = -1;   // retrieved clusters keep their far item (the rest of their keys)
+          lo[q] = ok ? a : 0;
+          hi[q] = ok ? e : 0;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = tid * 4 + q;
+          const int rv = Rr[min(r, pl.k1w - 1)];
+          cc[q] = r < pl.k1w ? rv : -1;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ci = min(max(cc[q], 0), C - 1);
+          const int a = koffs[ci], e = koffs[ci + 1];
+          lo[q] = cc[q] >= 0 ? a : 0;
+          hi[q] = cc[q] >= 0 ? e : 0;
+        }
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = tid * 4 + q;
-        if constexpr (V4) {
-          // retrieved (cluster, block) pairs: entry r is block slot r % k2w
-          // of retrieved cluster slot r / k2w
-          const size_t g1 = (((size_t)bh * pl.Cq + I) * pl.nb + vb) * pl.k1w;
-          const int j = r / pl.k2w;
-          const int c = r < pl.k1w * pl.k2w ? b.r1[g1 + j] : -1;
-          const int be = c >= 0 ? b.r2[g1 * pl.k2w + r] : -1;
-          const int32_t* kbr = b.kb + ((size_t)kvh * pl.Ck + max(c, 0)) * (pl.nb + 1);
-          cc[q] = -1;   // retrieved clusters keep their far item (the rest of their keys)
-          lo[q] = be >= 0 ? kbr[be] : 0;
-          hi[q] = be >= 0 ? kbr[be + 1] : 0;
-        } else {
-          cc[q] = r < pl.k1w ? Rr[r] : -1;
-          lo[q] = cc[q] >= 0 ? koffs[cc[q]] : 0;
-          hi[q] = cc[q] >= 0 ? koffs[cc[q] + 1] : 0;
-        }
         v[q] = hi[q] > lo[q] ? 1 : 0;
         sum += v[q];
       }
@@ -890,6 +922,17 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
       for (int mm = 32; mm >= 1; mm >>= 1) ntl += __shfl_xor(ntl, mm, 64);
       if (tid == 63) { sm.sel[4] = inc; sm.sel[5] = ntl; }   // inclusive total, and the all-reduced count
     }
+#pragma unroll
+    for (int i = 0; i < FBN; ++i) {
+      const int c = tid + i * NT;
+      float bias = -INFINITY;
+      if (c < Ck) {
+        const int nc = kn1[i] - kn0[i];
+        bias = xt ? fbv[i] : nc > 0 ? __log2f((float)nc) : -INFINITY;
+      }
+      sm.far_bias[c] = bias / s2;   // the logit is s2 (score + bias / s2)
+    }
+    if (tid < QT) sm.qrow[tid] = qrow_t;
     __syncthreads();
     // retrieved clusters leave the far field
     if (tid < 64) {
@@ -917,6 +960,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
       sm.seg_lo[0] = k0;
       sm.seg_hi[0] = qhi;
     }
+    if (tid < QT) sm.qrow[tid] = qrow_t;
     src.nseg = 1;
     src.Kx = reinterpret_cast<const TIn*>(b.K) + (size_t)kvh * pl.N * D;
     const size_t slice = (size_t)pl.nlev * pl.B * pl.Hkv + kvh;   // input-order copy follows the levels
@@ -1000,25 +1044,48 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
       return v;
     }
   };
+  // the first copies (one stage: the first tile) go out before the query
+  // reads, so that their latencies overlap
+  constexpr int P0 = PD == 0 ? 1 : PD;
 #pragma unroll
-  for (int p = 0; p < PD; ++p)
+  for (int p = 0; p < P0; ++p)
     if (p < ntiles) issue_next(stg[p]);
-  // query fragments (loaded after the first copies are on their way)
+  // query fragments, and at causal levels with one query group at D = 64 the
+  // row's fp32 partial that the result merges into (read now, not after the
+  // last tile)
+  constexpr bool PREF = MODE == MODE_LEVEL && D == 64 && QG == 1;
   int myq[QG];
   u16x8 qf[QG][KS][NS];
   AtState<D> st[QG];
+  f32x4 opre[DT];
+  float lpre = 0.f;
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     myq[qg] = sm.qrow[(w * QG + qg) * 16 + col];
     // lanes without a query row load row 0; their outputs are not written
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
+    for (int k = 0; k < KS; ++k)
       load8_split<TIn, NS>(Qh + (size_t)max(myq[qg], 0) * D + 32 * k + 8 * g, qf[qg][k]);
-      // keep the fragments in registers (a read-only load could otherwise be
-      // re-issued inside the tile loop)
+  }
+  if constexpr (PREF) {
+    const size_t r = (size_t)bh * pl.N + max(myq[0], 0);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) opre[dt] = *reinterpret_cast<const f32x4*>(b.oacc + r * D + 16 * dt + 4 * g);
+    lpre = b.lacc[r];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+v"(opre[dt]));
+    asm volatile("" : "+v"(lpre));
+  }
+  // keep the fragments in registers (a read-only load could otherwise be
+  // re-issued inside the tile loop)
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
 #pragma unroll
       for (int sp = 0; sp < NS; ++sp) asm volatile("" : "+v"(qf[qg][k][sp]));
-    }
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
     st[qg].m = -1e30f;
     st[qg].lsum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1040,11 +1107,14 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
     // and tile t-1 is consumed.  Only real tiles are copied.
     asm volatile("" ::: "memory");
     if constexpr (PD == 0) {
-      // one stage: after every wave is done with tile t-1, copy tile t and wait for it
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      issue_next(stg[0]);
-      asm volatile("" ::: "memory");
+      // one stage: after every wave is done with tile t-1, copy tile t (tile
+      // 0 went out before the query reads) and wait for it
+      if (t > 0) {
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue_next(stg[0]);
+        asm volatile("" ::: "memory");
+      }
       __builtin_amdgcn_s_waitcnt(at_wait(0, 0));
       __builtin_amdgcn_s_barrier();
     } else {
@@ -1110,7 +1180,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
         }
       } else {
         if (!(l > 0.f) && !fin) continue;
-        const float lold = *la;
+        const float lold = PREF ? lpre : *la;
         float fo = 1.f, fn = 0.f, lnew = lold;
         if (l > 0.f) {
           const float L = fmaxf(lold, lse);
@@ -1124,7 +1194,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
         f32x4 mv[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          mv[dt] = *reinterpret_cast<const f32x4*>(oa + 16 * dt + 4 * g) * fo + on[dt] * fn;
+          mv[dt] = (PREF ? opre[dt] : *reinterpret_cast<const f32x4*>(oa + 16 * dt + 4 * g)) * fo + on[dt] * fn;
         if (fin) {
           write_out(mv, lnew);
         } else {
