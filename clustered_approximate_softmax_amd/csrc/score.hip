@@ -232,118 +232,149 @@ struct alignas(16) TiltSmem {
   uint16_t nu[NS][TILT_IC][D + 8];   // nu rows of one query problem, bf16 parts
 };
 
-// One value dim d of T for the staged query clusters [i0, i0 + 16 nit):
+// Value dims d0 .. d0+nd-1 of T for the staged query clusters [i0, i0 + 16 nit):
 // jobs of NT2 adjacent 16-cluster tiles (A = rows of M in registers).  With
 // NT2 = 2 two lane exchanges give each lane eight consecutive clusters, so a
 // store writes 64 contiguous bytes of each of 16 rows (bf16); with NT2 = 1 a
 // lane stores its four clusters.  When there are fewer pairs than waves, pairs
 // would split the query clusters between waves and load each M row twice, so
-// small cluster counts take NT2 = 1.
+// small cluster counts take NT2 = 1.  Every read stays in range (clusters past
+// Ck read cluster Ck - 1, offsets past Ck offset Ck) and is issued before any
+// is used; the next dim's M rows and value sums are read while this dim's
+// products are formed and stored.
 template <typename TIn, int D, int NS, int NT2, typename SM>
-__device__ __forceinline__ void tilt_dim(const SM& sm, const float* Mk, const float* Sk, const int32_t* koffs,
-                                         TIn* T, int d, int C, int Ck, int Cp, int Cq, int i0, int nit, float s) {
+__device__ __forceinline__ void tilt_dims(const SM& sm, const float* Mk, const float* Sk, const int32_t* koffs,
+                                          TIn* T, int d0, int nd, int C, int Ck, int Cp, int Cq, int i0, int nit,
+                                          float s) {
   constexpr int KS = D / 32;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
   const int njob = Cp / (16 * NT2);
   for (int job = w; job < njob; job += 4) {
-    u16x8 a[NT2][KS][NS];
-    float sv[NT2][4], inv[NT2][4];
+    // the lane's four clusters of each tile (the same for every dim)
+    int o0[NT2][4], o1[NT2][4];
 #pragma unroll
-    for (int h = 0; h < NT2; ++h) {
-      const int cr = 16 * (NT2 * job + h) + col;   // A row: cluster
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        float v[8];
-        if (cr < Ck) {
-          const float* src = Mk + ((size_t)d * C + cr) * D + 32 * k + 8 * g;
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-          v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
-          v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          uint16_t hh, m, l;
-          split3(v[j], hh, m, l);
-          a[h][k][0][j] = NS == 1 ? f2bf(v[j]) : hh;
-          if (NS > 1) { a[h][k][NS > 1 ? 1 : 0][j] = m; a[h][k][NS > 2 ? 2 : 0][j] = l; }
-        }
-      }
-      // the lane's four clusters of this tile: value sum and 1 / n_c
+    for (int h = 0; h < NT2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 16 * (NT2 * job + h) + 4 * g + i;
-        const int nc = c < Ck ? koffs[c + 1] - koffs[c] : 0;
-        inv[h][i] = nc > 0 ? 1.f / (float)nc : 0.f;
-        sv[h][i] = nc > 0 ? Sk[(size_t)c * D + d] : 0.f;
+        o0[h][i] = koffs[min(c, Ck)];
+        o1[h][i] = koffs[min(c + 1, Ck)];
       }
-    }
-    for (int it = 0; it < nit; ++it) {
-      f32x4 acc[NT2];
-#pragma unroll
-      for (int h = 0; h < NT2; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        u16x8 bb[NS];
-#pragma unroll
-        for (int sp = 0; sp < NS; ++sp)
-          bb[sp] = *reinterpret_cast<const u16x8*>(&sm.nu[sp][16 * it + col][32 * k + 8 * g]);
-#pragma unroll
-        for (int h = 0; h < NT2; ++h) acc[h] = mfma_split<NS, NS>(a[h][k], bb, acc[h]);
-      }
-      // lane (col, g) holds clusters 16h + 4g + i of the job, WB dwords per tile
-      constexpr int WB = sizeof(TIn) == 2 ? 2 : 4;
-      uint32_t pw[NT2][WB];
+    // raw M rows of one dim (A row: cluster) and the value sums of its clusters
+    f32x4 mr[NT2][KS][2];
+    float sr[NT2][4];
+    auto fetch = [&](int d) __attribute__((always_inline)) {
 #pragma unroll
       for (int h = 0; h < NT2; ++h) {
-        float o[4];
+        const int cr = max(min(16 * (NT2 * job + h) + col, Ck - 1), 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (sv[h][i] + s * acc[h][i]) * inv[h][i];
-        if constexpr (sizeof(TIn) == 2) {
-          pw[h][0] = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-          pw[h][1] = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
-        } else {
+        for (int k = 0; k < KS; ++k) {
+          const float* src = Mk + ((size_t)d * C + cr) * D + 32 * k + 8 * g;
+          mr[h][k][0] = *reinterpret_cast<const f32x4*>(src);
+          mr[h][k][1] = *reinterpret_cast<const f32x4*>(src + 4);
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pw[h][i] = __float_as_uint(o[i]);
+        for (int i = 0; i < 4; ++i) {
+          const int c = max(min(16 * (NT2 * job + h) + 4 * g + i, Ck - 1), 0);
+          sr[h][i] = Sk[(size_t)c * D + d];
         }
       }
-      const int I = i0 + 16 * it + col;
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      if constexpr (NT2 == 1) {
-        if (I < Cq) {
-          TIn* dst = T + ((size_t)I * D + d) * Cp + 16 * job + 4 * g;
-          if constexpr (sizeof(TIn) == 2) *reinterpret_cast<u32x2*>(dst) = u32x2{pw[0][0], pw[0][1]};
-          else *reinterpret_cast<u32x4*>(dst) = u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]};
-        }
-      } else {
-        // across lane bit 5: groups 0, 1 keep tile 0 and take tile 0 of group g + 2;
-        // groups 2, 3 keep tile 1 and take tile 1 of group g - 2
-        const bool hi2 = g >= 2, odd = g & 1;
-        uint32_t e[2][WB], f[2][WB];
+    };
+    fetch(d0);
+    float inv[NT2][4];
 #pragma unroll
-        for (int q = 0; q < WB; ++q) {
-          const uint32_t r = lane_xor32(hi2 ? pw[0][q] : pw[NT2 - 1][q]);
-          e[0][q] = hi2 ? r : pw[0][q];
-          e[1][q] = hi2 ? pw[NT2 - 1][q] : r;
-        }
-        // across lane bit 4: even groups keep their first half, odd groups their second
+    for (int h = 0; h < NT2; ++h)
 #pragma unroll
-        for (int q = 0; q < WB; ++q) {
-          const uint32_t r = lane_xor16(odd ? e[0][q] : e[1][q]);
-          f[0][q] = odd ? r : e[0][q];
-          f[1][q] = odd ? e[1][q] : r;
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * (NT2 * job + h) + 4 * g + i;
+        const int nc = c < Ck ? o1[h][i] - o0[h][i] : 0;
+        inv[h][i] = nc > 0 ? 1.f / (float)nc : 0.f;
+      }
+    for (int dd = 0; dd < nd; ++dd) {
+      const int d = d0 + dd;
+      u16x8 a[NT2][KS][NS];
+      float sv[NT2][4];
+#pragma unroll
+      for (int h = 0; h < NT2; ++h) {
+        const bool live = 16 * (NT2 * job + h) + col < Ck;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float v = live ? mr[h][k][j >> 2][j & 3] : 0.f;
+            uint16_t hh, m, l;
+            split3(v, hh, m, l);
+            a[h][k][0][j] = NS == 1 ? f2bf(v) : hh;
+            if (NS > 1) { a[h][k][NS > 1 ? 1 : 0][j] = m; a[h][k][NS > 2 ? 2 : 0][j] = l; }
+          }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[h][i] = inv[h][i] > 0.f ? sr[h][i] : 0.f;
+      }
+      if (dd + 1 < nd) fetch(d + 1);
+      for (int it = 0; it < nit; ++it) {
+        f32x4 acc[NT2];
+#pragma unroll
+        for (int h = 0; h < NT2; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          u16x8 bb[NS];
+#pragma unroll
+          for (int sp = 0; sp < NS; ++sp)
+            bb[sp] = *reinterpret_cast<const u16x8*>(&sm.nu[sp][16 * it + col][32 * k + 8 * g]);
+#pragma unroll
+          for (int h = 0; h < NT2; ++h) acc[h] = mfma_split<NS, NS>(a[h][k], bb, acc[h]);
         }
-        if (I < Cq) {
-          TIn* dst = T + ((size_t)I * D + d) * Cp + 32 * job + 8 * g;
+        // lane (col, g) holds clusters 16h + 4g + i of the job, WB dwords per tile
+        constexpr int WB = sizeof(TIn) == 2 ? 2 : 4;
+        uint32_t pw[NT2][WB];
+#pragma unroll
+        for (int h = 0; h < NT2; ++h) {
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = (sv[h][i] + s * acc[h][i]) * inv[h][i];
           if constexpr (sizeof(TIn) == 2) {
-            *reinterpret_cast<u32x4*>(dst) = u32x4{f[0][0], f[0][1], f[1][0], f[1][1]};
+            pw[h][0] = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
+            pw[h][1] = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
           } else {
-            *reinterpret_cast<u32x4*>(dst) = u32x4{f[0][0], f[0][1], f[0][2], f[0][3]};
-            *reinterpret_cast<u32x4*>(dst + 4) = u32x4{f[1][0], f[1][1], f[1][2], f[1][3]};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pw[h][i] = __float_as_uint(o[i]);
+          }
+        }
+        const int I = i0 + 16 * it + col;
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        if constexpr (NT2 == 1) {
+          if (I < Cq) {
+            TIn* dst = T + ((size_t)I * D + d) * Cp + 16 * job + 4 * g;
+            if constexpr (sizeof(TIn) == 2) *reinterpret_cast<u32x2*>(dst) = u32x2{pw[0][0], pw[0][1]};
+            else *reinterpret_cast<u32x4*>(dst) = u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]};
+          }
+        } else {
+          // across lane bit 5: groups 0, 1 keep tile 0 and take tile 0 of group g + 2;
+          // groups 2, 3 keep tile 1 and take tile 1 of group g - 2
+          const bool hi2 = g >= 2, odd = g & 1;
+          uint32_t e[2][WB], f[2][WB];
+#pragma unroll
+          for (int q = 0; q < WB; ++q) {
+            const uint32_t r = lane_xor32(hi2 ? pw[0][q] : pw[NT2 - 1][q]);
+            e[0][q] = hi2 ? r : pw[0][q];
+            e[1][q] = hi2 ? pw[NT2 - 1][q] : r;
+          }
+          // across lane bit 4: even groups keep their first half, odd groups their second
+#pragma unroll
+          for (int q = 0; q < WB; ++q) {
+            const uint32_t r = lane_xor16(odd ? e[0][q] : e[1][q]);
+            f[0][q] = odd ? r : e[0][q];
+            f[1][q] = odd ? e[1][q] : r;
+          }
+          if (I < Cq) {
+            TIn* dst = T + ((size_t)I * D + d) * Cp + 32 * job + 8 * g;
+            if constexpr (sizeof(TIn) == 2) {
+              *reinterpret_cast<u32x4*>(dst) = u32x4{f[0][0], f[0][1], f[1][0], f[1][1]};
+            } else {
+              *reinterpret_cast<u32x4*>(dst) = u32x4{f[0][0], f[0][1], f[0][2], f[0][3]};
+              *reinterpret_cast<u32x4*>(dst + 4) = u32x4{f[1][0], f[1][1], f[1][2], f[1][3]};
+            }
           }
         }
       }
@@ -378,28 +409,33 @@ __device__ __forceinline__ void tilt_block(const Plan& pl, const AttnBufs& b, in
   for (int i0 = 0; i0 < Cq; i0 += TILT_IC) {
     const int nit = (min(TILT_IC, Cq - i0) + 15) / 16;
     __syncthreads();
-    for (int idx = tid; idx < nit * 16 * (D / 8); idx += 256) {
-      const int r = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
-      const int I = i0 + r;
-      float v[8];
-      if (I < Cq) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(nu + (size_t)I * D + e0);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(nu + (size_t)I * D + e0 + 4);
-        v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
-        v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
-      } else {
+    // nu rows, four 8-element pieces per thread in flight at a time (rows
+    // past Cq read row Cq - 1 and stage zeros)
+    const int npc = nit * 16 * (D / 8);
+    for (int idx0 = 0; idx0 < npc; idx0 += 4 * 256) {
+      f32x4 x[4][2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = 0.f;
+      for (int u = 0; u < 4; ++u) {
+        const int idx = min(idx0 + u * 256 + tid, npc - 1);
+        const int I = min(i0 + idx / (D / 8), Cq - 1), e0 = (idx % (D / 8)) * 8;
+        x[u][0] = *reinterpret_cast<const f32x4*>(nu + (size_t)I * D + e0);
+        x[u][1] = *reinterpret_cast<const f32x4*>(nu + (size_t)I * D + e0 + 4);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) split_store<NS>(v[j], &sm.nu[0][r][e0 + j], TILT_IC * (D + 8));
+      for (int u = 0; u < 4; ++u) {
+        const int idx = idx0 + u * 256 + tid;
+        if (idx < npc) {
+          const int r = idx / (D / 8), e0 = (idx % (D / 8)) * 8;
+          const bool live = i0 + r < Cq;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            split_store<NS>(live ? x[u][j >> 2][j & 3] : 0.f, &sm.nu[0][r][e0 + j], TILT_IC * (D + 8));
+        }
+      }
     }
     __syncthreads();
-    for (int dd = 0; dd < tb; ++dd) {
-      const int d = db * tb + dd;
-      if (Cp >= 128) tilt_dim<TIn, D, NS, 2>(sm, Mk, Sk, koffs, T, d, C, Ck, Cp, Cq, i0, nit, s);
-      else tilt_dim<TIn, D, NS, 1>(sm, Mk, Sk, koffs, T, d, C, Ck, Cp, Cq, i0, nit, s);
-    }
+    if (Cp >= 128) tilt_dims<TIn, D, NS, 2>(sm, Mk, Sk, koffs, T, db * tb, tb, C, Ck, Cp, Cq, i0, nit, s);
+    else tilt_dims<TIn, D, NS, 1>(sm, Mk, Sk, koffs, T, db * tb, tb, C, Ck, Cp, Cq, i0, nit, s);
   }
 }
 
