@@ -83,15 +83,23 @@ __device__ __forceinline__ int slot_of(int r) {
 }
 
 // wave-0 scan over per-cluster tile counts: the (cluster, tile) of `slot`.
-// sel[0] = cluster, sel[1] = tile within it, sel[2] = total tiles.
+// sel[0] = cluster, sel[1] = the tile's first row (offs[cluster] + tile * tile
+// size), sel[2] = total tiles, sel[3] = the cluster's end (offs[cluster + 1]).
 __device__ __forceinline__ void find_slot(const int32_t* offs, int Cn, int tile, int slot, int* sel) {
   const int tid = threadIdx.x;
   if (tid < 64) {
-    int v[4], sum = 0;
+    // every offset is read unconditionally (clusters past Cn read cluster
+    // Cn - 1), so the reads are one round trip
+    int lo[4], hi[4], v[4], sum = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int c = tid * 4 + q;
-      v[q] = c < Cn ? (offs[c + 1] - offs[c] + tile - 1) / tile : 0;
+      const int c = max(min(tid * 4 + q, Cn - 1), 0);
+      lo[q] = offs[c];
+      hi[q] = offs[c + 1];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = tid * 4 + q < Cn ? (hi[q] - lo[q] + tile - 1) / tile : 0;
       sum += v[q];
     }
     int inc = sum;
@@ -102,10 +110,10 @@ __device__ __forceinline__ void find_slot(const int32_t* offs, int Cn, int tile,
     int run = inc - sum;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int c = tid * 4 + q;
-      if (c < Cn && v[q] > 0 && slot >= run && slot < run + v[q]) {
-        sel[0] = c;
-        sel[1] = slot - run;
+      if (v[q] > 0 && slot >= run && slot < run + v[q]) {
+        sel[0] = tid * 4 + q;
+        sel[1] = lo[q] + (slot - run) * tile;
+        sel[3] = hi[q];
       }
       run += v[q];
     }
@@ -210,31 +218,40 @@ __device__ __forceinline__ void bq_stage(BqSmem<TIn, D>& sm, bool far, const TIn
     // bf16: raw 16-byte row chunks; K^T as 4-item runs in slot order
     for (int idx = threadIdx.x; idx < (BT / 4) * (D / 8); idx += NT) {
       const int kb = idx % (BT / 4), e0 = (idx / (BT / 4)) * 8;
+      // every read in range (absent items read row / cluster 0, or the last
+      // cluster) and issued in one group; absent items are zeroed after
       u16x8 kr[4], vr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int it = 4 * kb + r;
-        kr[r] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        vr[r] = kr[r];
-        if (far) {
-          if (c0 + it < Ck) kr[r] = *reinterpret_cast<const u16x8*>(mu + (size_t)(c0 + it) * D + e0);
-        } else {
-          const int row = sm.irow[it];
-          if (row >= 0) {
-            kr[r] = *reinterpret_cast<const u16x8*>(Kb + (size_t)row * D + e0);
-            vr[r] = *reinterpret_cast<const u16x8*>(Vb + (size_t)row * D + e0);
-          }
-        }
-      }
+      bool ok[4];
       if (far) {
-        // T / n_c is stored (d, c): four consecutive clusters per dim
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const u16x4 t4 = *reinterpret_cast<const u16x4*>(T + (size_t)(e0 + j) * Cp + c0 + 4 * kb);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) vr[r][j] = t4[r];
+        for (int r = 0; r < 4; ++r) {
+          const int c = c0 + 4 * kb + r;
+          ok[r] = c < Ck;
+          kr[r] = *reinterpret_cast<const u16x8*>(mu + (size_t)max(min(c, Ck - 1), 0) * D + e0);
         }
+        // T / n_c is stored (d, c): four consecutive clusters per dim
+        u16x4 t4[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t4[j] = *reinterpret_cast<const u16x4*>(T + (size_t)(e0 + j) * Cp + c0 + 4 * kb);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vr[r][j] = t4[j][r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = sm.irow[4 * kb + r];
+          ok[r] = row >= 0;
+          kr[r] = *reinterpret_cast<const u16x8*>(Kb + (size_t)max(row, 0) * D + e0);
+          vr[r] = *reinterpret_cast<const u16x8*>(Vb + (size_t)max(row, 0) * D + e0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (!ok[r]) vr[r] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (!ok[r]) kr[r] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       const int pos = 32 * ((4 * kb) / 32) + slot_of((4 * kb) % 32);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -340,31 +357,32 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_q_kernel(BwdArgs A, int lev) {
     find_slot(qoffs, Cq, QT, slot, sm.sel);
     __syncthreads();
     if (slot >= sm.sel[2]) return;
-    I = sm.sel[0];
-    qlo = qoffs[I] + sm.sel[1] * QT;
-    qhi = min(qoffs[I + 1], qlo + QT);
+    I = __builtin_amdgcn_readfirstlane(sm.sel[0]);
+    qlo = __builtin_amdgcn_readfirstlane(sm.sel[1]);
+    qhi = min(__builtin_amdgcn_readfirstlane(sm.sel[3]), qlo + QT);
   }
   const int kvh = (bh / pl.Hq) * pl.Hkv + ((bh % pl.Hq) * pl.Hkv) / pl.Hq;
   const int kp = kvh * pl.P + (ap % pl.P);
-  if (tid < 64) {
-    int r = -1;
-    if (qlo + tid < qhi) {
-      if (MODE == BQ_LOCAL) r = qlo + tid;
-      else r = b.qs.perm[((size_t)lev * pl.B * pl.Hq + bh) * pl.N + q0 + qlo + tid];
-    }
-    sm.qrow[tid] = r;
+  // query rows (one per thread of wave 0), far-item counts and the retrieved
+  // list: every read in range and issued before any is used
+  int qrow_t = -1;
+  if (MODE == BQ_LOCAL) {
+    qrow_t = qlo + tid < qhi ? qlo + tid : -1;
+  } else {
+    const int v = b.qs.perm[((size_t)lev * pl.B * pl.Hq + bh) * pl.N + q0 + min(qlo + tid, qhi - 1)];
+    qrow_t = qlo + tid < qhi ? v : -1;
   }
   int nfar = 0, nret = 0;
   if (MODE != BQ_LOCAL) {
     const int32_t* koffs = b.ks.offs + (size_t)kp * (C + 1);
     const int32_t* Rr = b.R + ((size_t)ap * C + I) * pl.k1w;
-    for (int c = tid; c < MUSE_MAXC; c += NT) {
-      float bias = -INFINITY;
-      if (c < Ck) {
-        const int nc = koffs[c + 1] - koffs[c];
-        if (nc > 0) bias = __log2f((float)nc);
-      }
-      sm.far_bias[c] = bias;
+    constexpr int FBN = (MUSE_MAXC + NT - 1) / NT;
+    int kn0[FBN], kn1[FBN];
+#pragma unroll
+    for (int i = 0; i < FBN; ++i) {
+      const int c = tid + i * NT;
+      kn0[i] = koffs[min(c, Ck)];
+      kn1[i] = koffs[min(c + 1, Ck)];
     }
     int cc[4];
     if (tid < 64) {
@@ -372,9 +390,15 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_q_kernel(BwdArgs A, int lev) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = tid * 4 + q;
-        cc[q] = r < pl.k1w ? Rr[r] : -1;
-        bg[q] = cc[q] >= 0 ? koffs[cc[q]] : 0;
-        v[q] = cc[q] >= 0 ? koffs[cc[q] + 1] - bg[q] : 0;
+        const int rv = Rr[min(r, pl.k1w - 1)];
+        cc[q] = r < pl.k1w ? rv : -1;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ci = min(max(cc[q], 0), C - 1);
+        const int a = koffs[ci], e = koffs[ci + 1];
+        bg[q] = cc[q] >= 0 ? a : 0;
+        v[q] = cc[q] >= 0 ? e - a : 0;
         sum += v[q];
       }
       int inc = sum;
@@ -392,6 +416,13 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_q_kernel(BwdArgs A, int lev) {
       }
       if (tid == 63) sm.rcum[MUSE_MAXC] = inc;
     }
+#pragma unroll
+    for (int i = 0; i < FBN; ++i) {
+      const int c = tid + i * NT;
+      const int nc = kn1[i] - kn0[i];
+      if (c < MUSE_MAXC) sm.far_bias[c] = c < Ck && nc > 0 ? __log2f((float)nc) : -INFINITY;
+    }
+    if (tid < 64) sm.qrow[tid] = qrow_t;
     __syncthreads();
     // retrieved clusters leave the far field
     if (tid < 64) {
@@ -403,6 +434,7 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_q_kernel(BwdArgs A, int lev) {
     nfar = (Ck + BT - 1) / BT;
   } else {
     nret = qhi - k0;
+    if (tid < 64) sm.qrow[tid] = qrow_t;
   }
   __syncthreads();
   const TIn* Qh = reinterpret_cast<const TIn*>(b.Q) + (size_t)bh * pl.N * D;
@@ -626,8 +658,14 @@ __device__ __forceinline__ void bk_consume(const BkSmem<TIn, D>& sm,
   }
 }
 
-// A stream of n queries: query q < n is row row_at(q) of Qh / dOh / lse /
-// delta (-1: none).  bf16: software-pipelined.  While tile t is contracted,
+// Where a stream position's row index lies: the row is base + *p.
+struct RowLoc {
+  const int32_t* p;
+  int base;
+};
+
+// A stream of n queries: query q < n is row base + *p of Qh / dOh / lse /
+// delta, {p, base} = row_of(q).  bf16: software-pipelined.  While tile t is contracted,
 // the Q / dO rows and the lse / Delta of tile t+1 are in flight, and the row
 // indices of tile t+2 (so that no load waits on another inside an
 // iteration).
@@ -647,14 +685,34 @@ __device__ __forceinline__ void bk_query_stream(BkSmem<TIn, D>& sm, const TIn* Q
     const bool stg = tid < NSTG;
     const int qb4 = tid % (QB / 4), e0 = (tid / (QB / 4)) * 8;
     const int ntile = (qb - qa + QB - 1) / QB;
-    auto row_at = [&](int q) __attribute__((always_inline)) -> int { return q < qb ? row_of(q) : -1; };
-    int r1[4], r2[4], s1 = -1, s2r = -1;
+    if (n <= 0) return;
+    int r1[4], s1 = -1;
     u16x8 qd[4], od[4];
     float l1 = 0.f, d1 = 0.f;
-    auto load_rows = [&](int q0, int (&rr)[4], int& sr) __attribute__((always_inline)) {
+    // the five row indices a thread needs are located first (LDS only), then
+    // read together (positions past the stream read its last row's index);
+    // the read values stay pending until take_rows needs them
+    int v2[5], b2[5];
+    bool f2[5];
+    auto load_rows = [&](int q0) __attribute__((always_inline)) {
+      RowLoc lc[5];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rr[r] = stg ? row_at(q0 + 4 * qb4 + r) : -1;
-      sr = tid < QB ? row_at(q0 + tid) : -1;
+      for (int r = 0; r < 4; ++r) {
+        lc[r] = row_of(min(q0 + 4 * qb4 + r, qb - 1));
+        f2[r] = stg && q0 + 4 * qb4 + r < qb;
+      }
+      lc[4] = row_of(min(q0 + tid, qb - 1));
+      f2[4] = tid < QB && q0 + tid < qb;
+#pragma unroll
+      for (int u = 0; u < 5; ++u) {
+        b2[u] = lc[u].base;
+        v2[u] = *lc[u].p;
+      }
+    };
+    auto take_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) r1[r] = f2[r] ? b2[r] + v2[r] : -1;
+      s1 = f2[4] ? b2[4] + v2[4] : -1;
     };
     auto load_data = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -666,12 +724,15 @@ __device__ __forceinline__ void bk_query_stream(BkSmem<TIn, D>& sm, const TIn* Q
           od[r] = *reinterpret_cast<const u16x8*>(dOh + (size_t)r1[r] * D + e0);
         }
       }
-      l1 = s1 >= 0 ? lse[s1] * B_LOG2E : 0.f;
-      d1 = s1 >= 0 ? delta[s1] : 0.f;
+      // raw values (row 0's for lanes without a row), scaled and masked when
+      // staged, so that nothing here waits for them
+      l1 = lse[max(s1, 0)];
+      d1 = delta[max(s1, 0)];
     };
-    load_rows(qa, r1, s1);
+    load_rows(qa);
+    take_rows();
     load_data();
-    if (ntile > 1) load_rows(qa + QB, r2, s2r);
+    if (ntile > 1) load_rows(qa + QB);
     for (int t = 0; t < ntile; ++t) {
       // tile t into LDS
       if (stg) {
@@ -689,17 +750,15 @@ __device__ __forceinline__ void bk_query_stream(BkSmem<TIn, D>& sm, const TIn* Q
       }
       if (tid < QB) {
         sm.qrow[tid] = s1;
-        sm.lse2[tid] = l1;
-        sm.dlt[tid] = d1;
+        sm.lse2[tid] = s1 >= 0 ? l1 * B_LOG2E : 0.f;
+        sm.dlt[tid] = s1 >= 0 ? d1 : 0.f;
       }
       __syncthreads();
       // tile t+1's rows and scalars, tile t+2's row indices: in flight during the contraction
       if (t + 1 < ntile) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) r1[r] = r2[r];
-        s1 = s2r;
+        take_rows();
         load_data();
-        if (t + 2 < ntile) load_rows(qa + (t + 2) * QB, r2, s2r);
+        if (t + 2 < ntile) load_rows(qa + (t + 2) * QB);
       }
       bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
       __syncthreads();
@@ -708,7 +767,12 @@ __device__ __forceinline__ void bk_query_stream(BkSmem<TIn, D>& sm, const TIn* Q
     for (int q0 = qa; q0 < qb; q0 += QB) {
       if (threadIdx.x < QB) {
         const int q = q0 + threadIdx.x;
-        sm.qrow[threadIdx.x] = q < qb ? row_of(q) : -1;
+        int r = -1;
+        if (q < qb) {
+          const RowLoc lc = row_of(q);
+          r = lc.base + *lc.p;
+        }
+        sm.qrow[threadIdx.x] = r;
       }
       __syncthreads();
       bk_stage_queries<TIn, D, NT>(sm, Qh, dOh, lse, delta);
@@ -742,16 +806,29 @@ __device__ __forceinline__ void bk_query_range(BkSmem<TIn, D>& sm, const BwdArgs
     const bool stg = tid < NSTG;
     const int qb4 = tid % (QB / 4), e0 = (tid / (QB / 4)) * 8;
     const int ntile = (qb - qa + QB - 1) / QB;
-    auto row_at = [&](int q) __attribute__((always_inline)) -> int {
-      return q < qb ? (rows ? rows[q] : q) : -1;
-    };
-    int r1[4], r2[4], s1 = -1, s2r = -1;
+    if (qb <= qa) return;
+    int r1[4], s1 = -1;
     u16x8 qd[4], od[4];
     float l1 = 0.f, d1 = 0.f;
-    auto load_rows = [&](int q0, int (&rr)[4], int& sr) __attribute__((always_inline)) {
+    // row indices read together (positions past the range read its last one);
+    // the read values stay pending until take_rows needs them
+    int v2[5];
+    bool f2[5];
+    auto load_rows = [&](int q0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rr[r] = stg ? row_at(q0 + 4 * qb4 + r) : -1;
-      sr = tid < QB ? row_at(q0 + tid) : -1;
+      for (int r = 0; r < 4; ++r) {
+        const int q = min(q0 + 4 * qb4 + r, qb - 1);
+        v2[r] = rows ? rows[q] : q;
+        f2[r] = stg && q0 + 4 * qb4 + r < qb;
+      }
+      const int q = min(q0 + tid, qb - 1);
+      v2[4] = rows ? rows[q] : q;
+      f2[4] = tid < QB && q0 + tid < qb;
+    };
+    auto take_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) r1[r] = f2[r] ? v2[r] : -1;
+      s1 = f2[4] ? v2[4] : -1;
     };
     auto load_data = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -763,12 +840,23 @@ __device__ __forceinline__ void bk_query_range(BkSmem<TIn, D>& sm, const BwdArgs
           od[r] = *reinterpret_cast<const u16x8*>(dOh + (size_t)r1[r] * D + e0);
         }
       }
-      l1 = s1 >= 0 ? lse[s1] * B_LOG2E : 0.f;
-      d1 = s1 >= 0 ? delta[s1] : 0.f;
+      if constexpr (CAUSAL) {
+        // local block: scaled and masked here (measured faster in this
+        // instantiation, where the deferred form split the row reads above
+        // into several waited groups)
+        l1 = s1 >= 0 ? lse[s1] * B_LOG2E : 0.f;
+        d1 = s1 >= 0 ? delta[s1] : 0.f;
+      } else {
+        // raw values (row 0's for lanes without a row), scaled and masked
+        // when staged, so that nothing here waits for them
+        l1 = lse[max(s1, 0)];
+        d1 = delta[max(s1, 0)];
+      }
     };
-    load_rows(qa, r1, s1);
+    load_rows(qa);
+    take_rows();
     load_data();
-    if (ntile > 1) load_rows(qa + QB, r2, s2r);
+    if (ntile > 1) load_rows(qa + QB);
     for (int t = 0; t < ntile; ++t) {
       // tile t into LDS
       if (stg) {
@@ -786,17 +874,15 @@ __device__ __forceinline__ void bk_query_range(BkSmem<TIn, D>& sm, const BwdArgs
       }
       if (tid < QB) {
         sm.qrow[tid] = s1;
-        sm.lse2[tid] = l1;
-        sm.dlt[tid] = d1;
+        sm.lse2[tid] = CAUSAL ? l1 : s1 >= 0 ? l1 * B_LOG2E : 0.f;
+        sm.dlt[tid] = CAUSAL ? d1 : s1 >= 0 ? d1 : 0.f;
       }
       __syncthreads();
       // tile t+1's rows and scalars, tile t+2's row indices: in flight during the contraction
       if (t + 1 < ntile) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) r1[r] = r2[r];
-        s1 = s2r;
+        take_rows();
         load_data();
-        if (t + 2 < ntile) load_rows(qa + (t + 2) * QB, r2, s2r);
+        if (t + 2 < ntile) load_rows(qa + (t + 2) * QB);
       }
       bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
       __syncthreads();
@@ -861,9 +947,9 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
     find_slot(koffs, Ck, IT, slot, sm.sel);
     __syncthreads();
     if (slot >= sm.sel[2]) return;
-    c = sm.sel[0];
-    ibeg = koffs[c] + sm.sel[1] * IT;
-    iend = min(koffs[c + 1], ibeg + IT);
+    c = __builtin_amdgcn_readfirstlane(sm.sel[0]);
+    ibeg = __builtin_amdgcn_readfirstlane(sm.sel[1]);
+    iend = min(__builtin_amdgcn_readfirstlane(sm.sel[3]), ibeg + IT);
   }
 
   // ---- this lane's item (wave w owns items 16w .. 16w+15) ----
@@ -916,11 +1002,21 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
     for (int base = 0; base < total; base += NT) {
       const int e = base + tid;
       bool hit = false;
-      if (e < total) {
-        const int hl = e / Cq, Iq = e % Cq;
+      {
+        // every read in range (pairs past the total read the last pair, entries
+        // past k1 the last entry), eight in flight at a time
+        const int ec = min(e, total - 1);
+        const int hl = ec / Cq, Iq = ec % Cq;
         const int bhx = bq * pl.Hq + (kvh % pl.Hkv) * Gq + hl;
         const int32_t* Rr = b.R + (((size_t)bhx * pl.P + p) * C + Iq) * pl.k1w;
-        for (int r = 0; r < pl.k1w; ++r) hit |= (Rr[r] == c);
+        for (int r0 = 0; r0 < pl.k1w; r0 += 8) {
+          int rv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) rv[u] = Rr[min(r0 + u, pl.k1w - 1)];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) hit |= rv[u] == c;
+        }
+        hit = hit && e < total;
       }
       const unsigned long long bal = __ballot(hit);
       if (lane == 0) sm.wc[w] = __popcll(bal);
@@ -937,18 +1033,21 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
       // its queries at q_perm positions hq0[li] + 0, 1, ... of head hbh[li]
       if (tid < 64) {
         int v[4], pos[4], hb[4], sum = 0;
+        // unlisted slots read pair 0's offsets (in range) and count nothing
+        int o1[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int li = tid * 4 + q;
-          v[q] = 0;
-          if (li < cnt) {
-            const int ent = sm.list[li];
-            const int hl = ent / Cq, Iq = ent % Cq;
-            hb[q] = bq * pl.Hq + (kvh % pl.Hkv) * Gq + hl;
-            const int32_t* qoffs = b.qs.offs + ((size_t)hb[q] * pl.P + p) * (C + 1);
-            pos[q] = qoffs[Iq];
-            v[q] = qoffs[Iq + 1] - pos[q];
-          }
+          const int ent = li < cnt ? sm.list[li] : 0;
+          const int hl = ent / Cq, Iq = ent % Cq;
+          hb[q] = bq * pl.Hq + (kvh % pl.Hkv) * Gq + hl;
+          const int32_t* qoffs = b.qs.offs + ((size_t)hb[q] * pl.P + p) * (C + 1);
+          pos[q] = qoffs[Iq];
+          o1[q] = qoffs[Iq + 1];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = tid * 4 + q < cnt ? o1[q] - pos[q] : 0;
           sum += v[q];
         }
         int inc = sum;
@@ -974,12 +1073,13 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
       const int32_t* permb = b.qs.perm + (size_t)lev * pl.B * pl.Hq * pl.N + gm.q0;
       if constexpr (KIND == BK_STREAM) {
         int hc = 0;   // this thread's cursor: successive lookups move it a few pairs at most
-        auto row_of = [&](int v) __attribute__((always_inline)) -> int {
-          // the pair holding stream position v: the last li with cum[li] <= v
+        auto row_of = [&](int v) __attribute__((always_inline)) -> RowLoc {
+          // the pair holding stream position v: the last li with cum[li] <= v;
+          // its row is base + *p
           while (hc > 0 && sm.cum[hc] > v) --hc;
           while (hc + 1 < cnt && sm.cum[hc + 1] <= v) ++hc;
           const int bhx = sm.hbh[hc];
-          return bhx * pl.N + permb[(size_t)bhx * pl.N + sm.hq0[hc] + (v - sm.cum[hc])];
+          return RowLoc{permb + (size_t)bhx * pl.N + sm.hq0[hc] + (v - sm.cum[hc]), bhx * pl.N};
         };
         bk_query_stream<TIn, D, false, NT>(sm, reinterpret_cast<const TIn*>(A.a.Q),
                                            reinterpret_cast<const TIn*>(A.dO), A.lse, A.delta, total, row_of, kf,
@@ -1473,9 +1573,10 @@ __global__ void __launch_bounds__(NT) bwd_bcast_k_kernel(BwdArgs A, int lev) {
   find_slot(koffs, Ck, 64, slot, sm.sel);
   __syncthreads();
   if (slot >= sm.sel[2]) return;
-  const int c = sm.sel[0];
-  const int beg = koffs[c] + sm.sel[1] * 64, cnt = min(koffs[c + 1], beg + 64) - beg;
-  const float inv = 1.f / (float)(koffs[c + 1] - koffs[c]);
+  const int c = __builtin_amdgcn_readfirstlane(sm.sel[0]);
+  const int beg = __builtin_amdgcn_readfirstlane(sm.sel[1]), end = __builtin_amdgcn_readfirstlane(sm.sel[3]);
+  const int cnt = min(end, beg + 64) - beg;
+  const float inv = 1.f / (float)(end - koffs[c]);
   const bool dip = pl.dipole != 0;
   if (dip) {
     // D x D floats as 16-byte loads, all of a thread's in flight at once
@@ -1547,13 +1648,22 @@ __global__ void __launch_bounds__(NT) bwd_bcast_k_kernel(BwdArgs A, int lev) {
       }
     }
   }
+  // read every key's running gradients first (keys past cnt read key cnt - 1,
+  // cnt >= 1), then add and write
+  float ok[NJ], ov[NJ];
+  size_t oo[NJ];
 #pragma unroll
   for (int q = 0; q < NJ; ++q) {
-    const int j = grp + NG * q;
-    if (j >= cnt) continue;
-    const size_t o = ((size_t)kvh * pl.N + sm.rows[j]) * D + e;
-    A.dk[o] += gk[q];
-    A.dv[o] += gv[q];
+    const int j = min(grp + NG * q, cnt - 1);
+    oo[q] = ((size_t)kvh * pl.N + sm.rows[j]) * D + e;
+    ok[q] = A.dk[oo[q]];
+    ov[q] = A.dv[oo[q]];
+  }
+#pragma unroll
+  for (int q = 0; q < NJ; ++q) {
+    if (grp + NG * q >= cnt) continue;
+    A.dk[oo[q]] = ok[q] + gk[q];
+    A.dv[oo[q]] = ov[q] + gv[q];
   }
 }
 
