@@ -309,21 +309,83 @@ __device__ __forceinline__ void km_finish_group(SM& sm, const XRegs<TIn, D>& xr,
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
   const int pl = w * (S::SUB / 4) + grp * 16 + col;
   const bool valid = pl < nvalid;
+  // the two-candidate shortcut below is taken from four cluster tiles up
+  // (with fewer, its registers cost occupancy and the full scan is short)
+  constexpr bool TWO = CT >= 4;
   m1 |= 4 * g;
+  int m3 = 0;
+  if constexpr (TWO) {
+    m2 |= 4 * g;
+    // merged over the lane groups: best m1, runner-up m2, and m3, a lower
+    // bound on the third key (a group's unknown third is bounded below by
+    // its runner-up); the third of two sorted triples is
+    // min(a3, b3, max(a1, b2), max(a2, b1))
+    m3 = m2;
 #pragma unroll
-  for (int m = 16; m <= 32; m <<= 1) {
-    const int b1 = __shfl_xor(m1, m, 64), b2 = __shfl_xor(m2, m, 64);
-    m2 = min(max(m1, b1), min(m2, b2));
-    m1 = min(m1, b1);
+    for (int m = 16; m <= 32; m <<= 1) {
+      const int b1 = __shfl_xor(m1, m, 64), b2 = __shfl_xor(m2, m, 64), b3 = __shfl_xor(m3, m, 64);
+      m3 = min(min(m3, b3), min(max(m1, b2), max(m2, b1)));
+      m2 = min(max(m1, b1), min(m2, b2));
+      m1 = min(m1, b1);
+    }
+  } else {
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+      const int b1 = __shfl_xor(m1, m, 64), b2 = __shfl_xor(m2, m, 64);
+      m2 = min(max(m1, b1), min(m2, b2));
+      m1 = min(m1, b1);
+    }
   }
   int label = m1 & ((1 << IB) - 1);
   const float f1 = __int_as_float(m1 & KMASK), f2 = __int_as_float(m2 & KMASK);
   const float xn = sqrtf(xsq);
   // screening error (split residual, accumulation, norm split) plus key truncation
+  const float trunc = IB == 7 ? 3.0517578125e-05f : 6.103515625e-05f;
   const float margin = 2.44140625e-4f * xn * Rmax + 1.220703125e-4f * (xsq + Rmax * Rmax) +
-                       (IB == 7 ? 3.0517578125e-05f : 6.103515625e-05f) * (fabsf(f1) + fabsf(f2));
+                       trunc * (fabsf(f1) + fabsf(f2));
   const bool need = valid && Ceff > 1 && (f2 - f1 <= margin);
-  if (__any(need)) {
+  // The candidates (screened distance within f1 + margin) are exactly the
+  // best and the runner-up when every other key is at least m3 >= 0 (keys of
+  // non-negative distances order as the distances, and a key's distance bits
+  // are at most its screened distance) with f3 beyond the threshold, and the
+  // runner-up's screened distance (below f2 plus its truncation) is inside it.
+  // (m3 = INT_MAX, a NaN pattern, means there is no third key.)
+  const float thr = f1 + margin;
+  const float f3 = __int_as_float(m3 & KMASK);
+  const bool two = TWO && m3 >= 0 && !(f3 <= thr) && f2 + trunc * fabsf(f2) <= thr;
+  if (TWO && !__any(need && !two)) {
+    if (TWO && __any(need)) {
+      // exact fp32 distances of the two candidates, both rows read together
+      const int c1 = min(m1 & ((1 << IB) - 1), Ceff - 1), c2 = min(m2 & ((1 << IB) - 1), Ceff - 1);
+      float mv1[KS][8], mv2[KS][8];
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if constexpr (SM::KEEP32) {
+            mv1[k][j] = sm.mu32[c1][32 * k + 8 * g + j];
+            mv2[k][j] = sm.mu32[c2][32 * k + 8 * g + j];
+          } else {
+            mv1[k][j] = cent[(size_t)c1 * D + 32 * k + 8 * g + j];
+            mv2[k][j] = cent[(size_t)c2 * D + 32 * k + 8 * g + j];
+          }
+        }
+      float p1 = 0.f, p2 = 0.f;
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float d1 = xval(xr.x[grp][k], j) - mv1[k][j], d2 = xval(xr.x[grp][k], j) - mv2[k][j];
+          p1 = fmaf(d1, d1, p1);
+          p2 = fmaf(d2, d2, p2);
+        }
+      p1 += __shfl_xor(p1, 16, 64);
+      p2 += __shfl_xor(p2, 16, 64);
+      p1 += __shfl_xor(p1, 32, 64);
+      p2 += __shfl_xor(p2, 32, 64);
+      if (need) label = (p2 < p1 || (p2 == p1 && c2 < c1)) ? c2 : c1;
+    }
+  } else if (__any(need)) {
     // candidates within the margin; the screening MFMAs are recomputed by the
     // whole wave (an MFMA reads its operands from every lane, active or not)
     const float thr = f1 + margin;

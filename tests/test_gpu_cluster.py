@@ -68,6 +68,49 @@ def test_kmeans_lockstep(G, n, D, C, dtype, iters):
         prev = cent[:, :Ce].astype(np.float64)
 
 
+@pytest.mark.parametrize("n,C,D", [(1500, 16, 64), (6000, 64, 64), (5000, 32, 128)])
+def test_kmeans_near_ties(n, C, D):
+    """Points near the bisector of two starting centroids (a third is far) and
+    near the circumcentre of three (the point of their plane equidistant from
+    all three): the screening cannot decide them,
+    so the fp32 refinement does, from the two-candidate shortcut (best and
+    runner-up, the third key provably outside the margin) and from the full
+    candidate scan.  Labels must be the fp64 nearest centroid except at
+    relative ties; in-workgroup (n <= 2048) and chunked paths."""
+    import torch
+    r = np.random.default_rng(n + C)
+    cen = 2.0 * r.standard_normal((C, D))
+
+    def circumcentre(a, b, c):
+        u, v = b - a, c - a
+        s, t = np.linalg.solve([[u @ u, u @ v], [u @ v, v @ v]], [0.5 * (u @ u), 0.5 * (v @ v)])
+        return a + s * u + t * v
+
+    pts = []
+    for i in range(n - C):
+        if i % 4 == 3:
+            a, b, c = r.choice(C, 3, replace=False)
+            x = circumcentre(cen[a], cen[b], cen[c])
+        else:
+            a, b = r.choice(C, 2, replace=False)
+            x = 0.5 * (cen[a] + cen[b])
+        pts.append(x + 1e-3 * r.standard_normal(D))
+    X = np.concatenate([cen, np.array(pts)])[None]
+    X = gu.synth.to_dtype(X, "bf16")
+    init = np.arange(C, dtype=np.int32)[None]
+    a, _, _, _ = (t.cpu().numpy() for t in M.musecluster(gu.to_dev(X, "bf16"), C, 1, torch.from_numpy(init).cuda()))
+    mu = X[0][:C].astype(np.float64)
+    gu.check_labels(X[0], mu, a[0])
+    # the workload does exercise the refinement: many points lie within a
+    # relative 1e-3 of a tie between their two nearest centroids, and some of
+    # a tie among three
+    x64 = X[0].astype(np.float64)
+    d = ((x64[:, None, :] - mu[None]) ** 2).sum(-1)
+    d.sort(axis=1)
+    assert np.mean((d[:, 1] - d[:, 0]) <= 1e-3 * d[:, 1]) > 0.2
+    assert np.mean((d[:, 2] - d[:, 0]) <= 1e-3 * d[:, 2]) > 0.03
+
+
 def test_kmeans_default_init_and_determinism():
     import torch
     X = _points(2, 4096, 64, "bf16", 32, 9)
