@@ -1269,12 +1269,13 @@ static hipError_t attn_all(const Plan& pl, const AttnBufs& b, bool vt_done, hipS
   // (at 8k, and at smaller clusters, the workgroups lost per CU to their
   // 200 VGPRs cost more than the reads save; 285 VGPRs at D = 128).
   if (pl.causal) {
-    // local blocks: 64-row query tiles
-    constexpr int WAVES = 4, QT = 16 * 4;
+    // local blocks: 128-row query tiles (two query groups per wave) for
+    // bf16 at D = 64, else 64-row tiles
+    constexpr int WAVES = 4, QGL = (sizeof(TIn) == 2 && D == 64) ? 2 : 1, QT = 16 * QGL * 4;
     const int nblk = (pl.N + pl.blk - 1) / pl.blk;
     const long long grid = (long long)pl.B * pl.Hq * nblk * ((pl.blk + QT - 1) / QT);
     MUSE_KT_PRE(st);
-    attn_kernel<TIn, TIn, D, WAVES, 1, MODE_LOCAL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, 0);
+    attn_kernel<TIn, TIn, D, WAVES, QGL, MODE_LOCAL><<<(unsigned)grid, 64 * WAVES, 0, st>>>(pl, b, 0);
     MUSE_KT_POST("attn_local", st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -878,12 +878,13 @@ __global__ void __launch_bounds__(KM_NT) km_local_kernel(Plan pl, CSet s0, CSet 
   using S = KmShape<TIn, D>;
   extern __shared__ __align__(16) unsigned char smraw[];
   KmSmem<TIn, D, CT>& sm = *reinterpret_cast<KmSmem<TIn, D, CT>*>(smraw);
-  int id = blockIdx.x;
-  // largest problems first: p descends within each set
-  const CSet& s = (id < s0.heads * plocal) ? s0 : s1;
-  if (id >= s0.heads * plocal) id -= s0.heads * plocal;
-  const int head = id % s.heads;
-  const int p = plocal - 1 - id / s.heads;
+  // largest problems first across both sets: p descends, and for each p
+  // every head of both sets
+  const int nh = s0.heads + s1.heads;
+  const int hh = (int)blockIdx.x % nh;
+  const int p = plocal - 1 - (int)blockIdx.x / nh;
+  const CSet& s = hh < s0.heads ? s0 : s1;
+  const int head = hh < s0.heads ? hh : hh - s0.heads;
   int lev, r0, n;
   cset_rows(pl, s, p, lev, r0, n);
   const int C = pl.C, Ceff = min(s.C, n);
