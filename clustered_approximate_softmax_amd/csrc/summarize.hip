@@ -63,9 +63,11 @@ __global__ void __launch_bounds__(SU_NT, 2) summarize_kernel(Plan pl, CSet ks, c
   static_assert(KT % KPP == 0 && KT % 32 == 0, "tile shape");
   __shared__ SM sm;
   const int C = pl.C;
+  // largest problems (highest p) first: problem rank, then head, then cluster
   const int c = blockIdx.x % C;
-  const int hp = blockIdx.x / C;      // head * P + p
-  const int head = hp / pl.P, p = hp % pl.P;
+  const int head = (blockIdx.x / C) % ks.heads;
+  const int p = pl.P - 1 - (int)(blockIdx.x / ((unsigned)C * ks.heads));
+  const int hp = head * pl.P + p;     // head * P + p
   int lev, r0, n;
   cset_rows(pl, ks, p, lev, r0, n);
   const int Ceff = min(C, n);
