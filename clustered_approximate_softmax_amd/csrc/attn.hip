@@ -549,12 +549,6 @@ __device__ __forceinline__ void lds_frag(const unsigned char* row, int lg, int k
   }
 }
 
-// two floats -> packed bf16 pair (hardware round to nearest even)
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
-  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-  bf2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 template <int D>
 struct AtState {

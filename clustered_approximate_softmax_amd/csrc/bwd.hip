@@ -44,18 +44,13 @@ struct BwdTraits {
   static constexpr int BT = sizeof(TIn) == 2 ? 64 : 32; // items per query-centric tile
 };
 
-__device__ __forceinline__ uint32_t b_pk_bf16(float a, float b) {
-  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-  bf2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 // 8 floats (contraction slots in order) -> NS bf16 parts
 template <int NS>
 __device__ __forceinline__ void pack8(const float* x, u16x8* out) {
   if constexpr (NS == 1) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 w = {b_pk_bf16(x[0], x[1]), b_pk_bf16(x[2], x[3]), b_pk_bf16(x[4], x[5]), b_pk_bf16(x[6], x[7])};
+    u32x4 w = {pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]), pk_bf16(x[6], x[7])};
     out[0] = __builtin_bit_cast(u16x8, w);
   } else {
 #pragma unroll

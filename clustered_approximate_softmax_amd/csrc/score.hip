@@ -233,10 +233,12 @@ struct alignas(16) TiltSmem {
 };
 
 // Value dims d0 .. d0+nd-1 of T for the staged query clusters [i0, i0 + 16 nit):
-// jobs of NT2 adjacent 16-cluster tiles (A = rows of M in registers).  With
-// NT2 = 2 two lane exchanges give each lane eight consecutive clusters, so a
-// store writes 64 contiguous bytes of each of 16 rows (bf16); with NT2 = 1 a
-// lane stores its four clusters.  When there are fewer pairs than waves, pairs
+// jobs of NT2 16-cluster tiles (A = rows of M in registers).  With NT2 = 2 a
+// job covers 32 consecutive clusters and MFMA row r of tile h is cluster
+// 8(r/4) + 4h + r%4 of the job, so the accumulator rows a lane holds (4g ..
+// 4g+3 of both tiles) are the eight consecutive clusters 8g .. 8g+7: a store
+// writes 64 contiguous bytes of each of 16 rows (bf16) with no lane exchange;
+// with NT2 = 1 a lane stores its four clusters.  When there are fewer pairs than waves, pairs
 // would split the query clusters between waves and load each M row twice, so
 // small cluster counts take NT2 = 1.  Every read stays in range (clusters past
 // Ck read cluster Ck - 1, offsets past Ck offset Ck) and is issued before any
@@ -250,13 +252,17 @@ __device__ __forceinline__ void tilt_dims(const SM& sm, const float* Mk, const f
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
   const int njob = Cp / (16 * NT2);
   for (int job = w; job < njob; job += 4) {
+    // the cluster of MFMA row r of tile h
+    auto clu = [&](int h, int r) __attribute__((always_inline)) {
+      return NT2 == 2 ? 32 * job + 8 * (r >> 2) + 4 * h + (r & 3) : 16 * job + r;
+    };
     // the lane's four clusters of each tile (the same for every dim)
     int o0[NT2][4], o1[NT2][4];
 #pragma unroll
     for (int h = 0; h < NT2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = 16 * (NT2 * job + h) + 4 * g + i;
+        const int c = clu(h, 4 * g + i);
         o0[h][i] = koffs[min(c, Ck)];
         o1[h][i] = koffs[min(c + 1, Ck)];
       }
@@ -266,7 +272,7 @@ __device__ __forceinline__ void tilt_dims(const SM& sm, const float* Mk, const f
     auto fetch = [&](int d) __attribute__((always_inline)) {
 #pragma unroll
       for (int h = 0; h < NT2; ++h) {
-        const int cr = max(min(16 * (NT2 * job + h) + col, Ck - 1), 0);
+        const int cr = max(min(clu(h, col), Ck - 1), 0);
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
           const float* src = Mk + ((size_t)d * C + cr) * D + 32 * k + 8 * g;
@@ -275,7 +281,7 @@ __device__ __forceinline__ void tilt_dims(const SM& sm, const float* Mk, const f
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int c = max(min(16 * (NT2 * job + h) + 4 * g + i, Ck - 1), 0);
+          const int c = max(min(clu(h, 4 * g + i), Ck - 1), 0);
           sr[h][i] = Sk[(size_t)c * D + d];
         }
       }
@@ -286,7 +292,7 @@ __device__ __forceinline__ void tilt_dims(const SM& sm, const float* Mk, const f
     for (int h = 0; h < NT2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = 16 * (NT2 * job + h) + 4 * g + i;
+        const int c = clu(h, 4 * g + i);
         const int nc = c < Ck ? o1[h][i] - o0[h][i] : 0;
         inv[h][i] = nc > 0 ? 1.f / (float)nc : 0.f;
       }
@@ -296,7 +302,7 @@ __device__ __forceinline__ void tilt_dims(const SM& sm, const float* Mk, const f
       float sv[NT2][4];
 #pragma unroll
       for (int h = 0; h < NT2; ++h) {
-        const bool live = 16 * (NT2 * job + h) + col < Ck;
+        const bool live = clu(h, col) < Ck;
 #pragma unroll
         for (int k = 0; k < KS; ++k)
 #pragma unroll
@@ -311,7 +317,11 @@ __device__ __forceinline__ void tilt_dims(const SM& sm, const float* Mk, const f
         for (int i = 0; i < 4; ++i) sv[h][i] = inv[h][i] > 0.f ? sr[h][i] : 0.f;
       }
       if (dd + 1 < nd) fetch(d + 1);
-      for (int it = 0; it < nit; ++it) {
+      // this lane's store address for query cluster i0 + col, stepped by 16
+      // query clusters per iteration
+      TIn* dst = T + ((size_t)(i0 + col) * D + d) * Cp + 16 * NT2 * job + (NT2 == 2 ? 8 : 4) * g;
+      const size_t dstep = (size_t)16 * D * Cp;
+      for (int it = 0; it < nit; ++it, dst += dstep) {
         f32x4 acc[NT2];
 #pragma unroll
         for (int h = 0; h < NT2; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -324,7 +334,8 @@ __device__ __forceinline__ void tilt_dims(const SM& sm, const float* Mk, const f
 #pragma unroll
           for (int h = 0; h < NT2; ++h) acc[h] = mfma_split<NS, NS>(a[h][k], bb, acc[h]);
         }
-        // lane (col, g) holds clusters 16h + 4g + i of the job, WB dwords per tile
+        // lane (col, g) holds MFMA rows 4g .. 4g+3 of each tile (clusters
+        // clu(h, 4g + i)) for query cluster i0 + 16 it + col, WB dwords per tile
         constexpr int WB = sizeof(TIn) == 2 ? 2 : 4;
         uint32_t pw[NT2][WB];
 #pragma unroll
@@ -333,8 +344,8 @@ __device__ __forceinline__ void tilt_dims(const SM& sm, const float* Mk, const f
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[i] = (sv[h][i] + s * acc[h][i]) * inv[h][i];
           if constexpr (sizeof(TIn) == 2) {
-            pw[h][0] = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-            pw[h][1] = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+            pw[h][0] = pk_bf16(o[0], o[1]);
+            pw[h][1] = pk_bf16(o[2], o[3]);
           } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) pw[h][i] = __float_as_uint(o[i]);
@@ -345,30 +356,13 @@ __device__ __forceinline__ void tilt_dims(const SM& sm, const float* Mk, const f
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         if constexpr (NT2 == 1) {
           if (I < Cq) {
-            TIn* dst = T + ((size_t)I * D + d) * Cp + 16 * job + 4 * g;
             if constexpr (sizeof(TIn) == 2) *reinterpret_cast<u32x2*>(dst) = u32x2{pw[0][0], pw[0][1]};
             else *reinterpret_cast<u32x4*>(dst) = u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]};
           }
         } else {
-          // across lane bit 5: groups 0, 1 keep tile 0 and take tile 0 of group g + 2;
-          // groups 2, 3 keep tile 1 and take tile 1 of group g - 2
-          const bool hi2 = g >= 2, odd = g & 1;
-          uint32_t e[2][WB], f[2][WB];
-#pragma unroll
-          for (int q = 0; q < WB; ++q) {
-            const uint32_t r = lane_xor32(hi2 ? pw[0][q] : pw[NT2 - 1][q]);
-            e[0][q] = hi2 ? r : pw[0][q];
-            e[1][q] = hi2 ? pw[NT2 - 1][q] : r;
-          }
-          // across lane bit 4: even groups keep their first half, odd groups their second
-#pragma unroll
-          for (int q = 0; q < WB; ++q) {
-            const uint32_t r = lane_xor16(odd ? e[0][q] : e[1][q]);
-            f[0][q] = odd ? r : e[0][q];
-            f[1][q] = odd ? e[1][q] : r;
-          }
+          // tile 0 holds clusters 8g .. 8g+3 of the job, tile 1 8g+4 .. 8g+7
+          const uint32_t (&f)[NT2][WB] = pw;
           if (I < Cq) {
-            TIn* dst = T + ((size_t)I * D + d) * Cp + 32 * job + 8 * g;
             if constexpr (sizeof(TIn) == 2) {
               *reinterpret_cast<u32x4*>(dst) = u32x4{f[0][0], f[0][1], f[1][0], f[1][1]};
             } else {
