@@ -1094,6 +1094,11 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) qmask[qg] = myq[qg] < 0 ? -1 : myq[qg];
 
+  // query rows of the tile are a prefix; a wave whose rows all lie past it
+  // (ragged query tiles) only copies and waits
+  const int nrow = __builtin_amdgcn_readfirstlane(qhi - qlo);
+  const bool wlive = 16 * QG * ws < nrow;
+
   int sl = PD % ST, sc_ = 0;   // stage of the next copy, stage being consumed
   for (int t = 0; t < ntiles; ++t) {
     // this thread's copies of tile t have landed (the PD-1 later tiles, when
@@ -1119,7 +1124,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_kernel(Plan pl, AttnBufs b, i
       if (t + PD < ntiles) issue_next(stg[sl]);
     }
     const TileView tv = view_next();
-    consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, stg[sc_], tv, qf, st, s2, qmask, ones);
+    if (wlive) consume_tile<TIn, D, WAVES, QG, MODE == MODE_LOCAL>(sm, stg[sc_], tv, qf, st, s2, qmask, ones);
     sl = sl + 1 == ST ? 0 : sl + 1;
     sc_ = sc_ + 1 == ST ? 0 : sc_ + 1;
   }
