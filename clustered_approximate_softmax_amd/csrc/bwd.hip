@@ -435,6 +435,9 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_q_kernel(BwdArgs A, int lev) {
   const TIn* Qh = reinterpret_cast<const TIn*>(b.Q) + (size_t)bh * pl.N * D;
   const TIn* dOh = reinterpret_cast<const TIn*>(A.dO) + (size_t)bh * pl.N * D;
   const int myq = sm.qrow[w * 16 + col];
+  // the query rows are a prefix of the tile: a wave past it stages items with
+  // the others but has nothing to contract (local-block tiles are full)
+  const bool wlive = MODE == BQ_LOCAL || 16 * w < qhi - qlo;
   u16x8 qf[KS][NS], df[KS][NS];
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
@@ -490,6 +493,10 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_q_kernel(BwdArgs A, int lev) {
     __syncthreads();
     bq_stage<TIn, D, NT>(sm, far, Kb, Vb, mu, T, b.Cp32, base, Ck);
     __syncthreads();
+    if (!wlive) {
+      __syncthreads();
+      continue;
+    }
     float ds[RT * 4];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
