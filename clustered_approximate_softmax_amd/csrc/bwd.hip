@@ -667,7 +667,9 @@ struct RowLoc {
 };
 
 // A stream of n queries: query q < n is row base + *p of Qh / dOh / lse /
-// delta, {p, base} = row_of(q).  bf16: software-pipelined.  While tile t is contracted,
+// delta, {p, base} = row_of(q).  A wave with no valid item (wlive false, the
+// small key clusters of the levels that stream) stages its share of every
+// tile but skips the contraction.  bf16: software-pipelined.  While tile t is contracted,
 // the Q / dO rows and the lse / Delta of tile t+1 are in flight, and the row
 // indices of tile t+2 (so that no load waits on another inside an
 // iteration).
@@ -676,7 +678,8 @@ __device__ __forceinline__ void bk_query_stream(BkSmem<TIn, D>& sm, const TIn* Q
                                                 const float* delta, int n, RowAt row_of,
                                                 const u16x8 (&kf)[D / 32][BwdTraits<TIn>::NS],
                                                 const u16x8 (&vf)[D / 32][BwdTraits<TIn>::NS], float ibias,
-                                                int irow, float s2, f32x4 (&dvt)[D / 16], f32x4 (&dkt)[D / 16]) {
+                                                int irow, float s2, f32x4 (&dvt)[D / 16], f32x4 (&dkt)[D / 16],
+                                                bool wlive) {
   const int qa = 0, qb = n;
   if constexpr (BkSmem<TIn, D>::NS == 1) {
     // staging layout: thread -> 4 queries (block qb4) x 8 dims (e0); the first QB
@@ -762,7 +765,7 @@ __device__ __forceinline__ void bk_query_stream(BkSmem<TIn, D>& sm, const TIn* Q
         load_data();
         if (t + 2 < ntile) load_rows(qa + (t + 2) * QB);
       }
-      bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
+      if (wlive) bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
       __syncthreads();
     }
   } else {
@@ -779,7 +782,7 @@ __device__ __forceinline__ void bk_query_stream(BkSmem<TIn, D>& sm, const TIn* Q
       __syncthreads();
       bk_stage_queries<TIn, D, NT>(sm, Qh, dOh, lse, delta);
       __syncthreads();
-      bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
+      if (wlive) bk_consume<TIn, D, CAUSAL>(sm, kf, vf, ibias, irow, s2, dvt, dkt);
       __syncthreads();
     }
   }
@@ -1085,7 +1088,7 @@ __global__ void __launch_bounds__(64 * WAVES) bwd_kv_kernel(BwdArgs A, int lev) 
         };
         bk_query_stream<TIn, D, false, NT>(sm, reinterpret_cast<const TIn*>(A.a.Q),
                                            reinterpret_cast<const TIn*>(A.dO), A.lse, A.delta, total, row_of, kf,
-                                           vf, ibias, irow, s2, dvt, dkt);
+                                           vf, ibias, irow, s2, dvt, dkt, 16 * w < iend - ibeg);
       } else {
         // one stream per pair (row indices read straight from q_perm)
         for (int li = 0; li < cnt; ++li) {
