@@ -156,21 +156,39 @@ __global__ void __launch_bounds__(64 * TX_WAVES) tiltx_kernel(Plan pl, AttnBufs 
     for (int ft = 0; ft < FT; ++ft) acc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lp = 0.f;
     for (int t0 = lo; t0 < hi; t0 += TX_KT) {
-      // stage [K | V]^T of keys t0 .. t0+31 (rows past the cluster are zero)
+      // stage [K | V]^T of keys t0 .. t0+31 (rows past the cluster are zero):
+      // a thread takes 4 consecutive keys x 8 features and writes each
+      // feature's 4 keys as one run
       __syncthreads();
-      for (int q = tid; q < TX_KT * (2 * D / 8); q += 64 * TX_WAVES) {
-        const int key = q / (2 * D / 8), f0 = (q % (2 * D / 8)) * 8;
-        float v[8];
-        if (t0 + key < hi) {
-          const TIn* src = f0 < D ? Kp + (size_t)(t0 + key) * D + f0 : Vp + (size_t)(t0 + key) * D + (f0 - D);
-          load8_f32<TIn>(src, v);
+      for (int q = tid; q < (TX_KT / 4) * (2 * D / 8); q += 64 * TX_WAVES) {
+        const int kb = q % (TX_KT / 4), f0 = (q / (TX_KT / 4)) * 8;
+        const TIn* src = f0 < D ? Kp + f0 : Vp + (f0 - D);
+        if constexpr (sizeof(TIn) == 2) {
+          u16x8 r[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int key = t0 + 4 * kb + u;
+            r[u] = key < hi ? *reinterpret_cast<const u16x8*>(src + (size_t)key * D) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<u16x4*>(sm.kv[f0 + j] + 8 * kb) = u16x4{r[0][j], r[1][j], r[2][j], r[3][j]};
         } else {
+          float v[4][8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = 0.f;
+          for (int u = 0; u < 4; ++u) {
+            const int key = t0 + 4 * kb + u;
+            if (key < hi) {
+              load8_f32<TIn>(src + (size_t)key * D, v[u]);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) v[u][j] = 0.f;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<f32x4*>(sm.kv[f0 + j] + 16 * kb) = f32x4{v[0][j], v[1][j], v[2][j], v[3][j]};
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          reinterpret_cast<E*>(sm.kv[f0 + j])[key] = tx_round<E>(v[j]);
       }
       __syncthreads();
       // S = K nu^T: row tile rt, A row r holds key 8 (r / 4) + 4 rt + r % 4, so
