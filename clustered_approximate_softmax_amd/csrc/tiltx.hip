@@ -156,24 +156,47 @@ __global__ void __launch_bounds__(64 * TX_WAVES) tiltx_kernel(Plan pl, AttnBufs 
     for (int ft = 0; ft < FT; ++ft) acc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lp = 0.f;
     for (int t0 = lo; t0 < hi; t0 += TX_KT) {
-      // stage [K | V]^T of keys t0 .. t0+31 (rows past the cluster are zero):
-      // a thread takes 4 consecutive keys x 8 features and writes each
-      // feature's 4 keys as one run
-      __syncthreads();
-      for (int q = tid; q < (TX_KT / 4) * (2 * D / 8); q += 64 * TX_WAVES) {
-        const int kb = q % (TX_KT / 4), f0 = (q / (TX_KT / 4)) * 8;
-        const TIn* src = f0 < D ? Kp + f0 : Vp + (f0 - D);
-        if constexpr (sizeof(TIn) == 2) {
-          u16x8 r[4];
+      // The tile's global reads go out together, before the barriers: the key
+      // rows of S = K nu^T (row tile rt, A row r: key 8 (r / 4) + 4 rt + r % 4,
+      // so lane (col, g) ends with keys 8 g + 4 rt + i of query cluster col)
+      // and, for bf16, the feature-major staging runs of [K | V]^T (4
+      // consecutive keys x 8 features per item, rows past the cluster zero).
+      constexpr int NIT = (TX_KT / 4) * (2 * D / 8) / (64 * TX_WAVES);
+      static_assert(NIT * 64 * TX_WAVES == (TX_KT / 4) * (2 * D / 8), "staging items cover the workgroup");
+      u16x8 ka[2][KS][NSK];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int key = min(t0 + 8 * (col >> 2) + 4 * rt + (col & 3), hi - 1);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) load8_split<TIn, NSK>(Kp + (size_t)key * D + 32 * k + 8 * g, ka[rt][k]);
+      }
+      u16x8 rr[sizeof(TIn) == 2 ? NIT : 1][4];
+      if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int q = tid + it * 64 * TX_WAVES;
+          const int kb = q % (TX_KT / 4), f0 = (q / (TX_KT / 4)) * 8;
+          const TIn* src = f0 < D ? Kp + f0 : Vp + (f0 - D);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int key = t0 + 4 * kb + u;
-            r[u] = key < hi ? *reinterpret_cast<const u16x8*>(src + (size_t)key * D) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            rr[it][u] = key < hi ? *reinterpret_cast<const u16x8*>(src + (size_t)key * D)
+                                 : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
           }
+        }
+      }
+      __syncthreads();   // the previous tile's stage is consumed
+      // each feature's 4 keys written as one run
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int q = tid + it * 64 * TX_WAVES;
+        const int kb = q % (TX_KT / 4), f0 = (q / (TX_KT / 4)) * 8;
+        if constexpr (sizeof(TIn) == 2) {
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<u16x4*>(sm.kv[f0 + j] + 8 * kb) = u16x4{r[0][j], r[1][j], r[2][j], r[3][j]};
+            *reinterpret_cast<u16x4*>(sm.kv[f0 + j] + 8 * kb) = u16x4{rr[it][0][j], rr[it][1][j], rr[it][2][j], rr[it][3][j]};
         } else {
+          const TIn* src = f0 < D ? Kp + f0 : Vp + (f0 - D);
           float v[4][8];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -191,20 +214,12 @@ __global__ void __launch_bounds__(64 * TX_WAVES) tiltx_kernel(Plan pl, AttnBufs 
         }
       }
       __syncthreads();
-      // S = K nu^T: row tile rt, A row r holds key 8 (r / 4) + 4 rt + r % 4, so
-      // lane (col, g) ends with keys 8 g + 4 rt + i of query cluster col
       float x[2][4];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        const int kr = 8 * (col >> 2) + 4 * rt + (col & 3);
-        const int key = min(t0 + kr, hi - 1);
         f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          u16x8 a[NSK];
-          load8_split<TIn, NSK>(Kp + (size_t)key * D + 32 * k + 8 * g, a);
-          sc = mfma_split<NSK, NSN>(a, nf[k], sc);
-        }
+        for (int k = 0; k < KS; ++k) sc = mfma_split<NSK, NSN>(ka[rt][k], nf[k], sc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[rt][i] = t0 + 8 * g + 4 * rt + i < hi ? s2 * sc[i] : -INFINITY;
       }
