@@ -16,11 +16,13 @@
 // This is attention with the query-cluster centroids as queries, the keys of
 // one cluster as keys and [k_j | v_j] as values: per key tile, S = K nu^T on
 // MFMA (nu split into bf16 parts so the scores keep fp32 accuracy), an online
-// base-2 softmax per query cluster, and O^T += [K|V]^T P^T on MFMA with the
-// tile staged feature-major in LDS.  One workgroup takes 32 query clusters
-// (16 per wave) and CB consecutive key clusters, so that the tilted value
-// means of one (I, d) are written as one 16-byte run of the (I, d, c) layout
-// the far tiles read.
+// base-2 softmax per (query cluster, key cluster), and O^T += [K|V]^T P^T on
+// MFMA with the tile staged feature-major in LDS.  One workgroup takes 32
+// query clusters (16 per wave) and CB consecutive key clusters, so that the
+// tilted value means of one (I, d) are written as one 16-byte run of the
+// (I, d, c) layout the far tiles read.  The CB clusters' keys are one range
+// of the sorted copy, tiled as a whole: small clusters share a tile, each
+// cluster masking the others' keys out of its softmax.
 #include "common.h"
 #include "launch.h"
 
@@ -148,81 +150,147 @@ __global__ void __launch_bounds__(64 * TX_WAVES) tiltx_kernel(Plan pl, AttnBufs 
 #pragma unroll
     for (int i = 0; i < 4; ++i) nuf[ft][i] = Iok ? nu[16 * ft + 4 * g + i] : 0.f;
 
-  for (int cl = 0; cl < CB; ++cl) {
-    const int c = cb * CB + cl;
-    const int lo = c < Ck ? koffs[c] : 0, hi = c < Ck ? koffs[c + 1] : 0;
-    f32x4 acc[FT];
+  // The block's clusters are consecutive, so their keys are one range [L, H)
+  // of the sorted copy.  It is walked in full tiles (small clusters share a
+  // tile instead of each padding its own); every cluster with keys in a tile
+  // takes the tile's scores under its own mask, in cluster order, with one
+  // running softmax state: the open cluster's.
+  const int cfirst = cb * CB;
+  const int L = cfirst < Ck ? koffs[cfirst] : 0;
+  const int H = cfirst < Ck ? koffs[min(cfirst + CB, Ck)] : 0;
+  int cl = 0, c = cfirst;
+  int lo = c < Ck ? koffs[c] : 0, hi = c < Ck ? koffs[c + 1] : 0;
+  f32x4 acc[FT];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) acc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lp = 0.f;
+  // write the open cluster's statistics, then open the next one
+  auto finish = [&]() __attribute__((always_inline)) {
+    // normalise; every lane of a column ends with the same m and total
+    float lt = lp + __shfl_xor(lp, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const bool ok = hi > lo;
+    const float inv = ok ? 1.f / lt : 0.f;
+    // tilted key centroid (rounded as the attention kernel reads it) and nu.kappa
+    float dot = 0.f;
+    E* krow = kap + ((size_t)(Iok ? Iw : 0) * Cp + c) * D;
+#pragma unroll
+    for (int ft = 0; ft < D / 16; ++ft) {
+      E kr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kr[i] = tx_round<E>(acc[ft][i] * inv);
+        dot = fmaf(nuf[ft][i], tx_value<E>(kr[i]), dot);
+      }
+      if (Iok) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) krow[16 * ft + 4 * g + i] = kr[i];
+      }
+    }
+    dot += __shfl_xor(dot, 16, 64);
+    dot += __shfl_xor(dot, 32, 64);
+    const int il = 16 * w + col;
+#pragma unroll
+    for (int ft = D / 16; ft < FT; ++ft)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.ust[il][16 * (ft - D / 16) + 4 * g + i][cl] = tx_round<E>(acc[ft][i] * inv);
+    if (g == 0) {
+      const float l2z = m + __log2f(lt);
+      sm.lz[il][cl] = ok ? l2z * TX_LN2 : -INFINITY;
+      sm.fb[il][cl] = ok ? l2z - s2 * dot : -INFINITY;
+    }
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) acc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, lp = 0.f;
-    for (int t0 = lo; t0 < hi; t0 += TX_KT) {
-      // The tile's global reads go out together, before the barriers: the key
-      // rows of S = K nu^T (row tile rt, A row r: key 8 (r / 4) + 4 rt + r % 4,
-      // so lane (col, g) ends with keys 8 g + 4 rt + i of query cluster col)
-      // and, for bf16, the feature-major staging runs of [K | V]^T (4
-      // consecutive keys x 8 features per item, rows past the cluster zero).
-      constexpr int NIT = (TX_KT / 4) * (2 * D / 8) / (64 * TX_WAVES);
-      static_assert(NIT * 64 * TX_WAVES == (TX_KT / 4) * (2 * D / 8), "staging items cover the workgroup");
-      u16x8 ka[2][KS][NSK];
+    m = -INFINITY;
+    lp = 0.f;
+    ++cl;
+    c = cfirst + cl;
+    lo = c < Ck ? koffs[c] : 0;
+    hi = c < Ck ? koffs[c + 1] : 0;
+  };
+  for (int t0 = L; t0 < H; t0 += TX_KT) {
+    // The tile's global reads go out together, before the barriers: the key
+    // rows of S = K nu^T (row tile rt, A row r: key 8 (r / 4) + 4 rt + r % 4,
+    // so lane (col, g) ends with keys 8 g + 4 rt + i of query cluster col)
+    // and, for bf16, the feature-major staging runs of [K | V]^T (4
+    // consecutive keys x 8 features per item, keys past the block zero).
+    constexpr int NIT = (TX_KT / 4) * (2 * D / 8) / (64 * TX_WAVES);
+    static_assert(NIT * 64 * TX_WAVES == (TX_KT / 4) * (2 * D / 8), "staging items cover the workgroup");
+    u16x8 ka[2][KS][NSK];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int key = min(t0 + 8 * (col >> 2) + 4 * rt + (col & 3), hi - 1);
+    for (int rt = 0; rt < 2; ++rt) {
+      const int key = min(t0 + 8 * (col >> 2) + 4 * rt + (col & 3), H - 1);
 #pragma unroll
-        for (int k = 0; k < KS; ++k) load8_split<TIn, NSK>(Kp + (size_t)key * D + 32 * k + 8 * g, ka[rt][k]);
-      }
-      u16x8 rr[sizeof(TIn) == 2 ? NIT : 1][4];
-      if constexpr (sizeof(TIn) == 2) {
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const int q = tid + it * 64 * TX_WAVES;
-          const int kb = q % (TX_KT / 4), f0 = (q / (TX_KT / 4)) * 8;
-          const TIn* src = f0 < D ? Kp + f0 : Vp + (f0 - D);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int key = t0 + 4 * kb + u;
-            rr[it][u] = key < hi ? *reinterpret_cast<const u16x8*>(src + (size_t)key * D)
-                                 : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-          }
-        }
-      }
-      __syncthreads();   // the previous tile's stage is consumed
-      // each feature's 4 keys written as one run
+      for (int k = 0; k < KS; ++k) load8_split<TIn, NSK>(Kp + (size_t)key * D + 32 * k + 8 * g, ka[rt][k]);
+    }
+    u16x8 rr[sizeof(TIn) == 2 ? NIT : 1][4];
+    if constexpr (sizeof(TIn) == 2) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int q = tid + it * 64 * TX_WAVES;
         const int kb = q % (TX_KT / 4), f0 = (q / (TX_KT / 4)) * 8;
-        if constexpr (sizeof(TIn) == 2) {
+        const TIn* src = f0 < D ? Kp + f0 : Vp + (f0 - D);
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<u16x4*>(sm.kv[f0 + j] + 8 * kb) = u16x4{rr[it][0][j], rr[it][1][j], rr[it][2][j], rr[it][3][j]};
-        } else {
-          const TIn* src = f0 < D ? Kp + f0 : Vp + (f0 - D);
-          float v[4][8];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int key = t0 + 4 * kb + u;
-            if (key < hi) {
-              load8_f32<TIn>(src + (size_t)key * D, v[u]);
-            } else {
-#pragma unroll
-              for (int j = 0; j < 8; ++j) v[u][j] = 0.f;
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<f32x4*>(sm.kv[f0 + j] + 16 * kb) = f32x4{v[0][j], v[1][j], v[2][j], v[3][j]};
+        for (int u = 0; u < 4; ++u) {
+          const int key = t0 + 4 * kb + u;
+          rr[it][u] = key < H ? *reinterpret_cast<const u16x8*>(src + (size_t)key * D)
+                               : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
       }
-      __syncthreads();
+    }
+    __syncthreads();   // the previous tile's stage is consumed
+    // each feature's 4 keys written as one run
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int q = tid + it * 64 * TX_WAVES;
+      const int kb = q % (TX_KT / 4), f0 = (q / (TX_KT / 4)) * 8;
+      if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<u16x4*>(sm.kv[f0 + j] + 8 * kb) = u16x4{rr[it][0][j], rr[it][1][j], rr[it][2][j], rr[it][3][j]};
+      } else {
+        const TIn* src = f0 < D ? Kp + f0 : Vp + (f0 - D);
+        float v[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int key = t0 + 4 * kb + u;
+          if (key < H) {
+            load8_f32<TIn>(src + (size_t)key * D, v[u]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[u][j] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<f32x4*>(sm.kv[f0 + j] + 16 * kb) = f32x4{v[0][j], v[1][j], v[2][j], v[3][j]};
+      }
+    }
+    __syncthreads();
+    float xs[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) sc = mfma_split<NSK, NSN>(ka[rt][k], nf[k], sc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[rt][i] = t0 + 8 * g + 4 * rt + i < H ? s2 * sc[i] : -INFINITY;
+    }
+    // the clusters with keys in this tile (empty ones finish as they come)
+    while (cl < CB) {
+      if (hi <= lo) {
+        finish();
+        continue;
+      }
+      if (lo >= t0 + TX_KT) break;   // starts in a later tile
       float x[2][4];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int k = 0; k < KS; ++k) sc = mfma_split<NSK, NSN>(ka[rt][k], nf[k], sc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[rt][i] = t0 + 8 * g + 4 * rt + i < hi ? s2 * sc[i] : -INFINITY;
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int key = t0 + 8 * g + 4 * rt + i;
+          x[rt][i] = key >= lo && key < hi ? xs[rt][i] : -INFINITY;
+        }
       float mt = -INFINITY;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
@@ -259,41 +327,12 @@ __global__ void __launch_bounds__(64 * TX_WAVES) tiltx_kernel(Plan pl, AttnBufs 
         tx_frag<TIn, NSK>(sm.kv[16 * ft + col], g, a);
         acc[ft] = mfma_split<NSK, NSK>(a, pb, acc[ft]);
       }
-    }
-    // normalise; every lane of a column ends with the same m and total
-    float lt = lp + __shfl_xor(lp, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    const bool ok = hi > lo;
-    const float inv = ok ? 1.f / lt : 0.f;
-    // tilted key centroid (rounded as the attention kernel reads it) and nu.kappa
-    float dot = 0.f;
-    E* krow = kap + ((size_t)(Iok ? Iw : 0) * Cp + c) * D;
-#pragma unroll
-    for (int ft = 0; ft < D / 16; ++ft) {
-      E kr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kr[i] = tx_round<E>(acc[ft][i] * inv);
-        dot = fmaf(nuf[ft][i], tx_value<E>(kr[i]), dot);
-      }
-      if (Iok) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) krow[16 * ft + 4 * g + i] = kr[i];
-      }
-    }
-    dot += __shfl_xor(dot, 16, 64);
-    dot += __shfl_xor(dot, 32, 64);
-    const int il = 16 * w + col;
-#pragma unroll
-    for (int ft = D / 16; ft < FT; ++ft)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.ust[il][16 * (ft - D / 16) + 4 * g + i][cl] = tx_round<E>(acc[ft][i] * inv);
-    if (g == 0) {
-      const float l2z = m + __log2f(lt);
-      sm.lz[il][cl] = ok ? l2z * TX_LN2 : -INFINITY;
-      sm.fb[il][cl] = ok ? l2z - s2 * dot : -INFINITY;
+      if (hi > t0 + TX_KT) break;   // continues in the next tile
+      finish();
     }
   }
+  // clusters left (empty, or all of them when the block holds no key)
+  while (cl < CB) finish();
   __syncthreads();
   // U rows of the block's clusters: one 16-byte run per (I, d)
   const int c0 = cb * CB;
